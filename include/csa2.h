@@ -1,0 +1,312 @@
+/*
+ * libcsa2: the CSA2 compressed-sparse-attention step with an FP4 KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The step, as five public news pages about DeepSeek-V4.1-Flash describe it:
+ *   - the main KV cache holds one latent per position as E2M1 values with one
+ *     E4M3 scale per 16 channels and no global scale (ai-wave.ru, "DeepSeek
+ *     V4.1-Flash: 1M context, FP4 KV cache and an attention-reuse
+ *     architecture", fourth paragraph; agentnet.co.il, "DeepSeek launches
+ *     V4.1-Flash ...", section "Quantization and deployment");
+ *   - an indexer scores the positions and keeps 512 of them, directly or
+ *     through a hierarchical pool of at most 2,048 blocks of 8 positions
+ *     (agentnet.co.il, section "CSA2: compression along the layer axis");
+ *   - attention runs over the kept entries plus a 128-token sliding window
+ *     (ai-wave.ru, second paragraph);
+ *   - every layer has a fixed mode: Full, Reindex or Reuse (agentnet.co.il,
+ *     section "CSA2: compression along the layer axis").
+ *
+ * Conventions for every call:
+ *   - Pointers documented as "device" point to GPU memory the caller owns;
+ *     pointers documented as "host" point to host memory read during the
+ *     call only.  The library never allocates or frees caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; the library never synchronises.
+ *   - Every argument is validated before anything is enqueued.  On an error
+ *     nothing is launched, no output is written, and a non-zero status is
+ *     returned; csa2_last_error() then gives a message (thread-local).
+ *   - Scratch memory comes from a caller-provided workspace of at least
+ *     csa2_workspace_bytes() bytes, 256-byte aligned.  Calls that share a
+ *     workspace must be ordered on one stream.
+ *   - Non-finite inputs are outside the contract.
+ *   - Results are deterministic: partial results are combined in a fixed
+ *     order, independent of scheduling.
+ *   - Layout: bf16 tensors are passed as uint16_t bit patterns.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+/* Model constants the kernels are built for. */
+#define CSA2_D_LATENT 512   /* channels of one main-KV latent (key = value)        */
+#define CSA2_SCALE_GROUP 16 /* channels sharing one E4M3 scale                     */
+#define CSA2_NIB_BYTES 256  /* packed E2M1 bytes per entry                          */
+#define CSA2_SCALE_BYTES 32 /* E4M3 scale bytes per entry                           */
+#define CSA2_D_INDEX 64     /* channels of the fp8 indexer key / query per head     */
+#define CSA2_H_INDEX 4      /* indexer heads                                        */
+#define CSA2_H_ATTN 16      /* attention heads                                      */
+#define CSA2_TOP_K 512      /* entries kept per query                               */
+#define CSA2_SWA 128        /* sliding-window length in tokens                      */
+#define CSA2_BLOCK 8        /* positions per hierarchical block                     */
+#define CSA2_N_BLOCKS 2048  /* blocks kept by the hierarchical indexer              */
+#define CSA2_MAX_K 2048     /* largest k accepted by csa2_index_topk                */
+
+/* Status codes. */
+#define CSA2_OK 0
+#define CSA2_ERR_ARG 1         /* a null, misaligned or inconsistent argument       */
+#define CSA2_ERR_UNSUPPORTED 2 /* a size or mode the kernels are not built for      */
+#define CSA2_ERR_STATE 3       /* Reindex/Reuse with no Full layer in the state     */
+#define CSA2_ERR_WORKSPACE 4   /* workspace missing or too small                    */
+#define CSA2_ERR_HIP 5         /* a HIP launch failed; see csa2_last_error()        */
+
+/* Indexer kinds. */
+#define CSA2_INDEX_FLAT 0 /* score every visible position                           */
+#define CSA2_INDEX_HIER 1 /* blocks first, then positions inside the kept blocks    */
+#define CSA2_INDEX_POOL 2 /* score only a given candidate pool                      */
+
+/* Layer modes. */
+#define CSA2_MODE_FULL 0
+#define CSA2_MODE_REINDEX 1
+#define CSA2_MODE_REUSE 2
+
+/* Version of this interface (CSA2_ABI_VERSION); no side effects. */
+int csa2_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none); owned by the
+ * library, valid until the next call on this thread. */
+const char* csa2_last_error(void);
+
+/* sizeof() of the argument structs, for bindings to check their layouts:
+ * 0 index_args, 1 attn_args, 2 kv, 3 layer, 4 group_state, 5 group_args;
+ * 0 for anything else. */
+size_t csa2_struct_size(int32_t which);
+
+/*
+ * Encode tokens into cache entries (the FP4 main-KV encoder, and optionally
+ * the fp8 indexer key).
+ *
+ * Entry j is built from tokens ratio*j .. ratio*j+ratio-1; at ratio 2 it is
+ * their float32 mean fp32(fp32(a+b)*0.5) (globalfeed.ai, "DeepSeek-V4.1-Flash
+ * released ...", section "What changed in the architecture", gives ratio 2
+ * for the encoder layers; the mean is a reading).
+ *
+ * Main KV (ai-wave.ru fourth paragraph; agentnet.co.il section "Quantization
+ * and deployment"): per 16-channel block, scale S = E4M3 nearest to amax/6
+ * (ties to even, saturating at 448); each element code = E2M1 nearest to x/S
+ * (ties to even, saturating at 6, sign bit = sign of x); S == 0 gives code 0.
+ * Byte i of an entry's 256 bytes holds channel 2i (low nibble) and channel
+ * 2i+1 (high nibble); scale j covers channels 16j..16j+15.
+ *
+ * Indexer key (a reading; agentnet.co.il section "CSA2: compression along the
+ * layer axis" says Full layers project an indexer K): ks = fp32(amax/448),
+ * code = E4M3 nearest to fp32(k/ks) (ties to even, saturating); amax == 0
+ * gives ks = 0 and codes 0.
+ *
+ *   x      device float32 [n_tok][ld_x], 16-byte aligned, ld_x a multiple of 4
+ *          and >= 512; the first 512 columns are used
+ *   n_tok  tokens (>= 0, a multiple of ratio); 0 enqueues nothing
+ *   ratio  1 or 2
+ *   nib    device uint8 [n_tok/ratio][256], 16-byte aligned   (out)
+ *   scale  device uint8 [n_tok/ratio][32]    (out)
+ *   k_in   device float32 [n_tok][ld_k] or NULL (then k8/kscale are ignored)
+ *   k8     device uint8 [n_tok/ratio][64], 16-byte aligned    (out)
+ *   kscale device float32 [n_tok/ratio]      (out)
+ * Errors: CSA2_ERR_ARG for null pointers, bad leading dimensions, bad ratio,
+ * n_tok not a multiple of ratio, or misaligned pointers.
+ */
+int csa2_quantize_kv(const float* x, int64_t n_tok, int64_t ld_x, int32_t ratio,
+                     uint8_t* nib, uint8_t* scale,
+                     const float* k_in, int64_t ld_k, uint8_t* k8, float* kscale,
+                     void* stream);
+
+/*
+ * Block keys of the hierarchical indexer (agentnet.co.il, section "CSA2:
+ * compression along the layer axis": blocks of 8 positions).  A reading:
+ * block b of a sequence is the float32 mean of the dequantised keys
+ * fp32(e4m3(code) * ks) of its entries 8b..8b+7 (fewer for a trailing partial
+ * block), summed in position order and divided by their count, then encoded
+ * like an indexer key.
+ *
+ *   k8, kscale   device: sequence s starts at k8 + s*k_stride*64 and
+ *                kscale + s*k_stride
+ *   batch        sequences (>= 0); n_entries[s] (host int64 [batch]) entries each
+ *   bk8, bkscale device out: sequence s at bk8 + s*bk_stride*64 and
+ *                bkscale + s*bk_stride; ceil(n_entries[s]/8) blocks each
+ * Errors: CSA2_ERR_ARG for null pointers, negative sizes, strides smaller
+ * than the data they hold.
+ */
+int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
+                          const int64_t* n_entries, int64_t k_stride,
+                          uint8_t* bk8, float* bkscale, int64_t bk_stride,
+                          void* stream);
+
+/*
+ * Indexer + top-k (agentnet.co.il, section "CSA2: compression along the
+ * layer axis": a Full layer picks 512 fresh positions; Reindex ranks with its
+ * own indexer Q; the hierarchical indexer builds a pool of 2,048 blocks of 8).
+ *
+ * Score (a reading, the pages give no formula):
+ *   s_p = ks_p * sum_h w_h * max(0, q_h . k_p),   h = 0..3, 64 channels,
+ * q_h and k_p being E4M3 code values; computed in float32 on the GPU.
+ * Selection: score descending, then position ascending; the min(k, n)
+ * winners are written in ascending position order, padded with -1.
+ *
+ * Visibility: query i of sequence s is at token position q_pos0[s] + i and
+ * sees entries j < min(n_entries[s], (pos + 1) / ratio).
+ *
+ * FLAT scores every visible entry.  HIER scores the visible blocks (block
+ * keys), keeps the top n_blocks blocks, and scores the visible positions of
+ * those blocks; out_pool (optional) receives the kept positions in ascending
+ * order, -1 padded.  POOL scores only the positions in cand.
+ */
+typedef struct csa2_index_args {
+  int32_t kind;              /* CSA2_INDEX_*                                          */
+  int32_t batch;             /* sequences, >= 1                                       */
+  int32_t n_q;               /* queries per sequence, >= 1                            */
+  int32_t ratio;             /* 1 or 2                                                */
+  const int64_t* q_pos0;     /* host [batch] token position of each sequence's query 0 */
+  const int64_t* n_entries;  /* host [batch] entries present per sequence             */
+  const uint8_t* idx_q;      /* device [batch][n_q][4][64] E4M3 codes                 */
+  const float* idx_w;        /* device [batch][n_q][4] or NULL (all weights 1)        */
+  const uint8_t* k8;         /* device, sequence s at k8 + s*k_stride*64              */
+  const float* kscale;       /* device, sequence s at kscale + s*k_stride             */
+  int64_t k_stride;          /* entries between sequences                             */
+  const uint8_t* bk8;        /* HIER: device block codes, sequence s at + s*bk_stride*64 */
+  const float* bkscale;      /* HIER: device block scales                             */
+  int64_t bk_stride;         /* HIER: blocks between sequences                        */
+  const int32_t* cand;       /* POOL: device [batch][n_q][n_cand] positions, -1 = none */
+  int32_t n_cand;            /* POOL: candidates per query, 1..16384                  */
+  int32_t k;                 /* entries kept per query, 1..CSA2_MAX_K (512 normally)  */
+  int32_t n_blocks;          /* HIER: blocks kept, 1..CSA2_MAX_K (2048 normally)      */
+  int32_t* out_idx;          /* device [batch][n_q][k] (out)                          */
+  int32_t* out_pool;         /* HIER: device [batch][n_q][n_blocks*8] or NULL (out)   */
+} csa2_index_args;
+
+int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse + sliding-window attention (ai-wave.ru second paragraph: every layer
+ * keeps a 128-token window; news.hamidun.com "... 890 bytes per token instead
+ * of 3514", section "Three memory-saving mechanisms": layers read the shared
+ * FP4 cache).  Readings: the latent is both key and value; the window is a
+ * separate bf16 buffer of raw token rows; a query at token p sees the rows of
+ * tokens max(0, p-127)..p and the selected entries in one softmax, without
+ * removing overlaps.  For head h:
+ *   out_h = sum_i softmax_i(scale * q_h . e_i) e_i
+ * with e_i the dequantised entries (exact in bf16) and window rows; products
+ * accumulate in float32.
+ *
+ *   q         device bf16 [batch][n_q][16][512]
+ *   nib/scale device, sequence s at nib + s*kv_stride*256, scale + s*kv_stride*32
+ *   idx       device int32 [batch][n_q][n_idx], -1 = unused; each must be
+ *             < n_entries[s] (not checked on the device)
+ *   swa       device bf16, sequence s at swa + s*swa_stride*512; row r holds
+ *             token swa_pos0[s] + r; swa_rows rows present
+ *   out       device float32 [batch][n_q][16][512] (out)
+ * Errors: CSA2_ERR_ARG when a window row a query needs is not in the buffer.
+ */
+typedef struct csa2_attn_args {
+  int32_t batch, n_q, n_idx;  /* n_idx 0..CSA2_MAX_K                                 */
+  const int64_t* q_pos0;      /* host [batch]                                         */
+  const uint16_t* q;
+  const uint8_t* nib;
+  const uint8_t* scale;
+  int64_t kv_stride;          /* entries between sequences                            */
+  const int32_t* idx;
+  const uint16_t* swa;
+  int64_t swa_stride;         /* rows between sequences                               */
+  const int64_t* swa_pos0;    /* host [batch]                                         */
+  int64_t swa_rows;           /* rows present per sequence                            */
+  float softmax_scale;
+  float* out;
+} csa2_attn_args;
+
+int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The static layer plan (agentnet.co.il, section "CSA2: compression along the
+ * layer axis"; tgviewer.app sof_news24 "DeepSeek V4.1 Flash: new architecture
+ * ...", section "Layers no longer store everything independently"):
+ *   FULL    takes its own encoded KV (kv), indexes it with its own indexer Q,
+ *           and records {kv, indices} in the state;
+ *   REINDEX indexes the state's KV with its own indexer Q (the reading of two
+ *           pages; a third says it keeps the indices) and records the indices;
+ *   REUSE   attends with the state's KV and latest indices, no indexer.
+ * Every layer then runs csa2_sparse_swa_attn with its own q and window rows.
+ * The state persists across calls; Reindex/Reuse with no Full in the state
+ * return CSA2_ERR_STATE.  With index_kind HIER the Full layer uses the
+ * hierarchical indexer and stores its pool; reindex_kind POOL makes Reindex
+ * rank only that pool.
+ */
+typedef struct csa2_kv {
+  const uint8_t* nib;      /* device, sequence s at + s*stride*256                    */
+  const uint8_t* scale;    /* device, sequence s at + s*stride*32                     */
+  const uint8_t* k8;       /* device, sequence s at + s*stride*64                     */
+  const float* kscale;     /* device, sequence s at + s*stride                        */
+  int64_t stride;          /* entries between sequences                               */
+  const uint8_t* bk8;      /* device block keys (HIER), sequence s at + s*bk_stride*64 */
+  const float* bkscale;
+  int64_t bk_stride;       /* blocks between sequences                                */
+} csa2_kv;
+
+typedef struct csa2_layer {
+  int32_t mode;            /* CSA2_MODE_*                                             */
+  const uint16_t* q;       /* device bf16 [batch][n_q][16][512]                       */
+  const uint16_t* swa;     /* device bf16, layout as in csa2_attn_args               */
+  const uint8_t* idx_q;    /* FULL/REINDEX: device [batch][n_q][4][64]                */
+  const float* idx_w;      /* FULL/REINDEX: device [batch][n_q][4] or NULL            */
+  const csa2_kv* kv;       /* FULL: host pointer to the layer's KV                    */
+  float* out;              /* device float32 [batch][n_q][16][512] (out)              */
+} csa2_layer;
+
+typedef struct csa2_group_state {
+  csa2_kv kv;              /* KV of the last Full layer                               */
+  int32_t* indices;        /* caller-owned device [batch][n_q][512]                   */
+  int32_t* pool;           /* caller-owned device [batch][n_q][n_blocks*8] or NULL    */
+  int32_t has_full, has_indices, has_pool;
+  int32_t batch, n_q;      /* shape the indices were made for                         */
+} csa2_group_state;
+
+typedef struct csa2_group_args {
+  int32_t batch, n_q, ratio;
+  int32_t index_kind;      /* CSA2_INDEX_FLAT or CSA2_INDEX_HIER for Full layers      */
+  int32_t reindex_kind;    /* CSA2_INDEX_FLAT or CSA2_INDEX_POOL for Reindex layers   */
+  const int64_t* q_pos0;   /* host [batch]                                            */
+  const int64_t* n_entries;/* host [batch]                                            */
+  const int64_t* swa_pos0; /* host [batch]                                            */
+  int64_t swa_stride, swa_rows;
+  float softmax_scale;
+  int32_t n_layers;
+  const csa2_layer* layers;/* host [n_layers]                                         */
+} csa2_group_args;
+
+int csa2_run_group(const csa2_group_args* a, csa2_group_state* state,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes sufficient for any call with at most max_batch sequences,
+ * max_n_q queries per sequence and max_entries entries per sequence
+ * (returns 0 for invalid sizes).
+ */
+size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entries);
+
+/*
+ * Zero a workspace once after allocating it.  Calls keep their counters and
+ * histograms at zero when they return, so a workspace stays ready for the
+ * next call on the same stream.
+ *   workspace  device, 256-byte aligned;  ws_bytes  a multiple of 4
+ */
+int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,472 @@
+// C ABI of libcsa2: argument validation, workspace carving, launches and the
+// Full / Reindex / Reuse state machine.  Every check runs before the first
+// HIP call, so an invalid call enqueues nothing (and needs no GPU to fail).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kernels.hpp"
+
+using namespace csa2;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxEntries = (int64_t)kMaxFChunks * kFilterChunk;
+constexpr size_t kWsAlign = 256;
+constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of attention partials
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t hist, scores, cand, fcount, blocks, nsel, partial, counter, total;
+  int64_t stride;  // items per row in scores / cand
+};
+
+WsLayout ws_layout(int64_t rows, int64_t max_items) {
+  WsLayout w{};
+  w.stride = (int64_t)round_up((size_t)std::max<int64_t>(max_items, 1), kFilterChunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
+  w.hist = take((size_t)rows * kHistBins * 4);
+  w.scores = take((size_t)rows * w.stride * 4);
+  w.cand = take((size_t)rows * w.stride * 8);
+  w.fcount = take((size_t)rows * kMaxFChunks * 4);
+  w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
+  w.nsel = take((size_t)rows * 4);
+  w.partial = take((size_t)kMaxPartialUnits * kH * (kD + 4) * 4);
+  w.counter = take((size_t)kMaxAttnLayers * std::max<int64_t>(rows, 1) * 4);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+int check_workspace(void* ws, size_t ws_bytes, const WsLayout& w) {
+  if (!ws) return fail(CSA2_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", w.total);
+  if (!aligned(ws, kWsAlign)) return fail(CSA2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < w.total)
+    return fail(CSA2_ERR_WORKSPACE, "workspace has %zu bytes, this call needs %zu", ws_bytes, w.total);
+  return CSA2_OK;
+}
+
+int64_t visible(int64_t q_pos, int32_t ratio, int64_t n_entries) {
+  int64_t v = (q_pos + 1) / ratio;
+  v = std::min(v, n_entries);
+  return v < 0 ? 0 : v;
+}
+
+// ------------------------------------------------------------- indexer
+int validate_index(const csa2_index_args* a) {
+  if (!a) return fail(CSA2_ERR_ARG, "index args are NULL");
+  if (a->kind < CSA2_INDEX_FLAT || a->kind > CSA2_INDEX_POOL) return fail(CSA2_ERR_ARG, "bad index kind %d", a->kind);
+  if (a->batch < 1 || a->n_q < 1) return fail(CSA2_ERR_ARG, "batch and n_q must be >= 1");
+  if (a->ratio != 1 && a->ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
+  if (a->k < 1 || a->k > CSA2_MAX_K) return fail(CSA2_ERR_UNSUPPORTED, "k must be in 1..%d", CSA2_MAX_K);
+  if (!a->q_pos0 || !a->n_entries) return fail(CSA2_ERR_ARG, "q_pos0 and n_entries (host) are required");
+  if (!a->idx_q || !a->k8 || !a->kscale || !a->out_idx) return fail(CSA2_ERR_ARG, "idx_q, k8, kscale, out_idx are required");
+  if (!aligned(a->idx_q, 16) || !aligned(a->k8, 16)) return fail(CSA2_ERR_ARG, "idx_q and k8 must be 16-byte aligned");
+  if (!aligned(a->kscale, 4) || !aligned(a->out_idx, 4) || (a->idx_w && !aligned(a->idx_w, 4)))
+    return fail(CSA2_ERR_ARG, "kscale, idx_w, out_idx must be 4-byte aligned");
+  int64_t max_ne = 0;
+  for (int s = 0; s < a->batch; ++s) {
+    if (a->q_pos0[s] < 0) return fail(CSA2_ERR_ARG, "q_pos0[%d] < 0", s);
+    if (a->n_entries[s] < 0) return fail(CSA2_ERR_ARG, "n_entries[%d] < 0", s);
+    max_ne = std::max(max_ne, a->n_entries[s]);
+  }
+  if (max_ne > kMaxEntries) return fail(CSA2_ERR_UNSUPPORTED, "at most %lld entries per sequence", (long long)kMaxEntries);
+  if (a->batch > 1 && a->k_stride < max_ne) return fail(CSA2_ERR_ARG, "k_stride smaller than n_entries");
+  if (a->kind == CSA2_INDEX_HIER) {
+    if (!a->bk8 || !a->bkscale) return fail(CSA2_ERR_ARG, "HIER needs bk8 and bkscale");
+    if (!aligned(a->bk8, 16) || !aligned(a->bkscale, 4)) return fail(CSA2_ERR_ARG, "bk8 must be 16-byte aligned");
+    if (a->n_blocks < 1 || a->n_blocks > CSA2_MAX_K) return fail(CSA2_ERR_UNSUPPORTED, "n_blocks must be in 1..%d", CSA2_MAX_K);
+    if (a->batch > 1 && a->bk_stride < (max_ne + 7) / 8) return fail(CSA2_ERR_ARG, "bk_stride smaller than the block count");
+    if (a->out_pool && !aligned(a->out_pool, 4)) return fail(CSA2_ERR_ARG, "out_pool must be 4-byte aligned");
+  }
+  if (a->kind == CSA2_INDEX_POOL) {
+    if (!a->cand || !aligned(a->cand, 4)) return fail(CSA2_ERR_ARG, "POOL needs a 4-byte aligned cand");
+    if (a->n_cand < 1 || a->n_cand > kMaxPool) return fail(CSA2_ERR_UNSUPPORTED, "n_cand must be in 1..%d", kMaxPool);
+  }
+  return CSA2_OK;
+}
+
+int64_t index_max_items(const csa2_index_args* a) {
+  int64_t m = 0;
+  for (int s = 0; s < a->batch; ++s) m = std::max(m, a->n_entries[s]);
+  if (a->kind == CSA2_INDEX_POOL) m = std::max<int64_t>(m, a->n_cand);
+  if (a->kind == CSA2_INDEX_HIER) m = std::max<int64_t>(m, (int64_t)a->n_blocks * CSA2_BLOCK);
+  return m;
+}
+
+int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t stream) {
+  for (int s0 = 0; s0 < a->batch; s0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, a->batch - s0);
+    IndexPass p{};
+    p.rows = nb * a->n_q;
+    p.n_q = a->n_q;
+    p.ratio = a->ratio;
+    int64_t max_vis = 0;
+    for (int i = 0; i < nb; ++i) {
+      p.seq.a[i] = a->q_pos0[s0 + i];
+      p.seq.b[i] = a->n_entries[s0 + i];
+      max_vis = std::max(max_vis, visible(a->q_pos0[s0 + i] + a->n_q - 1, a->ratio, a->n_entries[s0 + i]));
+    }
+    const int64_t row0 = (int64_t)s0 * a->n_q;
+    if (max_vis == 0) {  // nothing visible in these sequences: every output is -1
+      hipError_t f = launch_fill_u32(reinterpret_cast<uint32_t*>(a->out_idx + row0 * a->k),
+                                     (size_t)p.rows * a->k, 0xFFFFFFFFu, stream);
+      if (f == hipSuccess && a->kind == CSA2_INDEX_HIER && a->out_pool)
+        f = launch_fill_u32(reinterpret_cast<uint32_t*>(a->out_pool + row0 * a->n_blocks * CSA2_BLOCK),
+                            (size_t)p.rows * a->n_blocks * CSA2_BLOCK, 0xFFFFFFFFu, stream);
+      if (f != hipSuccess) return hip_fail(f, "fill");
+      continue;
+    }
+    p.idx_q = a->idx_q + row0 * kHI * kDI;
+    p.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;
+    p.hist = at<uint32_t>(ws, w.hist);
+    p.scores = at<uint32_t>(ws, w.scores);
+    p.cand = at<uint64_t>(ws, w.cand);
+    p.score_stride = w.stride;
+    p.fcount = at<uint32_t>(ws, w.fcount);
+    p.max_fchunks = kMaxFChunks;
+    hipError_t e;
+    if (a->kind == CSA2_INDEX_HIER) {
+      IndexPass b = p;  // pass 1: blocks
+      b.source = kItemsDirect;
+      b.block_level = 1;
+      b.k = a->n_blocks;
+      b.k8 = a->bk8 + (int64_t)s0 * a->bk_stride * kDI;
+      b.kscale = a->bkscale + (int64_t)s0 * a->bk_stride;
+      b.k_stride = a->bk_stride;
+      b.max_items = (max_vis + 7) / 8;
+      b.out = at<int32_t>(ws, w.blocks);
+      b.out_stride = CSA2_MAX_K;
+      b.out_count = at<int32_t>(ws, w.nsel);
+      b.out_pool = a->out_pool ? a->out_pool + row0 * a->n_blocks * CSA2_BLOCK : nullptr;
+      b.pool_stride = a->n_blocks * CSA2_BLOCK;
+      if ((e = launch_index_pass(b, stream)) != hipSuccess) return hip_fail(e, "hierarchical block pass");
+      p.source = kItemsBlocks;  // pass 2: positions of the kept blocks
+      p.blocks = b.out;
+      p.nsel = b.out_count;
+      p.max_items = (int64_t)a->n_blocks * CSA2_BLOCK;
+    } else if (a->kind == CSA2_INDEX_POOL) {
+      p.source = kItemsList;
+      p.list = a->cand + row0 * a->n_cand;
+      p.list_len = a->n_cand;
+      p.max_items = a->n_cand;
+    } else {
+      p.source = kItemsDirect;
+      p.max_items = max_vis;
+    }
+    p.block_level = 0;
+    p.k = a->k;
+    p.k8 = a->k8 + (int64_t)s0 * a->k_stride * kDI;
+    p.kscale = a->kscale + (int64_t)s0 * a->k_stride;
+    p.k_stride = a->k_stride;
+    p.out = a->out_idx + row0 * a->k;
+    p.out_stride = a->k;
+    if ((e = launch_index_pass(p, stream)) != hipSuccess) return hip_fail(e, "index pass");
+  }
+  return CSA2_OK;
+}
+
+// ------------------------------------------------------------- attention
+int validate_attn_common(int32_t batch, int32_t n_q, int32_t n_idx, const int64_t* q_pos0,
+                         const int64_t* swa_pos0, int64_t swa_rows, int64_t swa_stride) {
+  if (batch < 1 || n_q < 1) return fail(CSA2_ERR_ARG, "batch and n_q must be >= 1");
+  if (n_idx < 0 || n_idx > CSA2_MAX_K) return fail(CSA2_ERR_UNSUPPORTED, "n_idx must be in 0..%d", CSA2_MAX_K);
+  if (!q_pos0 || !swa_pos0) return fail(CSA2_ERR_ARG, "q_pos0 and swa_pos0 (host) are required");
+  if (swa_rows < 1) return fail(CSA2_ERR_ARG, "swa_rows must be >= 1");
+  if (batch > 1 && swa_stride < swa_rows) return fail(CSA2_ERR_ARG, "swa_stride smaller than swa_rows");
+  for (int s = 0; s < batch; ++s) {
+    if (q_pos0[s] < 0) return fail(CSA2_ERR_ARG, "q_pos0[%d] < 0", s);
+    const int64_t first = std::max<int64_t>(0, q_pos0[s] - (CSA2_SWA - 1));
+    const int64_t last = q_pos0[s] + n_q - 1;
+    if (first < swa_pos0[s] || last - swa_pos0[s] >= swa_rows)
+      return fail(CSA2_ERR_ARG, "sequence %d: window tokens %lld..%lld not in the buffer (rows %lld..%lld)", s,
+                  (long long)first, (long long)last, (long long)swa_pos0[s], (long long)(swa_pos0[s] + swa_rows - 1));
+  }
+  return CSA2_OK;
+}
+
+struct AttnJob {
+  int32_t batch, n_q, n_idx;
+  const int64_t* q_pos0;
+  const int64_t* swa_pos0;
+  const uint8_t* nib;
+  const uint8_t* scale;
+  int64_t kv_stride;
+  const int32_t* idx;
+  int64_t swa_stride;
+  float softmax_scale;
+  int n_layers;
+  AttnLayer layer[kMaxAttnLayers];
+};
+
+int run_attention(const AttnJob& j, void* ws, const WsLayout& w, hipStream_t stream) {
+  const int n_tile_idx = (j.n_idx + kAttnSplit - 1) / kAttnSplit;
+  const int n_tiles = n_tile_idx + (CSA2_SWA + kAttnSplit - 1) / kAttnSplit;
+  for (int s0 = 0; s0 < j.batch; s0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, j.batch - s0);
+    AttnPass p{};
+    p.rows = nb * j.n_q;
+    p.n_q = j.n_q;
+    p.n_idx = j.n_idx;
+    p.n_layers = j.n_layers;
+    for (int i = 0; i < nb; ++i) {
+      p.seq.a[i] = j.q_pos0[s0 + i];
+      p.seq.b[i] = j.swa_pos0[s0 + i];
+    }
+    const int64_t row0 = (int64_t)s0 * j.n_q;
+    p.nib = j.nib + (int64_t)s0 * j.kv_stride * CSA2_NIB_BYTES;
+    p.scale = j.scale + (int64_t)s0 * j.kv_stride * CSA2_SCALE_BYTES;
+    p.kv_stride = j.kv_stride;
+    p.idx = j.idx ? j.idx + row0 * j.n_idx : nullptr;
+    p.swa_stride = j.swa_stride;
+    p.softmax_scale = j.softmax_scale;
+    for (int l = 0; l < j.n_layers; ++l) {
+      p.layer[l].q = j.layer[l].q + row0 * kH * kD;
+      p.layer[l].swa = j.layer[l].swa + (int64_t)s0 * j.swa_stride * kD;
+      p.layer[l].out = j.layer[l].out + row0 * kH * kD;
+    }
+    // split the candidate tiles of a (layer, row) over workgroups until about
+    // 1024 workgroups are in flight; with many rows one workgroup walks them all
+    const int units = p.n_layers * p.rows;
+    int splits = std::max(1, std::min(n_tiles, (1024 + units - 1) / units));
+    while (splits > 1 && (int64_t)units * splits > kMaxPartialUnits) --splits;
+    p.n_tiles = n_tiles;
+    p.tiles_per_split = (n_tiles + splits - 1) / splits;
+    p.max_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+    p.partial = at<float>(ws, w.partial);
+    p.counter = at<uint32_t>(ws, w.counter);
+    hipError_t e = launch_attention(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention");
+  }
+  return CSA2_OK;
+}
+
+int validate_kv_ptrs(const uint8_t* nib, const uint8_t* scale) {
+  if (!nib || !scale) return fail(CSA2_ERR_ARG, "nib and scale are required");
+  if (!aligned(nib, 16) || !aligned(scale, 8)) return fail(CSA2_ERR_ARG, "nib must be 16-byte and scale 8-byte aligned");
+  return CSA2_OK;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+extern "C" {
+
+int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+size_t csa2_struct_size(int32_t which) {
+  switch (which) {
+    case 0: return sizeof(csa2_index_args);
+    case 1: return sizeof(csa2_attn_args);
+    case 2: return sizeof(csa2_kv);
+    case 3: return sizeof(csa2_layer);
+    case 4: return sizeof(csa2_group_state);
+    case 5: return sizeof(csa2_group_args);
+    default: return 0;
+  }
+}
+
+const char* csa2_last_error(void) { return g_err; }
+
+size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entries) {
+  if (max_batch < 1 || max_n_q < 1 || max_entries < 0) return 0;
+  const int64_t rows = std::min<int64_t>(max_batch, kMaxSeqPerLaunch) * max_n_q;
+  const int64_t items = std::max<int64_t>(max_entries, kMaxPool);
+  return ws_layout(rows, items).total;
+}
+
+int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || !aligned(workspace, kWsAlign) || ws_bytes % 4)
+    return fail(CSA2_ERR_WORKSPACE, "workspace must be non-NULL, 256-byte aligned, a multiple of 4 bytes");
+  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(workspace), ws_bytes / 4, 0u, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "workspace init");
+}
+
+int csa2_quantize_kv(const float* x, int64_t n_tok, int64_t ld_x, int32_t ratio, uint8_t* nib,
+                     uint8_t* scale, const float* k_in, int64_t ld_k, uint8_t* k8, float* kscale,
+                     void* stream) {
+  if (ratio != 1 && ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
+  if (n_tok < 0 || n_tok % ratio) return fail(CSA2_ERR_ARG, "n_tok must be >= 0 and a multiple of ratio");
+  if (n_tok == 0) return CSA2_OK;
+  if (!x || !nib || !scale) return fail(CSA2_ERR_ARG, "x, nib, scale are required");
+  if (ld_x < CSA2_D_LATENT || ld_x % 4) return fail(CSA2_ERR_ARG, "ld_x must be >= 512 and a multiple of 4");
+  if (!aligned(x, 16) || !aligned(nib, 16)) return fail(CSA2_ERR_ARG, "x and nib must be 16-byte aligned");
+  if (k_in) {
+    if (!k8 || !kscale) return fail(CSA2_ERR_ARG, "k8 and kscale are required with k_in");
+    if (ld_k < CSA2_D_INDEX) return fail(CSA2_ERR_ARG, "ld_k must be >= 64");
+    if (!aligned(k_in, 4) || !aligned(k8, 16) || !aligned(kscale, 4))
+      return fail(CSA2_ERR_ARG, "k_in/kscale must be 4-byte and k8 16-byte aligned");
+  }
+  hipError_t e = launch_quantize(x, n_tok / ratio, ld_x, ratio, nib, scale, k_in, ld_k, k8, kscale,
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "quantize");
+}
+
+int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
+                          const int64_t* n_entries, int64_t k_stride, uint8_t* bk8, float* bkscale,
+                          int64_t bk_stride, void* stream) {
+  if (batch < 0) return fail(CSA2_ERR_ARG, "batch < 0");
+  if (batch == 0) return CSA2_OK;
+  if (!k8 || !kscale || !n_entries || !bk8 || !bkscale) return fail(CSA2_ERR_ARG, "null argument");
+  if (!aligned(k8, 16) || !aligned(bk8, 16) || !aligned(kscale, 4) || !aligned(bkscale, 4))
+    return fail(CSA2_ERR_ARG, "k8/bk8 must be 16-byte and scales 4-byte aligned");
+  int64_t max_ne = 0;
+  for (int s = 0; s < batch; ++s) {
+    if (n_entries[s] < 0) return fail(CSA2_ERR_ARG, "n_entries[%d] < 0", s);
+    max_ne = std::max(max_ne, n_entries[s]);
+  }
+  if (batch > 1 && (k_stride < max_ne || bk_stride < (max_ne + 7) / 8))
+    return fail(CSA2_ERR_ARG, "strides smaller than the data they hold");
+  hipError_t e = launch_block_keys(k8, kscale, k_stride, n_entries, batch, bk8, bkscale, bk_stride,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "block keys");
+}
+
+int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = validate_index(a);
+  if (rc) return rc;
+  const WsLayout w = ws_layout((int64_t)std::min(a->batch, kMaxSeqPerLaunch) * a->n_q, index_max_items(a));
+  if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
+  return run_index(a, workspace, w, (hipStream_t)stream);
+}
+
+int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  if (!a) return fail(CSA2_ERR_ARG, "attention args are NULL");
+  int rc = validate_attn_common(a->batch, a->n_q, a->n_idx, a->q_pos0, a->swa_pos0, a->swa_rows, a->swa_stride);
+  if (rc) return rc;
+  if ((rc = validate_kv_ptrs(a->nib, a->scale))) return rc;
+  if (!a->q || !a->swa || !a->out || (a->n_idx > 0 && !a->idx)) return fail(CSA2_ERR_ARG, "q, swa, out, idx are required");
+  if (!aligned(a->q, 16) || !aligned(a->swa, 16) || !aligned(a->out, 16) || (a->idx && !aligned(a->idx, 4)))
+    return fail(CSA2_ERR_ARG, "q, swa, out must be 16-byte aligned");
+  if (a->batch > 1 && a->kv_stride < 0) return fail(CSA2_ERR_ARG, "kv_stride < 0");
+  const WsLayout w = ws_layout((int64_t)std::min(a->batch, kMaxSeqPerLaunch) * a->n_q, 0);
+  if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
+  AttnJob j{};
+  j.batch = a->batch; j.n_q = a->n_q; j.n_idx = a->n_idx;
+  j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0;
+  j.nib = a->nib; j.scale = a->scale; j.kv_stride = a->kv_stride;
+  j.idx = a->idx; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
+  j.n_layers = 1;
+  j.layer[0] = AttnLayer{a->q, a->swa, a->out};
+  return run_attention(j, workspace, w, (hipStream_t)stream);
+}
+
+int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  if (!a || !st) return fail(CSA2_ERR_ARG, "group args and state are required");
+  if (a->n_layers < 1 || !a->layers) return fail(CSA2_ERR_ARG, "at least one layer is required");
+  if (a->ratio != 1 && a->ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
+  if (a->index_kind != CSA2_INDEX_FLAT && a->index_kind != CSA2_INDEX_HIER)
+    return fail(CSA2_ERR_ARG, "index_kind must be FLAT or HIER");
+  if (a->reindex_kind != CSA2_INDEX_FLAT && a->reindex_kind != CSA2_INDEX_POOL)
+    return fail(CSA2_ERR_ARG, "reindex_kind must be FLAT or POOL");
+  if (!a->n_entries) return fail(CSA2_ERR_ARG, "n_entries (host) is required");
+  int rc = validate_attn_common(a->batch, a->n_q, CSA2_TOP_K, a->q_pos0, a->swa_pos0, a->swa_rows, a->swa_stride);
+  if (rc) return rc;
+  if (!st->indices || !aligned(st->indices, 4)) return fail(CSA2_ERR_ARG, "state.indices must be a device buffer");
+  // simulate the plan on the host: every mode change is checked before launching
+  int has_full = st->has_full, has_idx = st->has_indices, has_pool = st->has_pool;
+  if ((has_idx || has_full) && (st->batch != a->batch || st->n_q != a->n_q))
+    return fail(CSA2_ERR_STATE, "state was made for batch %d x n_q %d", st->batch, st->n_q);
+  int64_t max_ne = 0;
+  for (int s = 0; s < a->batch; ++s) {
+    if (a->n_entries[s] < 0) return fail(CSA2_ERR_ARG, "n_entries[%d] < 0", s);
+    max_ne = std::max(max_ne, a->n_entries[s]);
+  }
+  for (int l = 0; l < a->n_layers; ++l) {
+    const csa2_layer& L = a->layers[l];
+    if (L.mode < CSA2_MODE_FULL || L.mode > CSA2_MODE_REUSE) return fail(CSA2_ERR_ARG, "layer %d: bad mode", l);
+    if (!L.q || !L.swa || !L.out || !aligned(L.q, 16) || !aligned(L.swa, 16) || !aligned(L.out, 16))
+      return fail(CSA2_ERR_ARG, "layer %d: q, swa, out must be 16-byte aligned device pointers", l);
+    if (L.mode == CSA2_MODE_FULL) {
+      if (!L.kv) return fail(CSA2_ERR_ARG, "layer %d: FULL needs kv", l);
+      if ((rc = validate_kv_ptrs(L.kv->nib, L.kv->scale))) return rc;
+      if (!L.kv->k8 || !L.kv->kscale || !aligned(L.kv->k8, 16)) return fail(CSA2_ERR_ARG, "layer %d: kv.k8/kscale", l);
+      if (a->batch > 1 && L.kv->stride < max_ne) return fail(CSA2_ERR_ARG, "layer %d: kv.stride < n_entries", l);
+      if (a->index_kind == CSA2_INDEX_HIER && (!L.kv->bk8 || !L.kv->bkscale))
+        return fail(CSA2_ERR_ARG, "layer %d: HIER needs block keys", l);
+      if (a->index_kind == CSA2_INDEX_HIER && !st->pool && a->reindex_kind == CSA2_INDEX_POOL)
+        return fail(CSA2_ERR_ARG, "POOL reindexing needs state.pool");
+      has_full = has_idx = 1;
+      if (a->index_kind == CSA2_INDEX_HIER && st->pool) has_pool = 1;
+    } else if (L.mode == CSA2_MODE_REINDEX) {
+      if (!has_full) return fail(CSA2_ERR_STATE, "layer %d: REINDEX before any FULL layer", l);
+      if (a->reindex_kind == CSA2_INDEX_POOL && !has_pool)
+        return fail(CSA2_ERR_STATE, "layer %d: POOL REINDEX without a hierarchical pool", l);
+      has_idx = 1;
+    } else {
+      if (!has_full || !has_idx) return fail(CSA2_ERR_STATE, "layer %d: REUSE before any FULL layer", l);
+    }
+    if (L.mode != CSA2_MODE_REUSE) {
+      if (!L.idx_q || !aligned(L.idx_q, 16)) return fail(CSA2_ERR_ARG, "layer %d: idx_q must be 16-byte aligned", l);
+      if (L.idx_w && !aligned(L.idx_w, 4)) return fail(CSA2_ERR_ARG, "layer %d: idx_w alignment", l);
+    }
+  }
+  const int64_t rows = (int64_t)std::min(a->batch, kMaxSeqPerLaunch) * a->n_q;
+  const WsLayout w = ws_layout(rows, std::max<int64_t>(max_ne, kMaxPool));
+  if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
+
+  hipStream_t s = (hipStream_t)stream;
+  int l = 0;
+  while (l < a->n_layers) {
+    const csa2_layer& L = a->layers[l];
+    if (L.mode == CSA2_MODE_FULL) st->kv = *L.kv;
+    if (L.mode != CSA2_MODE_REUSE) {
+      csa2_index_args ia{};
+      const bool hier = (L.mode == CSA2_MODE_FULL && a->index_kind == CSA2_INDEX_HIER);
+      const bool pool = (L.mode == CSA2_MODE_REINDEX && a->reindex_kind == CSA2_INDEX_POOL);
+      ia.kind = hier ? CSA2_INDEX_HIER : pool ? CSA2_INDEX_POOL : CSA2_INDEX_FLAT;
+      ia.batch = a->batch; ia.n_q = a->n_q; ia.ratio = a->ratio;
+      ia.q_pos0 = a->q_pos0; ia.n_entries = a->n_entries;
+      ia.idx_q = L.idx_q; ia.idx_w = L.idx_w;
+      ia.k8 = st->kv.k8; ia.kscale = st->kv.kscale; ia.k_stride = st->kv.stride;
+      ia.bk8 = st->kv.bk8; ia.bkscale = st->kv.bkscale; ia.bk_stride = st->kv.bk_stride;
+      ia.cand = st->pool; ia.n_cand = kMaxPool;
+      ia.k = CSA2_TOP_K; ia.n_blocks = CSA2_N_BLOCKS;
+      ia.out_idx = st->indices;
+      ia.out_pool = hier ? st->pool : nullptr;
+      if ((rc = run_index(&ia, workspace, w, s))) return rc;
+      if (L.mode == CSA2_MODE_FULL) { st->has_full = 1; if (hier && st->pool) st->has_pool = 1; }
+      st->has_indices = 1;
+      st->batch = a->batch; st->n_q = a->n_q;
+    }
+    // this layer and the Reuse layers after it share KV and indices: one launch
+    AttnJob j{};
+    j.batch = a->batch; j.n_q = a->n_q; j.n_idx = CSA2_TOP_K;
+    j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0;
+    j.nib = st->kv.nib; j.scale = st->kv.scale; j.kv_stride = st->kv.stride;
+    j.idx = st->indices; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
+    j.n_layers = 0;
+    do {
+      const csa2_layer& M = a->layers[l];
+      j.layer[j.n_layers++] = AttnLayer{M.q, M.swa, M.out};
+      ++l;
+    } while (l < a->n_layers && a->layers[l].mode == CSA2_MODE_REUSE && j.n_layers < kMaxAttnLayers);
+    if ((rc = run_attention(j, workspace, w, s))) return rc;
+  }
+  return CSA2_OK;
+}
+
+}  // extern "C"

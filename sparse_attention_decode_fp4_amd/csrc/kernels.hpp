@@ -1,0 +1,97 @@
+// Internal interface between the host dispatch (api.cpp) and the HIP kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace csa2 {
+
+// Per-sequence scalars travel as kernel arguments (no host-to-device copy, so
+// a stream capture records them); a launch covers at most this many sequences.
+constexpr int kMaxSeqPerLaunch = 64;
+struct SeqArgs {
+  int64_t a[kMaxSeqPerLaunch];
+  int64_t b[kMaxSeqPerLaunch];
+};
+
+// Items scored per workgroup of the indexer scan, and per filter workgroup.
+constexpr int kScanChunk = 2048;
+constexpr int kFilterChunk = 8192;
+constexpr int kMaxPool = CSA2_N_BLOCKS * CSA2_BLOCK;  // 16,384 positions
+constexpr int kMaxFChunks = 1024;                     // filter chunks per row: <= 8M items
+
+// Where the items of an indexer pass come from.
+enum ItemSource : int32_t {
+  kItemsDirect = 0,  // item i is position i (entry or block id)
+  kItemsBlocks = 1,  // item i is position 8*blocks[i/8] + i%8 (hierarchical pool)
+  kItemsList = 2,    // item i is position list[i], -1 = empty (candidate pool)
+};
+
+// One indexer pass over `rows` query rows (row = seq * n_q + i).
+struct IndexPass {
+  int32_t rows, n_q, ratio, k;
+  int32_t source;
+  int32_t block_level;         // 1: scoring block keys (visibility in blocks)
+  SeqArgs seq;                 // a = q_pos0, b = n_entries (per sequence)
+  const uint8_t* idx_q;        // [rows][4][64]
+  const float* idx_w;          // [rows][4] or null
+  const uint8_t* k8;           // per sequence at + seq*k_stride*64
+  const float* kscale;
+  int64_t k_stride;
+  const int32_t* list;         // kItemsList: [rows][list_len]
+  int32_t list_len;
+  const int32_t* blocks;       // kItemsBlocks: [rows][CSA2_MAX_K] selected block ids
+  const int32_t* nsel;         // kItemsBlocks: [rows] number of selected blocks
+  int64_t max_items;           // items per row the grid covers
+  // workspace
+  uint32_t* hist;              // [rows][kHistBins], zero on entry, zero on exit
+  uint32_t* scores;            // [rows][score_stride]
+  int64_t score_stride;
+  uint64_t* cand;              // [rows][score_stride]
+  uint32_t* fcount;            // [rows][max_fchunks]
+  int32_t max_fchunks;
+  // output: either positions (out_idx, -1 padded to k) or block ids + count
+  int32_t* out;                // [rows][out_stride]
+  int32_t out_stride;
+  int32_t* out_count;          // [rows] or null
+  int32_t* out_pool;           // optional: pool positions of the kept blocks
+  int32_t pool_stride;
+};
+
+hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int32_t ratio,
+                           uint8_t* nib, uint8_t* scale, const float* kin, int64_t ld_k,
+                           uint8_t* k8, float* kscale, hipStream_t stream);
+hipError_t launch_block_keys(const uint8_t* k8, const float* ks, int64_t k_stride,
+                             const int64_t* n_entries, int32_t batch, uint8_t* bk8, float* bks,
+                             int64_t bk_stride, hipStream_t stream);
+hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
+
+// Attention over the candidates of each row for one or more layers that
+// share the KV and the index lists.
+struct AttnLayer {
+  const uint16_t* q;    // [rows][16][512]
+  const uint16_t* swa;  // per sequence at + seq*swa_stride*512
+  float* out;           // [rows][16][512]
+};
+constexpr int kMaxAttnLayers = 8;
+constexpr int kAttnSplit = 64;  // candidates per workgroup
+struct AttnPass {
+  int32_t rows, n_q, n_idx, n_layers;
+  SeqArgs seq;                  // a = q_pos0, b = swa_pos0
+  const uint8_t* nib;
+  const uint8_t* scale;
+  int64_t kv_stride;
+  const int32_t* idx;           // [rows][n_idx]
+  int64_t swa_stride;
+  float softmax_scale;
+  AttnLayer layer[kMaxAttnLayers];
+  int32_t n_tiles;              // candidate tiles of kAttnSplit rows per (layer, row)
+  int32_t tiles_per_split;      // tiles one workgroup walks (online softmax)
+  int32_t max_splits;           // ceil(n_tiles / tiles_per_split)
+  // workspace (used when max_splits > 1)
+  float* partial;               // [n_layers*rows][max_splits][16][516]
+  uint32_t* counter;            // [n_layers*rows], zero on entry, zero on exit
+};
+hipError_t launch_attention(const AttnPass& p, hipStream_t stream);
+
+}  // namespace csa2

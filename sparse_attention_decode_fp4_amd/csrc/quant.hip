@@ -1,0 +1,177 @@
+// Cache encoders: FP4 main KV, fp8 indexer key (with the ratio-2 pair mean),
+// and the hierarchical block keys.
+//
+// Main-KV format (ai-wave.ru "DeepSeek V4.1-Flash: 1M context, FP4 KV cache
+// ...", fourth paragraph; agentnet.co.il "DeepSeek launches V4.1-Flash ...",
+// section "Quantization and deployment"): E2M1 values, one E4M3 scale per 16
+// channels, no global scale.  Rounding decisions use exact binary32 products
+// and IEEE-rounded divisions (f32_div / f32_add / f32_mul), so the
+// stored bytes do not depend on FMA contraction or fast-math.
+#include "kernels.hpp"
+
+// Stored bytes must follow binary32 rounding of every step: no mul+add fusion.
+#pragma clang fp contract(off)
+
+namespace csa2 {
+
+// One thread per 16-channel block of one entry: 32 threads per latent row, so
+// a 256-thread workgroup encodes 8 entries.  The first four threads of each
+// entry's group also encode the 64-channel indexer key (16 channels each).
+__global__ __launch_bounds__(256) void k_quantize(
+    const float* __restrict__ x, int64_t ld_x, int32_t ratio, int64_t n_entries,
+    uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
+    const float* __restrict__ kin, int64_t ld_k, uint8_t* __restrict__ k8,
+    float* __restrict__ kscale) {
+  const int64_t entry = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int blk = threadIdx.x & 31;
+  if (entry >= n_entries) return;  // whole 32-lane groups leave together
+
+  // ---- main latent block
+  float v[16];
+  const float* r0 = x + entry * ratio * ld_x + blk * 16;
+  if (ratio == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      float4 t = *reinterpret_cast<const float4*>(r0 + i);
+      v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+    }
+  } else {
+    const float* r1 = r0 + ld_x;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      float4 a = *reinterpret_cast<const float4*>(r0 + i);
+      float4 b = *reinterpret_cast<const float4*>(r1 + i);
+      v[i] = f32_mul(f32_add(a.x, b.x), 0.5f);
+      v[i + 1] = f32_mul(f32_add(a.y, b.y), 0.5f);
+      v[i + 2] = f32_mul(f32_add(a.z, b.z), 0.5f);
+      v[i + 3] = f32_mul(f32_add(a.w, b.w), 0.5f);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+  const uint32_t sc = fp4_block_scale(amax);
+  const float s = e4m3_mag(sc);
+  uint32_t w0 = 0, w1 = 0;
+  if (s > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w0 |= fp4_code(v[i], s) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w1 |= fp4_code(v[8 + i], s) << (4 * i);
+  }
+  *reinterpret_cast<uint2*>(nib + entry * CSA2_NIB_BYTES + blk * 8) = make_uint2(w0, w1);
+  scale[entry * CSA2_SCALE_BYTES + blk] = (uint8_t)sc;
+
+  // ---- indexer key: 4 lanes x 16 channels
+  if (kin == nullptr) return;
+  float kv[16];
+  float kmax = 0.0f;
+  if (blk < 4) {
+    const float* q0 = kin + entry * ratio * ld_k + blk * 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float a = q0[i];
+      kv[i] = (ratio == 1) ? a : f32_mul(f32_add(a, q0[ld_k + i]), 0.5f);
+      kmax = fmaxf(kmax, __builtin_fabsf(kv[i]));
+    }
+  }
+  // amax over the 4 lanes of this entry (lanes 0..3 of the 32-lane group)
+  kmax = fmaxf(kmax, quad_xor1(kmax));
+  kmax = fmaxf(kmax, quad_xor2(kmax));
+  if (blk >= 4) return;
+  const float ks = f32_div(kmax, 448.0f);
+  uint32_t c[4] = {0, 0, 0, 0};
+  if (ks > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i >> 2] |= e4m3_from_f32(f32_div(kv[i], ks)) << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint4*>(k8 + entry * CSA2_D_INDEX + blk * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+  if (blk == 0) kscale[entry] = ks;
+}
+
+// Block keys: one thread per (block, 16-channel quarter); a quad encodes one
+// block.  Block b holds entries 8b .. min(8b+8, n)-1 of its sequence.
+__global__ __launch_bounds__(256) void k_block_keys(
+    const uint8_t* __restrict__ k8, const float* __restrict__ ks, int64_t k_stride,
+    SeqArgs sa, uint8_t* __restrict__ bk8, float* __restrict__ bks, int64_t bk_stride) {
+  const int seq = blockIdx.y;
+  const int64_t block = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int quarter = threadIdx.x & 3;
+  const int64_t n = sa.a[seq];
+  const int64_t nb = (n + 7) / 8;
+  const bool live = block < nb;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  int count = 0;
+  if (live) {
+    const uint8_t* kb = k8 + (seq * k_stride + block * 8) * CSA2_D_INDEX + quarter * 16;
+    const float* sb = ks + seq * k_stride + block * 8;
+    const int64_t rem = n - block * 8;
+    count = rem < 8 ? (int)rem : 8;
+    for (int j = 0; j < count; ++j) {          // position order
+      uint4 raw = *reinterpret_cast<const uint4*>(kb + j * CSA2_D_INDEX);
+      const float s = sb[j];
+      uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float d = f32_mul(e4m3_value((w[i >> 2] >> (8 * (i & 3))) & 0xFFu), s);
+        acc[i] = f32_add(acc[i], d);
+      }
+    }
+  }
+  float kmax = 0.0f;
+  const float fc = (float)(count > 0 ? count : 1);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[i] = f32_div(acc[i], fc);
+    kmax = fmaxf(kmax, __builtin_fabsf(acc[i]));
+  }
+  kmax = fmaxf(kmax, quad_xor1(kmax));
+  kmax = fmaxf(kmax, quad_xor2(kmax));
+  if (!live) return;
+  const float kss = f32_div(kmax, 448.0f);
+  uint32_t c[4] = {0, 0, 0, 0};
+  if (kss > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i >> 2] |= e4m3_from_f32(f32_div(acc[i], kss)) << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint4*>(bk8 + (seq * bk_stride + block) * CSA2_D_INDEX + quarter * 16) =
+      make_uint4(c[0], c[1], c[2], c[3]);
+  if (quarter == 0) bks[seq * bk_stride + block] = kss;
+}
+
+hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int32_t ratio,
+                           uint8_t* nib, uint8_t* scale, const float* kin, int64_t ld_k,
+                           uint8_t* k8, float* kscale, hipStream_t stream) {
+  if (n_entries == 0) return hipSuccess;
+  const int64_t grid = (n_entries + 7) / 8;
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, stream, x, ld_x, ratio,
+                     n_entries, nib, scale, kin, ld_k, k8, kscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_keys(const uint8_t* k8, const float* ks, int64_t k_stride,
+                             const int64_t* n_entries, int32_t batch, uint8_t* bk8, float* bks,
+                             int64_t bk_stride, hipStream_t stream) {
+  for (int32_t s0 = 0; s0 < batch; s0 += kMaxSeqPerLaunch) {
+    const int32_t nb = batch - s0 < kMaxSeqPerLaunch ? batch - s0 : kMaxSeqPerLaunch;
+    SeqArgs sa = {};
+    int64_t max_blocks = 0;
+    for (int32_t i = 0; i < nb; ++i) {
+      sa.a[i] = n_entries[s0 + i];
+      const int64_t b = (n_entries[s0 + i] + 7) / 8;
+      max_blocks = b > max_blocks ? b : max_blocks;
+    }
+    if (max_blocks == 0) continue;
+    dim3 grid((unsigned)((max_blocks + 63) / 64), (unsigned)nb);
+    hipLaunchKernelGGL(k_block_keys, grid, dim3(256), 0, stream, k8 + s0 * k_stride * CSA2_D_INDEX,
+                       ks + s0 * k_stride, k_stride, sa, bk8 + s0 * bk_stride * CSA2_D_INDEX,
+                       bks + s0 * bk_stride, bk_stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace csa2
