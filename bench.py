@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 decode step with an FP4 KV cache on one MI355X.
+
+Workload (the 128K-context decode group): 16 sequences, 131,072 cache
+entries each (ratio 1), one decoder group of 4 layers run twice on its state:
+Full + 3 Reuse, then Reindex + 3 Reuse.  One step = both runs, so every
+sequence sends one query token through each of the two groups: 32
+query-tokens per step.  Inputs are seeded synthetic tensors resident in HBM;
+the FP4 / fp8 caches are encoded before timing.
+
+To keep the 256 MB Infinity Cache from serving the 143 MB indexer-key scan,
+the step rotates over `--copies` independent copies of the caches (each with
+its own group state): the Full run of step i uses copy 2i mod C, the Reindex
+run copy 2i+1 mod C, whose state holds its own earlier Full layer.
+
+Printed: one JSON line with throughput, the roofline of the dominant kernel
+(the indexer scan: 68 algorithmic bytes per scanned key) timed with HIP
+events on its stream during the timed loop, and the CPU oracle's throughput
+on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+KEY_BYTES = 64 + 4         # fp8 indexer key + float32 scale
+ENTRY_BYTES = 256 + 32     # packed E2M1 + E4M3 scales
+ROW_BYTES = 512 * 2        # bf16 window row
+Q_BYTES, OUT_BYTES, IDX_BYTES, IDXQ_BYTES = 16 * 512 * 2, 16 * 512 * 4, 512 * 4, 4 * 64 + 4 * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--ctx", type=int, default=131072)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes_per_qtok(ctx):
+    """Bytes one query token must move through one 4-layer group: the key
+    scan of the Full/Reindex layer, and per layer the 512 gathered entries,
+    the 128 window rows, its query and output, the index list."""
+    per_layer = 512 * ENTRY_BYTES + 128 * ROW_BYTES + Q_BYTES + OUT_BYTES + IDX_BYTES
+    return ctx * KEY_BYTES + IDXQ_BYTES + 4 * per_layer
+
+
+def cpu_baseline(x0, k0, layers_host, ctx, seconds):
+    """The oracle, as it stands, on sequence 0 of the first cache copy: both
+    group runs per iteration (2 query-tokens), repeated for ~`seconds`."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    nib, sc, k8, ks = oracle.quantize_kv(x0, 1, k0)          # setup, untimed
+    kv = dict(nib=[nib], scale=[sc], k8=[k8], ks=[ks])
+    runs = []
+    for run in range(2):
+        ls = []
+        for j, L in enumerate(layers_host[run]):
+            d = dict(mode=L["mode"], q=L["q"][:1], swa=L["swa"][:1])
+            if "idx_q" in L:
+                d["idx_q"], d["idx_w"] = L["idx_q"][:1], None
+            if L["mode"] == oracle.FULL:
+                d["kv"] = kv
+            ls.append(d)
+        runs.append(ls)
+    st = oracle.new_state()
+    iters, t0 = 0, time.perf_counter()
+    while True:
+        for ls in runs:
+            oracle.run_group(ls, st, [ctx - 1], [ctx], [ctx - 128])
+        iters += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": 2 * iters / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"sequence 0 of the batch, both group runs (F+3U, R+3U) = 2 query-tokens per "
+                      f"iteration, {iters} iterations in {el:.1f} s; cache encoding excluded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(sequences are independent: a multi-GPU run would shard them by rank).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import csa2_inputs as gen
+    import sparse_attention_decode_fp4_amd as csa2
+
+    dev = "cuda"
+    B, ctx, C = args.batch, args.ctx, args.copies
+    seed = 1002
+    # ---- caches: C copies, each its own draw
+    kvs, keep = [], []
+    for c in range(C):
+        nib = torch.empty((B * ctx, 256), dtype=torch.uint8, device=dev)
+        sc = torch.empty((B * ctx, 32), dtype=torch.uint8, device=dev)
+        k8 = torch.empty((B * ctx, 64), dtype=torch.uint8, device=dev)
+        ks = torch.empty((B * ctx,), dtype=torch.float32, device=dev)
+        for b in range(B):
+            x = gen.latent(ctx, seed + 100 * c, seq=b, device=dev)
+            k = gen.index_key(ctx, seed + 100 * c, seq=b, device=dev)
+            sl = slice(b * ctx, (b + 1) * ctx)
+            csa2.csa2_quantize_kv(x, k_in=k, out=[nib[sl], sc[sl], k8[sl], ks[sl]])
+            del x, k
+        kvs.append(csa2.make_kv(nib, sc, k8, ks, ctx))
+        keep.append((nib, sc, k8, ks))
+    torch.cuda.synchronize()
+    # ---- per-layer inputs of the two runs (shared by the copies)
+    q_pos0, n_entries, swa_pos0 = [ctx - 1] * B, [ctx] * B, [ctx - 128] * B
+    plans = [["F", "U", "U", "U"], ["R", "U", "U", "U"]]
+    mode_of = {"F": csa2.MODE_FULL, "R": csa2.MODE_REINDEX, "U": csa2.MODE_REUSE}
+    layers = []
+    for run, plan in enumerate(plans):
+        ls = []
+        for j, m in enumerate(plan):
+            li = 4 * run + j
+            d = dict(mode=mode_of[m], q=gen.attn_query((B, 1), seed, li, device=dev),
+                     swa=gen.window_rows(B, 128, seed, li, device=dev),
+                     out=torch.empty((B, 1, 16, 512), dtype=torch.float32, device=dev))
+            if m in "FR":
+                d["idx_q"] = gen.index_query((B, 1), seed, li, device=dev)
+            ls.append(d)
+        layers.append(ls)
+    ws = csa2.Workspace(B, 1, ctx)
+    states = [csa2.State(B, 1) for _ in range(C)]
+
+    def run_full(c):
+        ls = [dict(L) for L in layers[0]]
+        ls[0]["kv"] = kvs[c]
+        csa2.csa2_run_group(ws, states[c], ls, q_pos0, n_entries, swa_pos0)
+
+    def run_reindex(c):
+        csa2.csa2_run_group(ws, states[c], layers[1], q_pos0, n_entries, swa_pos0)
+
+    def step(i):
+        run_full((2 * i) % C)
+        run_reindex((2 * i + 1) % C)
+
+    for c in range(C):  # every state gets its own Full layer first
+        run_full(c)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed loop (eager), with the library's HIP-event kernel timing on
+    csa2.csa2_profile_reset()
+    csa2.csa2_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t0
+    csa2.csa2_profile_enable(False)
+    kern = {}
+    for kid, name in enumerate(csa2.KERNEL_NAMES):
+        ms, n = csa2.csa2_profile_read(kid)
+        if n:
+            kern[name] = {"avg_us": round(1000.0 * ms / n, 3), "launches_per_step": n / args.steps}
+    scan_ms, scan_n = csa2.csa2_profile_read(csa2.K_INDEX_SCAN)
+    csa2.csa2_profile_reset()
+
+    # ---- timed loop replaying captured graphs (one per pair of copies)
+    graph_s = None
+    if not args.no_graph:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for g_i in range(C // 2):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    step(g_i)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(s)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        graph_s = time.perf_counter() - t0
+
+    best_s = min(eager_s, graph_s) if graph_s is not None else eager_s
+    qtok_per_step = 2 * B
+    value = qtok_per_step * args.steps / best_s
+    step_bytes = 2 * B * algorithmic_bytes_per_qtok(ctx)
+    scan_bytes = B * ctx * KEY_BYTES                       # one launch scans every sequence once
+    scan_avg_s = scan_ms / 1000.0 / scan_n
+    achieved = scan_bytes / scan_avg_s / 1e9
+    line = {
+        "metric": "CSA2 decode query-tokens/s at 128K ctx; % of peak HBM GB/s",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * best_s / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode group of 4 layers run as Full+3 Reuse then Reindex+3 Reuse, "
+                               f"batch {B}, {ctx} FP4 entries per sequence, top-512 + 128-token window",
+                   "batch": B, "ctx": ctx, "layers_per_step": 8, "query_tokens_per_step": qtok_per_step,
+                   "cache_copies": C, "timing": "graph replay" if best_s == graph_s else "eager"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_index_scan", "bytes_per_launch": scan_bytes,
+                     "avg_launch_us": round(scan_avg_s * 1e6, 3)},
+        "step_hbm": {"algorithmic_bytes": step_bytes,
+                     "achieved_GBs": round(step_bytes * args.steps / best_s / 1e9, 1),
+                     "frac": round(step_bytes * args.steps / best_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "eager_ms_per_step": round(1000.0 * eager_s / args.steps, 4),
+        "graph_ms_per_step": None if graph_s is None else round(1000.0 * graph_s / args.steps, 4),
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        x0 = gen.latent(ctx, seed, seq=0, device=dev).cpu().numpy()
+        k0 = gen.index_key(ctx, seed, seq=0, device=dev).cpu().numpy()
+        host_layers = []
+        for run in range(2):
+            hl = []
+            for L in layers[run]:
+                h = dict(mode=L["mode"], q=gen.bf16_bits(L["q"]), swa=gen.bf16_bits(L["swa"]))
+                if "idx_q" in L:
+                    h["idx_q"] = L["idx_q"].cpu().numpy()
+                hl.append(h)
+            host_layers.append(hl)
+        line["cpu_baseline"] = cpu_baseline(x0, k0, host_layers, ctx, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -306,6 +306,27 @@ size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entr
  */
 int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Optional kernel timing, for measurement tools (the pages say nothing about
+ * it).  While enabled, each kernel the library launches is bracketed by two
+ * HIP events recorded on the launch's own stream; csa2_profile_read waits for
+ * the recorded events of one kernel class and returns their summed elapsed
+ * milliseconds and count.  Process-wide; do not enable while a stream is
+ * being captured into a graph.  Returns CSA2_ERR_ARG for null outputs and
+ * CSA2_ERR_HIP if an event cannot be read.
+ */
+#define CSA2_K_QUANTIZE 0
+#define CSA2_K_BLOCK_KEYS 1
+#define CSA2_K_INDEX_SCAN 2
+#define CSA2_K_INDEX_FILTER 3
+#define CSA2_K_INDEX_SELECT 4
+#define CSA2_K_ATTENTION 5
+#define CSA2_K_PREFILL_INDEX 6
+#define CSA2_K_ATTENTION_MERGE 7
+int csa2_profile_enable(int32_t on);
+int csa2_profile_reset(void);
+int csa2_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,10 @@ TOP_K, SWA, BLOCK, N_BLOCKS, MAX_K = 512, 128, 8, 2048, 2048
 INDEX_FLAT, INDEX_HIER, INDEX_POOL = 0, 1, 2
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_STATE, ERR_WORKSPACE, ERR_HIP = range(6)
+(K_QUANTIZE, K_BLOCK_KEYS, K_INDEX_SCAN, K_INDEX_FILTER, K_INDEX_SELECT, K_ATTENTION,
+ K_PREFILL_INDEX, K_ATTENTION_MERGE) = range(8)
+KERNEL_NAMES = ["quantize", "block_keys", "index_scan", "index_filter", "index_select", "attention",
+                "prefill_index", "attention_merge"]
 ABI_VERSION = 1
 
 _p = ctypes.c_void_p
@@ -94,6 +98,9 @@ def _load():
         "csa2_sparse_swa_attn": (_i32, [ctypes.POINTER(AttnArgs), _p, ctypes.c_size_t, _p]),
         "csa2_run_group": (_i32, [ctypes.POINTER(GroupArgs), ctypes.POINTER(GroupState), _p,
                                   ctypes.c_size_t, _p]),
+        "csa2_profile_enable": (_i32, [_i32]),
+        "csa2_profile_reset": (_i32, []),
+        "csa2_profile_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -321,6 +328,22 @@ def csa2_run_group(ws, state, layers, q_pos0, n_entries, swa_pos0, *, ratio=1,
     if any(L["mode"] == MODE_FULL for L in layers):
         state._keep = [kv for kv in keep if isinstance(kv, KV)]
     return outs
+
+
+# --------------------------------------------------------------------- timing
+def csa2_profile_enable(on=True):
+    _check(lib.csa2_profile_enable(1 if on else 0))
+
+
+def csa2_profile_reset():
+    _check(lib.csa2_profile_reset())
+
+
+def csa2_profile_read(kernel):
+    """(total milliseconds, launches) of the recorded launches of one kernel class."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib.csa2_profile_read(int(kernel), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 __all__ = [n for n in dir() if n.startswith("csa2_")] + ["Workspace", "State", "make_kv", "Csa2Error"]

@@ -36,7 +36,7 @@ constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of atte
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t hist, scores, cand, fcount, blocks, nsel, partial, counter, total;
+  size_t hist, scores, cand, fcount, blocks, nsel, partial, total;
   int64_t stride;  // items per row in scores / cand
 };
 
@@ -52,7 +52,6 @@ WsLayout ws_layout(int64_t rows, int64_t max_items) {
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
   w.nsel = take((size_t)rows * 4);
   w.partial = take((size_t)kMaxPartialUnits * kH * (kD + 4) * 4);
-  w.counter = take((size_t)kMaxAttnLayers * std::max<int64_t>(rows, 1) * 4);
   w.total = off;
   return w;
 }
@@ -256,7 +255,6 @@ int run_attention(const AttnJob& j, void* ws, const WsLayout& w, hipStream_t str
     p.tiles_per_split = (n_tiles + splits - 1) / splits;
     p.max_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
     p.partial = at<float>(ws, w.partial);
-    p.counter = at<uint32_t>(ws, w.counter);
     hipError_t e = launch_attention(p, stream);
     if (e != hipSuccess) return hip_fail(e, "attention");
   }

@@ -14,7 +14,7 @@
 // E2M1 x E4M3 products are exact in bf16, so only P is rounded: it is split
 // into bf16 hi + lo parts (relative error ~2^-16).  A workgroup walks
 // `tiles_per_split` tiles with an online softmax.  When a (layer, row) is
-// split over several workgroups, the last one to finish merges the partial
+// split over several workgroups, a second kernel merges the partial
 // softmaxes in split order, so results do not depend on scheduling.
 #include "kernels.hpp"
 
@@ -136,7 +136,6 @@ __global__ __launch_bounds__(256) void k_attention(AttnPass p) {
   __shared__ __attribute__((aligned(16))) uint16_t Plo[kH * kPStride];
   __shared__ float red[4][kH];
   __shared__ uint8_t row_ok[kAttnSplit];
-  __shared__ uint32_t last_flag;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -260,51 +259,68 @@ __global__ __launch_bounds__(256) void k_attention(AttnPass p) {
     part[l16 * kPartStride + kD] = m_run;
     part[l16 * kPartStride + kD + 1] = l_run;
   }
+}
 
-  // the last workgroup of this (layer, row) merges the partials in split order
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(p.counter + unit, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (old == (uint32_t)p.max_splits - 1u) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  const int h = t >> 4, c0 = (t & 15) * 32;
+// Merge of the split partial softmaxes, in split order.  A kernel of its own:
+// the kernel boundary orders the partial writes before these reads on every
+// XCD, which in-kernel device-scope fences would do by writing back the whole
+// L2.  Workgroup (unit, quarter): 4 heads x 512 channels, 16 per thread.
+__global__ __launch_bounds__(128) void k_attention_merge(AttnPass p) {
+  const int unit = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const int layer = unit / p.rows, row = unit - layer * p.rows;
+  const int t = threadIdx.x;
+  const int h = 4 * quarter + (t >> 5), c0 = (t & 31) * 16;
   const float* pb = p.partial + ((int64_t)unit * p.max_splits * kH) * kPartStride;
   float M = -INFINITY;
   for (int s = 0; s < p.max_splits; ++s) M = fmaxf(M, pb[(s * kH + h) * kPartStride + kD]);
-  float acc_o[32];
+  float acc_o[16];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) acc_o[j] = 0.0f;
+  for (int j = 0; j < 16; ++j) acc_o[j] = 0.0f;
   float lsum = 0.0f;
-  for (int s = 0; s < p.max_splits; ++s) {
-    const float* ps = pb + (s * kH + h) * kPartStride;
-    const float ms = ps[kD];
-    const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-    lsum += wgt * ps[kD + 1];
+  // four splits per step: their loads are issued together
+  for (int s0 = 0; s0 < p.max_splits; s0 += 4) {
+    float4 v[4][4];
+    float ms[4], ls[4];
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(ps + c0 + j);
-      acc_o[j] += wgt * v.x; acc_o[j + 1] += wgt * v.y; acc_o[j + 2] += wgt * v.z; acc_o[j + 3] += wgt * v.w;
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u < p.max_splits ? s0 + u : p.max_splits - 1;
+      const float* ps = pb + (s * kH + h) * kPartStride;
+      ms[u] = s0 + u < p.max_splits ? ps[kD] : -INFINITY;
+      ls[u] = ps[kD + 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[u][j] = *reinterpret_cast<const float4*>(ps + c0 + 4 * j);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = (ms[u] == -INFINITY) ? 0.0f : exp2f(ms[u] - M);
+      lsum += wgt * ls[u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc_o[4 * j] += wgt * v[u][j].x; acc_o[4 * j + 1] += wgt * v[u][j].y;
+        acc_o[4 * j + 2] += wgt * v[u][j].z; acc_o[4 * j + 3] += wgt * v[u][j].w;
+      }
     }
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-  float* dsto = L.out + ((int64_t)row * kH + h) * kD + c0;
+  float* dsto = p.layer[layer].out + ((int64_t)row * kH + h) * kD + c0;
 #pragma unroll
-  for (int j = 0; j < 32; j += 4)
+  for (int j = 0; j < 16; j += 4)
     *reinterpret_cast<float4*>(dsto + j) =
         make_float4(acc_o[j] * inv, acc_o[j + 1] * inv, acc_o[j + 2] * inv, acc_o[j + 3] * inv);
-  if (t == 0) p.counter[unit] = 0u;  // ready for the next call
 }
 
 hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   const int units = p.n_layers * p.rows;
   if (units == 0) return hipSuccess;
   const int gu = (units >= kXcds && p.max_splits > 1) ? (units + kXcds - 1) / kXcds * kXcds : units;
+  int h = prof_begin(CSA2_K_ATTENTION, stream);
   hipLaunchKernelGGL(k_attention, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
+  prof_end(h, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_splits == 1) return e;
+  h = prof_begin(CSA2_K_ATTENTION_MERGE, stream);
+  hipLaunchKernelGGL(k_attention_merge, dim3((unsigned)(4 * units)), dim3(128), 0, stream, p);
+  prof_end(h, stream);
   return hipGetLastError();
 }
 

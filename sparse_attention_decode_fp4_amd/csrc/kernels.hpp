@@ -57,6 +57,10 @@ struct IndexPass {
   int32_t pool_stride;
 };
 
+// Kernel classes of the optional timing records (csa2_profile_*).
+int prof_begin(int32_t kernel, hipStream_t stream);
+void prof_end(int handle, hipStream_t stream);
+
 hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int32_t ratio,
                            uint8_t* nib, uint8_t* scale, const float* kin, int64_t ld_k,
                            uint8_t* k8, float* kscale, hipStream_t stream);
@@ -90,7 +94,6 @@ struct AttnPass {
   int32_t max_splits;           // ceil(n_tiles / tiles_per_split)
   // workspace (used when max_splits > 1)
   float* partial;               // [n_layers*rows][max_splits][16][516]
-  uint32_t* counter;            // [n_layers*rows], zero on entry, zero on exit
 };
 hipError_t launch_attention(const AttnPass& p, hipStream_t stream);
 

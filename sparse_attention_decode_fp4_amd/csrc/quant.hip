@@ -146,8 +146,10 @@ hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int3
                            uint8_t* k8, float* kscale, hipStream_t stream) {
   if (n_entries == 0) return hipSuccess;
   const int64_t grid = (n_entries + 7) / 8;
+  const int h = prof_begin(CSA2_K_QUANTIZE, stream);
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, stream, x, ld_x, ratio,
                      n_entries, nib, scale, kin, ld_k, k8, kscale);
+  prof_end(h, stream);
   return hipGetLastError();
 }
 
@@ -165,9 +167,11 @@ hipError_t launch_block_keys(const uint8_t* k8, const float* ks, int64_t k_strid
     }
     if (max_blocks == 0) continue;
     dim3 grid((unsigned)((max_blocks + 63) / 64), (unsigned)nb);
+    const int h = prof_begin(CSA2_K_BLOCK_KEYS, stream);
     hipLaunchKernelGGL(k_block_keys, grid, dim3(256), 0, stream, k8 + s0 * k_stride * CSA2_D_INDEX,
                        ks + s0 * k_stride, k_stride, sa, bk8 + s0 * bk_stride * CSA2_D_INDEX,
                        bks + s0 * bk_stride, bk_stride);
+    prof_end(h, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
