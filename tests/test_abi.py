@@ -1,0 +1,140 @@
+"""CPU tests of the C ABI: the library loads, exports every function the
+header declares, its struct layouts match the binding, and every validation
+error is reported before anything is enqueued (no GPU is touched: each call
+below fails validation, which runs before the first HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import sparse_attention_decode_fp4_amd as mod
+    return mod
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(m):
+    names = _declared()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_struct_layouts(m):
+    assert m.lib.csa2_abi_version() == m.ABI_VERSION
+    for i, st in enumerate(m._STRUCTS):
+        assert m.lib.csa2_struct_size(i) == ctypes.sizeof(st)
+    assert m.lib.csa2_struct_size(99) == 0
+
+
+def test_workspace_sizes(m):
+    assert m.lib.csa2_workspace_bytes(0, 1, 10) == 0
+    small = m.lib.csa2_workspace_bytes(1, 1, 4096)
+    big = m.lib.csa2_workspace_bytes(16, 1, 131072)
+    assert 0 < small < big
+    assert m.lib.csa2_workspace_init(None, 1024, None) == m.ERR_WORKSPACE
+    assert m.lib.csa2_workspace_init(ctypes.c_void_p(0x1001), 1024, None) == m.ERR_WORKSPACE
+
+
+FAKE = 0x10000000  # aligned, never dereferenced: every call here fails validation first
+
+
+def _p(off=0):
+    return ctypes.c_void_p(FAKE + off)
+
+
+def test_quantize_errors(m):
+    q = m.lib.csa2_quantize_kv
+    assert q(_p(), 4, 512, 3, _p(), _p(), None, 0, None, None, None) == m.ERR_ARG       # ratio
+    assert q(_p(), 3, 512, 2, _p(), _p(), None, 0, None, None, None) == m.ERR_ARG       # odd tokens
+    assert q(_p(), 4, 500, 1, _p(), _p(), None, 0, None, None, None) == m.ERR_ARG       # ld < 512
+    assert q(_p(4), 4, 512, 1, _p(), _p(), None, 0, None, None, None) == m.ERR_ARG      # misaligned x
+    assert q(None, 4, 512, 1, _p(), _p(), None, 0, None, None, None) == m.ERR_ARG       # null x
+    assert q(_p(), 4, 512, 1, _p(), _p(), _p(), 64, None, None, None) == m.ERR_ARG      # k_in without k8
+    assert q(None, 0, 512, 1, None, None, None, 0, None, None, None) == m.OK            # empty: nothing to do
+    q(_p(), 4, 512, 5, _p(), _p(), None, 0, None, None, None)
+    assert b"ratio" in m.lib.csa2_last_error()
+
+
+def _index_args(m, **kw):
+    a = m.IndexArgs()
+    qp = (ctypes.c_int64 * 2)(99, 99)
+    ne = (ctypes.c_int64 * 2)(100, 100)
+    a.kind, a.batch, a.n_q, a.ratio = m.INDEX_FLAT, 2, 1, 1
+    a.q_pos0, a.n_entries = ctypes.cast(qp, ctypes.c_void_p), ctypes.cast(ne, ctypes.c_void_p)
+    a.idx_q, a.k8, a.kscale, a.k_stride = _p(), _p(), _p(), 100
+    a.k, a.n_blocks, a.out_idx = 512, 2048, _p()
+    for k, v in kw.items():
+        setattr(a, k, v)
+    a._keep = (qp, ne)
+    return a
+
+
+def test_index_errors(m):
+    f = m.lib.csa2_index_topk
+    assert f(None, _p(), 1 << 30, None) == m.ERR_ARG
+    assert f(ctypes.byref(_index_args(m, kind=7)), _p(), 1 << 30, None) == m.ERR_ARG
+    assert f(ctypes.byref(_index_args(m, k=0)), _p(), 1 << 30, None) == m.ERR_UNSUPPORTED
+    assert f(ctypes.byref(_index_args(m, k=4096)), _p(), 1 << 30, None) == m.ERR_UNSUPPORTED
+    assert f(ctypes.byref(_index_args(m, ratio=3)), _p(), 1 << 30, None) == m.ERR_ARG
+    assert f(ctypes.byref(_index_args(m, k_stride=50)), _p(), 1 << 30, None) == m.ERR_ARG
+    assert f(ctypes.byref(_index_args(m, idx_q=_p(8))), _p(), 1 << 30, None) == m.ERR_ARG
+    assert f(ctypes.byref(_index_args(m, kind=m.INDEX_HIER)), _p(), 1 << 30, None) == m.ERR_ARG
+    assert f(ctypes.byref(_index_args(m, kind=m.INDEX_POOL)), _p(), 1 << 30, None) == m.ERR_ARG
+    assert f(ctypes.byref(_index_args(m)), None, 0, None) == m.ERR_WORKSPACE
+    assert f(ctypes.byref(_index_args(m)), _p(), 1024, None) == m.ERR_WORKSPACE
+    assert f(ctypes.byref(_index_args(m)), _p(16), 1 << 30, None) == m.ERR_WORKSPACE
+
+
+def test_attention_errors(m):
+    f = m.lib.csa2_sparse_swa_attn
+    a = m.AttnArgs()
+    qp = (ctypes.c_int64 * 1)(300)
+    sp = (ctypes.c_int64 * 1)(250)          # window of token 300 starts at 173: rows missing
+    a.batch, a.n_q, a.n_idx = 1, 1, 512
+    a.q_pos0, a.swa_pos0 = ctypes.cast(qp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p)
+    a.q, a.nib, a.scale, a.idx, a.swa, a.out = _p(), _p(), _p(), _p(), _p(), _p()
+    a.swa_rows, a.swa_stride, a.kv_stride = 128, 128, 1000
+    assert f(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_ARG
+    assert b"window" in m.lib.csa2_last_error()
+    sp[0] = 173
+    a.n_idx = 4096
+    assert f(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_UNSUPPORTED
+    a.n_idx = 512
+    a.q = _p(2)
+    assert f(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_ARG
+
+
+def test_group_state_errors(m):
+    st = m.GroupState()
+    st.indices = _p()
+    layer = (m.Layer * 1)()
+    layer[0].mode, layer[0].q, layer[0].swa, layer[0].out = m.MODE_REUSE, _p(), _p(), _p()
+    g = m.GroupArgs()
+    qp, ne, sp = (ctypes.c_int64 * 1)(999), (ctypes.c_int64 * 1)(1000), (ctypes.c_int64 * 1)(872)
+    g.batch, g.n_q, g.ratio = 1, 1, 1
+    g.q_pos0, g.n_entries, g.swa_pos0 = (ctypes.cast(x, ctypes.c_void_p) for x in (qp, ne, sp))
+    g.swa_stride, g.swa_rows, g.softmax_scale, g.n_layers, g.layers = 128, 128, 1.0, 1, layer
+    f = m.lib.csa2_run_group
+    assert f(ctypes.byref(g), ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_STATE
+    layer[0].mode = m.MODE_REINDEX
+    layer[0].idx_q = _p()
+    assert f(ctypes.byref(g), ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_STATE
+    layer[0].mode = m.MODE_FULL          # FULL without kv
+    assert f(ctypes.byref(g), ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_ARG
+    st.has_full, st.has_indices, st.batch, st.n_q = 1, 1, 2, 1   # state of another batch size
+    layer[0].mode = m.MODE_REUSE
+    assert f(ctypes.byref(g), ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_STATE
+    assert f(None, ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_ARG
