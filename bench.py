@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                    help="decode: the 128K decode group (default, the headline); prefill: a 4,096-token "
+                         "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers")
     return ap.parse_args()
 
 
@@ -94,12 +97,100 @@ def cpu_baseline(x0, k0, layers_host, ctx, seconds):
                       f"iteration, {iters} iterations in {el:.1f} s; cache encoding excluded"}
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8, published
+
+
+def prefill(args):
+    """The prefill chunk step: encode the chunk's 4,096 tokens into 2,048
+    entries (ratio-2 pair mean), index every query row on fp8 MFMA, and run
+    the 1 Full + 5 Reuse attention layers over 4,096 query rows."""
+    import torch
+
+    import csa2_inputs as gen
+    import sparse_attention_decode_fp4_amd as csa2
+
+    dev = "cuda"
+    c = gen.CONFIGS[4]
+    P, T = c["prefix_tokens"], c["chunk"]
+    seed = 1004
+    n_prefix, n_ent = P // 2, (P + T) // 2
+    nib = torch.empty((n_ent, 256), dtype=torch.uint8, device=dev)
+    sc = torch.empty((n_ent, 32), dtype=torch.uint8, device=dev)
+    k8 = torch.empty((n_ent, 64), dtype=torch.uint8, device=dev)
+    ks = torch.empty((n_ent,), dtype=torch.float32, device=dev)
+    x = gen.latent(P + T, seed, device=dev)
+    kin = gen.index_key(P + T, seed, device=dev)
+    csa2.csa2_quantize_kv(x[:P], ratio=2, k_in=kin[:P],
+                          out=[nib[:n_prefix], sc[:n_prefix], k8[:n_prefix], ks[:n_prefix]])
+    xc, kc = x[P:].contiguous(), kin[P:].contiguous()
+    del x, kin
+    kv = csa2.make_kv(nib, sc, k8, ks, n_ent)
+    swa_pos0 = P - 127
+    layers = []
+    for j, m in enumerate(c["plans"][0]):
+        d = dict(mode=csa2.MODE_FULL if m == "F" else csa2.MODE_REUSE,
+                 q=gen.attn_query((1, T), seed, j, device=dev),
+                 swa=gen.window_rows(1, P + T - swa_pos0, seed, j, device=dev),
+                 out=torch.empty((1, T, 16, 512), dtype=torch.float32, device=dev))
+        if m == "F":
+            d["idx_q"], d["kv"] = gen.index_query((1, T), seed, j, device=dev), kv
+        layers.append(d)
+    ws = csa2.Workspace(1, T, n_ent)
+    st = csa2.State(1, T)
+    chunk_out = [nib[n_prefix:], sc[n_prefix:], k8[n_prefix:], ks[n_prefix:]]
+
+    def step():
+        csa2.csa2_quantize_kv(xc, ratio=2, k_in=kc, out=chunk_out)
+        csa2.csa2_run_group(ws, st, layers, [P], [n_ent], [swa_pos0], ratio=2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    csa2.csa2_profile_reset()
+    csa2.csa2_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    csa2.csa2_profile_enable(False)
+    kern = {}
+    for kid, name in enumerate(csa2.KERNEL_NAMES):
+        ms, n = csa2.csa2_profile_read(kid)
+        if n:
+            kern[name] = {"avg_us": round(1000.0 * ms / n, 3), "launches_per_step": n / args.steps}
+    fms, fn = csa2.csa2_profile_read(csa2.K_PREFILL_FILTER)
+    # visible (query, entry) pairs: query i at token P + i sees (P + i + 1) // 2 entries
+    pairs = sum((P + i + 1) // 2 for i in range(T))
+    flops = 2 * pairs * 4 * 64
+    filt_s = fms / 1000.0 / fn
+    achieved = flops / filt_s / 1e12
+    line = {
+        "metric": "CSA2 prefill chunk query-tokens/s (4,096-token chunk, 262,144-token prefix)",
+        "value": round(T * args.steps / el, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1000.0 * el / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "prefill chunk: 4,096 query tokens at ratio 2 on a 262,144-token prefix, "
+                               "1 Full + 5 Reuse layers, top-512 + 128-token window",
+                   "prefix_tokens": P, "chunk": T, "entries": n_ent, "layers": 6, "timing": "eager"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_prefill_mfma (filter pass)", "flops_per_launch": flops,
+                     "avg_launch_us": round(filt_s * 1e6, 3)},
+        "kernels": kern,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(sequences are independent: a multi-GPU run would shard them by rank).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "prefill":
+        prefill(args)
+        return
     import torch
 
     import csa2_inputs as gen

@@ -165,7 +165,10 @@ int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
  * FLAT scores every visible entry.  HIER scores the visible blocks (block
  * keys), keeps the top n_blocks blocks, and scores the visible positions of
  * those blocks; out_pool (optional) receives the kept positions in ascending
- * order, -1 padded.  POOL scores only the positions in cand.
+ * order, -1 padded.  POOL scores only the positions in cand, which must be
+ * ascending with any -1 padding at the end.  With n_q >= 32 (a prefill
+ * chunk) FLAT scoring runs on fp8 MFMA; HIER and POOL then return
+ * CSA2_ERR_UNSUPPORTED.
  */
 typedef struct csa2_index_args {
   int32_t kind;              /* CSA2_INDEX_*                                          */
@@ -321,8 +324,10 @@ int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 #define CSA2_K_INDEX_FILTER 3
 #define CSA2_K_INDEX_SELECT 4
 #define CSA2_K_ATTENTION 5
-#define CSA2_K_PREFILL_INDEX 6
+#define CSA2_K_PREFILL_SAMPLE 6
 #define CSA2_K_ATTENTION_MERGE 7
+#define CSA2_K_PREFILL_FILTER 8
+#define CSA2_K_PREFILL_SELECT 9
 int csa2_profile_enable(int32_t on);
 int csa2_profile_reset(void);
 int csa2_profile_read(int32_t kernel, double* total_ms, int64_t* launches);

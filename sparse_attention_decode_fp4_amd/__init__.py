@@ -25,9 +25,9 @@ INDEX_FLAT, INDEX_HIER, INDEX_POOL = 0, 1, 2
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_STATE, ERR_WORKSPACE, ERR_HIP = range(6)
 (K_QUANTIZE, K_BLOCK_KEYS, K_INDEX_SCAN, K_INDEX_FILTER, K_INDEX_SELECT, K_ATTENTION,
- K_PREFILL_INDEX, K_ATTENTION_MERGE) = range(8)
+ K_PREFILL_SAMPLE, K_ATTENTION_MERGE, K_PREFILL_FILTER, K_PREFILL_SELECT) = range(10)
 KERNEL_NAMES = ["quantize", "block_keys", "index_scan", "index_filter", "index_select", "attention",
-                "prefill_index", "attention_merge"]
+                "prefill_sample", "attention_merge", "prefill_filter", "prefill_select"]
 ABI_VERSION = 1
 
 _p = ctypes.c_void_p

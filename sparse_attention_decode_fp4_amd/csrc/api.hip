@@ -36,11 +36,14 @@ constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of atte
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t hist, scores, cand, fcount, blocks, nsel, partial, total;
+  size_t hist, scores, cand, fcount, blocks, nsel, partial;
+  size_t pf_sample, pf_thresh, pf_count, pf_list, total;
   int64_t stride;  // items per row in scores / cand
 };
 
-WsLayout ws_layout(int64_t rows, int64_t max_items) {
+// Decode-path buffers cover `rows` query rows of up to `max_items` items;
+// prefill-path buffers cover `pf_rows` query rows (0 when unused).
+WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   WsLayout w{};
   w.stride = (int64_t)round_up((size_t)std::max<int64_t>(max_items, 1), kFilterChunk);
   size_t off = 0;
@@ -52,8 +55,20 @@ WsLayout ws_layout(int64_t rows, int64_t max_items) {
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
   w.nsel = take((size_t)rows * 4);
   w.partial = take((size_t)kMaxPartialUnits * kH * (kD + 4) * 4);
+  w.pf_sample = take((size_t)pf_rows * kPfSample * 4);
+  w.pf_thresh = take((size_t)pf_rows * 4);
+  w.pf_count = take((size_t)pf_rows * kPfSplits * 4);
+  w.pf_list = take((size_t)pf_rows * kPfSplits * kPfSeg * 8);
   w.total = off;
   return w;
+}
+
+// Layout for calls of `batch` sequences x `n_q` queries: prefill-sized calls
+// use the MFMA indexer and need no per-item decode buffers.
+WsLayout ws_for(int32_t batch, int32_t n_q, int64_t max_items) {
+  const int64_t seqs = std::min(batch, kMaxSeqPerLaunch);
+  if (n_q >= kPrefillMinQ) return ws_layout(0, 0, seqs * n_q);
+  return ws_layout(seqs * n_q, max_items, 0);
 }
 
 template <typename T>
@@ -100,6 +115,8 @@ int validate_index(const csa2_index_args* a) {
     if (a->batch > 1 && a->bk_stride < (max_ne + 7) / 8) return fail(CSA2_ERR_ARG, "bk_stride smaller than the block count");
     if (a->out_pool && !aligned(a->out_pool, 4)) return fail(CSA2_ERR_ARG, "out_pool must be 4-byte aligned");
   }
+  if (a->kind != CSA2_INDEX_FLAT && a->n_q >= kPrefillMinQ)
+    return fail(CSA2_ERR_UNSUPPORTED, "HIER and POOL indexing take fewer than %d queries per sequence", kPrefillMinQ);
   if (a->kind == CSA2_INDEX_POOL) {
     if (!a->cand || !aligned(a->cand, 4)) return fail(CSA2_ERR_ARG, "POOL needs a 4-byte aligned cand");
     if (a->n_cand < 1 || a->n_cand > kMaxPool) return fail(CSA2_ERR_UNSUPPORTED, "n_cand must be in 1..%d", kMaxPool);
@@ -136,6 +153,28 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
         f = launch_fill_u32(reinterpret_cast<uint32_t*>(a->out_pool + row0 * a->n_blocks * CSA2_BLOCK),
                             (size_t)p.rows * a->n_blocks * CSA2_BLOCK, 0xFFFFFFFFu, stream);
       if (f != hipSuccess) return hip_fail(f, "fill");
+      continue;
+    }
+    if (a->n_q >= kPrefillMinQ) {  // prefill chunk: MFMA indexer
+      PrefillPass f{};
+      f.rows = p.rows; f.n_q = a->n_q; f.ratio = a->ratio; f.k = a->k; f.batch = nb;
+      f.tiles_per_seq = (a->n_q + kPfRows - 1) / kPfRows;
+      const int tiles = nb * f.tiles_per_seq;
+      f.esplit = std::max(1, std::min(kPfSplits, (1024 + tiles - 1) / tiles));
+      f.seq = p.seq;
+      f.idx_q = a->idx_q + row0 * kHI * kDI;
+      f.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;
+      f.k8 = a->k8 + (int64_t)s0 * a->k_stride * kDI;
+      f.kscale = a->kscale + (int64_t)s0 * a->k_stride;
+      f.k_stride = a->k_stride;
+      f.sample = at<float>(ws, w.pf_sample);
+      f.thresh = at<float>(ws, w.pf_thresh);
+      f.count = at<uint32_t>(ws, w.pf_count);
+      f.list = at<uint64_t>(ws, w.pf_list);
+      f.out = a->out_idx + row0 * a->k;
+      f.out_stride = a->k;
+      hipError_t e = launch_prefill_index(f, stream);
+      if (e != hipSuccess) return hip_fail(e, "prefill index");
       continue;
     }
     p.idx_q = a->idx_q + row0 * kHI * kDI;
@@ -290,9 +329,11 @@ const char* csa2_last_error(void) { return g_err; }
 
 size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entries) {
   if (max_batch < 1 || max_n_q < 1 || max_entries < 0) return 0;
-  const int64_t rows = std::min<int64_t>(max_batch, kMaxSeqPerLaunch) * max_n_q;
+  const int64_t seqs = std::min<int64_t>(max_batch, kMaxSeqPerLaunch);
   const int64_t items = std::max<int64_t>(max_entries, kMaxPool);
-  return ws_layout(rows, items).total;
+  const int64_t dec_rows = seqs * std::min<int64_t>(max_n_q, kPrefillMinQ - 1);
+  const int64_t pf_rows = max_n_q >= kPrefillMinQ ? seqs * max_n_q : 0;
+  return ws_layout(dec_rows, items, pf_rows).total;
 }
 
 int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
@@ -345,7 +386,7 @@ int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
 int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, void* stream) {
   int rc = validate_index(a);
   if (rc) return rc;
-  const WsLayout w = ws_layout((int64_t)std::min(a->batch, kMaxSeqPerLaunch) * a->n_q, index_max_items(a));
+  const WsLayout w = ws_for(a->batch, a->n_q, index_max_items(a));
   if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
   return run_index(a, workspace, w, (hipStream_t)stream);
 }
@@ -359,7 +400,7 @@ int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_byt
   if (!aligned(a->q, 16) || !aligned(a->swa, 16) || !aligned(a->out, 16) || (a->idx && !aligned(a->idx, 4)))
     return fail(CSA2_ERR_ARG, "q, swa, out must be 16-byte aligned");
   if (a->batch > 1 && a->kv_stride < 0) return fail(CSA2_ERR_ARG, "kv_stride < 0");
-  const WsLayout w = ws_layout((int64_t)std::min(a->batch, kMaxSeqPerLaunch) * a->n_q, 0);
+  const WsLayout w = ws_layout(0, 0, 0);  // attention uses only the partials
   if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
   AttnJob j{};
   j.batch = a->batch; j.n_q = a->n_q; j.n_idx = a->n_idx;
@@ -380,6 +421,8 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
     return fail(CSA2_ERR_ARG, "index_kind must be FLAT or HIER");
   if (a->reindex_kind != CSA2_INDEX_FLAT && a->reindex_kind != CSA2_INDEX_POOL)
     return fail(CSA2_ERR_ARG, "reindex_kind must be FLAT or POOL");
+  if ((a->index_kind != CSA2_INDEX_FLAT || a->reindex_kind != CSA2_INDEX_FLAT) && a->n_q >= kPrefillMinQ)
+    return fail(CSA2_ERR_UNSUPPORTED, "HIER and POOL indexing take fewer than %d queries per sequence", kPrefillMinQ);
   if (!a->n_entries) return fail(CSA2_ERR_ARG, "n_entries (host) is required");
   int rc = validate_attn_common(a->batch, a->n_q, CSA2_TOP_K, a->q_pos0, a->swa_pos0, a->swa_rows, a->swa_stride);
   if (rc) return rc;
@@ -422,8 +465,7 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
       if (L.idx_w && !aligned(L.idx_w, 4)) return fail(CSA2_ERR_ARG, "layer %d: idx_w alignment", l);
     }
   }
-  const int64_t rows = (int64_t)std::min(a->batch, kMaxSeqPerLaunch) * a->n_q;
-  const WsLayout w = ws_layout(rows, std::max<int64_t>(max_ne, kMaxPool));
+  const WsLayout w = ws_for(a->batch, a->n_q, std::max<int64_t>(max_ne, kMaxPool));
   if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
 
   hipStream_t s = (hipStream_t)stream;

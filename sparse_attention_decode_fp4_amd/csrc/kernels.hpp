@@ -97,4 +97,31 @@ struct AttnPass {
 };
 hipError_t launch_attention(const AttnPass& p, hipStream_t stream);
 
+// Prefill chunk indexer (fp8 MFMA): used for FLAT indexing of calls with at
+// least kPrefillMinQ queries per sequence.
+constexpr int kPrefillMinQ = 32;
+constexpr int kPfRows = 256;      // query rows per workgroup
+constexpr int kPfSample = 2048;   // sampled keys per row tile
+constexpr int kPfCap = 4096;      // candidates a row's selection holds in LDS
+constexpr int kPfSplits = 64;     // key ranges (filter workgroups) per row tile, at most
+constexpr int kPfSeg = 128;       // candidates kept per (row, key range)
+struct PrefillPass {
+  int32_t rows, n_q, ratio, k, batch;
+  int32_t tiles_per_seq, esplit;
+  SeqArgs seq;                   // a = q_pos0, b = n_entries
+  const uint8_t* idx_q;          // [rows][4][64]
+  const float* idx_w;            // [rows][4] or null
+  const uint8_t* k8;
+  const float* kscale;
+  int64_t k_stride;
+  // workspace
+  float* sample;                 // [rows][kPfSample]
+  float* thresh;                 // [rows]
+  uint32_t* count;               // [rows][kPfSplits] candidates per segment
+  uint64_t* list;                // [rows][kPfSplits][kPfSeg]
+  int32_t* out;                  // [rows][out_stride]
+  int32_t out_stride;
+};
+hipError_t launch_prefill_index(const PrefillPass& p, hipStream_t stream);
+
 }  // namespace csa2

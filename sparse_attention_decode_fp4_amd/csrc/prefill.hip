@@ -1,0 +1,567 @@
+// Indexer of a prefill chunk: many query rows scored against the same keys.
+//
+// Here the indexer scoring is a real dense contraction (query rows x 4 heads
+// against every visible key), so it runs on fp8 MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales).  The score and the
+// selection rule are those of the decode indexer (a reading, see index.hip).
+//
+// Per-row top-k without materialising the score matrix, in four kernels:
+//   sample     MFMA scores of every row against a strided sample of at most
+//              2,048 keys of its row tile;
+//   threshold  per row, T0 = the k_s-th largest sample score, with k_s sized
+//              so that about 2.5 k keys of the full row reach T0;
+//   filter     MFMA scores of every visible (row, key) pair; pairs scoring at
+//              least T0 are appended to the row's candidate list, one segment
+//              per (row, key range) counted in LDS, so no global atomics;
+//   select     if the list holds at least min(k, visible) candidates and did
+//              not overflow, it contains the whole top k.  MFMA scores are
+//              not binary32-exact (measured error up to ~2.5e-5 of the sum
+//              of |products|), so they settle only keys clearly above or
+//              below the MFMA k-th score; keys within 2^-8 of it are rescored
+//              on VALU (the decode scan's arithmetic) and ranked exactly.
+//              Winners are sorted by position.  If the list cannot hold the
+//              answer (overflow, too few keys, or the 2^-8 band reaches below
+//              the sampled threshold) the row is recomputed exactly on its own
+//              (VALU scoring, radix steps over recomputed keys): slow, exact,
+//              and reached only when the sample misleads.
+#include "kernels.hpp"
+
+namespace csa2 {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+constexpr int kPfStage = 256;   // keys staged in LDS per step
+constexpr uint32_t kUnitScales = 0x7F7F7F7Fu;  // E8M0 127 = 1.0 in every byte
+
+__device__ __forceinline__ int64_t pf_visible(const PrefillPass& p, int seq, int64_t qi) {
+  const int64_t pos = p.seq.a[seq] + qi;
+  int64_t v = (pos + 1) / p.ratio;
+  const int64_t ne = p.seq.b[seq];
+  v = v < ne ? v : ne;
+  return v < 0 ? 0 : v;
+}
+
+// Samples of a row tile: S = min(V, kPfSample) keys j(t) = t*V/S, V being the
+// visible count of the tile's first query (the smallest of the tile).
+__device__ __forceinline__ int64_t pf_sample_key(int64_t t, int64_t V, int64_t S) {
+  return S == V ? t : (t * V) / S;
+}
+
+__device__ __forceinline__ float key_to_score(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+// ------------------------------------------------------------------ MFMA pass
+// Workgroup: 256 query rows of one sequence (wave w: rows 64w..64w+63 as
+// eight A tiles of 8 queries x 4 heads) against a range of keys staged in LDS.
+template <bool kFilter, bool kHasW>
+__global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
+  const int split = blockIdx.x % p.esplit;
+  const int tile = blockIdx.x / p.esplit;
+  const int seq = tile / p.tiles_per_seq;
+  const int64_t q0 = (int64_t)(tile % p.tiles_per_seq) * kPfRows;
+  const int nq_tile = (int)((p.n_q - q0) < kPfRows ? (p.n_q - q0) : kPfRows);
+  const int64_t row0 = (int64_t)seq * p.n_q + q0;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  const int64_t v_first = pf_visible(p, seq, q0);
+  const int64_t v_last = pf_visible(p, seq, q0 + nq_tile - 1);
+  // key range of this workgroup
+  int64_t n_keys, k_begin, k_end;
+  if (kFilter) {
+    n_keys = v_last;
+  } else {
+    n_keys = v_first < kPfSample ? v_first : kPfSample;
+  }
+  {
+    const int64_t per = ((n_keys + p.esplit - 1) / p.esplit + 31) / 32 * 32;
+    k_begin = split * per;
+    k_end = k_begin + per < n_keys ? k_begin + per : n_keys;
+  }
+  if (k_begin >= k_end) {
+    if (kFilter)
+      for (int i = t; i < nq_tile; i += 256) p.count[(row0 + i) * kPfSplits + split] = 0;
+    return;
+  }
+
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kPfStage * kDI];
+  __shared__ float stage_ks[2][kPfStage];
+  __shared__ int64_t vis_row[kPfRows];
+  __shared__ float w_row[kHasW ? kPfRows * kHI : 1];
+  __shared__ uint32_t seg_count[kFilter ? kPfRows : 1];
+
+  for (int i = t; i < kPfRows; i += 256) vis_row[i] = i < nq_tile ? pf_visible(p, seq, q0 + i) : 0;
+  if (kFilter)
+    for (int i = t; i < kPfRows; i += 256) seg_count[i] = 0;
+  if (kHasW)
+    for (int i = t; i < kPfRows * kHI; i += 256)
+      w_row[i] = (i / kHI) < nq_tile ? p.idx_w[(row0 + i / kHI) * kHI + (i % kHI)] : 0.0f;
+
+  // A operands: tile a = queries 64w + 8a .. +8, row m = 4*query + head,
+  // lane holds 32 consecutive channels 32*half .. of row l32
+  v8i_t A[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int ql = 64 * wave + 8 * a + (l32 >> 2);
+    const int h = l32 & 3;
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (ql < nq_tile) {
+      const uint8_t* src = p.idx_q + ((row0 + ql) * kHI + h) * kDI + 32 * half;
+      lo = *reinterpret_cast<const uint4*>(src);
+      hi = *reinterpret_cast<const uint4*>(src + 16);
+    }
+    A[a] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  // thresholds of the 32 query rows this lane sees (filter only)
+  float T[8][4];
+  if (kFilter) {
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ql = 64 * wave + 8 * a + 2 * i + half;
+        T[a][i] = ql < nq_tile ? p.thresh[row0 + ql] : INFINITY;
+      }
+  }
+
+  const int seq_keys = 0;
+  (void)seq_keys;
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
+  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
+
+  auto key_of = [&](int64_t slot) -> int64_t {
+    return kFilter ? slot : pf_sample_key(slot, v_first, n_keys);
+  };
+  // cooperative staging: thread t brings key (base + t)
+  auto stage_load = [&](int buf, int64_t base) {
+    const int64_t slot = base + t;
+    uint4 v[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    float ksv = 0.0f;
+    if (slot < k_end) {
+      const int64_t key = key_of(slot);
+      const uint4* src = reinterpret_cast<const uint4*>(kb + key * kDI);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = src[i];
+      ksv = sb[key];
+    }
+    uint4* dst = reinterpret_cast<uint4*>(&stage[buf][t * kDI]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    stage_ks[buf][t] = ksv;
+  };
+
+  int buf = 0;
+  stage_load(0, k_begin);
+  for (int64_t base = k_begin; base < k_end; base += kPfStage) {
+    __syncthreads();  // stage[buf] complete; stage[buf^1] free
+    if (base + kPfStage < k_end) stage_load(buf ^ 1, base + kPfStage);
+    const int n_here = (int)(k_end - base < kPfStage ? k_end - base : kPfStage);
+    for (int bt = 0; bt < n_here; bt += 32) {
+      const uint8_t* brow = &stage[buf][(bt + l32) * kDI + 32 * half];
+      const uint4 b0 = *reinterpret_cast<const uint4*>(brow);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(brow + 16);
+      const v8i_t B = v8i_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      const float ksn = stage_ks[buf][bt + l32];
+      const int64_t slot = base + bt + l32;
+      const bool slot_ok = (bt + l32) < n_here;
+      const bool all_visible = kFilter ? (base + bt + 32 <= v_first) : true;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        v16f_t acc = {};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a], B, acc, 0, 0, 0, kUnitScales, 0, kUnitScales);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ql = 64 * wave + 8 * a + 2 * i + half;
+          float sum;
+          if (kHasW) {
+            sum = w_row[ql * kHI] * fmaxf(acc[4 * i], 0.0f) + w_row[ql * kHI + 1] * fmaxf(acc[4 * i + 1], 0.0f) +
+                  w_row[ql * kHI + 2] * fmaxf(acc[4 * i + 2], 0.0f) + w_row[ql * kHI + 3] * fmaxf(acc[4 * i + 3], 0.0f);
+          } else {
+            sum = (fmaxf(acc[4 * i], 0.0f) + fmaxf(acc[4 * i + 1], 0.0f)) +
+                  (fmaxf(acc[4 * i + 2], 0.0f) + fmaxf(acc[4 * i + 3], 0.0f));
+          }
+          const float s = ksn * sum;
+          if (kFilter) {
+            bool hit = slot_ok && s >= T[a][i];
+            if (hit && !all_visible) hit = slot < vis_row[ql];
+            if (hit) {  // append to this row's segment for this key range
+              const uint32_t at = atomicAdd(&seg_count[ql], 1u);
+              if (at < (uint32_t)kPfSeg)
+                p.list[((row0 + ql) * kPfSplits + split) * kPfSeg + at] = select_key(score_key(s), (uint32_t)slot);
+            }
+          } else if (slot_ok && ql < nq_tile) {
+            p.sample[(row0 + ql) * kPfSample + slot] = s;
+          }
+        }
+      }
+    }
+    buf ^= 1;
+  }
+  if (kFilter) {
+    __syncthreads();
+    for (int i = t; i < nq_tile; i += 256) p.count[(row0 + i) * kPfSplits + split] = seg_count[i];
+  }
+}
+
+// ------------------------------------------------------------------ threshold
+// One wave per row: T0 = the k_s-th largest of the row's samples (exact, by
+// 8-bit radix steps over order-preserving keys held in registers).
+__global__ __launch_bounds__(256) void k_prefill_threshold(PrefillPass p) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  __shared__ uint32_t hist[4][256];
+  if (row >= p.rows) return;
+  const int seq = (int)(row / p.n_q);
+  const int64_t qi = row - (int64_t)seq * p.n_q;
+  const int64_t q0 = qi / kPfRows * kPfRows;
+  const int64_t V = pf_visible(p, seq, q0);
+  const int64_t S = V < kPfSample ? V : kPfSample;
+  const int64_t vis = pf_visible(p, seq, qi);
+  const uint32_t k = (uint32_t)p.k;
+  if (vis <= (int64_t)k || S == 0) {  // every visible key is a winner, or no sample
+    if (lane == 0) p.thresh[row] = -INFINITY;
+    return;
+  }
+  uint32_t ks;
+  if (S == vis) {
+    ks = k;
+  } else {
+    const double want = 2.5 * (double)k * (double)S / (double)vis + 4.0;
+    ks = want >= (double)S ? (uint32_t)S : (uint32_t)want;
+  }
+  if (ks >= (uint32_t)S) {  // the sample is too small to bound the row
+    if (lane == 0) p.thresh[row] = -INFINITY;
+    return;
+  }
+  uint32_t keys[kPfSample / 64];
+#pragma unroll
+  for (int j = 0; j < kPfSample / 64; ++j) {
+    const int64_t s = (int64_t)j * 64 + lane;
+    keys[j] = s < S ? score_key(p.sample[row * kPfSample + s]) : 0u;
+  }
+  uint32_t prefix = 0, need = ks;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    const uint32_t hmask = shift == 24 ? 0u : (~0u << (shift + 8));
+#pragma unroll
+    for (int j = 0; j < kPfSample / 64; ++j) {
+      const int64_t s = (int64_t)j * 64 + lane;
+      if (s < S && (keys[j] & hmask) == prefix) atomicAdd(&hist[wave][(keys[j] >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t c0 = hist[wave][4 * lane], c1 = hist[wave][4 * lane + 1];
+    const uint32_t c2 = hist[wave][4 * lane + 2], c3 = hist[wave][4 * lane + 3];
+    const uint32_t mine = c0 + c1 + c2 + c3;
+    uint32_t x = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_down(x, d, 64);
+      if (lane + d < 64) x += y;
+    }
+    uint32_t ab = x - mine;
+    const uint32_t cs[4] = {c0, c1, c2, c3};
+    uint32_t found = 0xFFFFFFFFu, nneed = 0;
+    for (int j = 3; j >= 0; --j) {
+      if (ab < need && ab + cs[j] >= need) { found = 4 * lane + j; nneed = need - ab; }
+      ab += cs[j];
+    }
+    // exactly one lane found the digit
+    const unsigned long long ball = __ballot(found != 0xFFFFFFFFu);
+    const int src = __ffsll(ball) - 1;
+    const uint32_t digit = __shfl(found, src, 64);
+    need = __shfl(nneed, src, 64);
+    prefix |= digit << shift;
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (lane == 0) p.thresh[row] = key_to_score(prefix);
+}
+
+// ------------------------------------------------------------------ select
+__device__ __forceinline__ uint32_t pf_scan_256(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < wave; ++i) before += wsum[i];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return before + x;
+}
+
+// Exact score of key `pos` for a row whose query (16 channels per lane, 4
+// heads) sits in q; a lane quad scores one key.  Mirrors the decode scan.
+__device__ __forceinline__ float pf_quad_score(const half2_t (&q)[kHI][8], const float (&w)[kHI],
+                                               const uint8_t* kb, const float* sb, int64_t pos, bool valid,
+                                               int quarter) {
+  u32x4_t raw = u32x4_t{0, 0, 0, 0};
+  float ks = 0.0f;
+  if (valid) {
+    raw = *reinterpret_cast<const u32x4_t*>(kb + pos * kDI + quarter * 16);
+    ks = sb[pos];
+  }
+  float d[kHI] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[j], 1.0f, false);
+    const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[j], 1.0f, true);
+#pragma unroll
+    for (int h = 0; h < kHI; ++h) {
+      d[h] = __builtin_amdgcn_fdot2(q[h][2 * j], lo, d[h], false);
+      d[h] = __builtin_amdgcn_fdot2(q[h][2 * j + 1], hi, d[h], false);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) {
+    d[h] += quad_xor1(d[h]);
+    d[h] += quad_xor2(d[h]);
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) acc += w[h] * fmaxf(d[h], 0.0f);
+  return ks * acc;
+}
+
+__global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int seq = (int)(row / p.n_q);
+  const int64_t qi = row - (int64_t)seq * p.n_q;
+  const int64_t vis = pf_visible(p, seq, qi);
+  const uint32_t k = (uint32_t)p.k;
+  const uint32_t need_all = vis < (int64_t)k ? (uint32_t)vis : k;
+  int32_t* out = p.out + row * p.out_stride;
+
+  __shared__ uint64_t lc[kPfCap];
+  __shared__ uint32_t win[CSA2_MAX_K];
+  __shared__ uint32_t bt[kPfCap];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t wsum[4];
+  __shared__ uint64_t sh_kth;
+  __shared__ uint32_t sh_need;
+  __shared__ uint32_t seg_start[kPfSplits + 1];
+
+  // exact k-th largest over n keys from `get`, by 8-bit radix steps
+  auto radix_kth = [&](auto get, uint32_t n, uint32_t want) -> uint64_t {
+    if (t == 0) { sh_kth = 0; sh_need = want; }
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      h256[t] = 0;
+      __syncthreads();
+      const uint64_t prefix = sh_kth;
+      const uint64_t hmask = (shift == 56) ? 0ull : (~0ull << (shift + 8));
+      get(n, [&](uint32_t g, uint64_t key) {
+        (void)g;
+        if ((key & hmask) == prefix) atomicAdd(&h256[(key >> shift) & 255u], 1u);
+      });
+      __syncthreads();
+      if (t < 64) {
+        const uint32_t nd = sh_need;
+        const uint32_t c0 = h256[4 * t], c1 = h256[4 * t + 1], c2 = h256[4 * t + 2], c3 = h256[4 * t + 3];
+        const uint32_t mine = c0 + c1 + c2 + c3;
+        uint32_t x = mine;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint32_t y = __shfl_down(x, d, 64);
+          if (t + d < 64) x += y;
+        }
+        uint32_t ab = x - mine;
+        const uint32_t cs[4] = {c0, c1, c2, c3};
+        for (int j = 3; j >= 0; --j) {
+          if (ab < nd && ab + cs[j] >= nd) {
+            sh_need = nd - ab;
+            sh_kth = prefix | ((uint64_t)(4 * t + j) << shift);
+          }
+          ab += cs[j];
+        }
+      }
+      __syncthreads();
+    }
+    return sh_kth;
+  };
+
+  // the row's query as packed f16 (16 channels of each head per lane of a
+  // quad) for exact rescoring on VALU
+  const int quarter = t & 3;
+  half2_t q[kHI][8];
+  {
+    const uint8_t* qp = p.idx_q + row * (kHI * kDI) + quarter * 16;
+#pragma unroll
+    for (int h = 0; h < kHI; ++h) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qp + h * kDI);
+      const uint32_t ws4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        q[h][2 * j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws4[j], 1.0f, false);
+        q[h][2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws4[j], 1.0f, true);
+      }
+    }
+  }
+  float w[kHI];
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) w[h] = p.idx_w ? p.idx_w[row * kHI + h] : 1.0f;
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
+  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
+
+  // segment counts of this row (one per key range of the filter pass)
+  uint32_t seg = t < p.esplit ? p.count[row * kPfSplits + t] : 0u;
+  const bool seg_over = __syncthreads_or(seg > (uint32_t)kPfSeg);
+  uint32_t cnt;
+  const uint32_t seg_off = pf_scan_256(seg, wsum, cnt) - seg;
+  bool fast = !seg_over && cnt >= need_all && cnt <= (uint32_t)kPfCap;
+  uint32_t n_win = 0;
+  if (fast) {
+    if (t < p.esplit) seg_start[t] = seg_off;
+    if (t == 0) seg_start[p.esplit] = cnt;
+    __syncthreads();
+    for (uint32_t g = t; g < cnt; g += 256) {
+      int lo = 0, hi = p.esplit - 1;  // last segment starting at or before g
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg_start[mid] <= g) lo = mid; else hi = mid - 1;
+      }
+      lc[g] = p.list[(row * kPfSplits + lo) * kPfSeg + (g - seg_start[lo])];
+    }
+    __syncthreads();
+    if (vis <= (int64_t)k) {  // threshold -inf: the list is every visible key
+      for (uint32_t g = t; g < cnt; g += 256) win[g] = select_key_pos(lc[g]);
+      n_win = cnt;
+    } else {
+      // MFMA scores are not binary32-exact (error up to ~2.5e-5 of the sum
+      // of |products|): they settle only the clear winners and losers.  Keys
+      // within 2^-8 of the MFMA k-th score are rescored exactly on VALU.
+      const uint64_t kth_m = radix_kth([&](uint32_t n, auto&& f) { for (uint32_t g = t; g < n; g += 256) f(g, lc[g]); }, cnt, k);
+      const float sk = key_to_score((uint32_t)(kth_m >> 32));
+      const float mg = fabsf(sk) * 0.00390625f;
+      const uint32_t lo_key = score_key(sk - mg), hi_key = score_key(sk + mg);
+      // keys below the list's threshold are unknown: the band must sit above it
+      if (!(sk - mg >= p.thresh[row])) fast = false;
+      if (fast) {
+        // clear winners first, band members compacted into bt
+        uint32_t n_band = 0;
+        for (uint32_t g0 = 0; g0 < cnt; g0 += 256) {
+          const uint32_t g = g0 + t;
+          const uint32_t sk32 = g < cnt ? (uint32_t)(lc[g] >> 32) : 0u;
+          const bool a = g < cnt && sk32 > hi_key;
+          const bool b = g < cnt && sk32 >= lo_key && sk32 <= hi_key;
+          uint32_t na, nbnd;
+          const uint32_t oa = pf_scan_256(a ? 1u : 0u, wsum, na) - (a ? 1u : 0u);
+          const uint32_t ob = pf_scan_256(b ? 1u : 0u, wsum, nbnd) - (b ? 1u : 0u);
+          if (a) win[n_win + oa] = select_key_pos(lc[g]);
+          if (b && n_band + ob < (uint32_t)kPfCap) bt[n_band + ob] = select_key_pos(lc[g]);
+          n_win += na;
+          n_band += nbnd;
+        }
+        __syncthreads();
+        const uint32_t need = k - n_win;
+        // exact keys of the band, a lane quad per key
+        for (uint32_t base = 0; base < n_band; base += 64) {
+          const uint32_t g = base + (t >> 2);
+          const bool valid = g < n_band;
+          const uint32_t pos = valid ? (uint32_t)bt[g] : 0u;
+          const float sx = pf_quad_score(q, w, kb, sb, pos, valid, quarter);
+          if (valid && quarter == 0) lc[g] = select_key(score_key(sx), pos);  // lc reused for exact keys
+        }
+        __syncthreads();
+        uint64_t kth_x = 0;
+        if (n_band > need)
+          kth_x = radix_kth([&](uint32_t n, auto&& f) { for (uint32_t g = t; g < n; g += 256) f(g, lc[g]); }, n_band, need);
+        for (uint32_t g0 = 0; g0 < n_band; g0 += 256) {
+          const uint32_t g = g0 + t;
+          const bool f = g < n_band && lc[g] >= kth_x;
+          uint32_t nr;
+          const uint32_t o = pf_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
+          if (f) win[n_win + o] = select_key_pos(lc[g]);
+          n_win += nr;
+        }
+      }
+    }
+  }
+  if (fast) {
+    // winners ascending by position (bitonic sort, padded to a power of two)
+    uint32_t n2 = 1;
+    while (n2 < n_win) n2 <<= 1;
+    __syncthreads();
+    for (uint32_t i = n_win + t; i < n2; i += 256) win[i] = 0xFFFFFFFFu;
+    __syncthreads();
+    for (uint32_t size = 2; size <= n2; size <<= 1) {
+      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+        for (uint32_t i = t; i < n2 / 2; i += 256) {
+          const uint32_t lo = 2 * i - (i & (stride - 1));
+          const uint32_t hi = lo + stride;
+          const bool asc = (lo & size) == 0;
+          const uint32_t a = win[lo], b = win[hi];
+          if ((a > b) == asc) { win[lo] = b; win[hi] = a; }
+        }
+        __syncthreads();
+      }
+    }
+    for (uint32_t j = t; j < k; j += 256) out[j] = j < n_win ? (int32_t)win[j] : -1;
+  } else {
+    // ---- exact recompute of this row (rare): radix steps over recomputed keys
+    const uint32_t nv = (uint32_t)vis;
+    // visit every visible key: a lane quad per key, 64 keys per step
+    auto visit = [&](uint32_t n, auto&& f) {
+      for (uint32_t base = 0; base < n; base += 64) {
+        const uint32_t pos = base + (t >> 2);
+        const bool valid = pos < n;
+        const float sx = pf_quad_score(q, w, kb, sb, pos, valid, quarter);
+        if (valid && quarter == 0) f(pos, select_key(score_key(sx), pos));
+      }
+    };
+    uint64_t kth = 0;
+    if (nv > k) kth = radix_kth(visit, nv, k);
+    // winners in position order: each step of 64 keys keeps its order
+    uint32_t written = 0;
+    for (uint32_t base = 0; base < nv; base += 64) {
+      const uint32_t pos = base + (t >> 2);
+      const bool valid = pos < nv;
+      const float sx = pf_quad_score(q, w, kb, sb, pos, valid, quarter);
+      const bool f = valid && quarter == 0 && select_key(score_key(sx), pos) >= kth;
+      uint32_t nr;
+      const uint32_t o = pf_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
+      if (f && written + o < k) out[written + o] = (int32_t)pos;
+      written += nr;
+    }
+    for (uint32_t j = written + t; j < k; j += 256) out[j] = -1;
+  }
+}
+
+hipError_t launch_prefill_index(const PrefillPass& p, hipStream_t stream) {
+  if (p.rows == 0) return hipSuccess;
+  const int tiles = p.batch * p.tiles_per_seq;
+  const unsigned grid = (unsigned)(tiles * p.esplit);
+  int h = prof_begin(CSA2_K_PREFILL_SAMPLE, stream);
+  if (p.idx_w)
+    hipLaunchKernelGGL((k_prefill_mfma<false, true>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_prefill_mfma<false, false>), dim3(grid), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_prefill_threshold, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_end(h, stream);
+  h = prof_begin(CSA2_K_PREFILL_FILTER, stream);
+  if (p.idx_w)
+    hipLaunchKernelGGL((k_prefill_mfma<true, true>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_prefill_mfma<true, false>), dim3(grid), dim3(256), 0, stream, p);
+  prof_end(h, stream);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  h = prof_begin(CSA2_K_PREFILL_SELECT, stream);
+  hipLaunchKernelGGL(k_prefill_select, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+  prof_end(h, stream);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

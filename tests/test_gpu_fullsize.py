@@ -133,3 +133,51 @@ def test_config_full_size(csa2, cfg):
                 kinds.append(check_topk(idx[b, 0], ref_idx, oracle.scores(iq, None, rk, rks), 512, ctx,
                                         f"reindex seq {b}"))
     print(f"config {cfg}: {kinds}")
+
+
+def test_prefill_full_size(csa2):
+    """The full prefill chunk (262,144-token prefix + 4,096 queries, ratio 2):
+    sampled query rows against the oracle, the chunk's encoding bit-exact."""
+    c = gen.CONFIGS[4]
+    P, T = c["prefix_tokens"], c["chunk"]
+    seed = 1004
+    n_ent = (P + T) // 2
+    dev = "cuda"
+    x = gen.latent(P + T, seed, device=dev)
+    kin = gen.index_key(P + T, seed, device=dev)
+    nib, sc, k8, ks = csa2.csa2_quantize_kv(x, ratio=2, k_in=kin)
+    kv = csa2.make_kv(nib, sc, k8, ks, n_ent)
+    swa_pos0 = P - 127
+    layers = []
+    for j, m in enumerate(c["plans"][0]):
+        d = dict(mode=csa2.MODE_FULL if m == "F" else csa2.MODE_REUSE,
+                 q=gen.attn_query((1, T), seed, j, device=dev),
+                 swa=gen.window_rows(1, P + T - swa_pos0, seed, j, device=dev))
+        if m == "F":
+            d["idx_q"], d["kv"] = gen.index_query((1, T), seed, j, device=dev), kv
+        layers.append(d)
+    ws = csa2.Workspace(1, T, n_ent)
+    st = csa2.State(1, T)
+    outs = csa2.csa2_run_group(ws, st, layers, [P], [n_ent], [swa_pos0], ratio=2)
+    torch.cuda.synchronize()
+    kh = kin.cpu().numpy()
+    rk, rks = oracle.index_key_encode(oracle.compress_pairs(kh, 2))
+    assert np.array_equal(k8.cpu().numpy(), rk) and np.array_equal(ks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    iq = layers[0]["idx_q"].cpu().numpy()
+    idx = st.indices.cpu().numpy()
+    xh = x.cpu().numpy()
+    kinds = []
+    for i in [0, 1, 2, 777, 2048, 4094, 4095]:
+        nv = oracle.visible_entries(P + i, 2)
+        ref = oracle.index_flat(iq[0, i], None, rk, rks, nv)
+        kinds.append(check_topk(idx[0, i], ref, oracle.scores(iq[0, i], None, rk[:nv], rks[:nv]), 512, nv, f"query {i}"))
+        if not np.array_equal(idx[0, i], ref):
+            continue
+        sel = ref[ref >= 0]
+        rows = np.concatenate([2 * sel[:, None], 2 * sel[:, None] + 1], axis=1).reshape(-1)
+        sn, ss = oracle.fp4_encode_rows(oracle.compress_pairs(xh[rows], 2))
+        for j, L in enumerate(layers):
+            r = oracle.sparse_swa_attention(gen.bf16_bits(L["q"][:, i:i + 1])[0, 0], sn, ss, np.arange(len(sel)),
+                                            gen.bf16_bits(L["swa"])[0], swa_pos0, P + i)
+            check_close(outs[j][0, i].cpu().numpy(), r, f"query {i} layer {j}")
+    print("prefill full size:", kinds)
