@@ -302,9 +302,7 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* state,
 size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entries);
 
 /*
- * Zero a workspace once after allocating it.  Calls keep their counters and
- * histograms at zero when they return, so a workspace stays ready for the
- * next call on the same stream.
+ * Zero a workspace (optional: every call initialises what it reads).
  *   workspace  device, 256-byte aligned;  ws_bytes  a multiple of 4
  */
 int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);
@@ -321,7 +319,7 @@ int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 #define CSA2_K_QUANTIZE 0
 #define CSA2_K_BLOCK_KEYS 1
 #define CSA2_K_INDEX_SCAN 2
-#define CSA2_K_INDEX_FILTER 3
+#define CSA2_K_INDEX_SAMPLE 3
 #define CSA2_K_INDEX_SELECT 4
 #define CSA2_K_ATTENTION 5
 #define CSA2_K_PREFILL_SAMPLE 6

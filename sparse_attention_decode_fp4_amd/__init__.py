@@ -24,9 +24,9 @@ TOP_K, SWA, BLOCK, N_BLOCKS, MAX_K = 512, 128, 8, 2048, 2048
 INDEX_FLAT, INDEX_HIER, INDEX_POOL = 0, 1, 2
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_STATE, ERR_WORKSPACE, ERR_HIP = range(6)
-(K_QUANTIZE, K_BLOCK_KEYS, K_INDEX_SCAN, K_INDEX_FILTER, K_INDEX_SELECT, K_ATTENTION,
+(K_QUANTIZE, K_BLOCK_KEYS, K_INDEX_SCAN, K_INDEX_SAMPLE, K_INDEX_SELECT, K_ATTENTION,
  K_PREFILL_SAMPLE, K_ATTENTION_MERGE, K_PREFILL_FILTER, K_PREFILL_SELECT) = range(10)
-KERNEL_NAMES = ["quantize", "block_keys", "index_scan", "index_filter", "index_select", "attention",
+KERNEL_NAMES = ["quantize", "block_keys", "index_scan", "index_sample", "index_select", "attention",
                 "prefill_sample", "attention_merge", "prefill_filter", "prefill_select"]
 ABI_VERSION = 1
 

@@ -29,29 +29,29 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-constexpr int64_t kMaxEntries = (int64_t)kMaxFChunks * kFilterChunk;
+constexpr int64_t kMaxEntries = (int64_t)kMaxChunks * kScanChunk;
 constexpr size_t kWsAlign = 256;
 constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of attention partials
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t hist, scores, cand, fcount, blocks, nsel, partial;
+  size_t samples, thresh, seg_count, seg_list, blocks, nsel, partial;
   size_t pf_sample, pf_thresh, pf_count, pf_list, total;
-  int64_t stride;  // items per row in scores / cand
+  int32_t max_chunks;  // scan chunks per row covered by the segment buffers
 };
 
 // Decode-path buffers cover `rows` query rows of up to `max_items` items;
 // prefill-path buffers cover `pf_rows` query rows (0 when unused).
 WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   WsLayout w{};
-  w.stride = (int64_t)round_up((size_t)std::max<int64_t>(max_items, 1), kFilterChunk);
+  w.max_chunks = (int32_t)((std::max<int64_t>(max_items, 1) + kScanChunk - 1) / kScanChunk);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
-  w.hist = take((size_t)rows * kHistBins * 4);
-  w.scores = take((size_t)rows * w.stride * 4);
-  w.cand = take((size_t)rows * w.stride * 8);
-  w.fcount = take((size_t)rows * kMaxFChunks * 4);
+  w.samples = take((size_t)rows * 2048 * 4);
+  w.thresh = take((size_t)rows * 4);
+  w.seg_count = take((size_t)rows * w.max_chunks * 4);
+  w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
   w.nsel = take((size_t)rows * 4);
   w.partial = take((size_t)kMaxPartialUnits * kH * (kD + 4) * 4);
@@ -179,12 +179,11 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     }
     p.idx_q = a->idx_q + row0 * kHI * kDI;
     p.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;
-    p.hist = at<uint32_t>(ws, w.hist);
-    p.scores = at<uint32_t>(ws, w.scores);
-    p.cand = at<uint64_t>(ws, w.cand);
-    p.score_stride = w.stride;
-    p.fcount = at<uint32_t>(ws, w.fcount);
-    p.max_fchunks = kMaxFChunks;
+    p.samples = at<uint32_t>(ws, w.samples);
+    p.thresh = at<float>(ws, w.thresh);
+    p.seg_count = at<uint32_t>(ws, w.seg_count);
+    p.seg_list = at<uint64_t>(ws, w.seg_list);
+    p.max_chunks = w.max_chunks;
     hipError_t e;
     if (a->kind == CSA2_INDEX_HIER) {
       IndexPass b = p;  // pass 1: blocks

@@ -19,7 +19,6 @@ constexpr int kD = CSA2_D_LATENT;
 constexpr int kDI = CSA2_D_INDEX;
 constexpr int kHI = CSA2_H_INDEX;
 constexpr int kH = CSA2_H_ATTN;
-constexpr int kHistBins = 4096;  // histogram over the top 12 bits of a score key
 
 // ---------------------------------------------------------------- binary32
 // One rounding per operation.  The pragma keeps these from being fused into
@@ -132,6 +131,22 @@ __device__ __forceinline__ float quad_xor2(float v) {
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
+}
+
+// Histogram increment of `bin` by the calling lanes.  When every calling lane
+// of the wave hits the same bin (keys sharing their high bits, the common case
+// in top-k refinement) one lane adds the whole count: without it the LDS
+// atomics of the wave serialise on one address.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin) {
+  const unsigned long long act = __ballot(1);
+  const int first = __ffsll((long long)act) - 1;
+  const uint32_t ref = (uint32_t)__shfl((int)bin, first, 64);
+  const unsigned long long same = __ballot(bin == ref);
+  if (same == act) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(hist + ref, (uint32_t)__popcll(act));
+  } else {
+    atomicAdd(hist + bin, 1u);
+  }
 }
 
 // Number of workgroups per XCD group: consecutive workgroup ids are spread

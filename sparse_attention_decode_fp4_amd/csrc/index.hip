@@ -7,21 +7,30 @@
 //   s_p = ks_p * sum_h w_h * max(0, q_h . k_p)   over 4 indexer heads.
 //
 // One pass = three kernels over the rows (query rows) of a call:
+//   sample  eight workgroups per row score a strided sample of at most 2,048
+//           of its items and store their order keys; each scan workgroup
+//           derives the row threshold T0 from them: the lower edge, at 20
+//           key bits, of the bin holding the k_s-th largest sample, k_s sized
+//           so that about 2.5 k items of the row reach T0 (every item when
+//           the sample is the whole row);
 //   scan    streams the fp8 keys once (4 lanes per key, 16 B each, fully
 //           coalesced), scores every item with packed f16 dot products
-//           (v_dot2c_f32_f16; fp8 -> f16 is exact), writes an order-preserving
-//           uint32 score key per item and a 4096-bin histogram of the key's
-//           top 12 bits per row;
-//   filter  finds the histogram bin T at which the count of items at or above
-//           it reaches k, and compacts the items of bin >= T in item order;
-//   select  radix-selects, among those few candidates, the exact k-th largest
-//           (score, -item) key and writes the winners in ascending order.
-// The candidates are exact: every item of the top k lies in a bin >= T.
+//           (v_dot2c_f32_f16; fp8 -> f16 is exact) and appends the items
+//           scoring at least T0 to a segment per (row, 2,048-item chunk),
+//           counted in LDS;
+//   select  gathers the segments (about 2.5 k candidates), radix-selects the
+//           exact k-th largest (score, -item) key, sorts the winners by
+//           item and writes their positions.  If the candidates cannot hold
+//           the answer (fewer than k, or a segment overflowed: the sample
+//           misled, e.g. all scores equal) the row is recomputed exactly by
+//           itself (radix steps over recomputed keys): slow, exact, rare.
 #include "kernels.hpp"
 
 namespace csa2 {
 
-constexpr int kSelectLds = 6144;    // candidates kept in LDS by the select kernel
+constexpr int kSample = 2048;       // sampled items per row
+constexpr int kSelCap = 4096;       // candidates the select kernel holds in LDS
+constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
 
 __device__ __forceinline__ int64_t row_vis_positions(const IndexPass& p, int row) {
   const int seq = row / p.n_q, i = row - seq * p.n_q;
@@ -54,7 +63,7 @@ __device__ __forceinline__ int64_t item_position(const IndexPass& p, int row, in
 
 // Workgroup -> (row, chunk).  With 8 or more rows every row's chunks share
 // one XCD (workgroup ids are dealt round-robin over the 8 XCDs), so the
-// scores and histogram a row writes stay in that XCD's L2 for the next pass.
+// candidate segments a row writes stay in that XCD's L2 for the select.
 __device__ __forceinline__ void map_row_chunk(int rows, int per_row, int& row, int& chunk) {
   const int lin = blockIdx.x;
   if (rows >= kXcds) {
@@ -74,6 +83,283 @@ __device__ __forceinline__ void fp8x4_to_f16(uint32_t w, half2_t& lo, half2_t& h
   hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
 }
 
+
+__device__ __forceinline__ float key_to_score(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+// Query of a row as packed f16, 16 channels of each head per lane of a quad.
+__device__ __forceinline__ void load_query_f16(const IndexPass& p, int row, int quarter, half2_t (&q)[kHI][8],
+                                               float (&w)[kHI]) {
+  const uint8_t* qp = p.idx_q + (int64_t)row * (kHI * kDI) + quarter * 16;
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(qp + h * kDI);
+    fp8x4_to_f16(raw.x, q[h][0], q[h][1]);
+    fp8x4_to_f16(raw.y, q[h][2], q[h][3]);
+    fp8x4_to_f16(raw.z, q[h][4], q[h][5]);
+    fp8x4_to_f16(raw.w, q[h][6], q[h][7]);
+  }
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) w[h] = p.idx_w ? p.idx_w[(int64_t)row * kHI + h] : 1.0f;
+}
+
+// Score of one key from its 16 bytes in this lane (a lane quad holds the key).
+__device__ __forceinline__ float quad_score(const half2_t (&q)[kHI][8], const float (&w)[kHI], u32x4_t raw,
+                                            float ks) {
+  float d[kHI] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    half2_t lo, hi;
+    fp8x4_to_f16(raw[j], lo, hi);
+#pragma unroll
+    for (int h = 0; h < kHI; ++h) {
+      d[h] = __builtin_amdgcn_fdot2(q[h][2 * j], lo, d[h], false);
+      d[h] = __builtin_amdgcn_fdot2(q[h][2 * j + 1], hi, d[h], false);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) {
+    d[h] += quad_xor1(d[h]);
+    d[h] += quad_xor2(d[h]);
+  }
+  float acc = 0.0f;
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) acc += w[h] * fmaxf(d[h], 0.0f);
+  return ks * acc;
+}
+
+__device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t (&q)[kHI][8],
+                                               const float (&w)[kHI], int seq, int quarter, int64_t pos,
+                                               bool valid) {
+  u32x4_t raw = u32x4_t{0, 0, 0, 0};
+  float ks = 0.0f;
+  if (valid) {
+    raw = *reinterpret_cast<const u32x4_t*>(p.k8 + ((int64_t)seq * p.k_stride + pos) * kDI + quarter * 16);
+    ks = p.kscale[(int64_t)seq * p.k_stride + pos];
+  }
+  return quad_score(q, w, raw, ks);
+}
+
+// Inclusive prefix sum over the 256 threads of a workgroup: shuffles inside
+// each wave, one LDS exchange of the four wave totals.
+__device__ __forceinline__ uint32_t block_incl_scan_256(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < wave; ++i) before += wsum[i];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return before + x;
+}
+
+// Exact k-th largest of n keys visited by `visit(n, f)` (f(key) per key), by
+// radix steps of 8 bits from bit `top` down.  256 threads; keys are unique
+// or the result is the k-th in the multiset order.
+template <typename Key, typename Visit>
+__device__ Key radix_kth(Visit visit, uint32_t n, uint32_t want, uint32_t* h256, Key* sh_kth, uint32_t* sh_need) {
+  const int t = threadIdx.x;
+  constexpr int kBits = 8 * (int)sizeof(Key);
+  if (t == 0) { *sh_kth = 0; *sh_need = want; }
+  for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+    h256[t] = 0;
+    __syncthreads();
+    const Key prefix = *sh_kth;
+    const Key hmask = (shift == kBits - 8) ? (Key)0 : (Key)(~(Key)0 << (shift + 8));
+    visit(n, [&](Key key) {
+      if ((key & hmask) == prefix) hist_add(h256, (uint32_t)(key >> shift) & 255u);
+    });
+    __syncthreads();
+    if (t < 64) {  // one wave: suffix sums over 256 digits, 4 per lane
+      const uint32_t nd = *sh_need;
+      const uint32_t c0 = h256[4 * t], c1 = h256[4 * t + 1], c2 = h256[4 * t + 2], c3 = h256[4 * t + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      uint32_t x = mine;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_down(x, d, 64);
+        if (t + d < 64) x += y;
+      }
+      uint32_t ab = x - mine;
+      const uint32_t cs[4] = {c0, c1, c2, c3};
+      for (int j = 3; j >= 0; --j) {
+        if (ab < nd && ab + cs[j] >= nd) {
+          *sh_need = nd - ab;
+          *sh_kth = prefix | ((Key)(4 * t + j) << shift);
+        }
+        ab += cs[j];
+      }
+    }
+    __syncthreads();
+  }
+  return *sh_kth;
+}
+
+// Exact k-th largest of the unique non-zero 64-bit keys held in registers
+// (kPer per thread, 256 threads, zeros for empty slots): radix steps of
+// 11, 11, 10, 11, 11 and 10 bits from the top, ending as soon as the chosen
+// bucket is taken whole.  Returns the k-th key, or the lower edge of a
+// bucket that holds exactly the keys from the top down to the k-th; either
+// way the keys >= the result are the k largest.  `bins` is 2048 words of LDS.
+template <int kPer>
+__device__ uint64_t block_kth_regs(const uint64_t (&key)[kPer], uint32_t want, uint32_t* bins, uint32_t* wsum,
+                                   uint32_t* sh) {
+  const int t = threadIdx.x;
+  uint64_t prefix = 0, pmask = 0;
+  uint32_t need = want;
+  int shift = 64;
+#pragma unroll 1
+  for (int step = 0; step < 6; ++step) {
+    const int width = (step == 2 || step == 5) ? 10 : 11;
+    shift -= width;
+    const uint32_t nb = 1u << width;
+    for (uint32_t i = t; i < 2048; i += 256) bins[i] = 0;
+    if (t == 0) sh[0] = 0xFFFFFFFFu;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (key[i] != 0ull && (key[i] & pmask) == prefix) atomicAdd(&bins[(uint32_t)(key[i] >> shift) & (nb - 1)], 1u);
+    __syncthreads();
+    // thread t owns bins 8t .. 8t+7
+    uint32_t hb[8], local = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      hb[j] = bins[8 * t + j];
+      local += hb[j];
+    }
+    uint32_t total;
+    const uint32_t incl = block_incl_scan_256(local, wsum, total);
+    uint32_t run = total - incl;  // keys in bins above 8t + 7
+    if (run < need && run + local >= need) {
+      for (int j = 7; j >= 0; --j) {
+        if (run + hb[j] >= need) { sh[0] = 8 * t + j; sh[1] = need - run; sh[2] = hb[j]; break; }
+        run += hb[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = sh[0], nneed = sh[1], count = sh[2];
+    __syncthreads();
+    prefix |= (uint64_t)digit << shift;
+    pmask |= (uint64_t)(nb - 1) << shift;
+    need = nneed;
+    if (need == count) break;  // the whole bucket is taken
+  }
+  return prefix;
+}
+
+// ------------------------------------------------------------------ sample
+// Sample size of a row and the rank k_s its threshold is taken at; k_s == 0
+// means "no threshold" (every item is a candidate).
+__device__ __forceinline__ void sample_plan(int64_t n_items, uint32_t k, int64_t& S, uint32_t& ks) {
+  S = n_items < kSample ? n_items : kSample;
+  ks = 0;
+  if (n_items > (int64_t)k && S > 0) {
+    if (S == n_items) {
+      ks = k;
+    } else {
+      const double want = 2.5 * (double)k * (double)S / (double)n_items + 4.0;
+      ks = want >= (double)S ? 0u : (uint32_t)want;
+    }
+  }
+}
+
+// kSampleSplit workgroups per row each score kSample / kSampleSplit of the
+// row's strided sample and store the order keys (0 for an empty slot).
+constexpr int kSampleSplit = 8;
+__global__ __launch_bounds__(256) void k_index_sample(IndexPass p) {
+  const int row = blockIdx.x / kSampleSplit, part = blockIdx.x % kSampleSplit;
+  const int t = threadIdx.x, quarter = t & 3;
+  const int seq = row / p.n_q;
+  const int64_t vis = row_vis_positions(p, row);
+  const int64_t n_items = row_items(p, row, vis);
+  int64_t S;
+  uint32_t ks;
+  sample_plan(n_items, (uint32_t)p.k, S, ks);
+  if (ks == 0) return;
+  half2_t q[kHI][8];
+  float w[kHI];
+  load_query_f16(p, row, quarter, q, w);
+  constexpr int U = kSample / kSampleSplit / 64;  // items per lane quad
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + quarter * 16;
+  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
+  u32x4_t raw[U];
+  float kv[U];
+  bool valid[U];
+  int64_t slot[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    slot[u] = (int64_t)part * (kSample / kSampleSplit) + u * 64 + (t >> 2);
+    // S == kSample (a power of two) whenever the sample is strided
+    const int64_t item = slot[u] < S ? (S == n_items ? slot[u] : (slot[u] * n_items) / kSample) : n_items;
+    const int64_t pos = item_position(p, row, item, n_items, vis, valid[u]);
+    raw[u] = valid[u] ? *reinterpret_cast<const u32x4_t*>(kb + pos * kDI) : u32x4_t{0, 0, 0, 0};
+    kv[u] = valid[u] ? sb[pos] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float sc = quad_score(q, w, raw[u], kv[u]);
+    if (quarter == 0) p.samples[(int64_t)row * kSample + slot[u]] = valid[u] ? score_key(sc) : 0u;
+  }
+}
+
+// Row threshold T0 from the row's sample keys `sk` (8 per thread, 256
+// threads): the lower edge, at 20-bit key precision, of the key bin that
+// holds the k_s-th largest sample; -inf when fewer than k_s samples are
+// valid.  `bins` is 4096 words of LDS.
+__device__ __forceinline__ float row_threshold(const uint32_t (&sk)[8], uint32_t ks, uint32_t* bins, uint32_t* wsum,
+                                               uint32_t* sh) {
+  const int t = threadIdx.x;
+  for (int i = t; i < 4096; i += 256) bins[i] = 0;
+  if (t == 0) { sh[0] = 0xFFFFFFFFu; sh[2] = 0; }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (sk[j]) hist_add(bins, sk[j] >> 20);
+  __syncthreads();
+  // level 1: top 12 key bits; thread t owns bins 16t .. 16t+15
+  uint32_t hb[16], local = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    hb[j] = bins[16 * t + j];
+    local += hb[j];
+  }
+  uint32_t total;
+  const uint32_t incl = block_incl_scan_256(local, wsum, total);
+  uint32_t run = total - incl;  // samples in bins above 16t + 15
+  if (run < ks && run + local >= ks) {
+    for (int j = 15; j >= 0; --j) {
+      if (run + hb[j] >= ks) { sh[0] = 16 * t + j; sh[1] = ks - run; break; }
+      run += hb[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t b1 = sh[0], need = sh[1];
+  if (b1 == 0xFFFFFFFFu || b1 == 0u) return -INFINITY;  // uniform
+  bins[t] = 0;
+  __syncthreads();
+  // level 2: the next 8 bits, over the samples in bin b1
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if ((sk[j] >> 20) == b1) hist_add(bins, (sk[j] >> 12) & 255u);
+  __syncthreads();
+  const uint32_t c = bins[t];
+  uint32_t tot2;
+  const uint32_t incl2 = block_incl_scan_256(c, wsum, tot2);
+  const uint32_t above = tot2 - incl2;  // samples of bin b1 in sub-bins above t
+  if (above < need && above + c >= need) sh[2] = t;
+  __syncthreads();
+  const uint32_t key = (b1 << 20) | (sh[2] << 12);
+  return key_to_score(key);
+}
+
 // ------------------------------------------------------------------ scan
 template <int U>
 __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
@@ -86,29 +372,31 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   if (base >= n_items) return;
   const int64_t end = base + kScanChunk < n_items ? base + kScanChunk : n_items;
 
-  __shared__ uint32_t hist[kHistBins];
-  for (int i = threadIdx.x; i < kHistBins; i += 256) hist[i] = 0;
-
+  __shared__ uint32_t n_hit;
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t sh[3];
+  __shared__ uint32_t bins[4096];
+  if (threadIdx.x == 0) n_hit = 0;
   const int quarter = threadIdx.x & 3;
   half2_t q[kHI][8];
-  const uint8_t* qp = p.idx_q + (int64_t)row * (kHI * kDI) + quarter * 16;
-#pragma unroll
-  for (int h = 0; h < kHI; ++h) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(qp + h * kDI);
-    fp8x4_to_f16(raw.x, q[h][0], q[h][1]);
-    fp8x4_to_f16(raw.y, q[h][2], q[h][3]);
-    fp8x4_to_f16(raw.z, q[h][4], q[h][5]);
-    fp8x4_to_f16(raw.w, q[h][6], q[h][7]);
-  }
   float w[kHI];
-#pragma unroll
-  for (int h = 0; h < kHI; ++h) w[h] = p.idx_w ? p.idx_w[(int64_t)row * kHI + h] : 1.0f;
-  __syncthreads();
+  load_query_f16(p, row, quarter, q, w);
+  int64_t S;
+  uint32_t ks;
+  sample_plan(n_items, (uint32_t)p.k, S, ks);
+  uint32_t sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (ks) {
+    const uint4* sp = reinterpret_cast<const uint4*>(p.samples + (int64_t)row * kSample) + 2 * threadIdx.x;
+    const uint4 v0 = sp[0], v1 = sp[1];
+    sk[0] = v0.x; sk[1] = v0.y; sk[2] = v0.z; sk[3] = v0.w;
+    sk[4] = v1.x; sk[5] = v1.y; sk[6] = v1.z; sk[7] = v1.w;
+  }
+  float T0 = -INFINITY;
 
   const int seq = row / p.n_q;
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + quarter * 16;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
-  uint32_t* so = p.scores + (int64_t)row * p.score_stride;
+  uint64_t* seg = p.seg_list + ((int64_t)row * p.max_chunks + chunk) * kSeg;
   const int sub = threadIdx.x >> 2;  // item within a 64-item step
 
   // U items per lane quad per batch; two batches in flight (double buffer)
@@ -134,38 +422,19 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   auto score = [&](const Batch& B, int64_t it0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float d[kHI] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half2_t lo, hi;
-        fp8x4_to_f16(B.raw[u][j], lo, hi);
-#pragma unroll
-        for (int h = 0; h < kHI; ++h) {
-          d[h] = __builtin_amdgcn_fdot2(q[h][2 * j], lo, d[h], false);
-          d[h] = __builtin_amdgcn_fdot2(q[h][2 * j + 1], hi, d[h], false);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < kHI; ++h) {
-        d[h] += quad_xor1(d[h]);
-        d[h] += quad_xor2(d[h]);
-      }
-      float acc = 0.0f;
-#pragma unroll
-      for (int h = 0; h < kHI; ++h) acc += w[h] * fmaxf(d[h], 0.0f);
-      const float sc = B.ks[u] * acc;
-      const int64_t item = it0 + u * 64 + sub;
-      if (quarter == 0 && item < end) {
-        const uint32_t key = B.valid[u] ? score_key(sc) : 0u;
-        so[item] = key;
-        if (B.valid[u]) atomicAdd(&hist[key >> 20], 1u);
+      const float sc = quad_score(q, w, B.raw[u], B.ks[u]);
+      if (quarter == 0 && B.valid[u] && sc >= T0) {
+        const uint32_t at = atomicAdd(&n_hit, 1u);
+        if (at < (uint32_t)kSeg) seg[at] = select_key(score_key(sc), (uint32_t)(it0 + u * 64 + sub));
       }
     }
   };
   constexpr int kStep = 64 * U;
   Batch A, Bb;
   int64_t it = base;
-  load(A, it);
+  load(A, it);  // in flight while the threshold is worked out
+  if (ks) T0 = row_threshold(sk, ks, bins, wsum, sh);
+  if (chunk == 0 && threadIdx.x == 0) p.thresh[row] = T0;
   while (true) {
     const int64_t nxt = it + kStep;
     if (nxt < end) load(Bb, nxt);
@@ -178,269 +447,226 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
     it = nxt2;
   }
   __syncthreads();
-  uint32_t* gh = p.hist + (int64_t)row * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += 256) {
-    const uint32_t c = hist[i];
-    if (c) atomicAdd(gh + i, c);
-  }
-}
-
-// ------------------------------------------------------------------ threshold
-// Inclusive prefix sum over the 256 threads of a workgroup: shuffles inside
-// each wave, one LDS exchange of the four wave totals.
-__device__ __forceinline__ uint32_t block_incl_scan_256(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < wave; ++i) before += wsum[i];
-  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-  return before + x;
-}
-
-// From a row's 4096-bin histogram (256 threads, 16 bins each): the largest
-// bin T whose count of items at or above it reaches k (0 if fewer than k
-// items exist), and the number of items strictly above T.
-__device__ __forceinline__ void row_threshold(const uint32_t* gh, uint32_t k, uint32_t* wsum,
-                                              uint32_t* sh2, uint32_t& T, uint32_t& above) {
-  const int t = threadIdx.x;
-  const uint4* g4 = reinterpret_cast<const uint4*>(gh) + 4 * t;
-  uint32_t hb[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = g4[i];
-    hb[4 * i] = v.x; hb[4 * i + 1] = v.y; hb[4 * i + 2] = v.z; hb[4 * i + 3] = v.w;
-  }
-  uint32_t local = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) local += hb[j];
-  // items in bins >= 16t = total - (inclusive prefix up to thread t-1)
-  uint32_t total;
-  const uint32_t incl = block_incl_scan_256(local, wsum, total);
-  const uint32_t at_or_above = total - (incl - local);
-  if (t == 0) { sh2[0] = 0; sh2[1] = total; }
-  __syncthreads();
-  uint32_t run = at_or_above - local;  // items in bins above this thread's 16
-  if (run < k && at_or_above >= k) {
-    for (int j = 15; j >= 0; --j) {
-      const uint32_t nrun = run + hb[j];
-      if (nrun >= k) { sh2[0] = 16 * t + j; sh2[1] = run; break; }
-      run = nrun;
-    }
-  }
-  __syncthreads();
-  T = sh2[0];
-  above = sh2[1];  // when T = 0 because fewer than k items exist: all of them
-}
-
-// ------------------------------------------------------------------ filter
-__global__ __launch_bounds__(256) void k_index_filter(IndexPass p, int per_row) {
-  int row, chunk;
-  map_row_chunk(p.rows, per_row, row, chunk);
-  if (row >= p.rows) return;
-  const int64_t vis = row_vis_positions(p, row);
-  const int64_t n_items = row_items(p, row, vis);
-  const int64_t base = (int64_t)chunk * kFilterChunk;
-  if (base >= n_items) return;
-
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t sh2[2];
-  const int t = threadIdx.x;
-  uint32_t T, above;
-  row_threshold(p.hist + (int64_t)row * kHistBins, (uint32_t)p.k, wsum, sh2, T, above);
-
-  // each thread compacts 32 consecutive items, in item order
-  const uint32_t* so = p.scores + (int64_t)row * p.score_stride;
-  uint32_t keys[32];
-  const int64_t i0 = base + 32 * t;
-#pragma unroll
-  for (int j = 0; j < 32; j += 4) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (i0 + j < n_items) v = *reinterpret_cast<const uint4*>(so + i0 + j);
-    keys[j] = v.x; keys[j + 1] = v.y; keys[j + 2] = v.z; keys[j + 3] = v.w;
-  }
-  uint32_t flags = 0;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const bool f = (i0 + j < n_items) && keys[j] != 0u && (keys[j] >> 20) >= T;
-    flags |= (uint32_t)f << j;
-  }
-  const uint32_t c = __builtin_popcount(flags);
-  uint32_t total;
-  uint32_t off = block_incl_scan_256(c, wsum, total) - c;
-  uint64_t* co = p.cand + (int64_t)row * p.score_stride + base;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    if (flags & (1u << j)) co[off++] = select_key(keys[j], (uint32_t)(i0 + j));
-  }
-  if (t == 0) p.fcount[(int64_t)row * p.max_fchunks + chunk] = total;
+  if (threadIdx.x == 0) p.seg_count[(int64_t)row * p.max_chunks + chunk] = n_hit;
 }
 
 // ------------------------------------------------------------------ select
-constexpr int kRankMax = 2048;  // threshold-bin candidates kept in LDS for the radix steps
-
 __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   const int row = blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, quarter = t & 3;
+  const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
-  const int nf = (int)((n_items + kFilterChunk - 1) / kFilterChunk);
+  const int nch = (int)((n_items + kScanChunk - 1) / kScanChunk);
+  const uint32_t k = (uint32_t)p.k;
+  const float T0 = n_items > 0 ? p.thresh[row] : -INFINITY;  // written by the row's first scan chunk
 
-  __shared__ uint32_t off[kMaxFChunks + 1];
-  __shared__ uint64_t lc[kSelectLds];
-  __shared__ uint64_t bt[kRankMax];
+  __shared__ uint32_t seg_start[kMaxChunks + 1];
+  __shared__ uint64_t lc[kSelCap];
+  __shared__ uint32_t bitmap[kBitmapItems / 32];
+  __shared__ uint32_t win[CSA2_MAX_K];
   __shared__ uint32_t h256[256];
+  __shared__ uint32_t h2048[2048];
   __shared__ uint32_t wsum[4];
-  __shared__ uint32_t sh2[2];
+  __shared__ uint32_t sh3[3];
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need;
 
-  // chunk offsets: thread t owns chunks 4t .. 4t+3
-  uint32_t cnt[4], local = 0;
+  // segment counts: thread t owns chunks 16t .. 16t+15
+  const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
+  uint32_t c[16], local = 0;
+  bool over = false;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int f = 4 * t + j;
-    cnt[j] = f < nf ? p.fcount[(int64_t)row * p.max_fchunks + f] : 0u;
-    local += cnt[j];
+  for (int j = 0; j < 16; ++j) {
+    const int ch = 16 * t + j;
+    c[j] = ch < nch ? cnt_row[ch] : 0u;
+    over |= c[j] > (uint32_t)kSeg;
+    local += c[j];
   }
+  over = __syncthreads_or(over);
   uint32_t total;
   uint32_t run = block_incl_scan_256(local, wsum, total) - local;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int f = 4 * t + j;
-    if (f <= nf) off[f] = run;
-    run += cnt[j];
+  for (int j = 0; j < 16; ++j) {
+    const int ch = 16 * t + j;
+    if (ch < nch) seg_start[ch] = run;
+    run += c[j];
   }
+  if (t == 0) seg_start[nch] = total;
   __syncthreads();
 
-  uint32_t T, above;
-  row_threshold(p.hist + (int64_t)row * kHistBins, (uint32_t)p.k, wsum, sh2, T, above);
-
-  const uint64_t* cbase = p.cand + (int64_t)row * p.score_stride;
-  const bool in_lds = total <= (uint32_t)kSelectLds;
-  auto fetch = [&](uint32_t g) -> uint64_t {
-    int lo = 0, hi = nf - 1;  // last chunk f with off[f] <= g
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= g) lo = mid; else hi = mid - 1;
+  const bool fast = !over && total <= (uint32_t)kSelCap && (total >= k || T0 == -INFINITY);
+  uint32_t n_win = 0;
+  if (fast) {
+    const bool use_bitmap = n_items <= (int64_t)kBitmapItems;
+    if (use_bitmap) {
+      uint4* bm4 = reinterpret_cast<uint4*>(bitmap);
+      for (int i = t; i < kBitmapItems / 128; i += 256) bm4[i] = make_uint4(0, 0, 0, 0);
     }
-    return cbase[(int64_t)lo * kFilterChunk + (g - off[lo])];
-  };
-  if (in_lds) {
-    for (uint32_t g = t; g < total; g += 256) lc[g] = fetch(g);
-  }
-  __syncthreads();
-  auto get = [&](uint32_t g) -> uint64_t { return in_lds ? lc[g] : fetch(g); };
-
-  // kth = the k-th largest candidate key (keys are unique); 0 selects all.
-  // Radix steps over the key bits below the threshold bin: 8-bit digits at
-  // shifts 44, 36, .., 4, then the last 4 bits.  In the common case the
-  // threshold-bin keys are first compacted into LDS; otherwise every
-  // candidate is visited through `get` (still exact, slower).
-  const uint32_t k = (uint32_t)p.k;
-  uint64_t kth = 0;
-  if (total > k) {
-    const uint32_t m = total - above;      // candidates in the threshold bin
-    const bool use_bt = in_lds && m <= (uint32_t)kRankMax;
-    if (use_bt) {
-      uint32_t base_out = 0;
-      for (uint32_t g0 = 0; g0 < total; g0 += 256) {
-        const uint32_t g = g0 + t;
-        const uint64_t key = g < total ? lc[g] : 0ull;
-        const bool f = g < total && (uint32_t)(key >> 52) == T;
-        uint32_t n_round;
-        const uint32_t o = block_incl_scan_256(f ? 1u : 0u, wsum, n_round) - (f ? 1u : 0u);
-        if (f) bt[base_out + o] = key;
-        base_out += n_round;
-      }
-    }
-    const uint32_t n_keys = use_bt ? m : total;
-    if (t == 0) { sh_kth = (uint64_t)T << 52; sh_need = k - above; }
-    for (int shift = 44; shift >= 0; shift -= (shift == 4 ? 4 : 8)) {
-      const int nb = shift == 0 ? 4 : 8;
-      h256[t] = 0;
-      __syncthreads();
-      const uint64_t prefix = sh_kth;
-      const uint64_t hmask = ~0ull << (shift + nb);
-      const uint32_t dmask = (1u << nb) - 1u;
-      for (uint32_t g = t; g < n_keys; g += 256) {
-        const uint64_t key = use_bt ? bt[g] : get(g);
-        if ((key & hmask) == prefix) atomicAdd(&h256[(key >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      if (t < 64) {  // one wave: suffix sums over 256 digits, 4 per lane
-        const uint32_t nd = sh_need;
-        const uint32_t c0 = h256[4 * t], c1 = h256[4 * t + 1], c2 = h256[4 * t + 2], c3 = h256[4 * t + 3];
-        const uint32_t mine = c0 + c1 + c2 + c3;
-        uint32_t x = mine;  // inclusive suffix over lanes t..63
+    // gather the segments: wave w copies chunks w, w + 4, ..., eight chunks
+    // (up to 16 independent loads per lane) at a time
+    const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
+    const int wave = t >> 6, lane = t & 63;
+    for (int c0 = wave; c0 < nch; c0 += 32) {
+      uint64_t v[8][2];
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t y = __shfl_down(x, d, 64);
-          if (t + d < 64) x += y;
+      for (int j = 0; j < 8; ++j) {
+        const int ch = c0 + 4 * j;
+        const uint32_t n = ch < nch ? seg_start[ch + 1] - seg_start[ch] : 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t i = lane + 64 * h;
+          v[j][h] = i < n ? segs[(int64_t)ch * kSeg + i] : 0ull;
         }
-        uint32_t ab = x - mine;
-        const uint32_t cs[4] = {c0, c1, c2, c3};
-        for (int j = 3; j >= 0; --j) {
-          if (ab < nd && ab + cs[j] >= nd) {
-            sh_need = nd - ab;
-            sh_kth = prefix | ((uint64_t)(4 * t + j) << shift);
-          }
-          ab += cs[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ch = c0 + 4 * j;
+        const uint32_t n = ch < nch ? seg_start[ch + 1] - seg_start[ch] : 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t i = lane + 64 * h;
+          if (i < n) lc[seg_start[ch] + i] = v[j][h];
+        }
+      }
+    }
+    __syncthreads();
+    // candidates into registers: thread t holds lc[t + 256 i]
+    constexpr int kPer = kSelCap / 256;
+    uint64_t key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t g = t + 256 * i;
+      key[i] = g < total ? lc[g] : 0ull;  // 0 is below every candidate key
+    }
+    const uint64_t kth = total > k ? block_kth_regs<kPer>(key, k, h2048, wsum, sh3) : 1ull;
+    // winners: every candidate key >= kth
+    if (t == 0) sh_need = 0;
+    __syncthreads();
+    if (use_bitmap) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (key[i] >= kth) {
+          const uint32_t it = select_key_pos(key[i]);
+          atomicOr(&bitmap[it >> 5], 1u << (it & 31u));
+        }
+      __syncthreads();
+      // thread t owns words 16t .. 16t+15 (512 items)
+      const uint32_t nwords = (uint32_t)((n_items + 31) / 32);
+      uint32_t wb[16], cnt_t = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t wi = 16 * t + j;
+        wb[j] = wi < nwords ? bitmap[wi] : 0u;
+        cnt_t += __builtin_popcount(wb[j]);
+      }
+      uint32_t tot;
+      uint32_t o = block_incl_scan_256(cnt_t, wsum, tot) - cnt_t;
+      n_win = tot;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        uint32_t bits = wb[j];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          win[o++] = (16 * t + j) * 32 + b;
+          bits &= bits - 1;
         }
       }
       __syncthreads();
-      if (shift == 0) break;
+    } else {
+      // compaction, then a bitonic sort padded to a power of two
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (key[i] >= kth) win[atomicAdd(&sh_need, 1u)] = select_key_pos(key[i]);
+      __syncthreads();
+      n_win = sh_need;
+      uint32_t n2 = 1;
+      while (n2 < n_win) n2 <<= 1;
+      for (uint32_t i = n_win + t; i < n2; i += 256) win[i] = 0xFFFFFFFFu;
+      __syncthreads();
+      for (uint32_t size = 2; size <= n2; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+          for (uint32_t i = t; i < n2 / 2; i += 256) {
+            const uint32_t lo = 2 * i - (i & (stride - 1));
+            const uint32_t hi = lo + stride;
+            const bool asc = (lo & size) == 0;
+            const uint32_t a = win[lo], b = win[hi];
+            if ((a > b) == asc) { win[lo] = b; win[hi] = a; }
+          }
+          __syncthreads();
+        }
+      }
     }
-    kth = sh_kth;
+  } else {
+    // exact recompute of this row (rare): radix steps over recomputed keys
+    half2_t q[kHI][8];
+    float w[kHI];
+    load_query_f16(p, row, quarter, q, w);
+    auto visit = [&](uint32_t n, auto&& f) {
+      for (uint32_t base = 0; base < n; base += 64) {
+        const uint32_t item = base + (t >> 2);
+        bool valid = false;
+        const int64_t pos = item < n ? item_position(p, row, item, n, vis, valid) : 0;
+        const float sc = quad_score_at(p, q, w, seq, quarter, pos, valid);
+        if (valid && quarter == 0) f(select_key(score_key(sc), item));
+      }
+    };
+    const uint32_t ni = (uint32_t)n_items;
+    uint64_t kth = 0;
+    // winners must be valid items: count them first
+    uint32_t n_valid = 0;
+    {
+      uint32_t mine = 0;
+      for (uint32_t base = 0; base < ni; base += 64) {
+        const uint32_t item = base + (t >> 2);
+        bool valid = false;
+        if (item < ni && quarter == 0) (void)item_position(p, row, item, ni, vis, valid);
+        mine += valid ? 1u : 0u;
+      }
+      (void)block_incl_scan_256(mine, wsum, n_valid);
+    }
+    if (n_valid > k) kth = radix_kth<uint64_t>(visit, ni, k, h256, &sh_kth, &sh_need);
+    for (uint32_t base = 0; base < ni; base += 64) {
+      const uint32_t item = base + (t >> 2);
+      bool valid = false;
+      const int64_t pos = item < ni ? item_position(p, row, item, ni, vis, valid) : 0;
+      const float sc = quad_score_at(p, q, w, seq, quarter, pos, valid);
+      const bool f = valid && quarter == 0 && select_key(score_key(sc), item) >= kth;
+      uint32_t nr;
+      const uint32_t o = block_incl_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
+      if (f && n_win + o < (uint32_t)CSA2_MAX_K) win[n_win + o] = item;
+      n_win += nr;
+    }
+    if (n_win > k) n_win = k;
+    __syncthreads();
   }
 
-  // winners (key >= kth) in item order
+  // positions of the winners, in ascending order
   const int32_t* blocks = p.blocks;
-  uint32_t written = 0;
-  for (uint32_t g0 = 0; g0 < total; g0 += 256) {
-    const uint32_t g = g0 + t;
-    uint64_t key = 0;
-    bool f = false;
-    if (g < total) { key = get(g); f = key >= kth; }
-    uint32_t n_round;
-    const uint32_t o = written + block_incl_scan_256(f ? 1u : 0u, wsum, n_round) - (f ? 1u : 0u);
-    if (f) {
-      const uint32_t item = select_key_pos(key);
-      int32_t val;
-      if (p.source == kItemsDirect) val = (int32_t)item;
-      else if (p.source == kItemsBlocks)
-        val = 8 * blocks[(int64_t)row * CSA2_MAX_K + (item >> 3)] + (int32_t)(item & 7u);
-      else val = p.list[(int64_t)row * p.list_len + item];
-      p.out[(int64_t)row * p.out_stride + o] = val;
-    }
-    written += n_round;
+  for (uint32_t j = t; j < n_win; j += 256) {
+    const uint32_t item = win[j];
+    int32_t val;
+    if (p.source == kItemsDirect) val = (int32_t)item;
+    else if (p.source == kItemsBlocks)
+      val = 8 * blocks[(int64_t)row * CSA2_MAX_K + (item >> 3)] + (int32_t)(item & 7u);
+    else val = p.list[(int64_t)row * p.list_len + item];
+    p.out[(int64_t)row * p.out_stride + j] = val;
   }
-  // pad, counts, pool, and reset the histogram for the next pass
   if (!p.block_level) {
-    for (uint32_t j = written + t; j < k; j += 256) p.out[(int64_t)row * p.out_stride + j] = -1;
+    for (uint32_t j = n_win + t; j < k; j += 256) p.out[(int64_t)row * p.out_stride + j] = -1;
   }
-  if (p.out_count && t == 0) p.out_count[row] = (int32_t)written;
+  if (p.out_count && t == 0) p.out_count[row] = (int32_t)n_win;
   if (p.out_pool) {
-    __syncthreads();  // block ids written above are read back here
     const int32_t total_pool = CSA2_N_BLOCKS * CSA2_BLOCK;
     for (int32_t j = t; j < p.pool_stride && j < total_pool; j += 256) {
       int32_t v = -1;
-      if ((uint32_t)(j >> 3) < written) {
-        const int64_t pos = 8 * (int64_t)p.out[(int64_t)row * p.out_stride + (j >> 3)] + (j & 7);
+      if ((uint32_t)(j >> 3) < n_win) {
+        const int64_t pos = 8 * (int64_t)win[j >> 3] + (j & 7);
         if (pos < vis) v = (int32_t)pos;
       }
       p.out_pool[(int64_t)row * p.pool_stride + j] = v;
     }
   }
-  uint4* gh = reinterpret_cast<uint4*>(p.hist + (int64_t)row * kHistBins);
-  for (int i = t; i < kHistBins / 4; i += 256) gh[i] = make_uint4(0, 0, 0, 0);
 }
 
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
@@ -460,17 +686,15 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream
 hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   if (p.rows == 0 || p.max_items == 0) return hipSuccess;
   const int scan_per_row = (int)((p.max_items + kScanChunk - 1) / kScanChunk);
-  const int filt_per_row = (int)((p.max_items + kFilterChunk - 1) / kFilterChunk);
   const int gr = grid_rows(p.rows);
-  int h = prof_begin(CSA2_K_INDEX_SCAN, stream);
-  hipLaunchKernelGGL(k_index_scan<4>, dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
-                     scan_per_row);
+  int h = prof_begin(CSA2_K_INDEX_SAMPLE, stream);
+  hipLaunchKernelGGL(k_index_sample, dim3((unsigned)(p.rows * kSampleSplit)), dim3(256), 0, stream, p);
   prof_end(h, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  h = prof_begin(CSA2_K_INDEX_FILTER, stream);
-  hipLaunchKernelGGL(k_index_filter, dim3((unsigned)(gr * filt_per_row)), dim3(256), 0, stream, p,
-                     filt_per_row);
+  h = prof_begin(CSA2_K_INDEX_SCAN, stream);
+  hipLaunchKernelGGL(k_index_scan<4>, dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
+                     scan_per_row);
   prof_end(h, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -13,11 +13,12 @@ struct SeqArgs {
   int64_t b[kMaxSeqPerLaunch];
 };
 
-// Items scored per workgroup of the indexer scan, and per filter workgroup.
+// Items scored per workgroup of the indexer scan; candidates kept per
+// (row, chunk) segment; chunks per row (items per row <= 8M).
 constexpr int kScanChunk = 2048;
-constexpr int kFilterChunk = 8192;
+constexpr int kSeg = 128;
+constexpr int kMaxChunks = 4096;
 constexpr int kMaxPool = CSA2_N_BLOCKS * CSA2_BLOCK;  // 16,384 positions
-constexpr int kMaxFChunks = 1024;                     // filter chunks per row: <= 8M items
 
 // Where the items of an indexer pass come from.
 enum ItemSource : int32_t {
@@ -43,13 +44,12 @@ struct IndexPass {
   const int32_t* nsel;         // kItemsBlocks: [rows] number of selected blocks
   int64_t max_items;           // items per row the grid covers
   // workspace
-  uint32_t* hist;              // [rows][kHistBins], zero on entry, zero on exit
-  uint32_t* scores;            // [rows][score_stride]
-  int64_t score_stride;
-  uint64_t* cand;              // [rows][score_stride]
-  uint32_t* fcount;            // [rows][max_fchunks]
-  int32_t max_fchunks;
-  // output: either positions (out_idx, -1 padded to k) or block ids + count
+  uint32_t* samples;           // [rows][2048] order keys of the sampled items
+  float* thresh;               // [rows] sampled threshold
+  uint32_t* seg_count;         // [rows][max_chunks]
+  uint64_t* seg_list;          // [rows][max_chunks][kSeg]
+  int32_t max_chunks;
+  // output: either positions (out, -1 padded to k) or block ids + count
   int32_t* out;                // [rows][out_stride]
   int32_t out_stride;
   int32_t* out_count;          // [rows] or null

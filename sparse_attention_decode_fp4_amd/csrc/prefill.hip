@@ -45,7 +45,7 @@ __device__ __forceinline__ int64_t pf_visible(const PrefillPass& p, int seq, int
 // Samples of a row tile: S = min(V, kPfSample) keys j(t) = t*V/S, V being the
 // visible count of the tile's first query (the smallest of the tile).
 __device__ __forceinline__ int64_t pf_sample_key(int64_t t, int64_t V, int64_t S) {
-  return S == V ? t : (t * V) / S;
+  return S == V ? t : (t * V) / kPfSample;  // S == kPfSample whenever strided
 }
 
 __device__ __forceinline__ float key_to_score(uint32_t key) {
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void k_prefill_threshold(PrefillPass p) {
 #pragma unroll
     for (int j = 0; j < kPfSample / 64; ++j) {
       const int64_t s = (int64_t)j * 64 + lane;
-      if (s < S && (keys[j] & hmask) == prefix) atomicAdd(&hist[wave][(keys[j] >> shift) & 255u], 1u);
+      if (s < S && (keys[j] & hmask) == prefix) hist_add(hist[wave], (keys[j] >> shift) & 255u);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
       const uint64_t hmask = (shift == 56) ? 0ull : (~0ull << (shift + 8));
       get(n, [&](uint32_t g, uint64_t key) {
         (void)g;
-        if ((key & hmask) == prefix) atomicAdd(&h256[(key >> shift) & 255u], 1u);
+        if ((key & hmask) == prefix) hist_add(h256, (uint32_t)(key >> shift) & 255u);
       });
       __syncthreads();
       if (t < 64) {
