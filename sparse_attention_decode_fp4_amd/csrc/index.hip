@@ -8,11 +8,10 @@
 //
 // One pass = three kernels over the rows (query rows) of a call:
 //   sample  eight workgroups per row score a strided sample of at most 2,048
-//           of its items and store their order keys; each scan workgroup
-//           derives the row threshold T0 from them: the lower edge, at 20
-//           key bits, of the bin holding the k_s-th largest sample, k_s sized
-//           so that about 2.5 k items of the row reach T0 (every item when
-//           the sample is the whole row);
+//           of its items; the last to finish sets the row threshold T0: the
+//           lower edge, at 20 key bits, of the key bin holding the k_s-th
+//           largest sample, k_s sized so that about 2.5 k items of the row
+//           reach T0 (every item when the sample is the whole row);
 //   scan    streams the fp8 keys once (4 lanes per key, 16 B each, fully
 //           coalesced), scores every item with packed f16 dot products
 //           (v_dot2c_f32_f16; fp8 -> f16 is exact) and appends the items
@@ -90,60 +89,88 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
 }
 
 // Query of a row as packed f16, 16 channels of each head per lane of a quad.
-__device__ __forceinline__ void load_query_f16(const IndexPass& p, int row, int quarter, half2_t (&q)[kHI][8],
-                                               float (&w)[kHI]) {
-  const uint8_t* qp = p.idx_q + (int64_t)row * (kHI * kDI) + quarter * 16;
-#pragma unroll
-  for (int h = 0; h < kHI; ++h) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(qp + h * kDI);
-    fp8x4_to_f16(raw.x, q[h][0], q[h][1]);
-    fp8x4_to_f16(raw.y, q[h][2], q[h][3]);
-    fp8x4_to_f16(raw.z, q[h][4], q[h][5]);
-    fp8x4_to_f16(raw.w, q[h][6], q[h][7]);
-  }
-#pragma unroll
-  for (int h = 0; h < kHI; ++h) w[h] = p.idx_w ? p.idx_w[(int64_t)row * kHI + h] : 1.0f;
+// Query of a row as packed f16, 16 channels of each head per lane of a quad.
+// Lane j of a quad (bits b1 b0) keeps head (s ^ 2 b0 ^ b1) in slot s, so the
+// quad reduction in quad_score needs three cross-lane adds instead of eight;
+// `w_mine` is the weight of head 2 b0 ^ b1, the head the lane ends up with.
+__device__ __forceinline__ int quad_head(int slot, int quarter) {
+  return slot ^ ((quarter & 1) << 1) ^ (quarter >> 1);
 }
 
-// Score of one key from its 16 bytes in this lane (a lane quad holds the key).
-__device__ __forceinline__ float quad_score(const half2_t (&q)[kHI][8], const float (&w)[kHI], u32x4_t raw,
-                                            float ks) {
+__device__ __forceinline__ void load_query_f16(const IndexPass& p, int row, int quarter, half2_t (&q)[kHI][8],
+                                               float& w_mine) {
+  const uint8_t* qp = p.idx_q + (int64_t)row * (kHI * kDI) + quarter * 16;
+#pragma unroll
+  for (int s = 0; s < kHI; ++s) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(qp + quad_head(s, quarter) * kDI);
+    fp8x4_to_f16(raw.x, q[s][0], q[s][1]);
+    fp8x4_to_f16(raw.y, q[s][2], q[s][3]);
+    fp8x4_to_f16(raw.z, q[s][4], q[s][5]);
+    fp8x4_to_f16(raw.w, q[s][6], q[s][7]);
+  }
+  w_mine = p.idx_w ? p.idx_w[(int64_t)row * kHI + quad_head(0, quarter)] : 1.0f;
+}
+
+// Score of one key from its 16 bytes in this lane (a lane quad holds the
+// key); every lane of the quad returns it.
+__device__ __forceinline__ float quad_score(const half2_t (&q)[kHI][8], float w_mine, u32x4_t raw, float ks) {
   float d[kHI] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     half2_t lo, hi;
     fp8x4_to_f16(raw[j], lo, hi);
 #pragma unroll
-    for (int h = 0; h < kHI; ++h) {
-      d[h] = __builtin_amdgcn_fdot2(q[h][2 * j], lo, d[h], false);
-      d[h] = __builtin_amdgcn_fdot2(q[h][2 * j + 1], hi, d[h], false);
+    for (int s = 0; s < kHI; ++s) {
+      d[s] = __builtin_amdgcn_fdot2(q[s][2 * j], lo, d[s], false);
+      d[s] = __builtin_amdgcn_fdot2(q[s][2 * j + 1], hi, d[s], false);
     }
   }
-#pragma unroll
-  for (int h = 0; h < kHI; ++h) {
-    d[h] += quad_xor1(d[h]);
-    d[h] += quad_xor2(d[h]);
-  }
-  float acc = 0.0f;
-#pragma unroll
-  for (int h = 0; h < kHI; ++h) acc += w[h] * fmaxf(d[h], 0.0f);
-  return ks * acc;
+  // slot s of the partner lane (lane ^ 1) holds head (s ^ 2) of this lane,
+  // and slot 1 of lane ^ 2 the head of slot 0 here
+  const float e0 = d[0] + quad_xor1(d[2]);
+  const float e1 = d[1] + quad_xor1(d[3]);
+  const float f = e0 + quad_xor2(e1);  // full dot product of head quad_head(0, lane)
+  float v = w_mine * fmaxf(f, 0.0f);
+  v += quad_xor1(v);
+  v += quad_xor2(v);
+  return ks * v;
 }
 
-__device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t (&q)[kHI][8],
-                                               const float (&w)[kHI], int seq, int quarter, int64_t pos,
-                                               bool valid) {
+__device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t (&q)[kHI][8], float w_mine,
+                                               int seq, int quarter, int64_t pos, bool valid) {
   u32x4_t raw = u32x4_t{0, 0, 0, 0};
   float ks = 0.0f;
   if (valid) {
     raw = *reinterpret_cast<const u32x4_t*>(p.k8 + ((int64_t)seq * p.k_stride + pos) * kDI + quarter * 16);
     ks = p.kscale[(int64_t)seq * p.k_stride + pos];
   }
-  return quad_score(q, w, raw, ks);
+  return quad_score(q, w_mine, raw, ks);
 }
 
-// Inclusive prefix sum over the 256 threads of a workgroup: shuffles inside
-// each wave, one LDS exchange of the four wave totals.
+// Inclusive prefix sum over the NW waves of a workgroup: shuffles inside
+// each wave, one LDS exchange of the wave totals.
+template <int NW>
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    before += i < wave ? wsum[i] : 0u;
+    all += wsum[i];
+  }
+  total = all;
+  __syncthreads();
+  return before + x;
+}
+
 __device__ __forceinline__ uint32_t block_incl_scan_256(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -271,45 +298,6 @@ __device__ __forceinline__ void sample_plan(int64_t n_items, uint32_t k, int64_t
   }
 }
 
-// kSampleSplit workgroups per row each score kSample / kSampleSplit of the
-// row's strided sample and store the order keys (0 for an empty slot).
-constexpr int kSampleSplit = 8;
-__global__ __launch_bounds__(256) void k_index_sample(IndexPass p) {
-  const int row = blockIdx.x / kSampleSplit, part = blockIdx.x % kSampleSplit;
-  const int t = threadIdx.x, quarter = t & 3;
-  const int seq = row / p.n_q;
-  const int64_t vis = row_vis_positions(p, row);
-  const int64_t n_items = row_items(p, row, vis);
-  int64_t S;
-  uint32_t ks;
-  sample_plan(n_items, (uint32_t)p.k, S, ks);
-  if (ks == 0) return;
-  half2_t q[kHI][8];
-  float w[kHI];
-  load_query_f16(p, row, quarter, q, w);
-  constexpr int U = kSample / kSampleSplit / 64;  // items per lane quad
-  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + quarter * 16;
-  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
-  u32x4_t raw[U];
-  float kv[U];
-  bool valid[U];
-  int64_t slot[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    slot[u] = (int64_t)part * (kSample / kSampleSplit) + u * 64 + (t >> 2);
-    // S == kSample (a power of two) whenever the sample is strided
-    const int64_t item = slot[u] < S ? (S == n_items ? slot[u] : (slot[u] * n_items) / kSample) : n_items;
-    const int64_t pos = item_position(p, row, item, n_items, vis, valid[u]);
-    raw[u] = valid[u] ? *reinterpret_cast<const u32x4_t*>(kb + pos * kDI) : u32x4_t{0, 0, 0, 0};
-    kv[u] = valid[u] ? sb[pos] : 0.0f;
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const float sc = quad_score(q, w, raw[u], kv[u]);
-    if (quarter == 0) p.samples[(int64_t)row * kSample + slot[u]] = valid[u] ? score_key(sc) : 0u;
-  }
-}
-
 // Row threshold T0 from the row's sample keys `sk` (8 per thread, 256
 // threads): the lower edge, at 20-bit key precision, of the key bin that
 // holds the k_s-th largest sample; -inf when fewer than k_s samples are
@@ -322,7 +310,7 @@ __device__ __forceinline__ float row_threshold(const uint32_t (&sk)[8], uint32_t
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (sk[j]) hist_add(bins, sk[j] >> 20);
+    if (sk[j]) atomicAdd(&bins[sk[j] >> 20], 1u);
   __syncthreads();
   // level 1: top 12 key bits; thread t owns bins 16t .. 16t+15
   uint32_t hb[16], local = 0;
@@ -348,7 +336,7 @@ __device__ __forceinline__ float row_threshold(const uint32_t (&sk)[8], uint32_t
   // level 2: the next 8 bits, over the samples in bin b1
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if ((sk[j] >> 20) == b1) hist_add(bins, (sk[j] >> 12) & 255u);
+    if ((sk[j] >> 20) == b1) atomicAdd(&bins[(sk[j] >> 12) & 255u], 1u);
   __syncthreads();
   const uint32_t c = bins[t];
   uint32_t tot2;
@@ -360,8 +348,88 @@ __device__ __forceinline__ float row_threshold(const uint32_t (&sk)[8], uint32_t
   return key_to_score(key);
 }
 
+
+// kSampleSplit workgroups per row each score kSample / kSampleSplit items
+// of the row's strided sample (loads issued together) and store their order
+// keys; the last of them to finish (a ticket counter per row, zero between
+// passes: the last workgroup resets it) turns the 2,048 keys into the row
+// threshold T0.  T0 = -inf when there is no sample plan.  Keys and tickets
+// travel as relaxed device-scope atomics, without fences (which would write
+// back and invalidate the L2): a key read early only moves T0, and the
+// select kernel checks that at least k candidates reached T0 before it
+// trusts them, so results never depend on this ordering.
+constexpr int kSampleSplit = 8;
+__global__ __launch_bounds__(256) void k_index_sample(IndexPass p) {
+  const int row = blockIdx.x / kSampleSplit, part = blockIdx.x % kSampleSplit;
+  const int t = threadIdx.x, quarter = t & 3;
+  const int seq = row / p.n_q;
+  const int64_t vis = row_vis_positions(p, row);
+  const int64_t n_items = row_items(p, row, vis);
+  int64_t S;
+  uint32_t ks;
+  sample_plan(n_items, (uint32_t)p.k, S, ks);
+  if (ks == 0) {
+    if (part == 0 && t == 0) p.thresh[row] = -INFINITY;
+    return;
+  }
+  __shared__ uint32_t bins[4096];
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t sh[3];
+  __shared__ uint32_t ticket;
+
+  half2_t q[kHI][8];
+  float w_mine;
+  load_query_f16(p, row, quarter, q, w_mine);
+  constexpr int U = kSample / kSampleSplit / 64;  // items per lane quad
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + quarter * 16;
+  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
+  uint32_t* keys = p.samples + (int64_t)row * kSample;
+  u32x4_t raw[U];
+  float kv[U];
+  bool valid[U];
+  int slot[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    slot[u] = part * (kSample / kSampleSplit) + u * 64 + (t >> 2);
+    // S == kSample (a power of two) whenever the sample is strided
+    const int64_t item = slot[u] < S ? (S == n_items ? slot[u] : ((int64_t)slot[u] * n_items) / kSample) : n_items;
+    const int64_t pos = item_position(p, row, item, n_items, vis, valid[u]);
+    raw[u] = valid[u] ? *reinterpret_cast<const u32x4_t*>(kb + pos * kDI) : u32x4_t{0, 0, 0, 0};
+    kv[u] = valid[u] ? sb[pos] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float sc = quad_score(q, w_mine, raw[u], kv[u]);
+    if (quarter == 0)
+      __hip_atomic_store(keys + slot[u], valid[u] ? score_key(sc) : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's key stores have completed
+  __syncthreads();
+  if (t == 0) ticket = __hip_atomic_fetch_add(p.sample_done + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (ticket % kSampleSplit != kSampleSplit - 1) return;
+  // last workgroup of the row: thread t takes keys 8t .. 8t+7
+  uint32_t sk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sk[j] = __hip_atomic_load(keys + 8 * t + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float T0 = row_threshold(sk, ks, bins, wsum, sh);
+  if (t == 0) {
+    p.thresh[row] = T0;
+    p.sample_done[row] = 0;  // every workgroup of the row has taken its ticket
+  }
+}
+
 // ------------------------------------------------------------------ scan
-template <int U>
+// Buffer descriptor word 3 for untyped (raw) buffer access on gfx9 parts.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kLoadNonTemporal = 2;  // cache-policy bit of raw buffer loads
+
+// Workgroup (row, chunk of kScanChunk items).  kDirect: item i is position
+// i (flat keys or block keys); keys and scales are read through buffer
+// descriptors whose range ends at the chunk's last item, so the hardware
+// returns zeros past it and the loads need no bounds branches.  Otherwise
+// positions come from a block or position list.
+template <int U, bool kDirect>
 __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   int row, chunk;
   map_row_chunk(p.rows, per_row, row, chunk);
@@ -373,68 +441,70 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   const int64_t end = base + kScanChunk < n_items ? base + kScanChunk : n_items;
 
   __shared__ uint32_t n_hit;
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t sh[3];
-  __shared__ uint32_t bins[4096];
   if (threadIdx.x == 0) n_hit = 0;
   const int quarter = threadIdx.x & 3;
-  half2_t q[kHI][8];
-  float w[kHI];
-  load_query_f16(p, row, quarter, q, w);
-  int64_t S;
-  uint32_t ks;
-  sample_plan(n_items, (uint32_t)p.k, S, ks);
-  uint32_t sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (ks) {
-    const uint4* sp = reinterpret_cast<const uint4*>(p.samples + (int64_t)row * kSample) + 2 * threadIdx.x;
-    const uint4 v0 = sp[0], v1 = sp[1];
-    sk[0] = v0.x; sk[1] = v0.y; sk[2] = v0.z; sk[3] = v0.w;
-    sk[4] = v1.x; sk[5] = v1.y; sk[6] = v1.z; sk[7] = v1.w;
-  }
-  float T0 = -INFINITY;
-
-  const int seq = row / p.n_q;
-  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + quarter * 16;
-  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
-  uint64_t* seg = p.seg_list + ((int64_t)row * p.max_chunks + chunk) * kSeg;
   const int sub = threadIdx.x >> 2;  // item within a 64-item step
+  const int seq = row / p.n_q;
+  half2_t q[kHI][8];
+  float w_mine;
+  load_query_f16(p, row, quarter, q, w_mine);
+  const float T0 = p.thresh[row];
+  uint64_t* seg = p.seg_list + ((int64_t)row * p.max_chunks + chunk) * kSeg;
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
+  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
+  // (used by the kDirect loads only)
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, (int)(end * kDI), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)sb, 0, (int)(end * 4), kRawBufferWord3);
 
   // U items per lane quad per batch; two batches in flight (double buffer)
   struct Batch {
     u32x4_t raw[U];
     float ks[U];
-    bool valid[U];
   };
   auto load = [&](Batch& B, int64_t it0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t item = it0 + u * 64 + sub;
-      const int64_t pos = item_position(p, row, item, end, vis, B.valid[u]);
-      if (B.valid[u]) {
-        B.raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + pos * kDI));
-        B.ks[u] = sb[pos];
+      if constexpr (kDirect) {
+        B.raw[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(item * kDI) + quarter * 16, 0, kLoadNonTemporal);
+        B.ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(item * 4), 0, 0));
       } else {
-        B.raw[u] = u32x4_t{0, 0, 0, 0};
-        B.ks[u] = 0.0f;
+        bool valid;
+        const int64_t pos = item_position(p, row, item, end, vis, valid);
+        if (valid) {
+          B.raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + pos * kDI + quarter * 16));
+          B.ks[u] = sb[pos];
+        } else {
+          B.raw[u] = u32x4_t{0, 0, 0, 0};
+          B.ks[u] = 0.0f;
+        }
       }
     }
   };
   auto score = [&](const Batch& B, int64_t it0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float sc = quad_score(q, w, B.raw[u], B.ks[u]);
-      if (quarter == 0 && B.valid[u] && sc >= T0) {
+      const float sc = quad_score(q, w_mine, B.raw[u], B.ks[u]);
+      const int64_t item = it0 + u * 64 + sub;
+      bool take = quarter == 0 && item < end && sc >= T0;
+      if constexpr (!kDirect) {
+        if (take) {  // invalid list entries never become candidates
+          bool valid;
+          (void)item_position(p, row, item, end, vis, valid);
+          take = valid;
+        }
+      }
+      if (take) {
         const uint32_t at = atomicAdd(&n_hit, 1u);
-        if (at < (uint32_t)kSeg) seg[at] = select_key(score_key(sc), (uint32_t)(it0 + u * 64 + sub));
+        if (at < (uint32_t)kSeg) seg[at] = select_key(score_key(sc), (uint32_t)item);
       }
     }
   };
   constexpr int kStep = 64 * U;
+  __syncthreads();  // n_hit is initialised
   Batch A, Bb;
   int64_t it = base;
-  load(A, it);  // in flight while the threshold is worked out
-  if (ks) T0 = row_threshold(sk, ks, bins, wsum, sh);
-  if (chunk == 0 && threadIdx.x == 0) p.thresh[row] = T0;
+  load(A, it);
   while (true) {
     const int64_t nxt = it + kStep;
     if (nxt < end) load(Bb, nxt);
@@ -600,14 +670,14 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   } else {
     // exact recompute of this row (rare): radix steps over recomputed keys
     half2_t q[kHI][8];
-    float w[kHI];
-    load_query_f16(p, row, quarter, q, w);
+    float w_mine;
+    load_query_f16(p, row, quarter, q, w_mine);
     auto visit = [&](uint32_t n, auto&& f) {
       for (uint32_t base = 0; base < n; base += 64) {
         const uint32_t item = base + (t >> 2);
         bool valid = false;
         const int64_t pos = item < n ? item_position(p, row, item, n, vis, valid) : 0;
-        const float sc = quad_score_at(p, q, w, seq, quarter, pos, valid);
+        const float sc = quad_score_at(p, q, w_mine, seq, quarter, pos, valid);
         if (valid && quarter == 0) f(select_key(score_key(sc), item));
       }
     };
@@ -630,7 +700,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       const uint32_t item = base + (t >> 2);
       bool valid = false;
       const int64_t pos = item < ni ? item_position(p, row, item, ni, vis, valid) : 0;
-      const float sc = quad_score_at(p, q, w, seq, quarter, pos, valid);
+      const float sc = quad_score_at(p, q, w_mine, seq, quarter, pos, valid);
       const bool f = valid && quarter == 0 && select_key(score_key(sc), item) >= kth;
       uint32_t nr;
       const uint32_t o = block_incl_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
@@ -693,8 +763,12 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   h = prof_begin(CSA2_K_INDEX_SCAN, stream);
-  hipLaunchKernelGGL(k_index_scan<4>, dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
-                     scan_per_row);
+  if (p.source == kItemsDirect)
+    hipLaunchKernelGGL((k_index_scan<4, true>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
+                       scan_per_row);
+  else
+    hipLaunchKernelGGL((k_index_scan<4, false>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
+                       scan_per_row);
   prof_end(h, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
