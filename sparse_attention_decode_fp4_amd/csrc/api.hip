@@ -58,7 +58,7 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
   w.nsel = take((size_t)rows * 4);
-  w.partial = take((size_t)kMaxPartialUnits * kH * (kD + 4) * 4);
+  w.partial = take((size_t)kMaxPartialUnits * kPartFloats * 4);
   w.pf_sample = take((size_t)pf_rows * kPfSample * 4);
   w.pf_thresh = take((size_t)pf_rows * 4);
   w.pf_count = take((size_t)pf_rows * kPfSplits * 4);

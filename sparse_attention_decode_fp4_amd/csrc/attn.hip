@@ -11,22 +11,40 @@
 // (v_mfma_f32_16x16x32_bf16) with float32 accumulation:
 //   S^T[64 rows][16 heads] = E[64][512] . Q^T      (wave w: rows 16w..16w+15)
 //   O[16][512] += P[16][64] . E[64][512]            (wave w: channels 128w..)
-// E2M1 x E4M3 products are exact in bf16, so only P is rounded: it is split
-// into bf16 hi + lo parts (relative error ~2^-16).  A workgroup walks
-// `tiles_per_split` tiles with an online softmax.  When a (layer, row) is
-// split over several workgroups, a second kernel merges the partial
-// softmaxes in split order, so results do not depend on scheduling.
+// The tile sits in LDS row-major (E).  The first product contracts over
+// channels and reads its E operand with 16-byte loads; the second contracts
+// over rows and reads its E operand with the transposing LDS load of gfx950
+// (ds_read_b64_tr_b16), two per MFMA.  E2M1 x E4M3 products are exact in bf16,
+// so only P is rounded: it is split into bf16 hi + lo parts (relative error
+// ~2^-16).  Two forms:
+//   walk   a workgroup walks `tiles_per_split` tiles of one (layer, row)
+//          with an online softmax (many rows: prefill chunks);
+//   tiles  one tile per workgroup (few rows: decode); the tiles of selected
+//          entries are shared by all layers of the launch, since the layers
+//          of a group attend over the same entries, so each is gathered and
+//          dequantised once and then serves every layer.
+// When a (layer, row) is split over several workgroups, a second kernel
+// merges the partial softmaxes in split order, so results do not depend on
+// scheduling.
 #include "kernels.hpp"
 
 namespace csa2 {
 
-constexpr int kEStride = kD + 8;     // bf16 elements per LDS row (padding against bank conflicts)
+// bf16 per row of E: rows 8 banks apart, so neither the 16-byte row reads
+// (8 lanes per LDS cycle) nor the transposing reads (4 rows x 32 bytes per
+// cycle) conflict
+constexpr int kEStride = kD + 16;
 constexpr int kPStride = kAttnSplit + 8;
-constexpr int kPartStride = kD + 4;  // floats per head in a partial: O[512], m, l, 2 pad
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  // exact values only: truncation equals rounding
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i mod 4) of the 4-element chunk addressed by lane 4 e + (i / 4), as its
+// element e.  So if lane j of group G addresses row r0 + 8 G + j / 4,
+// columns c0 + 4 (j mod 4) .. +3 of E, lane (G, i) receives rows r0 + 8 G ..
+// +3 of column c0 + i: 4 consecutive k of the B operand of an MFMA.
+__device__ __forceinline__ v4i16_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -36,76 +54,270 @@ __device__ __forceinline__ uint32_t bf16_round(float x) {  // round to nearest e
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Gather one tile of 64 candidate rows into LDS as bf16 (thread: row t/4,
-// quarter t%4 = 128 channels).  Returns whether this thread's row is real.
-__device__ __forceinline__ bool load_tile(const AttnPass& p, const AttnLayer& L, int tile,
-                                          int n_tile_idx, int row, int seq, int64_t t0, int n_win,
-                                          uint16_t* E) {
-  const int t = threadIdx.x, er = t >> 2, quarter = t & 3;
-  uint16_t* dst = E + er * kEStride + quarter * 128;
-  bool valid;
-  if (tile < n_tile_idx) {
-    const int c = tile * kAttnSplit + er;
-    const int32_t pos = c < p.n_idx ? p.idx[(int64_t)row * p.n_idx + c] : -1;
-    valid = pos >= 0;
-    if (valid) {
-      const int64_t ent = (int64_t)seq * p.kv_stride + pos;
-      const uint8_t* nb = p.nib + ent * CSA2_NIB_BYTES + quarter * 64;
-      const uint8_t* sb = p.scale + ent * CSA2_SCALE_BYTES + quarter * 8;
-      uint4 raw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const uint4*>(nb + 16 * i);
-      const uint2 sc = *reinterpret_cast<const uint2*>(sb);
-      const uint32_t scw[2] = {sc.x, sc.y};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // 16 bytes = 32 channels = 2 scale groups
-        const uint32_t wds[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int g = 2 * i + half;  // scale group within this quarter
-          const float s = e4m3_value((scw[g >> 2] >> (8 * (g & 3))) & 0xFFu);
-          uint32_t outw[8];
-#pragma unroll
-          for (int wd = 0; wd < 2; ++wd) {
-            const uint32_t word = wds[2 * half + wd];
-            // byte b -> (low nibble, high nibble) = consecutive channels; scale 1: exact
-            const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
-            const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
-            const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
-            const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
-            outw[4 * wd + 0] = pack_bf16(v0.x * s, v0.y * s);
-            outw[4 * wd + 1] = pack_bf16(v1.x * s, v1.y * s);
-            outw[4 * wd + 2] = pack_bf16(v2.x * s, v2.y * s);
-            outw[4 * wd + 3] = pack_bf16(v3.x * s, v3.y * s);
-          }
-          *reinterpret_cast<uint4*>(dst + 32 * i + 16 * half) =
-              make_uint4(outw[0], outw[1], outw[2], outw[3]);
-          *reinterpret_cast<uint4*>(dst + 32 * i + 16 * half + 8) =
-              make_uint4(outw[4], outw[5], outw[6], outw[7]);
-        }
-      }
-    }
-  } else {
-    const int wi = (tile - n_tile_idx) * kAttnSplit + er;
-    valid = wi < n_win;
-    if (valid) {
-      const int64_t r = t0 + wi - p.seq.b[seq];
-      const uint16_t* src = L.swa + ((int64_t)seq * p.swa_stride + r) * kD + quarter * 128;
-      uint4 v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4*>(src + 8 * i);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = v[i];
-    }
-  }
-  if (!valid) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = make_uint4(0, 0, 0, 0);
-  }
-  return valid;
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  // exact values only: truncation equals rounding
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
-__global__ __launch_bounds__(256) void k_attention(AttnPass p) {
+struct TileLds {
+  uint16_t E[kAttnSplit * kEStride];  // [row][channel]
+  uint16_t Phi[kH * kPStride];
+  uint16_t Plo[kH * kPStride];
+  float red[4][kH];
+  uint8_t row_ok[kAttnSplit];
+};
+
+// 16 channels (one E4M3 scale group) of one entry as bf16: 8 bytes of E2M1
+// codes, low nibble first, times the group scale (exact in bf16).
+__device__ __forceinline__ void dequant16(uint2 codes, float s, uint4 (&v)[2]) {
+  const uint32_t wds[2] = {codes.x, codes.y};
+  uint32_t o[8];
+#pragma unroll
+  for (int wd = 0; wd < 2; ++wd) {
+    const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wds[wd], 1.0f, 0);
+    const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wds[wd], 1.0f, 1);
+    const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wds[wd], 1.0f, 2);
+    const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wds[wd], 1.0f, 3);
+    o[4 * wd + 0] = pack_bf16(v0.x * s, v0.y * s);
+    o[4 * wd + 1] = pack_bf16(v1.x * s, v1.y * s);
+    o[4 * wd + 2] = pack_bf16(v2.x * s, v2.y * s);
+    o[4 * wd + 3] = pack_bf16(v3.x * s, v3.y * s);
+  }
+  v[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  v[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// One entry of a selected-entry tile in flight: thread t owns row t / 4,
+// channels 128 (t % 4) .. +128 (64 bytes of codes, 8 scales).
+struct EntryFetch {
+  uint4 raw[4];
+  uint2 sc;
+  bool valid;
+};
+
+__device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, int row) {
+  const int c = tile * kAttnSplit + (threadIdx.x >> 2);
+  return c < p.n_idx ? p.idx[(int64_t)row * p.n_idx + c] : -1;
+}
+
+__device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t pos, EntryFetch& f) {
+  const int quarter = threadIdx.x & 3;
+  f.valid = pos >= 0;
+  const int64_t ent = (int64_t)seq * p.kv_stride + (f.valid ? pos : 0);
+  const uint8_t* nb = p.nib + ent * CSA2_NIB_BYTES + quarter * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.raw[i] = f.valid ? *reinterpret_cast<const uint4*>(nb + 16 * i) : make_uint4(0, 0, 0, 0);
+  f.sc = f.valid ? *reinterpret_cast<const uint2*>(p.scale + ent * CSA2_SCALE_BYTES + quarter * 8) : make_uint2(0, 0);
+}
+
+// Dequantise a fetched entry into its row of E (zeros for an empty slot).
+__device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
+  const int er = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  uint16_t* dst = s.E + er * kEStride + quarter * 128;
+  const uint32_t scw[2] = {f.sc.x, f.sc.y};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // 16 bytes = 32 channels = 2 scale groups
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int g = 2 * i + half;
+      uint4 v[2];
+      dequant16(half ? make_uint2(f.raw[i].z, f.raw[i].w) : make_uint2(f.raw[i].x, f.raw[i].y),
+                e4m3_value((scw[g >> 2] >> (8 * (g & 3))) & 0xFFu), v);
+      *reinterpret_cast<uint4*>(dst + 16 * g) = v[0];
+      *reinterpret_cast<uint4*>(dst + 16 * g + 8) = v[1];
+    }
+  }
+  if (quarter == 0) s.row_ok[er] = f.valid ? 1 : 0;
+}
+
+// A window tile into E: thread t copies row t / 4, channels 128 (t % 4) ..
+__device__ __forceinline__ void load_window(const AttnPass& p, const AttnLayer& L, int wtile, int seq, int64_t t0,
+                                            int n_win, TileLds& s) {
+  const int er = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  uint16_t* dst = s.E + er * kEStride + quarter * 128;
+  const int wi = wtile * kAttnSplit + er;
+  const bool valid = wi < n_win;
+  const int64_t r = t0 + wi - p.seq.b[seq];
+  const uint16_t* src = L.swa + ((int64_t)seq * p.swa_stride + (valid ? r : 0)) * kD + quarter * 128;
+  uint4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = valid ? *reinterpret_cast<const uint4*>(src + 8 * i) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = v[i];
+  if (quarter == 0) s.row_ok[er] = valid ? 1 : 0;
+}
+
+// Gather tile `tile` (selected entries first, then window rows) into E.
+__device__ __forceinline__ void load_tile(const AttnPass& p, const AttnLayer& L, int tile, int n_tile_idx, int row,
+                                          int seq, int64_t t0, int n_win, TileLds& s) {
+  if (tile < n_tile_idx) {
+    EntryFetch f;
+    fetch_entry(p, seq, tile_position(p, tile, row), f);
+    store_entry(f, s);
+  } else {
+    load_window(p, L, tile - n_tile_idx, seq, t0, n_win, s);
+  }
+}
+
+__device__ __forceinline__ void load_q(const uint16_t* q, int row, uint4 (&qb)[16]) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  const uint16_t* qrow = q + ((int64_t)row * kH + l16) * kD + 8 * g4;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
+}
+
+// One tile step for all 16 heads of a (layer, row): S^T = E . Q^T,
+// online-softmax update of (m, l) and O = alpha O + P . E.  If `q_next` is
+// given, the Q^T operands of the next layer are loaded into `qb` as soon as
+// this step's S^T no longer needs them.  Starts with a workgroup barrier.
+__device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uint16_t* q_next, int row, float sc2,
+                                          float& m_run, float& l_run, f32x4_t (&o)[8]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  __syncthreads();  // the tile is in LDS; the previous step's readers of P / red are done
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* arow = s.E + (16 * wave + l16) * kEStride + 8 * g4;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[ks]), acc, 0, 0, 0);
+  }
+  if (q_next) load_q(q_next, row, qb);
+  float lg[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    lg[r] = s.row_ok[16 * wave + 4 * g4 + r] ? acc[r] * sc2 : -INFINITY;
+    mx = fmaxf(mx, lg[r]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (g4 == 0) s.red[wave][l16] = mx;
+  __syncthreads();
+  const float m_tile = fmaxf(fmaxf(s.red[0][l16], s.red[1][l16]), fmaxf(s.red[2][l16], s.red[3][l16]));
+  const float m_new = fmaxf(m_run, m_tile);
+  const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+  float sum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int cr = 16 * wave + 4 * g4 + r;
+    const float pv = (m_new == -INFINITY) ? 0.0f : exp2f(lg[r] - m_new);
+    sum += pv;
+    const uint32_t hi = bf16_round(pv);
+    s.Phi[l16 * kPStride + cr] = (uint16_t)hi;
+    s.Plo[l16 * kPStride + cr] = (uint16_t)bf16_round(pv - __uint_as_float(hi << 16));
+  }
+  sum += __shfl_xor(sum, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+  __syncthreads();  // red[] (tile maxima) is read by everyone before reuse
+  if (g4 == 0) s.red[wave][l16] = sum;
+  __syncthreads();
+  l_run = l_run * alpha + (s.red[0][l16] + s.red[1][l16] + s.red[2][l16] + s.red[3][l16]);
+  m_run = m_new;
+
+  // O = alpha * O + P . E   (the rescale factor of row 4*g4+r lives in lane 4*g4+r)
+  float arow_alpha[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) arow_alpha[r] = __shfl(alpha, 4 * g4 + r, 64);
+  const uint4 ahi0 = *reinterpret_cast<const uint4*>(s.Phi + l16 * kPStride + 8 * g4);
+  const uint4 ahi1 = *reinterpret_cast<const uint4*>(s.Phi + l16 * kPStride + 32 + 8 * g4);
+  const uint4 alo0 = *reinterpret_cast<const uint4*>(s.Plo + l16 * kPStride + 8 * g4);
+  const uint4 alo1 = *reinterpret_cast<const uint4*>(s.Plo + l16 * kPStride + 32 + 8 * g4);
+  // transposing reads of E: lane (g4, l16) addresses row 8 g4 + l16 / 4 (+4,
+  // +32) and 4 channels at 4 (l16 % 4) of each 16-channel block
+  const uint16_t* bbase = s.E + (8 * g4 + (l16 >> 2)) * kEStride + 128 * wave + 4 * (l16 & 3);
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const uint16_t* bp = bbase + 16 * nt;
+    const v4i16_t k0 = lds_read_tr16(bp), k1 = lds_read_tr16(bp + 4 * kEStride);
+    const v4i16_t k2 = lds_read_tr16(bp + 32 * kEStride), k3 = lds_read_tr16(bp + 36 * kEStride);
+    const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(k2, k3, 0, 1, 2, 3, 4, 5, 6, 7));
+    f32x4_t acc2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc2[r] = o[nt][r] * arow_alpha[r];
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi0), b0, acc2, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo0), b0, acc2, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi1), b1, acc2, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo1), b1, acc2, 0, 0, 0);
+    o[nt] = acc2;
+  }
+}
+
+// Partial softmax of one (layer, row) and split: unnormalised O, m and l.
+// Lane (l16, g4) of wave w holds heads 4 g4 .. +3 of channels 128 w + 16 nt
+// + l16: one float4 per channel.
+__device__ __forceinline__ void write_partial(const AttnPass& p, int unit, int split, float m_run, float l_run,
+                                              const f32x4_t (&o)[8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  float* part = p.partial + ((int64_t)unit * p.max_splits + split) * kPartFloats;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int ch = 128 * wave + 16 * nt + l16;
+    *reinterpret_cast<float4*>(part + ch * kH + 4 * g4) = make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
+  }
+  if (wave == 0 && g4 == 0) {
+    part[kD * kH + l16] = m_run;
+    part[kD * kH + kH + l16] = l_run;
+  }
+}
+
+__device__ __forceinline__ int64_t window_start(const AttnPass& p, int row, int& n_win) {
+  const int seq = row / p.n_q, qi = row - seq * p.n_q;
+  const int64_t q_pos = p.seq.a[seq] + qi;
+  const int64_t t0 = q_pos - (CSA2_SWA - 1) > 0 ? q_pos - (CSA2_SWA - 1) : 0;
+  n_win = (int)(q_pos - t0 + 1);
+  return t0;
+}
+
+// Tile-parallel form (one tile per workgroup, partials merged afterwards):
+// workgroup (row, j).  j < n_tile_idx: selected-entry tile j, shared by the
+// NL layers of the launch, gathered and dequantised once and then used by
+// each layer in turn (the layer loop is unrolled, so waiting for the next
+// layer's Q does not wait for this layer's partial stores); otherwise window
+// tile (j - n_tile_idx) % n_win_tiles of one layer.
+template <int NL>
+__global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
+  const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
+  const int n_win_tiles = p.n_tiles - n_tile_idx;
+  const int per_row = n_tile_idx + NL * n_win_tiles;
+  const int row = blockIdx.x / per_row, j = blockIdx.x - row * per_row;
+  if (row >= p.rows) return;
+  const int seq = row / p.n_q;
+  int n_win;
+  const int64_t t0 = window_start(p, row, n_win);
+  __shared__ __attribute__((aligned(16))) TileLds s;
+  const float sc2 = p.softmax_scale * 1.4426950408889634f;  // logits in the log2 domain
+  uint4 qb[16];
+  float m_run, l_run;
+  f32x4_t o[8];
+  auto reset = [&]() {
+    m_run = -INFINITY;
+    l_run = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  if (j < n_tile_idx) {
+    load_q(p.layer[0].q, row, qb);
+    load_tile(p, p.layer[0], j, n_tile_idx, row, seq, t0, n_win, s);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      reset();
+      tile_step(s, qb, l + 1 < NL ? p.layer[l + 1].q : nullptr, row, sc2, m_run, l_run, o);
+      write_partial(p, l * p.rows + row, j, m_run, l_run, o);
+    }
+  } else {
+    const int jj = j - n_tile_idx, layer = jj / n_win_tiles, tile = n_tile_idx + jj % n_win_tiles;
+    load_q(p.layer[layer].q, row, qb);
+    load_tile(p, p.layer[layer], tile, n_tile_idx, row, seq, t0, n_win, s);
+    reset();
+    tile_step(s, qb, nullptr, row, sc2, m_run, l_run, o);
+    write_partial(p, layer * p.rows + row, tile, m_run, l_run, o);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
   const int units = p.n_layers * p.rows;
   int unit, split;
   {
@@ -121,121 +333,53 @@ __global__ __launch_bounds__(256) void k_attention(AttnPass p) {
   }
   if (unit >= units) return;
   const int layer = unit / p.rows, row = unit - layer * p.rows;
-  const int seq = row / p.n_q, qi = row - seq * p.n_q;
+  const int seq = row / p.n_q;
   const AttnLayer& L = p.layer[layer];
-  const int64_t q_pos = p.seq.a[seq] + qi;
-  const int64_t t0 = q_pos - (CSA2_SWA - 1) > 0 ? q_pos - (CSA2_SWA - 1) : 0;
-  const int n_win = (int)(q_pos - t0 + 1);
+  int n_win;
+  const int64_t t0 = window_start(p, row, n_win);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
   const int tile_begin = split * p.tiles_per_split;
   int tile_end = tile_begin + p.tiles_per_split;
   tile_end = tile_end < p.n_tiles ? tile_end : p.n_tiles;
 
-  __shared__ __attribute__((aligned(16))) uint16_t E[kAttnSplit * kEStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Phi[kH * kPStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Plo[kH * kPStride];
-  __shared__ float red[4][kH];
-  __shared__ uint8_t row_ok[kAttnSplit];
-
+  __shared__ __attribute__((aligned(16))) TileLds s;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-
-  // Q^T operands of all 16 k-steps: head l16, channels 32*ks + 8*g4 .. +8
-  const uint16_t* qrow = L.q + ((int64_t)row * kH + l16) * kD + 8 * g4;
   uint4 qb[16];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
-
+  load_q(L.q, row, qb);
   const float sc2 = p.softmax_scale * 1.4426950408889634f;  // logits in the log2 domain
   float m_run = -INFINITY, l_run = 0.0f;                     // per head l16 (replicated)
   f32x4_t o[8];                                              // O[4*g4+r][128*wave + 16*nt + l16]
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    __syncthreads();  // the previous tile's readers of E / P are done
-    const bool valid = load_tile(p, L, tile, n_tile_idx, row, seq, t0, n_win, E);
-    if ((t & 3) == 0) row_ok[t >> 2] = valid ? 1 : 0;
-    __syncthreads();
-
-    // S^T tile of this wave: candidate rows 16*wave .. +16, all 16 heads
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* arow = E + (16 * wave + l16) * kEStride + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[ks]), acc, 0, 0, 0);
-    }
-    float lg[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      lg[r] = row_ok[16 * wave + 4 * g4 + r] ? acc[r] * sc2 : -INFINITY;
-      mx = fmaxf(mx, lg[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (g4 == 0) red[wave][l16] = mx;
-    __syncthreads();
-    const float m_tile = fmaxf(fmaxf(red[0][l16], red[1][l16]), fmaxf(red[2][l16], red[3][l16]));
-    const float m_new = fmaxf(m_run, m_tile);
-    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
-    float sum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int cr = 16 * wave + 4 * g4 + r;
-      const float pv = (m_new == -INFINITY) ? 0.0f : exp2f(lg[r] - m_new);
-      sum += pv;
-      const uint32_t hi = bf16_round(pv);
-      Phi[l16 * kPStride + cr] = (uint16_t)hi;
-      Plo[l16 * kPStride + cr] = (uint16_t)bf16_round(pv - __uint_as_float(hi << 16));
-    }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    __syncthreads();  // red[] (tile maxima) is read by everyone before reuse
-    if (g4 == 0) red[wave][l16] = sum;
-    __syncthreads();
-    l_run = l_run * alpha + (red[0][l16] + red[1][l16] + red[2][l16] + red[3][l16]);
-    m_run = m_new;
-
-    // O = alpha * O + P . E   (the rescale factor of row 4*g4+r lives in lane 4*g4+r)
-    float arow_alpha[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) arow_alpha[r] = __shfl(alpha, 4 * g4 + r, 64);
-    const uint4 ahi0 = *reinterpret_cast<const uint4*>(Phi + l16 * kPStride + 8 * g4);
-    const uint4 ahi1 = *reinterpret_cast<const uint4*>(Phi + l16 * kPStride + 32 + 8 * g4);
-    const uint4 alo0 = *reinterpret_cast<const uint4*>(Plo + l16 * kPStride + 8 * g4);
-    const uint4 alo1 = *reinterpret_cast<const uint4*>(Plo + l16 * kPStride + 32 + 8 * g4);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int ch = 128 * wave + 16 * nt + l16;
-      f32x4_t acc2;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc2[r] = o[nt][r] * arow_alpha[r];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* col = E + (32 * kk + 8 * g4) * kEStride + ch;
-        uint32_t bw[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bw[j] = (uint32_t)col[(2 * j) * kEStride] | ((uint32_t)col[(2 * j + 1) * kEStride] << 16);
-        const bf16x8_t b = as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
-        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk ? ahi1 : ahi0), b, acc2, 0, 0, 0);
-        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk ? alo1 : alo0), b, acc2, 0, 0, 0);
-      }
-      o[nt] = acc2;
-    }
+  // selected-entry tiles are software-pipelined: the entries of tile i + 1
+  // and the positions of tile i + 2 are in flight while tile i is computed
+  const int last_sel = (tile_end < n_tile_idx ? tile_end : n_tile_idx) - 1;  // last selected-entry tile here
+  EntryFetch f;
+  int32_t pos_next = -1;
+  if (tile_begin <= last_sel) {
+    fetch_entry(p, seq, tile_position(p, tile_begin, row), f);
+    if (tile_begin + 1 <= last_sel) pos_next = tile_position(p, tile_begin + 1, row);
   }
-
-  // final normaliser of the head held in each output row 4*g4+r
-  float m_out[4], l_out[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_out[r] = __shfl(m_run, 4 * g4 + r, 64);
-    l_out[r] = __shfl(l_run, 4 * g4 + r, 64);
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    if (tile > tile_begin) __syncthreads();  // the previous tile's readers of E are done
+    if (tile <= last_sel) {
+      store_entry(f, s);
+      if (tile + 1 <= last_sel) {
+        fetch_entry(p, seq, pos_next, f);
+        if (tile + 2 <= last_sel) pos_next = tile_position(p, tile + 2, row);
+      }
+    } else {
+      load_window(p, L, tile - n_tile_idx, seq, t0, n_win, s);
+    }
+    tile_step(s, qb, nullptr, row, sc2, m_run, l_run, o);
   }
 
   if (p.max_splits == 1) {  // whole row in this workgroup: write the output
+    float l_out[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_out[r] = __shfl(l_run, 4 * g4 + r, 64);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const int ch = 128 * wave + 16 * nt + l16;
@@ -247,66 +391,64 @@ __global__ __launch_bounds__(256) void k_attention(AttnPass p) {
     }
     return;
   }
-
-  float* part = p.partial + (((int64_t)unit * p.max_splits + split) * kH) * kPartStride;
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int ch = 128 * wave + 16 * nt + l16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) part[(4 * g4 + r) * kPartStride + ch] = o[nt][r];
-  }
-  if (wave == 0 && g4 == 0) {
-    part[l16 * kPartStride + kD] = m_run;
-    part[l16 * kPartStride + kD + 1] = l_run;
-  }
+  write_partial(p, unit, split, m_run, l_run, o);
 }
 
-// Merge of the split partial softmaxes, in split order.  A kernel of its own:
-// the kernel boundary orders the partial writes before these reads on every
-// XCD, which in-kernel device-scope fences would do by writing back the whole
-// L2.  Workgroup (unit, quarter): 4 heads x 512 channels, 16 per thread.
-__global__ __launch_bounds__(128) void k_attention_merge(AttnPass p) {
+// Merge of the split partial softmaxes, in split order.  A kernel of its
+// own: the kernel boundary orders the partial writes before these reads on
+// every XCD, which in-kernel device-scope fences would do by writing back
+// the whole L2.  Workgroup (unit, channel quarter): 16 threads turn the m
+// and l of every split into per-head weights exp2(m_s - M) / L in LDS while
+// all threads' partial loads are in flight; thread t then sums channel 128
+// quarter + t / 2, heads 8 (t % 2) .. +8 (32 contiguous bytes per split).
+constexpr int kMaxMergeSplits = 64;
+__global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
   const int unit = blockIdx.x >> 2, quarter = blockIdx.x & 3;
   const int layer = unit / p.rows, row = unit - layer * p.rows;
   const int t = threadIdx.x;
-  const int h = 4 * quarter + (t >> 5), c0 = (t & 31) * 16;
-  const float* pb = p.partial + ((int64_t)unit * p.max_splits * kH) * kPartStride;
-  float M = -INFINITY;
-  for (int s = 0; s < p.max_splits; ++s) M = fmaxf(M, pb[(s * kH + h) * kPartStride + kD]);
-  float acc_o[16];
+  const int ch = 128 * quarter + (t >> 1), h0 = 8 * (t & 1);
+  const int ns = p.max_splits;
+  const float* pb = p.partial + (int64_t)unit * ns * kPartFloats;
+  __shared__ float wgt[kMaxMergeSplits][kH];
+  float acc[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc_o[j] = 0.0f;
-  float lsum = 0.0f;
-  // four splits per step: their loads are issued together
-  for (int s0 = 0; s0 < p.max_splits; s0 += 4) {
-    float4 v[4][4];
-    float ms[4], ls[4];
+  for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float4 v[8][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + u < p.max_splits ? s0 + u : p.max_splits - 1;
-      const float* ps = pb + (s * kH + h) * kPartStride;
-      ms[u] = s0 + u < p.max_splits ? ps[kD] : -INFINITY;
-      ls[u] = ps[kD + 1];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[u][j] = *reinterpret_cast<const float4*>(ps + c0 + 4 * j);
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u < ns ? s0 + u : ns - 1;
+      const float* ps = pb + (int64_t)s * kPartFloats + ch * kH + h0;
+      v[u][0] = *reinterpret_cast<const float4*>(ps);
+      v[u][1] = *reinterpret_cast<const float4*>(ps + 4);
+    }
+    if (s0 == 0) {
+      if (t < kH) {  // head t: weights of every split
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, pb[(int64_t)s * kPartFloats + kD * kH + t]);
+        float L = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+          const float* ps = pb + (int64_t)s * kPartFloats + kD * kH;
+          const float w = ps[t] == -INFINITY ? 0.0f : exp2f(ps[t] - M);
+          wgt[s][t] = w;
+          L += w * ps[kH + t];
+        }
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        for (int s = 0; s < ns; ++s) wgt[s][t] *= inv;
+      }
+      __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wgt = (ms[u] == -INFINITY) ? 0.0f : exp2f(ms[u] - M);
-      lsum += wgt * ls[u];
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u >= ns) break;
+      const float x[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc_o[4 * j] += wgt * v[u][j].x; acc_o[4 * j + 1] += wgt * v[u][j].y;
-        acc_o[4 * j + 2] += wgt * v[u][j].z; acc_o[4 * j + 3] += wgt * v[u][j].w;
-      }
+      for (int h = 0; h < 8; ++h) acc[h] += wgt[s0 + u][h0 + h] * x[h];
     }
   }
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-  float* dsto = p.layer[layer].out + ((int64_t)row * kH + h) * kD + c0;
+  float* dst = p.layer[layer].out + ((int64_t)row * kH + h0) * kD + ch;
 #pragma unroll
-  for (int j = 0; j < 16; j += 4)
-    *reinterpret_cast<float4*>(dsto + j) =
-        make_float4(acc_o[j] * inv, acc_o[j + 1] * inv, acc_o[j + 2] * inv, acc_o[j + 3] * inv);
+  for (int h = 0; h < 8; ++h) dst[h * kD] = acc[h];
 }
 
 hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
@@ -314,12 +456,29 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   if (units == 0) return hipSuccess;
   const int gu = (units >= kXcds && p.max_splits > 1) ? (units + kXcds - 1) / kXcds * kXcds : units;
   int h = prof_begin(CSA2_K_ATTENTION, stream);
-  hipLaunchKernelGGL(k_attention, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
+  const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
+  if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles && p.n_layers > 1) {
+    // one tile per workgroup: selected-entry tiles are shared by the layers
+    const int per_row = n_tile_idx + p.n_layers * (p.n_tiles - n_tile_idx);
+    const dim3 grid((unsigned)(p.rows * per_row));
+    switch (p.n_layers) {
+      case 2: hipLaunchKernelGGL(k_attention_tiles<2>, grid, dim3(256), 0, stream, p); break;
+      case 3: hipLaunchKernelGGL(k_attention_tiles<3>, grid, dim3(256), 0, stream, p); break;
+      case 4: hipLaunchKernelGGL(k_attention_tiles<4>, grid, dim3(256), 0, stream, p); break;
+      case 5: hipLaunchKernelGGL(k_attention_tiles<5>, grid, dim3(256), 0, stream, p); break;
+      case 6: hipLaunchKernelGGL(k_attention_tiles<6>, grid, dim3(256), 0, stream, p); break;
+      case 7: hipLaunchKernelGGL(k_attention_tiles<7>, grid, dim3(256), 0, stream, p); break;
+      default: hipLaunchKernelGGL(k_attention_tiles<8>, grid, dim3(256), 0, stream, p); break;
+    }
+  } else {
+    hipLaunchKernelGGL(k_attention, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
+  }
   prof_end(h, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_splits == 1) return e;
+  if (p.max_splits > kMaxMergeSplits) return hipErrorInvalidValue;
   h = prof_begin(CSA2_K_ATTENTION_MERGE, stream);
-  hipLaunchKernelGGL(k_attention_merge, dim3((unsigned)(4 * units)), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(k_attention_merge, dim3((unsigned)(4 * units)), dim3(256), 0, stream, p);
   prof_end(h, stream);
   return hipGetLastError();
 }

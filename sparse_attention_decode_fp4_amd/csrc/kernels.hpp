@@ -80,6 +80,8 @@ struct AttnLayer {
 };
 constexpr int kMaxAttnLayers = 8;
 constexpr int kAttnSplit = 64;  // candidates per workgroup
+// A partial softmax: O as [512 channels][16 heads] floats, then m[16], l[16].
+constexpr int kPartFloats = kD * kH + 2 * kH;
 struct AttnPass {
   int32_t rows, n_q, n_idx, n_layers;
   SeqArgs seq;                  // a = q_pos0, b = swa_pos0
@@ -94,7 +96,7 @@ struct AttnPass {
   int32_t tiles_per_split;      // tiles one workgroup walks (online softmax)
   int32_t max_splits;           // ceil(n_tiles / tiles_per_split)
   // workspace (used when max_splits > 1)
-  float* partial;               // [n_layers*rows][max_splits][16][516]
+  float* partial;               // [n_layers*rows][max_splits][kPartFloats]
 };
 hipError_t launch_attention(const AttnPass& p, hipStream_t stream);
 
