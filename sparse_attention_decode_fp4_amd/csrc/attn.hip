@@ -272,16 +272,20 @@ __device__ __forceinline__ int64_t window_start(const AttnPass& p, int row, int&
 }
 
 // Tile-parallel form (one tile per workgroup, partials merged afterwards):
-// workgroup (row, j).  j < n_tile_idx: selected-entry tile j, shared by the
-// NL layers of the launch, gathered and dequantised once and then used by
-// each layer in turn (the layer loop is unrolled, so waiting for the next
-// layer's Q does not wait for this layer's partial stores); otherwise window
-// tile (j - n_tile_idx) % n_win_tiles of one layer.
-template <int NL>
+// workgroup (row, j).  j < n_tile_idx * n_groups: selected-entry tile
+// j / n_groups for layer group j % n_groups (layers LG g .. LG g + LG - 1):
+// the layers of a group attend over the same entries, so a tile is gathered
+// and dequantised once per layer group and then used by each of its layers
+// in turn (the layer loop is unrolled, so waiting for the next layer's Q
+// does not wait for this layer's partial stores); otherwise a window tile
+// of one layer.
+template <int LG>
 __global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
   const int n_win_tiles = p.n_tiles - n_tile_idx;
-  const int per_row = n_tile_idx + NL * n_win_tiles;
+  const int n_groups = (p.n_layers + LG - 1) / LG;
+  const int n_sel = n_tile_idx * n_groups;
+  const int per_row = n_sel + p.n_layers * n_win_tiles;
   const int row = blockIdx.x / per_row, j = blockIdx.x - row * per_row;
   if (row >= p.rows) return;
   const int seq = row / p.n_q;
@@ -298,17 +302,20 @@ __global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
-  if (j < n_tile_idx) {
-    load_q(p.layer[0].q, row, qb);
-    load_tile(p, p.layer[0], j, n_tile_idx, row, seq, t0, n_win, s);
+  if (j < n_sel) {
+    const int tile = j / n_groups, l0 = LG * (j % n_groups);
+    load_q(p.layer[l0].q, row, qb);
+    load_tile(p, p.layer[l0], tile, n_tile_idx, row, seq, t0, n_win, s);
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
+    for (int i = 0; i < LG; ++i) {
+      const int l = l0 + i;
+      if (l >= p.n_layers) break;  // uniform
       reset();
-      tile_step(s, qb, l + 1 < NL ? p.layer[l + 1].q : nullptr, row, sc2, m_run, l_run, o);
-      write_partial(p, l * p.rows + row, j, m_run, l_run, o);
+      tile_step(s, qb, (i + 1 < LG && l + 1 < p.n_layers) ? p.layer[l + 1].q : nullptr, row, sc2, m_run, l_run, o);
+      write_partial(p, l * p.rows + row, tile, m_run, l_run, o);
     }
   } else {
-    const int jj = j - n_tile_idx, layer = jj / n_win_tiles, tile = n_tile_idx + jj % n_win_tiles;
+    const int jj = j - n_sel, layer = jj / n_win_tiles, tile = n_tile_idx + jj % n_win_tiles;
     load_q(p.layer[layer].q, row, qb);
     load_tile(p, p.layer[layer], tile, n_tile_idx, row, seq, t0, n_win, s);
     reset();
@@ -397,11 +404,13 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
 // Merge of the split partial softmaxes, in split order.  A kernel of its
 // own: the kernel boundary orders the partial writes before these reads on
 // every XCD, which in-kernel device-scope fences would do by writing back
-// the whole L2.  Workgroup (unit, channel quarter): 16 threads turn the m
-// and l of every split into per-head weights exp2(m_s - M) / L in LDS while
-// all threads' partial loads are in flight; thread t then sums channel 128
-// quarter + t / 2, heads 8 (t % 2) .. +8 (32 contiguous bytes per split).
+// the whole L2.  Workgroup (unit, channel quarter): thread t sums channel
+// 128 quarter + t / 2, heads 8 (t % 2) .. +8 (32 contiguous bytes of each
+// partial), with per-head weights exp2(m_s - M) / L that 16 threads work out
+// in LDS from the (m, l) of every split, loaded in one round trip while the
+// partial loads of up to 16 splits are in flight.
 constexpr int kMaxMergeSplits = 64;
+constexpr int kMergeBatch = 16;
 __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
   const int unit = blockIdx.x >> 2, quarter = blockIdx.x & 3;
   const int layer = unit / p.rows, row = unit - layer * p.rows;
@@ -410,28 +419,35 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
   const int ns = p.max_splits;
   const float* pb = p.partial + (int64_t)unit * ns * kPartFloats;
   __shared__ float wgt[kMaxMergeSplits][kH];
+  __shared__ float lsh[kMaxMergeSplits][kH];
   float acc[8];
 #pragma unroll
   for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float4 v[8][2];
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float4 v[kMergeBatch][2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       const int s = s0 + u < ns ? s0 + u : ns - 1;
       const float* ps = pb + (int64_t)s * kPartFloats + ch * kH + h0;
       v[u][0] = *reinterpret_cast<const float4*>(ps);
       v[u][1] = *reinterpret_cast<const float4*>(ps + 4);
     }
     if (s0 == 0) {
-      if (t < kH) {  // head t: weights of every split
+      for (int i = t; i < ns * kH; i += 256) {  // (split, head) = (i / 16, i % 16)
+        const float* ps = pb + (int64_t)(i / kH) * kPartFloats + kD * kH;
+        wgt[i / kH][i % kH] = ps[i % kH];
+        lsh[i / kH][i % kH] = ps[kH + i % kH];
+      }
+      __syncthreads();
+      if (t < kH) {  // head t
         float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, pb[(int64_t)s * kPartFloats + kD * kH + t]);
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, wgt[s][t]);
         float L = 0.0f;
         for (int s = 0; s < ns; ++s) {
-          const float* ps = pb + (int64_t)s * kPartFloats + kD * kH;
-          const float w = ps[t] == -INFINITY ? 0.0f : exp2f(ps[t] - M);
+          const float m = wgt[s][t];
+          const float w = m == -INFINITY ? 0.0f : exp2f(m - M);
           wgt[s][t] = w;
-          L += w * ps[kH + t];
+          L += w * lsh[s][t];
         }
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         for (int s = 0; s < ns; ++s) wgt[s][t] *= inv;
@@ -439,7 +455,7 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
       __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       if (s0 + u >= ns) break;
       const float x[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
 #pragma unroll
@@ -457,19 +473,14 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   const int gu = (units >= kXcds && p.max_splits > 1) ? (units + kXcds - 1) / kXcds * kXcds : units;
   int h = prof_begin(CSA2_K_ATTENTION, stream);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
-  if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles && p.n_layers > 1) {
+  if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles) {
     // one tile per workgroup: selected-entry tiles are shared by the layers
-    const int per_row = n_tile_idx + p.n_layers * (p.n_tiles - n_tile_idx);
-    const dim3 grid((unsigned)(p.rows * per_row));
-    switch (p.n_layers) {
-      case 2: hipLaunchKernelGGL(k_attention_tiles<2>, grid, dim3(256), 0, stream, p); break;
-      case 3: hipLaunchKernelGGL(k_attention_tiles<3>, grid, dim3(256), 0, stream, p); break;
-      case 4: hipLaunchKernelGGL(k_attention_tiles<4>, grid, dim3(256), 0, stream, p); break;
-      case 5: hipLaunchKernelGGL(k_attention_tiles<5>, grid, dim3(256), 0, stream, p); break;
-      case 6: hipLaunchKernelGGL(k_attention_tiles<6>, grid, dim3(256), 0, stream, p); break;
-      case 7: hipLaunchKernelGGL(k_attention_tiles<7>, grid, dim3(256), 0, stream, p); break;
-      default: hipLaunchKernelGGL(k_attention_tiles<8>, grid, dim3(256), 0, stream, p); break;
-    }
+    // layer groups of two: gathering a tile twice is cheap next to running
+    // four layers one after another in one workgroup
+    constexpr int LG = 2;
+    const int n_groups = (p.n_layers + LG - 1) / LG;
+    const int per_row = n_tile_idx * n_groups + p.n_layers * (p.n_tiles - n_tile_idx);
+    hipLaunchKernelGGL(k_attention_tiles<LG>, dim3((unsigned)(p.rows * per_row)), dim3(256), 0, stream, p);
   } else {
     hipLaunchKernelGGL(k_attention, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
   }

@@ -30,6 +30,7 @@ namespace csa2 {
 constexpr int kSample = 2048;       // sampled items per row
 constexpr int kSelCap = 4096;       // candidates the select kernel holds in LDS
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
+constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks gather in one round trip
 
 __device__ __forceinline__ int64_t row_vis_positions(const IndexPass& p, int row) {
   const int seq = row / p.n_q, i = row - seq * p.n_q;
@@ -542,16 +543,37 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need;
 
-  // segment counts: thread t owns chunks 16t .. 16t+15
   const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
+  const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
+  // Rows of at most kSpecChunks chunks load every segment slot together with
+  // the counts (one memory round trip): thread t takes slots 32 (t % 4) ..
+  // +32 of chunk t / 4.
+  const bool spec = nch <= kSpecChunks;
+  uint64_t sv[kSeg / 4];
+  uint32_t spec_n = 0;
+  if (spec && (t >> 2) < nch) {
+    const uint64_t* src = segs + (int64_t)(t >> 2) * kSeg + 32 * (t & 3);
+    spec_n = cnt_row[t >> 2];
+#pragma unroll
+    for (int i = 0; i < kSeg / 4; i += 2) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + i);
+      sv[i] = ((uint64_t)v.y << 32) | v.x;
+      sv[i + 1] = ((uint64_t)v.w << 32) | v.z;
+    }
+  }
+  // segment counts: thread t owns chunks 16t .. 16t+15
   uint32_t c[16], local = 0;
   bool over = false;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int ch = 16 * t + j;
-    c[j] = ch < nch ? cnt_row[ch] : 0u;
+    c[j] = ch < nch ? (spec ? 0u : cnt_row[ch]) : 0u;
     over |= c[j] > (uint32_t)kSeg;
     local += c[j];
+  }
+  if (spec) {  // thread t holds the count of chunk t / 4; count it once
+    local = (t & 3) == 0 ? spec_n : 0u;
+    over = (t & 3) == 0 && spec_n > (uint32_t)kSeg;
   }
   over = __syncthreads_or(over);
   uint32_t total;
@@ -559,9 +581,10 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int ch = 16 * t + j;
-    if (ch < nch) seg_start[ch] = run;
+    if (!spec && ch < nch) seg_start[ch] = run;
     run += c[j];
   }
+  if (spec && (t & 3) == 0 && (t >> 2) < nch) seg_start[t >> 2] = run;  // exclusive prefix
   if (t == 0) seg_start[nch] = total;
   __syncthreads();
 
@@ -573,11 +596,21 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       uint4* bm4 = reinterpret_cast<uint4*>(bitmap);
       for (int i = t; i < kBitmapItems / 128; i += 256) bm4[i] = make_uint4(0, 0, 0, 0);
     }
-    // gather the segments: wave w copies chunks w, w + 4, ..., eight chunks
-    // (up to 16 independent loads per lane) at a time
-    const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
+    if (spec) {  // the slots loaded above: keep the first count of each chunk
+      if ((t >> 2) < nch) {
+        const uint32_t n = seg_start[(t >> 2) + 1] - seg_start[t >> 2];
+        const uint32_t base = seg_start[t >> 2];
+#pragma unroll
+        for (int i = 0; i < kSeg / 4; ++i) {
+          const uint32_t slot = 32 * (t & 3) + i;
+          if (slot < n) lc[base + slot] = sv[i];
+        }
+      }
+    }
+    // otherwise gather the segments: wave w copies chunks w, w + 4, ...,
+    // eight chunks (up to 16 independent loads per lane) at a time
     const int wave = t >> 6, lane = t & 63;
-    for (int c0 = wave; c0 < nch; c0 += 32) {
+    for (int c0 = spec ? nch : wave; c0 < nch; c0 += 32) {
       uint64_t v[8][2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -764,10 +797,10 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   h = prof_begin(CSA2_K_INDEX_SCAN, stream);
   if (p.source == kItemsDirect)
-    hipLaunchKernelGGL((k_index_scan<4, true>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL((k_index_scan<2, true>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
                        scan_per_row);
   else
-    hipLaunchKernelGGL((k_index_scan<4, false>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL((k_index_scan<2, false>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
                        scan_per_row);
   prof_end(h, stream);
   e = hipGetLastError();
