@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 256 MiB five times (the known-size reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
                     help="decode: the 128K decode group (default, the headline); prefill: a 4,096-token "
                          "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers")
@@ -182,12 +185,49 @@ def prefill(args):
     print(json.dumps(line), flush=True)
 
 
+COPY_BYTES = 256 << 20
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of COPY_BYTES, five times: under
+    rocprofv3 --pmc FETCH_SIZE (or WRITE_SIZE) each dispatch should read (and
+    write) COPY_BYTES; the ratio to the counter's reading scales the counters
+    taken on the library's kernels."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 5}), flush=True)
+
+
+def scan_traffic(path=os.path.join(ROOT, "profiles", "k_index_scan_decode128k_b16_traffic.txt")):
+    """HBM bytes per k_index_scan launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel source."""
+    import hashlib
+    try:
+        with open(path) as f:
+            fields = dict(line.split(":", 1) for line in f if line.startswith("@"))
+    except OSError:
+        return None
+    src = os.path.join(ROOT, "sparse_attention_decode_fp4_amd", "csrc", "index.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("@index_hip_sha256", "").strip() != digest:
+        return None
+    return int(fields["@traffic_bytes_per_launch"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(sequences are independent: a multi-GPU run would shard them by rank).", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.workload == "prefill":
         prefill(args)
         return
@@ -317,7 +357,7 @@ def main():
                    "batch": B, "ctx": ctx, "layers_per_step": 8, "query_tokens_per_step": qtok_per_step,
                    "cache_copies": C, "timing": "graph replay" if best_s == graph_s else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic(),
                      "kernel": "k_index_scan", "bytes_per_launch": scan_bytes,
                      "avg_launch_us": round(scan_avg_s * 1e6, 3)},
         "step_hbm": {"algorithmic_bytes": step_bytes,
