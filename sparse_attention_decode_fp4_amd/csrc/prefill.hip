@@ -32,6 +32,10 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
 constexpr int kPfStage = 256;   // keys staged in LDS per step
+
+// max(x, 0) as one integer max on the bits (negative floats, -0 included,
+// are negative integers), without the NaN canonicalisation of fmaxf.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 constexpr uint32_t kUnitScales = 0x7F7F7F7Fu;  // E8M0 127 = 1.0 in every byte
 
 __device__ __forceinline__ int64_t pf_visible(const PrefillPass& p, int seq, int64_t qi) {
@@ -168,34 +172,59 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
       const int64_t slot = base + bt + l32;
       const bool slot_ok = (bt + l32) < n_here;
       const bool all_visible = kFilter ? (base + bt + 32 <= v_first) : true;
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        v16f_t acc = {};
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a], B, acc, 0, 0, 0, kUnitScales, 0, kUnitScales);
+      // epilogue of A tile a: ReLU-sum of the 4 heads, times the key scale;
+      // filter: append the pairs at or above the row threshold
+      auto epilogue = [&](const v16f_t& acc, int a) {
+        float sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ql = 64 * wave + 8 * a + 2 * i + half;
+          const float r0 = relu(acc[4 * i]), r1 = relu(acc[4 * i + 1]);
+          const float r2 = relu(acc[4 * i + 2]), r3 = relu(acc[4 * i + 3]);
           float sum;
           if (kHasW) {
-            sum = w_row[ql * kHI] * fmaxf(acc[4 * i], 0.0f) + w_row[ql * kHI + 1] * fmaxf(acc[4 * i + 1], 0.0f) +
-                  w_row[ql * kHI + 2] * fmaxf(acc[4 * i + 2], 0.0f) + w_row[ql * kHI + 3] * fmaxf(acc[4 * i + 3], 0.0f);
+            sum = w_row[ql * kHI] * r0 + w_row[ql * kHI + 1] * r1 + w_row[ql * kHI + 2] * r2 + w_row[ql * kHI + 3] * r3;
           } else {
-            sum = (fmaxf(acc[4 * i], 0.0f) + fmaxf(acc[4 * i + 1], 0.0f)) +
-                  (fmaxf(acc[4 * i + 2], 0.0f) + fmaxf(acc[4 * i + 3], 0.0f));
+            sum = (r0 + r1) + (r2 + r3);
           }
-          const float s = ksn * sum;
+          sc[i] = ksn * sum;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ql = 64 * wave + 8 * a + 2 * i + half;
           if (kFilter) {
-            bool hit = slot_ok && s >= T[a][i];
+            bool hit = slot_ok && sc[i] >= T[a][i];
             if (hit && !all_visible) hit = slot < vis_row[ql];
             if (hit) {  // append to this row's segment for this key range
               const uint32_t at = atomicAdd(&seg_count[ql], 1u);
               if (at < (uint32_t)kPfSeg)
-                p.list[((row0 + ql) * kPfSplits + split) * kPfSeg + at] = select_key(score_key(s), (uint32_t)slot);
+                p.list[((row0 + ql) * kPfSplits + split) * kPfSeg + at] = select_key(score_key(sc[i]), (uint32_t)slot);
             }
           } else if (slot_ok && ql < nq_tile) {
-            p.sample[(row0 + ql) * kPfSample + slot] = s;
+            p.sample[(row0 + ql) * kPfSample + slot] = sc[i];
           }
         }
+      };
+      // software pipeline: the MFMA of tile a + 1 runs under the epilogue of
+      // a (scheduling barriers keep the compiler from serialising them)
+      v16f_t acc0 = {}, acc1 = {};
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[0], B, acc0, 0, 0, 0, kUnitScales, 0, kUnitScales);
+#pragma unroll
+      for (int a = 0; a < 8; a += 2) {
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 1], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
+                                                              kUnitScales);
+        asm volatile("" ::"a"(acc1));  // issued here, not sunk to its first use
+        __builtin_amdgcn_sched_barrier(0);
+        epilogue(acc0, a);
+        __builtin_amdgcn_sched_barrier(0);
+        if (a + 2 < 8) {
+          acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 2], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
+                                                                kUnitScales);
+          asm volatile("" ::"a"(acc0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        epilogue(acc1, a + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     buf ^= 1;
