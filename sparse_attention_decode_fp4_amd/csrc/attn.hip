@@ -17,8 +17,9 @@
 // (ds_read_b64_tr_b16), two per MFMA.  E2M1 x E4M3 products are exact in bf16,
 // so only P is rounded: it is split into bf16 hi + lo parts (relative error
 // ~2^-16).  Two forms:
-//   walk   a workgroup walks `tiles_per_split` tiles of one (layer, row)
-//          with an online softmax (many rows: prefill chunks);
+//   walk   a workgroup walks `tiles_per_split` tiles of one row for a group
+//          of LG layers, one online softmax per layer, a selected-entry tile
+//          dequantised once for the group (many rows: prefill chunks);
 //   tiles  one tile per workgroup (few rows: decode); the tiles of selected
 //          entries are shared by all layers of the launch, since the layers
 //          of a group attend over the same entries, so each is gathered and
@@ -244,22 +245,32 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
   }
 }
 
-// Partial softmax of one (layer, row) and split: unnormalised O, m and l.
+// Partial softmax of one (layer, row) and split: O / l in fp16, m and l.
 // Lane (l16, g4) of wave w holds heads 4 g4 .. +3 of channels 128 w + 16 nt
-// + l16: one float4 per channel.
+// + l16: 8 bytes per channel.
 __device__ __forceinline__ void write_partial(const AttnPass& p, int unit, int split, float m_run, float l_run,
                                               const f32x4_t (&o)[8]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   float* part = p.partial + ((int64_t)unit * p.max_splits + split) * kPartFloats;
+  uint16_t* po = reinterpret_cast<uint16_t*>(part);
+  float inv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float l = __shfl(l_run, 4 * g4 + r, 64);  // l of head 4 g4 + r
+    inv[r] = l > 0.0f ? 1.0f / l : 0.0f;
+  }
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const int ch = 128 * wave + 16 * nt + l16;
-    *reinterpret_cast<float4*>(part + ch * kH + 4 * g4) = make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
+    const half2_t a = {(_Float16)(o[nt][0] * inv[0]), (_Float16)(o[nt][1] * inv[1])};  // round to nearest
+    const half2_t b = {(_Float16)(o[nt][2] * inv[2]), (_Float16)(o[nt][3] * inv[3])};
+    *reinterpret_cast<uint2*>(po + ch * kH + 4 * g4) =
+        make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
   }
   if (wave == 0 && g4 == 0) {
-    part[kD * kH + l16] = m_run;
-    part[kD * kH + kH + l16] = l_run;
+    part[kPartOWords + l16] = m_run;
+    part[kPartOWords + kH + l16] = l_run;
   }
 }
 
@@ -324,8 +335,16 @@ __global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
   }
 }
 
+// Walk form: workgroup (group of LG layers, row, split) walks its tiles
+// with one online softmax per layer.  The selected-entry tiles are shared by
+// the layers (dequantised once per tile for the group), window tiles are
+// per layer.  Selected-entry tiles are software-pipelined: the entries of
+// tile i + 1 and the positions of tile i + 2 are in flight while tile i is
+// computed.
+template <int LG>
 __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
-  const int units = p.n_layers * p.rows;
+  const int n_groups = (p.n_layers + LG - 1) / LG;
+  const int units = n_groups * p.rows;
   int unit, split;
   {
     const int lin = blockIdx.x;
@@ -339,9 +358,10 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
     }
   }
   if (unit >= units) return;
-  const int layer = unit / p.rows, row = unit - layer * p.rows;
+  const int grp = unit / p.rows, row = unit - grp * p.rows;
+  const int l0 = LG * grp;
+  const int nl = p.n_layers - l0 < LG ? p.n_layers - l0 : LG;
   const int seq = row / p.n_q;
-  const AttnLayer& L = p.layer[layer];
   int n_win;
   const int64_t t0 = window_start(p, row, n_win);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
@@ -350,18 +370,21 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
   tile_end = tile_end < p.n_tiles ? tile_end : p.n_tiles;
 
   __shared__ __attribute__((aligned(16))) TileLds s;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  uint4 qb[16];
-  load_q(L.q, row, qb);
   const float sc2 = p.softmax_scale * 1.4426950408889634f;  // logits in the log2 domain
-  float m_run = -INFINITY, l_run = 0.0f;                     // per head l16 (replicated)
-  f32x4_t o[8];                                              // O[4*g4+r][128*wave + 16*nt + l16]
+  uint4 qb[LG][16];
+  float m_run[LG], l_run[LG];  // per head l16 (replicated)
+  f32x4_t o[LG][8];            // O[4*g4+r][128*wave + 16*nt + l16]
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < LG; ++i) {
+    if (i < nl) load_q(p.layer[l0 + i].q, row, qb[i]);
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // selected-entry tiles are software-pipelined: the entries of tile i + 1
-  // and the positions of tile i + 2 are in flight while tile i is computed
   const int last_sel = (tile_end < n_tile_idx ? tile_end : n_tile_idx) - 1;  // last selected-entry tile here
   EntryFetch f;
   int32_t pos_next = -1;
@@ -377,38 +400,51 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
         fetch_entry(p, seq, pos_next, f);
         if (tile + 2 <= last_sel) pos_next = tile_position(p, tile + 2, row);
       }
+#pragma unroll
+      for (int i = 0; i < LG; ++i)
+        if (i < nl) tile_step(s, qb[i], nullptr, row, sc2, m_run[i], l_run[i], o[i]);
     } else {
-      load_window(p, L, tile - n_tile_idx, seq, t0, n_win, s);
-    }
-    tile_step(s, qb, nullptr, row, sc2, m_run, l_run, o);
-  }
-
-  if (p.max_splits == 1) {  // whole row in this workgroup: write the output
-    float l_out[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) l_out[r] = __shfl(l_run, 4 * g4 + r, 64);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int ch = 128 * wave + 16 * nt + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float inv = l_out[r] > 0.0f ? 1.0f / l_out[r] : 0.0f;
-        L.out[((int64_t)row * kH + 4 * g4 + r) * kD + ch] = o[nt][r] * inv;
+      for (int i = 0; i < LG; ++i) {
+        if (i >= nl) break;
+        if (i > 0) __syncthreads();  // the previous layer's readers of E are done
+        load_window(p, p.layer[l0 + i], tile - n_tile_idx, seq, t0, n_win, s);
+        tile_step(s, qb[i], nullptr, row, sc2, m_run[i], l_run[i], o[i]);
       }
     }
-    return;
   }
-  write_partial(p, unit, split, m_run, l_run, o);
+
+#pragma unroll
+  for (int i = 0; i < LG; ++i) {
+    if (i >= nl) break;
+    if (p.max_splits == 1) {  // whole row in this workgroup: write the output
+      float l_out[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) l_out[r] = __shfl(l_run[i], 4 * g4 + r, 64);
+      float* out = p.layer[l0 + i].out;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int ch = 128 * wave + 16 * nt + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float inv = l_out[r] > 0.0f ? 1.0f / l_out[r] : 0.0f;
+          out[((int64_t)row * kH + 4 * g4 + r) * kD + ch] = o[i][nt][r] * inv;
+        }
+      }
+    } else {
+      write_partial(p, (l0 + i) * p.rows + row, split, m_run[i], l_run[i], o[i]);
+    }
+  }
 }
 
 // Merge of the split partial softmaxes, in split order.  A kernel of its
 // own: the kernel boundary orders the partial writes before these reads on
 // every XCD, which in-kernel device-scope fences would do by writing back
 // the whole L2.  Workgroup (unit, channel quarter): thread t sums channel
-// 128 quarter + t / 2, heads 8 (t % 2) .. +8 (32 contiguous bytes of each
-// partial), with per-head weights exp2(m_s - M) / L that 16 threads work out
-// in LDS from the (m, l) of every split, loaded in one round trip while the
-// partial loads of up to 16 splits are in flight.
+// 128 quarter + t / 2, heads 8 (t % 2) .. +8 (16 contiguous bytes of each
+// partial), with per-head weights l_s exp2(m_s - M) / L that 16 threads work
+// out in LDS from the (m, l) of every split, loaded in one round trip while
+// the partial loads of up to 16 splits are in flight.
 constexpr int kMaxMergeSplits = 64;
 constexpr int kMergeBatch = 16;
 __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
@@ -424,17 +460,16 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
 #pragma unroll
   for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
   for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
-    float4 v[kMergeBatch][2];
+    uint4 v[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       const int s = s0 + u < ns ? s0 + u : ns - 1;
-      const float* ps = pb + (int64_t)s * kPartFloats + ch * kH + h0;
-      v[u][0] = *reinterpret_cast<const float4*>(ps);
-      v[u][1] = *reinterpret_cast<const float4*>(ps + 4);
+      const uint16_t* ps = reinterpret_cast<const uint16_t*>(pb + (int64_t)s * kPartFloats) + ch * kH + h0;
+      v[u] = *reinterpret_cast<const uint4*>(ps);
     }
     if (s0 == 0) {
       for (int i = t; i < ns * kH; i += 256) {  // (split, head) = (i / 16, i % 16)
-        const float* ps = pb + (int64_t)(i / kH) * kPartFloats + kD * kH;
+        const float* ps = pb + (int64_t)(i / kH) * kPartFloats + kPartOWords;
         wgt[i / kH][i % kH] = ps[i % kH];
         lsh[i / kH][i % kH] = ps[kH + i % kH];
       }
@@ -445,9 +480,9 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
         float L = 0.0f;
         for (int s = 0; s < ns; ++s) {
           const float m = wgt[s][t];
-          const float w = m == -INFINITY ? 0.0f : exp2f(m - M);
+          const float w = m == -INFINITY ? 0.0f : exp2f(m - M) * lsh[s][t];
           wgt[s][t] = w;
-          L += w * lsh[s][t];
+          L += w;
         }
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         for (int s = 0; s < ns; ++s) wgt[s][t] *= inv;
@@ -457,9 +492,12 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       if (s0 + u >= ns) break;
-      const float x[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-      for (int h = 0; h < 8; ++h) acc[h] += wgt[s0 + u][h0 + h] * x[h];
+      for (int h = 0; h < 8; ++h) {
+        const half2_t pr = __builtin_bit_cast(half2_t, wd[h >> 1]);
+        acc[h] += wgt[s0 + u][h0 + h] * (float)pr[h & 1];
+      }
     }
   }
   float* dst = p.layer[layer].out + ((int64_t)row * kH + h0) * kD + ch;
@@ -470,7 +508,12 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
 hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   const int units = p.n_layers * p.rows;
   if (units == 0) return hipSuccess;
-  const int gu = (units >= kXcds && p.max_splits > 1) ? (units + kXcds - 1) / kXcds * kXcds : units;
+  // walk form: one layer per workgroup (a pair of layers needs about 320
+  // registers, and the single wave per SIMD that leaves costs more than the
+  // shared dequantisation saves)
+  constexpr int kWalkLG = 1;
+  const int wunits = (p.n_layers + kWalkLG - 1) / kWalkLG * p.rows;
+  const int gu = (wunits >= kXcds && p.max_splits > 1) ? (wunits + kXcds - 1) / kXcds * kXcds : wunits;
   int h = prof_begin(CSA2_K_ATTENTION, stream);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
   if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles) {
@@ -482,7 +525,7 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
     const int per_row = n_tile_idx * n_groups + p.n_layers * (p.n_tiles - n_tile_idx);
     hipLaunchKernelGGL(k_attention_tiles<LG>, dim3((unsigned)(p.rows * per_row)), dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(k_attention, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(k_attention<kWalkLG>, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
   }
   prof_end(h, stream);
   hipError_t e = hipGetLastError();

@@ -128,6 +128,43 @@ __device__ __forceinline__ float quad_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
+// round trips): steps of 1, 2, 4 and 8 lanes inside each row of 16, then the
+// totals of lanes 15 and 31 are broadcast into the rows above them.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// One step of a 64-bit max (kMax) or min scan; lanes without a source keep
+// their own value (the identity is fed in as the old value).
+template <bool kMax, int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_step64(uint64_t x) {
+  const int id = kMax ? 0 : -1;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(id, (int)(uint32_t)x, kCtrl, kRowMask, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(id, (int)(uint32_t)(x >> 32), kCtrl, kRowMask, 0xF, false);
+  const uint64_t y = ((uint64_t)hi << 32) | lo;
+  return kMax ? (y > x ? y : x) : (y < x ? y : x);
+}
+
+// Largest (kMax) or smallest 64-bit value of the wave, in every lane.
+template <bool kMax>
+__device__ __forceinline__ uint64_t wave_reduce64(uint64_t x) {
+  x = dpp_step64<kMax, 0x111, 0xF>(x);
+  x = dpp_step64<kMax, 0x112, 0xF>(x);
+  x = dpp_step64<kMax, 0x114, 0xF>(x);
+  x = dpp_step64<kMax, 0x118, 0xF>(x);
+  x = dpp_step64<kMax, 0x142, 0xA>(x);
+  x = dpp_step64<kMax, 0x143, 0xC>(x);
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);

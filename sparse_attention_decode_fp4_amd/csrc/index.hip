@@ -153,12 +153,7 @@ __device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t
 template <int NW>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_add(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -173,20 +168,7 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, 
 }
 
 __device__ __forceinline__ uint32_t block_incl_scan_256(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < wave; ++i) before += wsum[i];
-  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-  return before + x;
+  return block_incl_scan<4>(v, wsum, total);
 }
 
 // Exact k-th largest of n keys visited by `visit(n, f)` (f(key) per key), by
@@ -232,22 +214,42 @@ __device__ Key radix_kth(Visit visit, uint32_t n, uint32_t want, uint32_t* h256,
 }
 
 // Exact k-th largest of the unique non-zero 64-bit keys held in registers
-// (kPer per thread, 256 threads, zeros for empty slots): radix steps of
-// 11, 11, 10, 11, 11 and 10 bits from the top, ending as soon as the chosen
-// bucket is taken whole.  Returns the k-th key, or the lower edge of a
-// bucket that holds exactly the keys from the top down to the k-th; either
-// way the keys >= the result are the k largest.  `bins` is 2048 words of LDS.
+// (kPer per thread, 256 threads, zeros for empty slots; at least two keys).
+// All keys lie between the smallest and the largest, so they share the bits
+// above the highest bit where those two differ: the radix starts there, with
+// 11-bit steps, and ends as soon as the chosen bucket is taken whole.
+// Returns the k-th key, or the lower edge of a bucket that holds exactly the
+// keys from the top down to the k-th; either way the keys >= the result are
+// the k largest.  `bins` is 2048 words of LDS.
 template <int kPer>
 __device__ uint64_t block_kth_regs(const uint64_t (&key)[kPer], uint32_t want, uint32_t* bins, uint32_t* wsum,
                                    uint32_t* sh) {
-  const int t = threadIdx.x;
-  uint64_t prefix = 0, pmask = 0;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  __shared__ uint64_t mm[2][4];
+  // smallest and largest key
+  uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (key[i] != 0ull && key[i] < lo) lo = key[i];
+    if (key[i] > hi) hi = key[i];
+  }
+  lo = wave_reduce64<false>(lo);
+  hi = wave_reduce64<true>(hi);
+  if (lane == 0) { mm[0][wave] = lo; mm[1][wave] = hi; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    lo = mm[0][w] < lo ? mm[0][w] : lo;
+    hi = mm[1][w] > hi ? mm[1][w] : hi;
+  }
+  int top = 64 - __clzll((long long)(lo ^ hi));  // bits [top - 1, 0] are undecided
+  uint64_t pmask = top >= 64 ? 0ull : ~((1ull << top) - 1ull);
+  uint64_t prefix = lo & pmask;
   uint32_t need = want;
-  int shift = 64;
 #pragma unroll 1
-  for (int step = 0; step < 6; ++step) {
-    const int width = (step == 2 || step == 5) ? 10 : 11;
-    shift -= width;
+  while (top > 0) {
+    const int width = top < 11 ? top : 11;
+    const int shift = top - width;
     const uint32_t nb = 1u << width;
     for (uint32_t i = t; i < 2048; i += 256) bins[i] = 0;
     if (t == 0) sh[0] = 0xFFFFFFFFu;
@@ -278,6 +280,7 @@ __device__ uint64_t block_kth_regs(const uint64_t (&key)[kPer], uint32_t want, u
     prefix |= (uint64_t)digit << shift;
     pmask |= (uint64_t)(nb - 1) << shift;
     need = nneed;
+    top = shift;
     if (need == count) break;  // the whole bucket is taken
   }
   return prefix;
@@ -522,6 +525,12 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
 }
 
 // ------------------------------------------------------------------ select
+__device__ __forceinline__ int32_t item_to_position(const IndexPass& p, int row, uint32_t item) {
+  if (p.source == kItemsDirect) return (int32_t)item;
+  if (p.source == kItemsBlocks) return 8 * p.blocks[(int64_t)row * CSA2_MAX_K + (item >> 3)] + (int32_t)(item & 7u);
+  return p.list[(int64_t)row * p.list_len + item];
+}
+
 __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   const int row = blockIdx.x;
   const int t = threadIdx.x, quarter = t & 3;
@@ -590,6 +599,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
 
   const bool fast = !over && total <= (uint32_t)kSelCap && (total >= k || T0 == -INFINITY);
   uint32_t n_win = 0;
+  bool written = false;  // positions already stored
   if (fast) {
     const bool use_bitmap = n_items <= (int64_t)kBitmapItems;
     if (use_bitmap) {
@@ -666,16 +676,21 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       uint32_t tot;
       uint32_t o = block_incl_scan_256(cnt_t, wsum, tot) - cnt_t;
       n_win = tot;
+      // positions straight from the scan (and into win[] for the pool)
+      int32_t* out_row = p.out + (int64_t)row * p.out_stride;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         uint32_t bits = wb[j];
         while (bits) {
           const int b = __ffs(bits) - 1;
-          win[o++] = (16 * t + j) * 32 + b;
+          const uint32_t item = (16 * t + j) * 32 + b;
+          if (p.out_pool) win[o] = item;
+          out_row[o++] = item_to_position(p, row, item);
           bits &= bits - 1;
         }
       }
-      __syncthreads();
+      if (p.out_pool) __syncthreads();
+      written = true;
     } else {
       // compaction, then a bitonic sort padded to a power of two
 #pragma unroll
@@ -745,16 +760,8 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   }
 
   // positions of the winners, in ascending order
-  const int32_t* blocks = p.blocks;
-  for (uint32_t j = t; j < n_win; j += 256) {
-    const uint32_t item = win[j];
-    int32_t val;
-    if (p.source == kItemsDirect) val = (int32_t)item;
-    else if (p.source == kItemsBlocks)
-      val = 8 * blocks[(int64_t)row * CSA2_MAX_K + (item >> 3)] + (int32_t)(item & 7u);
-    else val = p.list[(int64_t)row * p.list_len + item];
-    p.out[(int64_t)row * p.out_stride + j] = val;
-  }
+  if (!written)
+    for (uint32_t j = t; j < n_win; j += 256) p.out[(int64_t)row * p.out_stride + j] = item_to_position(p, row, win[j]);
   if (!p.block_level) {
     for (uint32_t j = n_win + t; j < k; j += 256) p.out[(int64_t)row * p.out_stride + j] = -1;
   }

@@ -80,8 +80,11 @@ struct AttnLayer {
 };
 constexpr int kMaxAttnLayers = 8;
 constexpr int kAttnSplit = 64;  // candidates per workgroup
-// A partial softmax: O as [512 channels][16 heads] floats, then m[16], l[16].
-constexpr int kPartFloats = kD * kH + 2 * kH;
+// A partial softmax, in 4-byte words: O / l as [512 channels][16 heads] fp16
+// (normalised, so every value is a convex combination of value rows), then
+// m[16] and l[16] as float32.
+constexpr int kPartOWords = kD * kH / 2;
+constexpr int kPartFloats = kPartOWords + 2 * kH;
 struct AttnPass {
   int32_t rows, n_q, n_idx, n_layers;
   SeqArgs seq;                  // a = q_pos0, b = swa_pos0
