@@ -302,9 +302,7 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* state,
 size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entries);
 
 /*
- * Zero a workspace.  Call once after allocating it: the decode indexer keeps
- * per-row counters in it that every call leaves at zero.  (A workspace that
- * was never zeroed still gives exact results, more slowly.)
+ * Zero a workspace (optional: every call initialises what it reads).
  *   workspace  device, 256-byte aligned;  ws_bytes  a multiple of 4
  */
 int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);

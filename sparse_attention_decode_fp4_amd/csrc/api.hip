@@ -32,12 +32,11 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int64_t kMaxEntries = (int64_t)kMaxChunks * kScanChunk;
 constexpr size_t kWsAlign = 256;
 constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of attention partials
-constexpr int64_t kMaxTicketRows = (int64_t)kMaxSeqPerLaunch * kPrefillMinQ;  // decode-path rows per launch
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t samples, sample_done, thresh, seg_count, seg_list, blocks, nsel, partial;
+  size_t thresh, seg_count, seg_list, blocks, nsel, partial;
   size_t pf_sample, pf_thresh, pf_count, pf_list, total;
   int32_t max_chunks;  // scan chunks per row covered by the segment buffers
 };
@@ -49,10 +48,6 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   w.max_chunks = (int32_t)((std::max<int64_t>(max_items, 1) + kScanChunk - 1) / kScanChunk);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
-  // the sample tickets sit at one fixed place for every call (each pass
-  // leaves them at zero for the next)
-  w.sample_done = take((size_t)kMaxTicketRows * 4);
-  w.samples = take((size_t)rows * 2048 * 4);
   w.thresh = take((size_t)rows * 4);
   w.seg_count = take((size_t)rows * w.max_chunks * 4);
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
@@ -183,8 +178,6 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     }
     p.idx_q = a->idx_q + row0 * kHI * kDI;
     p.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;
-    p.samples = at<uint32_t>(ws, w.samples);
-    p.sample_done = at<uint32_t>(ws, w.sample_done);
     p.thresh = at<float>(ws, w.thresh);
     p.seg_count = at<uint32_t>(ws, w.seg_count);
     p.seg_list = at<uint64_t>(ws, w.seg_list);

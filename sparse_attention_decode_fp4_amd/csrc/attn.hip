@@ -297,7 +297,18 @@ __global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
   const int n_groups = (p.n_layers + LG - 1) / LG;
   const int n_sel = n_tile_idx * n_groups;
   const int per_row = n_sel + p.n_layers * n_win_tiles;
-  const int row = blockIdx.x / per_row, j = blockIdx.x - row * per_row;
+  // workgroup ids are dealt round-robin over the 8 XCDs: with 8 or more rows,
+  // all workgroups of a row run on one XCD, which then reads the row's
+  // queries from memory once
+  int row, j;
+  if (p.rows >= kXcds) {
+    const int xcd = blockIdx.x & (kXcds - 1), w = blockIdx.x >> 3;
+    row = xcd + kXcds * (w / per_row);
+    j = w % per_row;
+  } else {
+    row = blockIdx.x / per_row;
+    j = blockIdx.x - row * per_row;
+  }
   if (row >= p.rows) return;
   const int seq = row / p.n_q;
   int n_win;
@@ -523,7 +534,8 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
     constexpr int LG = 2;
     const int n_groups = (p.n_layers + LG - 1) / LG;
     const int per_row = n_tile_idx * n_groups + p.n_layers * (p.n_tiles - n_tile_idx);
-    hipLaunchKernelGGL(k_attention_tiles<LG>, dim3((unsigned)(p.rows * per_row)), dim3(256), 0, stream, p);
+    const int grows = p.rows >= kXcds ? (p.rows + kXcds - 1) / kXcds * kXcds : p.rows;
+    hipLaunchKernelGGL(k_attention_tiles<LG>, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p);
   } else {
     hipLaunchKernelGGL(k_attention<kWalkLG>, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
   }

@@ -7,11 +7,11 @@
 //   s_p = ks_p * sum_h w_h * max(0, q_h . k_p)   over 4 indexer heads.
 //
 // One pass = three kernels over the rows (query rows) of a call:
-//   sample  eight workgroups per row score a strided sample of at most 2,048
-//           of its items; the last to finish sets the row threshold T0: the
-//           lower edge, at 20 key bits, of the key bin holding the k_s-th
-//           largest sample, k_s sized so that about 2.5 k items of the row
-//           reach T0 (every item when the sample is the whole row);
+//   sample  one 1,024-thread workgroup per row scores a strided sample of at
+//           most 1,024 of its items and sets the row threshold T0: the lower
+//           edge, at 20 key bits, of the key bin holding the k_s-th largest
+//           sample, k_s sized so that about 2.5 k items of the row reach T0
+//           (every item when the sample is the whole row);
 //   scan    streams the fp8 keys once (4 lanes per key, 16 B each, fully
 //           coalesced), scores every item with packed f16 dot products
 //           (v_dot2c_f32_f16; fp8 -> f16 is exact) and appends the items
@@ -27,7 +27,7 @@
 
 namespace csa2 {
 
-constexpr int kSample = 2048;       // sampled items per row
+constexpr int kSample = 1024;       // sampled items per row (one per thread of the sample kernel)
 constexpr int kSelCap = 4096;       // candidates the select kernel holds in LDS
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
 constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks gather in one round trip
@@ -302,69 +302,16 @@ __device__ __forceinline__ void sample_plan(int64_t n_items, uint32_t k, int64_t
   }
 }
 
-// Row threshold T0 from the row's sample keys `sk` (8 per thread, 256
-// threads): the lower edge, at 20-bit key precision, of the key bin that
-// holds the k_s-th largest sample; -inf when fewer than k_s samples are
-// valid.  `bins` is 4096 words of LDS.
-__device__ __forceinline__ float row_threshold(const uint32_t (&sk)[8], uint32_t ks, uint32_t* bins, uint32_t* wsum,
-                                               uint32_t* sh) {
-  const int t = threadIdx.x;
-  for (int i = t; i < 4096; i += 256) bins[i] = 0;
-  if (t == 0) { sh[0] = 0xFFFFFFFFu; sh[2] = 0; }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (sk[j]) atomicAdd(&bins[sk[j] >> 20], 1u);
-  __syncthreads();
-  // level 1: top 12 key bits; thread t owns bins 16t .. 16t+15
-  uint32_t hb[16], local = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    hb[j] = bins[16 * t + j];
-    local += hb[j];
-  }
-  uint32_t total;
-  const uint32_t incl = block_incl_scan_256(local, wsum, total);
-  uint32_t run = total - incl;  // samples in bins above 16t + 15
-  if (run < ks && run + local >= ks) {
-    for (int j = 15; j >= 0; --j) {
-      if (run + hb[j] >= ks) { sh[0] = 16 * t + j; sh[1] = ks - run; break; }
-      run += hb[j];
-    }
-  }
-  __syncthreads();
-  const uint32_t b1 = sh[0], need = sh[1];
-  if (b1 == 0xFFFFFFFFu || b1 == 0u) return -INFINITY;  // uniform
-  bins[t] = 0;
-  __syncthreads();
-  // level 2: the next 8 bits, over the samples in bin b1
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if ((sk[j] >> 20) == b1) atomicAdd(&bins[(sk[j] >> 12) & 255u], 1u);
-  __syncthreads();
-  const uint32_t c = bins[t];
-  uint32_t tot2;
-  const uint32_t incl2 = block_incl_scan_256(c, wsum, tot2);
-  const uint32_t above = tot2 - incl2;  // samples of bin b1 in sub-bins above t
-  if (above < need && above + c >= need) sh[2] = t;
-  __syncthreads();
-  const uint32_t key = (b1 << 20) | (sh[2] << 12);
-  return key_to_score(key);
-}
-
-
-// kSampleSplit workgroups per row each score kSample / kSampleSplit items
-// of the row's strided sample (loads issued together) and store their order
-// keys; the last of them to finish (a ticket counter per row, zero between
-// passes: the last workgroup resets it) turns the 2,048 keys into the row
-// threshold T0.  T0 = -inf when there is no sample plan.  Keys and tickets
-// travel as relaxed device-scope atomics, without fences (which would write
-// back and invalidate the L2): a key read early only moves T0, and the
-// select kernel checks that at least k candidates reached T0 before it
-// trusts them, so results never depend on this ordering.
-constexpr int kSampleSplit = 8;
-__global__ __launch_bounds__(256) void k_index_sample(IndexPass p) {
-  const int row = blockIdx.x / kSampleSplit, part = blockIdx.x % kSampleSplit;
+// One workgroup of 1,024 threads per row scores the row's strided sample
+// (4 keys per lane quad, loads issued together), keeps the order keys in LDS
+// and turns them into the row threshold T0: the lower edge, at 20 key bits,
+// of the key bin holding the k_s-th largest sample (a 4,096-bin histogram of
+// the top 12 bits, then 256 bins of the next 8 within the chosen bin).
+// T0 = -inf when there is no sample plan or fewer than k_s valid samples.
+constexpr int kSampleThreads = 1024;
+__global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
+  constexpr int NW = kSampleThreads / 64;
+  const int row = blockIdx.x;
   const int t = threadIdx.x, quarter = t & 3;
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
@@ -373,54 +320,75 @@ __global__ __launch_bounds__(256) void k_index_sample(IndexPass p) {
   uint32_t ks;
   sample_plan(n_items, (uint32_t)p.k, S, ks);
   if (ks == 0) {
-    if (part == 0 && t == 0) p.thresh[row] = -INFINITY;
+    if (t == 0) p.thresh[row] = -INFINITY;
     return;
   }
+  __shared__ uint32_t skey[kSample];
   __shared__ uint32_t bins[4096];
-  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t wsum[NW];
   __shared__ uint32_t sh[3];
-  __shared__ uint32_t ticket;
 
-  half2_t q[kHI][8];
-  float w_mine;
-  load_query_f16(p, row, quarter, q, w_mine);
-  constexpr int U = kSample / kSampleSplit / 64;  // items per lane quad
+  constexpr int U = kSample / (kSampleThreads / 4);  // keys per lane quad
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + quarter * 16;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
-  uint32_t* keys = p.samples + (int64_t)row * kSample;
   u32x4_t raw[U];
   float kv[U];
   bool valid[U];
-  int slot[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    slot[u] = part * (kSample / kSampleSplit) + u * 64 + (t >> 2);
+    const int64_t slot = u * (kSampleThreads / 4) + (t >> 2);
     // S == kSample (a power of two) whenever the sample is strided
-    const int64_t item = slot[u] < S ? (S == n_items ? slot[u] : ((int64_t)slot[u] * n_items) / kSample) : n_items;
+    const int64_t item = slot < S ? (S == n_items ? slot : (slot * n_items) / kSample) : n_items;
     const int64_t pos = item_position(p, row, item, n_items, vis, valid[u]);
     raw[u] = valid[u] ? *reinterpret_cast<const u32x4_t*>(kb + pos * kDI) : u32x4_t{0, 0, 0, 0};
     kv[u] = valid[u] ? sb[pos] : 0.0f;
   }
+  // the query after the keys: its loads overlap theirs
+  half2_t q[kHI][8];
+  float w_mine;
+  load_query_f16(p, row, quarter, q, w_mine);
+  for (int i = t; i < 4096; i += kSampleThreads) bins[i] = 0;
+  if (t == 0) { sh[0] = 0xFFFFFFFFu; sh[2] = 0; }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const float sc = quad_score(q, w_mine, raw[u], kv[u]);
-    if (quarter == 0)
-      __hip_atomic_store(keys + slot[u], valid[u] ? score_key(sc) : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (quarter == 0) skey[u * (kSampleThreads / 4) + (t >> 2)] = valid[u] ? score_key(sc) : 0u;
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's key stores have completed
   __syncthreads();
-  if (t == 0) ticket = __hip_atomic_fetch_add(p.sample_done + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t k0 = skey[t];  // one key per thread (kSample == kSampleThreads)
+  if (k0) atomicAdd(&bins[k0 >> 20], 1u);
   __syncthreads();
-  if (ticket % kSampleSplit != kSampleSplit - 1) return;
-  // last workgroup of the row: thread t takes keys 8t .. 8t+7
-  uint32_t sk[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) sk[j] = __hip_atomic_load(keys + 8 * t + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const float T0 = row_threshold(sk, ks, bins, wsum, sh);
-  if (t == 0) {
-    p.thresh[row] = T0;
-    p.sample_done[row] = 0;  // every workgroup of the row has taken its ticket
+  // level 1: thread t owns bins 4t .. 4t+3
+  const uint4 hb = reinterpret_cast<const uint4*>(bins)[t];
+  const uint32_t hv[4] = {hb.x, hb.y, hb.z, hb.w};
+  const uint32_t local = hb.x + hb.y + hb.z + hb.w;
+  uint32_t total;
+  const uint32_t incl = block_incl_scan<NW>(local, wsum, total);
+  uint32_t run = total - incl;  // samples in bins above 4t + 3
+  if (run < ks && run + local >= ks) {
+    for (int j = 3; j >= 0; --j) {
+      if (run + hv[j] >= ks) { sh[0] = 4 * t + j; sh[1] = ks - run; break; }
+      run += hv[j];
+    }
   }
+  __syncthreads();
+  const uint32_t b1 = sh[0], need = sh[1];
+  if (b1 == 0xFFFFFFFFu || b1 == 0u) {  // fewer than k_s valid samples (uniform)
+    if (t == 0) p.thresh[row] = -INFINITY;
+    return;
+  }
+  if (t < 256) bins[t] = 0;
+  __syncthreads();
+  // level 2: the next 8 bits, over the samples in bin b1
+  if ((k0 >> 20) == b1) atomicAdd(&bins[(k0 >> 12) & 255u], 1u);
+  __syncthreads();
+  const uint32_t c = t < 256 ? bins[t] : 0u;
+  uint32_t tot2;
+  const uint32_t incl2 = block_incl_scan<NW>(c, wsum, tot2);
+  const uint32_t above = tot2 - incl2;  // samples of bin b1 in sub-bins above t
+  if (t < 256 && above < need && above + c >= need) sh[2] = t;
+  __syncthreads();
+  if (t == 0) p.thresh[row] = key_to_score((b1 << 20) | (sh[2] << 12));
 }
 
 // ------------------------------------------------------------------ scan
@@ -449,11 +417,9 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   const int quarter = threadIdx.x & 3;
   const int sub = threadIdx.x >> 2;  // item within a 64-item step
   const int seq = row / p.n_q;
-  half2_t q[kHI][8];
-  float w_mine;
-  load_query_f16(p, row, quarter, q, w_mine);
-  const float T0 = p.thresh[row];
   uint64_t* seg = p.seg_list + ((int64_t)row * p.max_chunks + chunk) * kSeg;
+  half2_t q[kHI][8];
+  float w_mine, T0;  // loaded after the first keys: their loads overlap
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
   // (used by the kDirect loads only)
@@ -505,10 +471,12 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
     }
   };
   constexpr int kStep = 64 * U;
-  __syncthreads();  // n_hit is initialised
   Batch A, Bb;
   int64_t it = base;
   load(A, it);
+  load_query_f16(p, row, quarter, q, w_mine);
+  T0 = p.thresh[row];
+  __syncthreads();  // n_hit is initialised
   while (true) {
     const int64_t nxt = it + kStep;
     if (nxt < end) load(Bb, nxt);
@@ -798,7 +766,7 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   const int scan_per_row = (int)((p.max_items + kScanChunk - 1) / kScanChunk);
   const int gr = grid_rows(p.rows);
   int h = prof_begin(CSA2_K_INDEX_SAMPLE, stream);
-  hipLaunchKernelGGL(k_index_sample, dim3((unsigned)(p.rows * kSampleSplit)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(k_index_sample, dim3((unsigned)p.rows), dim3(kSampleThreads), 0, stream, p);
   prof_end(h, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

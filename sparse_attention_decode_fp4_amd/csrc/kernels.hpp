@@ -44,8 +44,6 @@ struct IndexPass {
   const int32_t* nsel;         // kItemsBlocks: [rows] number of selected blocks
   int64_t max_items;           // items per row the grid covers
   // workspace
-  uint32_t* samples;           // [rows][2048] order keys of the sampled items
-  uint32_t* sample_done;       // [rows] sample tickets (zero once, then counts up by 8 per pass)
   float* thresh;               // [rows] sampled threshold
   uint32_t* seg_count;         // [rows][max_chunks]
   uint64_t* seg_list;          // [rows][max_chunks][kSeg]
