@@ -7,8 +7,10 @@
 //   s_p = ks_p * sum_h w_h * max(0, q_h . k_p)   over 4 indexer heads.
 //
 // One pass = three kernels over the rows (query rows) of a call:
-//   sample  one 1,024-thread workgroup per row scores a strided sample of at
-//           most 1,024 of its items and sets the row threshold T0: the lower
+//   sample  one 1,024-thread workgroup per row scores a sample of at most
+//           2,048 of its items, 256 evenly spaced runs of 8 (fp8 MFMA: the
+//           sample only steers the threshold) and sets the row threshold T0:
+//           the lower
 //           edge, at 20 key bits, of the key bin holding the k_s-th largest
 //           sample, k_s sized so that about 2.5 k items of the row reach T0
 //           (every item when the sample is the whole row);
@@ -27,7 +29,7 @@
 
 namespace csa2 {
 
-constexpr int kSample = 1024;       // sampled items per row (one per thread of the sample kernel)
+constexpr int kSample = 2048;       // sampled items per row (two per thread of the sample kernel)
 constexpr int kSelCap = 4096;       // candidates the select kernel holds in LDS
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
 constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks gather in one round trip
@@ -302,17 +304,39 @@ __device__ __forceinline__ void sample_plan(int64_t n_items, uint32_t k, int64_t
   }
 }
 
-// One workgroup of 1,024 threads per row scores the row's strided sample
-// (4 keys per lane quad, loads issued together), keeps the order keys in LDS
-// and turns them into the row threshold T0: the lower edge, at 20 key bits,
-// of the key bin holding the k_s-th largest sample (a 4,096-bin histogram of
-// the top 12 bits, then 256 bins of the next 8 within the chosen bin).
-// T0 = -inf when there is no sample plan or fewer than k_s valid samples.
+// Item of sample slot `slot` (< S): every item when the sample is the whole
+// row, otherwise kSample / kSampleRun evenly spaced runs of kSampleRun
+// consecutive items, so the sampled keys fill whole cache lines.
+constexpr int kSampleRun = 8;
+__device__ __forceinline__ int64_t sample_item(int64_t slot, int64_t S, int64_t n_items) {
+  if (S == n_items) return slot;
+  // S == kSample < n_items here
+  return ((slot / kSampleRun) * n_items) / (kSample / kSampleRun) + slot % kSampleRun;
+}
+
+// One workgroup of 1,024 threads per row scores the row's sample of 2,048
+// keys (256 runs of 8) and turns the order keys, kept in LDS, into the row threshold
+// T0: the lower edge, at 20 key bits, of the key bin holding the k_s-th
+// largest sample (a 4,096-bin histogram of the top 12 bits, then 256 bins of
+// the next 8 within the chosen bin).  T0 = -inf when there is no sample plan
+// or fewer than k_s valid samples.
+//
+// The sample scores only steer T0 (the select kernel checks that at least k
+// candidates reached it), so they are computed on fp8 MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales) rather than with the scan's
+// VALU arithmetic: one MFMA scores 32 sampled keys (B columns) against the
+// row's 4 query heads (A rows 0..3, rows 4..31 zero), so the 2,048 keys take
+// 64 MFMAs instead of the VALU work of one CU for 2,048 quad scores.
 constexpr int kSampleThreads = 1024;
+constexpr uint32_t kMfmaUnitScales = 0x7F7F7F7Fu;  // E8M0 127 = 1.0 in every byte
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
 __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   constexpr int NW = kSampleThreads / 64;
+  constexpr int kTilesPerWave = kSample / 32 / NW;  // 32-key MFMA tiles per wave
   const int row = blockIdx.x;
-  const int t = threadIdx.x, quarter = t & 3;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
@@ -323,40 +347,63 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
     if (t == 0) p.thresh[row] = -INFINITY;
     return;
   }
-  __shared__ uint32_t skey[kSample];
+  __shared__ uint32_t skey[kSample + 32];  // + a slot per lane for the lanes without a key
   __shared__ uint32_t bins[4096];
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t sh[3];
 
-  constexpr int U = kSample / (kSampleThreads / 4);  // keys per lane quad
-  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + quarter * 16;
+  // B operands: lane (l32, half) holds channels 32 half .. +32 of key l32 of
+  // each tile (loads issued first: they do not depend on the query)
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + 32 * half;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
-  u32x4_t raw[U];
-  float kv[U];
-  bool valid[U];
+  v8i_t B[kTilesPerWave];
+  float kv[kTilesPerWave];
+  bool valid[kTilesPerWave];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t slot = u * (kSampleThreads / 4) + (t >> 2);
-    // S == kSample (a power of two) whenever the sample is strided
-    const int64_t item = slot < S ? (S == n_items ? slot : (slot * n_items) / kSample) : n_items;
+  for (int u = 0; u < kTilesPerWave; ++u) {
+    const int64_t slot = (wave * kTilesPerWave + u) * 32 + l32;
+    const int64_t item = slot < S ? sample_item(slot, S, n_items) : n_items;
     const int64_t pos = item_position(p, row, item, n_items, vis, valid[u]);
-    raw[u] = valid[u] ? *reinterpret_cast<const u32x4_t*>(kb + pos * kDI) : u32x4_t{0, 0, 0, 0};
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (valid[u]) {
+      lo = *reinterpret_cast<const uint4*>(kb + pos * kDI);
+      hi = *reinterpret_cast<const uint4*>(kb + pos * kDI + 16);
+    }
+    B[u] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     kv[u] = valid[u] ? sb[pos] : 0.0f;
   }
-  // the query after the keys: its loads overlap theirs
-  half2_t q[kHI][8];
-  float w_mine;
-  load_query_f16(p, row, quarter, q, w_mine);
+  // A operand: row l32 < 4 is query head l32 (channels 32 half .. +32)
+  v8i_t A = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (l32 < kHI) {
+    const uint8_t* src = p.idx_q + ((int64_t)row * kHI + l32) * kDI + 32 * half;
+    const uint4 lo = *reinterpret_cast<const uint4*>(src), hi = *reinterpret_cast<const uint4*>(src + 16);
+    A = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  float w[kHI];
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) w[h] = p.idx_w ? p.idx_w[(int64_t)row * kHI + h] : 1.0f;
   for (int i = t; i < 4096; i += kSampleThreads) bins[i] = 0;
   if (t == 0) { sh[0] = 0xFFFFFFFFu; sh[2] = 0; }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const float sc = quad_score(q, w_mine, raw[u], kv[u]);
-    if (quarter == 0) skey[u * (kSampleThreads / 4) + (t >> 2)] = valid[u] ? score_key(sc) : 0u;
+  for (int u = 0; u < kTilesPerWave; ++u) {
+    v16f_t acc = {};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B[u], acc, 0, 0, 0, kMfmaUnitScales, 0,
+                                                          kMfmaUnitScales);
+    // The MFMA reads every lane's operands, so it must run with the whole
+    // wave active: the empty asm pins it here, in uniform control flow, and
+    // the store below is unconditional (instead of a branch on the half
+    // that the compiler could sink the MFMA into).
+    asm volatile("" ::"v"(acc));
+    // lanes 0..31 hold rows 0..3 (the heads) of column l32 in acc[0..3]
+    const float sc =
+        kv[u] * (w[0] * fmaxf(acc[0], 0.0f) + w[1] * fmaxf(acc[1], 0.0f) + w[2] * fmaxf(acc[2], 0.0f) +
+                 w[3] * fmaxf(acc[3], 0.0f));
+    skey[half ? kSample + l32 : (wave * kTilesPerWave + u) * 32 + l32] = valid[u] ? score_key(sc) : 0u;
   }
   __syncthreads();
-  const uint32_t k0 = skey[t];  // one key per thread (kSample == kSampleThreads)
+  const uint32_t k0 = skey[2 * t], k1 = skey[2 * t + 1];  // two keys per thread
   if (k0) atomicAdd(&bins[k0 >> 20], 1u);
+  if (k1) atomicAdd(&bins[k1 >> 20], 1u);
   __syncthreads();
   // level 1: thread t owns bins 4t .. 4t+3
   const uint4 hb = reinterpret_cast<const uint4*>(bins)[t];
@@ -381,6 +428,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   __syncthreads();
   // level 2: the next 8 bits, over the samples in bin b1
   if ((k0 >> 20) == b1) atomicAdd(&bins[(k0 >> 12) & 255u], 1u);
+  if ((k1 >> 20) == b1) atomicAdd(&bins[(k1 >> 12) & 255u], 1u);
   __syncthreads();
   const uint32_t c = t < 256 ? bins[t] : 0u;
   uint32_t tot2;

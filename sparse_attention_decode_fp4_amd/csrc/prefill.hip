@@ -189,6 +189,9 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
           }
           sc[i] = ksn * sum;
         }
+        // every lane computes its scores before any per-lane branch: the
+        // MFMA reads all lanes' operands, so it must not be sunk into one
+        asm volatile("" ::"v"(sc[0]), "v"(sc[1]), "v"(sc[2]), "v"(sc[3]));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ql = 64 * wave + 8 * a + 2 * i + half;
@@ -205,26 +208,19 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
           }
         }
       };
-      // software pipeline: the MFMA of tile a + 1 runs under the epilogue of
-      // a (scheduling barriers keep the compiler from serialising them)
+      // software pipeline: the MFMA of tile a + 1 is issued before the
+      // epilogue of tile a, so it runs under it
       v16f_t acc0 = {}, acc1 = {};
       acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[0], B, acc0, 0, 0, 0, kUnitScales, 0, kUnitScales);
 #pragma unroll
       for (int a = 0; a < 8; a += 2) {
         acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 1], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
                                                               kUnitScales);
-        asm volatile("" ::"a"(acc1));  // issued here, not sunk to its first use
-        __builtin_amdgcn_sched_barrier(0);
         epilogue(acc0, a);
-        __builtin_amdgcn_sched_barrier(0);
-        if (a + 2 < 8) {
+        if (a + 2 < 8)
           acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 2], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
                                                                 kUnitScales);
-          asm volatile("" ::"a"(acc0));
-        }
-        __builtin_amdgcn_sched_barrier(0);
         epilogue(acc1, a + 1);
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     buf ^= 1;
