@@ -109,6 +109,7 @@ constexpr int kPfSample = 2048;   // sampled keys per row tile
 constexpr int kPfCap = 4096;      // candidates a row's selection holds in LDS
 constexpr int kPfSplits = 64;     // key ranges (filter workgroups) per row tile, at most
 constexpr int kPfSeg = 128;       // candidates kept per (row, key range)
+constexpr int kPfBitmapItems = 1 << 18;  // rows with at most this many visible keys order winners by bitmap
 struct PrefillPass {
   int32_t rows, n_q, ratio, k, batch;
   int32_t tiles_per_seq, esplit;

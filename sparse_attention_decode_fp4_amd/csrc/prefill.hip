@@ -25,6 +25,7 @@
 //              (VALU scoring, radix steps over recomputed keys): slow, exact,
 //              and reached only when the sample misleads.
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace csa2 {
 
@@ -308,22 +309,6 @@ __global__ __launch_bounds__(256) void k_prefill_threshold(PrefillPass p) {
 }
 
 // ------------------------------------------------------------------ select
-__device__ __forceinline__ uint32_t pf_scan_256(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < wave; ++i) before += wsum[i];
-  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-  return before + x;
-}
 
 // Exact score of key `pos` for a row whose query (16 channels per lane, 4
 // heads) sits in q; a lane quad scores one key.  Mirrors the decode scan.
@@ -368,16 +353,19 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
   const uint32_t need_all = vis < (int64_t)k ? (uint32_t)vis : k;
   int32_t* out = p.out + row * p.out_stride;
 
-  __shared__ uint64_t lc[kPfCap];
+  __shared__ uint64_t lc[kPfCap];  // candidates; after the band is settled, the position bitmap
   __shared__ uint32_t win[CSA2_MAX_K];
   __shared__ uint32_t bt[kPfCap];
   __shared__ uint32_t h256[256];
+  __shared__ uint32_t h2048[2048];
   __shared__ uint32_t wsum[4];
+  __shared__ uint32_t sh3[3];
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need;
   __shared__ uint32_t seg_start[kPfSplits + 1];
 
-  // exact k-th largest over n keys from `get`, by 8-bit radix steps
+  // exact k-th largest over n keys from `get`, by 8-bit radix steps (the
+  // exact-recompute path only)
   auto radix_kth = [&](auto get, uint32_t n, uint32_t want) -> uint64_t {
     if (t == 0) { sh_kth = 0; sh_need = want; }
     for (int shift = 56; shift >= 0; shift -= 8) {
@@ -387,28 +375,18 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
       const uint64_t hmask = (shift == 56) ? 0ull : (~0ull << (shift + 8));
       get(n, [&](uint32_t g, uint64_t key) {
         (void)g;
-        if ((key & hmask) == prefix) hist_add(h256, (uint32_t)(key >> shift) & 255u);
+        if ((key & hmask) == prefix) atomicAdd(&h256[(uint32_t)(key >> shift) & 255u], 1u);
       });
       __syncthreads();
-      if (t < 64) {
-        const uint32_t nd = sh_need;
-        const uint32_t c0 = h256[4 * t], c1 = h256[4 * t + 1], c2 = h256[4 * t + 2], c3 = h256[4 * t + 3];
-        const uint32_t mine = c0 + c1 + c2 + c3;
-        uint32_t x = mine;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t y = __shfl_down(x, d, 64);
-          if (t + d < 64) x += y;
-        }
-        uint32_t ab = x - mine;
-        const uint32_t cs[4] = {c0, c1, c2, c3};
-        for (int j = 3; j >= 0; --j) {
-          if (ab < nd && ab + cs[j] >= nd) {
-            sh_need = nd - ab;
-            sh_kth = prefix | ((uint64_t)(4 * t + j) << shift);
-          }
-          ab += cs[j];
-        }
+      const uint32_t c = h256[t];
+      uint32_t tot;
+      const uint32_t incl = block_incl_scan_256(c, wsum, tot);
+      const uint32_t above = tot - incl;  // keys in digits above t
+      const uint32_t nd = sh_need;
+      __syncthreads();
+      if (above < nd && above + c >= nd) {
+        sh_need = nd - above;
+        sh_kth = prefix | ((uint64_t)t << shift);
       }
       __syncthreads();
     }
@@ -438,54 +416,93 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
 
-  // segment counts of this row (one per key range of the filter pass)
-  uint32_t seg = t < p.esplit ? p.count[row * kPfSplits + t] : 0u;
-  const bool seg_over = __syncthreads_or(seg > (uint32_t)kPfSeg);
+  // segment counts and every segment slot in one round trip: thread t takes
+  // slots 32 (t % 4) .. +32 of segment t / 4 (kPfSplits = 64 segments)
+  const int sgi = t >> 2;
+  const uint32_t seg = sgi < p.esplit ? p.count[row * kPfSplits + sgi] : 0u;
+  uint64_t sv[kPfSeg / 4];
+  if (sgi < p.esplit) {
+    const uint64_t* src = p.list + (row * kPfSplits + sgi) * kPfSeg + 32 * (t & 3);
+#pragma unroll
+    for (int i = 0; i < kPfSeg / 4; i += 2) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + i);
+      sv[i] = ((uint64_t)v.y << 32) | v.x;
+      sv[i + 1] = ((uint64_t)v.w << 32) | v.z;
+    }
+  }
+  const bool seg_over = __syncthreads_or((t & 3) == 0 && seg > (uint32_t)kPfSeg);
   uint32_t cnt;
-  const uint32_t seg_off = pf_scan_256(seg, wsum, cnt) - seg;
-  bool fast = !seg_over && cnt >= need_all && cnt <= (uint32_t)kPfCap;
+  const uint32_t mine = (t & 3) == 0 ? seg : 0u;
+  const uint32_t seg_off = block_incl_scan_256(mine, wsum, cnt) - mine;
+  // a row with every visible key listed (vis <= k) must list no more than k
+  bool fast = !seg_over && cnt >= need_all && cnt <= (uint32_t)kPfCap && (vis > (int64_t)k || cnt <= k);
   uint32_t n_win = 0;
   if (fast) {
-    if (t < p.esplit) seg_start[t] = seg_off;
+    if ((t & 3) == 0 && sgi < p.esplit) seg_start[sgi] = seg_off;
     if (t == 0) seg_start[p.esplit] = cnt;
     __syncthreads();
-    for (uint32_t g = t; g < cnt; g += 256) {
-      int lo = 0, hi = p.esplit - 1;  // last segment starting at or before g
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seg_start[mid] <= g) lo = mid; else hi = mid - 1;
+    if (sgi < p.esplit) {
+      const uint32_t base = seg_start[sgi], n = seg_start[sgi + 1] - base;
+#pragma unroll
+      for (int i = 0; i < kPfSeg / 4; ++i) {
+        const uint32_t slot = 32 * (t & 3) + i;
+        if (slot < n) lc[base + slot] = sv[i];
       }
-      lc[g] = p.list[(row * kPfSplits + lo) * kPfSeg + (g - seg_start[lo])];
     }
     __syncthreads();
+    constexpr int kPer = kPfCap / 256;
+    uint64_t key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t g = t + 256 * i;
+      key[i] = g < cnt ? lc[g] : 0ull;  // 0 is below every candidate key
+    }
+    if (t == 0) sh_need = 0;
     if (vis <= (int64_t)k) {  // threshold -inf: the list is every visible key
-      for (uint32_t g = t; g < cnt; g += 256) win[g] = select_key_pos(lc[g]);
-      n_win = cnt;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (key[i]) win[atomicAdd(&sh_need, 1u)] = select_key_pos(key[i]);
+      __syncthreads();
+      n_win = sh_need;
     } else {
       // MFMA scores are not binary32-exact (error up to ~2.5e-5 of the sum
       // of |products|): they settle only the clear winners and losers.  Keys
       // within 2^-8 of the MFMA k-th score are rescored exactly on VALU.
-      const uint64_t kth_m = radix_kth([&](uint32_t n, auto&& f) { for (uint32_t g = t; g < n; g += 256) f(g, lc[g]); }, cnt, k);
+      const uint64_t kth_m = block_min_at_least<kPer>(key, block_kth_regs<kPer>(key, k, h2048, wsum, sh3));
       const float sk = key_to_score((uint32_t)(kth_m >> 32));
       const float mg = fabsf(sk) * 0.00390625f;
       const uint32_t lo_key = score_key(sk - mg), hi_key = score_key(sk + mg);
       // keys below the list's threshold are unknown: the band must sit above it
       if (!(sk - mg >= p.thresh[row])) fast = false;
+      uint32_t oa = 0, ob = 0, n_band = 0;
       if (fast) {
-        // clear winners first, band members compacted into bt
-        uint32_t n_band = 0;
-        for (uint32_t g0 = 0; g0 < cnt; g0 += 256) {
-          const uint32_t g = g0 + t;
-          const uint32_t sk32 = g < cnt ? (uint32_t)(lc[g] >> 32) : 0u;
-          const bool a = g < cnt && sk32 > hi_key;
-          const bool b = g < cnt && sk32 >= lo_key && sk32 <= hi_key;
-          uint32_t na, nbnd;
-          const uint32_t oa = pf_scan_256(a ? 1u : 0u, wsum, na) - (a ? 1u : 0u);
-          const uint32_t ob = pf_scan_256(b ? 1u : 0u, wsum, nbnd) - (b ? 1u : 0u);
-          if (a) win[n_win + oa] = select_key_pos(lc[g]);
-          if (b && n_band + ob < (uint32_t)kPfCap) bt[n_band + ob] = select_key_pos(lc[g]);
-          n_win += na;
-          n_band += nbnd;
+        // clear winners to win[], band members to bt[]: counts packed as
+        // (winners << 16) | band in one scan
+        uint32_t na = 0, nb = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const uint32_t s32 = (uint32_t)(key[i] >> 32);
+          na += (key[i] != 0ull && s32 > hi_key) ? 1u : 0u;
+          nb += (key[i] != 0ull && s32 >= lo_key && s32 <= hi_key) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t packed = (na << 16) | nb;
+        const uint32_t off = block_incl_scan_256(packed, wsum, tot) - packed;
+        oa = off >> 16;
+        ob = off & 0xFFFFu;
+        n_win = tot >> 16;
+        n_band = tot & 0xFFFFu;
+        // every clear winner ranks above the k-th key, so n_win < k <= n_win + n_band
+        if (n_win >= k || n_win + n_band < k) fast = false;
+      }
+      if (fast) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const uint32_t s32 = (uint32_t)(key[i] >> 32);
+          if (key[i] == 0ull) continue;
+          if (s32 > hi_key) win[oa++] = select_key_pos(key[i]);
+          else if (s32 >= lo_key) bt[ob++] = select_key_pos(key[i]);
         }
         __syncthreads();
         const uint32_t need = k - n_win;
@@ -493,45 +510,83 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
         for (uint32_t base = 0; base < n_band; base += 64) {
           const uint32_t g = base + (t >> 2);
           const bool valid = g < n_band;
-          const uint32_t pos = valid ? (uint32_t)bt[g] : 0u;
+          const uint32_t pos = valid ? bt[g] : 0u;
           const float sx = pf_quad_score(q, w, kb, sb, pos, valid, quarter);
           if (valid && quarter == 0) lc[g] = select_key(score_key(sx), pos);  // lc reused for exact keys
         }
         __syncthreads();
-        uint64_t kth_x = 0;
-        if (n_band > need)
-          kth_x = radix_kth([&](uint32_t n, auto&& f) { for (uint32_t g = t; g < n; g += 256) f(g, lc[g]); }, n_band, need);
-        for (uint32_t g0 = 0; g0 < n_band; g0 += 256) {
-          const uint32_t g = g0 + t;
-          const bool f = g < n_band && lc[g] >= kth_x;
-          uint32_t nr;
-          const uint32_t o = pf_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
-          if (f) win[n_win + o] = select_key_pos(lc[g]);
-          n_win += nr;
+        uint64_t bkey[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const uint32_t g = t + 256 * i;
+          bkey[i] = g < n_band ? lc[g] : 0ull;
         }
+        uint64_t kth_x = 1ull;  // every band key when the band is no larger than what is missing
+        if (n_band > need) kth_x = block_kth_regs<kPer>(bkey, need, h2048, wsum, sh3);
+        if (t == 0) sh_need = n_win;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (bkey[i] != 0ull && bkey[i] >= kth_x) win[atomicAdd(&sh_need, 1u)] = select_key_pos(bkey[i]);
+        __syncthreads();
+        n_win = sh_need;
       }
     }
   }
   if (fast) {
-    // winners ascending by position (bitonic sort, padded to a power of two)
-    uint32_t n2 = 1;
-    while (n2 < n_win) n2 <<= 1;
-    __syncthreads();
-    for (uint32_t i = n_win + t; i < n2; i += 256) win[i] = 0xFFFFFFFFu;
-    __syncthreads();
-    for (uint32_t size = 2; size <= n2; size <<= 1) {
-      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t i = t; i < n2 / 2; i += 256) {
-          const uint32_t lo = 2 * i - (i & (stride - 1));
-          const uint32_t hi = lo + stride;
-          const bool asc = (lo & size) == 0;
-          const uint32_t a = win[lo], b = win[hi];
-          if ((a > b) == asc) { win[lo] = b; win[hi] = a; }
-        }
-        __syncthreads();
+    if (vis <= (int64_t)kPfBitmapItems) {
+      // winners ascending by position through a bitmap (aliasing lc)
+      uint32_t* bitmap = reinterpret_cast<uint32_t*>(lc);
+      const uint32_t nwords = (uint32_t)((vis + 31) / 32);
+      for (uint32_t i = t; i < nwords; i += 256) bitmap[i] = 0u;
+      __syncthreads();
+      for (uint32_t j = t; j < n_win; j += 256)
+        if (win[j] < (uint32_t)vis) atomicOr(&bitmap[win[j] >> 5], 1u << (win[j] & 31u));
+      __syncthreads();
+      // thread t owns words wpt t .. wpt t + wpt - 1
+      constexpr int kMaxWpt = kPfBitmapItems / 32 / 256;
+      const uint32_t wpt = (nwords + 255) / 256;
+      uint32_t wb[kMaxWpt], cnt_t = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxWpt; ++j) {
+        const uint32_t wi = wpt * t + j;
+        wb[j] = (j < (int)wpt && wi < nwords) ? bitmap[wi] : 0u;
+        cnt_t += __builtin_popcount(wb[j]);
       }
+      uint32_t tot;
+      uint32_t o = block_incl_scan_256(cnt_t, wsum, tot) - cnt_t;
+      n_win = tot;
+#pragma unroll
+      for (int j = 0; j < kMaxWpt; ++j) {
+        uint32_t bits = wb[j];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          out[o++] = (int32_t)((wpt * t + j) * 32 + b);
+          bits &= bits - 1;
+        }
+      }
+      for (uint32_t j = n_win + t; j < k; j += 256) out[j] = -1;
+    } else {
+      // winners ascending by position (bitonic sort, padded to a power of two)
+      uint32_t n2 = 1;
+      while (n2 < n_win) n2 <<= 1;
+      __syncthreads();
+      for (uint32_t i = n_win + t; i < n2; i += 256) win[i] = 0xFFFFFFFFu;
+      __syncthreads();
+      for (uint32_t size = 2; size <= n2; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+          for (uint32_t i = t; i < n2 / 2; i += 256) {
+            const uint32_t lo = 2 * i - (i & (stride - 1));
+            const uint32_t hi = lo + stride;
+            const bool asc = (lo & size) == 0;
+            const uint32_t a = win[lo], b = win[hi];
+            if ((a > b) == asc) { win[lo] = b; win[hi] = a; }
+          }
+          __syncthreads();
+        }
+      }
+      for (uint32_t j = t; j < k; j += 256) out[j] = j < n_win ? (int32_t)win[j] : -1;
     }
-    for (uint32_t j = t; j < k; j += 256) out[j] = j < n_win ? (int32_t)win[j] : -1;
   } else {
     // ---- exact recompute of this row (rare): radix steps over recomputed keys
     const uint32_t nv = (uint32_t)vis;
@@ -554,7 +609,7 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
       const float sx = pf_quad_score(q, w, kb, sb, pos, valid, quarter);
       const bool f = valid && quarter == 0 && select_key(score_key(sx), pos) >= kth;
       uint32_t nr;
-      const uint32_t o = pf_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
+      const uint32_t o = block_incl_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
       if (f && written + o < k) out[written + o] = (int32_t)pos;
       written += nr;
     }
