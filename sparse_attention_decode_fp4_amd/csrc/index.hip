@@ -367,7 +367,11 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   if (base >= n_items) return;
   const int64_t end = base + kScanChunk < n_items ? base + kScanChunk : n_items;
 
+  // candidates are staged in LDS and stored after the loop: a global store
+  // inside it would make every later wait for the key loads also wait for
+  // the store (one counter covers both on gfx9)
   __shared__ uint32_t n_hit;
+  __shared__ uint64_t hits[kSeg];
   if (threadIdx.x == 0) n_hit = 0;
   const int quarter = threadIdx.x & 3;
   const int sub = threadIdx.x >> 2;  // item within a 64-item step
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
       }
       if (take) {
         const uint32_t at = atomicAdd(&n_hit, 1u);
-        if (at < (uint32_t)kSeg) seg[at] = select_key(score_key(sc), (uint32_t)item);
+        if (at < (uint32_t)kSeg) hits[at] = select_key(score_key(sc), (uint32_t)item);
       }
     }
   };
@@ -432,18 +436,23 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   load_query_f16(p, row, quarter, q, w_mine);
   T0 = p.thresh[row];
   __syncthreads();  // n_hit is initialised
+  // kDirect loads past the chunk read zeros without touching memory, so they
+  // are issued unconditionally and every path has the same loads in flight
   while (true) {
     const int64_t nxt = it + kStep;
-    if (nxt < end) load(Bb, nxt);
+    if (kDirect || nxt < end) load(Bb, nxt);
     score(A, it);
     if (nxt >= end) break;
     const int64_t nxt2 = nxt + kStep;
-    if (nxt2 < end) load(A, nxt2);
+    if (kDirect || nxt2 < end) load(A, nxt2);
     score(Bb, nxt);
     if (nxt2 >= end) break;
     it = nxt2;
   }
   __syncthreads();
+  static_assert(kSeg <= 256, "one staged candidate per thread");
+  const uint32_t n = n_hit < (uint32_t)kSeg ? n_hit : (uint32_t)kSeg;
+  if (threadIdx.x < n) seg[threadIdx.x] = hits[threadIdx.x];
   if (threadIdx.x == 0) p.seg_count[(int64_t)row * p.max_chunks + chunk] = n_hit;
 }
 
@@ -522,7 +531,6 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
 
   const bool fast = !over && total <= (uint32_t)kSelCap && (total >= k || T0 == -INFINITY);
   uint32_t n_win = 0;
-  bool written = false;  // positions already stored
   if (fast) {
     const bool use_bitmap = n_items <= (int64_t)kBitmapItems;
     if (use_bitmap) {
@@ -599,21 +607,18 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       uint32_t tot;
       uint32_t o = block_incl_scan_256(cnt_t, wsum, tot) - cnt_t;
       n_win = tot;
-      // positions straight from the scan (and into win[] for the pool)
-      int32_t* out_row = p.out + (int64_t)row * p.out_stride;
+      // winners in order into LDS; the global stores follow in one coalesced
+      // pass (a store inside this loop would wait on every earlier store)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         uint32_t bits = wb[j];
         while (bits) {
           const int b = __ffs(bits) - 1;
-          const uint32_t item = (16 * t + j) * 32 + b;
-          if (p.out_pool) win[o] = item;
-          out_row[o++] = item_to_position(p, row, item);
+          win[o++] = (16 * t + j) * 32 + b;
           bits &= bits - 1;
         }
       }
-      if (p.out_pool) __syncthreads();
-      written = true;
+      __syncthreads();
     } else {
       // compaction, then a bitonic sort padded to a power of two
 #pragma unroll
@@ -683,8 +688,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   }
 
   // positions of the winners, in ascending order
-  if (!written)
-    for (uint32_t j = t; j < n_win; j += 256) p.out[(int64_t)row * p.out_stride + j] = item_to_position(p, row, win[j]);
+  for (uint32_t j = t; j < n_win; j += 256) p.out[(int64_t)row * p.out_stride + j] = item_to_position(p, row, win[j]);
   if (!p.block_level) {
     for (uint32_t j = n_win + t; j < k; j += 256) p.out[(int64_t)row * p.out_stride + j] = -1;
   }
