@@ -49,9 +49,10 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 256 MiB five times (the known-size reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "hier"], default="decode",
                     help="decode: the 128K decode group (default, the headline); prefill: a 4,096-token "
-                         "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers")
+                         "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers; hier: the "
+                         "hierarchical Full layer at 1M context, batch 4")
     return ap.parse_args()
 
 
@@ -185,6 +186,121 @@ def prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def hier(args):
+    """The hierarchical Full layer at 1M context, batch 4: block-key scan and
+    top-2,048 blocks, pool scan and top-512, then attention over the 512
+    entries and the 128-token window.  The indexer keys and block keys are
+    rotated over 8 copies (each 285 MB) so the Infinity Cache cannot hold
+    them between steps; the FP4 main cache is one copy (only 512 entries per
+    query are gathered)."""
+    import torch
+
+    import csa2_inputs as gen
+    import sparse_attention_decode_fp4_amd as csa2
+
+    dev = "cuda"
+    c = gen.CONFIGS[3]
+    B, ctx, C = c["batch"], c["ctx"], 8
+    seed = 1003
+    chunk = 1 << 17
+    nib = torch.empty((B * ctx, 256), dtype=torch.uint8, device=dev)
+    sc = torch.empty((B * ctx, 32), dtype=torch.uint8, device=dev)
+    copies = []
+    zbuf = torch.zeros((chunk, 512), dtype=torch.float32, device=dev)
+    scratch = [torch.empty((chunk, 256), dtype=torch.uint8, device=dev),
+               torch.empty((chunk, 32), dtype=torch.uint8, device=dev)]
+    for ci in range(C):
+        k8 = torch.empty((B * ctx, 64), dtype=torch.uint8, device=dev)
+        ks = torch.empty((B * ctx,), dtype=torch.float32, device=dev)
+        for b in range(B):
+            k = gen.index_key(ctx, seed + 100 * ci, seq=b, device=dev)
+            for r0 in range(0, ctx, chunk):
+                sl = slice(b * ctx + r0, b * ctx + r0 + chunk)
+                if ci == 0:  # copy 0 also writes the FP4 main cache
+                    xs = gen.normal((chunk, 512), seed, "latent", layer=r0 // chunk, seq=b, device=dev)
+                    out_main = [nib[sl], sc[sl]]
+                else:  # other copies encode indexer keys only
+                    xs, out_main = zbuf, scratch
+                csa2.csa2_quantize_kv(xs, k_in=k[r0:r0 + chunk], out=out_main + [k8[sl], ks[sl]])
+            del k
+        bk8, bks = csa2.csa2_build_block_keys(k8, ks, [ctx] * B, ctx)
+        copies.append(csa2.make_kv(nib, sc, k8, ks, ctx, bk8, bks, (ctx + 7) // 8))
+    torch.cuda.synchronize()
+    q_pos0, n_entries, swa_pos0 = [ctx - 1] * B, [ctx] * B, [ctx - 128] * B
+    layer = dict(mode=csa2.MODE_FULL, q=gen.attn_query((B, 1), seed, 0, device=dev),
+                 swa=gen.window_rows(B, 128, seed, 0, device=dev),
+                 out=torch.empty((B, 1, 16, 512), dtype=torch.float32, device=dev),
+                 idx_q=gen.index_query((B, 1), seed, 0, device=dev))
+    ws = csa2.Workspace(B, 1, ctx)
+    states = [csa2.State(B, 1, with_pool=True) for _ in range(C)]
+
+    def step(i):
+        L = dict(layer)
+        L["kv"] = copies[i % C]
+        csa2.csa2_run_group(ws, states[i % C], [L], q_pos0, n_entries, swa_pos0, index_kind=csa2.INDEX_HIER)
+
+    for i in range(C + args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    csa2.csa2_profile_reset()
+    csa2.csa2_profile_enable(True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t0
+    csa2.csa2_profile_enable(False)
+    kern = {}
+    for kid, name in enumerate(csa2.KERNEL_NAMES):
+        ms, n = csa2.csa2_profile_read(kid)
+        if n:
+            kern[name] = {"avg_us": round(1000.0 * ms / n, 3), "launches_per_step": n / args.steps}
+    scan_ms, _ = csa2.csa2_profile_read(csa2.K_INDEX_SCAN)
+    graph_s = None
+    if not args.no_graph:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for g_i in range(C):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    step(g_i)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(s)
+        for i in range(args.warmup):
+            graphs[i % C].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % C].replay()
+        torch.cuda.synchronize()
+        graph_s = time.perf_counter() - t0
+    best_s = min(eager_s, graph_s) if graph_s is not None else eager_s
+    # the two scans of a step: every block key once, then the 16,384-position pool
+    scan_bytes = B * ((ctx + 7) // 8) * KEY_BYTES + B * 2048 * 8 * KEY_BYTES
+    scan_s = scan_ms / 1000.0 / args.steps
+    achieved = scan_bytes / scan_s / 1e9
+    line = {
+        "metric": "CSA2 hierarchical decode query-tokens/s at 1M ctx (batch 4, one Full layer)",
+        "value": round(B * args.steps / best_s, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1000.0 * best_s / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "hierarchical Full layer: 131,072 block keys, top-2,048 blocks, 16,384-position "
+                               "pool, top-512, attention with a 128-token window; batch 4, 1,048,576 entries",
+                   "batch": B, "ctx": ctx, "key_copies": C,
+                   "timing": "graph replay" if best_s == graph_s else "eager"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_index_scan (block scan + pool scan per step)", "bytes_per_step": scan_bytes,
+                     "scan_us_per_step": round(scan_s * 1e6, 3)},
+        "eager_ms_per_step": round(1000.0 * eager_s / args.steps, 4),
+        "graph_ms_per_step": None if graph_s is None else round(1000.0 * graph_s / args.steps, 4),
+        "kernels": kern,
+    }
+    print(json.dumps(line), flush=True)
+
+
 COPY_BYTES = 256 << 20
 
 
@@ -230,6 +346,9 @@ def main():
         return
     if args.workload == "prefill":
         prefill(args)
+        return
+    if args.workload == "hier":
+        hier(args)
         return
     import torch
 

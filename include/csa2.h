@@ -58,6 +58,7 @@ extern "C" {
 #define CSA2_BLOCK 8        /* positions per hierarchical block                     */
 #define CSA2_N_BLOCKS 2048  /* blocks kept by the hierarchical indexer              */
 #define CSA2_MAX_K 2048     /* largest k accepted by csa2_index_topk                */
+#define CSA2_MAX_ENTRIES 8388607 /* cache entries per sequence, at most (2^23 - 1)  */
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -210,7 +211,8 @@ int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, 
  *   q         device bf16 [batch][n_q][16][512]
  *   nib/scale device, sequence s at nib + s*kv_stride*256, scale + s*kv_stride*32
  *   idx       device int32 [batch][n_q][n_idx], -1 = unused; each must be
- *             < n_entries[s] (not checked on the device)
+ *             < the entries present and < CSA2_MAX_ENTRIES (not checked on
+ *             the device)
  *   swa       device bf16, sequence s at swa + s*swa_stride*512; row r holds
  *             token swa_pos0[s] + r; swa_rows rows present
  *   out       device float32 [batch][n_q][16][512] (out)

@@ -45,7 +45,9 @@ struct WsLayout {
 // prefill-path buffers cover `pf_rows` query rows (0 when unused).
 WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   WsLayout w{};
-  w.max_chunks = (int32_t)((std::max<int64_t>(max_items, 1) + kScanChunk - 1) / kScanChunk);
+  // rows of fewer items are cut into more, smaller chunks (scan_chunk_items)
+  w.max_chunks = (int32_t)std::max<int64_t>((std::max<int64_t>(max_items, 1) + kScanChunk - 1) / kScanChunk,
+                                            scan_chunks_min(CSA2_MAX_K));
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
   w.thresh = take((size_t)rows * 4);
@@ -103,6 +105,8 @@ int validate_index(const csa2_index_args* a) {
   for (int s = 0; s < a->batch; ++s) {
     if (a->q_pos0[s] < 0) return fail(CSA2_ERR_ARG, "q_pos0[%d] < 0", s);
     if (a->n_entries[s] < 0) return fail(CSA2_ERR_ARG, "n_entries[%d] < 0", s);
+    if (a->n_entries[s] > CSA2_MAX_ENTRIES)
+      return fail(CSA2_ERR_UNSUPPORTED, "n_entries[%d] above CSA2_MAX_ENTRIES (%d)", s, CSA2_MAX_ENTRIES);
     max_ne = std::max(max_ne, a->n_entries[s]);
   }
   if (max_ne > kMaxEntries) return fail(CSA2_ERR_UNSUPPORTED, "at most %lld entries per sequence", (long long)kMaxEntries);
@@ -371,6 +375,8 @@ int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
   int64_t max_ne = 0;
   for (int s = 0; s < batch; ++s) {
     if (n_entries[s] < 0) return fail(CSA2_ERR_ARG, "n_entries[%d] < 0", s);
+    if (n_entries[s] > CSA2_MAX_ENTRIES)
+      return fail(CSA2_ERR_UNSUPPORTED, "n_entries[%d] above CSA2_MAX_ENTRIES (%d)", s, CSA2_MAX_ENTRIES);
     max_ne = std::max(max_ne, n_entries[s]);
   }
   if (batch > 1 && (k_stride < max_ne || bk_stride < (max_ne + 7) / 8))
@@ -431,6 +437,8 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
   int64_t max_ne = 0;
   for (int s = 0; s < a->batch; ++s) {
     if (a->n_entries[s] < 0) return fail(CSA2_ERR_ARG, "n_entries[%d] < 0", s);
+    if (a->n_entries[s] > CSA2_MAX_ENTRIES)
+      return fail(CSA2_ERR_UNSUPPORTED, "n_entries[%d] above CSA2_MAX_ENTRIES (%d)", s, CSA2_MAX_ENTRIES);
     max_ne = std::max(max_ne, a->n_entries[s]);
   }
   for (int l = 0; l < a->n_layers; ++l) {

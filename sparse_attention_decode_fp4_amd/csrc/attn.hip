@@ -101,14 +101,26 @@ __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, in
   return c < p.n_idx ? p.idx[(int64_t)row * p.n_idx + c] : -1;
 }
 
+// Every load of an entry is an unconditional buffer load on a descriptor
+// at the sequence start: an empty slot uses the entry index
+// CSA2_MAX_ENTRIES, whose offsets equal the descriptors' ranges, so the
+// hardware returns zeros without touching memory.  No load waits on another.
 __device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t pos, EntryFetch& f) {
   const int quarter = threadIdx.x & 3;
   f.valid = pos >= 0;
-  const int64_t ent = (int64_t)seq * p.kv_stride + (f.valid ? pos : 0);
-  const uint8_t* nb = p.nib + ent * CSA2_NIB_BYTES + quarter * 64;
+  const int64_t s0 = (int64_t)seq * p.kv_stride;
+  const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.nib + s0 * CSA2_NIB_BYTES), 0, CSA2_MAX_ENTRIES * CSA2_NIB_BYTES, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.scale + s0 * CSA2_SCALE_BYTES), 0, CSA2_MAX_ENTRIES * CSA2_SCALE_BYTES, kRawBufferWord3);
+  const uint32_t e = f.valid ? (uint32_t)pos : (uint32_t)CSA2_MAX_ENTRIES;
+  const u32x2_t sc = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(e * CSA2_SCALE_BYTES) + quarter * 8, 0, 0);
+  f.sc = make_uint2(sc[0], sc[1]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.raw[i] = f.valid ? *reinterpret_cast<const uint4*>(nb + 16 * i) : make_uint4(0, 0, 0, 0);
-  f.sc = f.valid ? *reinterpret_cast<const uint2*>(p.scale + ent * CSA2_SCALE_BYTES + quarter * 8) : make_uint2(0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(e * CSA2_NIB_BYTES) + quarter * 64 + 16 * i, 0, 0);
+    f.raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 // Dequantise a fetched entry into its row of E (zeros for an empty slot).
@@ -132,20 +144,27 @@ __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
 }
 
 // A window tile into E: thread t copies row t / 4, channels 128 (t % 4) ..
+// The loads go through a descriptor that starts at the query's first window
+// row and ends after its last, so rows past the window read as zeros and all
+// sixteen loads are issued before any wait.
 __device__ __forceinline__ void load_window(const AttnPass& p, const AttnLayer& L, int wtile, int seq, int64_t t0,
                                             int n_win, TileLds& s) {
   const int er = threadIdx.x >> 2, quarter = threadIdx.x & 3;
   uint16_t* dst = s.E + er * kEStride + quarter * 128;
   const int wi = wtile * kAttnSplit + er;
-  const bool valid = wi < n_win;
-  const int64_t r = t0 + wi - p.seq.b[seq];
-  const uint16_t* src = L.swa + ((int64_t)seq * p.swa_stride + (valid ? r : 0)) * kD + quarter * 128;
+  const int64_t r0 = t0 - p.seq.b[seq];
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(L.swa + ((int64_t)seq * p.swa_stride + r0) * kD), 0, n_win * kD * 2, kRawBufferWord3);
+  const int off = wi * kD * 2 + quarter * 256;
   uint4 v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = valid ? *reinterpret_cast<const uint4*>(src + 8 * i) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 16; ++i) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16 * i, 0, 0);
+    v[i] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = v[i];
-  if (quarter == 0) s.row_ok[er] = valid ? 1 : 0;
+  if (quarter == 0) s.row_ok[er] = wi < n_win ? 1 : 0;
 }
 
 // Gather tile `tile` (selected entries first, then window rows) into E.
@@ -363,6 +382,13 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
       const int xcd = lin & (kXcds - 1), w = lin >> 3;
       unit = xcd + kXcds * (w / p.max_splits);
       split = w % p.max_splits;
+    } else if (units >= kXcds) {
+      // one workgroup per unit: each XCD takes a contiguous range of units,
+      // so the queries resident on it together are consecutive tokens whose
+      // windows overlap in all but one row, and the rows come from its L2
+      const int xcd = lin & (kXcds - 1), w = lin >> 3;
+      unit = xcd * ((units + kXcds - 1) / kXcds) + w;
+      split = 0;
     } else {
       unit = lin / p.max_splits;
       split = lin % p.max_splits;
@@ -524,7 +550,7 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   // shared dequantisation saves)
   constexpr int kWalkLG = 1;
   const int wunits = (p.n_layers + kWalkLG - 1) / kWalkLG * p.rows;
-  const int gu = (wunits >= kXcds && p.max_splits > 1) ? (wunits + kXcds - 1) / kXcds * kXcds : wunits;
+  const int gu = wunits >= kXcds ? (wunits + kXcds - 1) / kXcds * kXcds : wunits;
   int h = prof_begin(CSA2_K_ATTENTION, stream);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
   if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles) {

@@ -13,6 +13,12 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor word 3 for untyped (raw) buffer access on gfx9 parts;
+// the cache-policy bit of nontemporal raw buffer loads.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kLoadNonTemporal = 2;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kD = CSA2_D_LATENT;

@@ -31,7 +31,6 @@
 namespace csa2 {
 
 constexpr int kSample = 2048;       // sampled items per row (two per thread of the sample kernel)
-constexpr int kSelCap = 4096;       // candidates the select kernel holds in LDS
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
 constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks gather in one round trip
 
@@ -347,9 +346,6 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
 }
 
 // ------------------------------------------------------------------ scan
-// Buffer descriptor word 3 for untyped (raw) buffer access on gfx9 parts.
-constexpr int kRawBufferWord3 = 0x00020000;
-constexpr int kLoadNonTemporal = 2;  // cache-policy bit of raw buffer loads
 
 // Workgroup (row, chunk of kScanChunk items).  kDirect: item i is position
 // i (flat keys or block keys); keys and scales are read through buffer
@@ -363,9 +359,10 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   if (row >= p.rows) return;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
-  const int64_t base = (int64_t)chunk * kScanChunk;
+  const int64_t csize = scan_chunk_items(n_items, p.k);
+  const int64_t base = (int64_t)chunk * csize;
   if (base >= n_items) return;
-  const int64_t end = base + kScanChunk < n_items ? base + kScanChunk : n_items;
+  const int64_t end = base + csize < n_items ? base + csize : n_items;
 
   // candidates are staged in LDS and stored after the loop: a global store
   // inside it would make every later wait for the key loads also wait for
@@ -463,13 +460,18 @@ __device__ __forceinline__ int32_t item_to_position(const IndexPass& p, int row,
   return p.list[(int64_t)row * p.list_len + item];
 }
 
+// kPer candidates per thread, 256 kPer in all: 16 serves k <= 1,024 (about
+// 2.5 k candidates reach the sampled threshold), 32 the 2,048-block stage
+template <int kPer>
 __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
+  constexpr int kSelCap = 256 * kPer;
   const int row = blockIdx.x;
   const int t = threadIdx.x, quarter = t & 3;
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
-  const int nch = (int)((n_items + kScanChunk - 1) / kScanChunk);
+  const int64_t csize = scan_chunk_items(n_items, p.k);
+  const int nch = (int)((n_items + csize - 1) / csize);
   const uint32_t k = (uint32_t)p.k;
   const float T0 = n_items > 0 ? p.thresh[row] : -INFINITY;  // written by the row's first scan chunk
 
@@ -576,7 +578,6 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
     }
     __syncthreads();
     // candidates into registers: thread t holds lc[t + 256 i]
-    constexpr int kPer = kSelCap / 256;
     uint64_t key[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -722,7 +723,11 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream
 
 hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   if (p.rows == 0 || p.max_items == 0) return hipSuccess;
-  const int scan_per_row = (int)((p.max_items + kScanChunk - 1) / kScanChunk);
+  // chunks per row, at most: scan_chunk_items keeps a row of n items within
+  // max(scan_chunks_min(k), ceil(n / kScanChunk)) chunks
+  const int scan_per_row =
+      std::max<int>(scan_chunks_min(p.k), (int)((p.max_items + kScanChunk - 1) / kScanChunk));
+  if (scan_per_row > p.max_chunks) return hipErrorInvalidValue;
   const int gr = grid_rows(p.rows);
   int h = prof_begin(CSA2_K_INDEX_SAMPLE, stream);
   hipLaunchKernelGGL(k_index_sample, dim3((unsigned)p.rows), dim3(kSampleThreads), 0, stream, p);
@@ -740,7 +745,10 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   h = prof_begin(CSA2_K_INDEX_SELECT, stream);
-  hipLaunchKernelGGL(k_index_select, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+  if (p.k > 1024)
+    hipLaunchKernelGGL(k_index_select<32>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(k_index_select<16>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
   prof_end(h, stream);
   return hipGetLastError();
 }

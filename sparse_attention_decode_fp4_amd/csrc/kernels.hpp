@@ -15,7 +15,19 @@ struct SeqArgs {
 
 // Items scored per workgroup of the indexer scan; candidates kept per
 // (row, chunk) segment; chunks per row (items per row <= 8M).
-constexpr int kScanChunk = 2048;
+constexpr int kScanChunk = 2048;  // items per scan workgroup, at most
+// Items per scan chunk of a row with n_items items and top-k: the row is cut
+// into at least kChunksMin(k) chunks (between 128 and kScanChunk items
+// each), so the ~2.5 k keys that reach the sampled threshold fill a chunk's
+// kSeg-slot segment to about a third on average, and a row with at most k
+// items (every item a candidate) has chunks of 128 = kSeg items.
+__host__ __device__ constexpr int scan_chunks_min(int k) { return k <= 512 ? 32 : k <= 1024 ? 64 : 128; }
+__host__ __device__ inline int64_t scan_chunk_items(int64_t n_items, int k) {
+  const int64_t want = (n_items + scan_chunks_min(k) - 1) / scan_chunks_min(k);
+  int64_t c = 128;
+  while (c < want && c < kScanChunk) c <<= 1;
+  return c;
+}
 constexpr int kSeg = 128;
 constexpr int kMaxChunks = 4096;
 constexpr int kMaxPool = CSA2_N_BLOCKS * CSA2_BLOCK;  // 16,384 positions
