@@ -310,6 +310,19 @@ size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entr
 int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Diagnostic: how many query rows, since the workspace was last zeroed by
+ * csa2_workspace_init, had their top-k recomputed exactly because the
+ * candidate list of the threshold pass could not hold the answer (a
+ * segment overflowed, fewer than k keys reached the sampled threshold, or
+ * the prefill MFMA band reached below it).  Results are exact either way;
+ * a count above zero on a steady workload means the slow path is taken.
+ *   workspace  device, the workspace the calls used;  count  host (out)
+ * Waits for the stream.  Errors: CSA2_ERR_ARG / CSA2_ERR_WORKSPACE for bad
+ * pointers, CSA2_ERR_HIP if the copy fails.
+ */
+int csa2_workspace_fallbacks(const void* workspace, uint32_t* count, void* stream);
+
+/*
  * Optional kernel timing, for measurement tools (the pages say nothing about
  * it).  While enabled, each kernel the library launches is bracketed by two
  * HIP events recorded on the launch's own stream; csa2_profile_read waits for

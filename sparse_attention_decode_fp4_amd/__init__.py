@@ -92,6 +92,7 @@ def _load():
         "csa2_struct_size": (ctypes.c_size_t, [_i32]),
         "csa2_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i64]),
         "csa2_workspace_init": (_i32, [_p, ctypes.c_size_t, _p]),
+        "csa2_workspace_fallbacks": (_i32, [_p, ctypes.POINTER(ctypes.c_uint32), _p]),
         "csa2_quantize_kv": (_i32, [_p, _i64, _i64, _i32, _p, _p, _p, _i64, _p, _p, _p]),
         "csa2_build_block_keys": (_i32, [_p, _p, _i32, _p, _i64, _p, _p, _i64, _p]),
         "csa2_index_topk": (_i32, [ctypes.POINTER(IndexArgs), _p, ctypes.c_size_t, _p]),
@@ -164,6 +165,17 @@ class Workspace:
         self.buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
         off = (-self.buf.data_ptr()) % 256
         self.ptr = ctypes.c_void_p(self.buf.data_ptr() + off)
+        _check(lib.csa2_workspace_init(self.ptr, self.nbytes, _stream(stream)))
+
+    def fallbacks(self, stream=None):
+        """Query rows whose top-k took the exact recompute since the workspace
+        was zeroed (waits for the stream)."""
+        n = ctypes.c_uint32(0)
+        _check(lib.csa2_workspace_fallbacks(self.ptr, ctypes.byref(n), _stream(stream)))
+        return int(n.value)
+
+    def reset(self, stream=None):
+        """Zero the workspace, the fallback counter included."""
         _check(lib.csa2_workspace_init(self.ptr, self.nbytes, _stream(stream)))
 
 

@@ -36,7 +36,7 @@ constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of atte
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t thresh, seg_count, seg_list, blocks, nsel, partial;
+  size_t stats, thresh, seg_count, seg_list, blocks, nsel, partial;
   size_t pf_sample, pf_thresh, pf_count, pf_list, total;
   int32_t max_chunks;  // scan chunks per row covered by the segment buffers
 };
@@ -50,6 +50,7 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
                                             scan_chunks_min(CSA2_MAX_K));
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
+  w.stats = take(kWsAlign);  // offset 0 in every layout: the fallback counter
   w.thresh = take((size_t)rows * 4);
   w.seg_count = take((size_t)rows * w.max_chunks * 4);
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
@@ -172,6 +173,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
       f.k_stride = a->k_stride;
       f.sample = at<float>(ws, w.pf_sample);
       f.thresh = at<float>(ws, w.pf_thresh);
+      f.fallbacks = at<uint32_t>(ws, w.stats);
       f.count = at<uint32_t>(ws, w.pf_count);
       f.list = at<uint64_t>(ws, w.pf_list);
       f.out = a->out_idx + row0 * a->k;
@@ -183,6 +185,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     p.idx_q = a->idx_q + row0 * kHI * kDI;
     p.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;
     p.thresh = at<float>(ws, w.thresh);
+    p.fallbacks = at<uint32_t>(ws, w.stats);
     p.seg_count = at<uint32_t>(ws, w.seg_count);
     p.seg_list = at<uint64_t>(ws, w.seg_list);
     p.max_chunks = w.max_chunks;
@@ -342,6 +345,15 @@ int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
     return fail(CSA2_ERR_WORKSPACE, "workspace must be non-NULL, 256-byte aligned, a multiple of 4 bytes");
   hipError_t e = launch_fill_u32(static_cast<uint32_t*>(workspace), ws_bytes / 4, 0u, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "workspace init");
+}
+
+int csa2_workspace_fallbacks(const void* workspace, uint32_t* count, void* stream) {
+  if (!workspace || !count) return fail(CSA2_ERR_ARG, "workspace and count are required");
+  if (!aligned(workspace, kWsAlign)) return fail(CSA2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(count, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "reading the fallback counter");
 }
 
 int csa2_quantize_kv(const float* x, int64_t n_tok, int64_t ld_x, int32_t ratio, uint8_t* nib,

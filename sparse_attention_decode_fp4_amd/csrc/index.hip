@@ -646,6 +646,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
     }
   } else {
     // exact recompute of this row (rare): radix steps over recomputed keys
+    if (t == 0) atomicAdd(p.fallbacks, 1u);
     half2_t q[kHI][8];
     float w_mine;
     load_query_f16(p, row, quarter, q, w_mine);

@@ -57,6 +57,7 @@ struct IndexPass {
   int64_t max_items;           // items per row the grid covers
   // workspace
   float* thresh;               // [rows] sampled threshold
+  uint32_t* fallbacks;         // rows that took the exact recompute (a counter)
   uint32_t* seg_count;         // [rows][max_chunks]
   uint64_t* seg_list;          // [rows][max_chunks][kSeg]
   int32_t max_chunks;
@@ -134,6 +135,7 @@ struct PrefillPass {
   // workspace
   float* sample;                 // [rows][kPfSample]
   float* thresh;                 // [rows]
+  uint32_t* fallbacks;           // rows that took the exact recompute (a counter)
   uint32_t* count;               // [rows][kPfSplits] candidates per segment
   uint64_t* list;                // [rows][kPfSplits][kPfSeg]
   int32_t* out;                  // [rows][out_stride]

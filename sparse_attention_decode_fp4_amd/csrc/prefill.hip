@@ -589,6 +589,7 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
     }
   } else {
     // ---- exact recompute of this row (rare): radix steps over recomputed keys
+    if (t == 0) atomicAdd(p.fallbacks, 1u);
     const uint32_t nv = (uint32_t)vis;
     // visit every visible key: a lane quad per key, 64 keys per step
     auto visit = [&](uint32_t n, auto&& f) {

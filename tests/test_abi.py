@@ -46,6 +46,11 @@ def test_workspace_sizes(m):
     assert 0 < small < big
     assert m.lib.csa2_workspace_init(None, 1024, None) == m.ERR_WORKSPACE
     assert m.lib.csa2_workspace_init(ctypes.c_void_p(0x1001), 1024, None) == m.ERR_WORKSPACE
+    n = ctypes.c_uint32(7)
+    assert m.lib.csa2_workspace_fallbacks(None, ctypes.byref(n), None) == m.ERR_ARG
+    assert m.lib.csa2_workspace_fallbacks(ctypes.c_void_p(0x10000000), None, None) == m.ERR_ARG
+    assert m.lib.csa2_workspace_fallbacks(ctypes.c_void_p(0x10000001), ctypes.byref(n), None) == m.ERR_WORKSPACE
+    assert n.value == 7
 
 
 FAKE = 0x10000000  # aligned, never dereferenced: every call here fails validation first

@@ -133,6 +133,8 @@ def test_config_full_size(csa2, cfg):
                 kinds.append(check_topk(idx[b, 0], ref_idx, oracle.scores(iq, None, rk, rks), 512, ctx,
                                         f"reindex seq {b}"))
     print(f"config {cfg}: {kinds}")
+    # the threshold pass held every row's answer: no exact recompute
+    assert ws.fallbacks() == 0
 
 
 def test_prefill_full_size(csa2):
@@ -180,4 +182,6 @@ def test_prefill_full_size(csa2):
             r = oracle.sparse_swa_attention(gen.bf16_bits(L["q"][:, i:i + 1])[0, 0], sn, ss, np.arange(len(sel)),
                                             gen.bf16_bits(L["swa"])[0], swa_pos0, P + i)
             check_close(outs[j][0, i].cpu().numpy(), r, f"query {i} layer {j}")
-    print("prefill full size:", kinds)
+    nfb = ws.fallbacks()
+    print("prefill full size:", kinds, "exact recomputes:", nfb)
+    assert nfb <= T // 100

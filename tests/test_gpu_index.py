@@ -61,6 +61,8 @@ def test_flat_topk(csa2, n_entries, n_q, ratio, k):
     # workspace left clean: a second call gives the same answer
     out2 = csa2.csa2_index_topk(ws, q, k8, ks, n_entries, q_pos0, stride, ratio=ratio, idx_w=w, k=k)
     assert torch.equal(out, out2)
+    # random keys: every row's candidate list holds its answer (no exact recompute)
+    assert ws.fallbacks() == 0
 
 
 def test_zero_query_picks_first_positions(csa2):
@@ -69,6 +71,9 @@ def test_zero_query_picks_first_positions(csa2):
     ws = csa2.Workspace(1, 1, 5000)
     out = csa2.csa2_index_topk(ws, q, k8, ks, [5000], [4999], 5000)
     assert np.array_equal(out[0, 0].cpu().numpy(), np.arange(512))
+    # every score is 0: all 5,000 keys reach the threshold, the segments
+    # overflow and the row is recomputed exactly (this covers that path)
+    assert ws.fallbacks() == 1
 
 
 def test_equal_scores_tie_to_lower_position(csa2):
@@ -121,6 +126,7 @@ def test_hierarchical_topk(csa2, n_entries):
         if n <= 16384:
             flat = oracle.index_flat(qh[b, 0], None, kb, sb, n)
             assert np.array_equal(ref_idx, flat)
+    assert ws.fallbacks() == 0
 
 
 def test_pool_topk(csa2):
