@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 /* Model constants the kernels are built for. */
 #define CSA2_D_LATENT 512   /* channels of one main-KV latent (key = value)        */
@@ -86,8 +86,8 @@ int csa2_abi_version(void);
 const char* csa2_last_error(void);
 
 /* sizeof() of the argument structs, for bindings to check their layouts:
- * 0 index_args, 1 attn_args, 2 kv, 3 layer, 4 group_state, 5 group_args;
- * 0 for anything else. */
+ * 0 index_args, 1 attn_args, 2 kv, 3 layer, 4 group_state, 5 group_args,
+ * 6 append_args; 0 for anything else. */
 size_t csa2_struct_size(int32_t which);
 
 /*
@@ -213,10 +213,15 @@ int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, 
  *   idx       device int32 [batch][n_q][n_idx], -1 = unused; each must be
  *             < the entries present and < CSA2_MAX_ENTRIES (not checked on
  *             the device)
- *   swa       device bf16, sequence s at swa + s*swa_stride*512; row r holds
- *             token swa_pos0[s] + r; swa_rows rows present
+ *   swa       device bf16, sequence s at swa + s*swa_stride*512.  Linear
+ *             (swa_ring = 0): row r holds token swa_pos0[s] + r, swa_rows rows
+ *             present.  Ring (swa_ring > 0, as csa2_append writes it): token
+ *             t is row t mod swa_ring; swa_pos0 and swa_rows are not read, and
+ *             the caller guarantees the rows of every token a query sees hold
+ *             that token (swa_ring >= n_q + 127 so they are distinct rows)
  *   out       device float32 [batch][n_q][16][512] (out)
- * Errors: CSA2_ERR_ARG when a window row a query needs is not in the buffer.
+ * Errors: CSA2_ERR_ARG when a window row a query needs is not in the buffer
+ * (linear), or swa_ring is below n_q + 127 or not below 2^21 (ring).
  */
 typedef struct csa2_attn_args {
   int32_t batch, n_q, n_idx;  /* n_idx 0..CSA2_MAX_K                                 */
@@ -232,6 +237,7 @@ typedef struct csa2_attn_args {
   int64_t swa_rows;           /* rows present per sequence                            */
   float softmax_scale;
   float* out;
+  int64_t swa_ring;           /* 0: linear window rows; > 0: ring of this many rows   */
 } csa2_attn_args;
 
 int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_bytes, void* stream);
@@ -291,10 +297,67 @@ typedef struct csa2_group_args {
   float softmax_scale;
   int32_t n_layers;
   const csa2_layer* layers;/* host [n_layers]                                         */
+  int64_t swa_ring;        /* window layout of every layer, as in csa2_attn_args      */
 } csa2_group_args;
 
 int csa2_run_group(const csa2_group_args* a, csa2_group_state* state,
                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The write side of one decode step: one new token per sequence goes into
+ * the caches the read side uses.  The cache format is the one
+ * csa2_quantize_kv writes (ai-wave.ru "DeepSeek V4.1-Flash: 1M context, FP4
+ * KV cache ...", fourth paragraph); at ratio 2 two tokens make one entry
+ * (globalfeed.ai "DeepSeek-V4.1-Flash released ...", section "What changed
+ * in the architecture"; the pair mean is a reading); block keys cover 8
+ * entries (agentnet.co.il "DeepSeek launches V4.1-Flash ...", section
+ * "CSA2: compression along the layer axis"); the window keeps the last 128
+ * tokens uncompressed (ai-wave.ru, second paragraph).  For sequence s and
+ * its new token at position pos[s]:
+ *   ratio 1   entry pos is encoded from x, k_in;
+ *   ratio 2   an even pos is held in pending; an odd pos completes entry
+ *             (pos-1)/2 from the pair mean fp32(fp32(held + new) * 0.5);
+ *   blocks    with kv.bk8 set, the block holding a new entry is re-derived
+ *             from its entries present (a trailing block averages those);
+ *   window    with swa set, bf16(x) (round to nearest even) goes to row
+ *             pos mod swa_ring.
+ * Results equal csa2_quantize_kv / csa2_build_block_keys over the whole
+ * token history, byte for byte, when tokens are appended in position order
+ * (entries 8*(e/8) .. e-1 of a block must be in the cache before entry e).
+ *   x          device float32 [batch][512], the new tokens' latents
+ *   k_in       device float32 [batch][64], their indexer keys
+ *   nib..kscale  device cache to write, laid out as csa2_kv (all four
+ *              required); entry e of sequence s must be < stride and
+ *              < CSA2_MAX_ENTRIES
+ *   bk8, bkscale device block keys, as csa2_kv, or NULL
+ *   pending    ratio 2: device float32 [batch][576] (latent, then key) that
+ *              holds an even token until its pair arrives; caller-owned
+ *   swa        device bf16 or NULL: sequence s's ring at swa + s*swa_stride*512
+ *              (swa_stride >= swa_ring >= 128 when batch > 1)
+ * Errors: CSA2_ERR_ARG for missing pointers, negative positions, entries
+ * past stride, a ring under 128 rows; CSA2_ERR_UNSUPPORTED for entries at
+ * or past CSA2_MAX_ENTRIES; CSA2_ERR_HIP for launch failures.
+ */
+typedef struct csa2_append_args {
+  int32_t batch, ratio;       /* ratio 1 or 2                                         */
+  const int64_t* pos;         /* host [batch]: position of each new token             */
+  const float* x;
+  const float* k_in;
+  uint8_t* nib;               /* device, sequence s at + s*stride*256                 */
+  uint8_t* scale;             /* device, sequence s at + s*stride*32                  */
+  uint8_t* k8;                /* device, sequence s at + s*stride*64                  */
+  float* kscale;              /* device, sequence s at + s*stride                     */
+  int64_t stride;             /* entries between sequences                            */
+  uint8_t* bk8;               /* device or NULL, sequence s at + s*bk_stride*64       */
+  float* bkscale;
+  int64_t bk_stride;          /* blocks between sequences                             */
+  float* pending;
+  uint16_t* swa;
+  int64_t swa_stride;         /* rows between sequences                               */
+  int64_t swa_ring;           /* ring rows per sequence (>= 128)                      */
+} csa2_append_args;
+
+int csa2_append(const csa2_append_args* a, void* stream);
 
 /*
  * Workspace bytes sufficient for any call with at most max_batch sequences,
@@ -341,6 +404,7 @@ int csa2_workspace_fallbacks(const void* workspace, uint32_t* count, void* strea
 #define CSA2_K_ATTENTION_MERGE 7
 #define CSA2_K_PREFILL_FILTER 8
 #define CSA2_K_PREFILL_SELECT 9
+#define CSA2_K_APPEND 10
 int csa2_profile_enable(int32_t on);
 int csa2_profile_reset(void);
 int csa2_profile_read(int32_t kernel, double* total_ms, int64_t* launches);

@@ -25,10 +25,10 @@ INDEX_FLAT, INDEX_HIER, INDEX_POOL = 0, 1, 2
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_STATE, ERR_WORKSPACE, ERR_HIP = range(6)
 (K_QUANTIZE, K_BLOCK_KEYS, K_INDEX_SCAN, K_INDEX_SAMPLE, K_INDEX_SELECT, K_ATTENTION,
- K_PREFILL_SAMPLE, K_ATTENTION_MERGE, K_PREFILL_FILTER, K_PREFILL_SELECT) = range(10)
+ K_PREFILL_SAMPLE, K_ATTENTION_MERGE, K_PREFILL_FILTER, K_PREFILL_SELECT, K_APPEND) = range(11)
 KERNEL_NAMES = ["quantize", "block_keys", "index_scan", "index_sample", "index_select", "attention",
-                "prefill_sample", "attention_merge", "prefill_filter", "prefill_select"]
-ABI_VERSION = 1
+                "prefill_sample", "attention_merge", "prefill_filter", "prefill_select", "append"]
+ABI_VERSION = 2
 
 _p = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -47,7 +47,7 @@ class AttnArgs(ctypes.Structure):
     _fields_ = [("batch", _i32), ("n_q", _i32), ("n_idx", _i32), ("q_pos0", _p),
                 ("q", _p), ("nib", _p), ("scale", _p), ("kv_stride", _i64), ("idx", _p),
                 ("swa", _p), ("swa_stride", _i64), ("swa_pos0", _p), ("swa_rows", _i64),
-                ("softmax_scale", _f32), ("out", _p)]
+                ("softmax_scale", _f32), ("out", _p), ("swa_ring", _i64)]
 
 
 class KV(ctypes.Structure):
@@ -69,10 +69,17 @@ class GroupArgs(ctypes.Structure):
     _fields_ = [("batch", _i32), ("n_q", _i32), ("ratio", _i32), ("index_kind", _i32),
                 ("reindex_kind", _i32), ("q_pos0", _p), ("n_entries", _p), ("swa_pos0", _p),
                 ("swa_stride", _i64), ("swa_rows", _i64), ("softmax_scale", _f32),
-                ("n_layers", _i32), ("layers", ctypes.POINTER(Layer))]
+                ("n_layers", _i32), ("layers", ctypes.POINTER(Layer)), ("swa_ring", _i64)]
 
 
-_STRUCTS = [IndexArgs, AttnArgs, KV, Layer, GroupState, GroupArgs]
+class AppendArgs(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("ratio", _i32), ("pos", _p), ("x", _p), ("k_in", _p),
+                ("nib", _p), ("scale", _p), ("k8", _p), ("kscale", _p), ("stride", _i64),
+                ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64), ("pending", _p),
+                ("swa", _p), ("swa_stride", _i64), ("swa_ring", _i64)]
+
+
+_STRUCTS = [IndexArgs, AttnArgs, KV, Layer, GroupState, GroupArgs, AppendArgs]
 
 
 class Csa2Error(RuntimeError):
@@ -99,6 +106,7 @@ def _load():
         "csa2_sparse_swa_attn": (_i32, [ctypes.POINTER(AttnArgs), _p, ctypes.c_size_t, _p]),
         "csa2_run_group": (_i32, [ctypes.POINTER(GroupArgs), ctypes.POINTER(GroupState), _p,
                                   ctypes.c_size_t, _p]),
+        "csa2_append": (_i32, [ctypes.POINTER(AppendArgs), _p]),
         "csa2_profile_enable": (_i32, [_i32]),
         "csa2_profile_reset": (_i32, []),
         "csa2_profile_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
@@ -211,6 +219,31 @@ def csa2_quantize_kv(x, ratio=1, k_in=None, out=None, stream=None):
     return tuple(out)
 
 
+def csa2_append(x, k_in, pos, nib, scale, k8, kscale, stride, *, ratio=1, bk8=None, bkscale=None,
+                bk_stride=0, pending=None, swa=None, swa_ring=0, stream=None):
+    """One decode step's write side: token pos[b] of sequence b (x float32
+    [batch, 512], k_in float32 [batch, 64]) goes into the cache (sequence b
+    at entry offset b * stride), its block key (bk8 / bkscale, optional) and
+    the window ring swa (bf16 [batch, swa_ring, 512], optional).  Ratio 2
+    holds even tokens in pending (float32 [batch, 576])."""
+    _need(x, torch.float32, "x")
+    _need(k_in, torch.float32, "k_in")
+    batch = x.shape[0]
+    a = AppendArgs()
+    a.batch, a.ratio = batch, ratio
+    pp = _host_i64(pos)
+    a.pos = ctypes.cast(pp, _p)
+    a.x, a.k_in = _ptr(x), _ptr(k_in)
+    a.nib, a.scale, a.k8, a.kscale, a.stride = _ptr(nib), _ptr(scale), _ptr(k8), _ptr(kscale), stride
+    a.bk8, a.bkscale, a.bk_stride = _ptr(bk8), _ptr(bkscale), bk_stride
+    a.pending = _ptr(pending)
+    sb = None
+    if swa is not None:
+        sb = _bits16(swa, "swa")
+        a.swa, a.swa_stride, a.swa_ring = _ptr(sb), swa.shape[1], swa_ring
+    _check(lib.csa2_append(ctypes.byref(a), _stream(stream)))
+
+
 def csa2_build_block_keys(k8, kscale, n_entries, k_stride, bk8=None, bkscale=None, bk_stride=None,
                           stream=None):
     """Block keys of batch = len(n_entries) sequences stored k_stride entries apart."""
@@ -259,9 +292,10 @@ def csa2_index_topk(ws, idx_q, k8, kscale, n_entries, q_pos0, k_stride, *, kind=
 
 # --------------------------------------------------------------------- attention
 def csa2_sparse_swa_attn(ws, q, nib, scale, idx, swa, q_pos0, swa_pos0, kv_stride, *,
-                         softmax_scale=1.0, out=None, stream=None):
+                         softmax_scale=1.0, out=None, swa_ring=0, stream=None):
     """q bf16 [batch, n_q, 16, 512]; idx int32 [batch, n_q, n_idx]; swa bf16
-    [batch, rows, 512] (row r = token swa_pos0[b] + r) -> float32 [batch, n_q, 16, 512]."""
+    [batch, rows, 512] (row r = token swa_pos0[b] + r; with swa_ring > 0 a
+    ring, token t at row t % swa_ring, swa_pos0 unused) -> float32 [batch, n_q, 16, 512]."""
     qb = _bits16(q, "q")
     sb = _bits16(swa, "swa")
     _need(idx, torch.int32, "idx")
@@ -270,11 +304,12 @@ def csa2_sparse_swa_attn(ws, q, nib, scale, idx, swa, q_pos0, swa_pos0, kv_strid
         out = torch.empty((batch, n_q, H_ATTN, D_LATENT), dtype=torch.float32, device=q.device)
     a = AttnArgs()
     a.batch, a.n_q, a.n_idx = batch, n_q, idx.shape[-1]
-    qp, sp = _host_i64(q_pos0), _host_i64(swa_pos0)
+    qp = _host_i64(q_pos0)
+    sp = _host_i64(swa_pos0 if swa_pos0 is not None else [0] * batch)
     a.q_pos0, a.swa_pos0 = ctypes.cast(qp, _p), ctypes.cast(sp, _p)
     a.q, a.nib, a.scale, a.kv_stride = _ptr(qb), _ptr(nib), _ptr(scale), kv_stride
     a.idx, a.swa, a.swa_stride, a.swa_rows = _ptr(idx), _ptr(sb), swa.shape[1], swa.shape[1]
-    a.softmax_scale, a.out = softmax_scale, _ptr(out)
+    a.softmax_scale, a.out, a.swa_ring = softmax_scale, _ptr(out), swa_ring
     _check(lib.csa2_sparse_swa_attn(ctypes.byref(a), ws.ptr, ws.nbytes, _stream(stream)))
     return out
 
@@ -302,7 +337,8 @@ def make_kv(nib, scale, k8, kscale, stride, bk8=None, bkscale=None, bk_stride=0)
 
 
 def csa2_run_group(ws, state, layers, q_pos0, n_entries, swa_pos0, *, ratio=1,
-                   index_kind=INDEX_FLAT, reindex_kind=INDEX_FLAT, softmax_scale=1.0, stream=None):
+                   index_kind=INDEX_FLAT, reindex_kind=INDEX_FLAT, softmax_scale=1.0, swa_ring=0,
+                   stream=None):
     """Run a plan.  layers: list of dicts {mode, q, swa, idx_q?, idx_w?, kv? (make_kv), out?}.
     Returns the float32 outputs [batch, n_q, 16, 512], one per layer."""
     n = len(layers)
@@ -331,9 +367,10 @@ def csa2_run_group(ws, state, layers, q_pos0, n_entries, swa_pos0, *, ratio=1,
     a = GroupArgs()
     a.batch, a.n_q, a.ratio = batch, n_q, ratio
     a.index_kind, a.reindex_kind = index_kind, reindex_kind
-    qp, ne, sp = _host_i64(q_pos0), _host_i64(n_entries), _host_i64(swa_pos0)
+    qp, ne = _host_i64(q_pos0), _host_i64(n_entries)
+    sp = _host_i64(swa_pos0 if swa_pos0 is not None else [0] * batch)
     a.q_pos0, a.n_entries, a.swa_pos0 = ctypes.cast(qp, _p), ctypes.cast(ne, _p), ctypes.cast(sp, _p)
-    a.swa_stride, a.swa_rows = swa_rows, swa_rows
+    a.swa_stride, a.swa_rows, a.swa_ring = swa_rows, swa_rows, swa_ring
     a.softmax_scale, a.n_layers, a.layers = softmax_scale, n, arr
     _check(lib.csa2_run_group(ctypes.byref(a), ctypes.byref(state.c), ws.ptr, ws.nbytes,
                               _stream(stream)))

@@ -231,11 +231,24 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
 }
 
 // ------------------------------------------------------------- attention
+constexpr int64_t kMaxRing = (1 << 21) - 1;  // ring rows x 1 KB must fit a 32-bit buffer range
+
 int validate_attn_common(int32_t batch, int32_t n_q, int32_t n_idx, const int64_t* q_pos0,
-                         const int64_t* swa_pos0, int64_t swa_rows, int64_t swa_stride) {
+                         const int64_t* swa_pos0, int64_t swa_rows, int64_t swa_stride, int64_t swa_ring) {
   if (batch < 1 || n_q < 1) return fail(CSA2_ERR_ARG, "batch and n_q must be >= 1");
   if (n_idx < 0 || n_idx > CSA2_MAX_K) return fail(CSA2_ERR_UNSUPPORTED, "n_idx must be in 0..%d", CSA2_MAX_K);
-  if (!q_pos0 || !swa_pos0) return fail(CSA2_ERR_ARG, "q_pos0 and swa_pos0 (host) are required");
+  if (!q_pos0) return fail(CSA2_ERR_ARG, "q_pos0 (host) is required");
+  if (swa_ring < 0) return fail(CSA2_ERR_ARG, "swa_ring < 0");
+  if (swa_ring > 0) {  // ring: token t at row t mod swa_ring
+    if (swa_ring < (int64_t)n_q + CSA2_SWA - 1)
+      return fail(CSA2_ERR_ARG, "swa_ring %lld is below n_q + %d", (long long)swa_ring, CSA2_SWA - 1);
+    if (swa_ring > kMaxRing) return fail(CSA2_ERR_ARG, "swa_ring above %lld", (long long)kMaxRing);
+    if (batch > 1 && swa_stride < swa_ring) return fail(CSA2_ERR_ARG, "swa_stride smaller than swa_ring");
+    for (int s = 0; s < batch; ++s)
+      if (q_pos0[s] < 0) return fail(CSA2_ERR_ARG, "q_pos0[%d] < 0", s);
+    return CSA2_OK;
+  }
+  if (!swa_pos0) return fail(CSA2_ERR_ARG, "swa_pos0 (host) is required for a linear window");
   if (swa_rows < 1) return fail(CSA2_ERR_ARG, "swa_rows must be >= 1");
   if (batch > 1 && swa_stride < swa_rows) return fail(CSA2_ERR_ARG, "swa_stride smaller than swa_rows");
   for (int s = 0; s < batch; ++s) {
@@ -253,6 +266,7 @@ struct AttnJob {
   int32_t batch, n_q, n_idx;
   const int64_t* q_pos0;
   const int64_t* swa_pos0;
+  int64_t swa_ring;
   const uint8_t* nib;
   const uint8_t* scale;
   int64_t kv_stride;
@@ -275,7 +289,7 @@ int run_attention(const AttnJob& j, void* ws, const WsLayout& w, hipStream_t str
     p.n_layers = j.n_layers;
     for (int i = 0; i < nb; ++i) {
       p.seq.a[i] = j.q_pos0[s0 + i];
-      p.seq.b[i] = j.swa_pos0[s0 + i];
+      p.seq.b[i] = j.swa_ring > 0 ? 0 : j.swa_pos0[s0 + i];
     }
     const int64_t row0 = (int64_t)s0 * j.n_q;
     p.nib = j.nib + (int64_t)s0 * j.kv_stride * CSA2_NIB_BYTES;
@@ -283,6 +297,7 @@ int run_attention(const AttnJob& j, void* ws, const WsLayout& w, hipStream_t str
     p.kv_stride = j.kv_stride;
     p.idx = j.idx ? j.idx + row0 * j.n_idx : nullptr;
     p.swa_stride = j.swa_stride;
+    p.swa_ring = j.swa_ring;
     p.softmax_scale = j.softmax_scale;
     for (int l = 0; l < j.n_layers; ++l) {
       p.layer[l].q = j.layer[l].q + row0 * kH * kD;
@@ -325,6 +340,7 @@ size_t csa2_struct_size(int32_t which) {
     case 3: return sizeof(csa2_layer);
     case 4: return sizeof(csa2_group_state);
     case 5: return sizeof(csa2_group_args);
+    case 6: return sizeof(csa2_append_args);
     default: return 0;
   }
 }
@@ -345,6 +361,59 @@ int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
     return fail(CSA2_ERR_WORKSPACE, "workspace must be non-NULL, 256-byte aligned, a multiple of 4 bytes");
   hipError_t e = launch_fill_u32(static_cast<uint32_t*>(workspace), ws_bytes / 4, 0u, (hipStream_t)stream);
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "workspace init");
+}
+
+int csa2_append(const csa2_append_args* a, void* stream) {
+  if (!a) return fail(CSA2_ERR_ARG, "append args are NULL");
+  if (a->batch < 0) return fail(CSA2_ERR_ARG, "batch < 0");
+  if (a->batch == 0) return CSA2_OK;
+  if (a->ratio != 1 && a->ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
+  if (!a->pos || !a->x || !a->k_in || !a->nib || !a->scale || !a->k8 || !a->kscale)
+    return fail(CSA2_ERR_ARG, "pos (host), x, k_in, nib, scale, k8, kscale are required");
+  if (a->ratio == 2 && !a->pending) return fail(CSA2_ERR_ARG, "ratio 2 needs the pending buffer");
+  if ((a->bk8 == nullptr) != (a->bkscale == nullptr)) return fail(CSA2_ERR_ARG, "bk8 and bkscale go together");
+  if (!aligned(a->x, 16) || !aligned(a->k_in, 16) || !aligned(a->nib, 8) || !aligned(a->k8, 16) ||
+      (a->bk8 && !aligned(a->bk8, 16)) || (a->pending && !aligned(a->pending, 16)) ||
+      (a->swa && !aligned(a->swa, 16)))
+    return fail(CSA2_ERR_ARG, "x, k_in, k8, bk8, pending, swa must be 16-byte aligned, nib 8-byte aligned");
+  if (a->batch > 1 && a->stride < 1) return fail(CSA2_ERR_ARG, "stride must be >= 1");
+  if (a->swa) {
+    if (a->swa_ring < CSA2_SWA) return fail(CSA2_ERR_ARG, "swa_ring must be >= %d", CSA2_SWA);
+    if (a->batch > 1 && a->swa_stride < a->swa_ring) return fail(CSA2_ERR_ARG, "swa_stride smaller than swa_ring");
+  }
+  for (int s = 0; s < a->batch; ++s) {
+    if (a->pos[s] < 0) return fail(CSA2_ERR_ARG, "pos[%d] < 0", s);
+    const int64_t e = a->pos[s] / a->ratio;
+    if (e >= CSA2_MAX_ENTRIES)
+      return fail(CSA2_ERR_UNSUPPORTED, "sequence %d: entry %lld at or past CSA2_MAX_ENTRIES", s, (long long)e);
+    if (a->batch > 1 && e >= a->stride) return fail(CSA2_ERR_ARG, "sequence %d: entry %lld past stride", s, (long long)e);
+    if (a->bk8 && a->batch > 1 && e / CSA2_BLOCK >= a->bk_stride)
+      return fail(CSA2_ERR_ARG, "sequence %d: block %lld past bk_stride", s, (long long)(e / CSA2_BLOCK));
+  }
+  hipStream_t st = (hipStream_t)stream;
+  for (int s0 = 0; s0 < a->batch; s0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(kMaxSeqPerLaunch, a->batch - s0);
+    AppendPass p{};
+    p.ratio = a->ratio;
+    for (int i = 0; i < nb; ++i) p.seq.a[i] = a->pos[s0 + i];
+    p.x = a->x + (int64_t)s0 * CSA2_D_LATENT;
+    p.k_in = a->k_in + (int64_t)s0 * CSA2_D_INDEX;
+    p.nib = a->nib + (int64_t)s0 * a->stride * CSA2_NIB_BYTES;
+    p.scale = a->scale + (int64_t)s0 * a->stride * CSA2_SCALE_BYTES;
+    p.k8 = a->k8 + (int64_t)s0 * a->stride * CSA2_D_INDEX;
+    p.kscale = a->kscale + (int64_t)s0 * a->stride;
+    p.stride = a->stride;
+    p.bk8 = a->bk8 ? a->bk8 + (int64_t)s0 * a->bk_stride * CSA2_D_INDEX : nullptr;
+    p.bks = a->bkscale ? a->bkscale + (int64_t)s0 * a->bk_stride : nullptr;
+    p.bk_stride = a->bk_stride;
+    p.pending = a->pending ? a->pending + (int64_t)s0 * (CSA2_D_LATENT + CSA2_D_INDEX) : nullptr;
+    p.swa = a->swa ? a->swa + (int64_t)s0 * a->swa_stride * CSA2_D_LATENT : nullptr;
+    p.swa_stride = a->swa_stride;
+    p.swa_ring = a->swa_ring;
+    hipError_t e = launch_append(p, nb, st);
+    if (e != hipSuccess) return hip_fail(e, "append");
+  }
+  return CSA2_OK;
 }
 
 int csa2_workspace_fallbacks(const void* workspace, uint32_t* count, void* stream) {
@@ -408,7 +477,8 @@ int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, 
 
 int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
   if (!a) return fail(CSA2_ERR_ARG, "attention args are NULL");
-  int rc = validate_attn_common(a->batch, a->n_q, a->n_idx, a->q_pos0, a->swa_pos0, a->swa_rows, a->swa_stride);
+  int rc = validate_attn_common(a->batch, a->n_q, a->n_idx, a->q_pos0, a->swa_pos0, a->swa_rows, a->swa_stride,
+                                a->swa_ring);
   if (rc) return rc;
   if ((rc = validate_kv_ptrs(a->nib, a->scale))) return rc;
   if (!a->q || !a->swa || !a->out || (a->n_idx > 0 && !a->idx)) return fail(CSA2_ERR_ARG, "q, swa, out, idx are required");
@@ -419,7 +489,7 @@ int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_byt
   if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
   AttnJob j{};
   j.batch = a->batch; j.n_q = a->n_q; j.n_idx = a->n_idx;
-  j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0;
+  j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0; j.swa_ring = a->swa_ring;
   j.nib = a->nib; j.scale = a->scale; j.kv_stride = a->kv_stride;
   j.idx = a->idx; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
   j.n_layers = 1;
@@ -439,7 +509,8 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
   if ((a->index_kind != CSA2_INDEX_FLAT || a->reindex_kind != CSA2_INDEX_FLAT) && a->n_q >= kPrefillMinQ)
     return fail(CSA2_ERR_UNSUPPORTED, "HIER and POOL indexing take fewer than %d queries per sequence", kPrefillMinQ);
   if (!a->n_entries) return fail(CSA2_ERR_ARG, "n_entries (host) is required");
-  int rc = validate_attn_common(a->batch, a->n_q, CSA2_TOP_K, a->q_pos0, a->swa_pos0, a->swa_rows, a->swa_stride);
+  int rc = validate_attn_common(a->batch, a->n_q, CSA2_TOP_K, a->q_pos0, a->swa_pos0, a->swa_rows, a->swa_stride,
+                                a->swa_ring);
   if (rc) return rc;
   if (!st->indices || !aligned(st->indices, 4)) return fail(CSA2_ERR_ARG, "state.indices must be a device buffer");
   // simulate the plan on the host: every mode change is checked before launching
@@ -512,7 +583,7 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
     // this layer and the Reuse layers after it share KV and indices: one launch
     AttnJob j{};
     j.batch = a->batch; j.n_q = a->n_q; j.n_idx = CSA2_TOP_K;
-    j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0;
+    j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0; j.swa_ring = a->swa_ring;
     j.nib = st->kv.nib; j.scale = st->kv.scale; j.kv_stride = st->kv.stride;
     j.idx = st->indices; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
     j.n_layers = 0;

@@ -144,18 +144,31 @@ __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
 }
 
 // A window tile into E: thread t copies row t / 4, channels 128 (t % 4) ..
-// The loads go through a descriptor that starts at the query's first window
-// row and ends after its last, so rows past the window read as zeros and all
-// sixteen loads are issued before any wait.
+// The loads go through a buffer descriptor, so rows past the window read as
+// zeros and all sixteen loads are issued before any wait: linear windows use
+// a descriptor from the query's first window row to its last; a ring uses
+// the whole ring, token t at row t mod swa_ring, and an out-of-range offset
+// for rows past the window.
 __device__ __forceinline__ void load_window(const AttnPass& p, const AttnLayer& L, int wtile, int seq, int64_t t0,
                                             int n_win, TileLds& s) {
   const int er = threadIdx.x >> 2, quarter = threadIdx.x & 3;
   uint16_t* dst = s.E + er * kEStride + quarter * 128;
   const int wi = wtile * kAttnSplit + er;
-  const int64_t r0 = t0 - p.seq.b[seq];
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(L.swa + ((int64_t)seq * p.swa_stride + r0) * kD), 0, n_win * kD * 2, kRawBufferWord3);
-  const int off = wi * kD * 2 + quarter * 256;
+  __amdgpu_buffer_rsrc_t rw;
+  int off;
+  if (p.swa_ring > 0) {
+    const int ring = (int)p.swa_ring;
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)(L.swa + (int64_t)seq * p.swa_stride * kD), 0, ring * kD * 2,
+                                           kRawBufferWord3);
+    int r = (int)(t0 % ring) + wi;  // wi < 128 <= ring: one wrap at most
+    r = r >= ring ? r - ring : r;
+    off = wi < n_win ? r * kD * 2 + quarter * 256 : ring * kD * 2;
+  } else {
+    const int64_t r0 = t0 - p.seq.b[seq];
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)(L.swa + ((int64_t)seq * p.swa_stride + r0) * kD), 0,
+                                           n_win * kD * 2, kRawBufferWord3);
+    off = wi * kD * 2 + quarter * 256;
+  }
   uint4 v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {

@@ -73,6 +73,27 @@ struct IndexPass {
 int prof_begin(int32_t kernel, hipStream_t stream);
 void prof_end(int handle, hipStream_t stream);
 
+// One decode step's appends: sequence s writes its token at position
+// seq.a[s] (see csa2_append).
+struct AppendPass {
+  int32_t ratio;
+  SeqArgs seq;                  // a = position of the new token
+  const float* x;               // [batch][512]
+  const float* k_in;            // [batch][64]
+  uint8_t* nib;
+  uint8_t* scale;
+  uint8_t* k8;
+  float* kscale;
+  int64_t stride;
+  uint8_t* bk8;                 // or null
+  float* bks;
+  int64_t bk_stride;
+  float* pending;               // ratio 2: [batch][576]
+  uint16_t* swa;                // or null
+  int64_t swa_stride, swa_ring;
+};
+hipError_t launch_append(const AppendPass& p, int32_t batch, hipStream_t stream);
+
 hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int32_t ratio,
                            uint8_t* nib, uint8_t* scale, const float* kin, int64_t ld_k,
                            uint8_t* k8, float* kscale, hipStream_t stream);
@@ -109,6 +130,7 @@ struct AttnPass {
   int32_t n_tiles;              // candidate tiles of kAttnSplit rows per (layer, row)
   int32_t tiles_per_split;      // tiles one workgroup walks (online softmax)
   int32_t max_splits;           // ceil(n_tiles / tiles_per_split)
+  int64_t swa_ring;             // 0: linear window rows from seq.b; > 0: token t at row t mod swa_ring
   // workspace (used when max_splits > 1)
   float* partial;               // [n_layers*rows][max_splits][kPartFloats]
 };

@@ -122,6 +122,36 @@ def test_attention_errors(m):
     assert f(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_ARG
 
 
+def test_append_errors(m):
+    A = m.AppendArgs
+    pos = (ctypes.c_int64 * 2)(5, 7)
+
+    def args(**kw):
+        a = A()
+        a.batch, a.ratio, a.pos = 2, 1, ctypes.cast(pos, ctypes.c_void_p)
+        a.x, a.k_in, a.nib, a.scale, a.k8, a.kscale = _p(), _p(0x1000), _p(0x2000), _p(0x3000), _p(0x4000), _p(0x5000)
+        a.stride = 16
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return ctypes.byref(a)
+
+    ap = m.lib.csa2_append
+    assert ap(None, None) == m.ERR_ARG
+    assert ap(args(ratio=3), None) == m.ERR_ARG
+    assert ap(args(x=None), None) == m.ERR_ARG
+    assert ap(args(ratio=2), None) == m.ERR_ARG                         # no pending buffer
+    assert ap(args(bk8=_p(0x6000)), None) == m.ERR_ARG                 # bk8 without bkscale
+    assert ap(args(x=_p(4)), None) == m.ERR_ARG                        # misaligned
+    assert ap(args(stride=6), None) == m.ERR_ARG                       # entry 7 past the stride
+    assert ap(args(swa=_p(0x7000), swa_ring=100, swa_stride=100), None) == m.ERR_ARG  # ring < 128
+    big = (ctypes.c_int64 * 2)(5, 1 << 23)
+    assert ap(args(pos=ctypes.cast(big, ctypes.c_void_p), stride=1 << 24), None) == m.ERR_UNSUPPORTED
+    neg = (ctypes.c_int64 * 2)(5, -1)
+    assert ap(args(pos=ctypes.cast(neg, ctypes.c_void_p)), None) == m.ERR_ARG
+    zero = A()
+    assert ap(ctypes.byref(zero), None) == m.OK                         # batch 0: nothing to do
+
+
 def test_group_state_errors(m):
     st = m.GroupState()
     st.indices = _p()
