@@ -186,6 +186,45 @@ def prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def append_timing(csa2, gen, B, dev, launches=200):
+    """The write side of a decode step, timed apart from the step: one
+    csa2_append per launch puts a new token of each of the B sequences into
+    the FP4 cache and indexer keys, updates its block key and writes its
+    bf16 window row (HIP events around each launch).  The cache here is a
+    small one: the append's cost does not depend on the context."""
+    import torch
+    stride, ring, pos = 1024, 128, 1005
+    nib = torch.zeros((B * stride, 256), dtype=torch.uint8, device=dev)
+    sc = torch.zeros((B * stride, 32), dtype=torch.uint8, device=dev)
+    k8 = torch.zeros((B * stride, 64), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B * stride,), dtype=torch.float32, device=dev)
+    bk8 = torch.zeros((B * stride // 8, 64), dtype=torch.uint8, device=dev)
+    bks = torch.zeros((B * stride // 8,), dtype=torch.float32, device=dev)
+    swa = torch.zeros((B, ring, 512), dtype=torch.bfloat16, device=dev)
+    x = gen.latent(B, 77, device=dev)
+    k = gen.index_key(B, 77, device=dev)
+
+    def one():
+        csa2.csa2_append(x, k, [pos] * B, nib, sc, k8, ks, stride, bk8=bk8, bkscale=bks, bk_stride=stride // 8,
+                         swa=swa, swa_ring=ring)
+
+    for _ in range(10):
+        one()
+    torch.cuda.synchronize()
+    csa2.csa2_profile_reset()
+    csa2.csa2_profile_enable(True)
+    for _ in range(launches):
+        one()
+    torch.cuda.synchronize()
+    csa2.csa2_profile_enable(False)
+    ms, n = csa2.csa2_profile_read(csa2.K_APPEND)
+    csa2.csa2_profile_reset()
+    # bytes per launch: x and k read, entry (288 + 68 B) and block key (68 B)
+    # written, the block's earlier keys re-read (pos % 8 of them), window row
+    return {"kernel": "k_append", "sequences": B, "avg_us": round(1000.0 * ms / n, 3),
+            "bytes_per_launch": B * (512 * 4 + 64 * 4 + 288 + 68 + 68 + (pos % 8) * 68 + 1024)}
+
+
 def hier(args):
     """The hierarchical Full layer at 1M context, batch 4: block-key scan and
     top-2,048 blocks, pool scan and top-512, then attention over the 512
@@ -452,6 +491,7 @@ def main():
         graph_s = time.perf_counter() - t0
 
     best_s = min(eager_s, graph_s) if graph_s is not None else eager_s
+    append = append_timing(csa2, gen, B, dev)
     qtok_per_step = 2 * B
     value = qtok_per_step * args.steps / best_s
     step_bytes = 2 * B * algorithmic_bytes_per_qtok(ctx)
@@ -485,6 +525,7 @@ def main():
         "eager_ms_per_step": round(1000.0 * eager_s / args.steps, 4),
         "graph_ms_per_step": None if graph_s is None else round(1000.0 * graph_s / args.steps, 4),
         "kernels": kern,
+        "append": append,
     }
     if not args.no_cpu_baseline:
         x0 = gen.latent(ctx, seed, seq=0, device=dev).cpu().numpy()

@@ -145,19 +145,53 @@ __global__ __launch_bounds__(256) void k_block_keys(
 // The encoding arithmetic is k_quantize's and k_block_keys' (same helpers,
 // same binary32 order), so appended tokens give the bytes the bulk encoders
 // give for the whole history.
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
 __global__ __launch_bounds__(64) void k_append(AppendPass p) {
-  const int s = blockIdx.x, t = threadIdx.x;
+  const int s = blockIdx.x, t = threadIdx.x;  // lane t: latent channels 8t..8t+7, key channel t
   const int64_t pos = p.seq.a[s];
   const float* xr = p.x + (int64_t)s * CSA2_D_LATENT;
   const float* kr = p.k_in + (int64_t)s * CSA2_D_INDEX;
+  float* pend = p.pending ? p.pending + (int64_t)s * (CSA2_D_LATENT + CSA2_D_INDEX) : nullptr;
+  const bool hold = p.ratio == 2 && (pos & 1) == 0;  // an even token waits for its pair
+  const bool paired = p.ratio == 2 && !hold;
+  const int64_t e = p.ratio == 1 ? pos : pos >> 1;
+  const int64_t blk = e >> 3;
+  const int count = (int)(e - 8 * blk) + 1;           // entries of the block, the new one included
+  const bool blocks = p.bk8 != nullptr && !hold;
 
-  // window ring: thread t writes channels 8t .. 8t+7 as bf16 (nearest, ties
-  // to even)
+  // every global load first, so their latencies overlap
+  const float4 xa = *reinterpret_cast<const float4*>(xr + 8 * t);
+  const float4 xb = *reinterpret_cast<const float4*>(xr + 8 * t + 4);
+  const float kin = kr[t];
+  float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
+  float kpend = 0.0f;
+  if (paired) {
+    pa = *reinterpret_cast<const float4*>(pend + 8 * t);
+    pb = *reinterpret_cast<const float4*>(pend + 8 * t + 4);
+    kpend = pend[CSA2_D_LATENT + t];
+  }
+  uint32_t prev[7];
+  float prev_s[7];
+  {
+    const uint8_t* kb = p.k8 + ((int64_t)s * p.stride + 8 * blk) * CSA2_D_INDEX + t;
+    const float* sb = p.kscale + (int64_t)s * p.stride + 8 * blk;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const bool ok = blocks && j + 1 < count;
+      prev[j] = ok ? kb[j * CSA2_D_INDEX] : 0u;
+      prev_s[j] = ok ? sb[j] : 0.0f;
+    }
+  }
+
+  // window ring: bf16 of channels 8t .. 8t+7 (nearest, ties to even)
+  const float f[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
   if (p.swa) {
     const int64_t row = pos % p.swa_ring;
-    const float4 a = *reinterpret_cast<const float4*>(xr + 8 * t);
-    const float4 b = *reinterpret_cast<const float4*>(xr + 8 * t + 4);
-    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -169,106 +203,55 @@ __global__ __launch_bounds__(64) void k_append(AppendPass p) {
     *reinterpret_cast<uint4*>(p.swa + ((int64_t)s * p.swa_stride + row) * CSA2_D_LATENT + 8 * t) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
-  float* pend = p.pending ? p.pending + (int64_t)s * (CSA2_D_LATENT + CSA2_D_INDEX) : nullptr;
-  if (p.ratio == 2 && (pos & 1) == 0) {  // hold the even token for its pair
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pend[8 * t + i] = xr[8 * t + i];
-    if (t < 8)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pend[CSA2_D_LATENT + 8 * t + i] = kr[8 * t + i];
+  if (hold) {
+    *reinterpret_cast<float4*>(pend + 8 * t) = xa;
+    *reinterpret_cast<float4*>(pend + 8 * t + 4) = xb;
+    pend[CSA2_D_LATENT + t] = kin;
     return;
   }
-  const int64_t e = p.ratio == 1 ? pos : pos >> 1;
 
-  // ---- main latent: threads 0..31, one 16-channel block each
-  if (t < 32) {
-    float v[16];
+  // ---- main latent: 16-channel block b on lanes 2b (channels 16b..16b+7)
+  // and 2b+1 (the next 8); the entry is the token (ratio 1) or the pair
+  // mean (ratio 2)
+  float v[8];
+  const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float a = xr[16 * t + i];
-      v[i] = p.ratio == 1 ? a : f32_mul(f32_add(pend[16 * t + i], a), 0.5f);
-    }
-    float amax = 0.0f;
+  for (int i = 0; i < 8; ++i) v[i] = paired ? f32_mul(f32_add(pv[i], f[i]), 0.5f) : f[i];
+  float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-    const uint32_t sc = fp4_block_scale(amax);
-    const float sv = e4m3_mag(sc);
-    uint32_t w0 = 0, w1 = 0;
-    if (sv > 0.0f) {
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+  amax = fmaxf(amax, quad_xor1(amax));  // both lanes of the block
+  const uint32_t sc = fp4_block_scale(amax);
+  const float sv = e4m3_mag(sc);
+  uint32_t w8 = 0;
+  if (sv > 0.0f) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w0 |= fp4_code(v[i], sv) << (4 * i);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w1 |= fp4_code(v[8 + i], sv) << (4 * i);
-    }
-    const int64_t ent = (int64_t)s * p.stride + e;
-    *reinterpret_cast<uint2*>(p.nib + ent * CSA2_NIB_BYTES + t * 8) = make_uint2(w0, w1);
-    p.scale[ent * CSA2_SCALE_BYTES + t] = (uint8_t)sc;
-  }
-
-  // ---- indexer key: lanes 0..3, 16 channels each (a quad)
-  float kv[16];
-  float kmax = 0.0f;
-  if (t < 4) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float a = kr[16 * t + i];
-      kv[i] = p.ratio == 1 ? a : f32_mul(f32_add(pend[CSA2_D_LATENT + 16 * t + i], a), 0.5f);
-      kmax = fmaxf(kmax, __builtin_fabsf(kv[i]));
-    }
-  }
-  kmax = fmaxf(kmax, quad_xor1(kmax));
-  kmax = fmaxf(kmax, quad_xor2(kmax));
-  const float ks = f32_div(kmax, 448.0f);
-  uint32_t c[4] = {0, 0, 0, 0};
-  if (t < 4 && ks > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) c[i >> 2] |= e4m3_from_f32(f32_div(kv[i], ks)) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) w8 |= fp4_code(v[i], sv) << (4 * i);
   }
   const int64_t ent = (int64_t)s * p.stride + e;
-  if (t < 4) {
-    *reinterpret_cast<uint4*>(p.k8 + ent * CSA2_D_INDEX + t * 16) = make_uint4(c[0], c[1], c[2], c[3]);
-    if (t == 0) p.kscale[ent] = ks;
-  }
+  *reinterpret_cast<uint32_t*>(p.nib + ent * CSA2_NIB_BYTES + t * 4) = w8;
+  if ((t & 1) == 0) p.scale[ent * CSA2_SCALE_BYTES + (t >> 1)] = (uint8_t)sc;
 
-  // ---- block key of the new entry's block: its earlier entries from the
-  // cache in position order, then the new key from registers
-  if (p.bk8 == nullptr) return;
-  const int64_t blk = e >> 3;
-  const int count = (int)(e - 8 * blk) + 1;
-  float acc[16];
+  // ---- indexer key: channel t
+  const float kv = paired ? f32_mul(f32_add(kpend, kin), 0.5f) : kin;
+  const float ks = f32_div(wave_max64(__builtin_fabsf(kv)), 448.0f);
+  const uint32_t code = ks > 0.0f ? e4m3_from_f32(f32_div(kv, ks)) : 0u;
+  p.k8[ent * CSA2_D_INDEX + t] = (uint8_t)code;
+  if (t == 0) p.kscale[ent] = ks;
+
+  // ---- block key of the new entry's block, channel t: its earlier entries
+  // in position order, then the new key
+  if (!blocks) return;
+  float acc = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-  if (t < 4) {
-    const uint8_t* kb = p.k8 + ((int64_t)s * p.stride + 8 * blk) * CSA2_D_INDEX + t * 16;
-    const float* sb = p.kscale + (int64_t)s * p.stride + 8 * blk;
-    for (int j = 0; j + 1 < count; ++j) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(kb + j * CSA2_D_INDEX);
-      const float sj = sb[j];
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = f32_add(acc[i], f32_mul(e4m3_value((w[i >> 2] >> (8 * (i & 3))) & 0xFFu), sj));
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = f32_add(acc[i], f32_mul(e4m3_value((c[i >> 2] >> (8 * (i & 3))) & 0xFFu), ks));
+  for (int j = 0; j < 7; ++j) {
+    if (j + 1 >= count) break;
+    acc = f32_add(acc, f32_mul(e4m3_value(prev[j]), prev_s[j]));
   }
-  float bmax = 0.0f;
-  const float fc = (float)count;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    acc[i] = f32_div(acc[i], fc);
-    bmax = fmaxf(bmax, __builtin_fabsf(acc[i]));
-  }
-  bmax = fmaxf(bmax, quad_xor1(bmax));
-  bmax = fmaxf(bmax, quad_xor2(bmax));
-  if (t >= 4) return;
-  const float bs = f32_div(bmax, 448.0f);
-  uint32_t bc[4] = {0, 0, 0, 0};
-  if (bs > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bc[i >> 2] |= e4m3_from_f32(f32_div(acc[i], bs)) << (8 * (i & 3));
-  }
-  *reinterpret_cast<uint4*>(p.bk8 + ((int64_t)s * p.bk_stride + blk) * CSA2_D_INDEX + t * 16) =
-      make_uint4(bc[0], bc[1], bc[2], bc[3]);
+  acc = f32_add(acc, f32_mul(e4m3_value(code), ks));
+  acc = f32_div(acc, (float)count);
+  const float bs = f32_div(wave_max64(__builtin_fabsf(acc)), 448.0f);
+  p.bk8[((int64_t)s * p.bk_stride + blk) * CSA2_D_INDEX + t] = (uint8_t)(bs > 0.0f ? e4m3_from_f32(f32_div(acc, bs)) : 0u);
   if (t == 0) p.bks[(int64_t)s * p.bk_stride + blk] = bs;
 }
 
