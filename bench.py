@@ -49,19 +49,21 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 256 MiB five times (the known-size reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
-    ap.add_argument("--workload", choices=["decode", "prefill", "hier"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "multi", "prefill", "hier"], default="decode",
                     help="decode: the 128K decode group (default, the headline); prefill: a 4,096-token "
                          "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers; hier: the "
-                         "hierarchical Full layer at 1M context, batch 4")
+                         "hierarchical Full layer at 1M context, batch 4; multi: the decode group with 4 query "
+                         "tokens per sequence (speculative decoding)")
     return ap.parse_args()
 
 
-def algorithmic_bytes_per_qtok(ctx):
-    """Bytes one query token must move through one 4-layer group: the key
-    scan of the Full/Reindex layer, and per layer the 512 gathered entries,
-    the 128 window rows, its query and output, the index list."""
+def algorithmic_bytes_per_qtok(ctx, nq=1):
+    """Bytes one query token must move through one 4-layer group: its share
+    of the key scan of the Full/Reindex layer (the nq query tokens of a
+    sequence share one scan), and per layer the 512 gathered entries, the 128
+    window rows, its query and output, the index list."""
     per_layer = 512 * ENTRY_BYTES + 128 * ROW_BYTES + Q_BYTES + OUT_BYTES + IDX_BYTES
-    return ctx * KEY_BYTES + IDXQ_BYTES + 4 * per_layer
+    return ctx * KEY_BYTES / nq + IDXQ_BYTES + 4 * per_layer
 
 
 def cpu_baseline(x0, k0, layers_host, ctx, seconds):
@@ -396,6 +398,7 @@ def main():
 
     dev = "cuda"
     B, ctx, C = args.batch, args.ctx, args.copies
+    nq = 4 if args.workload == "multi" else 1   # query tokens per sequence per step
     seed = 1002
     # ---- caches: C copies, each its own draw
     kvs, keep = [], []
@@ -414,7 +417,7 @@ def main():
         keep.append((nib, sc, k8, ks))
     torch.cuda.synchronize()
     # ---- per-layer inputs of the two runs (shared by the copies)
-    q_pos0, n_entries, swa_pos0 = [ctx - 1] * B, [ctx] * B, [ctx - 128] * B
+    q_pos0, n_entries, swa_pos0 = [ctx - nq] * B, [ctx] * B, [ctx - nq - 127] * B
     plans = [["F", "U", "U", "U"], ["R", "U", "U", "U"]]
     mode_of = {"F": csa2.MODE_FULL, "R": csa2.MODE_REINDEX, "U": csa2.MODE_REUSE}
     layers = []
@@ -422,15 +425,15 @@ def main():
         ls = []
         for j, m in enumerate(plan):
             li = 4 * run + j
-            d = dict(mode=mode_of[m], q=gen.attn_query((B, 1), seed, li, device=dev),
-                     swa=gen.window_rows(B, 128, seed, li, device=dev),
-                     out=torch.empty((B, 1, 16, 512), dtype=torch.float32, device=dev))
+            d = dict(mode=mode_of[m], q=gen.attn_query((B, nq), seed, li, device=dev),
+                     swa=gen.window_rows(B, 127 + nq, seed, li, device=dev),
+                     out=torch.empty((B, nq, 16, 512), dtype=torch.float32, device=dev))
             if m in "FR":
-                d["idx_q"] = gen.index_query((B, 1), seed, li, device=dev)
+                d["idx_q"] = gen.index_query((B, nq), seed, li, device=dev)
             ls.append(d)
         layers.append(ls)
-    ws = csa2.Workspace(B, 1, ctx)
-    states = [csa2.State(B, 1) for _ in range(C)]
+    ws = csa2.Workspace(B, nq, ctx)
+    states = [csa2.State(B, nq) for _ in range(C)]
 
     def run_full(c):
         ls = [dict(L) for L in layers[0]]
@@ -491,15 +494,16 @@ def main():
         graph_s = time.perf_counter() - t0
 
     best_s = min(eager_s, graph_s) if graph_s is not None else eager_s
-    append = append_timing(csa2, gen, B, dev)
-    qtok_per_step = 2 * B
+    append = append_timing(csa2, gen, B, dev) if nq == 1 else None
+    qtok_per_step = 2 * B * nq
     value = qtok_per_step * args.steps / best_s
-    step_bytes = 2 * B * algorithmic_bytes_per_qtok(ctx)
+    step_bytes = int(2 * B * nq * algorithmic_bytes_per_qtok(ctx, nq))
     scan_bytes = B * ctx * KEY_BYTES                       # one launch scans every sequence once
     scan_avg_s = scan_ms / 1000.0 / scan_n
     achieved = scan_bytes / scan_avg_s / 1e9
     line = {
-        "metric": "CSA2 decode query-tokens/s at 128K ctx; % of peak HBM GB/s",
+        "metric": ("CSA2 decode query-tokens/s at 128K ctx; % of peak HBM GB/s" if nq == 1 else
+                   f"CSA2 multi-token decode query-tokens/s at 128K ctx ({nq} query tokens per sequence)"),
         "value": round(value, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -512,8 +516,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"decode group of 4 layers run as Full+3 Reuse then Reindex+3 Reuse, "
-                               f"batch {B}, {ctx} FP4 entries per sequence, top-512 + 128-token window",
-                   "batch": B, "ctx": ctx, "layers_per_step": 8, "query_tokens_per_step": qtok_per_step,
+                               f"batch {B}, {ctx} FP4 entries per sequence, top-512 + 128-token window"
+                               + ("" if nq == 1 else f", {nq} query tokens per sequence"),
+                   "batch": B, "ctx": ctx, "query_tokens_per_sequence": nq, "layers_per_step": 8, "query_tokens_per_step": qtok_per_step,
                    "cache_copies": C, "timing": "graph replay" if best_s == graph_s else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic(),
@@ -527,7 +532,7 @@ def main():
         "kernels": kern,
         "append": append,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and nq == 1:
         x0 = gen.latent(ctx, seed, seq=0, device=dev).cpu().numpy()
         k0 = gen.index_key(ctx, seed, seq=0, device=dev).cpu().numpy()
         host_layers = []

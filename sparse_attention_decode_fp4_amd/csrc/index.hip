@@ -50,6 +50,15 @@ __device__ __forceinline__ int64_t row_items(const IndexPass& p, int row, int64_
   return p.list_len;
 }
 
+// Items per scan chunk of a row (scan_chunk_items).  Over direct items every
+// row of a sequence takes the size of the sequence's last query, which sees
+// the most items, so one workgroup can scan a chunk for several queries; the
+// select derives the same.
+__device__ __forceinline__ int64_t row_chunk_items(const IndexPass& p, int row) {
+  const int last = p.source == kItemsDirect ? (row / p.n_q) * p.n_q + p.n_q - 1 : row;
+  return scan_chunk_items(row_items(p, last, row_vis_positions(p, last)), p.k);
+}
+
 __device__ __forceinline__ int64_t item_position(const IndexPass& p, int row, int64_t item,
                                                  int64_t n_items, int64_t vis_pos, bool& valid) {
   if (item >= n_items) { valid = false; return 0; }
@@ -114,18 +123,23 @@ __device__ __forceinline__ void load_query_f16(const IndexPass& p, int row, int 
   w_mine = p.idx_w ? p.idx_w[(int64_t)row * kHI + quad_head(0, quarter)] : 1.0f;
 }
 
-// Score of one key from its 16 bytes in this lane (a lane quad holds the
-// key); every lane of the quad returns it.
-__device__ __forceinline__ float quad_score(const half2_t (&q)[kHI][8], float w_mine, u32x4_t raw, float ks) {
+// This lane's 16 bytes of a key as packed f16 (exact).
+__device__ __forceinline__ void key_f16(u32x4_t raw, half2_t (&kh)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fp8x4_to_f16(raw[j], kh[2 * j], kh[2 * j + 1]);
+}
+
+// Score of one key from its 16 bytes in this lane, already as f16 (a lane
+// quad holds the key); every lane of the quad returns it.
+__device__ __forceinline__ float quad_score_f16(const half2_t (&q)[kHI][8], float w_mine, const half2_t (&kh)[8],
+                                                float ks) {
   float d[kHI] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    half2_t lo, hi;
-    fp8x4_to_f16(raw[j], lo, hi);
 #pragma unroll
     for (int s = 0; s < kHI; ++s) {
-      d[s] = __builtin_amdgcn_fdot2(q[s][2 * j], lo, d[s], false);
-      d[s] = __builtin_amdgcn_fdot2(q[s][2 * j + 1], hi, d[s], false);
+      d[s] = __builtin_amdgcn_fdot2(q[s][2 * j], kh[2 * j], d[s], false);
+      d[s] = __builtin_amdgcn_fdot2(q[s][2 * j + 1], kh[2 * j + 1], d[s], false);
     }
   }
   // slot s of the partner lane (lane ^ 1) holds head (s ^ 2) of this lane,
@@ -137,6 +151,12 @@ __device__ __forceinline__ float quad_score(const half2_t (&q)[kHI][8], float w_
   v += quad_xor1(v);
   v += quad_xor2(v);
   return ks * v;
+}
+
+__device__ __forceinline__ float quad_score(const half2_t (&q)[kHI][8], float w_mine, u32x4_t raw, float ks) {
+  half2_t kh[8];
+  key_f16(raw, kh);
+  return quad_score_f16(q, w_mine, kh, ks);
 }
 
 __device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t (&q)[kHI][8], float w_mine,
@@ -352,30 +372,39 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
 // descriptors whose range ends at the chunk's last item, so the hardware
 // returns zeros past it and the loads need no bounds branches.  Otherwise
 // positions come from a block or position list.
-template <int U, bool kDirect>
-__global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
-  int row, chunk;
-  map_row_chunk(p.rows, per_row, row, chunk);
-  if (row >= p.rows) return;
-  const int64_t vis = row_vis_positions(p, row);
-  const int64_t n_items = row_items(p, row, vis);
-  const int64_t csize = scan_chunk_items(n_items, p.k);
+template <int U, bool kDirect, int NQ>
+__global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, int n_groups) {
+  static_assert(NQ == 1 || kDirect, "queries share a chunk only over direct items");
+  // workgroup (group of NQ queries of one sequence, chunk)
+  int grp, chunk;
+  map_row_chunk(n_groups, per_row, grp, chunk);
+  if (grp >= n_groups) return;
+  const int qgroups = (p.n_q + NQ - 1) / NQ;
+  const int seq = grp / qgroups;
+  const int row0 = seq * p.n_q + (grp - seq * qgroups) * NQ;
+  const int nq = p.n_q - (row0 - seq * p.n_q) < NQ ? p.n_q - (row0 - seq * p.n_q) : NQ;
+  const int64_t csize = row_chunk_items(p, row0);  // shared by the rows of a sequence
   const int64_t base = (int64_t)chunk * csize;
-  if (base >= n_items) return;
-  const int64_t end = base + csize < n_items ? base + csize : n_items;
+  int64_t vis[NQ], n_items[NQ], end = 0;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    vis[i] = i < nq ? row_vis_positions(p, row0 + i) : 0;
+    n_items[i] = i < nq ? row_items(p, row0 + i, vis[i]) : 0;
+    const int64_t e = base + csize < n_items[i] ? base + csize : n_items[i];
+    end = e > end ? e : end;
+  }
+  if (base >= end) return;
 
   // candidates are staged in LDS and stored after the loop: a global store
   // inside it would make every later wait for the key loads also wait for
   // the store (one counter covers both on gfx9)
-  __shared__ uint32_t n_hit;
-  __shared__ uint64_t hits[kSeg];
-  if (threadIdx.x == 0) n_hit = 0;
+  __shared__ uint32_t n_hit[NQ];
+  __shared__ uint64_t hits[NQ][kSeg];
+  if (threadIdx.x < NQ) n_hit[threadIdx.x] = 0;
   const int quarter = threadIdx.x & 3;
   const int sub = threadIdx.x >> 2;  // item within a 64-item step
-  const int seq = row / p.n_q;
-  uint64_t* seg = p.seg_list + ((int64_t)row * p.max_chunks + chunk) * kSeg;
-  half2_t q[kHI][8];
-  float w_mine, T0;  // loaded after the first keys: their loads overlap
+  half2_t q[NQ][kHI][8];
+  float w_mine[NQ], T0[NQ];  // loaded after the first keys: their loads overlap
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
   // (used by the kDirect loads only)
@@ -396,7 +425,7 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
         B.ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(item * 4), 0, 0));
       } else {
         bool valid;
-        const int64_t pos = item_position(p, row, item, end, vis, valid);
+        const int64_t pos = item_position(p, row0, item, end, vis[0], valid);
         if (valid) {
           B.raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + pos * kDI + quarter * 16));
           B.ks[u] = sb[pos];
@@ -410,19 +439,24 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   auto score = [&](const Batch& B, int64_t it0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float sc = quad_score(q, w_mine, B.raw[u], B.ks[u]);
+      half2_t kh[8];
+      key_f16(B.raw[u], kh);  // converted once for every query of the group
       const int64_t item = it0 + u * 64 + sub;
-      bool take = quarter == 0 && item < end && sc >= T0;
-      if constexpr (!kDirect) {
-        if (take) {  // invalid list entries never become candidates
-          bool valid;
-          (void)item_position(p, row, item, end, vis, valid);
-          take = valid;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const float sc = quad_score_f16(q[i], w_mine[i], kh, B.ks[u]);
+        bool take = quarter == 0 && item < n_items[i] && item < base + csize && sc >= T0[i];
+        if constexpr (!kDirect) {
+          if (take) {  // invalid list entries never become candidates
+            bool valid;
+            (void)item_position(p, row0, item, end, vis[0], valid);
+            take = valid;
+          }
         }
-      }
-      if (take) {
-        const uint32_t at = atomicAdd(&n_hit, 1u);
-        if (at < (uint32_t)kSeg) hits[at] = select_key(score_key(sc), (uint32_t)item);
+        if (take) {
+          const uint32_t at = atomicAdd(&n_hit[i], 1u);
+          if (at < (uint32_t)kSeg) hits[i][at] = select_key(score_key(sc), (uint32_t)item);
+        }
       }
     }
   };
@@ -430,8 +464,12 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   Batch A, Bb;
   int64_t it = base;
   load(A, it);
-  load_query_f16(p, row, quarter, q, w_mine);
-  T0 = p.thresh[row];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int r = i < nq ? row0 + i : row0;
+    load_query_f16(p, r, quarter, q[i], w_mine[i]);
+    T0[i] = i < nq ? p.thresh[r] : INFINITY;
+  }
   __syncthreads();  // n_hit is initialised
   // kDirect loads past the chunk read zeros without touching memory, so they
   // are issued unconditionally and every path has the same loads in flight
@@ -448,9 +486,15 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row) {
   }
   __syncthreads();
   static_assert(kSeg <= 256, "one staged candidate per thread");
-  const uint32_t n = n_hit < (uint32_t)kSeg ? n_hit : (uint32_t)kSeg;
-  if (threadIdx.x < n) seg[threadIdx.x] = hits[threadIdx.x];
-  if (threadIdx.x == 0) p.seg_count[(int64_t)row * p.max_chunks + chunk] = n_hit;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    if (i >= nq || base >= n_items[i]) continue;
+    const int64_t r = row0 + i;
+    uint64_t* seg = p.seg_list + (r * p.max_chunks + chunk) * kSeg;
+    const uint32_t n = n_hit[i] < (uint32_t)kSeg ? n_hit[i] : (uint32_t)kSeg;
+    if (threadIdx.x < n) seg[threadIdx.x] = hits[i][threadIdx.x];
+    if (threadIdx.x == 0) p.seg_count[r * p.max_chunks + chunk] = n_hit[i];
+  }
 }
 
 // ------------------------------------------------------------------ select
@@ -470,7 +514,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
-  const int64_t csize = scan_chunk_items(n_items, p.k);
+  const int64_t csize = row_chunk_items(p, row);
   const int nch = (int)((n_items + csize - 1) / csize);
   const uint32_t k = (uint32_t)p.k;
   const float T0 = n_items > 0 ? p.thresh[row] : -INFINITY;  // written by the row's first scan chunk
@@ -736,12 +780,19 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   h = prof_begin(CSA2_K_INDEX_SCAN, stream);
-  if (p.source == kItemsDirect)
-    hipLaunchKernelGGL((k_index_scan<2, true>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
-                       scan_per_row);
+  // the queries of a sequence share the scan of a chunk, up to 4 per
+  // workgroup (direct items only)
+  const int nqg = (p.source != kItemsDirect || p.n_q == 1) ? 1 : p.n_q == 2 ? 2 : 4;
+  const int n_groups = p.rows / p.n_q * ((p.n_q + nqg - 1) / nqg);
+  const dim3 sgrid((unsigned)(grid_rows(n_groups) * scan_per_row));
+  if (p.source != kItemsDirect)
+    hipLaunchKernelGGL((k_index_scan<2, false, 1>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+  else if (nqg == 1)
+    hipLaunchKernelGGL((k_index_scan<2, true, 1>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+  else if (nqg == 2)
+    hipLaunchKernelGGL((k_index_scan<2, true, 2>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else
-    hipLaunchKernelGGL((k_index_scan<2, false>), dim3((unsigned)(gr * scan_per_row)), dim3(256), 0, stream, p,
-                       scan_per_row);
+    hipLaunchKernelGGL((k_index_scan<1, true, 4>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   prof_end(h, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -33,6 +33,9 @@ def _keys(csa2, seed, batch, stride):
     ([20000, 9000], 1, 1, 2048),         # large k
     ([300], 1, 1, 512),                  # fewer entries than k: all of them, -1 padded
     ([3000], 7, 2, 512),                 # several queries per sequence, ratio-2 visibility
+    ([9000, 5000], 2, 1, 512),           # two queries share each scan workgroup
+    ([40000], 4, 1, 512),                # four queries share each scan workgroup
+    ([20000, 12000], 6, 2, 512),         # a full and a partial group of four, ratio 2
     ([1], 1, 1, 5),
 ])
 def test_flat_topk(csa2, n_entries, n_q, ratio, k):
