@@ -222,7 +222,11 @@ __device__ __forceinline__ void sample_plan(int64_t n_items, uint32_t k, int64_t
   ks = 0;
   if (n_items > (int64_t)k && S > 0) {
     if (S == n_items) {
-      ks = k;
+      // a row this short needs no threshold: every key is a candidate (at
+      // most kSample, 128-key chunks), and the select ranks them exactly.
+      // A threshold at the k-th sampled score would put the row's answer at
+      // the mercy of the sample's MFMA rounding against the scan's.
+      ks = 0;
     } else {
       const double want = 2.5 * (double)k * (double)S / (double)n_items + 4.0;
       ks = want >= (double)S ? 0u : (uint32_t)want;
