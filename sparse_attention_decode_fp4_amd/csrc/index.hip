@@ -7,18 +7,17 @@
 //   s_p = ks_p * sum_h w_h * max(0, q_h . k_p)   over 4 indexer heads.
 //
 // One pass = three kernels over the rows (query rows) of a call:
-//   sample  one 1,024-thread workgroup per row scores a sample of at most
-//           2,048 of its items, 256 evenly spaced runs of 8 (fp8 MFMA: the
-//           sample only steers the threshold) and sets the row threshold T0:
-//           the lower
+//   sample  one 1,024-thread workgroup per row scores a sample of 2,048 of
+//           its items, 256 evenly spaced runs of 8 (fp8 MFMA: the sample only
+//           steers the threshold) and sets the row threshold T0: the lower
 //           edge, at 20 key bits, of the key bin holding the k_s-th largest
 //           sample, k_s sized so that about 2.5 k items of the row reach T0
-//           (every item when the sample is the whole row);
+//           (no threshold when the row has at most 2,048 items);
 //   scan    streams the fp8 keys once (4 lanes per key, 16 B each, fully
-//           coalesced), scores every item with packed f16 dot products
-//           (v_dot2c_f32_f16; fp8 -> f16 is exact) and appends the items
-//           scoring at least T0 to a segment per (row, 2,048-item chunk),
-//           counted in LDS;
+//           coalesced; up to 4 queries of a sequence share a workgroup),
+//           scores every item with packed f16 dot products (v_dot2c_f32_f16;
+//           fp8 -> f16 is exact) and appends the items scoring at least T0
+//           to a segment per (row, chunk), staged in LDS;
 //   select  gathers the segments (about 2.5 k candidates), radix-selects the
 //           exact k-th largest (score, -item) key, sorts the winners by
 //           item and writes their positions.  If the candidates cannot hold
@@ -371,11 +370,14 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
 
 // ------------------------------------------------------------------ scan
 
-// Workgroup (row, chunk of kScanChunk items).  kDirect: item i is position
-// i (flat keys or block keys); keys and scales are read through buffer
-// descriptors whose range ends at the chunk's last item, so the hardware
-// returns zeros past it and the loads need no bounds branches.  Otherwise
-// positions come from a block or position list.
+// Workgroup (NQ queries of one sequence, chunk of row_chunk_items items):
+// every key of the chunk is scored against each of the queries and those at
+// or above a query's threshold T0 become that query's candidates.  kDirect:
+// item i is position i (flat keys or block keys); keys and scales are read
+// through buffer descriptors whose range ends at the chunk's last item, so
+// the hardware returns zeros past it and the loads need no bounds branches.
+// Otherwise positions come from a block or position list (one query per
+// workgroup).
 template <int U, bool kDirect, int NQ>
 __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, int n_groups) {
   static_assert(NQ == 1 || kDirect, "queries share a chunk only over direct items");
