@@ -31,9 +31,11 @@
 
 namespace csa2 {
 
-// bf16 per row of E: rows 8 banks apart, so neither the 16-byte row reads
-// (8 lanes per LDS cycle) nor the transposing reads (4 rows x 32 bytes per
-// cycle) conflict
+// bf16 per row of E: rows 8 banks apart, so the transposing reads (4 rows x
+// 32 bytes per cycle) do not conflict.  Consecutive lanes write consecutive
+// rows, and in rows whose bit 2 is set the 16-byte chunks are swapped in
+// pairs (chunk c at c ^ 1), so rows r and r + 4 of the 16-byte MFMA operand
+// reads and writes fall in different banks.
 constexpr int kEStride = kD + 16;
 constexpr int kPStride = kAttnSplit + 8;
 
@@ -88,8 +90,8 @@ __device__ __forceinline__ void dequant16(uint2 codes, float s, uint4 (&v)[2]) {
   v[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// One entry of a selected-entry tile in flight: thread t owns row t / 4,
-// channels 128 (t % 4) .. +128 (64 bytes of codes, 8 scales).
+// One entry of a selected-entry tile in flight: thread t owns row t % 64,
+// channels 128 (t / 64) .. +128 (64 bytes of codes, 8 scales).
 struct EntryFetch {
   uint4 raw[4];
   uint2 sc;
@@ -97,7 +99,7 @@ struct EntryFetch {
 };
 
 __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, int row) {
-  const int c = tile * kAttnSplit + (threadIdx.x >> 2);
+  const int c = tile * kAttnSplit + (threadIdx.x & 63);
   return c < p.n_idx ? p.idx[(int64_t)row * p.n_idx + c] : -1;
 }
 
@@ -106,7 +108,7 @@ __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, in
 // CSA2_MAX_ENTRIES, whose offsets equal the descriptors' ranges, so the
 // hardware returns zeros without touching memory.  No load waits on another.
 __device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t pos, EntryFetch& f) {
-  const int quarter = threadIdx.x & 3;
+  const int quarter = threadIdx.x >> 6;
   f.valid = pos >= 0;
   const int64_t s0 = (int64_t)seq * p.kv_stride;
   const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
@@ -125,7 +127,7 @@ __device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t 
 
 // Dequantise a fetched entry into its row of E (zeros for an empty slot).
 __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
-  const int er = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  const int er = threadIdx.x & 63, quarter = threadIdx.x >> 6;
   uint16_t* dst = s.E + er * kEStride + quarter * 128;
   const uint32_t scw[2] = {f.sc.x, f.sc.y};
 #pragma unroll
@@ -136,14 +138,15 @@ __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
       uint4 v[2];
       dequant16(half ? make_uint2(f.raw[i].z, f.raw[i].w) : make_uint2(f.raw[i].x, f.raw[i].y),
                 e4m3_value((scw[g >> 2] >> (8 * (g & 3))) & 0xFFu), v);
-      *reinterpret_cast<uint4*>(dst + 16 * g) = v[0];
-      *reinterpret_cast<uint4*>(dst + 16 * g + 8) = v[1];
+      const int sw = (er >> 2) & 1;  // chunk 2g ^ sw, 2g+1 ^ sw
+      *reinterpret_cast<uint4*>(dst + 16 * g + 8 * sw) = v[0];
+      *reinterpret_cast<uint4*>(dst + 16 * g + 8 * (1 - sw)) = v[1];
     }
   }
   if (quarter == 0) s.row_ok[er] = f.valid ? 1 : 0;
 }
 
-// A window tile into E: thread t copies row t / 4, channels 128 (t % 4) ..
+// A window tile into E: thread t copies row t % 64, channels 128 (t / 64) ..
 // The loads go through a buffer descriptor, so rows past the window read as
 // zeros and all sixteen loads are issued before any wait: linear windows use
 // a descriptor from the query's first window row to its last; a ring uses
@@ -151,7 +154,7 @@ __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
 // for rows past the window.
 __device__ __forceinline__ void load_window(const AttnPass& p, const AttnLayer& L, int wtile, int seq, int64_t t0,
                                             int n_win, TileLds& s) {
-  const int er = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  const int er = threadIdx.x & 63, quarter = threadIdx.x >> 6;
   uint16_t* dst = s.E + er * kEStride + quarter * 128;
   const int wi = wtile * kAttnSplit + er;
   __amdgpu_buffer_rsrc_t rw;
@@ -176,7 +179,7 @@ __device__ __forceinline__ void load_window(const AttnPass& p, const AttnLayer& 
     v[i] = make_uint4(x[0], x[1], x[2], x[3]);
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = v[i];
+  for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(dst + 8 * (i ^ ((er >> 2) & 1))) = v[i];
   if (quarter == 0) s.row_ok[er] = wi < n_win ? 1 : 0;
 }
 
@@ -209,7 +212,7 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
   const int l16 = lane & 15, g4 = lane >> 4;
   __syncthreads();  // the tile is in LDS; the previous step's readers of P / red are done
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* arow = s.E + (16 * wave + l16) * kEStride + 8 * g4;
+  const uint16_t* arow = s.E + (16 * wave + l16) * kEStride + 8 * (g4 ^ ((l16 >> 2) & 1));
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks);
@@ -262,8 +265,9 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const uint16_t* bp = bbase + 16 * nt;
-    const v4i16_t k0 = lds_read_tr16(bp), k1 = lds_read_tr16(bp + 4 * kEStride);
-    const v4i16_t k2 = lds_read_tr16(bp + 32 * kEStride), k3 = lds_read_tr16(bp + 36 * kEStride);
+    const int dsw = (l16 & 2) ? -8 : 8;  // rows +4 and +36 hold their chunks swapped in pairs
+    const v4i16_t k0 = lds_read_tr16(bp), k1 = lds_read_tr16(bp + 4 * kEStride + dsw);
+    const v4i16_t k2 = lds_read_tr16(bp + 32 * kEStride), k3 = lds_read_tr16(bp + 36 * kEStride + dsw);
     const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
     const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(k2, k3, 0, 1, 2, 3, 4, 5, 6, 7));
     f32x4_t acc2;

@@ -69,11 +69,8 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
   const int64_t q0 = (int64_t)(tile % p.tiles_per_seq) * kPfRows;
   const int nq_tile = (int)((p.n_q - q0) < kPfRows ? (p.n_q - q0) : kPfRows);
   const int64_t row0 = (int64_t)seq * p.n_q + q0;
-  const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // scalar: the tile branches below are uniform
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  // A tiles of this wave (8 query rows each) that hold at least one query row
-  const int n_a = nq_tile <= 64 * wave ? 0 : (nq_tile - 64 * wave + 7) / 8 < 8 ? (nq_tile - 64 * wave + 7) / 8 : 8;
 
   const int64_t v_first = pf_visible(p, seq, q0);
   const int64_t v_last = pf_visible(p, seq, q0 + nq_tile - 1);
@@ -213,22 +210,18 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
         }
       };
       // software pipeline: the MFMA of tile a + 1 is issued before the
-      // epilogue of tile a, so it runs under it.  Only the wave's n_a tiles
-      // that hold query rows are computed (few-query calls fill one tile).
-      if (n_a == 0) continue;
+      // epilogue of tile a, so it runs under it
       v16f_t acc0 = {}, acc1 = {};
       acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[0], B, acc0, 0, 0, 0, kUnitScales, 0, kUnitScales);
 #pragma unroll
       for (int a = 0; a < 8; a += 2) {
-        if (a >= n_a) break;
-        if (a + 1 < n_a)
-          acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 1], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
-                                                                kUnitScales);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 1], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
+                                                              kUnitScales);
         epilogue(acc0, a);
-        if (a + 2 < n_a)
+        if (a + 2 < 8)
           acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 2], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
                                                                 kUnitScales);
-        if (a + 1 < n_a) epilogue(acc1, a + 1);
+        epilogue(acc1, a + 1);
       }
     }
     buf ^= 1;
