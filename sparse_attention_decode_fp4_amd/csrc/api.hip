@@ -36,7 +36,7 @@ constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of atte
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t stats, thresh, seg_count, seg_list, blocks, nsel, partial;
+  size_t stats, thresh, hist, seg_count, seg_list, blocks, nsel, partial;
   size_t pf_sample, pf_thresh, pf_count, pf_list, total;
   int32_t max_chunks;  // scan chunks per row covered by the segment buffers
 };
@@ -52,6 +52,7 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
   w.stats = take(kWsAlign);  // offset 0 in every layout: the fallback counter
   w.thresh = take((size_t)rows * 4);
+  w.hist = take((size_t)rows * kHistBins * 4);
   w.seg_count = take((size_t)rows * w.max_chunks * 4);
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
@@ -185,6 +186,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     p.idx_q = a->idx_q + row0 * kHI * kDI;
     p.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;
     p.thresh = at<float>(ws, w.thresh);
+    p.hist = at<uint32_t>(ws, w.hist);
     p.fallbacks = at<uint32_t>(ws, w.stats);
     p.seg_count = at<uint32_t>(ws, w.seg_count);
     p.seg_list = at<uint64_t>(ws, w.seg_list);

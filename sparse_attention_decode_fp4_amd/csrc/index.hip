@@ -58,6 +58,12 @@ __device__ __forceinline__ int64_t row_chunk_items(const IndexPass& p, int row) 
   return scan_chunk_items(row_items(p, last, row_vis_positions(p, last)), p.k);
 }
 
+// Histogram bin of a candidate's score key (candidates are at or above T0).
+__device__ __forceinline__ uint32_t hist_bin(uint32_t key32, uint32_t t0key) {
+  const uint32_t b = (key32 - t0key) >> kHistShift;
+  return b < (uint32_t)(kHistBins - 1) ? b : (uint32_t)(kHistBins - 1);
+}
+
 __device__ __forceinline__ int64_t item_position(const IndexPass& p, int row, int64_t item,
                                                  int64_t n_items, int64_t vis_pos, bool& valid) {
   if (item >= n_items) { valid = false; return 0; }
@@ -272,6 +278,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   int64_t S;
   uint32_t ks;
   sample_plan(n_items, (uint32_t)p.k, S, ks);
+  // the row's candidate histogram starts empty (the scan counts into it)
+  for (int i = t; i < kHistBins; i += kSampleThreads) p.hist[(int64_t)row * kHistBins + i] = 0u;
   if (ks == 0) {
     if (t == 0) p.thresh[row] = -INFINITY;
     return;
@@ -498,7 +506,11 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
     const int64_t r = row0 + i;
     uint64_t* seg = p.seg_list + (r * p.max_chunks + chunk) * kSeg;
     const uint32_t n = n_hit[i] < (uint32_t)kSeg ? n_hit[i] : (uint32_t)kSeg;
-    if (threadIdx.x < n) seg[threadIdx.x] = hits[i][threadIdx.x];
+    if (threadIdx.x < n) {
+      const uint64_t h = hits[i][threadIdx.x];
+      seg[threadIdx.x] = h;
+      atomicAdd(&p.hist[r * kHistBins + hist_bin((uint32_t)(h >> 32), score_key(T0[i]))], 1u);
+    }
     if (threadIdx.x == 0) p.seg_count[r * p.max_chunks + chunk] = n_hit[i];
   }
 }
@@ -533,9 +545,18 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   __shared__ uint32_t h2048[2048];
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t sh3[3];
+  __shared__ uint64_t bin_keys[64];
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need;
 
+  // the row's candidate histogram (filled by the scan), thread t: bins 8t..8t+7
+  uint32_t hb[8];
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistBins + 8 * t);
+    const uint4 a = hp[0], b = hp[1];
+    hb[0] = a.x; hb[1] = a.y; hb[2] = a.z; hb[3] = a.w;
+    hb[4] = b.x; hb[5] = b.y; hb[6] = b.z; hb[7] = b.w;
+  }
   const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
   const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
   // Rows of at most kSpecChunks chunks load every segment slot together with
@@ -634,7 +655,53 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       const uint32_t g = t + 256 * i;
       key[i] = g < total ? lc[g] : 0ull;  // 0 is below every candidate key
     }
-    const uint64_t kth = total > k ? block_kth_regs<kPer>(key, k, h2048, wsum, sh3) : 1ull;
+    uint64_t kth = 1ull;
+    if (total > k) {
+      // the bin holding the k-th largest key, from the histogram: bins above
+      // it hold fewer than k keys, with it at least k.  When it is a proper
+      // bin with a few keys, the k-th key is ranked among those alone;
+      // otherwise (the top bin, which also takes scores far above T0) the
+      // radix over every candidate decides.
+      uint32_t hl = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hl += hb[j];
+      uint32_t htot;
+      const uint32_t hincl = block_incl_scan_256(hl, wsum, htot);
+      uint32_t above = htot - hincl;  // keys in bins above 8t + 7
+      if (t == 0) sh3[0] = 0xFFFFFFFFu;
+      __syncthreads();
+      if (htot == total && above < k && above + hl >= k) {
+        for (int j = 7; j >= 0; --j) {
+          if (above + hb[j] >= k) { sh3[0] = 8 * t + j; sh3[1] = k - above; sh3[2] = hb[j]; break; }
+          above += hb[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t kb_bin = sh3[0], need = sh3[1], in_bin = sh3[2];
+      if (kb_bin < (uint32_t)(kHistBins - 1) && in_bin <= 64u) {
+        // the bin's keys into LDS, then key j's rank among them
+        if (t == 0) sh_need = 0;
+        __syncthreads();
+        const uint32_t t0key = score_key(T0);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (key[i] != 0ull && hist_bin((uint32_t)(key[i] >> 32), t0key) == kb_bin) {
+            const uint32_t slot = atomicAdd(&sh_need, 1u);
+            if (slot < 64u) bin_keys[slot] = key[i];
+          }
+        __syncthreads();
+        if (t < (int)in_bin) {
+          const uint64_t mine = bin_keys[t];
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < in_bin; ++j) rank += bin_keys[j] > mine ? 1u : 0u;
+          if (rank == need - 1) sh_kth = mine;
+        }
+        __syncthreads();
+        kth = sh_kth;
+      } else {
+        kth = block_kth_regs<kPer>(key, k, h2048, wsum, sh3);
+      }
+    }
     // winners: every candidate key >= kth
     if (t == 0) sh_need = 0;
     __syncthreads();
