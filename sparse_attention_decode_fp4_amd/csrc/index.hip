@@ -17,10 +17,13 @@
 //           coalesced; up to 4 queries of a sequence share a workgroup),
 //           scores every item with packed f16 dot products (v_dot2c_f32_f16;
 //           fp8 -> f16 is exact) and appends the items scoring at least T0
-//           to a segment per (row, chunk), staged in LDS;
-//   select  gathers the segments (about 2.5 k candidates), radix-selects the
-//           exact k-th largest (score, -item) key, sorts the winners by
-//           item and writes their positions.  If the candidates cannot hold
+//           to a segment per (row, chunk), staged in LDS, counting each in
+//           a histogram of score bins above T0;
+//   select  gathers the segments (about 2.5 k candidates), finds the exact
+//           k-th largest (score, -item) key (its bin from the histogram,
+//           then a rank among that bin's few keys; a radix when the bins
+//           cannot tell), orders the winners by item and writes their
+//           positions.  If the candidates cannot hold
 //           the answer (fewer than k, or a segment overflowed: the sample
 //           misled, e.g. all scores equal) the row is recomputed exactly by
 //           itself (radix steps over recomputed keys): slow, exact, rare.
