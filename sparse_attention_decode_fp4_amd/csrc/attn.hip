@@ -90,12 +90,17 @@ __device__ __forceinline__ void dequant16(uint2 codes, float s, uint4 (&v)[2]) {
   v[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// One entry of a selected-entry tile in flight: thread t owns row t % 64,
-// channels 128 (t / 64) .. +128 (64 bytes of codes, 8 scales).
+// A selected-entry tile in flight, read with consecutive lanes on
+// consecutive bytes: in load step i (0..3) wave w takes entries
+// 16 w + 4 i + lane / 16, lane % 16 reading 16 bytes of codes (channels
+// 32 (lane % 16) .. +31, two scale groups) and those groups' two scales.  A
+// wave instruction thus covers four whole entries; a lane per entry, 16
+// bytes each, would touch 64 lines per instruction and take several times
+// as long to load the same tile.
 struct EntryFetch {
   uint4 raw[4];
-  uint2 sc;
-  bool valid;
+  uint32_t sc[4];  // the two E4M3 scales of step i in bits 0..15
+  uint32_t valid;  // bit i: the entry of step i is present
 };
 
 __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, int row) {
@@ -103,84 +108,109 @@ __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, in
   return c < p.n_idx ? p.idx[(int64_t)row * p.n_idx + c] : -1;
 }
 
-// Every load of an entry is an unconditional buffer load on a descriptor
-// at the sequence start: an empty slot uses the entry index
-// CSA2_MAX_ENTRIES, whose offsets equal the descriptors' ranges, so the
+// `pos_lane` is the position of entry lane % 64 of the tile (-1: empty), as
+// tile_position gives it.  Every load is an unconditional buffer load on a
+// descriptor at the sequence start: an empty slot uses the entry index
+// CSA2_MAX_ENTRIES, whose offsets reach the descriptors' ranges, so the
 // hardware returns zeros without touching memory.  No load waits on another.
-__device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t pos, EntryFetch& f) {
-  const int quarter = threadIdx.x >> 6;
-  f.valid = pos >= 0;
+__device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t pos_lane, EntryFetch& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
   const int64_t s0 = (int64_t)seq * p.kv_stride;
   const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.nib + s0 * CSA2_NIB_BYTES), 0, CSA2_MAX_ENTRIES * CSA2_NIB_BYTES, kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.scale + s0 * CSA2_SCALE_BYTES), 0, CSA2_MAX_ENTRIES * CSA2_SCALE_BYTES, kRawBufferWord3);
-  const uint32_t e = f.valid ? (uint32_t)pos : (uint32_t)CSA2_MAX_ENTRIES;
-  const u32x2_t sc = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(e * CSA2_SCALE_BYTES) + quarter * 8, 0, 0);
-  f.sc = make_uint2(sc[0], sc[1]);
+  f.valid = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(e * CSA2_NIB_BYTES) + quarter * 64 + 16 * i, 0, 0);
+    const int32_t pos = __shfl(pos_lane, 16 * wave + 4 * i + (lane >> 4), 64);
+    const uint32_t e = pos >= 0 ? (uint32_t)pos : (uint32_t)CSA2_MAX_ENTRIES;
+    f.valid |= (pos >= 0 ? 1u : 0u) << i;
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(e * CSA2_NIB_BYTES) + 16 * l16, 0, 0);
     f.raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    f.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(e * CSA2_SCALE_BYTES) + 2 * l16, 0, 0);
   }
 }
 
-// Dequantise a fetched entry into its row of E (zeros for an empty slot).
+// Dequantise a fetched tile into E (zeros for empty slots): each lane
+// writes 64 bytes of one row, the 16 lanes of an entry its whole row.
 __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
-  const int er = threadIdx.x & 63, quarter = threadIdx.x >> 6;
-  uint16_t* dst = s.E + er * kEStride + quarter * 128;
-  const uint32_t scw[2] = {f.sc.x, f.sc.y};
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {  // 16 bytes = 32 channels = 2 scale groups
+  for (int i = 0; i < 4; ++i) {
+    const int er = 16 * wave + 4 * i + (lane >> 4);
+    const int sw = i & 1;  // bit 2 of er: chunk c of the row sits at c ^ sw
+    uint16_t* dst = s.E + er * kEStride;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int g = 2 * i + half;
       uint4 v[2];
       dequant16(half ? make_uint2(f.raw[i].z, f.raw[i].w) : make_uint2(f.raw[i].x, f.raw[i].y),
-                e4m3_value((scw[g >> 2] >> (8 * (g & 3))) & 0xFFu), v);
-      const int sw = (er >> 2) & 1;  // chunk 2g ^ sw, 2g+1 ^ sw
-      *reinterpret_cast<uint4*>(dst + 16 * g + 8 * sw) = v[0];
-      *reinterpret_cast<uint4*>(dst + 16 * g + 8 * (1 - sw)) = v[1];
+                e4m3_value((f.sc[i] >> (8 * half)) & 0xFFu), v);
+      const int c = 4 * l16 + 2 * half;
+      *reinterpret_cast<uint4*>(dst + 8 * (c ^ sw)) = v[0];
+      *reinterpret_cast<uint4*>(dst + 8 * ((c + 1) ^ sw)) = v[1];
     }
+    if (l16 == 0) s.row_ok[er] = (uint8_t)((f.valid >> i) & 1u);
   }
-  if (quarter == 0) s.row_ok[er] = f.valid ? 1 : 0;
 }
 
-// A window tile into E: thread t copies row t % 64, channels 128 (t / 64) ..
-// The loads go through a buffer descriptor, so rows past the window read as
-// zeros and all sixteen loads are issued before any wait: linear windows use
-// a descriptor from the query's first window row to its last; a ring uses
-// the whole ring, token t at row t mod swa_ring, and an out-of-range offset
-// for rows past the window.
-__device__ __forceinline__ void load_window(const AttnPass& p, const AttnLayer& L, int wtile, int seq, int64_t t0,
-                                            int n_win, TileLds& s) {
-  const int er = threadIdx.x & 63, quarter = threadIdx.x >> 6;
-  uint16_t* dst = s.E + er * kEStride + quarter * 128;
-  const int wi = wtile * kAttnSplit + er;
+// A window tile: wave w copies rows 16 w .. +15 of the tile, one row (1 KB,
+// 16 bytes per lane) per load.  The loads go through a buffer descriptor, so
+// rows past the window read as zeros and all sixteen loads are issued before
+// any wait: linear windows use a descriptor from the query's first window
+// row to its last; a ring uses the whole ring, token t at row t mod
+// swa_ring, and an out-of-range offset for rows past the window.
+struct WindowFetch {
+  uint4 v[16];
+};
+
+__device__ __forceinline__ void fetch_window(const AttnPass& p, const AttnLayer& L, int wtile, int seq, int64_t t0,
+                                             int n_win, WindowFetch& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w0 = wtile * kAttnSplit + 16 * wave;  // window index of the wave's first row
   __amdgpu_buffer_rsrc_t rw;
-  int off;
+  int ring = 0, r_first = 0;
   if (p.swa_ring > 0) {
-    const int ring = (int)p.swa_ring;
+    ring = (int)p.swa_ring;
     rw = __builtin_amdgcn_make_buffer_rsrc((void*)(L.swa + (int64_t)seq * p.swa_stride * kD), 0, ring * kD * 2,
                                            kRawBufferWord3);
-    int r = (int)(t0 % ring) + wi;  // wi < 128 <= ring: one wrap at most
-    r = r >= ring ? r - ring : r;
-    off = wi < n_win ? r * kD * 2 + quarter * 256 : ring * kD * 2;
+    r_first = (int)(t0 % ring);
   } else {
     const int64_t r0 = t0 - p.seq.b[seq];
     rw = __builtin_amdgcn_make_buffer_rsrc((void*)(L.swa + ((int64_t)seq * p.swa_stride + r0) * kD), 0,
                                            n_win * kD * 2, kRawBufferWord3);
-    off = wi * kD * 2 + quarter * 256;
   }
-  uint4 v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16 * i, 0, 0);
-    v[i] = make_uint4(x[0], x[1], x[2], x[3]);
+    const int wi = w0 + i;
+    int off;
+    if (ring > 0) {
+      int r = r_first + wi;  // wi < 128 <= ring: one wrap at most
+      r = r >= ring ? r - ring : r;
+      off = wi < n_win ? r * kD * 2 + 16 * lane : ring * kD * 2;
+    } else {
+      off = wi * kD * 2 + 16 * lane;
+    }
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+    f.v[i] = make_uint4(x[0], x[1], x[2], x[3]);
   }
+}
+
+__device__ __forceinline__ void store_window(const WindowFetch& f, int wtile, int n_win, TileLds& s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4*>(dst + 8 * (i ^ ((er >> 2) & 1))) = v[i];
-  if (quarter == 0) s.row_ok[er] = wi < n_win ? 1 : 0;
+  for (int i = 0; i < 16; ++i) {
+    const int sw = (i >> 2) & 1;  // bit 2 of row 16 wave + i
+    *reinterpret_cast<uint4*>(s.E + (16 * wave + i) * kEStride + 8 * (lane ^ sw)) = f.v[i];
+  }
+  if (lane < 16) s.row_ok[16 * wave + lane] = wtile * kAttnSplit + 16 * wave + lane < n_win ? 1 : 0;
+}
+
+__device__ __forceinline__ void load_window(const AttnPass& p, const AttnLayer& L, int wtile, int seq, int64_t t0,
+                                            int n_win, TileLds& s) {
+  WindowFetch f;
+  fetch_window(p, L, wtile, seq, t0, n_win, f);
+  store_window(f, wtile, n_win, s);
 }
 
 // Gather tile `tile` (selected entries first, then window rows) into E.
@@ -200,6 +230,46 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int row, uint4 (&qb)[1
   const uint16_t* qrow = q + ((int64_t)row * kH + l16) * kD + 8 * g4;
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
+}
+
+// The queries of NL layers for the tile form, loaded once per workgroup:
+// thread t reads bytes 16 t + 4 KB i of each layer's 16 KB (whole lines per
+// wave instruction), the rows go to E (head h of layer j at row 16 j + h),
+// and every wave then reads its MFMA operands from there.  Each wave loading
+// its operands from memory would request the query four times over in
+// half-line pieces.  Ends with E free again.
+template <int NL>
+__device__ __forceinline__ void stage_q(const AttnPass& p, int l0, int nl, int row, TileLds& s,
+                                        uint4 (&qb)[NL][16]) {
+  const int t = threadIdx.x, lane = t & 63, l16 = lane & 15, g4 = lane >> 4;
+  uint4 v[NL][4];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    // a layer past the last loads the first layer's query again, unused
+    const uint4* src = reinterpret_cast<const uint4*>(p.layer[l0 + (j < nl ? j : 0)].q + (int64_t)row * kH * kD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[j][i] = src[t + 256 * i];
+  }
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    if (j < nl) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 8 * (t + 256 * i);  // bf16 index within the layer's [16][512]
+        *reinterpret_cast<uint4*>(s.E + (16 * j + (o >> 9)) * kEStride + (o & 511)) = v[j][i];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    if (j < nl) {
+      const uint16_t* qrow = s.E + (16 * j + l16) * kEStride + 8 * g4;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qb[j][ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
+    }
+  }
+  __syncthreads();
 }
 
 // One tile step for all 16 heads of a (layer, row): S^T = E . Q^T,
@@ -351,7 +421,6 @@ __global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
   const int64_t t0 = window_start(p, row, n_win);
   __shared__ __attribute__((aligned(16))) TileLds s;
   const float sc2 = p.softmax_scale * 1.4426950408889634f;  // logits in the log2 domain
-  uint4 qb[16];
   float m_run, l_run;
   f32x4_t o[8];
   auto reset = [&]() {
@@ -362,22 +431,32 @@ __global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
   };
   if (j < n_sel) {
     const int tile = j / n_groups, l0 = LG * (j % n_groups);
-    load_q(p.layer[l0].q, row, qb);
-    load_tile(p, p.layer[l0], tile, n_tile_idx, row, seq, t0, n_win, s);
+    const int nl = p.n_layers - l0 < LG ? p.n_layers - l0 : LG;
+    // the positions and the queries go out together; the entries follow as
+    // soon as the positions are in
+    const int32_t pos = tile_position(p, tile, row);
+    uint4 qb[LG][16];
+    EntryFetch f;
+    fetch_entry(p, seq, pos, f);
+    stage_q<LG>(p, l0, nl, row, s, qb);
+    store_entry(f, s);
 #pragma unroll
     for (int i = 0; i < LG; ++i) {
       const int l = l0 + i;
-      if (l >= p.n_layers) break;  // uniform
+      if (i >= nl) break;  // uniform
       reset();
-      tile_step(s, qb, (i + 1 < LG && l + 1 < p.n_layers) ? p.layer[l + 1].q : nullptr, row, sc2, m_run, l_run, o);
+      tile_step(s, qb[i], nullptr, row, sc2, m_run, l_run, o);
       write_partial(p, l * p.rows + row, tile, m_run, l_run, o);
     }
   } else {
     const int jj = j - n_sel, layer = jj / n_win_tiles, tile = n_tile_idx + jj % n_win_tiles;
-    load_q(p.layer[layer].q, row, qb);
-    load_tile(p, p.layer[layer], tile, n_tile_idx, row, seq, t0, n_win, s);
+    uint4 qb[1][16];
+    WindowFetch wf;
+    fetch_window(p, p.layer[layer], tile - n_tile_idx, seq, t0, n_win, wf);
+    stage_q<1>(p, layer, 1, row, s, qb);
+    store_window(wf, tile - n_tile_idx, n_win, s);
     reset();
-    tile_step(s, qb, nullptr, row, sc2, m_run, l_run, o);
+    tile_step(s, qb[0], nullptr, row, sc2, m_run, l_run, o);
     write_partial(p, layer * p.rows + row, tile, m_run, l_run, o);
   }
 }

@@ -36,10 +36,13 @@ constexpr int kSample = 2048;       // sampled items per row (two per thread of 
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
 constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks gather in one round trip
 
+// The row geometry below is all the kernels compute before their first
+// loads, so it avoids 64-bit divisions: the ratio is 1 or 2 and chunk sizes
+// are powers of two.
 __device__ __forceinline__ int64_t row_vis_positions(const IndexPass& p, int row) {
   const int seq = row / p.n_q, i = row - seq * p.n_q;
   const int64_t pos = p.seq.a[seq] + i;
-  int64_t vis = (pos + 1) / p.ratio;
+  int64_t vis = p.ratio == 2 ? (pos + 1) >> 1 : pos + 1;
   const int64_t ne = p.seq.b[seq];
   vis = vis < ne ? vis : ne;
   return vis < 0 ? 0 : vis;
@@ -47,7 +50,7 @@ __device__ __forceinline__ int64_t row_vis_positions(const IndexPass& p, int row
 
 // Items of a row, and the limit positions must stay below.
 __device__ __forceinline__ int64_t row_items(const IndexPass& p, int row, int64_t vis_pos) {
-  if (p.source == kItemsDirect) return p.block_level ? (vis_pos + 7) / 8 : vis_pos;
+  if (p.source == kItemsDirect) return p.block_level ? (vis_pos + 7) >> 3 : vis_pos;
   if (p.source == kItemsBlocks) return 8 * (int64_t)p.nsel[row];
   return p.list_len;
 }
@@ -59,6 +62,28 @@ __device__ __forceinline__ int64_t row_items(const IndexPass& p, int row, int64_
 __device__ __forceinline__ int64_t row_chunk_items(const IndexPass& p, int row) {
   const int last = p.source == kItemsDirect ? (row / p.n_q) * p.n_q + p.n_q - 1 : row;
   return scan_chunk_items(row_items(p, last, row_vis_positions(p, last)), p.k);
+}
+
+// The same for a kernel compiled for one kind of item source (kDirect: the
+// source is kItemsDirect; otherwise a block or position list), so the
+// direct path has no branches on the source.
+template <bool kDirect>
+__device__ __forceinline__ int64_t row_items_of(const IndexPass& p, int row, int64_t vis_pos) {
+  if constexpr (kDirect) return p.block_level ? (vis_pos + 7) >> 3 : vis_pos;
+  else return p.source == kItemsBlocks ? 8 * (int64_t)p.nsel[row] : (int64_t)p.list_len;
+}
+template <bool kDirect>
+__device__ __forceinline__ int64_t row_chunk_items_of(const IndexPass& p, int row) {
+  const int last = kDirect ? (row / p.n_q) * p.n_q + p.n_q - 1 : row;
+  return scan_chunk_items(row_items_of<kDirect>(p, last, row_vis_positions(p, last)), p.k);
+}
+
+// The sampled threshold of a row, read with a vector load: a scalar load of
+// memory the previous kernel wrote would hold up the scalar loads of the
+// row geometry (one counter covers them all) until it arrives.
+__device__ __forceinline__ float load_thresh(const IndexPass& p, int row) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(p.thresh + row), 0, 4, kRawBufferWord3);
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
 }
 
 // Histogram bin of a candidate's score key (candidates are at or above T0).
@@ -269,6 +294,7 @@ constexpr int kSampleThreads = 1024;
 constexpr uint32_t kMfmaUnitScales = 0x7F7F7F7Fu;  // E8M0 127 = 1.0 in every byte
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
+template <bool kDirect>
 __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   constexpr int NW = kSampleThreads / 64;
   constexpr int kTilesPerWave = kSample / 32 / NW;  // 32-key MFMA tiles per wave
@@ -277,7 +303,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   const int l32 = lane & 31, half = lane >> 5;
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
-  const int64_t n_items = row_items(p, row, vis);
+  const int64_t n_items = row_items_of<kDirect>(p, row, vis);
   int64_t S;
   uint32_t ks;
   sample_plan(n_items, (uint32_t)p.k, S, ks);
@@ -303,7 +329,13 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   for (int u = 0; u < kTilesPerWave; ++u) {
     const int64_t slot = (wave * kTilesPerWave + u) * 32 + l32;
     const int64_t item = slot < S ? sample_item(slot, S, n_items) : n_items;
-    const int64_t pos = item_position(p, row, item, n_items, vis, valid[u]);
+    int64_t pos;
+    if constexpr (kDirect) {
+      valid[u] = item < n_items;
+      pos = valid[u] ? item : 0;
+    } else {
+      pos = item_position(p, row, item, n_items, vis, valid[u]);
+    }
     uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
     if (valid[u]) {
       lo = *reinterpret_cast<const uint4*>(kb + pos * kDI);
@@ -319,9 +351,17 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
     const uint4 lo = *reinterpret_cast<const uint4*>(src), hi = *reinterpret_cast<const uint4*>(src + 16);
     A = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
+  // head weights by vector loads (see load_thresh)
   float w[kHI];
+  if (p.idx_w) {
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.idx_w + (int64_t)row * kHI), 0, 4 * kHI, kRawBufferWord3);
 #pragma unroll
-  for (int h = 0; h < kHI; ++h) w[h] = p.idx_w ? p.idx_w[(int64_t)row * kHI + h] : 1.0f;
+    for (int h = 0; h < kHI; ++h) w[h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, 4 * h, 0, 0));
+  } else {
+#pragma unroll
+    for (int h = 0; h < kHI; ++h) w[h] = 1.0f;
+  }
   for (int i = t; i < 4096; i += kSampleThreads) bins[i] = 0;
   if (t == 0) { sh[0] = 0xFFFFFFFFu; sh[2] = 0; }
 #pragma unroll
@@ -400,13 +440,13 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   const int seq = grp / qgroups;
   const int row0 = seq * p.n_q + (grp - seq * qgroups) * NQ;
   const int nq = p.n_q - (row0 - seq * p.n_q) < NQ ? p.n_q - (row0 - seq * p.n_q) : NQ;
-  const int64_t csize = row_chunk_items(p, row0);  // shared by the rows of a sequence
+  const int64_t csize = row_chunk_items_of<kDirect>(p, row0);  // shared by the rows of a sequence
   const int64_t base = (int64_t)chunk * csize;
   int64_t vis[NQ], n_items[NQ], end = 0;
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     vis[i] = i < nq ? row_vis_positions(p, row0 + i) : 0;
-    n_items[i] = i < nq ? row_items(p, row0 + i, vis[i]) : 0;
+    n_items[i] = i < nq ? row_items_of<kDirect>(p, row0 + i, vis[i]) : 0;
     const int64_t e = base + csize < n_items[i] ? base + csize : n_items[i];
     end = e > end ? e : end;
   }
@@ -485,7 +525,7 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   for (int i = 0; i < NQ; ++i) {
     const int r = i < nq ? row0 + i : row0;
     load_query_f16(p, r, quarter, q[i], w_mine[i]);
-    T0[i] = i < nq ? p.thresh[r] : INFINITY;
+    T0[i] = i < nq ? load_thresh(p, r) : INFINITY;
   }
   __syncthreads();  // n_hit is initialised
   // kDirect loads past the chunk read zeros without touching memory, so they
@@ -525,6 +565,11 @@ __device__ __forceinline__ int32_t item_to_position(const IndexPass& p, int row,
   return p.list[(int64_t)row * p.list_len + item];
 }
 
+// LDS slot of bitmap word w: thread t reads words 16t .. 16t+15, so word
+// 16t + j sits at j * 256 + t and each of those reads is conflict-free.
+__device__ __forceinline__ uint32_t bitmap_slot(uint32_t w) { return (w & 15u) * 256u + (w >> 4); }
+static_assert(kBitmapItems / 32 == 16 * 256, "bitmap words: 16 per select thread");
+
 // kPer candidates per thread, 256 kPer in all: 16 serves k <= 1,024 (about
 // 2.5 k candidates reach the sampled threshold), 32 the 2,048-block stage
 template <int kPer>
@@ -532,13 +577,27 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   constexpr int kSelCap = 256 * kPer;
   const int row = blockIdx.x;
   const int t = threadIdx.x, quarter = t & 3;
+  const int wave = t >> 6, lane = t & 63;
+  // the loads that need only the row go out first: the row's candidate
+  // histogram (filled by the scan; thread t: bins 8t..8t+7) and the counts
+  // of chunks 0..63 (every row has room for them; chunks past the row's
+  // last are masked below)
+  uint32_t hb[8];
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistBins + 8 * t);
+    const uint4 a = hp[0], b = hp[1];
+    hb[0] = a.x; hb[1] = a.y; hb[2] = a.z; hb[3] = a.w;
+    hb[4] = b.x; hb[5] = b.y; hb[6] = b.z; hb[7] = b.w;
+  }
+  const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
+  const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
+  const uint32_t cnt_lane = cnt_row[lane];
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
   const int64_t csize = row_chunk_items(p, row);
-  const int nch = (int)((n_items + csize - 1) / csize);
+  const int nch = (int)scan_chunk_count(n_items, csize);
   const uint32_t k = (uint32_t)p.k;
-  const float T0 = n_items > 0 ? p.thresh[row] : -INFINITY;  // written by the row's first scan chunk
 
   __shared__ uint32_t seg_start[kMaxChunks + 1];
   __shared__ uint64_t lc[kSelCap];
@@ -552,59 +611,50 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need;
 
-  // the row's candidate histogram (filled by the scan), thread t: bins 8t..8t+7
-  uint32_t hb[8];
-  {
-    const uint4* hp = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistBins + 8 * t);
-    const uint4 a = hp[0], b = hp[1];
-    hb[0] = a.x; hb[1] = a.y; hb[2] = a.z; hb[3] = a.w;
-    hb[4] = b.x; hb[5] = b.y; hb[6] = b.z; hb[7] = b.w;
-  }
-  const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
-  const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
   // Rows of at most kSpecChunks chunks load every segment slot together with
-  // the counts (one memory round trip): thread t takes slots 32 (t % 4) ..
-  // +32 of chunk t / 4.
+  // the counts (one memory round trip), a whole 1 KB segment per wave
+  // instruction: wave w takes chunks w, w + 4, ..., lane l their slots 2l,
+  // 2l + 1.  Each wave holds the count of chunk l in lane l, so its own
+  // prefix sum gives every chunk's start without a workgroup scan.
   const bool spec = nch <= kSpecChunks;
-  uint64_t sv[kSeg / 4];
-  uint32_t spec_n = 0;
-  if (spec && (t >> 2) < nch) {
-    const uint64_t* src = segs + (int64_t)(t >> 2) * kSeg + 32 * (t & 3);
-    spec_n = cnt_row[t >> 2];
-#pragma unroll
-    for (int i = 0; i < kSeg / 4; i += 2) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + i);
-      sv[i] = ((uint64_t)v.y << 32) | v.x;
-      sv[i + 1] = ((uint64_t)v.w << 32) | v.z;
-    }
-  }
-  // segment counts: thread t owns chunks 16t .. 16t+15
-  uint32_t c[16], local = 0;
-  bool over = false;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int ch = 16 * t + j;
-    c[j] = ch < nch ? (spec ? 0u : cnt_row[ch]) : 0u;
-    over |= c[j] > (uint32_t)kSeg;
-    local += c[j];
-  }
-  if (spec) {  // thread t holds the count of chunk t / 4; count it once
-    local = (t & 3) == 0 ? spec_n : 0u;
-    over = (t & 3) == 0 && spec_n > (uint32_t)kSeg;
-  }
-  over = __syncthreads_or(over);
+  uint4 sv[kSpecChunks / 4];
+  uint32_t spec_cnt = 0, spec_start = 0;
   uint32_t total;
-  uint32_t run = block_incl_scan_256(local, wsum, total) - local;
+  bool over = false;
+  if (spec) {
+    spec_cnt = lane < nch ? cnt_lane : 0u;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int ch = 16 * t + j;
-    if (!spec && ch < nch) seg_start[ch] = run;
-    run += c[j];
+    for (int j = 0; j < kSpecChunks / 4; ++j) {
+      const int ch = wave + 4 * j;
+      sv[j] = ch < nch ? *reinterpret_cast<const uint4*>(segs + (int64_t)ch * kSeg + 2 * lane) : make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t incl = wave_incl_add(spec_cnt);
+    spec_start = incl - spec_cnt;
+    total = (uint32_t)__shfl((int)incl, 63, 64);
+    over = __any(spec_cnt > (uint32_t)kSeg);
+  } else {
+    // segment counts: thread t owns chunks 16t .. 16t+15
+    uint32_t c[16], local = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ch = 16 * t + j;
+      c[j] = ch < nch ? cnt_row[ch] : 0u;
+      over |= c[j] > (uint32_t)kSeg;
+      local += c[j];
+    }
+    over = __syncthreads_or(over);
+    uint32_t run = block_incl_scan_256(local, wsum, total) - local;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ch = 16 * t + j;
+      if (ch < nch) seg_start[ch] = run;
+      run += c[j];
+    }
+    if (t == 0) seg_start[nch] = total;
+    __syncthreads();
   }
-  if (spec && (t & 3) == 0 && (t >> 2) < nch) seg_start[t >> 2] = run;  // exclusive prefix
-  if (t == 0) seg_start[nch] = total;
-  __syncthreads();
 
+  const float T0 = n_items > 0 ? load_thresh(p, row) : -INFINITY;  // written by the sample pass
   const bool fast = !over && total <= (uint32_t)kSelCap && (total >= k || T0 == -INFINITY);
   uint32_t n_win = 0;
   if (fast) {
@@ -614,19 +664,19 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       for (int i = t; i < kBitmapItems / 128; i += 256) bm4[i] = make_uint4(0, 0, 0, 0);
     }
     if (spec) {  // the slots loaded above: keep the first count of each chunk
-      if ((t >> 2) < nch) {
-        const uint32_t n = seg_start[(t >> 2) + 1] - seg_start[t >> 2];
-        const uint32_t base = seg_start[t >> 2];
 #pragma unroll
-        for (int i = 0; i < kSeg / 4; ++i) {
-          const uint32_t slot = 32 * (t & 3) + i;
-          if (slot < n) lc[base + slot] = sv[i];
+      for (int j = 0; j < kSpecChunks / 4; ++j) {
+        const int ch = wave + 4 * j;
+        if (ch < nch) {
+          const uint32_t n = (uint32_t)__shfl((int)spec_cnt, ch, 64);
+          const uint32_t base = (uint32_t)__shfl((int)spec_start, ch, 64);
+          if (2u * lane < n) lc[base + 2 * lane] = ((uint64_t)sv[j].y << 32) | sv[j].x;
+          if (2u * lane + 1u < n) lc[base + 2 * lane + 1] = ((uint64_t)sv[j].w << 32) | sv[j].z;
         }
       }
     }
     // otherwise gather the segments: wave w copies chunks w, w + 4, ...,
     // eight chunks (up to 16 independent loads per lane) at a time
-    const int wave = t >> 6, lane = t & 63;
     for (int c0 = spec ? nch : wave; c0 < nch; c0 += 32) {
       uint64_t v[8][2];
 #pragma unroll
@@ -713,7 +763,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       for (int i = 0; i < kPer; ++i)
         if (key[i] >= kth) {
           const uint32_t it = select_key_pos(key[i]);
-          atomicOr(&bitmap[it >> 5], 1u << (it & 31u));
+          atomicOr(&bitmap[bitmap_slot(it >> 5)], 1u << (it & 31u));
         }
       __syncthreads();
       // thread t owns words 16t .. 16t+15 (512 items)
@@ -722,7 +772,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const uint32_t wi = 16 * t + j;
-        wb[j] = wi < nwords ? bitmap[wi] : 0u;
+        wb[j] = wi < nwords ? bitmap[bitmap_slot(wi)] : 0u;
         cnt_t += __builtin_popcount(wb[j]);
       }
       uint32_t tot;
@@ -851,7 +901,10 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   if (scan_per_row > p.max_chunks) return hipErrorInvalidValue;
   const int gr = grid_rows(p.rows);
   int h = prof_begin(CSA2_K_INDEX_SAMPLE, stream);
-  hipLaunchKernelGGL(k_index_sample, dim3((unsigned)p.rows), dim3(kSampleThreads), 0, stream, p);
+  if (p.source == kItemsDirect)
+    hipLaunchKernelGGL(k_index_sample<true>, dim3((unsigned)p.rows), dim3(kSampleThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(k_index_sample<false>, dim3((unsigned)p.rows), dim3(kSampleThreads), 0, stream, p);
   prof_end(h, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -25,12 +25,20 @@ constexpr int kScanChunk = 2048;  // items per scan workgroup, at most
 // each), so the ~2.5 k keys that reach the sampled threshold fill a chunk's
 // kSeg-slot segment to about a third on average, and a row with at most k
 // items (every item a candidate) has chunks of 128 = kSeg items.
-__host__ __device__ constexpr int scan_chunks_min(int k) { return k <= 512 ? 32 : k <= 1024 ? 64 : 128; }
+__host__ __device__ constexpr int scan_chunks_min_log2(int k) { return k <= 512 ? 5 : k <= 1024 ? 6 : 7; }
+__host__ __device__ constexpr int scan_chunks_min(int k) { return 1 << scan_chunks_min_log2(k); }
 __host__ __device__ inline int64_t scan_chunk_items(int64_t n_items, int k) {
-  const int64_t want = (n_items + scan_chunks_min(k) - 1) / scan_chunks_min(k);
+  const int lg = scan_chunks_min_log2(k);
+  const int64_t want = (n_items + (1 << lg) - 1) >> lg;  // n_items >= 0
   int64_t c = 128;
   while (c < want && c < kScanChunk) c <<= 1;
   return c;
+}
+// Chunks of a row of n_items items cut into chunks of csize (a power of two).
+__host__ __device__ inline int64_t scan_chunk_count(int64_t n_items, int64_t csize) {
+  int lg = 0;
+  while (((int64_t)1 << lg) < csize) ++lg;
+  return (n_items + csize - 1) >> lg;
 }
 constexpr int kSeg = 128;
 constexpr int kMaxChunks = 4096;
