@@ -52,7 +52,7 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
   w.stats = take(kWsAlign);  // offset 0 in every layout: the fallback counter
   w.thresh = take((size_t)rows * 4);
-  w.hist = take((size_t)rows * kHistBins * 4);
+  w.hist = take((size_t)rows * kHistWords * 4);
   w.seg_count = take((size_t)rows * w.max_chunks * 4);
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);

@@ -35,6 +35,7 @@ namespace csa2 {
 constexpr int kSample = 2048;       // sampled items per row (two per thread of the sample kernel)
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
 constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks gather in one round trip
+constexpr int kSpecSlots = 64;        // ... of the first this many slots of each segment
 
 // The row geometry below is all the kernels compute before their first
 // loads, so it avoids 64-bit divisions: the ratio is 1 or 2 and chunk sizes
@@ -308,7 +309,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   uint32_t ks;
   sample_plan(n_items, (uint32_t)p.k, S, ks);
   // the row's candidate histogram starts empty (the scan counts into it)
-  for (int i = t; i < kHistBins; i += kSampleThreads) p.hist[(int64_t)row * kHistBins + i] = 0u;
+  static_assert(kHistWords == kSampleThreads, "one histogram word per thread");
+  p.hist[(int64_t)row * kHistWords + t] = 0u;
   if (ks == 0) {
     if (t == 0) p.thresh[row] = -INFINITY;
     return;
@@ -552,7 +554,10 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
     if (threadIdx.x < n) {
       const uint64_t h = hits[i][threadIdx.x];
       seg[threadIdx.x] = h;
-      atomicAdd(&p.hist[r * kHistBins + hist_bin((uint32_t)(h >> 32), score_key(T0[i]))], 1u);
+      // 16-bit bins: a row whose bins could overflow has more candidates
+      // than the select's fast path takes, which then ignores the histogram
+      const uint32_t b = hist_bin((uint32_t)(h >> 32), score_key(T0[i]));
+      atomicAdd(&p.hist[r * kHistWords + (b >> 1)], 1u << (16 * (b & 1u)));
     }
     if (threadIdx.x == 0) p.seg_count[r * p.max_chunks + chunk] = n_hit[i];
   }
@@ -584,10 +589,13 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   // last are masked below)
   uint32_t hb[8];
   {
-    const uint4* hp = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistBins + 8 * t);
-    const uint4 a = hp[0], b = hp[1];
-    hb[0] = a.x; hb[1] = a.y; hb[2] = a.z; hb[3] = a.w;
-    hb[4] = b.x; hb[5] = b.y; hb[6] = b.z; hb[7] = b.w;
+    const uint4 a = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistWords)[t];
+    const uint32_t wd[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hb[2 * i] = wd[i] & 0xFFFFu;
+      hb[2 * i + 1] = wd[i] >> 16;
+    }
   }
   const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
   const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
@@ -611,27 +619,31 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need;
 
-  // Rows of at most kSpecChunks chunks load every segment slot together with
-  // the counts (one memory round trip), a whole 1 KB segment per wave
-  // instruction: wave w takes chunks w, w + 4, ..., lane l their slots 2l,
-  // 2l + 1.  Each wave holds the count of chunk l in lane l, so its own
-  // prefix sum gives every chunk's start without a workgroup scan.
+  // Rows of at most kSpecChunks chunks load the first kSpecSlots slots of
+  // every segment together with the counts (one memory round trip), two
+  // segments per wave instruction: wave w takes chunks 2 (w + 4 j) + lane / 32,
+  // lane % 32 their slots 2 (lane % 32) and the next.  Segments hold about 40
+  // candidates on average; fuller ones load the rest afterwards.  Each wave
+  // holds the count of chunk l in lane l, so its own prefix sum gives every
+  // chunk's start without a workgroup scan.
   const bool spec = nch <= kSpecChunks;
-  uint4 sv[kSpecChunks / 4];
+  uint4 sv[kSpecChunks / 8];
   uint32_t spec_cnt = 0, spec_start = 0;
   uint32_t total;
-  bool over = false;
+  bool over = false, more = false;
   if (spec) {
     spec_cnt = lane < nch ? cnt_lane : 0u;
 #pragma unroll
-    for (int j = 0; j < kSpecChunks / 4; ++j) {
-      const int ch = wave + 4 * j;
-      sv[j] = ch < nch ? *reinterpret_cast<const uint4*>(segs + (int64_t)ch * kSeg + 2 * lane) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kSpecChunks / 8; ++j) {
+      const int ch = 2 * (wave + 4 * j) + (lane >> 5);
+      sv[j] = ch < nch ? *reinterpret_cast<const uint4*>(segs + (int64_t)ch * kSeg + 2 * (lane & 31))
+                       : make_uint4(0, 0, 0, 0);
     }
     const uint32_t incl = wave_incl_add(spec_cnt);
     spec_start = incl - spec_cnt;
     total = (uint32_t)__shfl((int)incl, 63, 64);
     over = __any(spec_cnt > (uint32_t)kSeg);
+    more = __any(spec_cnt > (uint32_t)kSpecSlots);
   } else {
     // segment counts: thread t owns chunks 16t .. 16t+15
     uint32_t c[16], local = 0;
@@ -665,13 +677,22 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
     }
     if (spec) {  // the slots loaded above: keep the first count of each chunk
 #pragma unroll
-      for (int j = 0; j < kSpecChunks / 4; ++j) {
-        const int ch = wave + 4 * j;
+      for (int j = 0; j < kSpecChunks / 8; ++j) {
+        const int ch = 2 * (wave + 4 * j) + (lane >> 5);
+        const uint32_t n = (uint32_t)__shfl((int)spec_cnt, ch, 64);
+        const uint32_t base = (uint32_t)__shfl((int)spec_start, ch, 64);
+        const uint32_t s0 = 2u * (lane & 31);
         if (ch < nch) {
+          if (s0 < n) lc[base + s0] = ((uint64_t)sv[j].y << 32) | sv[j].x;
+          if (s0 + 1u < n) lc[base + s0 + 1] = ((uint64_t)sv[j].w << 32) | sv[j].z;
+        }
+      }
+      if (more) {  // the slots past kSpecSlots of fuller segments
+        for (int ch = wave; ch < nch; ch += 4) {
           const uint32_t n = (uint32_t)__shfl((int)spec_cnt, ch, 64);
           const uint32_t base = (uint32_t)__shfl((int)spec_start, ch, 64);
-          if (2u * lane < n) lc[base + 2 * lane] = ((uint64_t)sv[j].y << 32) | sv[j].x;
-          if (2u * lane + 1u < n) lc[base + 2 * lane + 1] = ((uint64_t)sv[j].w << 32) | sv[j].z;
+          const uint32_t i = kSpecSlots + lane;
+          if (i < n) lc[base + i] = segs[(int64_t)ch * kSeg + i];
         }
       }
     }

@@ -18,6 +18,7 @@ struct SeqArgs {
 // Candidate histogram of a row: bin = (score key - key of T0) >> kHistShift,
 // the last bin taking everything above (1,024 bins per binade of scores).
 constexpr int kHistBins = 2048;
+constexpr int kHistWords = kHistBins / 2;  // two 16-bit bins per word, bin 2w in the low half
 constexpr int kHistShift = 13;
 constexpr int kScanChunk = 2048;  // items per scan workgroup, at most
 // Items per scan chunk of a row with n_items items and top-k: the row is cut
@@ -70,7 +71,7 @@ struct IndexPass {
   // workspace
   float* thresh;               // [rows] sampled threshold
   uint32_t* fallbacks;         // rows that took the exact recompute (a counter)
-  uint32_t* hist;              // [rows][kHistBins] candidates per score bin above T0
+  uint32_t* hist;              // [rows][kHistWords] candidates per score bin above T0, 16 bits a bin
   uint32_t* seg_count;         // [rows][max_chunks]
   uint64_t* seg_list;          // [rows][max_chunks][kSeg]
   int32_t max_chunks;
