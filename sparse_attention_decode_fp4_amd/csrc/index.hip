@@ -574,6 +574,7 @@ __device__ __forceinline__ int32_t item_to_position(const IndexPass& p, int row,
 // 16t + j sits at j * 256 + t and each of those reads is conflict-free.
 __device__ __forceinline__ uint32_t bitmap_slot(uint32_t w) { return (w & 15u) * 256u + (w >> 4); }
 static_assert(kBitmapItems / 32 == 16 * 256, "bitmap words: 16 per select thread");
+static_assert(kBitmapItems / 32 * 4 <= 256 * 16 * 8, "the word prefixes fit in the candidate array");
 
 // kPer candidates per thread, 256 kPer in all: 16 serves k <= 1,024 (about
 // 2.5 k candidates reach the sampled threshold), 32 the 2,048-block stage
@@ -617,7 +618,7 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   __shared__ uint32_t sh3[3];
   __shared__ uint64_t bin_keys[64];
   __shared__ uint64_t sh_kth;
-  __shared__ uint32_t sh_need;
+  __shared__ uint32_t sh_need, sh_binn;
 
   // Rows of at most kSpecChunks chunks load the first kSpecSlots slots of
   // every segment together with the counts (one memory round trip), two
@@ -670,6 +671,10 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   const bool fast = !over && total <= (uint32_t)kSelCap && (total >= k || T0 == -INFINITY);
   uint32_t n_win = 0;
   if (fast) {
+    if (t == 0) {  // (ordered before their users by the barrier after the gather)
+      sh3[0] = 0xFFFFFFFFu;
+      sh_binn = 0;
+    }
     const bool use_bitmap = n_items <= (int64_t)kBitmapItems;
     if (use_bitmap) {
       uint4* bm4 = reinterpret_cast<uint4*>(bitmap);
@@ -742,8 +747,6 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       uint32_t htot;
       const uint32_t hincl = block_incl_scan_256(hl, wsum, htot);
       uint32_t above = htot - hincl;  // keys in bins above 8t + 7
-      if (t == 0) sh3[0] = 0xFFFFFFFFu;
-      __syncthreads();
       if (htot == total && above < k && above + hl >= k) {
         for (int j = 7; j >= 0; --j) {
           if (above + hb[j] >= k) { sh3[0] = 8 * t + j; sh3[1] = k - above; sh3[2] = hb[j]; break; }
@@ -754,13 +757,11 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       const uint32_t kb_bin = sh3[0], need = sh3[1], in_bin = sh3[2];
       if (kb_bin < (uint32_t)(kHistBins - 1) && in_bin <= 64u) {
         // the bin's keys into LDS, then key j's rank among them
-        if (t == 0) sh_need = 0;
-        __syncthreads();
         const uint32_t t0key = score_key(T0);
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
           if (key[i] != 0ull && hist_bin((uint32_t)(key[i] >> 32), t0key) == kb_bin) {
-            const uint32_t slot = atomicAdd(&sh_need, 1u);
+            const uint32_t slot = atomicAdd(&sh_binn, 1u);
             if (slot < 64u) bin_keys[slot] = key[i];
           }
         __syncthreads();
@@ -777,8 +778,6 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       }
     }
     // winners: every candidate key >= kth
-    if (t == 0) sh_need = 0;
-    __syncthreads();
     if (use_bitmap) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
@@ -799,20 +798,28 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
       uint32_t tot;
       uint32_t o = block_incl_scan_256(cnt_t, wsum, tot) - cnt_t;
       n_win = tot;
-      // winners in order into LDS; the global stores follow in one coalesced
-      // pass (a store inside this loop would wait on every earlier store)
+      // winners before each word, into LDS (over lc: the candidates are in
+      // registers now); then each winner's rank is that count plus the set
+      // bits below it in its word, and it goes to its slot of `win` (the
+      // global stores follow in one coalesced pass)
+      uint32_t* wpre = reinterpret_cast<uint32_t*>(lc);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        uint32_t bits = wb[j];
-        while (bits) {
-          const int b = __ffs(bits) - 1;
-          win[o++] = (16 * t + j) * 32 + b;
-          bits &= bits - 1;
-        }
+        wpre[bitmap_slot(16 * t + j)] = o;
+        o += __builtin_popcount(wb[j]);
       }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (key[i] >= kth) {
+          const uint32_t it = select_key_pos(key[i]), ws = bitmap_slot(it >> 5);
+          win[wpre[ws] + __builtin_popcount(bitmap[ws] & ((1u << (it & 31u)) - 1u))] = it;
+        }
       __syncthreads();
     } else {
       // compaction, then a bitonic sort padded to a power of two
+      if (t == 0) sh_need = 0;
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
         if (key[i] >= kth) win[atomicAdd(&sh_need, 1u)] = select_key_pos(key[i]);
