@@ -321,9 +321,14 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   __shared__ uint32_t sh[3];
 
   // B operands: lane (l32, half) holds channels 32 half .. +32 of key l32 of
-  // each tile (loads issued first: they do not depend on the query)
-  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI + 32 * half;
-  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
+  // each tile (loads issued first: they do not depend on the query).  Every
+  // load is an unconditional buffer load: a slot without a key uses the
+  // entry index CSA2_MAX_ENTRIES, past the descriptors' ranges, and reads
+  // zeros, so no load waits for another.
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.k8 + (int64_t)seq * p.k_stride * kDI), 0, CSA2_MAX_ENTRIES * kDI, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.kscale + (int64_t)seq * p.k_stride), 0, CSA2_MAX_ENTRIES * 4, kRawBufferWord3);
   v8i_t B[kTilesPerWave];
   float kv[kTilesPerWave];
   bool valid[kTilesPerWave];
@@ -338,20 +343,22 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
     } else {
       pos = item_position(p, row, item, n_items, vis, valid[u]);
     }
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-    if (valid[u]) {
-      lo = *reinterpret_cast<const uint4*>(kb + pos * kDI);
-      hi = *reinterpret_cast<const uint4*>(kb + pos * kDI + 16);
-    }
-    B[u] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    kv[u] = valid[u] ? sb[pos] : 0.0f;
+    const uint32_t e = valid[u] ? (uint32_t)pos : (uint32_t)CSA2_MAX_ENTRIES;
+    const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half, 0, 0);
+    const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half + 16, 0, 0);
+    B[u] = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    kv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
   }
-  // A operand: row l32 < 4 is query head l32 (channels 32 half .. +32)
-  v8i_t A = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (l32 < kHI) {
-    const uint8_t* src = p.idx_q + ((int64_t)row * kHI + l32) * kDI + 32 * half;
-    const uint4 lo = *reinterpret_cast<const uint4*>(src), hi = *reinterpret_cast<const uint4*>(src + 16);
-    A = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  // A operand: row l32 < 4 is query head l32 (channels 32 half .. +32); the
+  // other lanes read past the row's 256 bytes and get zeros
+  v8i_t A;
+  {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.idx_q + (int64_t)row * kHI * kDI), 0, kHI * kDI, kRawBufferWord3);
+    const int off = l32 < kHI ? l32 * kDI + 32 * half : kHI * kDI;
+    const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+    A = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
   // head weights by vector loads (see load_thresh)
   float w[kHI];
