@@ -137,7 +137,8 @@ int64_t index_max_items(const csa2_index_args* a) {
   return m;
 }
 
-int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t stream) {
+int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t stream,
+              const AttnPass* window = nullptr) {
   for (int s0 = 0; s0 < a->batch; s0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, a->batch - s0);
     IndexPass p{};
@@ -227,7 +228,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     p.k_stride = a->k_stride;
     p.out = a->out_idx + row0 * a->k;
     p.out_stride = a->k;
-    if ((e = launch_index_pass(p, stream)) != hipSuccess) return hip_fail(e, "index pass");
+    if ((e = launch_index_pass(p, stream, window)) != hipSuccess) return hip_fail(e, "index pass");
   }
   return CSA2_OK;
 }
@@ -277,44 +278,55 @@ struct AttnJob {
   float softmax_scale;
   int n_layers;
   AttnLayer layer[kMaxAttnLayers];
+  bool window_elsewhere;  // the window tiles ran in the select launch
 };
 
-int run_attention(const AttnJob& j, void* ws, const WsLayout& w, hipStream_t stream) {
+// The attention pass of sequences s0 .. s0 + nb - 1 of a job.
+AttnPass make_attn_pass(const AttnJob& j, int s0, int nb, void* ws, const WsLayout& w) {
   const int n_tile_idx = (j.n_idx + kAttnSplit - 1) / kAttnSplit;
   const int n_tiles = n_tile_idx + (CSA2_SWA + kAttnSplit - 1) / kAttnSplit;
+  AttnPass p{};
+  p.rows = nb * j.n_q;
+  p.n_q = j.n_q;
+  p.n_idx = j.n_idx;
+  p.n_layers = j.n_layers;
+  for (int i = 0; i < nb; ++i) {
+    p.seq.a[i] = j.q_pos0[s0 + i];
+    p.seq.b[i] = j.swa_ring > 0 ? 0 : j.swa_pos0[s0 + i];
+  }
+  const int64_t row0 = (int64_t)s0 * j.n_q;
+  p.nib = j.nib + (int64_t)s0 * j.kv_stride * CSA2_NIB_BYTES;
+  p.scale = j.scale + (int64_t)s0 * j.kv_stride * CSA2_SCALE_BYTES;
+  p.kv_stride = j.kv_stride;
+  p.idx = j.idx ? j.idx + row0 * j.n_idx : nullptr;
+  p.swa_stride = j.swa_stride;
+  p.swa_ring = j.swa_ring;
+  p.softmax_scale = j.softmax_scale;
+  for (int l = 0; l < j.n_layers; ++l) {
+    p.layer[l].q = j.layer[l].q + row0 * kH * kD;
+    p.layer[l].swa = j.layer[l].swa + (int64_t)s0 * j.swa_stride * kD;
+    p.layer[l].out = j.layer[l].out + row0 * kH * kD;
+  }
+  // split the candidate tiles of a (layer, row) over workgroups until about
+  // 1024 workgroups are in flight; with many rows one workgroup walks them all
+  const int units = p.n_layers * p.rows;
+  int splits = std::max(1, std::min(n_tiles, (1024 + units - 1) / units));
+  while (splits > 1 && (int64_t)units * splits > kMaxPartialUnits) --splits;
+  p.n_tiles = n_tiles;
+  p.tiles_per_split = (n_tiles + splits - 1) / splits;
+  p.max_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  p.partial = at<float>(ws, w.partial);
+  p.window_elsewhere = j.window_elsewhere ? 1 : 0;
+  return p;
+}
+
+// The tile form (one tile per workgroup) takes the pass.
+bool tile_form(const AttnPass& p) { return p.tiles_per_split == 1 && p.max_splits == p.n_tiles; }
+
+int run_attention(const AttnJob& j, void* ws, const WsLayout& w, hipStream_t stream) {
   for (int s0 = 0; s0 < j.batch; s0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, j.batch - s0);
-    AttnPass p{};
-    p.rows = nb * j.n_q;
-    p.n_q = j.n_q;
-    p.n_idx = j.n_idx;
-    p.n_layers = j.n_layers;
-    for (int i = 0; i < nb; ++i) {
-      p.seq.a[i] = j.q_pos0[s0 + i];
-      p.seq.b[i] = j.swa_ring > 0 ? 0 : j.swa_pos0[s0 + i];
-    }
-    const int64_t row0 = (int64_t)s0 * j.n_q;
-    p.nib = j.nib + (int64_t)s0 * j.kv_stride * CSA2_NIB_BYTES;
-    p.scale = j.scale + (int64_t)s0 * j.kv_stride * CSA2_SCALE_BYTES;
-    p.kv_stride = j.kv_stride;
-    p.idx = j.idx ? j.idx + row0 * j.n_idx : nullptr;
-    p.swa_stride = j.swa_stride;
-    p.swa_ring = j.swa_ring;
-    p.softmax_scale = j.softmax_scale;
-    for (int l = 0; l < j.n_layers; ++l) {
-      p.layer[l].q = j.layer[l].q + row0 * kH * kD;
-      p.layer[l].swa = j.layer[l].swa + (int64_t)s0 * j.swa_stride * kD;
-      p.layer[l].out = j.layer[l].out + row0 * kH * kD;
-    }
-    // split the candidate tiles of a (layer, row) over workgroups until about
-    // 1024 workgroups are in flight; with many rows one workgroup walks them all
-    const int units = p.n_layers * p.rows;
-    int splits = std::max(1, std::min(n_tiles, (1024 + units - 1) / units));
-    while (splits > 1 && (int64_t)units * splits > kMaxPartialUnits) --splits;
-    p.n_tiles = n_tiles;
-    p.tiles_per_split = (n_tiles + splits - 1) / splits;
-    p.max_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
-    p.partial = at<float>(ws, w.partial);
+    const AttnPass p = make_attn_pass(j, s0, nb, ws, w);
     hipError_t e = launch_attention(p, stream);
     if (e != hipSuccess) return hip_fail(e, "attention");
   }
@@ -563,6 +575,19 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
   while (l < a->n_layers) {
     const csa2_layer& L = a->layers[l];
     if (L.mode == CSA2_MODE_FULL) st->kv = *L.kv;
+    // this layer and the Reuse layers after it share KV and indices: one
+    // attention launch
+    AttnJob j{};
+    j.batch = a->batch; j.n_q = a->n_q; j.n_idx = CSA2_TOP_K;
+    j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0; j.swa_ring = a->swa_ring;
+    j.nib = st->kv.nib; j.scale = st->kv.scale; j.kv_stride = st->kv.stride;
+    j.idx = st->indices; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
+    j.n_layers = 0;
+    do {
+      const csa2_layer& M = a->layers[l];
+      j.layer[j.n_layers++] = AttnLayer{M.q, M.swa, M.out};
+      ++l;
+    } while (l < a->n_layers && a->layers[l].mode == CSA2_MODE_REUSE && j.n_layers < kMaxAttnLayers);
     if (L.mode != CSA2_MODE_REUSE) {
       csa2_index_args ia{};
       const bool hier = (L.mode == CSA2_MODE_FULL && a->index_kind == CSA2_INDEX_HIER);
@@ -577,23 +602,21 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
       ia.k = CSA2_TOP_K; ia.n_blocks = CSA2_N_BLOCKS;
       ia.out_idx = st->indices;
       ia.out_pool = hier ? st->pool : nullptr;
-      if ((rc = run_index(&ia, workspace, w, s))) return rc;
+      // a flat decode pass in one launch runs the window tiles of the
+      // attention in its select launch (they need nothing the select
+      // computes), and the attention launch then takes the entry tiles only
+      AttnPass wp;
+      const AttnPass* win = nullptr;
+      if (ia.kind == CSA2_INDEX_FLAT && a->batch <= kMaxSeqPerLaunch && a->n_q < kPrefillMinQ) {
+        wp = make_attn_pass(j, 0, a->batch, workspace, w);
+        if (tile_form(wp)) win = &wp;
+      }
+      if ((rc = run_index(&ia, workspace, w, s, win))) return rc;
+      j.window_elsewhere = win != nullptr;
       if (L.mode == CSA2_MODE_FULL) { st->has_full = 1; if (hier && st->pool) st->has_pool = 1; }
       st->has_indices = 1;
       st->batch = a->batch; st->n_q = a->n_q;
     }
-    // this layer and the Reuse layers after it share KV and indices: one launch
-    AttnJob j{};
-    j.batch = a->batch; j.n_q = a->n_q; j.n_idx = CSA2_TOP_K;
-    j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0; j.swa_ring = a->swa_ring;
-    j.nib = st->kv.nib; j.scale = st->kv.scale; j.kv_stride = st->kv.stride;
-    j.idx = st->indices; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
-    j.n_layers = 0;
-    do {
-      const csa2_layer& M = a->layers[l];
-      j.layer[j.n_layers++] = AttnLayer{M.q, M.swa, M.out};
-      ++l;
-    } while (l < a->n_layers && a->layers[l].mode == CSA2_MODE_REUSE && j.n_layers < kMaxAttnLayers);
     if ((rc = run_attention(j, workspace, w, s))) return rc;
   }
   return CSA2_OK;

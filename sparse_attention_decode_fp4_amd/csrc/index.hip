@@ -29,6 +29,7 @@
 //           itself (radix steps over recomputed keys): slow, exact, rare.
 #include "kernels.hpp"
 #include "select.hpp"
+#include "tile.hpp"
 
 namespace csa2 {
 
@@ -586,9 +587,8 @@ static_assert(kBitmapItems / 32 * 4 <= 256 * 16 * 8, "the word prefixes fit in t
 // kPer candidates per thread, 256 kPer in all: 16 serves k <= 1,024 (about
 // 2.5 k candidates reach the sampled threshold), 32 the 2,048-block stage
 template <int kPer>
-__global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
+__device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
   constexpr int kSelCap = 256 * kPer;
-  const int row = blockIdx.x;
   const int t = threadIdx.x, quarter = t & 3;
   const int wave = t >> 6, lane = t & 63;
   // the loads that need only the row go out first: the row's candidate
@@ -913,6 +913,29 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   }
 }
 
+template <int kPer>
+__global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
+  select_row<kPer>(p, blockIdx.x);
+}
+
+// The select of a decode index pass with the window tiles of the group's
+// attention in the same launch: workgroups below p.rows select, each of the
+// others takes one window tile of one (layer, row).  The select occupies a
+// workgroup per row and leaves the rest of the chip idle, and the window
+// tiles need nothing it computes.
+template <int kPer>
+__global__ __launch_bounds__(256) void k_index_select_window(IndexPass p, AttnPass a) {
+  if ((int)blockIdx.x < p.rows) {
+    select_row<kPer>(p, blockIdx.x);
+    return;
+  }
+  __shared__ __attribute__((aligned(16))) TileLds s;
+  const int n_win_tiles = a.n_tiles - (a.n_idx + kAttnSplit - 1) / kAttnSplit;
+  const int per_row = a.n_layers * n_win_tiles;
+  const int w = blockIdx.x - p.rows, row = w / per_row, jj = w - row * per_row;
+  window_tile(a, row, jj / n_win_tiles, jj % n_win_tiles, s);
+}
+
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -927,7 +950,7 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream
   return hipGetLastError();
 }
 
-hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
+hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnPass* window) {
   if (p.rows == 0 || p.max_items == 0) return hipSuccess;
   // chunks per row, at most: scan_chunk_items keeps a row of n items within
   // max(scan_chunks_min(k), ceil(n / kScanChunk)) chunks
@@ -961,10 +984,15 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   h = prof_begin(CSA2_K_INDEX_SELECT, stream);
-  if (p.k > 1024)
+  if (p.k > 1024) {
     hipLaunchKernelGGL(k_index_select<32>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
-  else
+  } else if (window) {
+    const int n_win_tiles = window->n_tiles - (window->n_idx + kAttnSplit - 1) / kAttnSplit;
+    const int n_wg = window->rows * window->n_layers * n_win_tiles;
+    hipLaunchKernelGGL(k_index_select_window<16>, dim3((unsigned)(p.rows + n_wg)), dim3(256), 0, stream, p, *window);
+  } else {
     hipLaunchKernelGGL(k_index_select<16>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+  }
   prof_end(h, stream);
   return hipGetLastError();
 }

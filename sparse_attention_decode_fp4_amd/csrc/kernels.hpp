@@ -114,7 +114,10 @@ hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int3
 hipError_t launch_block_keys(const uint8_t* k8, const float* ks, int64_t k_stride,
                              const int64_t* n_entries, int32_t batch, uint8_t* bk8, float* bks,
                              int64_t bk_stride, hipStream_t stream);
-hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream);
+struct AttnPass;
+// `window`, if given, is the attention pass of the group the index pass
+// serves: its window tiles (window_tile) run in the select launch.
+hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnPass* window = nullptr);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
 
 // Attention over the candidates of each row for one or more layers that
@@ -145,6 +148,7 @@ struct AttnPass {
   int32_t tiles_per_split;      // tiles one workgroup walks (online softmax)
   int32_t max_splits;           // ceil(n_tiles / tiles_per_split)
   int64_t swa_ring;             // 0: linear window rows from seq.b; > 0: token t at row t mod swa_ring
+  int32_t window_elsewhere;     // tile form: the window tiles ran in the select launch (window_tile)
   // workspace (used when max_splits > 1)
   float* partial;               // [n_layers*rows][max_splits][kPartFloats]
 };
