@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 256 MiB five times (the known-size reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
-    ap.add_argument("--workload", choices=["decode", "multi", "prefill", "hier"], default="decode",
+    ap.add_argument("--page-size", type=int, default=256, help="entries per page of --workload paged")
+    ap.add_argument("--workload", choices=["decode", "multi", "prefill", "hier", "paged"], default="decode",
                     help="decode: the 128K decode group (default, the headline); prefill: a 4,096-token "
                          "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers; hier: the "
                          "hierarchical Full layer at 1M context, batch 4; multi: the decode group with 4 query "
@@ -391,6 +392,7 @@ def main():
     if args.workload == "hier":
         hier(args)
         return
+    import numpy as np
     import torch
 
     import csa2_inputs as gen
@@ -399,6 +401,9 @@ def main():
     dev = "cuda"
     B, ctx, C = args.batch, args.ctx, args.copies
     nq = 4 if args.workload == "multi" else 1   # query tokens per sequence per step
+    paged, page = args.workload == "paged", args.page_size
+    if paged and ctx % page:
+        raise SystemExit("--ctx must be a multiple of --page-size")
     seed = 1002
     # ---- caches: C copies, each its own draw
     kvs, keep = [], []
@@ -413,8 +418,24 @@ def main():
             sl = slice(b * ctx, (b + 1) * ctx)
             csa2.csa2_quantize_kv(x, k_in=k, out=[nib[sl], sc[sl], k8[sl], ks[sl]])
             del x, k
-        kvs.append(csa2.make_kv(nib, sc, k8, ks, ctx))
-        keep.append((nib, sc, k8, ks))
+        if paged:
+            # the same cache as a pool of pages in a random order, with its
+            # page table (setup, untimed)
+            n_pages = B * ctx // page
+            perm = torch.from_numpy(np.random.default_rng(seed + c).permutation(n_pages)).to(dev)
+            arrs = []
+            for a in (nib, sc, k8, ks):
+                pool = torch.empty_like(a)
+                pool.view(n_pages, page, -1)[perm] = a.view(n_pages, page, -1)
+                arrs.append(pool)
+            del nib, sc, k8, ks
+            nib, sc, k8, ks = arrs
+            table = perm.to(torch.int32).view(B, ctx // page).contiguous()
+            kvs.append(csa2.make_kv(nib, sc, k8, ks, 0, pages=csa2.make_pages(table, page, n_pages * page)))
+            keep.append((nib, sc, k8, ks, table))
+        else:
+            kvs.append(csa2.make_kv(nib, sc, k8, ks, ctx))
+            keep.append((nib, sc, k8, ks))
     torch.cuda.synchronize()
     # ---- per-layer inputs of the two runs (shared by the copies)
     q_pos0, n_entries, swa_pos0 = [ctx - nq] * B, [ctx] * B, [ctx - nq - 127] * B
@@ -494,7 +515,7 @@ def main():
         graph_s = time.perf_counter() - t0
 
     best_s = min(eager_s, graph_s) if graph_s is not None else eager_s
-    append = append_timing(csa2, gen, B, dev) if nq == 1 else None
+    append = append_timing(csa2, gen, B, dev) if nq == 1 and not paged else None
     qtok_per_step = 2 * B * nq
     value = qtok_per_step * args.steps / best_s
     step_bytes = int(2 * B * nq * algorithmic_bytes_per_qtok(ctx, nq))
@@ -502,8 +523,9 @@ def main():
     scan_avg_s = scan_ms / 1000.0 / scan_n
     achieved = scan_bytes / scan_avg_s / 1e9
     line = {
-        "metric": ("CSA2 decode query-tokens/s at 128K ctx; % of peak HBM GB/s" if nq == 1 else
-                   f"CSA2 multi-token decode query-tokens/s at 128K ctx ({nq} query tokens per sequence)"),
+        "metric": (f"CSA2 multi-token decode query-tokens/s at 128K ctx ({nq} query tokens per sequence)" if nq > 1 else
+                   f"CSA2 decode query-tokens/s at 128K ctx, paged KV ({page}-entry pages)" if paged else
+                   "CSA2 decode query-tokens/s at 128K ctx; % of peak HBM GB/s"),
         "value": round(value, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -517,11 +539,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"decode group of 4 layers run as Full+3 Reuse then Reindex+3 Reuse, "
                                f"batch {B}, {ctx} FP4 entries per sequence, top-512 + 128-token window"
-                               + ("" if nq == 1 else f", {nq} query tokens per sequence"),
+                               + ("" if nq == 1 else f", {nq} query tokens per sequence")
+                               + ("" if not paged else f", caches as a pool of {page}-entry pages in random order"),
                    "batch": B, "ctx": ctx, "query_tokens_per_sequence": nq, "layers_per_step": 8, "query_tokens_per_step": qtok_per_step,
                    "cache_copies": C, "timing": "graph replay" if best_s == graph_s else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if paged else scan_traffic(),
                      "kernel": "k_index_scan", "bytes_per_launch": scan_bytes,
                      "avg_launch_us": round(scan_avg_s * 1e6, 3)},
         "step_hbm": {"algorithmic_bytes": step_bytes,
@@ -532,7 +555,7 @@ def main():
         "kernels": kern,
         "append": append,
     }
-    if not args.no_cpu_baseline and nq == 1:
+    if not args.no_cpu_baseline and nq == 1 and not paged:
         x0 = gen.latent(ctx, seed, seq=0, device=dev).cpu().numpy()
         k0 = gen.index_key(ctx, seed, seq=0, device=dev).cpu().numpy()
         host_layers = []

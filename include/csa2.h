@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 /* Model constants the kernels are built for. */
 #define CSA2_D_LATENT 512   /* channels of one main-KV latent (key = value)        */
@@ -87,7 +87,7 @@ const char* csa2_last_error(void);
 
 /* sizeof() of the argument structs, for bindings to check their layouts:
  * 0 index_args, 1 attn_args, 2 kv, 3 layer, 4 group_state, 5 group_args,
- * 6 append_args; 0 for anything else. */
+ * 6 append_args, 7 pages; 0 for anything else. */
 size_t csa2_struct_size(int32_t which);
 
 /*
@@ -150,6 +150,36 @@ int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
                           void* stream);
 
 /*
+ * Paged caches (for serving: a pool of fixed-size pages and a page table per
+ * sequence, so sequences grow without a fixed stride).  With table set,
+ * position j of sequence s is pool entry
+ *   table[s*table_stride + j/page_size] * page_size + j % page_size
+ * of nib/scale/k8/kscale (each laid out as one [pool_entries] array), and
+ * the per-sequence strides of those arrays are not read.  Block keys (HIER)
+ * stay per-sequence arrays.  Paged caches serve the decode path: FLAT
+ * indexing with n_q < 32 (csa2_index_topk, csa2_run_group), attention and
+ * csa2_append; HIER, POOL and prefill-sized calls return
+ * CSA2_ERR_UNSUPPORTED with a table.  Results are those of the same cache
+ * laid out contiguously, bit for bit.
+ *   table         device int32 [batch][table_stride]: page indices; the
+ *                 caller guarantees one for every page a sequence's entries
+ *                 (and an append's new entry) fall in.  Indices are not
+ *                 checked on the host; an entry they place at or past
+ *                 pool_entries reads as zeros and is not written
+ *   table_stride  entries between sequences' table rows (>= the pages of the
+ *                 longest sequence; <= 65,536)
+ *   page_size     entries per page: a power of two, 128 .. 65,536
+ *   pool_entries  entries in the pool, 1 .. CSA2_MAX_ENTRIES
+ * A zero table means a contiguous cache (the other fields are then unused).
+ */
+typedef struct csa2_pages {
+  const int32_t* table;
+  int64_t table_stride;
+  int64_t pool_entries;
+  int32_t page_size;
+} csa2_pages;
+
+/*
  * Indexer + top-k (agentnet.co.il, section "CSA2: compression along the
  * layer axis": a Full layer picks 512 fresh positions; Reindex ranks with its
  * own indexer Q; the hierarchical indexer builds a pool of 2,048 blocks of 8).
@@ -192,6 +222,7 @@ typedef struct csa2_index_args {
   int32_t n_blocks;          /* HIER: blocks kept, 1..CSA2_MAX_K (2048 normally)      */
   int32_t* out_idx;          /* device [batch][n_q][k] (out)                          */
   int32_t* out_pool;         /* HIER: device [batch][n_q][n_blocks*8] or NULL (out)   */
+  csa2_pages pages;          /* paged k8/kscale (FLAT with n_q < 32), or all zero     */
 } csa2_index_args;
 
 int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, void* stream);
@@ -238,6 +269,7 @@ typedef struct csa2_attn_args {
   float softmax_scale;
   float* out;
   int64_t swa_ring;           /* 0: linear window rows; > 0: ring of this many rows   */
+  csa2_pages pages;           /* paged nib/scale, or all zero                         */
 } csa2_attn_args;
 
 int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_bytes, void* stream);
@@ -266,6 +298,7 @@ typedef struct csa2_kv {
   const uint8_t* bk8;      /* device block keys (HIER), sequence s at + s*bk_stride*64 */
   const float* bkscale;
   int64_t bk_stride;       /* blocks between sequences                                */
+  csa2_pages pages;        /* paged nib/scale/k8/kscale (stride unused), or all zero  */
 } csa2_kv;
 
 typedef struct csa2_layer {
@@ -355,6 +388,7 @@ typedef struct csa2_append_args {
   uint16_t* swa;
   int64_t swa_stride;         /* rows between sequences                               */
   int64_t swa_ring;           /* ring rows per sequence (>= 128)                      */
+  csa2_pages pages;           /* paged nib/scale/k8/kscale (stride unused), or all zero */
 } csa2_append_args;
 
 int csa2_append(const csa2_append_args* a, void* stream);

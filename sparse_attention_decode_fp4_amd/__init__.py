@@ -28,10 +28,15 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_STATE, ERR_WORKSPACE, ERR_HIP = range(6)
  K_PREFILL_SAMPLE, K_ATTENTION_MERGE, K_PREFILL_FILTER, K_PREFILL_SELECT, K_APPEND) = range(11)
 KERNEL_NAMES = ["quantize", "block_keys", "index_scan", "index_sample", "index_select", "attention",
                 "prefill_sample", "attention_merge", "prefill_filter", "prefill_select", "append"]
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _p = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class Pages(ctypes.Structure):
+    """csa2_pages: a paged cache's page table (a zero table: contiguous)."""
+    _fields_ = [("table", _p), ("table_stride", _i64), ("pool_entries", _i64), ("page_size", _i32)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -40,19 +45,19 @@ class IndexArgs(ctypes.Structure):
                 ("k8", _p), ("kscale", _p), ("k_stride", _i64),
                 ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64),
                 ("cand", _p), ("n_cand", _i32), ("k", _i32), ("n_blocks", _i32),
-                ("out_idx", _p), ("out_pool", _p)]
+                ("out_idx", _p), ("out_pool", _p), ("pages", Pages)]
 
 
 class AttnArgs(ctypes.Structure):
     _fields_ = [("batch", _i32), ("n_q", _i32), ("n_idx", _i32), ("q_pos0", _p),
                 ("q", _p), ("nib", _p), ("scale", _p), ("kv_stride", _i64), ("idx", _p),
                 ("swa", _p), ("swa_stride", _i64), ("swa_pos0", _p), ("swa_rows", _i64),
-                ("softmax_scale", _f32), ("out", _p), ("swa_ring", _i64)]
+                ("softmax_scale", _f32), ("out", _p), ("swa_ring", _i64), ("pages", Pages)]
 
 
 class KV(ctypes.Structure):
     _fields_ = [("nib", _p), ("scale", _p), ("k8", _p), ("kscale", _p), ("stride", _i64),
-                ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64)]
+                ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64), ("pages", Pages)]
 
 
 class Layer(ctypes.Structure):
@@ -76,10 +81,10 @@ class AppendArgs(ctypes.Structure):
     _fields_ = [("batch", _i32), ("ratio", _i32), ("pos", _p), ("x", _p), ("k_in", _p),
                 ("nib", _p), ("scale", _p), ("k8", _p), ("kscale", _p), ("stride", _i64),
                 ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64), ("pending", _p),
-                ("swa", _p), ("swa_stride", _i64), ("swa_ring", _i64)]
+                ("swa", _p), ("swa_stride", _i64), ("swa_ring", _i64), ("pages", Pages)]
 
 
-_STRUCTS = [IndexArgs, AttnArgs, KV, Layer, GroupState, GroupArgs, AppendArgs]
+_STRUCTS = [IndexArgs, AttnArgs, KV, Layer, GroupState, GroupArgs, AppendArgs, Pages]
 
 
 class Csa2Error(RuntimeError):
@@ -220,12 +225,13 @@ def csa2_quantize_kv(x, ratio=1, k_in=None, out=None, stream=None):
 
 
 def csa2_append(x, k_in, pos, nib, scale, k8, kscale, stride, *, ratio=1, bk8=None, bkscale=None,
-                bk_stride=0, pending=None, swa=None, swa_ring=0, stream=None):
+                bk_stride=0, pending=None, swa=None, swa_ring=0, pages=None, stream=None):
     """One decode step's write side: token pos[b] of sequence b (x float32
     [batch, 512], k_in float32 [batch, 64]) goes into the cache (sequence b
     at entry offset b * stride), its block key (bk8 / bkscale, optional) and
     the window ring swa (bf16 [batch, swa_ring, 512], optional).  Ratio 2
-    holds even tokens in pending (float32 [batch, 576])."""
+    holds even tokens in pending (float32 [batch, 576]).  With pages
+    (make_pages) the cache arrays are pools and stride is not read."""
     _need(x, torch.float32, "x")
     _need(k_in, torch.float32, "k_in")
     batch = x.shape[0]
@@ -237,6 +243,7 @@ def csa2_append(x, k_in, pos, nib, scale, k8, kscale, stride, *, ratio=1, bk8=No
     a.nib, a.scale, a.k8, a.kscale, a.stride = _ptr(nib), _ptr(scale), _ptr(k8), _ptr(kscale), stride
     a.bk8, a.bkscale, a.bk_stride = _ptr(bk8), _ptr(bkscale), bk_stride
     a.pending = _ptr(pending)
+    _set_pages(a, pages)
     sb = None
     if swa is not None:
         sb = _bits16(swa, "swa")
@@ -261,13 +268,30 @@ def csa2_build_block_keys(k8, kscale, n_entries, k_stride, bk8=None, bkscale=Non
     return bk8, bkscale
 
 
+def make_pages(table, page_size, pool_entries):
+    """A paged cache's page table: table int32 [batch, table_stride] of page
+    indices (position j of sequence b is pool entry table[b, j // page_size]
+    * page_size + j % page_size of the nib/scale/k8/kscale pools)."""
+    _need(table, torch.int32, "table")
+    pg = Pages()
+    pg.table, pg.table_stride, pg.pool_entries, pg.page_size = _ptr(table), table.shape[-1], pool_entries, page_size
+    pg._table = table
+    return pg
+
+
+def _set_pages(a, pages):
+    if pages is not None:
+        a.pages = pages
+
+
 # --------------------------------------------------------------------- indexer
 def csa2_index_topk(ws, idx_q, k8, kscale, n_entries, q_pos0, k_stride, *, kind=INDEX_FLAT,
                     ratio=1, idx_w=None, bk8=None, bkscale=None, bk_stride=0, cand=None,
                     k=TOP_K, n_blocks=N_BLOCKS, out_idx=None, out_pool=None, want_pool=False,
-                    stream=None):
+                    pages=None, stream=None):
     """Top-k positions per query.  idx_q u8 [batch, n_q, 4, 64]; returns
-    out_idx int32 [batch, n_q, k] (and the pool for HIER when want_pool)."""
+    out_idx int32 [batch, n_q, k] (and the pool for HIER when want_pool).
+    With pages (make_pages) k8/kscale are pools and k_stride is not read."""
     _need(idx_q, torch.uint8, "idx_q")
     batch, n_q = idx_q.shape[0], idx_q.shape[1]
     dev = idx_q.device
@@ -286,13 +310,14 @@ def csa2_index_topk(ws, idx_q, k8, kscale, n_entries, q_pos0, k_stride, *, kind=
     a.n_cand = 0 if cand is None else cand.shape[-1]
     a.k, a.n_blocks = k, n_blocks
     a.out_idx, a.out_pool = _ptr(out_idx), _ptr(out_pool)
+    _set_pages(a, pages)
     _check(lib.csa2_index_topk(ctypes.byref(a), ws.ptr, ws.nbytes, _stream(stream)))
     return (out_idx, out_pool) if want_pool else out_idx
 
 
 # --------------------------------------------------------------------- attention
 def csa2_sparse_swa_attn(ws, q, nib, scale, idx, swa, q_pos0, swa_pos0, kv_stride, *,
-                         softmax_scale=1.0, out=None, swa_ring=0, stream=None):
+                         softmax_scale=1.0, out=None, swa_ring=0, pages=None, stream=None):
     """q bf16 [batch, n_q, 16, 512]; idx int32 [batch, n_q, n_idx]; swa bf16
     [batch, rows, 512] (row r = token swa_pos0[b] + r; with swa_ring > 0 a
     ring, token t at row t % swa_ring, swa_pos0 unused) -> float32 [batch, n_q, 16, 512]."""
@@ -310,6 +335,7 @@ def csa2_sparse_swa_attn(ws, q, nib, scale, idx, swa, q_pos0, swa_pos0, kv_strid
     a.q, a.nib, a.scale, a.kv_stride = _ptr(qb), _ptr(nib), _ptr(scale), kv_stride
     a.idx, a.swa, a.swa_stride, a.swa_rows = _ptr(idx), _ptr(sb), swa.shape[1], swa.shape[1]
     a.softmax_scale, a.out, a.swa_ring = softmax_scale, _ptr(out), swa_ring
+    _set_pages(a, pages)
     _check(lib.csa2_sparse_swa_attn(ctypes.byref(a), ws.ptr, ws.nbytes, _stream(stream)))
     return out
 
@@ -328,11 +354,12 @@ class State:
         self._keep = []  # tensors the stored KV pointers refer to
 
 
-def make_kv(nib, scale, k8, kscale, stride, bk8=None, bkscale=None, bk_stride=0):
+def make_kv(nib, scale, k8, kscale, stride, bk8=None, bkscale=None, bk_stride=0, pages=None):
     kv = KV()
     kv.nib, kv.scale, kv.k8, kv.kscale, kv.stride = _ptr(nib), _ptr(scale), _ptr(k8), _ptr(kscale), stride
     kv.bk8, kv.bkscale, kv.bk_stride = _ptr(bk8), _ptr(bkscale), bk_stride
-    kv._tensors = (nib, scale, k8, kscale, bk8, bkscale)
+    _set_pages(kv, pages)
+    kv._tensors = (nib, scale, k8, kscale, bk8, bkscale, pages)
     return kv
 
 

@@ -92,6 +92,34 @@ int64_t visible(int64_t q_pos, int32_t ratio, int64_t n_entries) {
 }
 
 // ------------------------------------------------------------- indexer
+// A page description (csa2_pages): sane fields, and, when the longest
+// sequence is known (max_ne >= 0), a table row long enough for it.
+int validate_pages(const csa2_pages& pg, int64_t max_ne) {
+  if (!pg.table) return CSA2_OK;
+  if (!aligned(pg.table, 4)) return fail(CSA2_ERR_ARG, "pages.table must be 4-byte aligned");
+  if (pg.page_size < 128 || pg.page_size > 65536 || (pg.page_size & (pg.page_size - 1)))
+    return fail(CSA2_ERR_ARG, "pages.page_size must be a power of two in 128..65536");
+  if (pg.table_stride < 1 || pg.table_stride > 65536) return fail(CSA2_ERR_ARG, "pages.table_stride must be in 1..65536");
+  if (pg.pool_entries < 1 || pg.pool_entries > CSA2_MAX_ENTRIES)
+    return fail(CSA2_ERR_ARG, "pages.pool_entries must be in 1..%d", CSA2_MAX_ENTRIES);
+  if (max_ne >= 0 && pg.table_stride < (max_ne + pg.page_size - 1) / pg.page_size)
+    return fail(CSA2_ERR_ARG, "pages.table_stride smaller than the pages of the longest sequence");
+  return CSA2_OK;
+}
+
+// The kernels' page map of sequences s0.. (none for a contiguous cache).
+PageMap page_map(const csa2_pages& pg, int s0) {
+  PageMap m{};
+  if (!pg.table) return m;
+  m.pages = pg.table + (int64_t)s0 * pg.table_stride;
+  m.stride = pg.table_stride;
+  m.pool = pg.pool_entries;
+  int lg = 0;
+  while ((1 << lg) < pg.page_size) ++lg;
+  m.lg = lg;
+  return m;
+}
+
 int validate_index(const csa2_index_args* a) {
   if (!a) return fail(CSA2_ERR_ARG, "index args are NULL");
   if (a->kind < CSA2_INDEX_FLAT || a->kind > CSA2_INDEX_POOL) return fail(CSA2_ERR_ARG, "bad index kind %d", a->kind);
@@ -112,7 +140,13 @@ int validate_index(const csa2_index_args* a) {
     max_ne = std::max(max_ne, a->n_entries[s]);
   }
   if (max_ne > kMaxEntries) return fail(CSA2_ERR_UNSUPPORTED, "at most %lld entries per sequence", (long long)kMaxEntries);
-  if (a->batch > 1 && a->k_stride < max_ne) return fail(CSA2_ERR_ARG, "k_stride smaller than n_entries");
+  if (a->pages.table) {
+    if (a->kind != CSA2_INDEX_FLAT || a->n_q >= kPrefillMinQ)
+      return fail(CSA2_ERR_UNSUPPORTED, "paged caches take FLAT indexing with fewer than %d queries per sequence", kPrefillMinQ);
+    if (int rc = validate_pages(a->pages, max_ne)) return rc;
+  } else if (a->batch > 1 && a->k_stride < max_ne) {
+    return fail(CSA2_ERR_ARG, "k_stride smaller than n_entries");
+  }
   if (a->kind == CSA2_INDEX_HIER) {
     if (!a->bk8 || !a->bkscale) return fail(CSA2_ERR_ARG, "HIER needs bk8 and bkscale");
     if (!aligned(a->bk8, 16) || !aligned(a->bkscale, 4)) return fail(CSA2_ERR_ARG, "bk8 must be 16-byte aligned");
@@ -223,8 +257,10 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     }
     p.block_level = 0;
     p.k = a->k;
-    p.k8 = a->k8 + (int64_t)s0 * a->k_stride * kDI;
-    p.kscale = a->kscale + (int64_t)s0 * a->k_stride;
+    p.pm = page_map(a->pages, s0);
+    const int64_t koff = a->pages.table ? 0 : (int64_t)s0 * a->k_stride;  // paged: the pool
+    p.k8 = a->k8 + koff * kDI;
+    p.kscale = a->kscale + koff;
     p.k_stride = a->k_stride;
     p.out = a->out_idx + row0 * a->k;
     p.out_stride = a->k;
@@ -279,6 +315,7 @@ struct AttnJob {
   int n_layers;
   AttnLayer layer[kMaxAttnLayers];
   bool window_elsewhere;  // the window tiles ran in the select launch
+  csa2_pages pages;       // paged nib / scale, or a zero table
 };
 
 // The attention pass of sequences s0 .. s0 + nb - 1 of a job.
@@ -295,8 +332,10 @@ AttnPass make_attn_pass(const AttnJob& j, int s0, int nb, void* ws, const WsLayo
     p.seq.b[i] = j.swa_ring > 0 ? 0 : j.swa_pos0[s0 + i];
   }
   const int64_t row0 = (int64_t)s0 * j.n_q;
-  p.nib = j.nib + (int64_t)s0 * j.kv_stride * CSA2_NIB_BYTES;
-  p.scale = j.scale + (int64_t)s0 * j.kv_stride * CSA2_SCALE_BYTES;
+  const int64_t koff = j.pages.table ? 0 : (int64_t)s0 * j.kv_stride;  // paged: the pool
+  p.nib = j.nib + koff * CSA2_NIB_BYTES;
+  p.scale = j.scale + koff * CSA2_SCALE_BYTES;
+  p.pm = page_map(j.pages, s0);
   p.kv_stride = j.kv_stride;
   p.idx = j.idx ? j.idx + row0 * j.n_idx : nullptr;
   p.swa_stride = j.swa_stride;
@@ -355,6 +394,7 @@ size_t csa2_struct_size(int32_t which) {
     case 4: return sizeof(csa2_group_state);
     case 5: return sizeof(csa2_group_args);
     case 6: return sizeof(csa2_append_args);
+    case 7: return sizeof(csa2_pages);
     default: return 0;
   }
 }
@@ -390,7 +430,12 @@ int csa2_append(const csa2_append_args* a, void* stream) {
       (a->bk8 && !aligned(a->bk8, 16)) || (a->pending && !aligned(a->pending, 16)) ||
       (a->swa && !aligned(a->swa, 16)))
     return fail(CSA2_ERR_ARG, "x, k_in, k8, bk8, pending, swa must be 16-byte aligned, nib 8-byte aligned");
-  if (a->batch > 1 && a->stride < 1) return fail(CSA2_ERR_ARG, "stride must be >= 1");
+  const bool paged = a->pages.table != nullptr;
+  if (paged) {
+    if (int rc = validate_pages(a->pages, -1)) return rc;
+  } else if (a->batch > 1 && a->stride < 1) {
+    return fail(CSA2_ERR_ARG, "stride must be >= 1");
+  }
   if (a->swa) {
     if (a->swa_ring < CSA2_SWA) return fail(CSA2_ERR_ARG, "swa_ring must be >= %d", CSA2_SWA);
     if (a->batch > 1 && a->swa_stride < a->swa_ring) return fail(CSA2_ERR_ARG, "swa_stride smaller than swa_ring");
@@ -400,7 +445,10 @@ int csa2_append(const csa2_append_args* a, void* stream) {
     const int64_t e = a->pos[s] / a->ratio;
     if (e >= CSA2_MAX_ENTRIES)
       return fail(CSA2_ERR_UNSUPPORTED, "sequence %d: entry %lld at or past CSA2_MAX_ENTRIES", s, (long long)e);
-    if (a->batch > 1 && e >= a->stride) return fail(CSA2_ERR_ARG, "sequence %d: entry %lld past stride", s, (long long)e);
+    if (paged && e >= a->pages.table_stride * a->pages.page_size)
+      return fail(CSA2_ERR_ARG, "sequence %d: entry %lld past its page-table row", s, (long long)e);
+    if (!paged && a->batch > 1 && e >= a->stride)
+      return fail(CSA2_ERR_ARG, "sequence %d: entry %lld past stride", s, (long long)e);
     if (a->bk8 && a->batch > 1 && e / CSA2_BLOCK >= a->bk_stride)
       return fail(CSA2_ERR_ARG, "sequence %d: block %lld past bk_stride", s, (long long)(e / CSA2_BLOCK));
   }
@@ -412,11 +460,13 @@ int csa2_append(const csa2_append_args* a, void* stream) {
     for (int i = 0; i < nb; ++i) p.seq.a[i] = a->pos[s0 + i];
     p.x = a->x + (int64_t)s0 * CSA2_D_LATENT;
     p.k_in = a->k_in + (int64_t)s0 * CSA2_D_INDEX;
-    p.nib = a->nib + (int64_t)s0 * a->stride * CSA2_NIB_BYTES;
-    p.scale = a->scale + (int64_t)s0 * a->stride * CSA2_SCALE_BYTES;
-    p.k8 = a->k8 + (int64_t)s0 * a->stride * CSA2_D_INDEX;
-    p.kscale = a->kscale + (int64_t)s0 * a->stride;
+    const int64_t koff = paged ? 0 : (int64_t)s0 * a->stride;  // paged: the pool
+    p.nib = a->nib + koff * CSA2_NIB_BYTES;
+    p.scale = a->scale + koff * CSA2_SCALE_BYTES;
+    p.k8 = a->k8 + koff * CSA2_D_INDEX;
+    p.kscale = a->kscale + koff;
     p.stride = a->stride;
+    p.pm = page_map(a->pages, s0);
     p.bk8 = a->bk8 ? a->bk8 + (int64_t)s0 * a->bk_stride * CSA2_D_INDEX : nullptr;
     p.bks = a->bkscale ? a->bkscale + (int64_t)s0 * a->bk_stride : nullptr;
     p.bk_stride = a->bk_stride;
@@ -499,6 +549,7 @@ int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_byt
   if (!aligned(a->q, 16) || !aligned(a->swa, 16) || !aligned(a->out, 16) || (a->idx && !aligned(a->idx, 4)))
     return fail(CSA2_ERR_ARG, "q, swa, out must be 16-byte aligned");
   if (a->batch > 1 && a->kv_stride < 0) return fail(CSA2_ERR_ARG, "kv_stride < 0");
+  if ((rc = validate_pages(a->pages, -1))) return rc;
   const WsLayout w = ws_layout(0, 0, 0);  // attention uses only the partials
   if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
   AttnJob j{};
@@ -506,6 +557,7 @@ int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_byt
   j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0; j.swa_ring = a->swa_ring;
   j.nib = a->nib; j.scale = a->scale; j.kv_stride = a->kv_stride;
   j.idx = a->idx; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
+  j.pages = a->pages;
   j.n_layers = 1;
   j.layer[0] = AttnLayer{a->q, a->swa, a->out};
   return run_attention(j, workspace, w, (hipStream_t)stream);
@@ -529,6 +581,7 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
   if (!st->indices || !aligned(st->indices, 4)) return fail(CSA2_ERR_ARG, "state.indices must be a device buffer");
   // simulate the plan on the host: every mode change is checked before launching
   int has_full = st->has_full, has_idx = st->has_indices, has_pool = st->has_pool;
+  bool paged = st->has_full && st->kv.pages.table != nullptr;  // the KV a Reindex layer would index
   if ((has_idx || has_full) && (st->batch != a->batch || st->n_q != a->n_q))
     return fail(CSA2_ERR_STATE, "state was made for batch %d x n_q %d", st->batch, st->n_q);
   int64_t max_ne = 0;
@@ -547,17 +600,28 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
       if (!L.kv) return fail(CSA2_ERR_ARG, "layer %d: FULL needs kv", l);
       if ((rc = validate_kv_ptrs(L.kv->nib, L.kv->scale))) return rc;
       if (!L.kv->k8 || !L.kv->kscale || !aligned(L.kv->k8, 16)) return fail(CSA2_ERR_ARG, "layer %d: kv.k8/kscale", l);
-      if (a->batch > 1 && L.kv->stride < max_ne) return fail(CSA2_ERR_ARG, "layer %d: kv.stride < n_entries", l);
+      if (L.kv->pages.table) {
+        if (a->index_kind != CSA2_INDEX_FLAT || a->n_q >= kPrefillMinQ)
+          return fail(CSA2_ERR_UNSUPPORTED, "layer %d: paged caches take FLAT indexing with fewer than %d queries", l,
+                      kPrefillMinQ);
+        if ((rc = validate_pages(L.kv->pages, max_ne))) return rc;
+      } else if (a->batch > 1 && L.kv->stride < max_ne) {
+        return fail(CSA2_ERR_ARG, "layer %d: kv.stride < n_entries", l);
+      }
       if (a->index_kind == CSA2_INDEX_HIER && (!L.kv->bk8 || !L.kv->bkscale))
         return fail(CSA2_ERR_ARG, "layer %d: HIER needs block keys", l);
       if (a->index_kind == CSA2_INDEX_HIER && !st->pool && a->reindex_kind == CSA2_INDEX_POOL)
         return fail(CSA2_ERR_ARG, "POOL reindexing needs state.pool");
       has_full = has_idx = 1;
+      paged = L.kv->pages.table != nullptr;
       if (a->index_kind == CSA2_INDEX_HIER && st->pool) has_pool = 1;
     } else if (L.mode == CSA2_MODE_REINDEX) {
       if (!has_full) return fail(CSA2_ERR_STATE, "layer %d: REINDEX before any FULL layer", l);
       if (a->reindex_kind == CSA2_INDEX_POOL && !has_pool)
         return fail(CSA2_ERR_STATE, "layer %d: POOL REINDEX without a hierarchical pool", l);
+      if (paged && (a->reindex_kind != CSA2_INDEX_FLAT || a->n_q >= kPrefillMinQ))
+        return fail(CSA2_ERR_UNSUPPORTED, "layer %d: paged caches take FLAT indexing with fewer than %d queries", l,
+                    kPrefillMinQ);
       has_idx = 1;
     } else {
       if (!has_full || !has_idx) return fail(CSA2_ERR_STATE, "layer %d: REUSE before any FULL layer", l);
@@ -582,6 +646,7 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
     j.q_pos0 = a->q_pos0; j.swa_pos0 = a->swa_pos0; j.swa_ring = a->swa_ring;
     j.nib = st->kv.nib; j.scale = st->kv.scale; j.kv_stride = st->kv.stride;
     j.idx = st->indices; j.swa_stride = a->swa_stride; j.softmax_scale = a->softmax_scale;
+    j.pages = st->kv.pages;
     j.n_layers = 0;
     do {
       const csa2_layer& M = a->layers[l];
@@ -602,6 +667,7 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
       ia.k = CSA2_TOP_K; ia.n_blocks = CSA2_N_BLOCKS;
       ia.out_idx = st->indices;
       ia.out_pool = hier ? st->pool : nullptr;
+      ia.pages = st->kv.pages;
       // a flat decode pass in one launch runs the window tiles of the
       // attention in its select launch (they need nothing the select
       // computes), and the attention launch then takes the entry tiles only

@@ -199,8 +199,18 @@ __device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t
   u32x4_t raw = u32x4_t{0, 0, 0, 0};
   float ks = 0.0f;
   if (valid) {
-    raw = *reinterpret_cast<const u32x4_t*>(p.k8 + ((int64_t)seq * p.k_stride + pos) * kDI + quarter * 16);
-    ks = p.kscale[(int64_t)seq * p.k_stride + pos];
+    if (p.pm.pages) {
+      const uint32_t e = paged_entry_at(p.pm, seq, pos);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)p.k8, 0, (int)(p.pm.pool * kDI), kRawBufferWord3);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)p.kscale, 0, (int)(p.pm.pool * 4), kRawBufferWord3);
+      raw = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + quarter * 16, 0, 0);
+      ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
+    } else {
+      raw = *reinterpret_cast<const u32x4_t*>(p.k8 + ((int64_t)seq * p.k_stride + pos) * kDI + quarter * 16);
+      ks = p.kscale[(int64_t)seq * p.k_stride + pos];
+    }
   }
   return quad_score(q, w_mine, raw, ks);
 }
@@ -326,25 +336,38 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   // load is an unconditional buffer load: a slot without a key uses the
   // entry index CSA2_MAX_ENTRIES, past the descriptors' ranges, and reads
   // zeros, so no load waits for another.
+  // (paged: descriptors over the pool, the entry from the page table, every
+  // page-table load issued before the key loads)
+  const bool paged = p.pm.pages != nullptr;
+  const uint32_t lim = paged ? (uint32_t)p.pm.pool : (uint32_t)CSA2_MAX_ENTRIES;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.k8 + (int64_t)seq * p.k_stride * kDI), 0, CSA2_MAX_ENTRIES * kDI, kRawBufferWord3);
+      (void*)(paged ? p.k8 : p.k8 + (int64_t)seq * p.k_stride * kDI), 0, (int)(lim * kDI), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.kscale + (int64_t)seq * p.k_stride), 0, CSA2_MAX_ENTRIES * 4, kRawBufferWord3);
+      (void*)(paged ? p.kscale : p.kscale + (int64_t)seq * p.k_stride), 0, (int)(lim * 4), kRawBufferWord3);
   v8i_t B[kTilesPerWave];
   float kv[kTilesPerWave];
   bool valid[kTilesPerWave];
+  int64_t pos_u[kTilesPerWave];
+  uint32_t page_u[kTilesPerWave];
 #pragma unroll
   for (int u = 0; u < kTilesPerWave; ++u) {
     const int64_t slot = (wave * kTilesPerWave + u) * 32 + l32;
     const int64_t item = slot < S ? sample_item(slot, S, n_items) : n_items;
-    int64_t pos;
     if constexpr (kDirect) {
       valid[u] = item < n_items;
-      pos = valid[u] ? item : 0;
+      pos_u[u] = valid[u] ? item : 0;
     } else {
-      pos = item_position(p, row, item, n_items, vis, valid[u]);
+      pos_u[u] = item_position(p, row, item, n_items, vis, valid[u]);
     }
-    const uint32_t e = valid[u] ? (uint32_t)pos : (uint32_t)CSA2_MAX_ENTRIES;
+    page_u[u] = 0;
+    if (paged)
+      page_u[u] = __builtin_amdgcn_raw_buffer_load_b32(page_row(p.pm, seq),
+                                                       valid[u] ? (int)((pos_u[u] >> p.pm.lg) * 4) : (int)(p.pm.stride * 4), 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kTilesPerWave; ++u) {
+    const int64_t pos = pos_u[u];
+    const uint32_t e = !valid[u] ? lim : paged ? paged_entry(p.pm, page_u[u], pos) : (uint32_t)pos;
     const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half, 0, 0);
     const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half + 16, 0, 0);
     B[u] = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -474,9 +497,22 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   float w_mine[NQ], T0[NQ];  // loaded after the first keys: their loads overlap
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
-  // (used by the kDirect loads only)
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, (int)(end * kDI), kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)sb, 0, (int)(end * 4), kRawBufferWord3);
+  // (used by the kDirect loads only.)  Paged: descriptors over the pool, and
+  // lane j holds the page-table value of the chunk's page j: a batch of
+  // kStep items lies in one page (pages hold at least 128 entries, batches
+  // start at multiples of kStep), so its entries are one page's consecutive
+  // entries
+  const bool paged = kDirect && p.pm.pages != nullptr;
+  const uint32_t lim = paged ? (uint32_t)p.pm.pool : (uint32_t)end;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? p.k8 : kb), 0, (int)(lim * kDI), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? p.kscale : sb), 0, (int)(lim * 4), kRawBufferWord3);
+  uint32_t page_lane = 0;
+  if (paged) {
+    const int64_t pg = (base >> p.pm.lg) + (threadIdx.x & 63);
+    page_lane = __builtin_amdgcn_raw_buffer_load_b32(page_row(p.pm, seq), (int)(pg * 4), 0, 0);
+  }
 
   // U items per lane quad per batch; two batches in flight (double buffer)
   struct Batch {
@@ -484,12 +520,15 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
     float ks[U];
   };
   auto load = [&](Batch& B, int64_t it0) {
+    uint32_t page = 0;
+    if (paged) page = (uint32_t)__shfl((int)page_lane, (int)(((it0 >> p.pm.lg) - (base >> p.pm.lg)) & 63), 64);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t item = it0 + u * 64 + sub;
       if constexpr (kDirect) {
-        B.raw[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(item * kDI) + quarter * 16, 0, kLoadNonTemporal);
-        B.ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(item * 4), 0, 0));
+        const uint32_t e = !paged ? (uint32_t)item : item < end ? paged_entry(p.pm, page, item) : lim;
+        B.raw[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + quarter * 16, 0, kLoadNonTemporal);
+        B.ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
       } else {
         bool valid;
         const int64_t pos = item_position(p, row0, item, end, vis[0], valid);

@@ -13,6 +13,39 @@ struct SeqArgs {
   int64_t b[kMaxSeqPerLaunch];
 };
 
+// Paged caches: with `pages` set, position j of sequence s is entry
+// pages[s * stride + (j >> lg)] * 2^lg + (j mod 2^lg) of the pool the cache
+// pointers address (pages of 2^lg entries, 2^lg >= 128); otherwise sequence
+// s starts `stride` entries of its own pass after sequence s - 1.  Paged
+// accesses go through buffer descriptors over the pool's `pool` entries, so
+// an entry past the pool (a bad page index) reads zeros and is not written.
+struct PageMap {
+  const int32_t* pages;  // device [sequences][stride] or null
+  int64_t stride;        // page-table entries between sequences
+  int64_t pool;          // entries in the pool (<= CSA2_MAX_ENTRIES)
+  int32_t lg;            // log2 of the entries per page
+};
+
+// Descriptor over sequence `seq`'s row of the page table: an index past the
+// row reads 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_row(const PageMap& m, int seq) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(m.pages + (int64_t)seq * m.stride), 0, (int)(m.stride * 4),
+                                           kRawBufferWord3);
+}
+
+// Pool entry of position `pos` given its page's table value, clamped to the
+// pool size (which every paged descriptor treats as out of range).
+__device__ __forceinline__ uint32_t paged_entry(const PageMap& m, uint32_t page, int64_t pos) {
+  const int64_t e = ((int64_t)page << m.lg) | (pos & (((int64_t)1 << m.lg) - 1));
+  return e < m.pool && e >= 0 ? (uint32_t)e : (uint32_t)m.pool;
+}
+
+// Pool entry of position `pos` of sequence `seq` (one page-table load).
+__device__ __forceinline__ uint32_t paged_entry_at(const PageMap& m, int seq, int64_t pos) {
+  const uint32_t page = __builtin_amdgcn_raw_buffer_load_b32(page_row(m, seq), (int)((pos >> m.lg) * 4), 0, 0);
+  return paged_entry(m, page, pos);
+}
+
 // Items scored per workgroup of the indexer scan; candidates kept per
 // (row, chunk) segment; chunks per row (items per row <= 8M).
 // Candidate histogram of a row: bin = (score key - key of T0) >> kHistShift,
@@ -81,6 +114,7 @@ struct IndexPass {
   int32_t* out_count;          // [rows] or null
   int32_t* out_pool;           // optional: pool positions of the kept blocks
   int32_t pool_stride;
+  PageMap pm;                  // paged k8 / kscale (direct items over entries only)
 };
 
 // Kernel classes of the optional timing records (csa2_profile_*).
@@ -105,6 +139,7 @@ struct AppendPass {
   float* pending;               // ratio 2: [batch][576]
   uint16_t* swa;                // or null
   int64_t swa_stride, swa_ring;
+  PageMap pm;                   // paged nib / scale / k8 / kscale
 };
 hipError_t launch_append(const AppendPass& p, int32_t batch, hipStream_t stream);
 
@@ -149,6 +184,7 @@ struct AttnPass {
   int32_t max_splits;           // ceil(n_tiles / tiles_per_split)
   int64_t swa_ring;             // 0: linear window rows from seq.b; > 0: token t at row t mod swa_ring
   int32_t window_elsewhere;     // tile form: the window tiles ran in the select launch (window_tile)
+  PageMap pm;                   // paged nib / scale
   // workspace (used when max_splits > 1)
   float* partial;               // [n_layers*rows][max_splits][kPartFloats]
 };

@@ -175,16 +175,27 @@ __global__ __launch_bounds__(64) void k_append(AppendPass p) {
     pb = *reinterpret_cast<const float4*>(pend + 8 * t + 4);
     kpend = pend[CSA2_D_LATENT + t];
   }
+  // the cache entries: contiguous, or one page of a pool (the block's eight
+  // entries lie in the new entry's page: pages hold whole blocks); paged
+  // accesses go through descriptors over the pool
+  const bool paged = p.pm.pages != nullptr;
+  const uint32_t lim = paged ? (uint32_t)p.pm.pool : (uint32_t)CSA2_MAX_ENTRIES;
+  const int64_t ent = paged ? (int64_t)paged_entry_at(p.pm, s, e) : (int64_t)s * p.stride + e;
+  const int64_t base = paged ? 0 : (int64_t)s * p.stride;  // descriptor start, in entries
+  const uint32_t rel = (uint32_t)(ent - base);             // the new entry, from there
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.k8 + base * CSA2_D_INDEX), 0, (int)(lim * CSA2_D_INDEX), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.kscale + base), 0, (int)(lim * 4), kRawBufferWord3);
   uint32_t prev[7];
   float prev_s[7];
   {
-    const uint8_t* kb = p.k8 + ((int64_t)s * p.stride + 8 * blk) * CSA2_D_INDEX + t;
-    const float* sb = p.kscale + (int64_t)s * p.stride + 8 * blk;
+    const uint32_t e0 = rel - (uint32_t)(e - 8 * blk);  // the block's first entry
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
       const bool ok = blocks && j + 1 < count;
-      prev[j] = ok ? kb[j * CSA2_D_INDEX] : 0u;
-      prev_s[j] = ok ? sb[j] : 0.0f;
+      prev[j] = ok ? __builtin_amdgcn_raw_buffer_load_b8(rk, (int)((e0 + j) * CSA2_D_INDEX) + t, 0, 0) : 0u;
+      prev_s[j] = ok ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (int)((e0 + j) * 4), 0, 0)) : 0.0f;
     }
   }
 
@@ -228,16 +239,19 @@ __global__ __launch_bounds__(64) void k_append(AppendPass p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) w8 |= fp4_code(v[i], sv) << (4 * i);
   }
-  const int64_t ent = (int64_t)s * p.stride + e;
-  *reinterpret_cast<uint32_t*>(p.nib + ent * CSA2_NIB_BYTES + t * 4) = w8;
-  if ((t & 1) == 0) p.scale[ent * CSA2_SCALE_BYTES + (t >> 1)] = (uint8_t)sc;
+  const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.nib + base * CSA2_NIB_BYTES), 0, (int)(lim * CSA2_NIB_BYTES), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.scale + base * CSA2_SCALE_BYTES), 0, (int)(lim * CSA2_SCALE_BYTES), kRawBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b32(w8, rn, (int)(rel * CSA2_NIB_BYTES) + t * 4, 0, 0);
+  if ((t & 1) == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rsc, (int)(rel * CSA2_SCALE_BYTES) + (t >> 1), 0, 0);
 
   // ---- indexer key: channel t
   const float kv = paired ? f32_mul(f32_add(kpend, kin), 0.5f) : kin;
   const float ks = f32_div(wave_max64(__builtin_fabsf(kv)), 448.0f);
   const uint32_t code = ks > 0.0f ? e4m3_from_f32(f32_div(kv, ks)) : 0u;
-  p.k8[ent * CSA2_D_INDEX + t] = (uint8_t)code;
-  if (t == 0) p.kscale[ent] = ks;
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, rk, (int)(rel * CSA2_D_INDEX) + t, 0, 0);
+  if (t == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ks), rks, (int)(rel * 4), 0, 0);
 
   // ---- block key of the new entry's block, channel t: its earlier entries
   // in position order, then the new key

@@ -87,21 +87,29 @@ __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, in
 
 // `pos_lane` is the position of entry lane % 64 of the tile (-1: empty), as
 // tile_position gives it.  Every load is an unconditional buffer load on a
-// descriptor at the sequence start: an empty slot uses the entry index
-// CSA2_MAX_ENTRIES, whose offsets reach the descriptors' ranges, so the
-// hardware returns zeros without touching memory.  No load waits on another.
+// descriptor at the sequence start (or over the pool of a paged cache): an
+// empty slot uses the entry index at the descriptors' limit
+// (CSA2_MAX_ENTRIES, or the pool size), so the hardware returns zeros
+// without touching memory.  No load waits on another.
 __device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t pos_lane, EntryFetch& f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
-  const int64_t s0 = (int64_t)seq * p.kv_stride;
+  // paged caches: descriptors over the pool, and each lane first turns its
+  // position into a pool entry (one page-table load)
+  const bool paged = p.pm.pages != nullptr;
+  const uint32_t lim = paged ? (uint32_t)p.pm.pool : (uint32_t)CSA2_MAX_ENTRIES;
+  const int64_t s0 = paged ? 0 : (int64_t)seq * p.kv_stride;
   const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.nib + s0 * CSA2_NIB_BYTES), 0, CSA2_MAX_ENTRIES * CSA2_NIB_BYTES, kRawBufferWord3);
+      (void*)(p.nib + s0 * CSA2_NIB_BYTES), 0, (int)(lim * CSA2_NIB_BYTES), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.scale + s0 * CSA2_SCALE_BYTES), 0, CSA2_MAX_ENTRIES * CSA2_SCALE_BYTES, kRawBufferWord3);
+      (void*)(p.scale + s0 * CSA2_SCALE_BYTES), 0, (int)(lim * CSA2_SCALE_BYTES), kRawBufferWord3);
+  uint32_t e_lane = pos_lane >= 0 ? (uint32_t)pos_lane : lim;
+  if (paged && pos_lane >= 0) e_lane = paged_entry_at(p.pm, seq, pos_lane);
   f.valid = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int32_t pos = __shfl(pos_lane, 16 * wave + 4 * i + (lane >> 4), 64);
-    const uint32_t e = pos >= 0 ? (uint32_t)pos : (uint32_t)CSA2_MAX_ENTRIES;
+    const int src = 16 * wave + 4 * i + (lane >> 4);
+    const int32_t pos = __shfl(pos_lane, src, 64);
+    const uint32_t e = (uint32_t)__shfl((int)e_lane, src, 64);
     f.valid |= (pos >= 0 ? 1u : 0u) << i;
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(e * CSA2_NIB_BYTES) + 16 * l16, 0, 0);
     f.raw[i] = make_uint4(v[0], v[1], v[2], v[3]);

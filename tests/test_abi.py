@@ -173,3 +173,76 @@ def test_group_state_errors(m):
     layer[0].mode = m.MODE_REUSE
     assert f(ctypes.byref(g), ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_STATE
     assert f(None, ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_ARG
+
+
+def _pages(m, table=None, table_stride=1, page_size=128, pool_entries=1024):
+    pg = m.Pages()
+    pg.table = _p(0x8000) if table is None else table
+    pg.table_stride, pg.page_size, pg.pool_entries = table_stride, page_size, pool_entries
+    return pg
+
+
+def test_paged_cache_errors(m):
+    """Page descriptions are checked on the host: page size a power of two
+    in 128..65536, a table row long enough for the longest sequence, a pool
+    inside CSA2_MAX_ENTRIES, an aligned table; the non-decode index kinds and
+    prefill-sized calls refuse paged caches."""
+    f = m.lib.csa2_index_topk
+    ok = _pages(m)                                  # 100 entries fit one page of 128
+    bad = [
+        (_pages(m, page_size=64), m.ERR_ARG),       # page below 128 entries
+        (_pages(m, page_size=200), m.ERR_ARG),      # not a power of two
+        (_pages(m, page_size=1 << 17), m.ERR_ARG),  # above 65536
+        (_pages(m, table_stride=0), m.ERR_ARG),
+        (_pages(m, pool_entries=0), m.ERR_ARG),
+        (_pages(m, pool_entries=1 << 23), m.ERR_ARG),   # past CSA2_MAX_ENTRIES
+        (_pages(m, table=_p(0x8002)), m.ERR_ARG),       # misaligned table
+    ]
+    for pg, code in bad:
+        assert f(ctypes.byref(_index_args(m, pages=pg, k_stride=0)), _p(), 1 << 30, None) == code
+    ne = (ctypes.c_int64 * 2)(300, 100)             # 300 entries need 3 pages of 128
+    a = _index_args(m, pages=_pages(m, table_stride=2), k_stride=0)
+    a.n_entries = ctypes.cast(ne, ctypes.c_void_p)
+    assert f(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_ARG
+    assert b"table_stride" in m.lib.csa2_last_error()
+    assert f(ctypes.byref(_index_args(m, pages=ok, kind=m.INDEX_HIER, bk8=_p(), bkscale=_p())), _p(), 1 << 30,
+             None) == m.ERR_UNSUPPORTED
+    qp = (ctypes.c_int64 * 2)(99, 99)
+    a = _index_args(m, pages=ok, n_q=32)
+    a.q_pos0 = ctypes.cast(qp, ctypes.c_void_p)
+    assert f(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_UNSUPPORTED
+
+    # attention: the same field checks
+    at = m.AttnArgs()
+    qp1, sp1 = (ctypes.c_int64 * 1)(300), (ctypes.c_int64 * 1)(173)
+    at.batch, at.n_q, at.n_idx = 1, 1, 512
+    at.q_pos0, at.swa_pos0 = ctypes.cast(qp1, ctypes.c_void_p), ctypes.cast(sp1, ctypes.c_void_p)
+    at.q, at.nib, at.scale, at.idx, at.swa, at.out = _p(), _p(), _p(), _p(), _p(), _p()
+    at.swa_rows, at.swa_stride = 128, 128
+    at.pages = _pages(m, page_size=96)
+    assert m.lib.csa2_sparse_swa_attn(ctypes.byref(at), _p(), 1 << 30, None) == m.ERR_ARG
+
+    # append: an entry past the sequence's page-table row
+    pos = (ctypes.c_int64 * 2)(5, 300)
+    ap = m.AppendArgs()
+    ap.batch, ap.ratio, ap.pos = 2, 1, ctypes.cast(pos, ctypes.c_void_p)
+    ap.x, ap.k_in, ap.nib, ap.scale, ap.k8, ap.kscale = _p(), _p(0x1000), _p(0x2000), _p(0x3000), _p(0x4000), _p(0x5000)
+    ap.pages = _pages(m, table_stride=2)            # rows of 2 pages: entries < 256
+    assert m.lib.csa2_append(ctypes.byref(ap), None) == m.ERR_ARG
+    assert b"page-table row" in m.lib.csa2_last_error()
+
+    # group plan: a paged Full layer with hierarchical indexing
+    kv = m.KV()
+    kv.nib, kv.scale, kv.k8, kv.kscale = _p(), _p(), _p(), _p()
+    kv.bk8, kv.bkscale, kv.pages = _p(), _p(), ok
+    layer = (m.Layer * 1)()
+    layer[0].mode, layer[0].q, layer[0].swa, layer[0].out = m.MODE_FULL, _p(), _p(), _p()
+    layer[0].idx_q, layer[0].kv = _p(), ctypes.pointer(kv)
+    g = m.GroupArgs()
+    qp2, ne2, sp2 = (ctypes.c_int64 * 1)(99), (ctypes.c_int64 * 1)(100), (ctypes.c_int64 * 1)(0)
+    g.batch, g.n_q, g.ratio, g.index_kind = 1, 1, 1, m.INDEX_HIER
+    g.q_pos0, g.n_entries, g.swa_pos0 = (ctypes.cast(x, ctypes.c_void_p) for x in (qp2, ne2, sp2))
+    g.swa_stride, g.swa_rows, g.softmax_scale, g.n_layers, g.layers = 128, 128, 1.0, 1, layer
+    st = m.GroupState()
+    st.indices = _p()
+    assert m.lib.csa2_run_group(ctypes.byref(g), ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_UNSUPPORTED

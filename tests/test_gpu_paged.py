@@ -1,0 +1,208 @@
+"""Paged caches on the GPU: the caches as a pool of fixed-size pages with a
+page table per sequence (pages placed in a random order).  Every result
+must equal, bit for bit, the one the same cache gives laid out contiguously
+(whose parity with the oracle the other tests establish), and the indices
+are also checked against the oracle here."""
+
+import numpy as np
+import pytest
+import torch
+
+import csa2_inputs as gen
+import oracle
+from parity import check_close, check_topk
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa2():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import sparse_attention_decode_fp4_amd as m
+    return m
+
+
+def _contiguous(csa2, n_entries, stride, seed, dev="cuda"):
+    B = len(n_entries)
+    nib = torch.zeros((B * stride, 256), dtype=torch.uint8, device=dev)
+    sc = torch.zeros((B * stride, 32), dtype=torch.uint8, device=dev)
+    k8 = torch.zeros((B * stride, 64), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B * stride,), dtype=torch.float32, device=dev)
+    for b, n in enumerate(n_entries):
+        if n == 0:
+            continue
+        x = gen.latent(n, seed, seq=b, device=dev)
+        k = gen.index_key(n, seed, seq=b, device=dev)
+        e0 = b * stride
+        csa2.csa2_quantize_kv(x, k_in=k, out=[nib[e0:e0 + n], sc[e0:e0 + n], k8[e0:e0 + n], ks[e0:e0 + n]])
+    return nib, sc, k8, ks
+
+
+def _paginate(csa2, arrays, n_entries, stride, page, seed, extra_pages=3):
+    """The contiguous caches scattered over a pool, page by page in a random
+    order (plus unused pages); returns the pools and the page table."""
+    rng = np.random.default_rng(seed)
+    B = len(n_entries)
+    table_stride = max(1, max((stride + page - 1) // page, 1))
+    n_pages = B * table_stride + extra_pages
+    order = rng.permutation(n_pages)
+    table = np.zeros((B, table_stride), dtype=np.int32)
+    pools = [torch.zeros((n_pages * page,) + a.shape[1:], dtype=a.dtype, device=a.device) for a in arrays]
+    i = 0
+    for b in range(B):
+        for j in range(table_stride):
+            pg = int(order[i]); i += 1
+            table[b, j] = pg
+            lo, hi = j * page, min((j + 1) * page, stride)
+            if lo >= hi:
+                continue
+            for a, pool in zip(arrays, pools):
+                pool[pg * page: pg * page + (hi - lo)] = a[b * stride + lo: b * stride + hi]
+    t = torch.from_numpy(table).to(arrays[0].device)
+    return pools, csa2.make_pages(t, page, n_pages * page), t
+
+
+@pytest.mark.parametrize("n_q,page", [(1, 256), (4, 128)])
+def test_paged_index_matches_contiguous(csa2, n_q, page):
+    seed = 71 + n_q
+    n_entries = [9000, 40000, 1500]  # the last row is short: every key is a candidate
+    stride = 40000
+    nib, sc, k8, ks = _contiguous(csa2, n_entries, stride, seed)
+    (pk8, pks), pages, _ = _paginate(csa2, [k8, ks], n_entries, stride, page, seed)
+    q = gen.index_query((3, n_q), seed, device="cuda")
+    q_pos0 = [n - n_q for n in n_entries]
+    ws = csa2.Workspace(3, n_q, stride)
+    ref = csa2.csa2_index_topk(ws, q, k8, ks, n_entries, q_pos0, stride)
+    got = csa2.csa2_index_topk(ws, q, pk8, pks, n_entries, q_pos0, 0, pages=pages)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert ws.fallbacks() == 0
+    k8h, ksh, qh, gh = k8.cpu().numpy(), ks.cpu().numpy(), q.cpu().numpy(), got.cpu().numpy()
+    for b, n in enumerate(n_entries):
+        e0 = b * stride
+        for i in range(n_q):
+            vis = min(n, q_pos0[b] + i + 1)
+            r = oracle.index_flat(qh[b, i], None, k8h[e0:e0 + n], ksh[e0:e0 + n], vis)
+            check_topk(gh[b, i], r, oracle.scores(qh[b, i], None, k8h[e0:e0 + n], ksh[e0:e0 + n]), 512, vis,
+                       f"seq {b} q{i}")
+
+
+@pytest.mark.parametrize("n_q", [1, 3])
+def test_paged_attention_matches_contiguous(csa2, n_q):
+    """n_q 1 takes the tile form, 3 the walk form."""
+    seed, B, stride, page = 29 + n_q, 2, 6000, 512
+    n_entries = [6000, 4100]
+    nib, sc, k8, ks = _contiguous(csa2, n_entries, stride, seed)
+    (pnib, psc), pages, _ = _paginate(csa2, [nib, sc], n_entries, stride, page, seed)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([np.sort(rng.choice(n_entries[b], 512, replace=False)) for _ in range(n_q)])
+                    for b in range(B)]).astype(np.int32)
+    idx[1, 0, -5:] = -1  # a few empty slots
+    idx_d = torch.from_numpy(idx).cuda()
+    q_pos0 = [n - n_q for n in n_entries]
+    swa_pos0 = [p - 127 for p in q_pos0]
+    q = gen.attn_query((B, n_q), seed, device="cuda")
+    swa = gen.window_rows(B, 127 + n_q, seed, device="cuda")
+    ws = csa2.Workspace(B, n_q, stride)
+    ref = csa2.csa2_sparse_swa_attn(ws, q, nib, sc, idx_d, swa, q_pos0, swa_pos0, stride)
+    got = csa2.csa2_sparse_swa_attn(ws, q, pnib, psc, idx_d, swa, q_pos0, swa_pos0, 0, pages=pages)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    nh, sh = nib.cpu().numpy(), sc.cpu().numpy()
+    r = oracle.sparse_swa_attention(gen.bf16_bits(q[0, 0]), nh[:stride], sh[:stride], idx[0, 0],
+                                    gen.bf16_bits(swa[0]), swa_pos0[0], q_pos0[0])
+    check_close(got[0, 0].cpu().numpy(), r, "b0 q0")
+
+
+def test_paged_group_matches_contiguous(csa2):
+    """Full + 3 Reuse, then Reindex + 3 Reuse, at batch 4 (the decode group's
+    window tiles run in the select launch)."""
+    seed, B, stride, page = 53, 4, 20000, 1024
+    n_entries = [20000, 17000, 9000, 12345]
+    nib, sc, k8, ks = _contiguous(csa2, n_entries, stride, seed)
+    pools, pages, _ = _paginate(csa2, [nib, sc, k8, ks], n_entries, stride, page, seed)
+    kv_c = csa2.make_kv(nib, sc, k8, ks, stride)
+    kv_p = csa2.make_kv(*pools, 0, pages=pages)
+    q_pos0 = [n - 1 for n in n_entries]
+    swa_pos0 = [p - 127 for p in q_pos0]
+
+    def plan(kv, first):
+        ls = []
+        for j, m in enumerate([first] + [csa2.MODE_REUSE] * 3):
+            d = dict(mode=m, q=gen.attn_query((B, 1), seed + (first == csa2.MODE_REINDEX), j, device="cuda"),
+                     swa=gen.window_rows(B, 128, seed, j, device="cuda"))
+            if m != csa2.MODE_REUSE:
+                d["idx_q"] = gen.index_query((B, 1), seed + (first == csa2.MODE_REINDEX), j, device="cuda")
+            if m == csa2.MODE_FULL:
+                d["kv"] = kv
+            ls.append(d)
+        return ls
+
+    res = []
+    for kv in (kv_c, kv_p):
+        ws, st = csa2.Workspace(B, 1, stride), csa2.State(B, 1)
+        o1 = csa2.csa2_run_group(ws, st, plan(kv, csa2.MODE_FULL), q_pos0, n_entries, swa_pos0)
+        i1 = st.indices.clone()
+        o2 = csa2.csa2_run_group(ws, st, plan(kv, csa2.MODE_REINDEX), q_pos0, n_entries, swa_pos0)
+        torch.cuda.synchronize()
+        assert ws.fallbacks() == 0
+        res.append((o1, i1, o2, st.indices.clone()))
+    (a1, ai1, a2, ai2), (b1, bi1, b2, bi2) = res
+    assert torch.equal(ai1, bi1) and torch.equal(ai2, bi2)
+    for x, y in zip(a1 + a2, b1 + b2):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_paged_append_matches_contiguous(csa2, ratio):
+    """Decode steps appended into a paged pool leave every page holding the
+    bytes the contiguous cache holds for it (block keys stay per sequence)."""
+    seed, B, page, steps = 61 + ratio, 3, 128, 300
+    prefix = [0, 40, 200]
+    n_tok = [p + steps for p in prefix]
+    stride = max(n_tok) // ratio + 8
+    bst = (stride + 7) // 8
+    xs = [gen.latent(n, seed, seq=b, device="cuda") for b, n in enumerate(n_tok)]
+    kk = [gen.index_key(n, seed, seq=b, device="cuda") for b, n in enumerate(n_tok)]
+
+    def run(paged):
+        nib = torch.zeros((B * stride, 256), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros((B * stride, 32), dtype=torch.uint8, device="cuda")
+        k8 = torch.zeros((B * stride, 64), dtype=torch.uint8, device="cuda")
+        ks = torch.zeros((B * stride,), dtype=torch.float32, device="cuda")
+        bk8 = torch.zeros((B * bst, 64), dtype=torch.uint8, device="cuda")
+        bks = torch.zeros((B * bst,), dtype=torch.float32, device="cuda")
+        pend = torch.zeros((B, 576), dtype=torch.float32, device="cuda")
+        for b, p in enumerate(prefix):
+            if p:
+                e0, e1 = b * stride, b * stride + p // ratio
+                csa2.csa2_quantize_kv(xs[b][:p].contiguous(), ratio=ratio, k_in=kk[b][:p].contiguous(),
+                                      out=[nib[e0:e1], sc[e0:e1], k8[e0:e1], ks[e0:e1]])
+        csa2.csa2_build_block_keys(k8, ks, [p // ratio for p in prefix], stride, bk8, bks, bst)
+        arrays, pages, table = [nib, sc, k8, ks], None, None
+        if paged:
+            arrays, pages, table = _paginate(csa2, [nib, sc, k8, ks], [stride] * B, stride, page, seed)
+        for t in range(steps):
+            pos = [p + t for p in prefix]
+            x = torch.stack([xs[b][pos[b]] for b in range(B)]).contiguous()
+            k = torch.stack([kk[b][pos[b]] for b in range(B)]).contiguous()
+            csa2.csa2_append(x, k, pos, *arrays, stride if not paged else 0, ratio=ratio, bk8=bk8, bkscale=bks,
+                             bk_stride=bst, pending=pend, pages=pages)
+        torch.cuda.synchronize()
+        return arrays, table, bk8, bks
+
+    (cn, cs, ck, cks), _, cbk, cbks = run(False)
+    (pn, ps, pk, pks), table, pbk, pbks = run(True)
+    assert torch.equal(cbk, pbk) and torch.equal(cbks, pbks)
+    tab = table.cpu().numpy()
+    for b in range(B):
+        for j in range(tab.shape[1]):
+            lo, hi = j * page, min((j + 1) * page, stride)
+            if lo >= hi:
+                continue
+            pg = int(tab[b, j])
+            for c, p in ((cn, pn), (cs, ps), (ck, pk)):
+                assert torch.equal(c[b * stride + lo: b * stride + hi], p[pg * page: pg * page + hi - lo]), (b, j)
+            assert torch.equal(cks[b * stride + lo: b * stride + hi].view(torch.int32),
+                               pks[pg * page: pg * page + hi - lo].view(torch.int32)), (b, j)
