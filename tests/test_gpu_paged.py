@@ -206,3 +206,102 @@ def test_paged_append_matches_contiguous(csa2, ratio):
                 assert torch.equal(c[b * stride + lo: b * stride + hi], p[pg * page: pg * page + hi - lo]), (b, j)
             assert torch.equal(cks[b * stride + lo: b * stride + hi].view(torch.int32),
                                pks[pg * page: pg * page + hi - lo].view(torch.int32)), (b, j)
+
+
+def test_paged_decode_steps_match_oracle(csa2):
+    """Three decode steps on a paged pool with window rings, ratio 2: append
+    each new token (cache pages, window ring), then a Full + Reuse group; the
+    last step's indices and outputs match the oracle over the token history,
+    and equal those of the same steps on a contiguous cache."""
+    dev, B, ratio, page, ring, seed = "cuda", 2, 2, 128, 128, 83
+    prefix, steps = 5000, 4                      # even prefix: whole pairs
+    n_tok = prefix + steps
+    stride = n_tok // ratio + 8
+    xs = [gen.latent(n_tok, seed, seq=b, device=dev) for b in range(B)]
+    kk = [gen.index_key(n_tok, seed, seq=b, device=dev) for b in range(B)]
+
+    def run(paged):
+        nib = torch.zeros((B * stride, 256), dtype=torch.uint8, device=dev)
+        sc = torch.zeros((B * stride, 32), dtype=torch.uint8, device=dev)
+        k8 = torch.zeros((B * stride, 64), dtype=torch.uint8, device=dev)
+        ks = torch.zeros((B * stride,), dtype=torch.float32, device=dev)
+        pend = torch.zeros((B, 576), dtype=torch.float32, device=dev)
+        swa = [torch.zeros((B, ring, 512), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        for b in range(B):
+            e0 = b * stride
+            csa2.csa2_quantize_kv(xs[b][:prefix].contiguous(), ratio=ratio, k_in=kk[b][:prefix].contiguous(),
+                                  out=[nib[e0:e0 + prefix // ratio], sc[e0:e0 + prefix // ratio],
+                                       k8[e0:e0 + prefix // ratio], ks[e0:e0 + prefix // ratio]])
+            for L in range(2):
+                for tok in range(prefix - ring, prefix):
+                    swa[L][b, tok % ring] = xs[b][tok].to(torch.bfloat16)
+        arrays, pages = [nib, sc, k8, ks], None
+        if paged:
+            arrays, pages, _ = _paginate(csa2, arrays, [stride] * B, stride, page, seed)
+        kv = csa2.make_kv(*arrays, 0 if paged else stride, pages=pages)
+        ws, st = csa2.Workspace(B, 1, stride), csa2.State(B, 1)
+        for t in range(steps):
+            pos = prefix + t
+            x = torch.stack([xs[b][pos] for b in range(B)]).contiguous()
+            k = torch.stack([kk[b][pos] for b in range(B)]).contiguous()
+            for L in range(2):
+                csa2.csa2_append(x, k, [pos] * B, *arrays, 0 if paged else stride, ratio=ratio,
+                                 pending=pend if L == 0 else pend.clone(), swa=swa[L], swa_ring=ring, pages=pages)
+            layers = [dict(mode=csa2.MODE_FULL, q=gen.attn_query((B, 1), seed + t, 0, device=dev), swa=swa[0],
+                           idx_q=gen.index_query((B, 1), seed + t, 0, device=dev), kv=kv),
+                      dict(mode=csa2.MODE_REUSE, q=gen.attn_query((B, 1), seed + t, 1, device=dev), swa=swa[1])]
+            n_ent = (pos + 1) // ratio
+            outs = csa2.csa2_run_group(ws, st, layers, [pos] * B, [n_ent] * B, None, ratio=ratio, swa_ring=ring)
+        torch.cuda.synchronize()
+        assert ws.fallbacks() == 0
+        return outs, st.indices.clone(), layers
+
+    outs_c, idx_c, _ = run(False)
+    outs_p, idx_p, layers = run(True)
+    assert torch.equal(idx_c, idx_p)
+    for a, b in zip(outs_c, outs_p):
+        assert torch.equal(a, b)
+    pos = prefix + steps - 1
+    n_ent = (pos + 1) // ratio
+    idx = idx_p.cpu().numpy()
+    for b in range(B):
+        xh, kh = xs[b][:2 * n_ent].cpu().numpy(), kk[b][:2 * n_ent].cpu().numpy()
+        rn, rs, rk, rks = oracle.quantize_kv(xh, ratio, kh)
+        iq = layers[0]["idx_q"][b, 0].cpu().numpy()
+        ref = oracle.index_flat(iq, None, rk, rks, n_ent)
+        kind = check_topk(idx[b, 0], ref, oracle.scores(iq, None, rk, rks), 512, n_ent, f"seq {b}")
+        if kind != "exact":
+            continue
+        win = gen.bf16_bits(xs[b][pos - 127: pos + 1].to(torch.bfloat16))
+        for j, L in enumerate(layers):
+            r = oracle.sparse_swa_attention(gen.bf16_bits(L["q"][b, 0]), rn, rs, ref, win, pos - 127, pos)
+            check_close(outs_p[j][b, 0].cpu().numpy(), r, f"seq {b} layer {j}")
+
+
+def test_paged_multi_token_group_matches_contiguous(csa2):
+    """Four query tokens per sequence (shared scan, walk-form attention) on a
+    paged pool: Full + 3 Reuse equals the contiguous run."""
+    seed, B, n_q, stride, page = 97, 3, 4, 12000, 256
+    n_entries = [12000, 7000, 300]
+    nib, sc, k8, ks = _contiguous(csa2, n_entries, stride, seed)
+    pools, pages, _ = _paginate(csa2, [nib, sc, k8, ks], n_entries, stride, page, seed)
+    q_pos0 = [max(n - n_q, 0) for n in n_entries]
+    swa_pos0 = [max(p - 127, 0) for p in q_pos0]
+    res = []
+    for kv in (csa2.make_kv(nib, sc, k8, ks, stride), csa2.make_kv(*pools, 0, pages=pages)):
+        ls = []
+        for j, m in enumerate([csa2.MODE_FULL] + [csa2.MODE_REUSE] * 3):
+            d = dict(mode=m, q=gen.attn_query((B, n_q), seed, j, device="cuda"),
+                     swa=gen.window_rows(B, 127 + n_q, seed, j, device="cuda"))
+            if m == csa2.MODE_FULL:
+                d["idx_q"], d["kv"] = gen.index_query((B, n_q), seed, j, device="cuda"), kv
+            ls.append(d)
+        ws, st = csa2.Workspace(B, n_q, stride), csa2.State(B, n_q)
+        outs = csa2.csa2_run_group(ws, st, ls, q_pos0, n_entries, swa_pos0)
+        torch.cuda.synchronize()
+        assert ws.fallbacks() == 0
+        res.append((outs, st.indices.clone()))
+    (oc, ic), (op, ip) = res
+    assert torch.equal(ic, ip)
+    for a, b in zip(oc, op):
+        assert torch.equal(a, b)
