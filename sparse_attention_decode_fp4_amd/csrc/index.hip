@@ -462,9 +462,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
 // the hardware returns zeros past it and the loads need no bounds branches.
 // Otherwise positions come from a block or position list (one query per
 // workgroup).
-template <int U, bool kDirect, int NQ>
+template <int U, bool kDirect, int NQ, bool kPaged>
 __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, int n_groups) {
   static_assert(NQ == 1 || kDirect, "queries share a chunk only over direct items");
+  static_assert(!kPaged || kDirect, "paged caches are read over direct items");
   // workgroup (group of NQ queries of one sequence, chunk)
   int grp, chunk;
   map_row_chunk(n_groups, per_row, grp, chunk);
@@ -502,14 +503,14 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   // kStep items lies in one page (pages hold at least 128 entries, batches
   // start at multiples of kStep), so its entries are one page's consecutive
   // entries
-  const bool paged = kDirect && p.pm.pages != nullptr;
+  constexpr bool paged = kPaged;
   const uint32_t lim = paged ? (uint32_t)p.pm.pool : (uint32_t)end;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? p.k8 : kb), 0, (int)(lim * kDI), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? p.kscale : sb), 0, (int)(lim * 4), kRawBufferWord3);
   uint32_t page_lane = 0;
-  if (paged) {
+  if constexpr (paged) {
     const int64_t pg = (base >> p.pm.lg) + (threadIdx.x & 63);
     page_lane = __builtin_amdgcn_raw_buffer_load_b32(page_row(p.pm, seq), (int)(pg * 4), 0, 0);
   }
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   };
   auto load = [&](Batch& B, int64_t it0) {
     uint32_t page = 0;
-    if (paged) page = (uint32_t)__shfl((int)page_lane, (int)(((it0 >> p.pm.lg) - (base >> p.pm.lg)) & 63), 64);
+    if constexpr (paged) page = (uint32_t)__shfl((int)page_lane, (int)(((it0 >> p.pm.lg) - (base >> p.pm.lg)) & 63), 64);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t item = it0 + u * 64 + sub;
@@ -1011,14 +1012,21 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnP
   const int nqg = (p.source != kItemsDirect || p.n_q == 1) ? 1 : p.n_q == 2 ? 2 : 4;
   const int n_groups = p.rows / p.n_q * ((p.n_q + nqg - 1) / nqg);
   const dim3 sgrid((unsigned)(grid_rows(n_groups) * scan_per_row));
+  const bool paged = p.pm.pages != nullptr;  // (direct items only: the host refuses the others)
   if (p.source != kItemsDirect)
-    hipLaunchKernelGGL((k_index_scan<2, false, 1>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan<2, false, 1, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+  else if (nqg == 1 && paged)
+    hipLaunchKernelGGL((k_index_scan<2, true, 1, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 1)
-    hipLaunchKernelGGL((k_index_scan<2, true, 1>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan<2, true, 1, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+  else if (nqg == 2 && paged)
+    hipLaunchKernelGGL((k_index_scan<2, true, 2, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 2)
-    hipLaunchKernelGGL((k_index_scan<2, true, 2>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan<2, true, 2, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+  else if (paged)
+    hipLaunchKernelGGL((k_index_scan<1, true, 4, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else
-    hipLaunchKernelGGL((k_index_scan<1, true, 4>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan<1, true, 4, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   prof_end(h, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
