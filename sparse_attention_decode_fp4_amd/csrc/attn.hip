@@ -145,7 +145,6 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
   f32x4_t o[LG][8];            // O[4*g4+r][128*wave + 16*nt + l16]
 #pragma unroll
   for (int i = 0; i < LG; ++i) {
-    if (i < nl) load_q(p.layer[l0 + i].q, row, qb[i]);
     m_run[i] = -INFINITY;
     l_run[i] = 0.0f;
 #pragma unroll
@@ -159,6 +158,9 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
     fetch_entry(p, seq, tile_position(p, tile_begin, row), f);
     if (tile_begin + 1 <= last_sel) pos_next = tile_position(p, tile_begin + 1, row);
   }
+  // the queries, loaded once for the workgroup and staged through E (free
+  // again before the first tile goes in)
+  stage_q<LG>(p, l0, nl, row, s, qb);
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     if (tile > tile_begin) __syncthreads();  // the previous tile's readers of E are done
     if (tile <= last_sel) {
