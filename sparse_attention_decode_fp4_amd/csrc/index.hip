@@ -35,7 +35,7 @@ namespace csa2 {
 
 constexpr int kSample = 2048;       // sampled items per row (two per thread of the sample kernel)
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
-constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks gather in one round trip
+constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks (twice this at k > 1,024) gather in one round trip
 constexpr int kSpecSlots = 64;        // ... of the first this many slots of each segment
 
 // The row geometry below is all the kernels compute before their first
@@ -647,7 +647,9 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
   }
   const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
   const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
+  constexpr int kSpecCh = kPer <= 16 ? kSpecChunks : 2 * kSpecChunks;  // chunks gathered in one round trip
   const uint32_t cnt_lane = cnt_row[lane];
+  const uint32_t cnt_lane_b = kSpecCh > 64 ? cnt_row[lane + 64] : 0u;  // (every row has room for 128)
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
@@ -667,31 +669,39 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need, sh_binn;
 
-  // Rows of at most kSpecChunks chunks load the first kSpecSlots slots of
-  // every segment together with the counts (one memory round trip), two
-  // segments per wave instruction: wave w takes chunks 2 (w + 4 j) + lane / 32,
-  // lane % 32 their slots 2 (lane % 32) and the next.  Segments hold about 40
-  // candidates on average; fuller ones load the rest afterwards.  Each wave
-  // holds the count of chunk l in lane l, so its own prefix sum gives every
-  // chunk's start without a workgroup scan.
-  const bool spec = nch <= kSpecChunks;
-  uint4 sv[kSpecChunks / 8];
-  uint32_t spec_cnt = 0, spec_start = 0;
+  // Rows of at most kSpecCh chunks (64 for k <= 1,024, 128 for the 2,048-block
+  // stage) load the first kSpecSlots slots of every segment together with
+  // the counts (one memory round trip), two segments per wave instruction:
+  // wave w takes chunks 2 (w + 4 j) + lane / 32, lane % 32 their slots
+  // 2 (lane % 32) and the next.  Segments hold about 40 candidates on
+  // average; fuller ones load the rest afterwards.  Each wave holds the
+  // counts of chunks l and l + 64 in lane l, so its own prefix sums give
+  // every chunk's start without a workgroup scan.
+  const bool spec = nch <= kSpecCh;
+  uint4 sv[kSpecCh / 8];
+  uint32_t cnt_a = 0, cnt_b = 0, start_a = 0, start_b = 0;
   uint32_t total;
   bool over = false, more = false;
   if (spec) {
-    spec_cnt = lane < nch ? cnt_lane : 0u;
+    cnt_a = lane < nch ? cnt_lane : 0u;
+    cnt_b = lane + 64 < nch ? cnt_lane_b : 0u;
 #pragma unroll
-    for (int j = 0; j < kSpecChunks / 8; ++j) {
+    for (int j = 0; j < kSpecCh / 8; ++j) {
       const int ch = 2 * (wave + 4 * j) + (lane >> 5);
       sv[j] = ch < nch ? *reinterpret_cast<const uint4*>(segs + (int64_t)ch * kSeg + 2 * (lane & 31))
                        : make_uint4(0, 0, 0, 0);
     }
-    const uint32_t incl = wave_incl_add(spec_cnt);
-    spec_start = incl - spec_cnt;
-    total = (uint32_t)__shfl((int)incl, 63, 64);
-    over = __any(spec_cnt > (uint32_t)kSeg);
-    more = __any(spec_cnt > (uint32_t)kSpecSlots);
+    const uint32_t incl_a = wave_incl_add(cnt_a);
+    const uint32_t tot_a = (uint32_t)__shfl((int)incl_a, 63, 64);
+    start_a = incl_a - cnt_a;
+    total = tot_a;
+    if constexpr (kSpecCh > 64) {
+      const uint32_t incl_b = wave_incl_add(cnt_b);
+      start_b = tot_a + incl_b - cnt_b;
+      total = tot_a + (uint32_t)__shfl((int)incl_b, 63, 64);
+    }
+    over = __any(cnt_a > (uint32_t)kSeg || cnt_b > (uint32_t)kSeg);
+    more = __any(cnt_a > (uint32_t)kSpecSlots || cnt_b > (uint32_t)kSpecSlots);
   } else {
     // segment counts: thread t owns chunks 16t .. 16t+15
     uint32_t c[16], local = 0;
@@ -728,11 +738,23 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
       for (int i = t; i < kBitmapItems / 128; i += 256) bm4[i] = make_uint4(0, 0, 0, 0);
     }
     if (spec) {  // the slots loaded above: keep the first count of each chunk
+      // count and start of chunk ch (< 128; every lane takes both shuffles)
+      auto chunk_of = [&](int ch, uint32_t& n, uint32_t& base) {
+        const int l = ch & 63;
+        const uint32_t na = (uint32_t)__shfl((int)cnt_a, l, 64), sa = (uint32_t)__shfl((int)start_a, l, 64);
+        uint32_t nb = 0, sb = 0;
+        if constexpr (kSpecCh > 64) {
+          nb = (uint32_t)__shfl((int)cnt_b, l, 64);
+          sb = (uint32_t)__shfl((int)start_b, l, 64);
+        }
+        n = ch < 64 ? na : nb;
+        base = ch < 64 ? sa : sb;
+      };
 #pragma unroll
-      for (int j = 0; j < kSpecChunks / 8; ++j) {
+      for (int j = 0; j < kSpecCh / 8; ++j) {
         const int ch = 2 * (wave + 4 * j) + (lane >> 5);
-        const uint32_t n = (uint32_t)__shfl((int)spec_cnt, ch, 64);
-        const uint32_t base = (uint32_t)__shfl((int)spec_start, ch, 64);
+        uint32_t n, base;
+        chunk_of(ch, n, base);
         const uint32_t s0 = 2u * (lane & 31);
         if (ch < nch) {
           if (s0 < n) lc[base + s0] = ((uint64_t)sv[j].y << 32) | sv[j].x;
@@ -741,8 +763,8 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
       }
       if (more) {  // the slots past kSpecSlots of fuller segments
         for (int ch = wave; ch < nch; ch += 4) {
-          const uint32_t n = (uint32_t)__shfl((int)spec_cnt, ch, 64);
-          const uint32_t base = (uint32_t)__shfl((int)spec_start, ch, 64);
+          uint32_t n, base;
+          chunk_of(ch, n, base);
           const uint32_t i = kSpecSlots + lane;
           if (i < n) lc[base + i] = segs[(int64_t)ch * kSeg + i];
         }
