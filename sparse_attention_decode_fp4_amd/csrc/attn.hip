@@ -211,13 +211,35 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
 // every XCD, which in-kernel device-scope fences would do by writing back
 // the whole L2.  Workgroup (unit, channel quarter): thread t sums channel
 // 128 quarter + t / 2, heads 8 (t % 2) .. +8 (16 contiguous bytes of each
-// partial), with per-head weights l_s exp2(m_s - M) / L that 16 threads work
-// out in LDS from the (m, l) of every split, loaded in one round trip while
-// the partial loads of up to 16 splits are in flight.
+// partial), with per-head weights l_s exp2(m_s - M) / L from the (m, l) of
+// every split.  The (m, l) loads go out first and the partial loads of up to
+// 16 splits behind them, so the weights are worked out while the partials
+// are in flight.
 constexpr int kMaxMergeSplits = 64;
 constexpr int kMergeBatch = 16;
-__global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
-  const int unit = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+// Workgroups run on the XCD that wrote the unit's partials (their lines are
+// still in its L2): kMergeByRow, the tile form with 8 or more rows (row r's
+// tiles on XCD r mod 8); kMergeByUnit, the walk form with 8 or more units
+// (unit u's splits on XCD u mod 8); kMergeLinear otherwise.
+enum MergeMap : int32_t { kMergeLinear = 0, kMergeByRow = 1, kMergeByUnit = 2 };
+__global__ __launch_bounds__(256) void k_attention_merge(AttnPass p, int32_t map) {
+  int unit, quarter;
+  if (map == kMergeLinear) {
+    unit = blockIdx.x >> 2;
+    quarter = blockIdx.x & 3;
+  } else {
+    const int xcd = blockIdx.x & (kXcds - 1), w = blockIdx.x >> 3, k = w >> 2;
+    quarter = w & 3;
+    if (map == kMergeByRow) {
+      const int rpx = (p.rows + kXcds - 1) / kXcds;  // rows per XCD, at most
+      const int layer = k / rpx, row = xcd + kXcds * (k % rpx);
+      if (layer >= p.n_layers || row >= p.rows) return;
+      unit = layer * p.rows + row;
+    } else {
+      unit = xcd + kXcds * k;
+      if (unit >= p.n_layers * p.rows) return;
+    }
+  }
   const int layer = unit / p.rows, row = unit - layer * p.rows;
   const int t = threadIdx.x;
   const int ch = 128 * quarter + (t >> 1), h0 = 8 * (t & 1);
@@ -225,49 +247,93 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p) {
   const float* pb = p.partial + (int64_t)unit * ns * kPartFloats;
   __shared__ float wgt[kMaxMergeSplits][kH];
   __shared__ float lsh[kMaxMergeSplits][kH];
+  // every load is an unconditional buffer load over the unit's partials: a
+  // split past the last reads zeros without touching memory, so no branch
+  // holds a load back
+  const __amdgpu_buffer_rsrc_t rp =
+      __builtin_amdgcn_make_buffer_rsrc((void*)pb, 0, ns * kPartFloats * 4, kRawBufferWord3);
+  // (split, head) (i / 16, i % 16) for i = t + 256 j: its m and l
+  constexpr int kMl = kMaxMergeSplits * kH / 256;
+  float mv[kMl], lv[kMl];
+#pragma unroll
+  for (int j = 0; j < kMl; ++j) {
+    const int i = t + 256 * j;
+    const int off = ((i / kH) * kPartFloats + kPartOWords + i % kH) * 4;
+    mv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 0));
+    lv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off + kH * 4, 0, 0));
+  }
+  u32x4_t v[kMergeBatch];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rp, (s0 + u) * kPartFloats * 4 + (ch * kH + h0) * 2, 0, 0);
+  };
   float acc[8];
 #pragma unroll
   for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
-    uint4 v[kMergeBatch];
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = s0 + u < ns ? s0 + u : ns - 1;
-      const uint16_t* ps = reinterpret_cast<const uint16_t*>(pb + (int64_t)s * kPartFloats) + ch * kH + h0;
-      v[u] = *reinterpret_cast<const uint4*>(ps);
-    }
-    if (s0 == 0) {
-      for (int i = t; i < ns * kH; i += 256) {  // (split, head) = (i / 16, i % 16)
-        const float* ps = pb + (int64_t)(i / kH) * kPartFloats + kPartOWords;
-        wgt[i / kH][i % kH] = ps[i % kH];
-        lsh[i / kH][i % kH] = ps[kH + i % kH];
-      }
-      __syncthreads();
-      if (t < kH) {  // head t
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, wgt[s][t]);
-        float L = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-          const float m = wgt[s][t];
-          const float w = m == -INFINITY ? 0.0f : exp2f(m - M) * lsh[s][t];
-          wgt[s][t] = w;
-          L += w;
-        }
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        for (int s = 0; s < ns; ++s) wgt[s][t] *= inv;
-      }
-      __syncthreads();
-    }
+  auto accumulate = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       if (s0 + u >= ns) break;
-      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const uint32_t wd[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
 #pragma unroll
       for (int h = 0; h < 8; ++h) {
         const half2_t pr = __builtin_bit_cast(half2_t, wd[h >> 1]);
         acc[h] += wgt[s0 + u][h0 + h] * (float)pr[h & 1];
       }
     }
+  };
+  load_batch(0);
+  if (ns <= 256 / kH) {
+    // thread t is (split t / 16, head t % 16), its m and l in mv[0], lv[0]:
+    // the per-head max and sum over the splits are shuffles across the
+    // wave's four splits and an LDS exchange between the waves
+    __shared__ float red_m[4][kH], red_l[4][kH];
+    const int lane = t & 63, wave = t >> 6, s_t = t / kH, h_t = t % kH;
+    const bool live = s_t < ns;
+    const float m = live ? mv[0] : -INFINITY;
+    float M = fmaxf(m, __shfl_xor(m, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    if (lane < kH) red_m[wave][lane] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red_m[0][h_t], red_m[1][h_t]), fmaxf(red_m[2][h_t], red_m[3][h_t]));
+    const float w = m == -INFINITY ? 0.0f : exp2f(m - M) * lv[0];
+    float L = w + __shfl_xor(w, 16, 64);
+    L += __shfl_xor(L, 32, 64);
+    if (lane < kH) red_l[wave][lane] = L;
+    __syncthreads();
+    L = (red_l[0][h_t] + red_l[1][h_t]) + (red_l[2][h_t] + red_l[3][h_t]);
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if (live) wgt[s_t][h_t] = w * inv;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMl; ++j) {
+      const int i = t + 256 * j;
+      if (i < ns * kH) {
+        wgt[i / kH][i % kH] = mv[j];
+        lsh[i / kH][i % kH] = lv[j];
+      }
+    }
+    __syncthreads();
+    if (t < kH) {  // head t
+      float M = -INFINITY;
+      for (int s = 0; s < ns; ++s) M = fmaxf(M, wgt[s][t]);
+      float L = 0.0f;
+      for (int s = 0; s < ns; ++s) {
+        const float m = wgt[s][t];
+        const float w = m == -INFINITY ? 0.0f : exp2f(m - M) * lsh[s][t];
+        wgt[s][t] = w;
+        L += w;
+      }
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      for (int s = 0; s < ns; ++s) wgt[s][t] *= inv;
+    }
+  }
+  __syncthreads();
+  accumulate(0);
+  for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
+    load_batch(s0);
+    accumulate(s0);
   }
   float* dst = p.layer[layer].out + ((int64_t)row * kH + h0) * kD + ch;
 #pragma unroll
@@ -285,7 +351,7 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   const int gu = wunits >= kXcds ? (wunits + kXcds - 1) / kXcds * kXcds : wunits;
   int h = prof_begin(CSA2_K_ATTENTION, stream);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
-  if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles) {
+  if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles) {  // (the tile form)
     // one tile per workgroup: selected-entry tiles are shared by the layers
     // layer groups of two: gathering a tile twice is cheap next to running
     // four layers one after another in one workgroup
@@ -302,7 +368,12 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   if (e != hipSuccess || p.max_splits == 1) return e;
   if (p.max_splits > kMaxMergeSplits) return hipErrorInvalidValue;
   h = prof_begin(CSA2_K_ATTENTION_MERGE, stream);
-  hipLaunchKernelGGL(k_attention_merge, dim3((unsigned)(4 * units)), dim3(256), 0, stream, p);
+  const bool tiles = p.tiles_per_split == 1 && p.max_splits == p.n_tiles;
+  const int32_t map = tiles ? (p.rows >= kXcds ? kMergeByRow : kMergeLinear) : (units >= kXcds ? kMergeByUnit : kMergeLinear);
+  const int mgrid = map == kMergeByRow ? kXcds * 4 * p.n_layers * ((p.rows + kXcds - 1) / kXcds)
+                    : map == kMergeByUnit ? kXcds * 4 * ((units + kXcds - 1) / kXcds)
+                                          : 4 * units;
+  hipLaunchKernelGGL(k_attention_merge, dim3((unsigned)mgrid), dim3(256), 0, stream, p, map);
   prof_end(h, stream);
   return hipGetLastError();
 }

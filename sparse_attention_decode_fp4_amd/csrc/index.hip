@@ -956,21 +956,48 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
     __syncthreads();
   }
 
-  // positions of the winners, in ascending order
-  for (uint32_t j = t; j < n_win; j += 256) p.out[(int64_t)row * p.out_stride + j] = item_to_position(p, row, win[j]);
-  if (!p.block_level) {
-    for (uint32_t j = n_win + t; j < k; j += 256) p.out[(int64_t)row * p.out_stride + j] = -1;
+  // positions of the winners, in ascending order (then -1 up to k, except
+  // for block ids); rows that start on 16 bytes take four per store
+  int32_t* orow = p.out + (int64_t)row * p.out_stride;
+  const uint32_t n_out = p.block_level ? n_win : k;
+  if ((reinterpret_cast<uintptr_t>(orow) & 15u) == 0) {
+    for (uint32_t j = 4 * t; j < n_out; j += 1024) {
+      int32_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = j + e < n_win ? item_to_position(p, row, win[j + e]) : -1;
+      if (j + 4 <= n_out) {
+        *reinterpret_cast<int4*>(orow + j) = make_int4(v[0], v[1], v[2], v[3]);
+      } else {
+        for (uint32_t e = 0; j + e < n_out; ++e) orow[j + e] = v[e];
+      }
+    }
+  } else {
+    for (uint32_t j = t; j < n_out; j += 256) orow[j] = j < n_win ? item_to_position(p, row, win[j]) : -1;
   }
   if (p.out_count && t == 0) p.out_count[row] = (int32_t)n_win;
   if (p.out_pool) {
-    const int32_t total_pool = CSA2_N_BLOCKS * CSA2_BLOCK;
-    for (int32_t j = t; j < p.pool_stride && j < total_pool; j += 256) {
-      int32_t v = -1;
-      if ((uint32_t)(j >> 3) < n_win) {
-        const int64_t pos = 8 * (int64_t)win[j >> 3] + (j & 7);
-        if (pos < vis) v = (int32_t)pos;
+    // the 8 positions of kept block b (-1 past the visible ones or past the
+    // kept blocks) at 8 b .. 8 b + 7: two 16-byte stores per block when the
+    // row starts on 16 bytes
+    const int32_t n_pool = min(p.pool_stride, (int32_t)kMaxPool);
+    int32_t* prow = p.out_pool + (int64_t)row * p.pool_stride;
+    auto pool_at = [&](int32_t j) -> int32_t {
+      if ((uint32_t)(j >> 3) >= n_win) return -1;
+      const int64_t pos = 8 * (int64_t)win[j >> 3] + (j & 7);
+      return pos < vis ? (int32_t)pos : -1;
+    };
+    if ((reinterpret_cast<uintptr_t>(prow) & 15u) == 0 && (n_pool & 7) == 0) {
+      for (int32_t b = t; b < n_pool / 8; b += 256) {
+        const int64_t base = (uint32_t)b < n_win ? 8 * (int64_t)win[b] : vis;
+        int32_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = base + e < vis ? (int32_t)(base + e) : -1;
+        int4* d = reinterpret_cast<int4*>(prow + 8 * b);
+        d[0] = make_int4(v[0], v[1], v[2], v[3]);
+        d[1] = make_int4(v[4], v[5], v[6], v[7]);
       }
-      p.out_pool[(int64_t)row * p.pool_stride + j] = v;
+    } else {
+      for (int32_t j = t; j < n_pool; j += 256) prow[j] = pool_at(j);
     }
   }
 }
@@ -994,7 +1021,19 @@ __global__ __launch_bounds__(256) void k_index_select_window(IndexPass p, AttnPa
   __shared__ __attribute__((aligned(16))) TileLds s;
   const int n_win_tiles = a.n_tiles - (a.n_idx + kAttnSplit - 1) / kAttnSplit;
   const int per_row = a.n_layers * n_win_tiles;
-  const int w = blockIdx.x - p.rows, row = w / per_row, jj = w - row * per_row;
+  // with a multiple of 8 rows, the tiles of row r run on XCD r mod 8 (the
+  // XCD of its selected-entry tiles), so the merge finds every partial of
+  // the row in one L2
+  const int w = blockIdx.x - p.rows;
+  int row, jj;
+  if (p.rows >= kXcds && p.rows % kXcds == 0) {
+    const int xcd = w & (kXcds - 1), k = w >> 3;
+    row = xcd + kXcds * (k / per_row);
+    jj = k % per_row;
+  } else {
+    row = w / per_row;
+    jj = w - row * per_row;
+  }
   window_tile(a, row, jj / n_win_tiles, jj % n_win_tiles, s);
 }
 
