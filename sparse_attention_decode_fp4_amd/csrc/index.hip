@@ -632,17 +632,20 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
   const int t = threadIdx.x, quarter = t & 3;
   const int wave = t >> 6, lane = t & 63;
   // the loads that need only the row go out first: the row's candidate
-  // histogram (filled by the scan; thread t: bins 8t..8t+7) and the counts
-  // of chunks 0..63 (every row has room for them; chunks past the row's
-  // last are masked below)
-  uint32_t hb[8];
+  // histogram (filled by the scan; every wave holds all of it, lane l the
+  // words 16 l .. 16 l + 15, bins 32 l .. 32 l + 31) and the chunk counts
+  // (every row has room for 128; chunks past the row's last are masked
+  // below)
+  uint32_t hw[16];
   {
-    const uint4 a = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistWords)[t];
-    const uint32_t wd[4] = {a.x, a.y, a.z, a.w};
+    const uint4* h4 = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistWords) + 4 * lane;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      hb[2 * i] = wd[i] & 0xFFFFu;
-      hb[2 * i + 1] = wd[i] >> 16;
+      const uint4 a = h4[i];
+      hw[4 * i] = a.x;
+      hw[4 * i + 1] = a.y;
+      hw[4 * i + 2] = a.z;
+      hw[4 * i + 3] = a.w;
     }
   }
   const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
@@ -666,6 +669,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t sh3[3];
   __shared__ uint64_t bin_keys[64];
+  __shared__ uint32_t hsrc[4][16];
   __shared__ uint64_t sh_kth;
   __shared__ uint32_t sh_need, sh_binn;
 
@@ -797,11 +801,14 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
     }
     __syncthreads();
     // candidates into registers: thread t holds lc[t + 256 i]
+    // (the passes over the keys stop after the last slot any thread fills:
+    // a row has about 1.5 k candidates in 256 kPer slots)
+    const int nslots = (int)((total + 255u) / 256u);
     uint64_t key[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const uint32_t g = t + 256 * i;
-      key[i] = g < total ? lc[g] : 0ull;  // 0 is below every candidate key
+      key[i] = i < nslots && g < total ? lc[g] : 0ull;  // 0 is below every candidate key
     }
     uint64_t kth = 1ull;
     if (total > k) {
@@ -809,51 +816,79 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
       // it hold fewer than k keys, with it at least k.  When it is a proper
       // bin with a few keys, the k-th key is ranked among those alone;
       // otherwise (the top bin, which also takes scores far above T0) the
-      // radix over every candidate decides.
+      // radix over every candidate decides.  Every wave finds the bin in its
+      // own copy of the histogram and ranks the bin's keys itself, so the
+      // only barrier is the one that publishes those keys.
       uint32_t hl = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) hl += hb[j];
-      uint32_t htot;
-      const uint32_t hincl = block_incl_scan_256(hl, wsum, htot);
-      uint32_t above = htot - hincl;  // keys in bins above 8t + 7
-      if (htot == total && above < k && above + hl >= k) {
-        for (int j = 7; j >= 0; --j) {
-          if (above + hb[j] >= k) { sh3[0] = 8 * t + j; sh3[1] = k - above; sh3[2] = hb[j]; break; }
-          above += hb[j];
+      for (int j = 0; j < 16; ++j) hl += (hw[j] & 0xFFFFu) + (hw[j] >> 16);
+      const uint32_t hincl = wave_incl_add(hl);
+      const uint32_t htot = (uint32_t)__builtin_amdgcn_readlane((int)hincl, 63);
+      const uint32_t above_l = htot - hincl;  // keys in bins above 32 lane + 31
+      // the lane whose 32 bins hold the k-th key, then (its words through
+      // LDS, one bin per lane) the bin
+      const unsigned long long hit = __ballot(htot == total && above_l < k && above_l + hl >= k);
+      uint32_t kb_bin = 0xFFFFFFFFu, need = 0, in_bin = 0;
+      if (hit) {
+        const int src = __ffsll((long long)hit) - 1;
+        const uint32_t above_src = (uint32_t)__builtin_amdgcn_readlane((int)above_l, src);
+        if (lane == src) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) hsrc[wave][i] = hw[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t wj = hsrc[wave][(lane & 31) >> 1];
+        const uint32_t c = lane < 32 ? (wj >> (16 * (lane & 1))) & 0xFFFFu : 0u;
+        const uint32_t ci = wave_incl_add(c);
+        const uint32_t above_j = above_src + (uint32_t)__builtin_amdgcn_readlane((int)ci, 31) - ci;
+        const unsigned long long hj = __ballot(lane < 32 && above_j < k && above_j + c >= k);
+        if (hj) {
+          const int j = __ffsll((long long)hj) - 1;
+          kb_bin = 32 * src + j;
+          need = k - (uint32_t)__builtin_amdgcn_readlane((int)above_j, j);
+          in_bin = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
         }
       }
-      __syncthreads();
-      const uint32_t kb_bin = sh3[0], need = sh3[1], in_bin = sh3[2];
+      bool ranked = false;
       if (kb_bin < (uint32_t)(kHistBins - 1) && in_bin <= 64u) {
-        // the bin's keys into LDS, then key j's rank among them
+        // the bin's keys into LDS, then lane l ranks key l among them with
+        // register reads of the other lanes' keys
         const uint32_t t0key = score_key(T0);
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
-          if (key[i] != 0ull && hist_bin((uint32_t)(key[i] >> 32), t0key) == kb_bin) {
+        for (int i = 0; i < kPer; ++i) {
+          if (i < nslots && key[i] != 0ull && hist_bin((uint32_t)(key[i] >> 32), t0key) == kb_bin) {
             const uint32_t slot = atomicAdd(&sh_binn, 1u);
             if (slot < 64u) bin_keys[slot] = key[i];
           }
-        __syncthreads();
-        if (t < (int)in_bin) {
-          const uint64_t mine = bin_keys[t];
-          uint32_t rank = 0;
-          for (uint32_t j = 0; j < in_bin; ++j) rank += bin_keys[j] > mine ? 1u : 0u;
-          if (rank == need - 1) sh_kth = mine;
         }
         __syncthreads();
-        kth = sh_kth;
-      } else {
-        kth = block_kth_regs<kPer>(key, k, h2048, wsum, sh3);
+        const uint64_t mine = lane < (int)in_bin ? bin_keys[lane] : 0ull;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < in_bin; ++j) {
+          const uint64_t other = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), (int)j) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, (int)j);
+          rank += other > mine ? 1u : 0u;
+        }
+        // (keys are unique: one lane holds rank need - 1; the same in every wave)
+        const unsigned long long pick = __ballot(lane < (int)in_bin && rank == need - 1);
+        if (pick) {
+          const int src = __ffsll((long long)pick) - 1;
+          kth = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), src) << 32) |
+                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, src);
+          ranked = true;
+        }
       }
+      if (!ranked) kth = block_kth_regs<kPer>(key, k, h2048, wsum, sh3);
     }
     // winners: every candidate key >= kth
     if (use_bitmap) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (key[i] >= kth) {
+      for (int i = 0; i < kPer; ++i) {
+        if (i < nslots && key[i] >= kth) {
           const uint32_t it = select_key_pos(key[i]);
           atomicOr(&bitmap[bitmap_slot(it >> 5)], 1u << (it & 31u));
         }
+      }
       __syncthreads();
       // thread t owns words 16t .. 16t+15 (512 items)
       const uint32_t nwords = (uint32_t)((n_items + 31) / 32);
@@ -879,19 +914,21 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
       }
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (key[i] >= kth) {
+      for (int i = 0; i < kPer; ++i) {
+        if (i < nslots && key[i] >= kth) {
           const uint32_t it = select_key_pos(key[i]), ws = bitmap_slot(it >> 5);
           win[wpre[ws] + __builtin_popcount(bitmap[ws] & ((1u << (it & 31u)) - 1u))] = it;
         }
+      }
       __syncthreads();
     } else {
       // compaction, then a bitonic sort padded to a power of two
       if (t == 0) sh_need = 0;
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (key[i] >= kth) win[atomicAdd(&sh_need, 1u)] = select_key_pos(key[i]);
+      for (int i = 0; i < kPer; ++i) {
+        if (i < nslots && key[i] >= kth) win[atomicAdd(&sh_need, 1u)] = select_key_pos(key[i]);
+      }
       __syncthreads();
       n_win = sh_need;
       uint32_t n2 = 1;
