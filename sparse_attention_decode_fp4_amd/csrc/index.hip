@@ -611,6 +611,173 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   }
 }
 
+// The scan on fp8 MFMA (direct items): each 32-key tile of the chunk is
+// scored against the 4 NQ heads of the NQ queries in one
+// v_mfma_scale_f32_32x32x64_f8f6f4 (heads as A rows, keys as B columns,
+// exact fp8 codes, unit scales, binary32 accumulation) instead of 16 fdot2
+// per key quarter and query on VALU.  Lane (l32, half) holds bytes
+// 32 half .. +32 of key l32 of the tile (B) and of head row l32 (A): row
+// 4 i + h is head h of query i.  The output gives the four head dots of query
+// i for key l32 in the lanes of half i % 2, registers 4 (i / 2) .. +3, so a
+// lane scores queries half, half + 2, ...  Wave w takes tiles w, w + 4, ...
+// of the chunk with kScanTiles tiles in flight.
+constexpr int kScanTiles = 4;
+template <int NQ, bool kPaged>
+__global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_row, int n_groups) {
+  constexpr int NG = (NQ + 1) / 2;  // queries per lane, at most
+  int grp, chunk;
+  map_row_chunk(n_groups, per_row, grp, chunk);
+  if (grp >= n_groups) return;
+  const int qgroups = (p.n_q + NQ - 1) / NQ;
+  const int seq = grp / qgroups;
+  const int row0 = seq * p.n_q + (grp - seq * qgroups) * NQ;
+  const int nq = p.n_q - (row0 - seq * p.n_q) < NQ ? p.n_q - (row0 - seq * p.n_q) : NQ;
+  const int64_t csize = row_chunk_items_of<true>(p, row0);  // shared by the rows of a sequence
+  const int64_t base = (int64_t)chunk * csize;
+  int64_t lim_q[NQ], end = 0;  // items of query i in this chunk end at lim_q[i]
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int64_t n = i < nq ? row_items_of<true>(p, row0 + i, row_vis_positions(p, row0 + i)) : 0;
+    lim_q[i] = base + csize < n ? base + csize : n;
+    end = lim_q[i] > end ? lim_q[i] : end;
+  }
+  if (base >= end) return;
+
+  __shared__ uint32_t n_hit[NQ];
+  __shared__ uint64_t hits[NQ][kSeg];
+  if (threadIdx.x < NQ) n_hit[threadIdx.x] = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
+  const float* sb = p.kscale + (int64_t)seq * p.k_stride;
+  const uint32_t lim = kPaged ? (uint32_t)p.pm.pool : (uint32_t)end;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kPaged ? p.k8 : kb), 0, (int)(lim * kDI), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kPaged ? p.kscale : sb), 0, (int)(lim * 4), kRawBufferWord3);
+  // paged: lane j holds the table value of the chunk's page j (a tile lies
+  // in one page: pages hold at least 128 entries, tiles start at multiples
+  // of 32)
+  uint32_t page_lane = 0;
+  if constexpr (kPaged) {
+    const int64_t pg = (base >> p.pm.lg) + lane;
+    page_lane = __builtin_amdgcn_raw_buffer_load_b32(page_row(p.pm, seq), (int)(pg * 4), 0, 0);
+  }
+  const int n_tiles = (int)((end - base + 31) >> 5);
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) >> 2 : 0;
+
+  struct Tile {
+    u32x4_t lo, hi;
+    float ks;
+  };
+  // tile m of this wave; past the chunk the loads read zeros without
+  // touching memory (the descriptors end at the chunk, or at the pool)
+  auto load_tile = [&](Tile& T, int m) {
+    const int64_t item = base + 32 * (int64_t)(wave + 4 * m) + l32;
+    uint32_t e;
+    if constexpr (kPaged) {
+      const uint32_t page = (uint32_t)__shfl((int)page_lane, (int)(((item >> p.pm.lg) - (base >> p.pm.lg)) & 63), 64);
+      e = item < end ? paged_entry(p.pm, page, item) : lim;
+    } else {
+      e = item < end ? (uint32_t)item : lim;
+    }
+    T.lo = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half, 0, kLoadNonTemporal);
+    T.hi = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half + 16, 0, kLoadNonTemporal);
+    T.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
+  };
+  // A operand: head row l32 of query l32 / 4 (rows past the group's queries
+  // read zeros past the descriptor).  These loads, the weights and the
+  // thresholds go out before the tiles: every load is unconditional, so the
+  // waits for them inside the tile loop do not wait for tile data.
+  v8i_t A;
+  {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.idx_q + (int64_t)row0 * kHI * kDI), 0, nq * kHI * kDI, kRawBufferWord3);
+    const int off = l32 < 4 * NQ ? (l32 >> 2) * kHI * kDI + (l32 & 3) * kDI + 32 * half : NQ * kHI * kDI;
+    const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+    A = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+  // this lane's queries i = 2 g + half: head weights, threshold, item limit
+  float wq[NG][kHI], t0q[NG];
+  int64_t limq[NG];
+  float T0[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) T0[i] = load_thresh(p, row0 + (i < nq ? i : 0));
+  {
+    const bool has_w = p.idx_w != nullptr;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(has_w ? p.idx_w + (int64_t)row0 * kHI : p.thresh), 0, has_w ? nq * kHI * 4 : 0, kRawBufferWord3);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int i = 2 * g + half;
+#pragma unroll
+      for (int h = 0; h < kHI; ++h) {
+        const float wl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (i * kHI + h) * 4, 0, 0));
+        wq[g][h] = has_w ? wl : 1.0f;
+      }
+    }
+  }
+  Tile T[kScanTiles];
+#pragma unroll
+  for (int s = 0; s < kScanTiles; ++s) load_tile(T[s], s);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) T0[i] = i < nq ? T0[i] : INFINITY;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int ilo = 2 * g, ihi = 2 * g + 1 < NQ ? 2 * g + 1 : 2 * g;
+    t0q[g] = half ? (2 * g + 1 < NQ ? T0[ihi] : INFINITY) : T0[ilo];
+    limq[g] = half ? (2 * g + 1 < NQ ? lim_q[ihi] : 0) : lim_q[ilo];
+  }
+  __syncthreads();  // n_hit is initialised
+
+  auto score_tile = [&](const Tile& Tt, int m) {
+    const v8i_t Bop = v8i_t{(int)Tt.lo[0], (int)Tt.lo[1], (int)Tt.lo[2], (int)Tt.lo[3],
+                            (int)Tt.hi[0], (int)Tt.hi[1], (int)Tt.hi[2], (int)Tt.hi[3]};
+    v16f_t acc = {};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 0, 0, 0, kMfmaUnitScales, 0,
+                                                          kMfmaUnitScales);
+    // the whole wave runs the MFMA (uniform control flow, see the sample)
+    asm volatile("" ::"v"(acc));
+    const int64_t item = base + 32 * (int64_t)(wave + 4 * m) + l32;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const float sc = Tt.ks * (wq[g][0] * fmaxf(acc[4 * g], 0.0f) + wq[g][1] * fmaxf(acc[4 * g + 1], 0.0f) +
+                                wq[g][2] * fmaxf(acc[4 * g + 2], 0.0f) + wq[g][3] * fmaxf(acc[4 * g + 3], 0.0f));
+      if (item < limq[g] && sc >= t0q[g]) {
+        const int i = 2 * g + half;
+        const uint32_t at = atomicAdd(&n_hit[i], 1u);
+        if (at < (uint32_t)kSeg) hits[i][at] = select_key(score_key(sc), (uint32_t)item);
+      }
+    }
+  };
+  // whole groups of kScanTiles tiles, with no branch between the loads (a
+  // tile past the chunk reads zeros and its items fail the item limit), so
+  // each score waits only for its own tile
+  for (int m0 = 0; m0 < my_tiles; m0 += kScanTiles) {
+#pragma unroll
+    for (int s = 0; s < kScanTiles; ++s) {
+      score_tile(T[s], m0 + s);
+      load_tile(T[s], m0 + s + kScanTiles);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    if (i >= nq || base >= lim_q[i]) continue;
+    const int64_t r = row0 + i;
+    uint64_t* seg = p.seg_list + (r * p.max_chunks + chunk) * kSeg;
+    const uint32_t n = n_hit[i] < (uint32_t)kSeg ? n_hit[i] : (uint32_t)kSeg;
+    if (threadIdx.x < n) {
+      const uint64_t h = hits[i][threadIdx.x];
+      seg[threadIdx.x] = h;
+      const uint32_t b = hist_bin((uint32_t)(h >> 32), score_key(T0[i]));
+      atomicAdd(&p.hist[r * kHistWords + (b >> 1)], 1u << (16 * (b & 1u)));
+    }
+    if (threadIdx.x == 0) p.seg_count[r * p.max_chunks + chunk] = n_hit[i];
+  }
+}
+
 // ------------------------------------------------------------------ select
 __device__ __forceinline__ int32_t item_to_position(const IndexPass& p, int row, uint32_t item) {
   if (p.source == kItemsDirect) return (int32_t)item;
@@ -1118,13 +1285,13 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnP
   else if (nqg == 1)
     hipLaunchKernelGGL((k_index_scan<2, true, 1, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 2 && paged)
-    hipLaunchKernelGGL((k_index_scan<2, true, 2, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan_mfma<2, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 2)
-    hipLaunchKernelGGL((k_index_scan<2, true, 2, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan_mfma<2, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (paged)
-    hipLaunchKernelGGL((k_index_scan<1, true, 4, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan_mfma<4, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else
-    hipLaunchKernelGGL((k_index_scan<1, true, 4, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan_mfma<4, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   prof_end(h, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
