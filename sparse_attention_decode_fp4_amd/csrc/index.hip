@@ -611,6 +611,13 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   }
 }
 
+// A pointer every lane holds the same value of, moved to scalar registers.
+__device__ __forceinline__ void* uniform_ptr(const void* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
 // The scan on fp8 MFMA (direct items): each 32-key tile of the chunk is
 // scored against the 4 NQ heads of the NQ queries in one
 // v_mfma_scale_f32_32x32x64_f8f6f4 (heads as A rows, keys as B columns,
@@ -650,11 +657,14 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
   const int l32 = lane & 31, half = lane >> 5;
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
-  const uint32_t lim = kPaged ? (uint32_t)p.pm.pool : (uint32_t)end;
+  // (the descriptors' fields are read through readfirstlane: they are
+  // uniform, and a descriptor the compiler cannot prove uniform costs a
+  // waterfall loop around every load)
+  const uint32_t lim = (uint32_t)__builtin_amdgcn_readfirstlane((int)(kPaged ? (uint32_t)p.pm.pool : (uint32_t)end));
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(kPaged ? p.k8 : kb), 0, (int)(lim * kDI), kRawBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kPaged ? p.k8 : kb), 0, (int)(lim * kDI), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(kPaged ? p.kscale : sb), 0, (int)(lim * 4), kRawBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kPaged ? p.kscale : sb), 0, (int)(lim * 4), kRawBufferWord3);
   // paged: lane j holds the table value of the chunk's page j (a tile lies
   // in one page: pages hold at least 128 entries, tiles start at multiples
   // of 32)
@@ -681,9 +691,10 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
     } else {
       e = item < end ? (uint32_t)item : lim;
     }
+    // (the scale first: the wait for the key bytes then covers it too)
+    T.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
     T.lo = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half, 0, kLoadNonTemporal);
     T.hi = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half + 16, 0, kLoadNonTemporal);
-    T.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
   };
   // A operand: head row l32 of query l32 / 4 (rows past the group's queries
   // read zeros past the descriptor).  These loads, the weights and the
@@ -718,6 +729,8 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
       }
     }
   }
+  // (kept in this order: waiting for the setup loads must not wait for tiles)
+  __builtin_amdgcn_sched_barrier(0);
   Tile T[kScanTiles];
 #pragma unroll
   for (int s = 0; s < kScanTiles; ++s) load_tile(T[s], s);
