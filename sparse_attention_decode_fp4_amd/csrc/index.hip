@@ -310,7 +310,15 @@ template <bool kDirect>
 __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   constexpr int NW = kSampleThreads / 64;
   constexpr int kTilesPerWave = kSample / 32 / NW;  // 32-key MFMA tiles per wave
-  const int row = blockIdx.x;
+  // Workgroups from the multiple of 8 at or above the row count on are
+  // helpers: helper r fetches row r's sample on another CU of the row's XCD,
+  // so many of the row's own loads find the lines in that XCD's L2 (one CU
+  // alone is bound by its misses in flight; a helper fetching half the
+  // sample gained less).
+  const int rows_pad = (p.rows + kXcds - 1) / kXcds * kXcds;
+  const bool helper = (int)blockIdx.x >= p.rows;
+  const int row = helper ? (int)blockIdx.x - rows_pad : (int)blockIdx.x;
+  if (row < 0) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int seq = row / p.n_q;
@@ -321,9 +329,9 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
   sample_plan(n_items, (uint32_t)p.k, S, ks);
   // the row's candidate histogram starts empty (the scan counts into it)
   static_assert(kHistWords == kSampleThreads, "one histogram word per thread");
-  p.hist[(int64_t)row * kHistWords + t] = 0u;
+  if (!helper) p.hist[(int64_t)row * kHistWords + t] = 0u;
   if (ks == 0) {
-    if (t == 0) p.thresh[row] = -INFINITY;
+    if (t == 0 && !helper) p.thresh[row] = -INFINITY;
     return;
   }
   __shared__ uint32_t skey[kSample + 32];  // + a slot per lane for the lanes without a key
@@ -372,6 +380,11 @@ __global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
     const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half + 16, 0, 0);
     B[u] = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     kv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
+  }
+  if (helper) {  // wait for the lines, then leave
+#pragma unroll
+    for (int u = 0; u < kTilesPerWave; ++u) asm volatile("" ::"v"(B[u]), "v"(kv[u]));
+    return;
   }
   // A operand: row l32 < 4 is query head l32 (channels 32 half .. +32); the
   // other lanes read past the row's 256 bytes and get zeros
@@ -1277,10 +1290,12 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnP
   if (scan_per_row > p.max_chunks) return hipErrorInvalidValue;
   const int gr = grid_rows(p.rows);
   int h = prof_begin(CSA2_K_INDEX_SAMPLE, stream);
+  // (rows, then helpers from the next multiple of 8 on: see k_index_sample)
+  const unsigned sgrid_rows = (unsigned)((p.rows + kXcds - 1) / kXcds * kXcds + p.rows);
   if (p.source == kItemsDirect)
-    hipLaunchKernelGGL(k_index_sample<true>, dim3((unsigned)p.rows), dim3(kSampleThreads), 0, stream, p);
+    hipLaunchKernelGGL(k_index_sample<true>, dim3(sgrid_rows), dim3(kSampleThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(k_index_sample<false>, dim3((unsigned)p.rows), dim3(kSampleThreads), 0, stream, p);
+    hipLaunchKernelGGL(k_index_sample<false>, dim3(sgrid_rows), dim3(kSampleThreads), 0, stream, p);
   prof_end(h, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
