@@ -614,7 +614,9 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
         return fail(CSA2_ERR_ARG, "POOL reindexing needs state.pool");
       has_full = has_idx = 1;
       paged = L.kv->pages.table != nullptr;
-      if (a->index_kind == CSA2_INDEX_HIER && st->pool) has_pool = 1;
+      // a Full layer replaces the KV: only a hierarchical one leaves a pool
+      // of it (a flat one makes any earlier pool stale)
+      has_pool = (a->index_kind == CSA2_INDEX_HIER && st->pool) ? 1 : 0;
     } else if (L.mode == CSA2_MODE_REINDEX) {
       if (!has_full) return fail(CSA2_ERR_STATE, "layer %d: REINDEX before any FULL layer", l);
       if (a->reindex_kind == CSA2_INDEX_POOL && !has_pool)
@@ -679,7 +681,10 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
       }
       if ((rc = run_index(&ia, workspace, w, s, win))) return rc;
       j.window_elsewhere = win != nullptr;
-      if (L.mode == CSA2_MODE_FULL) { st->has_full = 1; if (hier && st->pool) st->has_pool = 1; }
+      if (L.mode == CSA2_MODE_FULL) {
+        st->has_full = 1;
+        st->has_pool = (hier && st->pool) ? 1 : 0;
+      }
       st->has_indices = 1;
       st->batch = a->batch; st->n_q = a->n_q;
     }

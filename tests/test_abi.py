@@ -175,6 +175,36 @@ def test_group_state_errors(m):
     assert f(None, ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_ARG
 
 
+def test_flat_full_drops_an_earlier_pool(m):
+    """A state whose pool came from an earlier hierarchical Full layer: a
+    flat Full layer replaces the KV, so a pool Reindex after it has no pool
+    of that KV to rank and is refused before anything is launched."""
+    st = m.GroupState()
+    st.indices, st.pool = _p(), _p(0x100000)
+    st.has_full, st.has_indices, st.has_pool, st.batch, st.n_q = 1, 1, 1, 1, 1
+    kv = m.KV()
+    kv.nib, kv.scale, kv.k8, kv.kscale, kv.stride = _p(0x200000), _p(0x300000), _p(0x400000), _p(0x500000), 1000
+    layers = (m.Layer * 2)()
+    for l in layers:
+        l.q, l.swa, l.out, l.idx_q = _p(0x600000), _p(0x700000), _p(0x800000), _p(0x900000)
+    layers[0].mode, layers[0].kv = m.MODE_FULL, ctypes.pointer(kv)
+    layers[1].mode = m.MODE_REINDEX
+    g = m.GroupArgs()
+    qp, ne, sp = (ctypes.c_int64 * 1)(999), (ctypes.c_int64 * 1)(1000), (ctypes.c_int64 * 1)(872)
+    g.batch, g.n_q, g.ratio = 1, 1, 1
+    g.index_kind, g.reindex_kind = m.INDEX_FLAT, m.INDEX_POOL
+    g.q_pos0, g.n_entries, g.swa_pos0 = (ctypes.cast(x, ctypes.c_void_p) for x in (qp, ne, sp))
+    g.swa_stride, g.swa_rows, g.softmax_scale, g.n_layers, g.layers = 128, 128, 1.0, 2, layers
+    f = m.lib.csa2_run_group
+    assert f(ctypes.byref(g), ctypes.byref(st), _p(), 1 << 30, None) == m.ERR_STATE
+    assert b"POOL" in m.lib.csa2_last_error()
+    assert st.has_pool == 1          # a refused call leaves the state as it was
+    # the same Reindex alone still finds the earlier pool valid (its workspace
+    # check then fails: nothing is launched either way)
+    g.n_layers, g.layers = 1, ctypes.cast(ctypes.byref(layers, ctypes.sizeof(m.Layer)), ctypes.POINTER(m.Layer))
+    assert f(ctypes.byref(g), ctypes.byref(st), _p(), 16, None) == m.ERR_WORKSPACE
+
+
 def _pages(m, table=None, table_stride=1, page_size=128, pool_entries=1024):
     pg = m.Pages()
     pg.table = _p(0x8000) if table is None else table

@@ -132,3 +132,20 @@ def test_fp4_roundtrip_error_bound_and_symmetries():
     nib3, scale3 = oracle.fp4_encode_rows(x * np.float32(4.0))
     assert np.array_equal(nib, nib3)
     assert np.array_equal(oracle.e4m3_value(scale3), 4 * oracle.e4m3_value(scale))
+
+
+def test_bf16_value_matches_torch_on_every_pattern():
+    # every one of the 65,536 bfloat16 bit patterns against torch's own
+    # bfloat16 -> float64 conversion: the value, its sign (signed zeros) and
+    # NaN-ness
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_value(bits)
+    assert got.dtype == np.float64
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+    # closed forms: 0x3F80 = 1, 0xC000 = -2, 0x7F80 = +inf, 0x0001 = 2^-133
+    assert got[0x3F80] == 1.0 and got[0xC000] == -2.0 and np.isposinf(got[0x7F80])
+    assert got[0x0001] == 2.0 ** -133

@@ -4,6 +4,7 @@ four single attention calls, and illegal orders are refused."""
 
 import numpy as np
 import pytest
+import torch
 
 import csa2_inputs as gen
 import oracle
@@ -106,3 +107,111 @@ def test_prefill_rows_match_single_queries_and_short_prefixes_take_all():
     st1 = oracle.new_state()
     out1 = oracle.run_group([last], st1, [n_q - 1], [n_tok // 2], [0], ratio=2)[0]
     assert np.array_equal(out1[0, 0], out[0, -1])
+
+
+# --- hierarchical Full layer, and Reindex over its pool ----------------------
+# A context of 20,000 entries has 2,500 blocks of 8, so the 2,048 kept blocks
+# are a strict subset and the pool is not the whole context.  The checks below
+# rank by brute force, with torch's float8 decoder and Python sorting, and so
+# share no arithmetic with the oracle's indexer.
+HCTX = 20000
+
+
+def _brute_scores(idx_q, k8, ks):
+    q = torch.from_numpy(np.ascontiguousarray(idx_q)).view(torch.float8_e4m3fn).to(torch.float64)
+    k = torch.from_numpy(np.ascontiguousarray(k8)).view(torch.float8_e4m3fn).to(torch.float64)
+    dots = torch.clamp(k @ q.T, min=0.0).sum(dim=1)
+    return (torch.from_numpy(np.asarray(ks, dtype=np.float64)) * dots).numpy()
+
+
+def _brute_top(score, positions, k):
+    order = sorted(range(len(positions)), key=lambda i: (-score[i], positions[i]))
+    return sorted(int(positions[i]) for i in order[:k])
+
+
+def _hier_kv(seed):
+    x = gen.latent(HCTX, seed).numpy()
+    k = gen.index_key(HCTX, seed).numpy()
+    nib, sc, k8, ks = oracle.quantize_kv(x, 1, k)
+    bk8, bks = oracle.block_keys(k8, ks)
+    return dict(nib=[nib], scale=[sc], k8=[k8], ks=[ks], bk8=[bk8], bks=[bks])
+
+
+def _hier_layer(mode, seed, layer, kv=None):
+    d = dict(mode=mode, q=gen.bf16_bits(gen.attn_query((1, 1), seed, layer)),
+             swa=gen.bf16_bits(gen.window_rows(1, 128, seed, layer)))
+    if mode != oracle.REUSE:
+        d["idx_q"] = gen.index_query((1, 1), seed, layer).numpy()
+        d["idx_w"] = None
+    if kv is not None:
+        d["kv"] = kv
+    return d
+
+
+def _hier_run(layers, st, reindex_kind="flat"):
+    return oracle.run_group(layers, st, [HCTX - 1], [HCTX], [HCTX - 128], kind="hier",
+                            reindex_kind=reindex_kind)
+
+
+def test_hier_full_stores_the_pool_of_the_best_blocks():
+    kv = _hier_kv(11)
+    st = oracle.new_state()
+    full = _hier_layer(oracle.FULL, 11, 0, kv)
+    _hier_run([full, _hier_layer(oracle.REUSE, 11, 1)], st)
+    iq = full["idx_q"][0, 0]
+    bsc = _brute_scores(iq, kv["bk8"][0], kv["bks"][0])
+    n_blk = len(bsc)
+    assert n_blk == HCTX // 8
+    blocks = _brute_top(bsc, np.arange(n_blk), 2048)
+    want_pool = sorted(p for b in blocks for p in range(8 * b, 8 * b + 8) if p < HCTX)
+    pool = np.asarray(st["pool"][0][0])
+    assert len(want_pool) == 2048 * 8
+    assert np.array_equal(pool[pool >= 0], want_pool) and np.all(pool[len(want_pool):] == -1)
+    # the Full layer's indices: the top 512 positions inside that pool
+    tsc = _brute_scores(iq, kv["k8"][0][want_pool], kv["ks"][0][want_pool])
+    assert np.array_equal(st["indices"][0, 0], _brute_top(tsc, np.asarray(want_pool), 512))
+    # and they differ from the flat top-512 over the whole context (the pool
+    # is a real restriction on this input)
+    flat = _brute_top(_brute_scores(iq, kv["k8"][0], kv["ks"][0]), np.arange(HCTX), 512)
+    assert not np.array_equal(st["indices"][0, 0], flat)
+
+
+def test_pool_reindex_ranks_only_the_stored_pool():
+    kv = _hier_kv(12)
+    st = oracle.new_state()
+    full = _hier_layer(oracle.FULL, 12, 0, kv)
+    _hier_run([full], st, "pool")
+    full_idx = st["indices"].copy()
+    pool = np.asarray(st["pool"][0][0])
+    pool = pool[pool >= 0]
+    # with the Full layer's own indexer query the pool Reindex gives the Full
+    # layer's indices back
+    re = _hier_layer(oracle.REINDEX, 12, 1)
+    re["idx_q"] = full["idx_q"]
+    _hier_run([re], st, "pool")
+    assert np.array_equal(st["indices"], full_idx)
+    # with a fresh query: the top 512 of the pool, not of the whole context
+    re2 = _hier_layer(oracle.REINDEX, 12, 2)
+    reuse = _hier_layer(oracle.REUSE, 12, 3)
+    outs = _hier_run([re2, reuse], st, "pool")
+    iq = re2["idx_q"][0, 0]
+    want = _brute_top(_brute_scores(iq, kv["k8"][0][pool], kv["ks"][0][pool]), pool, 512)
+    assert np.array_equal(st["indices"][0, 0], want)
+    flat = _brute_top(_brute_scores(iq, kv["k8"][0], kv["ks"][0]), np.arange(HCTX), 512)
+    assert not np.array_equal(want, flat)
+    # the Reuse layer attends over those indices
+    one = oracle.sparse_swa_attention(reuse["q"][0, 0], kv["nib"][0], kv["scale"][0], np.asarray(want),
+                                      reuse["swa"][0], HCTX - 128, HCTX - 1)
+    assert np.array_equal(outs[1][0, 0], one)
+    # a flat reindex of the same query ranks the whole context instead
+    st2 = oracle.new_state()
+    _hier_run([full, re2], st2, "flat")
+    assert np.array_equal(st2["indices"][0, 0], flat)
+
+
+def test_pool_reindex_needs_a_hierarchical_pool():
+    st = oracle.new_state()
+    kv = _hier_kv(13)
+    oracle.run_group([_hier_layer(oracle.FULL, 13, 0, kv)], st, [HCTX - 1], [HCTX], [HCTX - 128], kind="flat")
+    with pytest.raises(RuntimeError):
+        _hier_run([_hier_layer(oracle.REINDEX, 13, 1)], st, "pool")
