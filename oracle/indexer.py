@@ -45,6 +45,21 @@ def scores(idx_q, idx_w, k8, ks):
     return np.asarray(ks, dtype=np.float64) * per_head.sum(axis=1)
 
 
+def scores_many(idx_q, idx_w, k8, ks):
+    """Scores of n queries against the same keys, float64 [n, m]: row i is
+    scores(idx_q[i], idx_w[i], k8, ks) (idx_w None: all weights 1), with the
+    keys decoded once for all queries.
+
+    idx_q u8[n, 4, 64]; idx_w f32[n, 4] or None; k8 u8[m, 64]; ks f32[m]."""
+    q = e4m3_value(np.asarray(idx_q))                          # [n, 4, 64]
+    n, h, c = q.shape
+    w = np.ones((n, h)) if idx_w is None else np.asarray(idx_w, dtype=np.float64)
+    k = e4m3_value(np.asarray(k8))                             # [m, 64]
+    dots = (k @ q.reshape(n * h, c).T).reshape(-1, n, h)       # [m, n, 4], exact
+    per_head = np.maximum(dots, 0.0) * w[None, :, :]
+    return (np.asarray(ks, dtype=np.float64)[:, None] * per_head.sum(axis=2)).T
+
+
 def top_k(score, positions, k):
     """Top-k positions of (score, position) pairs: score descending, position
     ascending on ties; returned ascending, padded with -1 to length k."""

@@ -55,3 +55,33 @@ def check_close(gpu, ref, what=""):
     assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance, "
                            f"max err {err.max():.3g}")
     return float(err.max())
+
+
+def check_hier(gpu_idx, gpu_pool, q, w, k8, ks, bk8, bks, n_vis, k=512, n_blocks=2048, what=""):
+    """Hierarchical selection of one query, with nothing skipped on ties.
+
+    The block stage: the GPU's kept blocks (read from its pool) against the
+    oracle's block scores, tie-aware like any top-k.  The pool must then be
+    exactly the visible positions of those blocks, ascending, -1 padded.  The
+    token stage: the GPU's indices against the oracle's top-k of the GPU's
+    own pool (so a legitimate block-stage tie cannot hide a token-stage
+    error).  k8 / ks / bk8 / bks are the oracle's codes of the sequence.
+    Returns (block kind, token kind), each "exact" or "tie"."""
+    import oracle
+    nb = -(-n_vis // 8)
+    bscore = oracle.scores(q, w, bk8[:nb], bks[:nb])
+    gpool = np.asarray(gpu_pool)
+    gblocks = np.unique(gpool[gpool >= 0] // 8)
+    gb = np.full(n_blocks, -1, dtype=np.int64)
+    assert len(gblocks) <= n_blocks, f"{what}: more than {n_blocks} blocks in the pool"
+    gb[: len(gblocks)] = gblocks
+    rb = oracle.top_k(bscore, np.arange(nb), n_blocks)
+    kind_b = check_topk(gb, rb, bscore, n_blocks, nb, f"{what} blocks")
+    want = (gblocks[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    want = want[want < n_vis]
+    assert np.array_equal(gpool[: len(want)], want) and np.all(gpool[len(want):] == -1), \
+        f"{what}: the pool is not the visible positions of its blocks"
+    ref = oracle.index_pool(q, w, k8, ks, want, k)
+    sc = oracle.scores(q, w, k8[want], ks[want])
+    kind_t = check_topk(gpu_idx, ref, dict(zip(want.tolist(), sc.tolist())), k, len(want), f"{what} pool")
+    return kind_b, kind_t

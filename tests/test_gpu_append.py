@@ -11,6 +11,7 @@ import torch
 
 import csa2_inputs as gen
 import oracle
+import oracle_side
 from parity import check_close, check_topk
 
 pytestmark = pytest.mark.gpu
@@ -109,7 +110,7 @@ def test_ring_window_attention_matches_linear(csa2):
     out_ring = csa2.csa2_sparse_swa_attn(ws, q, nib, sc, idx_d, rg, q_pos0, None, ctx, swa_ring=ring)
     torch.cuda.synchronize()
     assert torch.equal(out_lin, out_ring)
-    nh, sh = nib.cpu().numpy(), sc.cpu().numpy()
+    nh, sh = oracle_side.fp4(x, nib, sc)
     for b in range(batch):
         for i in range(n_q):
             ref = oracle.sparse_swa_attention(gen.bf16_bits(q[b, i]), nh[b * ctx:(b + 1) * ctx],
@@ -164,11 +165,9 @@ def test_decode_steps_self_contained(csa2):
         rn, rs, rk, rks = oracle.quantize_kv(xh, 1, kh)
         iq = layers[0]["idx_q"][b, 0].cpu().numpy()
         ref_idx = oracle.index_flat(iq, None, rk, rks, pos + 1)
-        kind = check_topk(idx[b, 0], ref_idx, oracle.scores(iq, None, rk, rks), 512, pos + 1, f"seq {b}")
-        if kind != "exact":
-            continue
+        check_topk(idx[b, 0], ref_idx, oracle.scores(iq, None, rk, rks), 512, pos + 1, f"seq {b}")
         win = _bf16_bits(xs[b][pos - 127: pos + 1])
-        for j, L in enumerate(layers):
-            ref = oracle.sparse_swa_attention(gen.bf16_bits(L["q"][b, 0]), rn, rs, ref_idx, win, pos - 127, pos)
+        for j, L in enumerate(layers):  # on the GPU's own index set
+            ref = oracle.sparse_swa_attention(gen.bf16_bits(L["q"][b, 0]), rn, rs, idx[b, 0], win, pos - 127, pos)
             check_close(outs[j][b, 0].cpu().numpy(), ref, f"seq {b} layer {j}")
     assert ws.fallbacks() == 0

@@ -7,6 +7,7 @@ import torch
 
 import csa2_inputs as gen
 import oracle
+import oracle_side
 from parity import check_close
 
 pytestmark = pytest.mark.gpu
@@ -24,6 +25,7 @@ def _case(csa2, seed, batch, ctx, n_q, q_pos0, n_idx, lognormal=False, pad=0):
     dev = "cuda"
     x = gen.latent(batch * ctx, seed, lognormal=lognormal, device=dev)
     nib, sc = csa2.csa2_quantize_kv(x)
+    _case.oracle_codes = oracle_side.fp4(x, nib, sc)
     rng = np.random.default_rng(seed)
     idx = np.full((batch, n_q, n_idx), -1, np.int32)
     for b in range(batch):
@@ -52,7 +54,7 @@ def test_attention_matches_oracle(csa2, batch, ctx, n_q, n_idx, q_pos, pad, logn
     out = csa2.csa2_sparse_swa_attn(ws, q, nib, sc, idx, swa, [q_pos] * batch, swa_pos0, ctx,
                                     softmax_scale=1.0)
     torch.cuda.synchronize()
-    nh, sh, ih = nib.cpu().numpy(), sc.cpu().numpy(), idx.cpu().numpy()
+    (nh, sh), ih = _case.oracle_codes, idx.cpu().numpy()
     qb, sb = gen.bf16_bits(q), gen.bf16_bits(swa)
     for b in range(batch):
         for i in range(n_q):

@@ -6,7 +6,8 @@ import torch
 
 import csa2_inputs as gen
 import oracle
-from parity import check_topk
+import oracle_side
+from parity import check_hier, check_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -20,11 +21,13 @@ def csa2():
 
 
 def _keys(csa2, seed, batch, stride):
+    """GPU keys of fp32 draws, and the oracle's codes of the same draws."""
     dev = "cuda"
     k = gen.index_key(batch * stride, seed, device=dev)
     x = torch.zeros((batch * stride, 512), dtype=torch.float32, device=dev)
     _, _, k8, ks = csa2.csa2_quantize_kv(x, k_in=k)
-    return k8, ks
+    k8h, ksh = oracle_side.keys(k, k8, ks)
+    return k8, ks, k8h, ksh
 
 
 @pytest.mark.parametrize("n_entries,n_q,ratio,k", [
@@ -41,7 +44,7 @@ def _keys(csa2, seed, batch, stride):
 def test_flat_topk(csa2, n_entries, n_q, ratio, k):
     batch = len(n_entries)
     stride = max(n_entries)
-    k8, ks = _keys(csa2, 100 + stride, batch, stride)
+    k8, ks, k8h, ksh = _keys(csa2, 100 + stride, batch, stride)
     q = gen.index_query((batch, n_q), 5 + n_q, device="cuda")
     w = None
     if n_q > 1:
@@ -50,7 +53,7 @@ def test_flat_topk(csa2, n_entries, n_q, ratio, k):
     ws = csa2.Workspace(batch, n_q, stride)
     out = csa2.csa2_index_topk(ws, q, k8, ks, n_entries, q_pos0, stride, ratio=ratio, idx_w=w, k=k)
     torch.cuda.synchronize()
-    k8h, ksh, qh = k8.cpu().numpy(), ks.cpu().numpy(), q.cpu().numpy()
+    qh = q.cpu().numpy()
     wh = None if w is None else w.cpu().numpy()
     kinds = []
     for b, n in enumerate(n_entries):
@@ -69,7 +72,7 @@ def test_flat_topk(csa2, n_entries, n_q, ratio, k):
 
 
 def test_zero_query_picks_first_positions(csa2):
-    k8, ks = _keys(csa2, 9, 1, 5000)
+    k8, ks, _, _ = _keys(csa2, 9, 1, 5000)
     q = torch.zeros((1, 1, 4, 64), dtype=torch.uint8, device="cuda")
     ws = csa2.Workspace(1, 1, 5000)
     out = csa2.csa2_index_topk(ws, q, k8, ks, [5000], [4999], 5000)
@@ -95,7 +98,7 @@ def test_equal_scores_tie_to_lower_position(csa2):
 def test_hierarchical_topk(csa2, n_entries):
     batch = len(n_entries)
     stride = max(n_entries)
-    k8, ks = _keys(csa2, 77, batch, stride)
+    k8, ks, k8h, ksh = _keys(csa2, 77, batch, stride)
     bk8, bks = csa2.csa2_build_block_keys(k8, ks, n_entries, stride)
     bst = (stride + 7) // 8
     q = gen.index_query((batch, 1), 13, device="cuda")
@@ -104,28 +107,16 @@ def test_hierarchical_topk(csa2, n_entries):
                                      kind=csa2.INDEX_HIER, bk8=bk8, bkscale=bks, bk_stride=bst,
                                      want_pool=True)
     torch.cuda.synchronize()
-    k8h, ksh, qh = k8.cpu().numpy(), ks.cpu().numpy(), q.cpu().numpy()
-    bk8h, bksh = bk8.cpu().numpy(), bks.cpu().numpy()
+    qh = q.cpu().numpy()
+    bk8h, bksh = oracle_side.block_keys(k8h, ksh, n_entries, stride, bk8, bks)
     for b, n in enumerate(n_entries):
         kb, sb = k8h[b * stride: b * stride + n], ksh[b * stride: b * stride + n]
         bkb, bsb = bk8h[b * bst: b * bst + (n + 7) // 8], bksh[b * bst: b * bst + (n + 7) // 8]
         ref_idx, ref_pool = oracle.index_hier(qh[b, 0], None, kb, sb, bkb, bsb, n)
-        # block stage: tie-aware on block scores
-        nb = (n + 7) // 8
-        bscore = oracle.scores(qh[b, 0], None, bkb, bsb)
         gpool = pool[b, 0].cpu().numpy()
-        gblocks = np.unique(gpool[gpool >= 0] // 8)
-        rblocks = np.unique(ref_pool[ref_pool >= 0] // 8)
-        gb = np.full(2048, -1)
-        gb[: len(gblocks)] = gblocks
-        rb = np.full(2048, -1)
-        rb[: len(rblocks)] = rblocks
-        kind = check_topk(gb, rb, bscore, 2048, nb, f"blocks b{b}")
-        if kind == "exact":
+        kinds = check_hier(out[b, 0].cpu().numpy(), gpool, qh[b, 0], None, kb, sb, bkb, bsb, n, what=f"b{b}")
+        if kinds[0] == "exact":
             assert np.array_equal(gpool, ref_pool)
-            valid = ref_pool[ref_pool >= 0]
-            sc = dict(zip(valid.tolist(), oracle.scores(qh[b, 0], None, kb[valid], sb[valid]).tolist()))
-            check_topk(out[b, 0].cpu().numpy(), ref_idx, sc, 512, len(valid), f"pool b{b}")
         if n <= 16384:
             flat = oracle.index_flat(qh[b, 0], None, kb, sb, n)
             assert np.array_equal(ref_idx, flat)
@@ -134,7 +125,7 @@ def test_hierarchical_topk(csa2, n_entries):
 
 def test_pool_topk(csa2):
     stride = 9000
-    k8, ks = _keys(csa2, 5, 2, stride)
+    k8, ks, k8h, ksh = _keys(csa2, 5, 2, stride)
     rng = np.random.default_rng(1)
     cand = np.full((2, 1, 3000), -1, np.int32)
     cand[0, 0, :2500] = np.sort(rng.choice(stride, 2500, replace=False))
@@ -144,7 +135,7 @@ def test_pool_topk(csa2):
     out = csa2.csa2_index_topk(ws, q, k8, ks, [stride, stride], [stride - 1] * 2, stride,
                                kind=csa2.INDEX_POOL, cand=torch.from_numpy(cand).cuda())
     torch.cuda.synchronize()
-    k8h, ksh, qh = k8.cpu().numpy(), ks.cpu().numpy(), q.cpu().numpy()
+    qh = q.cpu().numpy()
     for b in range(2):
         c = cand[b, 0]
         c = c[c >= 0]

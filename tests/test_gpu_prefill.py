@@ -74,4 +74,9 @@ def test_prefill_chunk(csa2, prefix_tok, chunk):
             n_same += 1
             for j in range(len(plan)):
                 check_close(outs[j][0, i].cpu().numpy(), ref[j][0, i], f"layer {j} query {i}")
+        else:  # a tie: the oracle's attention on the GPU's own index set
+            for j in range(len(plan)):
+                r = oracle.sparse_swa_attention(host[j]["q"][0, i], rn, rs, gi[0, i], host[j]["swa"][0], swa_pos0,
+                                                prefix_tok + i)
+                check_close(outs[j][0, i].cpu().numpy(), r, f"layer {j} query {i}")
     assert n_same >= chunk * 0.9

@@ -8,6 +8,7 @@ import torch
 
 import csa2_inputs as gen
 import oracle
+import oracle_side
 from parity import check_topk
 
 pytestmark = pytest.mark.gpu
@@ -22,9 +23,11 @@ def csa2():
 
 
 def _keys(csa2, k_f32):
+    """GPU keys of fp32 draws, and the oracle's codes of the same draws."""
     n = k_f32.shape[0]
     x = torch.zeros((n, 512), dtype=torch.float32, device="cuda")
     _, _, k8, ks = csa2.csa2_quantize_kv(x, k_in=k_f32)
+    _keys.oracle_codes = oracle_side.keys(k_f32, k8, ks)
     return k8, ks
 
 
@@ -59,7 +62,7 @@ def test_prefill_index_matches_oracle(csa2, B, n_entries, n_q, ratio, with_w, k)
     out = csa2.csa2_index_topk(ws, q, k8, ks, n_entries, q_pos0, stride, ratio=ratio, idx_w=w, k=k)
     torch.cuda.synchronize()
     kinds = _check_rows(out.cpu().numpy(), q.cpu().numpy(), None if w is None else w.cpu().numpy(),
-                        k8.cpu().numpy(), ks.cpu().numpy(), n_entries, q_pos0, ratio, k, stride)
+                        *_keys.oracle_codes, n_entries, q_pos0, ratio, k, stride)
     assert kinds.count("exact") >= 0.9 * len(kinds)
     out2 = csa2.csa2_index_topk(ws, q, k8, ks, n_entries, q_pos0, stride, ratio=ratio, idx_w=w, k=k)
     assert torch.equal(out, out2)
@@ -88,5 +91,5 @@ def test_prefill_misleading_sample_takes_the_exact_recompute(csa2):
     ws = csa2.Workspace(1, 48, n)
     out = csa2.csa2_index_topk(ws, q, k8, ks, [n], [n + 500], n)
     torch.cuda.synchronize()
-    _check_rows(out.cpu().numpy(), q.cpu().numpy(), None, k8.cpu().numpy(), ks.cpu().numpy(), [n],
+    _check_rows(out.cpu().numpy(), q.cpu().numpy(), None, *_keys.oracle_codes, [n],
                 [n + 500], 1, 512, n, rows=[0, 1, 47])

@@ -6,6 +6,7 @@ import torch
 
 import csa2_inputs as gen
 import oracle
+import oracle_side
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +80,7 @@ def test_block_keys_bit_exact(csa2):
     _, _, k8, ks = csa2.csa2_quantize_kv(gen.latent(3 * stride, 21, device=dev), k_in=k)
     bk8, bks = csa2.csa2_build_block_keys(k8, ks, n_entries, stride)
     torch.cuda.synchronize()
-    k8h, ksh = k8.cpu().numpy(), ks.cpu().numpy()
+    k8h, ksh = oracle_side.keys(k, k8, ks)  # the oracle's own codes of the same draws
     bst = (stride + 7) // 8
     for s, n in enumerate(n_entries):
         rb, rbs = oracle.block_keys(k8h[s * stride: s * stride + n], ksh[s * stride: s * stride + n])

@@ -132,3 +132,21 @@ def test_visibility_rule():
     assert oracle.visible_entries(0, 2) == 0          # entry 0 needs tokens 0 and 1
     assert oracle.visible_entries(1, 2) == 1
     assert oracle.visible_entries(262144 + 4095, 2) == 131072 + 2048
+
+
+def test_scores_many_rows_equal_single_query_scores():
+    # the multi-query form is the single-query score row by row, bit for bit
+    # (with and without head weights, negative weights included)
+    rng = np.random.default_rng(7)
+    k8 = rng.integers(0, 256, size=(300, 64)).astype(np.uint8)
+    k8[(k8 & 0x7F) == 0x7F] = 0      # no NaN codes
+    ks = rng.random(300).astype(np.float32)
+    q = rng.integers(0, 256, size=(5, 4, 64)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 1
+    w = rng.standard_normal((5, 4)).astype(np.float32)
+    many = oracle.scores_many(q, None, k8, ks)
+    many_w = oracle.scores_many(q, w, k8, ks)
+    assert many.shape == (5, 300)
+    for i in range(5):
+        assert np.array_equal(many[i], oracle.scores(q[i], None, k8, ks))
+        assert np.array_equal(many_w[i], oracle.scores(q[i], w[i], k8, ks))
