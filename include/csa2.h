@@ -186,7 +186,12 @@ typedef struct csa2_pages {
  *
  * Score (a reading, the pages give no formula):
  *   s_p = ks_p * sum_h w_h * max(0, q_h . k_p),   h = 0..3, 64 channels,
- * q_h and k_p being E4M3 code values; computed in float32 on the GPU.
+ * q_h and k_p being E4M3 code values.  Scores are computed in float32 on the
+ * GPU.  With n_q < 32, keys whose float32 scores lie within the float32
+ * error bound of the k-th are rescored exactly (float64: every product of
+ * E4M3 codes and every partial sum of 64 is exact there) and ranked on those
+ * exact scores, so the selected set is the one the exact scores give; with
+ * n_q >= 32 a band around the MFMA k-th score is rescored in float32.
  * Selection: score descending, then position ascending; the min(k, n)
  * winners are written in ascending position order, padded with -1.
  *
@@ -401,18 +406,20 @@ int csa2_append(const csa2_append_args* a, void* stream);
 size_t csa2_workspace_bytes(int32_t max_batch, int32_t max_n_q, int64_t max_entries);
 
 /*
- * Zero a workspace (optional: every call initialises what it reads).
+ * Zero a workspace (optional: every call initialises what it reads; it also
+ * resets csa2_workspace_fallbacks).
  *   workspace  device, 256-byte aligned;  ws_bytes  a multiple of 4
  */
 int csa2_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Diagnostic: how many query rows, since the workspace was last zeroed by
- * csa2_workspace_init, had their top-k recomputed exactly because the
- * candidate list of the threshold pass could not hold the answer (a
- * segment overflowed, fewer than k keys reached the sampled threshold, or
- * the prefill MFMA band reached below it).  Results are exact either way;
- * a count above zero on a steady workload means the slow path is taken.
+ * csa2_workspace_init, had their top-k recomputed exactly over every item
+ * because the candidate bands of the scan could not hold the answer (a scan
+ * chunk holding more of the row's winners than its 128-slot segment, e.g.
+ * when many keys score the same, or, for prefill-sized calls, the sampled
+ * threshold or the MFMA band misled).  Results are exact either way; a
+ * count above zero on a steady workload means the slow path is taken.
  *   workspace  device, the workspace the calls used;  count  host (out)
  * Waits for the stream.  Errors: CSA2_ERR_ARG / CSA2_ERR_WORKSPACE for bad
  * pointers, CSA2_ERR_HIP if the copy fails.

@@ -36,7 +36,7 @@ constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of atte
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t stats, thresh, hist, seg_count, seg_list, blocks, nsel, partial;
+  size_t stats, chunk_info, seg_list, blocks, nsel, partial;
   size_t pf_sample, pf_thresh, pf_count, pf_list, total;
   int32_t max_chunks;  // scan chunks per row covered by the segment buffers
 };
@@ -45,15 +45,11 @@ struct WsLayout {
 // prefill-path buffers cover `pf_rows` query rows (0 when unused).
 WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   WsLayout w{};
-  // rows of fewer items are cut into more, smaller chunks (scan_chunk_items)
-  w.max_chunks = (int32_t)std::max<int64_t>((std::max<int64_t>(max_items, 1) + kScanChunk - 1) / kScanChunk,
-                                            scan_chunks_min(CSA2_MAX_K));
+  w.max_chunks = (int32_t)scan_max_chunks(std::max<int64_t>(max_items, 1));
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
   w.stats = take(kWsAlign);  // offset 0 in every layout: the fallback counter
-  w.thresh = take((size_t)rows * 4);
-  w.hist = take((size_t)rows * kHistWords * 4);
-  w.seg_count = take((size_t)rows * w.max_chunks * 4);
+  w.chunk_info = take((size_t)rows * w.max_chunks * 16);
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
   w.nsel = take((size_t)rows * 4);
@@ -172,7 +168,8 @@ int64_t index_max_items(const csa2_index_args* a) {
 }
 
 int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t stream,
-              const AttnPass* window = nullptr) {
+              const AttnPass* window = nullptr, bool* window_done = nullptr) {
+  if (window_done) *window_done = false;
   for (int s0 = 0; s0 < a->batch; s0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, a->batch - s0);
     IndexPass p{};
@@ -220,10 +217,8 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     }
     p.idx_q = a->idx_q + row0 * kHI * kDI;
     p.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;
-    p.thresh = at<float>(ws, w.thresh);
-    p.hist = at<uint32_t>(ws, w.hist);
     p.fallbacks = at<uint32_t>(ws, w.stats);
-    p.seg_count = at<uint32_t>(ws, w.seg_count);
+    p.chunk_info = at<u32x4_t>(ws, w.chunk_info);
     p.seg_list = at<uint64_t>(ws, w.seg_list);
     p.max_chunks = w.max_chunks;
     hipError_t e;
@@ -264,7 +259,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     p.k_stride = a->k_stride;
     p.out = a->out_idx + row0 * a->k;
     p.out_stride = a->k;
-    if ((e = launch_index_pass(p, stream, window)) != hipSuccess) return hip_fail(e, "index pass");
+    if ((e = launch_index_pass(p, stream, window, window_done)) != hipSuccess) return hip_fail(e, "index pass");
   }
   return CSA2_OK;
 }
@@ -679,8 +674,9 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
         wp = make_attn_pass(j, 0, a->batch, workspace, w);
         if (tile_form(wp)) win = &wp;
       }
-      if ((rc = run_index(&ia, workspace, w, s, win))) return rc;
-      j.window_elsewhere = win != nullptr;
+      bool win_done = false;
+      if ((rc = run_index(&ia, workspace, w, s, win, &win_done))) return rc;
+      j.window_elsewhere = win_done;
       if (L.mode == CSA2_MODE_FULL) {
         st->has_full = 1;
         st->has_pool = (hier && st->pool) ? 1 : 0;

@@ -6,37 +6,52 @@
 // a pool of 2,048 blocks of 8 positions.  The score is a reading:
 //   s_p = ks_p * sum_h w_h * max(0, q_h . k_p)   over 4 indexer heads.
 //
-// One pass = three kernels over the rows (query rows) of a call:
-//   sample  one 1,024-thread workgroup per row scores a sample of 2,048 of
-//           its items, 256 evenly spaced runs of 8 (fp8 MFMA: the sample only
-//           steers the threshold) and sets the row threshold T0: the lower
-//           edge, at 20 key bits, of the key bin holding the k_s-th largest
-//           sample, k_s sized so that about 2.5 k items of the row reach T0
-//           (no threshold when the row has at most 2,048 items);
-//   scan    streams the fp8 keys once (4 lanes per key, 16 B each, fully
-//           coalesced; up to 4 queries of a sequence share a workgroup),
-//           scores every item with packed f16 dot products (v_dot2c_f32_f16;
-//           fp8 -> f16 is exact) and appends the items scoring at least T0
-//           to a segment per (row, chunk), staged in LDS, counting each in
-//           a histogram of score bins above T0;
-//   select  gathers the segments (about 2.5 k candidates), finds the exact
-//           k-th largest (score, -item) key (its bin from the histogram,
-//           then a rank among that bin's few keys; a radix when the bins
-//           cannot tell), orders the winners by item and writes their
-//           positions.  If the candidates cannot hold
-//           the answer (fewer than k, or a segment overflowed: the sample
-//           misled, e.g. all scores equal) the row is recomputed exactly by
-//           itself (radix steps over recomputed keys): slow, exact, rare.
+// One pass = two kernels over the rows (query rows) of a call:
+//   scan    streams the fp8 keys once.  One query per workgroup: 4 lanes per
+//           key, 16 B each, fully coalesced, packed f16 dot products
+//           (v_dot2c_f32_f16; fp8 -> f16 is exact).  2 or 4 queries of a
+//           sequence: one fp8 MFMA per 32-key tile for all of them.  The
+//           workgroup keeps its chunk's scores in LDS and, after the stream,
+//           histograms them below the chunk's largest score (1/64 of a
+//           binade per bin) to cut two bands: band 0, about the number of
+//           the row's winners the chunk can hold at most with any
+//           likelihood (a Poisson bound on the expected share), and band 1,
+//           the next keys up to the 128-slot segment.  Both go to the
+//           (row, chunk) segment with the band edges and the chunk's largest
+//           key scale;
+//   select  gathers band 0 of every chunk (about 3 k keys), finds the k-th
+//           largest (score, -item) key, fetches band 1 only of chunks whose
+//           band-0 edge reaches down to it, and settles the set: keys more
+//           than twice the score's error bound above the k-th win, keys
+//           within it are rescored exactly (float64, the products of E4M3
+//           codes summed exactly) and ranked by (score, -position); the
+//           winners are ordered by position and written.  A row whose bands
+//           cannot hold the answer (a chunk holding more than its segment
+//           of the winners, e.g. all scores equal) is recomputed by itself
+//           over every item: slow, exact, rare, and counted.
+// No separate pass picks a threshold for the scan: each chunk cuts its own
+// bands from its own scores, so the scan needs nothing from another kernel.
 #include "kernels.hpp"
 #include "select.hpp"
 #include "tile.hpp"
 
 namespace csa2 {
 
-constexpr int kSample = 2048;       // sampled items per row (two per thread of the sample kernel)
 constexpr int kBitmapItems = 131072;  // rows with at most this many items order winners by bitmap
-constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks (twice this at k > 1,024) gather in one round trip
-constexpr int kSpecSlots = 64;        // ... of the first this many slots of each segment
+constexpr int kSpecChunks = 64;       // rows with at most this many scan chunks (twice this at kPer 32) gather in one round trip
+constexpr int kSpecSlots = 64;        // ... of the first this many slots of each segment (band 0 fits)
+constexpr int kBand0Max = kSpecSlots; // band 0 of a chunk holds at most this many keys
+constexpr int kBandMax = 1024;        // near-tie keys one select rescores exactly, at most
+// Error bound of a binary32 score against the exact one, as a multiple of
+// ks * sum_h |w_h| * sum_c |q_hc| * 448 (448 bounds every E4M3 key code):
+// the VALU dot takes at most 18 binary32 roundings per head, each within
+// 2^-24 of a partial sum no larger than that; the MFMA accumulation is taken
+// as 2^-12 (a measured worst case on random codes was 2.5e-5 of the summed
+// magnitudes, 10x below).  A further 2^-20 |s| covers the roundings after
+// the dots.
+constexpr float kErrValu = 0x1p-18f;
+constexpr float kErrMfma = 0x1p-12f;
+constexpr float kErrTail = 0x1p-20f;
 
 // The row geometry below is all the kernels compute before their first
 // loads, so it avoids 64-bit divisions: the ratio is 1 or 2 and chunk sizes
@@ -78,20 +93,6 @@ template <bool kDirect>
 __device__ __forceinline__ int64_t row_chunk_items_of(const IndexPass& p, int row) {
   const int last = kDirect ? (row / p.n_q) * p.n_q + p.n_q - 1 : row;
   return scan_chunk_items(row_items_of<kDirect>(p, last, row_vis_positions(p, last)), p.k);
-}
-
-// The sampled threshold of a row, read with a vector load: a scalar load of
-// memory the previous kernel wrote would hold up the scalar loads of the
-// row geometry (one counter covers them all) until it arrives.
-__device__ __forceinline__ float load_thresh(const IndexPass& p, int row) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(p.thresh + row), 0, 4, kRawBufferWord3);
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
-}
-
-// Histogram bin of a candidate's score key (candidates are at or above T0).
-__device__ __forceinline__ uint32_t hist_bin(uint32_t key32, uint32_t t0key) {
-  const uint32_t b = (key32 - t0key) >> kHistShift;
-  return b < (uint32_t)(kHistBins - 1) ? b : (uint32_t)(kHistBins - 1);
 }
 
 __device__ __forceinline__ int64_t item_position(const IndexPass& p, int row, int64_t item,
@@ -220,7 +221,7 @@ __device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t
 // radix steps of 8 bits from bit `top` down.  256 threads; keys are unique
 // or the result is the k-th in the multiset order.
 template <typename Key, typename Visit>
-__device__ Key radix_kth(Visit visit, uint32_t n, uint32_t want, uint32_t* h256, Key* sh_kth, uint32_t* sh_need) {
+__device__ __forceinline__ Key radix_kth(Visit visit, uint32_t n, uint32_t want, uint32_t* h256, Key* sh_kth, uint32_t* sh_need) {
   const int t = threadIdx.x;
   constexpr int kBits = 8 * (int)sizeof(Key);
   if (t == 0) { *sh_kth = 0; *sh_need = want; }
@@ -259,256 +260,163 @@ __device__ Key radix_kth(Visit visit, uint32_t n, uint32_t want, uint32_t* h256,
 }
 
 
-// ------------------------------------------------------------------ sample
-// Sample size of a row and the rank k_s its threshold is taken at; k_s == 0
-// means "no threshold" (every item is a candidate).
-__device__ __forceinline__ void sample_plan(int64_t n_items, uint32_t k, int64_t& S, uint32_t& ks) {
-  S = n_items < kSample ? n_items : kSample;
-  ks = 0;
-  if (n_items > (int64_t)k && S > 0) {
-    if (S == n_items) {
-      // a row this short needs no threshold: every key is a candidate (at
-      // most kSample, 128-key chunks), and the select ranks them exactly.
-      // A threshold at the k-th sampled score would put the row's answer at
-      // the mercy of the sample's MFMA rounding against the scan's.
-      ks = 0;
-    } else {
-      const double want = 2.5 * (double)k * (double)S / (double)n_items + 4.0;
-      ks = want >= (double)S ? 0u : (uint32_t)want;
-    }
-  }
-}
-
-// Item of sample slot `slot` (< S): every item when the sample is the whole
-// row, otherwise kSample / kSampleRun evenly spaced runs of kSampleRun
-// consecutive items, so the sampled keys fill whole cache lines.
-constexpr int kSampleRun = 8;
-__device__ __forceinline__ int64_t sample_item(int64_t slot, int64_t S, int64_t n_items) {
-  if (S == n_items) return slot;
-  // S == kSample < n_items here
-  return ((slot / kSampleRun) * n_items) / (kSample / kSampleRun) + slot % kSampleRun;
-}
-
-// One workgroup of 1,024 threads per row scores the row's sample of 2,048
-// keys (256 runs of 8) and turns the order keys, kept in LDS, into the row threshold
-// T0: the lower edge, at 20 key bits, of the key bin holding the k_s-th
-// largest sample (a 4,096-bin histogram of the top 12 bits, then 256 bins of
-// the next 8 within the chosen bin).  T0 = -inf when there is no sample plan
-// or fewer than k_s valid samples.
-//
-// The sample scores only steer T0 (the select kernel checks that at least k
-// candidates reached it), so they are computed on fp8 MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales) rather than with the scan's
-// VALU arithmetic: one MFMA scores 32 sampled keys (B columns) against the
-// row's 4 query heads (A rows 0..3, rows 4..31 zero), so the 2,048 keys take
-// 64 MFMAs instead of the VALU work of one CU for 2,048 quad scores.
-constexpr int kSampleThreads = 1024;
-constexpr uint32_t kMfmaUnitScales = 0x7F7F7F7Fu;  // E8M0 127 = 1.0 in every byte
-typedef int v8i_t __attribute__((ext_vector_type(8)));
-typedef float v16f_t __attribute__((ext_vector_type(16)));
-template <bool kDirect>
-__global__ __launch_bounds__(kSampleThreads) void k_index_sample(IndexPass p) {
-  constexpr int NW = kSampleThreads / 64;
-  constexpr int kTilesPerWave = kSample / 32 / NW;  // 32-key MFMA tiles per wave
-  // Workgroups from the multiple of 8 at or above the row count on are
-  // helpers: helper r fetches row r's sample on another CU of the row's XCD,
-  // so many of the row's own loads find the lines in that XCD's L2 (one CU
-  // alone is bound by its misses in flight; a helper fetching half the
-  // sample gained less).
-  const int rows_pad = (p.rows + kXcds - 1) / kXcds * kXcds;
-  const bool helper = (int)blockIdx.x >= p.rows;
-  const int row = helper ? (int)blockIdx.x - rows_pad : (int)blockIdx.x;
-  if (row < 0) return;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
-  const int seq = row / p.n_q;
-  const int64_t vis = row_vis_positions(p, row);
-  const int64_t n_items = row_items_of<kDirect>(p, row, vis);
-  int64_t S;
-  uint32_t ks;
-  sample_plan(n_items, (uint32_t)p.k, S, ks);
-  // the row's candidate histogram starts empty (the scan counts into it)
-  static_assert(kHistWords == kSampleThreads, "one histogram word per thread");
-  if (!helper) p.hist[(int64_t)row * kHistWords + t] = 0u;
-  if (ks == 0) {
-    if (t == 0 && !helper) p.thresh[row] = -INFINITY;
-    return;
-  }
-  __shared__ uint32_t skey[kSample + 32];  // + a slot per lane for the lanes without a key
-  __shared__ uint32_t bins[4096];
-  __shared__ uint32_t wsum[NW];
-  __shared__ uint32_t sh[3];
-
-  // B operands: lane (l32, half) holds channels 32 half .. +32 of key l32 of
-  // each tile (loads issued first: they do not depend on the query).  Every
-  // load is an unconditional buffer load: a slot without a key uses the
-  // entry index CSA2_MAX_ENTRIES, past the descriptors' ranges, and reads
-  // zeros, so no load waits for another.
-  // (paged: descriptors over the pool, the entry from the page table, every
-  // page-table load issued before the key loads)
-  const bool paged = p.pm.pages != nullptr;
-  const uint32_t lim = paged ? (uint32_t)p.pm.pool : (uint32_t)CSA2_MAX_ENTRIES;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(paged ? p.k8 : p.k8 + (int64_t)seq * p.k_stride * kDI), 0, (int)(lim * kDI), kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(paged ? p.kscale : p.kscale + (int64_t)seq * p.k_stride), 0, (int)(lim * 4), kRawBufferWord3);
-  v8i_t B[kTilesPerWave];
-  float kv[kTilesPerWave];
-  bool valid[kTilesPerWave];
-  int64_t pos_u[kTilesPerWave];
-  uint32_t page_u[kTilesPerWave];
-#pragma unroll
-  for (int u = 0; u < kTilesPerWave; ++u) {
-    const int64_t slot = (wave * kTilesPerWave + u) * 32 + l32;
-    const int64_t item = slot < S ? sample_item(slot, S, n_items) : n_items;
-    if constexpr (kDirect) {
-      valid[u] = item < n_items;
-      pos_u[u] = valid[u] ? item : 0;
-    } else {
-      pos_u[u] = item_position(p, row, item, n_items, vis, valid[u]);
-    }
-    page_u[u] = 0;
-    if (paged)
-      page_u[u] = __builtin_amdgcn_raw_buffer_load_b32(page_row(p.pm, seq),
-                                                       valid[u] ? (int)((pos_u[u] >> p.pm.lg) * 4) : (int)(p.pm.stride * 4), 0, 0);
-  }
-#pragma unroll
-  for (int u = 0; u < kTilesPerWave; ++u) {
-    const int64_t pos = pos_u[u];
-    const uint32_t e = !valid[u] ? lim : paged ? paged_entry(p.pm, page_u[u], pos) : (uint32_t)pos;
-    const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half, 0, 0);
-    const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half + 16, 0, 0);
-    B[u] = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    kv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
-  }
-  if (helper) {  // wait for the lines, then leave
-#pragma unroll
-    for (int u = 0; u < kTilesPerWave; ++u) asm volatile("" ::"v"(B[u]), "v"(kv[u]));
-    return;
-  }
-  // A operand: row l32 < 4 is query head l32 (channels 32 half .. +32); the
-  // other lanes read past the row's 256 bytes and get zeros
-  v8i_t A;
-  {
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.idx_q + (int64_t)row * kHI * kDI), 0, kHI * kDI, kRawBufferWord3);
-    const int off = l32 < kHI ? l32 * kDI + 32 * half : kHI * kDI;
-    const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-    const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
-    A = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  }
-  // head weights by vector loads (see load_thresh)
-  float w[kHI];
-  if (p.idx_w) {
-    const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(p.idx_w + (int64_t)row * kHI), 0, 4 * kHI, kRawBufferWord3);
-#pragma unroll
-    for (int h = 0; h < kHI; ++h) w[h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, 4 * h, 0, 0));
-  } else {
-#pragma unroll
-    for (int h = 0; h < kHI; ++h) w[h] = 1.0f;
-  }
-  for (int i = t; i < 4096; i += kSampleThreads) bins[i] = 0;
-  if (t == 0) { sh[0] = 0xFFFFFFFFu; sh[2] = 0; }
-#pragma unroll
-  for (int u = 0; u < kTilesPerWave; ++u) {
-    v16f_t acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B[u], acc, 0, 0, 0, kMfmaUnitScales, 0,
-                                                          kMfmaUnitScales);
-    // The MFMA reads every lane's operands, so it must run with the whole
-    // wave active: the empty asm pins it here, in uniform control flow, and
-    // the store below is unconditional (instead of a branch on the half
-    // that the compiler could sink the MFMA into).
-    asm volatile("" ::"v"(acc));
-    // lanes 0..31 hold rows 0..3 (the heads) of column l32 in acc[0..3]
-    const float sc =
-        kv[u] * (w[0] * fmaxf(acc[0], 0.0f) + w[1] * fmaxf(acc[1], 0.0f) + w[2] * fmaxf(acc[2], 0.0f) +
-                 w[3] * fmaxf(acc[3], 0.0f));
-    skey[half ? kSample + l32 : (wave * kTilesPerWave + u) * 32 + l32] = valid[u] ? score_key(sc) : 0u;
-  }
-  __syncthreads();
-  const uint32_t k0 = skey[2 * t], k1 = skey[2 * t + 1];  // two keys per thread
-  if (k0) atomicAdd(&bins[k0 >> 20], 1u);
-  if (k1) atomicAdd(&bins[k1 >> 20], 1u);
-  __syncthreads();
-  // level 1: thread t owns bins 4t .. 4t+3
-  const uint4 hb = reinterpret_cast<const uint4*>(bins)[t];
-  const uint32_t hv[4] = {hb.x, hb.y, hb.z, hb.w};
-  const uint32_t local = hb.x + hb.y + hb.z + hb.w;
-  uint32_t total;
-  const uint32_t incl = block_incl_scan<NW>(local, wsum, total);
-  uint32_t run = total - incl;  // samples in bins above 4t + 3
-  if (run < ks && run + local >= ks) {
-    for (int j = 3; j >= 0; --j) {
-      if (run + hv[j] >= ks) { sh[0] = 4 * t + j; sh[1] = ks - run; break; }
-      run += hv[j];
-    }
-  }
-  __syncthreads();
-  const uint32_t b1 = sh[0], need = sh[1];
-  if (b1 == 0xFFFFFFFFu || b1 == 0u) {  // fewer than k_s valid samples (uniform)
-    if (t == 0) p.thresh[row] = -INFINITY;
-    return;
-  }
-  if (t < 256) bins[t] = 0;
-  __syncthreads();
-  // level 2: the next 8 bits, over the samples in bin b1
-  if ((k0 >> 20) == b1) atomicAdd(&bins[(k0 >> 12) & 255u], 1u);
-  if ((k1 >> 20) == b1) atomicAdd(&bins[(k1 >> 12) & 255u], 1u);
-  __syncthreads();
-  const uint32_t c = t < 256 ? bins[t] : 0u;
-  uint32_t tot2;
-  const uint32_t incl2 = block_incl_scan<NW>(c, wsum, tot2);
-  const uint32_t above = tot2 - incl2;  // samples of bin b1 in sub-bins above t
-  if (t < 256 && above < need && above + c >= need) sh[2] = t;
-  __syncthreads();
-  if (t == 0) p.thresh[row] = key_to_score((b1 << 20) | (sh[2] << 12));
-}
-
 // ------------------------------------------------------------------ scan
+// Band 0 of a chunk: the largest number of the row's winners it may hold
+// with any likelihood, from the expected share mu = k * csize / n (at most 8,
+// or 16 for k above 1,024, by the chunk sizing): mu + 4 sqrt(mu) + 3 (the
+// Poisson tail beyond that is below 1e-5 for mu <= 16), at most the
+// select's room shared by the row's chunks.
+__device__ __forceinline__ uint32_t band0_size(int64_t n_items, int64_t csize, int64_t nch, int k) {
+  const float mu = (float)((int64_t)k * csize) / (float)(n_items > 0 ? n_items : 1);
+  uint32_t m0 = (uint32_t)(mu + 4.0f * sqrtf(mu) + 3.0f);
+  const int64_t room = (k > 1024 || nch > 128 ? 256 * 32 : 256 * 16) * 3 / 4;
+  const int64_t share = room / (nch > 0 ? nch : 1);
+  if ((int64_t)m0 > share) m0 = (uint32_t)share;
+  if (m0 > (uint32_t)kBand0Max) m0 = kBand0Max;
+  return m0 > 0 ? m0 : 1u;
+}
 
-// Workgroup (NQ queries of one sequence, chunk of row_chunk_items items):
-// every key of the chunk is scored against each of the queries and those at
-// or above a query's threshold T0 become that query's candidates.  kDirect:
-// item i is position i (flat keys or block keys); keys and scales are read
-// through buffer descriptors whose range ends at the chunk's last item, so
-// the hardware returns zeros past it and the loads need no bounds branches.
-// Otherwise positions come from a block or position list (one query per
-// workgroup).
-template <int U, bool kDirect, int NQ, bool kPaged>
-__global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, int n_groups) {
-  static_assert(NQ == 1 || kDirect, "queries share a chunk only over direct items");
-  static_assert(!kPaged || kDirect, "paged caches are read over direct items");
-  // workgroup (group of NQ queries of one sequence, chunk)
-  int grp, chunk;
-  map_row_chunk(n_groups, per_row, grp, chunk);
-  if (grp >= n_groups) return;
-  const int qgroups = (p.n_q + NQ - 1) / NQ;
-  const int seq = grp / qgroups;
-  const int row0 = seq * p.n_q + (grp - seq * qgroups) * NQ;
-  const int nq = p.n_q - (row0 - seq * p.n_q) < NQ ? p.n_q - (row0 - seq * p.n_q) : NQ;
-  const int64_t csize = row_chunk_items_of<kDirect>(p, row0);  // shared by the rows of a sequence
-  const int64_t base = (int64_t)chunk * csize;
-  int64_t vis[NQ], n_items[NQ], end = 0;
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    vis[i] = i < nq ? row_vis_positions(p, row0 + i) : 0;
-    n_items[i] = i < nq ? row_items_of<kDirect>(p, row0 + i, vis[i]) : 0;
-    const int64_t e = base + csize < n_items[i] ? base + csize : n_items[i];
-    end = e > end ? e : end;
+// The record of a chunk's candidate bands, as the select reads it back.
+//   x: n0 | ntot << 8 | (b0 + 1) << 16 | (b1 + 1) << 24
+//   y: the chunk's largest score key mx
+//   z: 1 when the chunk dropped no key
+//   w: the largest key scale of the chunk (float bits)
+// Band 0 holds the keys within the first b0 + 1 bins below mx, band 1 those
+// of the bins after it up to b1; a bin is 2^17 key units (1/64 of a binade).
+__device__ __forceinline__ uint32_t band_edge(uint32_t mx, int b) {  // keys >= edge lie in bins 0..b
+  const uint64_t span = (uint64_t)(b + 1) << 17;
+  return b < 0 ? mx + 1u : span > mx ? 1u : mx - (uint32_t)span + 1u;
+}
+__device__ __forceinline__ uint32_t rec_n0(const u32x4_t& r) { return r[0] & 0xFFu; }
+__device__ __forceinline__ uint32_t rec_ntot(const u32x4_t& r) { return (r[0] >> 8) & 0xFFu; }
+__device__ __forceinline__ uint32_t rec_thi(const u32x4_t& r) { return band_edge(r[1], (int)((r[0] >> 16) & 0xFFu) - 1); }
+// keys the chunk dropped all lie below this (0: it dropped none)
+__device__ __forceinline__ uint32_t rec_tlo(const u32x4_t& r) {
+  return r[2] ? 0u : band_edge(r[1], (int)(r[0] >> 24) - 1);
+}
+
+// Candidate bands of one chunk (see the file comment), from the chunk's
+// score keys keys[0 .. n_slots) in LDS (0: no item at that slot; slot i is
+// item base + i; the array holds kScanChunk keys).  Band 0 is every key
+// within the first b0 + 1 bins below the chunk's largest key, b0 the last
+// bin whose running count stays within m0; band 1 the keys of the
+// following bins whose running count stays within the segment.  A chunk of
+// at most kSeg keys keeps them all (nothing dropped).  mx_lane / ks_lane:
+// each lane's largest score key and key scale bits seen (0 if none).  All
+// 256 threads call it; the keys must be in LDS (its first barrier publishes
+// them), and it may be called again right after it returns.
+__device__ __forceinline__ void emit_chunk(const IndexPass& p, int64_t row, int chunk, const uint32_t* keys,
+                                           int n_slots, int64_t base, uint32_t m0, uint32_t mx_lane,
+                                           uint32_t ks_lane, uint32_t* hist, uint32_t* sh) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint32_t mxw = wave_max_u32(mx_lane), ksw = wave_max_u32(ks_lane);
+  hist[t] = 0u;
+  if (lane == 0) {
+    sh[wave] = mxw;
+    sh[4 + wave] = ksw;
   }
-  if (base >= end) return;
+  __syncthreads();
+  const uint32_t mx = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+  const uint32_t ksm = max(max(sh[4], sh[5]), max(sh[6], sh[7]));
+  uint32_t k[8];
+  {
+    const uint4 a = reinterpret_cast<const uint4*>(keys)[2 * t], b = reinterpret_cast<const uint4*>(keys)[2 * t + 1];
+    const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k[j] = 8 * t + j < n_slots ? v[j] : 0u;
+  }
+  // bins of the distance below mx; bin 255 takes everything further down
+  // (counted by one lane per wave: it can hold most keys)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t d = (mx - k[j]) >> 17;
+    const bool near = k[j] != 0u && d < 255u;
+    const bool far = k[j] != 0u && d >= 255u;
+    if (near) atomicAdd(&hist[d], 1u);
+    const unsigned long long fb = __ballot(far);
+    if (fb && lane == (__ffsll((long long)fb) - 1)) atomicAdd(&hist[255], (uint32_t)__popcll(fb));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane l owns bins 4l .. 4l+3; e_j = keys in bins 0 .. 4l+j
+    const uint4 h4 = reinterpret_cast<const uint4*>(hist)[lane];
+    const uint32_t mine = h4.x + h4.y + h4.z + h4.w;
+    const uint32_t incl = wave_incl_add(mine);
+    const uint32_t n_valid = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t e0 = incl - mine + h4.x, e1 = e0 + h4.y, e2 = e1 + h4.z, e3 = incl;
+    // cum is non-decreasing: the bins with cum <= m form a prefix, b = its length - 1
+    // (bin 255 never counts: it is not a band bin)
+    const uint32_t last = lane == 63 ? 0u : 1u;
+    const uint32_t c0 = (e0 <= m0) + (e1 <= m0) + (e2 <= m0) + last * (e3 <= m0);
+    const uint32_t c1 = (e0 <= (uint32_t)kSeg) + (e1 <= (uint32_t)kSeg) + (e2 <= (uint32_t)kSeg) + last * (e3 <= (uint32_t)kSeg);
+    const int b0 = (int)__builtin_amdgcn_readlane((int)wave_incl_add(c0), 63) - 1;
+    const int b1 = (int)__builtin_amdgcn_readlane((int)wave_incl_add(c1), 63) - 1;
+    auto cum_at = [&](int b) -> uint32_t {
+      if (b < 0) return 0u;
+      const int j = b & 3;
+      const uint32_t e = j == 0 ? e0 : j == 1 ? e1 : j == 2 ? e2 : e3;
+      return (uint32_t)__builtin_amdgcn_readlane((int)e, b >> 2);
+    };
+    const uint32_t n0 = cum_at(b0), n1 = cum_at(b1);
+    if (lane == 0) {
+      const bool complete = n_valid <= (uint32_t)kSeg;
+      sh[8] = band_edge(mx, b0);               // band 0: keys >= this
+      sh[9] = complete ? 1u : band_edge(mx, b1);  // band 1: keys >= this (below band 0)
+      sh[10] = n0;
+      sh[11] = complete ? n_valid : n1;
+      sh[12] = 0u;
+      sh[13] = 0u;
+      sh[14] = n0 | ((complete ? n_valid : n1) << 8) | ((uint32_t)(b0 + 1) << 16) | ((uint32_t)(b1 + 1) << 24);
+      sh[15] = complete ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t thi = sh[8], tlo = sh[9], n0 = sh[10];
+  const __amdgpu_buffer_rsrc_t rseg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.seg_list + (row * p.max_chunks + chunk) * kSeg), 0, kSeg * 8, kRawBufferWord3);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (k[j] != 0u && k[j] >= tlo) {
+      const uint32_t slot = k[j] >= thi ? atomicAdd(&sh[12], 1u) : n0 + atomicAdd(&sh[13], 1u);
+      const uint64_t v = select_key(k[j], (uint32_t)(base + 8 * t + j));
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{(uint32_t)v, (uint32_t)(v >> 32)}, rseg, (int)(slot * 8), 0, 0);
+    }
+  }
+  if (t == 0) {
+    const __amdgpu_buffer_rsrc_t rinfo = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.chunk_info + row * p.max_chunks + chunk), 0, 16, kRawBufferWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{sh[14], mx, sh[15], ksm}, rinfo, 0, 0, 0);
+  }
+}
 
-  // candidates are staged in LDS and stored after the loop: a global store
-  // inside it would make every later wait for the key loads also wait for
-  // the store (one counter covers both on gfx9)
-  __shared__ uint32_t n_hit[NQ];
-  __shared__ uint64_t hits[NQ][kSeg];
-  if (threadIdx.x < NQ) n_hit[threadIdx.x] = 0;
+// Workgroup (one query row, chunk of row_chunk_items items): every key of
+// the chunk is scored and its score key staged in LDS, then emit_chunk cuts
+// the bands.  kDirect: item i is position i (flat keys or block keys); keys
+// and scales are read through buffer descriptors whose range ends at the
+// chunk's last item, so the hardware returns zeros past it and the loads
+// need no bounds branches.  Otherwise positions come from a block or
+// position list.
+// The LDS of one query's scan workgroup.
+struct ScanLds {
+  uint32_t skeys[kScanChunk];
+  uint32_t hist[256];
+  uint32_t sh[24];
+};
+
+// Chunk `chunk` of row `row` (base < end): score every item, stage the keys,
+// cut and write the bands.
+template <int U, bool kDirect, bool kPaged>
+__device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chunk, int64_t csize, int64_t base,
+                                           int64_t end, int64_t vis, int64_t n_items, ScanLds& L) {
+  static_assert(!kPaged || kDirect, "paged caches are read over direct items");
+  const int seq = row / p.n_q;
+  uint32_t* skeys = L.skeys;
+  uint32_t* hist = L.hist;
+  uint32_t* sh = L.sh;
   const int quarter = threadIdx.x & 3;
   const int sub = threadIdx.x >> 2;  // item within a 64-item step
-  half2_t q[NQ][kHI][8];
-  float w_mine[NQ], T0[NQ];  // loaded after the first keys: their loads overlap
+  half2_t q[kHI][8];
+  float w_mine;  // loaded after the first keys: their loads overlap
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
   // (used by the kDirect loads only.)  Paged: descriptors over the pool, and
@@ -545,7 +453,7 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
         B.ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
       } else {
         bool valid;
-        const int64_t pos = item_position(p, row0, item, end, vis[0], valid);
+        const int64_t pos = item_position(p, row, item, end, vis, valid);
         if (valid) {
           B.raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + pos * kDI + quarter * 16));
           B.ks[u] = sb[pos];
@@ -556,41 +464,31 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
       }
     }
   };
+  uint32_t mx_lane = 0u, ks_lane = 0u;  // running maxima (key scales are >= 0: their bits order them)
   auto score = [&](const Batch& B, int64_t it0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      half2_t kh[8];
-      key_f16(B.raw[u], kh);  // converted once for every query of the group
+      const float sc = quad_score(q, w_mine, B.raw[u], B.ks[u]);
       const int64_t item = it0 + u * 64 + sub;
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const float sc = quad_score_f16(q[i], w_mine[i], kh, B.ks[u]);
-        bool take = quarter == 0 && item < n_items[i] && item < base + csize && sc >= T0[i];
-        if constexpr (!kDirect) {
-          if (take) {  // invalid list entries never become candidates
-            bool valid;
-            (void)item_position(p, row0, item, end, vis[0], valid);
-            take = valid;
-          }
-        }
-        if (take) {
-          const uint32_t at = atomicAdd(&n_hit[i], 1u);
-          if (at < (uint32_t)kSeg) hits[i][at] = select_key(score_key(sc), (uint32_t)item);
+      bool valid = item < end;
+      if constexpr (!kDirect) {
+        if (valid) {  // invalid list entries never become candidates
+          bool ok;
+          (void)item_position(p, row, item, end, vis, ok);
+          valid = ok;
         }
       }
+      const uint32_t key = valid ? score_key(sc) : 0u;
+      mx_lane = max(mx_lane, key);
+      ks_lane = max(ks_lane, valid ? __float_as_uint(B.ks[u]) : 0u);
+      if (quarter == 0 && item < end) skeys[item - base] = key;
     }
   };
   constexpr int kStep = 64 * U;
   Batch A, Bb;
   int64_t it = base;
   load(A, it);
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int r = i < nq ? row0 + i : row0;
-    load_query_f16(p, r, quarter, q[i], w_mine[i]);
-    T0[i] = i < nq ? load_thresh(p, r) : INFINITY;
-  }
-  __syncthreads();  // n_hit is initialised
+  load_query_f16(p, row, quarter, q, w_mine);
   // kDirect loads past the chunk read zeros without touching memory, so they
   // are issued unconditionally and every path has the same loads in flight
   while (true) {
@@ -604,24 +502,24 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
     if (nxt2 >= end) break;
     it = nxt2;
   }
-  __syncthreads();
-  static_assert(kSeg <= 256, "one staged candidate per thread");
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    if (i >= nq || base >= n_items[i]) continue;
-    const int64_t r = row0 + i;
-    uint64_t* seg = p.seg_list + (r * p.max_chunks + chunk) * kSeg;
-    const uint32_t n = n_hit[i] < (uint32_t)kSeg ? n_hit[i] : (uint32_t)kSeg;
-    if (threadIdx.x < n) {
-      const uint64_t h = hits[i][threadIdx.x];
-      seg[threadIdx.x] = h;
-      // 16-bit bins: a row whose bins could overflow has more candidates
-      // than the select's fast path takes, which then ignores the histogram
-      const uint32_t b = hist_bin((uint32_t)(h >> 32), score_key(T0[i]));
-      atomicAdd(&p.hist[r * kHistWords + (b >> 1)], 1u << (16 * (b & 1u)));
-    }
-    if (threadIdx.x == 0) p.seg_count[r * p.max_chunks + chunk] = n_hit[i];
-  }
+  const int64_t nch = scan_chunk_count(n_items, csize);
+  emit_chunk(p, row, chunk, skeys, (int)(end - base), base, band0_size(n_items, csize, nch, p.k), mx_lane, ks_lane,
+             hist, sh);
+}
+
+template <int U, bool kDirect, bool kPaged>
+__global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, int n_groups) {
+  int row, chunk;
+  map_row_chunk(n_groups, per_row, row, chunk);
+  if (row >= n_groups) return;
+  const int64_t csize = row_chunk_items_of<kDirect>(p, row);  // shared by the rows of a sequence
+  const int64_t base = (int64_t)chunk * csize;
+  const int64_t vis = row_vis_positions(p, row);
+  const int64_t n_items = row_items_of<kDirect>(p, row, vis);
+  const int64_t end = base + csize < n_items ? base + csize : n_items;
+  if (base >= end) return;
+  __shared__ ScanLds L;
+  scan_chunk<U, kDirect, kPaged>(p, row, chunk, csize, base, end, vis, n_items, L);
 }
 
 // A pointer every lane holds the same value of, moved to scalar registers.
@@ -631,17 +529,23 @@ __device__ __forceinline__ void* uniform_ptr(const void* q) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
-// The scan on fp8 MFMA (direct items): each 32-key tile of the chunk is
-// scored against the 4 NQ heads of the NQ queries in one
-// v_mfma_scale_f32_32x32x64_f8f6f4 (heads as A rows, keys as B columns,
-// exact fp8 codes, unit scales, binary32 accumulation) instead of 16 fdot2
-// per key quarter and query on VALU.  Lane (l32, half) holds bytes
-// 32 half .. +32 of key l32 of the tile (B) and of head row l32 (A): row
-// 4 i + h is head h of query i.  The output gives the four head dots of query
-// i for key l32 in the lanes of half i % 2, registers 4 (i / 2) .. +3, so a
-// lane scores queries half, half + 2, ...  Wave w takes tiles w, w + 4, ...
-// of the chunk with kScanTiles tiles in flight.
+// The scan on fp8 MFMA (direct items) for NQ queries of one sequence: each
+// 32-key tile of the chunk is scored against the 4 NQ heads of the NQ
+// queries in one v_mfma_scale_f32_32x32x64_f8f6f4 (heads as A rows, keys as
+// B columns, exact fp8 codes, unit scales, binary32 accumulation in the
+// unit's own order: the select settles keys near the k-th by exact
+// rescoring) instead of 16 fdot2 per key quarter and query on VALU.  Lane
+// (l32, half) holds bytes 32 half .. +32 of key l32 of the tile (B) and of
+// head row l32 (A): row 4 i + h is head h of query i.  The output gives the
+// four head dots of query i for key l32 in the lanes of half i % 2,
+// registers 4 (i / 2) .. +3, so a lane scores queries half, half + 2, ...
+// Wave w takes tiles w, w + 4, ... of the chunk with kScanTiles tiles in
+// flight.  Every query's score keys are staged in LDS, then each query's
+// bands are cut by emit_chunk.
 constexpr int kScanTiles = 4;
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+constexpr uint32_t kMfmaUnitScales = 0x7F7F7F7Fu;  // E8M0 127 = 1.0 in every byte
 template <int NQ, bool kPaged>
 __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_row, int n_groups) {
   constexpr int NG = (NQ + 1) / 2;  // queries per lane, at most
@@ -654,18 +558,18 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
   const int nq = p.n_q - (row0 - seq * p.n_q) < NQ ? p.n_q - (row0 - seq * p.n_q) : NQ;
   const int64_t csize = row_chunk_items_of<true>(p, row0);  // shared by the rows of a sequence
   const int64_t base = (int64_t)chunk * csize;
-  int64_t lim_q[NQ], end = 0;  // items of query i in this chunk end at lim_q[i]
+  int64_t lim_q[NQ], nit_q[NQ], end = 0;  // items of query i in this chunk end at lim_q[i]
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    const int64_t n = i < nq ? row_items_of<true>(p, row0 + i, row_vis_positions(p, row0 + i)) : 0;
-    lim_q[i] = base + csize < n ? base + csize : n;
+    nit_q[i] = i < nq ? row_items_of<true>(p, row0 + i, row_vis_positions(p, row0 + i)) : 0;
+    lim_q[i] = base + csize < nit_q[i] ? base + csize : nit_q[i];
     end = lim_q[i] > end ? lim_q[i] : end;
   }
   if (base >= end) return;
 
-  __shared__ uint32_t n_hit[NQ];
-  __shared__ uint64_t hits[NQ][kSeg];
-  if (threadIdx.x < NQ) n_hit[threadIdx.x] = 0;
+  __shared__ uint32_t skeys[NQ][kScanChunk];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[24];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
@@ -710,9 +614,9 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
     T.hi = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 32 * half + 16, 0, kLoadNonTemporal);
   };
   // A operand: head row l32 of query l32 / 4 (rows past the group's queries
-  // read zeros past the descriptor).  These loads, the weights and the
-  // thresholds go out before the tiles: every load is unconditional, so the
-  // waits for them inside the tile loop do not wait for tile data.
+  // read zeros past the descriptor).  These loads and the weights go out
+  // before the tiles: every load is unconditional, so the waits for them
+  // inside the tile loop do not wait for tile data.
   v8i_t A;
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -722,16 +626,13 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
     const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
     A = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
-  // this lane's queries i = 2 g + half: head weights, threshold, item limit
-  float wq[NG][kHI], t0q[NG];
+  // this lane's queries i = 2 g + half: head weights and item limit
+  float wq[NG][kHI];
   int64_t limq[NG];
-  float T0[NQ];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) T0[i] = load_thresh(p, row0 + (i < nq ? i : 0));
   {
     const bool has_w = p.idx_w != nullptr;
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(has_w ? p.idx_w + (int64_t)row0 * kHI : p.thresh), 0, has_w ? nq * kHI * 4 : 0, kRawBufferWord3);
+        (void*)(has_w ? p.idx_w + (int64_t)row0 * kHI : nullptr), 0, has_w ? nq * kHI * 4 : 0, kRawBufferWord3);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int i = 2 * g + half;
@@ -748,38 +649,40 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
 #pragma unroll
   for (int s = 0; s < kScanTiles; ++s) load_tile(T[s], s);
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) T0[i] = i < nq ? T0[i] : INFINITY;
-#pragma unroll
   for (int g = 0; g < NG; ++g) {
     const int ilo = 2 * g, ihi = 2 * g + 1 < NQ ? 2 * g + 1 : 2 * g;
-    t0q[g] = half ? (2 * g + 1 < NQ ? T0[ihi] : INFINITY) : T0[ilo];
-    limq[g] = half ? (2 * g + 1 < NQ ? lim_q[ihi] : 0) : lim_q[ilo];
+    // (arithmetic, not a select: a select of the two becomes an indexed
+    // load of lim_q through scratch)
+    const int64_t la = lim_q[ilo], lb = 2 * g + 1 < NQ ? lim_q[ihi] : 0;
+    limq[g] = la + (int64_t)half * (lb - la);
   }
-  __syncthreads();  // n_hit is initialised
-
+  uint32_t mxq[NG], ks_lane = 0u;  // running maxima: this lane's queries' score keys, key scales
+#pragma unroll
+  for (int g = 0; g < NG; ++g) mxq[g] = 0u;
   auto score_tile = [&](const Tile& Tt, int m) {
     const v8i_t Bop = v8i_t{(int)Tt.lo[0], (int)Tt.lo[1], (int)Tt.lo[2], (int)Tt.lo[3],
                             (int)Tt.hi[0], (int)Tt.hi[1], (int)Tt.hi[2], (int)Tt.hi[3]};
     v16f_t acc = {};
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bop, acc, 0, 0, 0, kMfmaUnitScales, 0,
                                                           kMfmaUnitScales);
-    // the whole wave runs the MFMA (uniform control flow, see the sample)
+    // the MFMA reads every lane's operands, so it must run with the whole
+    // wave active: the empty asm pins it here, in uniform control flow
     asm volatile("" ::"v"(acc));
     const int64_t item = base + 32 * (int64_t)(wave + 4 * m) + l32;
+    if (item < end) ks_lane = max(ks_lane, __float_as_uint(Tt.ks));
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const float sc = Tt.ks * (wq[g][0] * fmaxf(acc[4 * g], 0.0f) + wq[g][1] * fmaxf(acc[4 * g + 1], 0.0f) +
                                 wq[g][2] * fmaxf(acc[4 * g + 2], 0.0f) + wq[g][3] * fmaxf(acc[4 * g + 3], 0.0f));
-      if (item < limq[g] && sc >= t0q[g]) {
-        const int i = 2 * g + half;
-        const uint32_t at = atomicAdd(&n_hit[i], 1u);
-        if (at < (uint32_t)kSeg) hits[i][at] = select_key(score_key(sc), (uint32_t)item);
-      }
+      const int i = 2 * g + half;
+      const uint32_t key = item < limq[g] ? score_key(sc) : 0u;
+      mxq[g] = max(mxq[g], key);
+      if (i < NQ && item < end) skeys[i][item - base] = key;
     }
   };
   // whole groups of kScanTiles tiles, with no branch between the loads (a
-  // tile past the chunk reads zeros and its items fail the item limit), so
-  // each score waits only for its own tile
+  // tile past the chunk reads zeros and its items stay past the chunk's
+  // end), so each score waits only for its own tile
   for (int m0 = 0; m0 < my_tiles; m0 += kScanTiles) {
 #pragma unroll
     for (int s = 0; s < kScanTiles; ++s) {
@@ -787,20 +690,15 @@ __global__ __launch_bounds__(256) void k_index_scan_mfma(IndexPass p, int per_ro
       load_tile(T[s], m0 + s + kScanTiles);
     }
   }
-  __syncthreads();
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    if (i >= nq || base >= lim_q[i]) continue;
-    const int64_t r = row0 + i;
-    uint64_t* seg = p.seg_list + (r * p.max_chunks + chunk) * kSeg;
-    const uint32_t n = n_hit[i] < (uint32_t)kSeg ? n_hit[i] : (uint32_t)kSeg;
-    if (threadIdx.x < n) {
-      const uint64_t h = hits[i][threadIdx.x];
-      seg[threadIdx.x] = h;
-      const uint32_t b = hist_bin((uint32_t)(h >> 32), score_key(T0[i]));
-      atomicAdd(&p.hist[r * kHistWords + (b >> 1)], 1u << (16 * (b & 1u)));
+    if (i < nq && base < lim_q[i]) {  // (uniform)
+      const int64_t nch = scan_chunk_count(nit_q[i], csize);
+      // query i's maximum lives in the lanes of half i % 2, slot i / 2
+      const uint32_t mx_lane = half == (i & 1) ? mxq[i >> 1] : 0u;
+      emit_chunk(p, row0 + i, chunk, skeys[i], (int)(lim_q[i] - base), base,
+                 band0_size(nit_q[i], csize, nch, p.k), mx_lane, ks_lane, hist, sh);
     }
-    if (threadIdx.x == 0) p.seg_count[r * p.max_chunks + chunk] = n_hit[i];
   }
 }
 
@@ -817,100 +715,271 @@ __device__ __forceinline__ uint32_t bitmap_slot(uint32_t w) { return (w & 15u) *
 static_assert(kBitmapItems / 32 == 16 * 256, "bitmap words: 16 per select thread");
 static_assert(kBitmapItems / 32 * 4 <= 256 * 16 * 8, "the word prefixes fit in the candidate array");
 
-// kPer candidates per thread, 256 kPer in all: 16 serves k <= 1,024 (about
-// 2.5 k candidates reach the sampled threshold), 32 the 2,048-block stage
+// The query of a row for exact rescoring and the error bound: its 256 code
+// values as float64 in LDS (qd[c][h], channel c of head h) and the head
+// weights (qw); returns sum_h |w_h| sum_c |q_hc| in every lane.  Every wave
+// loads the 256 bytes itself (wave 0 stores them).
+__device__ __forceinline__ float load_query_codes(const IndexPass& p, int row, float* qw, double (*qd)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.idx_q + (int64_t)row * kHI * kDI), 0, kHI * kDI, kRawBufferWord3);
+  const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, 0, 0);
+  float w = 1.0f;
+  if (p.idx_w) {
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.idx_w + (int64_t)row * kHI), 0, 4 * kHI, kRawBufferWord3);
+    w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, 4 * (lane >> 4), 0, 0));
+  }
+  if (wave == 0) {
+    if ((lane & 15) == 0) qw[lane >> 4] = w;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) qd[4 * (lane & 15) + b][lane >> 4] = (double)e4m3_value((c >> (8 * b)) & 0xFFu);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a += e4m3_mag((c >> (8 * j)) & 0x7Fu);  // exact (integers of 2^-9)
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) a += __shfl_xor(a, d, 64);  // the head's L1 norm, exact
+  float cw = fabsf(w) * a;
+  cw += __shfl_xor(cw, 16, 64);
+  cw += __shfl_xor(cw, 32, 64);
+  return cw;
+}
+
+// Loads of one key's 64 code bytes and scale (position pos of row's
+// sequence) into registers.
+__device__ __forceinline__ void load_key_row(const IndexPass& p, int row, int64_t pos, u32x4_t (&raw)[4], float& ks) {
+  const int seq = row / p.n_q;
+  if (p.pm.pages) {
+    const uint32_t e = paged_entry_at(p.pm, seq, pos);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.k8, 0, (int)(p.pm.pool * kDI), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.kscale, 0, (int)(p.pm.pool * 4), kRawBufferWord3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + 16 * j, 0, 0);
+    ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
+  } else {
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(p.k8 + ((int64_t)seq * p.k_stride + pos) * kDI);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = kp[j];
+    ks = p.kscale[(int64_t)seq * p.k_stride + pos];
+  }
+}
+
+// Exact score of item `item` of `row`, float64, in the oracle's order of
+// operations: d_h = sum_c q_hc k_c exactly (every E4M3 value is n 2^-9 with
+// |n| < 2^18, so each product and every partial sum of 64 is an integer
+// multiple of 2^-18 below 2^42: exact in float64, in any order);
+// p_h = max(0, d_h) * w_h; s = ks * (((p_0 + p_1) + p_2) + p_3).  The four
+// lanes of a quad take the four heads (lane quarter h); every lane of the
+// quad returns s.  Lanes with valid == false return 0 and load nothing
+// (whole quads agree on valid).
+__device__ __forceinline__ double exact_score(const IndexPass& p, int row, uint32_t item, bool valid,
+                                              const double (*qd)[4], const float* qw) {
+#pragma clang fp contract(off)
+  const int h = threadIdx.x & 3;
+  double s = 0.0;
+  u32x4_t raw[4] = {};
+  float ks = 0.0f;
+  if (valid) load_key_row(p, row, item_to_position(p, row, item), raw, ks);
+  double d = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t kw = raw[j >> 2][j & 3];
+    // fp8 -> f32 exactly, two codes per convert
+    const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kw, 1.0f, false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kw, 1.0f, true);
+    const float kv[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) d = __builtin_fma(qd[4 * j + b][h], (double)kv[b], d);  // exact
+  }
+  const double ph = (d > 0.0 ? d : 0.0) * (double)qw[h];
+  const double p0 = __shfl(ph, (threadIdx.x & ~3) | 0, 64), p1 = __shfl(ph, (threadIdx.x & ~3) | 1, 64);
+  const double p2 = __shfl(ph, (threadIdx.x & ~3) | 2, 64), p3 = __shfl(ph, (threadIdx.x & ~3) | 3, 64);
+  s = (double)ks * (((p0 + p1) + p2) + p3);
+  return valid ? s : 0.0;
+}
+
+// Exact ranking of the near-tie band: items bitem[0 .. nb) (nb <= kBandMax)
+// are rescored exactly and the r best by (score descending, position
+// ascending) are flagged in bwin.  The items of a band are distinct, and
+// items ascend with positions (lists are ascending, kept blocks too), so
+// position ties are broken by item.
+__device__ __forceinline__ void rank_band(const IndexPass& p, int row, uint32_t nb, uint32_t r, const uint32_t* bitem,
+                                          double* bscore, uint32_t* bwin, const double (*qd)[4], const float* qw) {
+  const int t = threadIdx.x;
+  for (uint32_t m0 = 0; m0 < nb; m0 += 64) {
+    const uint32_t m = m0 + (t >> 2);
+    const bool valid = m < nb;
+    const double s = exact_score(p, row, valid ? bitem[m] : 0u, valid, qd, qw);
+    if (valid && (t & 3) == 0) bscore[m] = s;
+  }
+  __syncthreads();
+  for (uint32_t m = t; m < nb; m += 256) {
+    const double sm = bscore[m];
+    const uint32_t im = bitem[m];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < nb; ++j) {
+      const double sj = bscore[j];
+      rank += (sj > sm || (sj == sm && bitem[j] < im)) ? 1u : 0u;
+    }
+    bwin[m] = rank < r ? 1u : 0u;
+  }
+  __syncthreads();
+}
+
+// Score-key bounds of the near-tie band around the k-th key: keys above hi
+// win for sure, keys below lo lose for sure (each score is within delta of
+// the exact one, so a key more than 2 delta above the k-th has at most
+// k - 1 keys above it exactly, and one more than 2 delta below has at least
+// k).  Rounded outwards.
+__device__ __forceinline__ void band_bounds(uint64_t kth, float delta, uint32_t& lo, uint32_t& hi) {
+  const float s = key_to_score((uint32_t)(kth >> 32));
+  const float d2 = 2.0f * delta + kErrTail * fabsf(s) * 2.0f;
+  const float up = __builtin_fmaf(d2, 1.0f + 0x1p-12f, s);
+  const float dn = __builtin_fmaf(-d2, 1.0f + 0x1p-12f, s);
+  hi = score_key(up);
+  hi = hi < 0xFFFFFFFFu ? hi + 1u : hi;   // one ulp outwards for the rounding of the fma
+  lo = score_key(dn);
+  lo = lo > 1u ? lo - 1u : 1u;
+}
+
+// The select's LDS: kPer candidates per thread, room for the segment
+// starts of kChunks chunks and kWin winners.  The k-th key's histogram
+// (2,048 words) shares the bitmap's memory: it is done with before the
+// bitmap is cleared for the winners.
+template <int kPer, int kChunks, int kWin>
+struct SelLds {
+  uint64_t lc[256 * kPer];               // candidates; then the near-tie band
+  uint32_t bitmap[kBitmapItems / 32];    // winner bitmap; first the histogram
+  uint32_t win[kWin];
+  uint32_t seg_start[kChunks + 1];
+  uint32_t h256[256];
+  uint32_t wsum[4];
+  uint32_t sh3[3];
+  float qw[4];
+  double qd[64][4];
+  uint64_t bin_keys[64];
+  uint64_t sh_kth;
+  uint32_t sh_need, sh_binn, sh_nb, sh_nbge;
+  uint32_t sh_red[8];
+};
 template <int kPer>
-__device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
+using SelLdsFull = SelLds<kPer, kMaxChunks, CSA2_MAX_K>;
+
+// kPer candidates per thread, 256 kPer in all: 16 for k <= 1,024, 32 for
+// the 2,048-block stage and for rows of more than 128 chunks.
+template <int kPer, class Lds>
+__device__ __forceinline__ void select_row(const IndexPass& p, const int row, Lds& S) {
   constexpr int kSelCap = 256 * kPer;
   const int t = threadIdx.x, quarter = t & 3;
   const int wave = t >> 6, lane = t & 63;
-  // the loads that need only the row go out first: the row's candidate
-  // histogram (filled by the scan; every wave holds all of it, lane l the
-  // words 16 l .. 16 l + 15, bins 32 l .. 32 l + 31) and the chunk counts
-  // (every row has room for 128; chunks past the row's last are masked
-  // below)
-  uint32_t hw[16];
-  {
-    const uint4* h4 = reinterpret_cast<const uint4*>(p.hist + (int64_t)row * kHistWords) + 4 * lane;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 a = h4[i];
-      hw[4 * i] = a.x;
-      hw[4 * i + 1] = a.y;
-      hw[4 * i + 2] = a.z;
-      hw[4 * i + 3] = a.w;
-    }
-  }
-  const uint32_t* cnt_row = p.seg_count + (int64_t)row * p.max_chunks;
-  const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
-  constexpr int kSpecCh = kPer <= 16 ? kSpecChunks : 2 * kSpecChunks;  // chunks gathered in one round trip
-  const uint32_t cnt_lane = cnt_row[lane];
-  const uint32_t cnt_lane_b = kSpecCh > 64 ? cnt_row[lane + 64] : 0u;  // (every row has room for 128)
   const int seq = row / p.n_q;
   const int64_t vis = row_vis_positions(p, row);
   const int64_t n_items = row_items(p, row, vis);
   const int64_t csize = row_chunk_items(p, row);
   const int nch = (int)scan_chunk_count(n_items, csize);
   const uint32_t k = (uint32_t)p.k;
+  const u32x4_t* info_row = p.chunk_info + (int64_t)row * p.max_chunks;
+  const uint64_t* segs = p.seg_list + (int64_t)row * p.max_chunks * kSeg;
 
-  __shared__ uint32_t seg_start[kMaxChunks + 1];
-  __shared__ uint64_t lc[kSelCap];
-  __shared__ uint32_t bitmap[kBitmapItems / 32];
-  __shared__ uint32_t win[CSA2_MAX_K];
-  __shared__ uint32_t h256[256];
-  __shared__ uint32_t h2048[2048];
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t sh3[3];
-  __shared__ uint64_t bin_keys[64];
-  __shared__ uint32_t hsrc[4][16];
-  __shared__ uint64_t sh_kth;
-  __shared__ uint32_t sh_need, sh_binn;
+  static_assert(sizeof(S.lc) == kSelCap * 8, "candidate room");
+  constexpr uint32_t kWinCap = sizeof(S.win) / 4;
+  uint32_t* seg_start = S.seg_start;
+  uint64_t* lc = S.lc;
+  uint32_t* bitmap = S.bitmap;
+  uint32_t* win = S.win;
+  uint32_t* h256 = S.h256;
+  uint32_t* h2048 = S.bitmap;  // (the histogram is done before the bitmap is cleared)
+  uint32_t* wsum = S.wsum;
+  uint32_t* sh3 = S.sh3;
+  float* qw = S.qw;
+  double (*qd)[4] = S.qd;
+  uint64_t* bin_keys = S.bin_keys;
+  uint64_t& sh_kth = S.sh_kth;
+  uint32_t &sh_need = S.sh_need, &sh_binn = S.sh_binn, &sh_nb = S.sh_nb, &sh_nbge = S.sh_nbge;
+  uint32_t* sh_red = S.sh_red;
+  auto info_at = [&](int c) __attribute__((always_inline)) -> u32x4_t { return info_row[c]; };
+  auto seg_at = [&](int c, uint32_t i) __attribute__((always_inline)) -> uint64_t {
+    return segs[(int64_t)c * kSeg + i];
+  };
+  auto seg2_at = [&](int c, uint32_t i) __attribute__((always_inline)) -> uint4 {  // slots i, i + 1
+    return *reinterpret_cast<const uint4*>(segs + (int64_t)c * kSeg + i);
+  };
+  // the near-tie band (in lc once the candidates are in registers)
+  constexpr uint32_t kBandCap = kSelCap / 2 < kBandMax ? kSelCap / 2 : kBandMax;  // 16 bytes a band key
+  uint32_t* bitem = reinterpret_cast<uint32_t*>(lc);
+  uint32_t* bwin = bitem + kBandCap;
+  double* bscore = reinterpret_cast<double*>(lc) + kBandCap;
 
-  // Rows of at most kSpecCh chunks (64 for k <= 1,024, 128 for the 2,048-block
-  // stage) load the first kSpecSlots slots of every segment together with
-  // the counts (one memory round trip), two segments per wave instruction:
-  // wave w takes chunks 2 (w + 4 j) + lane / 32, lane % 32 their slots
-  // 2 (lane % 32) and the next.  Segments hold about 40 candidates on
-  // average; fuller ones load the rest afterwards.  Each wave holds the
-  // counts of chunks l and l + 64 in lane l, so its own prefix sums give
-  // every chunk's start without a workgroup scan.
+  // Rows of at most kSpecCh chunks load every chunk's record and the first
+  // slots of every segment (band 0 fits: 32 slots when band 0 holds at most
+  // 32 keys, else 64) in one round trip: wave w takes chunks
+  // G (w + 4 j) + lane / (64 / G), G chunks per wave instruction, each lane
+  // two slots.  Every wave holds the records of chunks l and l + 64 in lane
+  // l, so its own prefix sums give every chunk's band-0 start and its own
+  // ballots decide which chunks need band 1, with no workgroup barrier.
+  constexpr int kSpecCh = kPer <= 16 ? kSpecChunks : 2 * kSpecChunks;
   const bool spec = nch <= kSpecCh;
+  const bool slots32 = band0_size(n_items, csize, nch, (int)k) <= 32u;
+  u32x4_t ia = u32x4_t{0, 0, 0, 0}, ib = u32x4_t{0, 0, 0, 0};
   uint4 sv[kSpecCh / 8];
-  uint32_t cnt_a = 0, cnt_b = 0, start_a = 0, start_b = 0;
-  uint32_t total;
-  bool over = false, more = false;
   if (spec) {
-    cnt_a = lane < nch ? cnt_lane : 0u;
-    cnt_b = lane + 64 < nch ? cnt_lane_b : 0u;
+    if (lane < nch) ia = info_at(lane);
+    if (kSpecCh > 64 && lane + 64 < nch) ib = info_at(lane + 64);
+    if (slots32) {  // 4 chunks of 32 slots per instruction
 #pragma unroll
-    for (int j = 0; j < kSpecCh / 8; ++j) {
-      const int ch = 2 * (wave + 4 * j) + (lane >> 5);
-      sv[j] = ch < nch ? *reinterpret_cast<const uint4*>(segs + (int64_t)ch * kSeg + 2 * (lane & 31))
-                       : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < kSpecCh / 16; ++j) {
+        const int ch = 4 * (wave + 4 * j) + (lane >> 4);
+        sv[j] = ch < nch ? seg2_at(ch, 2 * (lane & 15)) : make_uint4(0, 0, 0, 0);
+      }
+    } else {  // 2 chunks of 64 slots per instruction
+#pragma unroll
+      for (int j = 0; j < kSpecCh / 8; ++j) {
+        const int ch = 2 * (wave + 4 * j) + (lane >> 5);
+        sv[j] = ch < nch ? seg2_at(ch, 2 * (lane & 31)) : make_uint4(0, 0, 0, 0);
+      }
     }
-    const uint32_t incl_a = wave_incl_add(cnt_a);
-    const uint32_t tot_a = (uint32_t)__shfl((int)incl_a, 63, 64);
-    start_a = incl_a - cnt_a;
+  }
+  const float cq = load_query_codes(p, row, qw, qd);
+  // band-0 counts and starts, the row's largest key and key scale
+  uint32_t total, rowmax = 0u, ksm = 0u;
+  if (spec) {
+    const uint32_t na = rec_n0(ia), nb = rec_n0(ib);
+    rowmax = wave_max_u32(max(ia[1], ib[1]));
+    ksm = wave_max_u32(max(ia[3], ib[3]));
+    const uint32_t incl_a = wave_incl_add(na);
+    const uint32_t tot_a = (uint32_t)__builtin_amdgcn_readlane((int)incl_a, 63);
     total = tot_a;
+    if (wave == 0) seg_start[lane] = incl_a - na;
     if constexpr (kSpecCh > 64) {
-      const uint32_t incl_b = wave_incl_add(cnt_b);
-      start_b = tot_a + incl_b - cnt_b;
-      total = tot_a + (uint32_t)__shfl((int)incl_b, 63, 64);
+      const uint32_t incl_b = wave_incl_add(nb);
+      if (wave == 0) seg_start[lane + 64] = tot_a + incl_b - nb;
+      total = tot_a + (uint32_t)__builtin_amdgcn_readlane((int)incl_b, 63);
     }
-    over = __any(cnt_a > (uint32_t)kSeg || cnt_b > (uint32_t)kSeg);
-    more = __any(cnt_a > (uint32_t)kSpecSlots || cnt_b > (uint32_t)kSpecSlots);
+    if (wave == 0 && lane == 0) seg_start[nch] = total;
   } else {
-    // segment counts: thread t owns chunks 16t .. 16t+15
+    // thread t owns chunks 16t .. 16t+15 (a row has at most 4,096)
     uint32_t c[16], local = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int ch = 16 * t + j;
-      c[j] = ch < nch ? cnt_row[ch] : 0u;
-      over |= c[j] > (uint32_t)kSeg;
+      const u32x4_t r = ch < nch ? info_at(ch) : u32x4_t{0, 0, 0, 0};
+      c[j] = rec_n0(r);
+      rowmax = max(rowmax, r[1]);
+      ksm = max(ksm, r[3]);
       local += c[j];
     }
-    over = __syncthreads_or(over);
-    uint32_t run = block_incl_scan_256(local, wsum, total) - local;
+    rowmax = wave_max_u32(rowmax);
+    ksm = wave_max_u32(ksm);
+    if (lane == 0) {
+      sh_red[wave] = rowmax;
+      sh_red[4 + wave] = ksm;
+    }
+    uint32_t run = block_incl_scan_256(local, wsum, total) - local;  // (its barriers publish sh_red)
+    rowmax = max(max(sh_red[0], sh_red[1]), max(sh_red[2], sh_red[3]));
+    ksm = max(max(sh_red[4], sh_red[5]), max(sh_red[6], sh_red[7]));
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int ch = 16 * t + j;
@@ -918,143 +987,123 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
       run += c[j];
     }
     if (t == 0) seg_start[nch] = total;
-    __syncthreads();
   }
+  const float delta = (p.mfma_scores ? kErrMfma : kErrValu) * cq * 448.0f * __uint_as_float(ksm);
 
-  const float T0 = n_items > 0 ? load_thresh(p, row) : -INFINITY;  // written by the sample pass
-  const bool fast = !over && total <= (uint32_t)kSelCap && (total >= k || T0 == -INFINITY);
+  bool fast = total <= (uint32_t)kSelCap;
   uint32_t n_win = 0;
+  const bool use_bitmap = n_items <= (int64_t)kBitmapItems;
   if (fast) {
-    if (t == 0) {  // (ordered before their users by the barrier after the gather)
-      sh3[0] = 0xFFFFFFFFu;
+    for (int i = t; i < 2048; i += 256) h2048[i] = 0u;
+    if (t == 0) {
+      sh_nb = 0;
+      sh_nbge = 0;
       sh_binn = 0;
+      sh_need = 0;
     }
-    const bool use_bitmap = n_items <= (int64_t)kBitmapItems;
-    if (use_bitmap) {
-      uint4* bm4 = reinterpret_cast<uint4*>(bitmap);
-      for (int i = t; i < kBitmapItems / 128; i += 256) bm4[i] = make_uint4(0, 0, 0, 0);
-    }
-    if (spec) {  // the slots loaded above: keep the first count of each chunk
-      // count and start of chunk ch (< 128; every lane takes both shuffles)
-      auto chunk_of = [&](int ch, uint32_t& n, uint32_t& base) {
-        const int l = ch & 63;
-        const uint32_t na = (uint32_t)__shfl((int)cnt_a, l, 64), sa = (uint32_t)__shfl((int)start_a, l, 64);
-        uint32_t nb = 0, sb = 0;
-        if constexpr (kSpecCh > 64) {
-          nb = (uint32_t)__shfl((int)cnt_b, l, 64);
-          sb = (uint32_t)__shfl((int)start_b, l, 64);
-        }
-        n = ch < 64 ? na : nb;
-        base = ch < 64 ? sa : sb;
-      };
+    __syncthreads();  // seg_start, qd, qw
+    // band 0 into lc
+    if (spec) {
+      if (slots32) {
 #pragma unroll
-      for (int j = 0; j < kSpecCh / 8; ++j) {
-        const int ch = 2 * (wave + 4 * j) + (lane >> 5);
-        uint32_t n, base;
-        chunk_of(ch, n, base);
-        const uint32_t s0 = 2u * (lane & 31);
-        if (ch < nch) {
-          if (s0 < n) lc[base + s0] = ((uint64_t)sv[j].y << 32) | sv[j].x;
-          if (s0 + 1u < n) lc[base + s0 + 1] = ((uint64_t)sv[j].w << 32) | sv[j].z;
+        for (int j = 0; j < kSpecCh / 16; ++j) {
+          const int ch = 4 * (wave + 4 * j) + (lane >> 4);
+          if (ch < nch) {
+            const uint32_t b = seg_start[ch], n = seg_start[ch + 1] - b;
+            const uint32_t s0 = 2u * (lane & 15);
+            if (s0 < n) lc[b + s0] = ((uint64_t)sv[j].y << 32) | sv[j].x;
+            if (s0 + 1u < n) lc[b + s0 + 1] = ((uint64_t)sv[j].w << 32) | sv[j].z;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSpecCh / 8; ++j) {
+          const int ch = 2 * (wave + 4 * j) + (lane >> 5);
+          if (ch < nch) {
+            const uint32_t b = seg_start[ch], n = seg_start[ch + 1] - b;
+            const uint32_t s0 = 2u * (lane & 31);
+            if (s0 < n) lc[b + s0] = ((uint64_t)sv[j].y << 32) | sv[j].x;
+            if (s0 + 1u < n) lc[b + s0 + 1] = ((uint64_t)sv[j].w << 32) | sv[j].z;
+          }
         }
       }
-      if (more) {  // the slots past kSpecSlots of fuller segments
-        for (int ch = wave; ch < nch; ch += 4) {
-          uint32_t n, base;
-          chunk_of(ch, n, base);
-          const uint32_t i = kSpecSlots + lane;
-          if (i < n) lc[base + i] = segs[(int64_t)ch * kSeg + i];
+    } else {
+      // wave w copies chunks w, w + 4, ..., eight at a time (loads first)
+      for (int c0 = wave; c0 < nch; c0 += 32) {
+        uint64_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int ch = c0 + 4 * j;
+          const uint32_t n = ch < nch ? seg_start[ch + 1] - seg_start[ch] : 0u;
+          v[j] = (uint32_t)lane < n ? seg_at(ch, lane) : 0ull;
         }
-      }
-    }
-    // otherwise gather the segments: wave w copies chunks w, w + 4, ...,
-    // eight chunks (up to 16 independent loads per lane) at a time
-    for (int c0 = spec ? nch : wave; c0 < nch; c0 += 32) {
-      uint64_t v[8][2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ch = c0 + 4 * j;
-        const uint32_t n = ch < nch ? seg_start[ch + 1] - seg_start[ch] : 0u;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t i = lane + 64 * h;
-          v[j][h] = i < n ? segs[(int64_t)ch * kSeg + i] : 0ull;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ch = c0 + 4 * j;
-        const uint32_t n = ch < nch ? seg_start[ch + 1] - seg_start[ch] : 0u;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t i = lane + 64 * h;
-          if (i < n) lc[seg_start[ch] + i] = v[j][h];
+        for (int j = 0; j < 8; ++j) {
+          const int ch = c0 + 4 * j;
+          const uint32_t n = ch < nch ? seg_start[ch + 1] - seg_start[ch] : 0u;
+          if ((uint32_t)lane < n) lc[seg_start[ch] + lane] = v[j];
         }
       }
     }
     __syncthreads();
-    // candidates into registers: thread t holds lc[t + 256 i]
-    // (the passes over the keys stop after the last slot any thread fills:
-    // a row has about 1.5 k candidates in 256 kPer slots)
-    const int nslots = (int)((total + 255u) / 256u);
     uint64_t key[kPer];
+    auto to_regs = [&](uint32_t tot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const uint32_t g = t + 256 * i;
-      key[i] = i < nslots && g < total ? lc[g] : 0ull;  // 0 is below every candidate key
-    }
-    uint64_t kth = 1ull;
-    if (total > k) {
-      // the bin holding the k-th largest key, from the histogram: bins above
-      // it hold fewer than k keys, with it at least k.  When it is a proper
-      // bin with a few keys, the k-th key is ranked among those alone;
-      // otherwise (the top bin, which also takes scores far above T0) the
-      // radix over every candidate decides.  Every wave finds the bin in its
-      // own copy of the histogram and ranks the bin's keys itself, so the
-      // only barrier is the one that publishes those keys.
-      uint32_t hl = 0;
+      for (int i = 0; i < kPer; ++i) {
+        const uint32_t g = t + 256 * i;
+        key[i] = g < tot ? lc[g] : 0ull;  // 0 is below every candidate key
+      }
+    };
+    // the k-th largest key (more than k keys): its bin in a histogram of
+    // the distance below the row's largest key (2,048 bins of 2^13 key
+    // units, 1/1024 of a binade; the last takes the rest), then its rank
+    // among that bin's few keys; a radix over every key when the bin is the
+    // last one or holds more than 64
+    auto kth_of = [&](bool zeroed) __attribute__((always_inline)) -> uint64_t {
+      if (!zeroed) {
+        for (int i = t; i < 2048; i += 256) h2048[i] = 0u;
+        if (t == 0) sh_binn = 0;
+        __syncthreads();
+      }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) hl += (hw[j] & 0xFFFFu) + (hw[j] >> 16);
-      const uint32_t hincl = wave_incl_add(hl);
-      const uint32_t htot = (uint32_t)__builtin_amdgcn_readlane((int)hincl, 63);
-      const uint32_t above_l = htot - hincl;  // keys in bins above 32 lane + 31
-      // the lane whose 32 bins hold the k-th key, then (its words through
-      // LDS, one bin per lane) the bin
-      const unsigned long long hit = __ballot(htot == total && above_l < k && above_l + hl >= k);
-      uint32_t kb_bin = 0xFFFFFFFFu, need = 0, in_bin = 0;
-      if (hit) {
-        const int src = __ffsll((long long)hit) - 1;
-        const uint32_t above_src = (uint32_t)__builtin_amdgcn_readlane((int)above_l, src);
-        if (lane == src) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) hsrc[wave][i] = hw[i];
-        }
-        __builtin_amdgcn_wave_barrier();
-        const uint32_t wj = hsrc[wave][(lane & 31) >> 1];
-        const uint32_t c = lane < 32 ? (wj >> (16 * (lane & 1))) & 0xFFFFu : 0u;
-        const uint32_t ci = wave_incl_add(c);
-        const uint32_t above_j = above_src + (uint32_t)__builtin_amdgcn_readlane((int)ci, 31) - ci;
-        const unsigned long long hj = __ballot(lane < 32 && above_j < k && above_j + c >= k);
-        if (hj) {
-          const int j = __ffsll((long long)hj) - 1;
-          kb_bin = 32 * src + j;
-          need = k - (uint32_t)__builtin_amdgcn_readlane((int)above_j, j);
-          in_bin = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
+      for (int i = 0; i < kPer; ++i) {
+        if (key[i] != 0ull) {
+          const uint32_t d = (rowmax - (uint32_t)(key[i] >> 32)) >> 13;
+          atomicAdd(&h2048[d < 2047u ? d : 2047u], 1u);
         }
       }
-      bool ranked = false;
-      if (kb_bin < (uint32_t)(kHistBins - 1) && in_bin <= 64u) {
-        // the bin's keys into LDS, then lane l ranks key l among them with
-        // register reads of the other lanes' keys
-        const uint32_t t0key = score_key(T0);
+      __syncthreads();
+      uint32_t hb[8], local = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hb[j] = h2048[8 * t + j];
+        local += hb[j];
+      }
+      uint32_t tot;
+      uint32_t run = block_incl_scan_256(local, wsum, tot) - local;  // keys in bins before 8t
+      if (run < k && run + local >= k) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (run < k && run + hb[j] >= k) {
+            sh3[0] = 8 * t + j;
+            sh3[1] = k - run;
+            sh3[2] = hb[j];
+          }
+          run += hb[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t kbin = sh3[0], need = sh3[1], in_bin = sh3[2];
+      if (kbin < 2047u && in_bin <= 64u) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-          if (i < nslots && key[i] != 0ull && hist_bin((uint32_t)(key[i] >> 32), t0key) == kb_bin) {
+          if (key[i] != 0ull && ((rowmax - (uint32_t)(key[i] >> 32)) >> 13) == kbin) {
             const uint32_t slot = atomicAdd(&sh_binn, 1u);
             if (slot < 64u) bin_keys[slot] = key[i];
           }
         }
         __syncthreads();
+        // lane l ranks bin key l among them by register reads (every wave alike)
         const uint64_t mine = lane < (int)in_bin ? bin_keys[lane] : 0ull;
         uint32_t rank = 0;
         for (uint32_t j = 0; j < in_bin; ++j) {
@@ -1062,88 +1111,215 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
                                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, (int)j);
           rank += other > mine ? 1u : 0u;
         }
-        // (keys are unique: one lane holds rank need - 1; the same in every wave)
         const unsigned long long pick = __ballot(lane < (int)in_bin && rank == need - 1);
-        if (pick) {
-          const int src = __ffsll((long long)pick) - 1;
-          kth = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), src) << 32) |
-                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, src);
-          ranked = true;
-        }
+        const int src = __ffsll((long long)pick) - 1;
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), src) << 32) |
+               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, src);
       }
-      if (!ranked) kth = block_kth_regs<kPer>(key, k, h2048, wsum, sh3);
-    }
-    // winners: every candidate key >= kth
-    if (use_bitmap) {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (i < nslots && key[i] >= kth) {
-          const uint32_t it = select_key_pos(key[i]);
-          atomicOr(&bitmap[bitmap_slot(it >> 5)], 1u << (it & 31u));
-        }
-      }
-      __syncthreads();
-      // thread t owns words 16t .. 16t+15 (512 items)
-      const uint32_t nwords = (uint32_t)((n_items + 31) / 32);
-      uint32_t wb[16], cnt_t = 0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t wi = 16 * t + j;
-        wb[j] = wi < nwords ? bitmap[bitmap_slot(wi)] : 0u;
-        cnt_t += __builtin_popcount(wb[j]);
-      }
-      uint32_t tot;
-      uint32_t o = block_incl_scan_256(cnt_t, wsum, tot) - cnt_t;
-      n_win = tot;
-      // winners before each word, into LDS (over lc: the candidates are in
-      // registers now); then each winner's rank is that count plus the set
-      // bits below it in its word, and it goes to its slot of `win` (the
-      // global stores follow in one coalesced pass)
-      uint32_t* wpre = reinterpret_cast<uint32_t*>(lc);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        wpre[bitmap_slot(16 * t + j)] = o;
-        o += __builtin_popcount(wb[j]);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (i < nslots && key[i] >= kth) {
-          const uint32_t it = select_key_pos(key[i]), ws = bitmap_slot(it >> 5);
-          win[wpre[ws] + __builtin_popcount(bitmap[ws] & ((1u << (it & 31u)) - 1u))] = it;
-        }
-      }
-      __syncthreads();
+      const uint64_t e = block_kth_regs<kPer>(key, k, h2048, wsum, sh3);
+      return block_min_at_least<kPer>(key, e);
+    };
+    to_regs(total);
+    uint64_t kth = total > k ? kth_of(true) : 0ull;
+    uint32_t lo = 1u, hi = 0xFFFFFFFFu;
+    if (total > k) band_bounds(kth, delta, lo, hi);
+    // A chunk is open when keys below its band 0 may still reach the band
+    // (its band-0 edge lies above the band's lower bound): its band 1 is
+    // gathered, a second round trip.  Spec rows decide it by ballot in every
+    // wave; the others through thread t's chunks 16t .. 16t+15.
+    auto opens = [&](const u32x4_t& r) __attribute__((always_inline)) -> bool {
+      return rec_thi(r) > lo && (rec_ntot(r) > rec_n0(r) || r[2] == 0u);
+    };
+    bool open;
+    if (spec) {
+      open = __ballot((lane < nch && opens(ia)) || (kSpecCh > 64 && lane + 64 < nch && opens(ib))) != 0ull;
     } else {
-      // compaction, then a bitonic sort padded to a power of two
-      if (t == 0) sh_need = 0;
+      bool any = false;
+      for (int j = 0; j < 16; ++j) {
+        const int ch = 16 * t + j;
+        if (ch < nch) any |= opens(info_at(ch));
+      }
+      open = __syncthreads_or(any ? 1 : 0) != 0;
+    }
+    if (open) {
+      // band-1 counts of the open chunks and their starts after band 0
+      uint32_t n1[16], local = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int ch = 16 * t + j;
+        n1[j] = 0u;
+        if (ch < nch) {
+          const u32x4_t r = info_at(ch);
+          if (opens(r)) n1[j] = rec_ntot(r) - rec_n0(r);
+        }
+        local += n1[j];
+      }
+      uint32_t more;
+      uint32_t run = block_incl_scan_256(local, wsum, more) - local;
+      const uint32_t tot2 = total + more;
+      fast = tot2 <= (uint32_t)kSelCap;
+      if (fast) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int ch = 16 * t + j;
+          if (ch < nch) seg_start[ch] = total + run;
+          run += n1[j];
+        }
+        __syncthreads();
+        // wave w copies the band 1 of chunks w, w + 4, ..., four at a time
+        for (int c0 = wave; c0 < nch; c0 += 16) {
+          uint64_t v[4][2];
+          uint32_t nn[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ch = c0 + 4 * j;
+            uint32_t n0 = 0u;
+            nn[j] = 0u;
+            if (ch < nch) {
+              const u32x4_t r = info_at(ch);
+              n0 = rec_n0(r);
+              if (opens(r)) nn[j] = rec_ntot(r) - n0;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t i = lane + 64 * h;
+              v[j][h] = i < nn[j] ? seg_at(ch, n0 + i) : 0ull;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ch = c0 + 4 * j;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t i = lane + 64 * h;
+              if (i < nn[j]) lc[seg_start[ch] + i] = v[j][h];
+            }
+          }
+        }
+        __syncthreads();
+        total = tot2;
+        to_regs(total);
+        kth = total > k ? kth_of(false) : 0ull;
+        lo = 1u;
+        hi = 0xFFFFFFFFu;
+        if (total > k) band_bounds(kth, delta, lo, hi);
+        // every chunk's dropped keys (below its band-1 edge) must lie below the band
+        bool dropped = false;
+        for (int c = t; c < nch; c += 256) dropped |= rec_tlo(info_at(c)) > lo;
+        fast = __syncthreads_or(dropped ? 1 : 0) == 0;
+      }
+    }
+    if (fast && use_bitmap) {  // the histogram is done with: clear the bitmap
+      uint4* bm4 = reinterpret_cast<uint4*>(bitmap);
+      for (int i = t; i < kBitmapItems / 128; i += 256) bm4[i] = make_uint4(0, 0, 0, 0);
       __syncthreads();
+    }
+    if (fast) {
+      // Winners.  With more than k candidates: keys above hi win for sure
+      // and go to the bitmap at once; keys in [lo, hi] form the near-tie
+      // band, of which the keys at or above the k-th number r = k - (sure
+      // winners): if the band holds just r keys they all win, otherwise the
+      // band is rescored exactly and its r best win.  With at most k
+      // candidates (and no chunk dropping a key) every candidate wins.
+      const bool all = total <= k;
+      if (!use_bitmap && t == 0) sh_need = 0;  // (published by the barrier below)
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        if (i < nslots && key[i] >= kth) win[atomicAdd(&sh_need, 1u)] = select_key_pos(key[i]);
+        const uint32_t sk = (uint32_t)(key[i] >> 32);
+        if (key[i] == 0ull) continue;
+        if (all || sk > hi) {
+          const uint32_t it = select_key_pos(key[i]);
+          if (use_bitmap) atomicOr(&bitmap[bitmap_slot(it >> 5)], 1u << (it & 31u));
+        } else if (sk >= lo) {
+          const uint32_t at = atomicAdd(&sh_nb, 1u);
+          if (at < kBandCap) bitem[at] = select_key_pos(key[i]);
+          if (key[i] >= kth) atomicAdd(&sh_nbge, 1u);
+        }
       }
       __syncthreads();
-      n_win = sh_need;
-      uint32_t n2 = 1;
-      while (n2 < n_win) n2 <<= 1;
-      for (uint32_t i = n_win + t; i < n2; i += 256) win[i] = 0xFFFFFFFFu;
-      __syncthreads();
-      for (uint32_t size = 2; size <= n2; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-          for (uint32_t i = t; i < n2 / 2; i += 256) {
-            const uint32_t lo = 2 * i - (i & (stride - 1));
-            const uint32_t hi = lo + stride;
-            const bool asc = (lo & size) == 0;
-            const uint32_t a = win[lo], b = win[hi];
-            if ((a > b) == asc) { win[lo] = b; win[hi] = a; }
+      const uint32_t nb = sh_nb, r = sh_nbge;
+      if (nb > r && nb > kBandCap) {
+        fast = false;  // a band this wide: the exact recompute settles the row
+      } else if (nb > r) {
+        rank_band(p, row, nb, r, bitem, bscore, bwin, qd, qw);
+      } else {
+        for (uint32_t m = t; m < nb; m += 256) bwin[m] = 1u;
+        __syncthreads();
+      }
+      if (fast) {
+        if (use_bitmap) {
+          for (uint32_t m = t; m < nb; m += 256) {
+            if (bwin[m]) {
+              const uint32_t it = bitem[m];
+              atomicOr(&bitmap[bitmap_slot(it >> 5)], 1u << (it & 31u));
+            }
           }
           __syncthreads();
+          // thread t owns words 16t .. 16t+15 (512 items); each winner goes
+          // to slot (winners before its word) + (set bits below it)
+          const uint32_t nwords = (uint32_t)((n_items + 31) / 32);
+          uint32_t wb[16], cnt_t = 0;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t wi = 16 * t + j;
+            wb[j] = wi < nwords ? bitmap[bitmap_slot(wi)] : 0u;
+            cnt_t += __builtin_popcount(wb[j]);
+          }
+          uint32_t tot;
+          uint32_t o = block_incl_scan_256(cnt_t, wsum, tot) - cnt_t;
+          n_win = tot;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            uint32_t b = wb[j];
+            while (b) {
+              const int bit = __ffs(b) - 1;
+              win[o++] = 32u * (16 * t + j) + (uint32_t)bit;
+              b &= b - 1u;
+            }
+          }
+          __syncthreads();
+        } else {
+          // compaction, then a bitonic sort padded to a power of two
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) {
+            const uint32_t sk = (uint32_t)(key[i] >> 32);
+            if (key[i] != 0ull && (all || sk > hi)) win[atomicAdd(&sh_need, 1u)] = select_key_pos(key[i]);
+          }
+          for (uint32_t m = t; m < nb; m += 256)
+            if (bwin[m]) win[atomicAdd(&sh_need, 1u)] = bitem[m];
+          __syncthreads();
+          n_win = sh_need;
+          uint32_t n2 = 1;
+          while (n2 < n_win) n2 <<= 1;
+          for (uint32_t i = n_win + t; i < n2; i += 256) win[i] = 0xFFFFFFFFu;
+          __syncthreads();
+          for (uint32_t size = 2; size <= n2; size <<= 1) {
+            for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+              for (uint32_t i = t; i < n2 / 2; i += 256) {
+                const uint32_t lo2 = 2 * i - (i & (stride - 1));
+                const uint32_t hi2 = lo2 + stride;
+                const bool asc = (lo2 & size) == 0;
+                const uint32_t a = win[lo2], b = win[hi2];
+                if ((a > b) == asc) {
+                  win[lo2] = b;
+                  win[hi2] = a;
+                }
+              }
+              __syncthreads();
+            }
+          }
         }
       }
     }
-  } else {
-    // exact recompute of this row (rare): radix steps over recomputed keys
-    if (t == 0) atomicAdd(p.fallbacks, 1u);
+  }
+  if (!fast) {
+    // exact recompute of this row (rare): every item's score again, a radix
+    // over the (score, -item) keys for the k-th, then the near-tie band
+    // rescored exactly as above
+    if (t == 0) {
+      atomicAdd(p.fallbacks, 1u);
+      sh_nb = 0;
+    }
     half2_t q[kHI][8];
     float w_mine;
     load_query_f16(p, row, quarter, q, w_mine);
@@ -1170,16 +1346,68 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
       }
       (void)block_incl_scan_256(mine, wsum, n_valid);
     }
-    if (n_valid > k) kth = radix_kth<uint64_t>(visit, ni, k, h256, &sh_kth, &sh_need);
+    uint32_t lo = 1u, hi = 0xFFFFFFFFu, nb = 0, r = 0;
+    // (the fallback scores on VALU even where the scan used MFMA)
+    const float delta_v = kErrValu * cq * 448.0f * ksm;
+    if (n_valid > k) {
+      kth = radix_kth<uint64_t>(visit, ni, k, h256, &sh_kth, &sh_need);
+      band_bounds(kth, delta_v, lo, hi);
+      // the band's items (at most kBandMax: wider bands keep the binary32 order)
+      uint32_t sure_l = 0;
+      visit(ni, [&](uint64_t kk) {
+        const uint32_t sk = (uint32_t)(kk >> 32);
+        if (sk > hi) ++sure_l;
+        else if (sk >= lo) {
+          const uint32_t at = atomicAdd(&sh_nb, 1u);
+          if (at < kBandCap) bitem[at] = select_key_pos(kk);
+        }
+      });
+      uint32_t sure;
+      (void)block_incl_scan_256(sure_l, wsum, sure);
+      nb = sh_nb;
+      r = k - sure;
+      if (nb > r && nb <= kBandCap) {
+        // ascending items, so the emission below can binary-search them
+        if (t == 0) {
+          for (uint32_t i = 1; i < nb; ++i) {
+            const uint32_t v = bitem[i];
+            uint32_t j = i;
+            while (j > 0 && bitem[j - 1] > v) { bitem[j] = bitem[j - 1]; --j; }
+            bitem[j] = v;
+          }
+        }
+        __syncthreads();
+        rank_band(p, row, nb, r, bitem, bscore, bwin, qd, qw);
+      }
+    }
+    const bool ranked = nb > r && nb <= kBandCap;
     for (uint32_t base = 0; base < ni; base += 64) {
       const uint32_t item = base + (t >> 2);
       bool valid = false;
       const int64_t pos = item < ni ? item_position(p, row, item, ni, vis, valid) : 0;
       const float sc = quad_score_at(p, q, w_mine, seq, quarter, pos, valid);
-      const bool f = valid && quarter == 0 && select_key(score_key(sc), item) >= kth;
+      const uint64_t kk = select_key(score_key(sc), item);
+      bool f = valid && quarter == 0;
+      if (f && n_valid > k) {
+        const uint32_t sk = (uint32_t)(kk >> 32);
+        if (!ranked) {
+          f = kk >= kth;
+        } else if (sk > hi) {
+          f = true;
+        } else if (sk < lo) {
+          f = false;
+        } else {
+          uint32_t a = 0, b = nb;  // binary search of the band's items
+          while (a < b) {
+            const uint32_t m = (a + b) >> 1;
+            if (bitem[m] < item) a = m + 1; else b = m;
+          }
+          f = a < nb && bitem[a] == item && bwin[a] != 0u;
+        }
+      }
       uint32_t nr;
       const uint32_t o = block_incl_scan_256(f ? 1u : 0u, wsum, nr) - (f ? 1u : 0u);
-      if (f && n_win + o < (uint32_t)CSA2_MAX_K) win[n_win + o] = item;
+      if (f && n_win + o < kWinCap) win[n_win + o] = item;
       n_win += nr;
     }
     if (n_win > k) n_win = k;
@@ -1234,7 +1462,8 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row) {
 
 template <int kPer>
 __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
-  select_row<kPer>(p, blockIdx.x);
+  __shared__ SelLdsFull<kPer> S;
+  select_row<kPer>(p, blockIdx.x, S);
 }
 
 // The select of a decode index pass with the window tiles of the group's
@@ -1244,11 +1473,15 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
 // tiles need nothing it computes.
 template <int kPer>
 __global__ __launch_bounds__(256) void k_index_select_window(IndexPass p, AttnPass a) {
+  __shared__ union {
+    SelLdsFull<kPer> sel;
+    TileLds tile;
+  } U;
   if ((int)blockIdx.x < p.rows) {
-    select_row<kPer>(p, blockIdx.x);
+    select_row<kPer>(p, blockIdx.x, U.sel);
     return;
   }
-  __shared__ __attribute__((aligned(16))) TileLds s;
+  TileLds& s = U.tile;
   const int n_win_tiles = a.n_tiles - (a.n_idx + kAttnSplit - 1) / kAttnSplit;
   const int per_row = a.n_layers * n_win_tiles;
   // with a multiple of 8 rows, the tiles of row r run on XCD r mod 8 (the
@@ -1281,37 +1514,49 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream
   return hipGetLastError();
 }
 
-hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnPass* window) {
-  if (p.rows == 0 || p.max_items == 0) return hipSuccess;
-  // chunks per row, at most: scan_chunk_items keeps a row of n items within
-  // max(scan_chunks_min(k), ceil(n / kScanChunk)) chunks
-  const int scan_per_row =
-      std::max<int>(scan_chunks_min(p.k), (int)((p.max_items + kScanChunk - 1) / kScanChunk));
+// Scan chunks per row of a pass, at most (the grid's chunk dimension): over
+// direct items from every sequence's item count, otherwise from the largest
+// row.
+static int pass_chunks_per_row(const IndexPass& p) {
+  auto chunks = [&](int64_t n) { return n > 0 ? scan_chunk_count(n, scan_chunk_items(n, p.k)) : 0; };
+  int64_t m = chunks(p.max_items);
+  if (p.source == kItemsDirect) {
+    for (int s = 0; s < p.rows / p.n_q; ++s) {
+      const int64_t pos = p.seq.a[s] + p.n_q - 1;
+      int64_t vis = p.ratio == 2 ? (pos + 1) >> 1 : pos + 1;
+      vis = std::min(vis, p.seq.b[s]);
+      const int64_t n = p.block_level ? (vis + 7) >> 3 : vis;
+      m = std::max(m, chunks(std::min(n, p.max_items)));
+    }
+  } else {
+    // block lists of fewer items can take more, smaller chunks: just below a
+    // size where the chunks double, a row has 2 k / chunk_winners(k) of them
+    const int64_t peak = 2 * (int64_t)p.k / chunk_winners(p.k);
+    m = std::max(m, std::min(peak, (p.max_items + 127) / 128));
+  }
+  return (int)m;
+}
+
+hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const AttnPass* window, bool* window_done) {
+  if (window_done) *window_done = false;
+  if (p0.rows == 0 || p0.max_items == 0) return hipSuccess;
+  IndexPass p = p0;
+  const int scan_per_row = pass_chunks_per_row(p);
   if (scan_per_row > p.max_chunks) return hipErrorInvalidValue;
-  const int gr = grid_rows(p.rows);
-  int h = prof_begin(CSA2_K_INDEX_SAMPLE, stream);
-  // (rows, then helpers from the next multiple of 8 on: see k_index_sample)
-  const unsigned sgrid_rows = (unsigned)((p.rows + kXcds - 1) / kXcds * kXcds + p.rows);
-  if (p.source == kItemsDirect)
-    hipLaunchKernelGGL(k_index_sample<true>, dim3(sgrid_rows), dim3(kSampleThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(k_index_sample<false>, dim3(sgrid_rows), dim3(kSampleThreads), 0, stream, p);
-  prof_end(h, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  h = prof_begin(CSA2_K_INDEX_SCAN, stream);
   // the queries of a sequence share the scan of a chunk, up to 4 per
-  // workgroup (direct items only)
+  // workgroup (direct items only), on fp8 MFMA
   const int nqg = (p.source != kItemsDirect || p.n_q == 1) ? 1 : p.n_q == 2 ? 2 : 4;
-  const int n_groups = p.rows / p.n_q * ((p.n_q + nqg - 1) / nqg);
+  p.mfma_scores = nqg > 1 ? 1 : 0;
+  const int n_groups = nqg == 1 ? p.rows : p.rows / p.n_q * ((p.n_q + nqg - 1) / nqg);
   const dim3 sgrid((unsigned)(grid_rows(n_groups) * scan_per_row));
   const bool paged = p.pm.pages != nullptr;  // (direct items only: the host refuses the others)
+  int h = prof_begin(CSA2_K_INDEX_SCAN, stream);
   if (p.source != kItemsDirect)
-    hipLaunchKernelGGL((k_index_scan<2, false, 1, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan<2, false, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 1 && paged)
-    hipLaunchKernelGGL((k_index_scan<2, true, 1, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan<2, true, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 1)
-    hipLaunchKernelGGL((k_index_scan<2, true, 1, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+    hipLaunchKernelGGL((k_index_scan<2, true, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 2 && paged)
     hipLaunchKernelGGL((k_index_scan_mfma<2, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 2)
@@ -1321,15 +1566,19 @@ hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnP
   else
     hipLaunchKernelGGL((k_index_scan_mfma<4, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   prof_end(h, stream);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   h = prof_begin(CSA2_K_INDEX_SELECT, stream);
-  if (p.k > 1024) {
+  // 32 candidates per thread for the 2,048-block stage and for rows of more
+  // than 128 chunks (their band-0 share is sized for that room)
+  const bool wide = p.k > 1024 || scan_per_row > 128;
+  if (wide) {
     hipLaunchKernelGGL(k_index_select<32>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
   } else if (window) {
     const int n_win_tiles = window->n_tiles - (window->n_idx + kAttnSplit - 1) / kAttnSplit;
     const int n_wg = window->rows * window->n_layers * n_win_tiles;
     hipLaunchKernelGGL(k_index_select_window<16>, dim3((unsigned)(p.rows + n_wg)), dim3(256), 0, stream, p, *window);
+    if (window_done) *window_done = true;
   } else {
     hipLaunchKernelGGL(k_index_select<16>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
   }

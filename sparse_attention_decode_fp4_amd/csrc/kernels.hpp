@@ -46,26 +46,17 @@ __device__ __forceinline__ uint32_t paged_entry_at(const PageMap& m, int seq, in
   return paged_entry(m, page, pos);
 }
 
-// Items scored per workgroup of the indexer scan; candidates kept per
-// (row, chunk) segment; chunks per row (items per row <= 8M).
-// Candidate histogram of a row: bin = (score key - key of T0) >> kHistShift,
-// the last bin taking everything above (1,024 bins per binade of scores).
-constexpr int kHistBins = 2048;
-constexpr int kHistWords = kHistBins / 2;  // two 16-bit bins per word, bin 2w in the low half
-constexpr int kHistShift = 13;
-constexpr int kScanChunk = 2048;  // items per scan workgroup, at most
-// Items per scan chunk of a row with n_items items and top-k: the row is cut
-// into at least kChunksMin(k) chunks (between 128 and kScanChunk items
-// each), so the ~2.5 k keys that reach the sampled threshold fill a chunk's
-// kSeg-slot segment to about a third on average, and a row with at most k
-// items (every item a candidate) has chunks of 128 = kSeg items.
-__host__ __device__ constexpr int scan_chunks_min_log2(int k) { return k <= 512 ? 5 : k <= 1024 ? 6 : 7; }
-__host__ __device__ constexpr int scan_chunks_min(int k) { return 1 << scan_chunks_min_log2(k); }
+// Items scored per workgroup of the indexer scan (a chunk), at most.
+constexpr int kScanChunk = 2048;
+// Items per scan chunk of a row with n_items items and top-k: the largest
+// power of two in [128, kScanChunk] that keeps the expected number of the
+// row's winners in one chunk, k * size / n_items, at most kChunkWinners (16
+// for k above 1,024).  A row then has at most max(ceil(n / 2048), k / 8 + 1)
+// chunks.
+__host__ __device__ constexpr int chunk_winners(int k) { return k > 1024 ? 16 : 8; }
 __host__ __device__ inline int64_t scan_chunk_items(int64_t n_items, int k) {
-  const int lg = scan_chunks_min_log2(k);
-  const int64_t want = (n_items + (1 << lg) - 1) >> lg;  // n_items >= 0
-  int64_t c = 128;
-  while (c < want && c < kScanChunk) c <<= 1;
+  int64_t c = kScanChunk;
+  while (c > 128 && (int64_t)k * c > (int64_t)chunk_winners(k) * n_items) c >>= 1;
   return c;
 }
 // Chunks of a row of n_items items cut into chunks of csize (a power of two).
@@ -73,6 +64,11 @@ __host__ __device__ inline int64_t scan_chunk_count(int64_t n_items, int64_t csi
   int lg = 0;
   while (((int64_t)1 << lg) < csize) ++lg;
   return (n_items + csize - 1) >> lg;
+}
+// Chunks per row a workspace must hold for rows of up to max_items items.
+inline int64_t scan_max_chunks(int64_t max_items) {
+  const int64_t a = (max_items + kScanChunk - 1) / kScanChunk;
+  return a > CSA2_MAX_K / 8 + 1 ? a : CSA2_MAX_K / 8 + 1;
 }
 constexpr int kSeg = 128;
 constexpr int kMaxChunks = 4096;
@@ -102,12 +98,14 @@ struct IndexPass {
   const int32_t* nsel;         // kItemsBlocks: [rows] number of selected blocks
   int64_t max_items;           // items per row the grid covers
   // workspace
-  float* thresh;               // [rows] sampled threshold
   uint32_t* fallbacks;         // rows that took the exact recompute (a counter)
-  uint32_t* hist;              // [rows][kHistWords] candidates per score bin above T0, 16 bits a bin
-  uint32_t* seg_count;         // [rows][max_chunks]
-  uint64_t* seg_list;          // [rows][max_chunks][kSeg]
+  // per (row, chunk): the chunk's two candidate bands (see the scan), as
+  // {n0 | ntot << 16, band-0 edge key, band-1 edge key (0: nothing dropped),
+  //  largest key scale of the chunk}
+  u32x4_t* chunk_info;         // [rows][max_chunks]
+  uint64_t* seg_list;          // [rows][max_chunks][kSeg] (score key << 32 | ~item)
   int32_t max_chunks;
+  int32_t mfma_scores;         // scores come from fp8 MFMA (queries sharing a scan)
   // output: either positions (out, -1 padded to k) or block ids + count
   int32_t* out;                // [rows][out_stride]
   int32_t out_stride;
@@ -151,8 +149,10 @@ hipError_t launch_block_keys(const uint8_t* k8, const float* ks, int64_t k_strid
                              int64_t bk_stride, hipStream_t stream);
 struct AttnPass;
 // `window`, if given, is the attention pass of the group the index pass
-// serves: its window tiles (window_tile) run in the select launch.
-hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnPass* window = nullptr);
+// serves: its window tiles (window_tile) may run in the select launch, and
+// *window_done then says whether they did.
+hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnPass* window = nullptr,
+                             bool* window_done = nullptr);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
 
 // Attention over the candidates of each row for one or more layers that
