@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
 // partial), with per-head weights l_s exp2(m_s - M) / L from the (m, l) of
 // every split.  The (m, l) loads go out first and the partial loads of up to
 // 16 splits behind them, so the weights are worked out while the partials
-// are in flight.
+// are in flight.  A split's weight carries its up-scale for the quarter.
 constexpr int kMaxMergeSplits = 64;
 constexpr int kMergeBatch = 16;
 // Workgroups run on the XCD that wrote the unit's partials (their lines are
@@ -253,14 +253,16 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p, int32_t map
   const __amdgpu_buffer_rsrc_t rp =
       __builtin_amdgcn_make_buffer_rsrc((void*)pb, 0, ns * kPartFloats * 4, kRawBufferWord3);
   // (split, head) (i / 16, i % 16) for i = t + 256 j: its m and l
+  // and the up-scale of this workgroup's channel quarter
   constexpr int kMl = kMaxMergeSplits * kH / 256;
-  float mv[kMl], lv[kMl];
+  float mv[kMl], lv[kMl], uv[kMl];
 #pragma unroll
   for (int j = 0; j < kMl; ++j) {
     const int i = t + 256 * j;
     const int off = ((i / kH) * kPartFloats + kPartOWords + i % kH) * 4;
     mv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 0));
     lv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off + kH * 4, 0, 0));
+    uv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off + (2 + quarter) * kH * 4, 0, 0));
   }
   u32x4_t v[kMergeBatch];
   auto load_batch = [&](int s0) {
@@ -304,14 +306,16 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p, int32_t map
     __syncthreads();
     L = (red_l[0][h_t] + red_l[1][h_t]) + (red_l[2][h_t] + red_l[3][h_t]);
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    if (live) wgt[s_t][h_t] = w * inv;
+    if (live) wgt[s_t][h_t] = w * inv * uv[0];
   } else {
+    __shared__ float ush[kMaxMergeSplits][kH];
 #pragma unroll
     for (int j = 0; j < kMl; ++j) {
       const int i = t + 256 * j;
       if (i < ns * kH) {
         wgt[i / kH][i % kH] = mv[j];
         lsh[i / kH][i % kH] = lv[j];
+        ush[i / kH][i % kH] = uv[j];
       }
     }
     __syncthreads();
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p, int32_t map
         L += w;
       }
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      for (int s = 0; s < ns; ++s) wgt[s][t] *= inv;
+      for (int s = 0; s < ns; ++s) wgt[s][t] = wgt[s][t] * inv * ush[s][t];
     }
   }
   __syncthreads();

@@ -166,9 +166,14 @@ constexpr int kMaxAttnLayers = 8;
 constexpr int kAttnSplit = 64;  // candidates per workgroup
 // A partial softmax, in 4-byte words: O / l as [512 channels][16 heads] fp16
 // (normalised, so every value is a convex combination of value rows), then
-// m[16] and l[16] as float32.
+// m[16] and l[16] as float32, then up[4][16]: the fp16 values of channel
+// quarter c (channels 128 c .. 128 c + 127) of head h are O / l times
+// 1 / up[c][h], a power of two (1 unless the quarter's largest magnitude is
+// 2^15 or more, as window rows of large values give), so fp16 holds every
+// value in range.
 constexpr int kPartOWords = kD * kH / 2;
-constexpr int kPartFloats = kPartOWords + 2 * kH;
+constexpr int kPartUp = kPartOWords + 2 * kH;
+constexpr int kPartFloats = kPartUp + 4 * kH;
 struct AttnPass {
   int32_t rows, n_q, n_idx, n_layers;
   SeqArgs seq;                  // a = q_pos0, b = swa_pos0

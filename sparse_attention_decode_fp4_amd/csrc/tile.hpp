@@ -345,20 +345,34 @@ __device__ __forceinline__ void write_partial(const AttnPass& p, int unit, int s
   const int l16 = lane & 15, g4 = lane >> 4;
   float* part = p.partial + ((int64_t)unit * p.max_splits + split) * kPartFloats;
   uint16_t* po = reinterpret_cast<uint16_t*>(part);
-  float inv[4];
+  float inv[4], down[4], up[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float l = __shfl(l_run, 4 * g4 + r, 64);  // l of head 4 g4 + r
     inv[r] = l > 0.0f ? 1.0f / l : 0.0f;
+    // the largest |O / l| of head 4 g4 + r over this wave's 128 channels
+    // (the 16 lanes of g4, 8 each): its float32 exponent field, since the
+    // bit patterns of non-negative floats order as integers
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) mb = max(mb, __float_as_uint(o[nt][r] * inv[r]) & 0x7FFFFFFFu);
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, d, 64));
+    // below 2^15 (biased exponent < 142) the values go as they are; else
+    // scale by 2^-e so the largest is below 2^15 (exact: a power of two)
+    const int e = (int)(mb >> 23) - 141 > 0 ? (int)(mb >> 23) - 141 : 0;
+    down[r] = __uint_as_float((uint32_t)(127 - e) << 23);
+    up[r] = __uint_as_float((uint32_t)(127 + e) << 23);
   }
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const int ch = 128 * wave + 16 * nt + l16;
-    const half2_t a = {(_Float16)(o[nt][0] * inv[0]), (_Float16)(o[nt][1] * inv[1])};  // round to nearest
-    const half2_t b = {(_Float16)(o[nt][2] * inv[2]), (_Float16)(o[nt][3] * inv[3])};
+    const half2_t a = {(_Float16)(o[nt][0] * inv[0] * down[0]), (_Float16)(o[nt][1] * inv[1] * down[1])};
+    const half2_t b = {(_Float16)(o[nt][2] * inv[2] * down[2]), (_Float16)(o[nt][3] * inv[3] * down[3])};
     *reinterpret_cast<uint2*>(po + ch * kH + 4 * g4) =
         make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
   }
+  if (l16 < 4) part[kPartUp + kH * wave + 4 * g4 + l16] = l16 == 0 ? up[0] : l16 == 1 ? up[1] : l16 == 2 ? up[2] : up[3];
   if (wave == 0 && g4 == 0) {
     part[kPartOWords + l16] = m_run;
     part[kPartOWords + kH + l16] = l_run;

@@ -64,3 +64,25 @@ def test_attention_matches_oracle(csa2, batch, ctx, n_q, n_idx, q_pos, pad, logn
     # a second call on the same workspace gives identical bits (deterministic merge)
     out2 = csa2.csa2_sparse_swa_attn(ws, q, nib, sc, idx, swa, [q_pos] * batch, swa_pos0, ctx)
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("big", [1e5, 1e30])
+def test_attention_with_window_values_past_fp16(csa2, big):
+    """Window rows of magnitude 1e5 or 1e30 (bf16 holds them, fp16 does not):
+    the split partials keep them in range, so the merged output matches."""
+    batch, ctx, q_pos, n_idx = 2, 2000, 1999, 512
+    nib, sc, idx, q, swa, swa_pos0 = _case(csa2, 29, batch, ctx, 1, [q_pos] * batch, n_idx)
+    swa = (swa.float() * big).to(torch.bfloat16)
+    ws = csa2.Workspace(batch, 1, ctx)
+    out = csa2.csa2_sparse_swa_attn(ws, q, nib, sc, idx, swa, [q_pos] * batch, swa_pos0, ctx,
+                                    softmax_scale=1.0 / big)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    (nh, sh), ih = _case.oracle_codes, idx.cpu().numpy()
+    qb, sb = gen.bf16_bits(q), gen.bf16_bits(swa)
+    for b in range(batch):
+        ref = oracle.sparse_swa_attention(qb[b, 0], nh[b * ctx:(b + 1) * ctx], sh[b * ctx:(b + 1) * ctx],
+                                          ih[b, 0], sb[b], swa_pos0[b], q_pos, 1.0 / big)
+        assert np.abs(ref).max() > big / 100  # the window rows do carry weight
+        # the tolerance holds in units of the window rows' scale
+        check_close(out[b, 0].cpu().numpy().astype(np.float64) / big, ref / big, f"b{b} x{big:g}")
