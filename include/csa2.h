@@ -342,6 +342,27 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* state,
                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_run_group for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, hosts that forbid hipMalloc.  It
+ * takes no workspace and allocates nothing; it works in a scratch array of
+ * CSA2_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on, from the first call on that device until the process ends.  Arguments,
+ * state, outputs and errors are those of csa2_run_group, and so are the
+ * results, bit for bit.  The call uses the scratch of the current device
+ * (the stream must belong to it).  All calls on one device share that
+ * device's scratch, which keeps the last call's contents: calls that may
+ * overlap on one device (other streams, other threads) race, and the caller
+ * must order them.  Nothing in the scratch has to start at zero (a call
+ * writes everything it reads).  Calls are not timed by csa2_profile_*.
+ * Size: decode steps of up to about 16 sequences x 131,072 entries with up
+ * to four layers per Full/Reindex layer need about 15 MiB.  Errors: those of
+ * csa2_run_group, and CSA2_ERR_UNSUPPORTED when the call needs more than
+ * CSA2_NOALLOC_SCRATCH_BYTES (csa2_last_error() gives both figures).
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20)
+int csa2_run_group_noalloc(const csa2_group_args* a, csa2_group_state* state, void* stream);
+
+/*
  * The write side of one decode step: one new token per sequence goes into
  * the caches the read side uses.  The cache format is the one
  * csa2_quantize_kv writes (ai-wave.ru "DeepSeek V4.1-Flash: 1M context, FP4

@@ -111,6 +111,7 @@ def _load():
         "csa2_sparse_swa_attn": (_i32, [ctypes.POINTER(AttnArgs), _p, ctypes.c_size_t, _p]),
         "csa2_run_group": (_i32, [ctypes.POINTER(GroupArgs), ctypes.POINTER(GroupState), _p,
                                   ctypes.c_size_t, _p]),
+        "csa2_run_group_noalloc": (_i32, [ctypes.POINTER(GroupArgs), ctypes.POINTER(GroupState), _p]),
         "csa2_append": (_i32, [ctypes.POINTER(AppendArgs), _p]),
         "csa2_profile_enable": (_i32, [_i32]),
         "csa2_profile_reset": (_i32, []),
@@ -368,6 +369,22 @@ def csa2_run_group(ws, state, layers, q_pos0, n_entries, swa_pos0, *, ratio=1,
                    stream=None):
     """Run a plan.  layers: list of dicts {mode, q, swa, idx_q?, idx_w?, kv? (make_kv), out?}.
     Returns the float32 outputs [batch, n_q, 16, 512], one per layer."""
+    return _group(ws, state, layers, q_pos0, n_entries, swa_pos0, ratio, index_kind, reindex_kind,
+                  softmax_scale, swa_ring, stream)
+
+
+def csa2_run_group_noalloc(state, layers, q_pos0, n_entries, swa_pos0, *, ratio=1,
+                           index_kind=INDEX_FLAT, reindex_kind=INDEX_FLAT, softmax_scale=1.0,
+                           swa_ring=0, stream=None):
+    """csa2_run_group in the library's own device scratch (no workspace).  The
+    C call allocates nothing; pass every layer's `out` for a call that makes
+    no tensor either."""
+    return _group(None, state, layers, q_pos0, n_entries, swa_pos0, ratio, index_kind, reindex_kind,
+                  softmax_scale, swa_ring, stream)
+
+
+def _group(ws, state, layers, q_pos0, n_entries, swa_pos0, ratio, index_kind, reindex_kind,
+           softmax_scale, swa_ring, stream):
     n = len(layers)
     arr = (Layer * n)()
     outs, keep = [], []
@@ -399,8 +416,11 @@ def csa2_run_group(ws, state, layers, q_pos0, n_entries, swa_pos0, *, ratio=1,
     a.q_pos0, a.n_entries, a.swa_pos0 = ctypes.cast(qp, _p), ctypes.cast(ne, _p), ctypes.cast(sp, _p)
     a.swa_stride, a.swa_rows, a.swa_ring = swa_rows, swa_rows, swa_ring
     a.softmax_scale, a.n_layers, a.layers = softmax_scale, n, arr
-    _check(lib.csa2_run_group(ctypes.byref(a), ctypes.byref(state.c), ws.ptr, ws.nbytes,
-                              _stream(stream)))
+    if ws is None:
+        _check(lib.csa2_run_group_noalloc(ctypes.byref(a), ctypes.byref(state.c), _stream(stream)))
+    else:
+        _check(lib.csa2_run_group(ctypes.byref(a), ctypes.byref(state.c), ws.ptr, ws.nbytes,
+                                  _stream(stream)))
     if any(L["mode"] == MODE_FULL for L in layers):
         state._keep = [kv for kv in keep if isinstance(kv, KV)]
     return outs

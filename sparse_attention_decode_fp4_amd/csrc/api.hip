@@ -6,10 +6,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.hpp"
 
 using namespace csa2;
+
+// Scratch of csa2_run_group_noalloc: device memory the library holds on every
+// device it runs on, for the life of the process.  On the host this name is
+// a stand-in, not a device address: host code uses only the per-device
+// address hipGetSymbolAddress returns for it.  Calls on one device share it.
+constexpr size_t kScratchBytes = CSA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -38,14 +46,18 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct WsLayout {
   size_t stats, chunk_info, seg_list, blocks, nsel, partial;
   size_t pf_sample, pf_thresh, pf_count, pf_list, total;
-  int32_t max_chunks;  // scan chunks per row covered by the segment buffers
+  int32_t max_chunks;     // scan chunks per row covered by the segment buffers
+  int64_t partial_units;  // (layer,row) x split slots the attention partials hold
 };
 
 // Decode-path buffers cover `rows` query rows of up to `max_items` items;
-// prefill-path buffers cover `pf_rows` query rows (0 when unused).
-WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
+// prefill-path buffers cover `pf_rows` query rows (0 when unused); the
+// attention partials, `partial_units` slots.
+WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0,
+                   int64_t partial_units = kMaxPartialUnits) {
   WsLayout w{};
   w.max_chunks = (int32_t)scan_max_chunks(std::max<int64_t>(max_items, 1));
+  w.partial_units = partial_units;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, kWsAlign); return o; };
   w.stats = take(kWsAlign);  // offset 0 in every layout: the fallback counter
@@ -53,7 +65,7 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
   w.nsel = take((size_t)rows * 4);
-  w.partial = take((size_t)kMaxPartialUnits * kPartFloats * 4);
+  w.partial = take((size_t)partial_units * kPartFloats * 4);
   w.pf_sample = take((size_t)pf_rows * kPfSample * 4);
   w.pf_thresh = take((size_t)pf_rows * 4);
   w.pf_count = take((size_t)pf_rows * kPfSplits * 4);
@@ -64,10 +76,10 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0) {
 
 // Layout for calls of `batch` sequences x `n_q` queries: prefill-sized calls
 // use the MFMA indexer and need no per-item decode buffers.
-WsLayout ws_for(int32_t batch, int32_t n_q, int64_t max_items) {
+WsLayout ws_for(int32_t batch, int32_t n_q, int64_t max_items, int64_t partial_units = kMaxPartialUnits) {
   const int64_t seqs = std::min(batch, kMaxSeqPerLaunch);
-  if (n_q >= kPrefillMinQ) return ws_layout(0, 0, seqs * n_q);
-  return ws_layout(seqs * n_q, max_items, 0);
+  if (n_q >= kPrefillMinQ) return ws_layout(0, 0, seqs * n_q, partial_units);
+  return ws_layout(seqs * n_q, max_items, 0, partial_units);
 }
 
 template <typename T>
@@ -313,10 +325,21 @@ struct AttnJob {
   csa2_pages pages;       // paged nib / scale, or a zero table
 };
 
+// Candidate tiles of one (layer, row): the selected entries, then the window.
+int attn_tiles(int n_idx) { return (n_idx + kAttnSplit - 1) / kAttnSplit + (CSA2_SWA + kAttnSplit - 1) / kAttnSplit; }
+
+// Workgroups the tiles of a (layer, row) are split over: enough for about
+// 1024 workgroups in flight, with at most `cap` partial slots in all; with
+// many rows one workgroup walks them all.
+int attn_splits(int units, int n_tiles, int64_t cap) {
+  int splits = std::max(1, std::min(n_tiles, (1024 + units - 1) / units));
+  while (splits > 1 && (int64_t)units * splits > cap) --splits;
+  return splits;
+}
+
 // The attention pass of sequences s0 .. s0 + nb - 1 of a job.
 AttnPass make_attn_pass(const AttnJob& j, int s0, int nb, void* ws, const WsLayout& w) {
-  const int n_tile_idx = (j.n_idx + kAttnSplit - 1) / kAttnSplit;
-  const int n_tiles = n_tile_idx + (CSA2_SWA + kAttnSplit - 1) / kAttnSplit;
+  const int n_tiles = attn_tiles(j.n_idx);
   AttnPass p{};
   p.rows = nb * j.n_q;
   p.n_q = j.n_q;
@@ -341,11 +364,7 @@ AttnPass make_attn_pass(const AttnJob& j, int s0, int nb, void* ws, const WsLayo
     p.layer[l].swa = j.layer[l].swa + (int64_t)s0 * j.swa_stride * kD;
     p.layer[l].out = j.layer[l].out + row0 * kH * kD;
   }
-  // split the candidate tiles of a (layer, row) over workgroups until about
-  // 1024 workgroups are in flight; with many rows one workgroup walks them all
-  const int units = p.n_layers * p.rows;
-  int splits = std::max(1, std::min(n_tiles, (1024 + units - 1) / units));
-  while (splits > 1 && (int64_t)units * splits > kMaxPartialUnits) --splits;
+  const int splits = attn_splits(p.n_layers * p.rows, n_tiles, kMaxPartialUnits);
   p.n_tiles = n_tiles;
   p.tiles_per_split = (n_tiles + splits - 1) / splits;
   p.max_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
@@ -558,8 +577,62 @@ int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_byt
   return run_attention(j, workspace, w, (hipStream_t)stream);
 }
 
-int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, size_t ws_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Partial slots the attention launches of a plan use at most: the plan's
+// largest attention job (a layer and the Reuse layers after it) over each
+// launch's rows.
+int64_t plan_partial_units(const csa2_group_args* a) {
+  int max_layers = 0;
+  for (int l = 0; l < a->n_layers;) {
+    int n = 0;
+    do {
+      ++n;
+      ++l;
+    } while (l < a->n_layers && a->layers[l].mode == CSA2_MODE_REUSE && n < kMaxAttnLayers);
+    max_layers = std::max(max_layers, n);
+  }
+  int64_t need = 0;
+  const int tiles = attn_tiles(CSA2_TOP_K);
+  for (int s0 = 0; s0 < a->batch; s0 += kMaxSeqPerLaunch) {
+    const int units = max_layers * std::min(kMaxSeqPerLaunch, a->batch - s0) * a->n_q;
+    const int splits = attn_splits(units, tiles, kMaxPartialUnits);
+    if (splits > 1) need = std::max<int64_t>(need, (int64_t)units * splits);
+  }
+  return need;
+}
+
+// The library's own scratch for csa2_run_group_noalloc (see there).
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The current device's copy of the scratch array, its address looked up
+// once per device (with that device current).
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(CSA2_ERR_UNSUPPORTED, "csa2_run_group_noalloc: device %d (at most %d devices)", dev, kScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, kWsAlign)) return fail(CSA2_ERR_HIP, "scratch address is not 256-byte aligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+
+// csa2_run_group; with noalloc set, workspace and ws_bytes are ignored and
+// the call runs in the device's scratch array, its partials sized to the plan.
+int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, size_t ws_bytes, hipStream_t stream,
+              bool noalloc) {
   if (!a || !st) return fail(CSA2_ERR_ARG, "group args and state are required");
   if (a->n_layers < 1 || !a->layers) return fail(CSA2_ERR_ARG, "at least one layer is required");
   if (a->ratio != 1 && a->ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
@@ -628,10 +701,21 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
       if (L.idx_w && !aligned(L.idx_w, 4)) return fail(CSA2_ERR_ARG, "layer %d: idx_w alignment", l);
     }
   }
-  const WsLayout w = ws_for(a->batch, a->n_q, std::max<int64_t>(max_ne, kMaxPool));
+  const int64_t max_items = std::max<int64_t>(max_ne, kMaxPool);
+  const WsLayout w = noalloc ? ws_for(a->batch, a->n_q, max_items, plan_partial_units(a))
+                             : ws_for(a->batch, a->n_q, max_items);
+  if (noalloc) {
+    if (w.total > kScratchBytes)
+      return fail(CSA2_ERR_UNSUPPORTED,
+                  "csa2_run_group_noalloc: this call needs %zu bytes of scratch, the library holds %zu "
+                  "(fewer sequences, queries per sequence or entries per call fit)",
+                  w.total, kScratchBytes);
+    if ((rc = scratch_of_current_device(&workspace))) return rc;
+    ws_bytes = kScratchBytes;
+  }
   if ((rc = check_workspace(workspace, ws_bytes, w))) return rc;
 
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   int l = 0;
   while (l < a->n_layers) {
     const csa2_layer& L = a->layers[l];
@@ -687,6 +771,22 @@ int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspa
     if ((rc = run_attention(j, workspace, w, s))) return rc;
   }
   return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa2_run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  return run_group(a, st, workspace, ws_bytes, (hipStream_t)stream, false);
+}
+
+int csa2_run_group_noalloc(const csa2_group_args* a, csa2_group_state* st, void* stream) {
+  prof_suspend(true);  // timing records would create events
+  const int rc = run_group(a, st, nullptr, 0, (hipStream_t)stream, true);
+  prof_suspend(false);
+  return rc;
 }
 
 }  // extern "C"

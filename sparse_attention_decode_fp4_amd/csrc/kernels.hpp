@@ -118,6 +118,7 @@ struct IndexPass {
 // Kernel classes of the optional timing records (csa2_profile_*).
 int prof_begin(int32_t kernel, hipStream_t stream);
 void prof_end(int handle, hipStream_t stream);
+void prof_suspend(bool on);  // while on, this thread's launches are not timed
 
 // One decode step's appends: sequence s writes its token at position
 // seq.a[s] (see csa2_append).

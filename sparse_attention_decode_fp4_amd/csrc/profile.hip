@@ -18,6 +18,7 @@ struct Record {
 
 std::mutex g_mu;
 bool g_on = false;
+thread_local bool t_suspended = false;  // this thread's launches go unrecorded
 std::vector<Record> g_records;
 std::vector<hipEvent_t> g_free;
 
@@ -34,8 +35,10 @@ hipEvent_t take_event() {
 
 }  // namespace
 
+void prof_suspend(bool on) { t_suspended = on; }
+
 int prof_begin(int32_t kernel, hipStream_t stream) {
-  if (!g_on) return -1;
+  if (!g_on || t_suspended) return -1;
   std::lock_guard<std::mutex> lk(g_mu);
   Record r{kernel, take_event(), take_event()};
   if (!r.start || !r.stop) return -1;

@@ -205,6 +205,31 @@ def test_flat_full_drops_an_earlier_pool(m):
     assert f(ctypes.byref(g), ctypes.byref(st), _p(), 16, None) == m.ERR_WORKSPACE
 
 
+def test_noalloc_validates_like_run_group_and_rejects_calls_past_its_scratch(m):
+    f = m.lib.csa2_run_group_noalloc
+    st = m.GroupState()
+    st.indices = _p()
+    layers = (m.Layer * 1)()
+    layers[0].q, layers[0].swa, layers[0].out, layers[0].idx_q = _p(0x600000), _p(0x700000), _p(0x800000), _p(0x900000)
+    layers[0].mode = m.MODE_REUSE
+    n_q, n_ent = 31, 8_000_000
+    g = m.GroupArgs()
+    qp, ne = (ctypes.c_int64 * 1)(n_ent - n_q), (ctypes.c_int64 * 1)(n_ent)
+    g.batch, g.n_q, g.ratio = 1, n_q, 1
+    g.q_pos0, g.n_entries = (ctypes.cast(x, ctypes.c_void_p) for x in (qp, ne))
+    g.swa_stride, g.swa_ring, g.softmax_scale, g.n_layers, g.layers = 256, 256, 1.0, 1, layers
+    assert f(ctypes.byref(g), ctypes.byref(st), None) == m.ERR_STATE   # Reuse before any Full
+    assert f(None, ctypes.byref(st), None) == m.ERR_ARG
+    kv = m.KV()
+    kv.nib, kv.scale, kv.k8, kv.kscale, kv.stride = _p(0x200000), _p(0x300000), _p(0x400000), _p(0x500000), n_ent
+    layers[0].mode, layers[0].kv = m.MODE_FULL, ctypes.pointer(kv)
+    # 31 query rows over 8 million entries need far more than the scratch holds
+    assert f(ctypes.byref(g), ctypes.byref(st), None) == m.ERR_UNSUPPORTED
+    msg = m.lib.csa2_last_error()
+    assert b"scratch" in msg and str(32 << 20).encode() in msg
+    assert st.has_full == 0 and st.has_indices == 0  # a refused call leaves the state as it was
+
+
 def _pages(m, table=None, table_stride=1, page_size=128, pool_entries=1024):
     pg = m.Pages()
     pg.table = _p(0x8000) if table is None else table
