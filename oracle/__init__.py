@@ -22,7 +22,7 @@ from . import attention, formats, group, indexer, kv, storage  # noqa: F401
 from .attention import sparse_swa_attention, swa_token_range  # noqa: F401
 from .formats import bf16_value, e2m1_encode, e2m1_value, e4m3_encode, e4m3_value  # noqa: F401
 from .group import FULL, REINDEX, REUSE, new_state, run_group  # noqa: F401
-from .indexer import (index_flat, index_hier, index_pool, scores, scores_many,  # noqa: F401
-                      top_k, visible_entries)
+from .indexer import (index_flat, index_flat_pool, index_hier, index_pool, scores,  # noqa: F401
+                      scores_many, top_k, visible_entries)
 from .kv import (block_keys, compress_pairs, fp4_decode_rows, fp4_encode_rows,  # noqa: F401
                  index_key_decode, index_key_encode, quantize_kv)

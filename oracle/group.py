@@ -25,7 +25,7 @@ Readings:
 import numpy as np
 
 from .attention import sparse_swa_attention
-from .indexer import TOP_K, index_flat, index_hier, index_pool, visible_entries
+from .indexer import TOP_K, index_flat, index_flat_pool, index_hier, index_pool, visible_entries
 
 FULL, REINDEX, REUSE = 0, 1, 2
 
@@ -40,6 +40,8 @@ def _index_one(kind, kv, b, idx_q, idx_w, n_vis, k):
     if kind == "hier":
         return index_hier(idx_q, idx_w, kv["k8"][b], kv["ks"][b], kv["bk8"][b],
                           kv["bks"][b], n_vis, k)
+    if kind == "flatpool":
+        return index_flat_pool(idx_q, idx_w, kv["k8"][b], kv["ks"][b], n_vis, k)
     raise ValueError(kind)
 
 
@@ -52,8 +54,11 @@ def run_group(layers, state, q_pos0, n_entries, swa_pos0, ratio=1,
     (f32 [B, n_q, 4] or None) for Full and Reindex, and "kv" for Full: per
     sequence lists "nib", "scale", "k8", "ks" (+ "bk8", "bks" for kind "hier").
     state: dict from new_state(), updated in place.
-    reindex_kind "pool" ranks only the pool kept by the last hierarchical Full
-    layer instead of every visible position."""
+    kind "flatpool" indexes Full layers flat and keeps the pool of the blocks
+    their token scores rank highest (index_flat_pool).  reindex_kind "pool"
+    ranks only the pool kept by the last Full layer instead of every visible
+    position; a Full layer that keeps no pool (kind "flat") drops the pool
+    of an earlier one, which belonged to the KV it replaces."""
     outs = []
     for layer in layers:
         mode = layer["mode"]
@@ -66,15 +71,15 @@ def run_group(layers, state, q_pos0, n_entries, swa_pos0, ratio=1,
         kv = state["kv"]
         if mode in (FULL, REINDEX):
             idx = np.full((B, n_q, k), -1, dtype=np.int32)
-            pools = ([[None] * n_q for _ in range(B)]
-                     if (mode == FULL and kind == "hier") else None)
+            keeps_pool = mode == FULL and kind in ("hier", "flatpool")
+            pools = [[None] * n_q for _ in range(B)] if keeps_pool else None
             for b in range(B):
                 for i in range(n_q):
                     n_vis = min(int(n_entries[b]), visible_entries(int(q_pos0[b]) + i, ratio))
                     w = None if layer.get("idx_w") is None else layer["idx_w"][b, i]
                     if mode == REINDEX and reindex_kind == "pool":
                         if state["pool"] is None:
-                            raise RuntimeError("pool Reindex needs a hierarchical Full first")
+                            raise RuntimeError("pool Reindex needs a Full layer that keeps a pool")
                         idx[b, i] = index_pool(layer["idx_q"][b, i], w, kv["k8"][b],
                                                kv["ks"][b], state["pool"][b][i], k)
                         continue
@@ -84,7 +89,7 @@ def run_group(layers, state, q_pos0, n_entries, swa_pos0, ratio=1,
                     if pools is not None:
                         pools[b][i] = pool
             state["indices"] = idx
-            if pools is not None:
+            if mode == FULL:
                 state["pool"] = pools
         elif state["indices"] is None:
             raise RuntimeError("Reuse layer before any indices exist")

@@ -20,7 +20,13 @@ Readings (the pages give no formula):
     min(k, n); report them in ascending position, padded with -1;
   * hierarchical: the same score over the block keys, top 2,048 blocks (ties
     to the lower block), the pool is every visible position of those blocks,
-    then top-512 positions inside the pool.
+    then top-512 positions inside the pool;
+  * flat with a pool (the other reading of the same section: the pool comes
+    from the Full layer's own token scores, aggregated per block): every
+    visible position is scored and the top 512 are the indices; a block of 8
+    scores the largest score among its visible positions (so the blocks of
+    the 512 indices are always kept), top 2,048 blocks (ties to the lower
+    block), the pool is every visible position of those blocks.
 """
 
 import numpy as np
@@ -107,3 +113,24 @@ def index_hier(idx_q, idx_w, k8, ks, bk8, bks, n_visible, k=TOP_K,
     pool = np.full(n_blocks * block, -1, dtype=np.int32)
     pool[: len(pos)] = pos
     return index_pool(idx_q, idx_w, k8, ks, pos, k), pool
+
+
+def index_flat_pool(idx_q, idx_w, k8, ks, n_visible, k=TOP_K, n_blocks=N_BLOCKS, block=BLOCK):
+    """Flat indexer that also keeps a pool built from the same token scores:
+    block b (positions b*block .. b*block + block - 1) scores the largest
+    score of its visible positions; the top n_blocks blocks are kept.
+
+    Returns (indices i32[k] as index_flat, pool i32[n_blocks * block] ascending, -1 padded)."""
+    s = scores(idx_q, idx_w, k8[:n_visible], ks[:n_visible])
+    indices = top_k(s, np.arange(n_visible), k)
+    nb_visible = -(-n_visible // block)
+    padded = np.full(nb_visible * block, -np.inf)
+    padded[:n_visible] = s
+    bs = padded.reshape(nb_visible, block).max(axis=1)        # block max over visible positions
+    chosen_blocks = top_k(bs, np.arange(nb_visible), n_blocks)
+    chosen_blocks = chosen_blocks[chosen_blocks >= 0]
+    pos = (chosen_blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    pos = pos[pos < n_visible]
+    pool = np.full(n_blocks * block, -1, dtype=np.int32)
+    pool[: len(pos)] = pos
+    return indices, pool

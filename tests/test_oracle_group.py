@@ -215,3 +215,65 @@ def test_pool_reindex_needs_a_hierarchical_pool():
     oracle.run_group([_hier_layer(oracle.FULL, 13, 0, kv)], st, [HCTX - 1], [HCTX], [HCTX - 128], kind="flat")
     with pytest.raises(RuntimeError):
         _hier_run([_hier_layer(oracle.REINDEX, 13, 1)], st, "pool")
+
+
+# --- flat Full layer that keeps a pool from its own token scores -------------
+def test_flat_pool_keeps_the_blocks_of_the_best_token_scores():
+    kv = _hier_kv(14)
+    st = oracle.new_state()
+    full = _hier_layer(oracle.FULL, 14, 0, kv)
+    oracle.run_group([full], st, [HCTX - 1], [HCTX], [HCTX - 128], kind="flatpool")
+    iq = full["idx_q"][0, 0]
+    tsc = _brute_scores(iq, kv["k8"][0], kv["ks"][0])
+    # the indices are the flat top 512 over the whole context
+    flat = _brute_top(tsc, np.arange(HCTX), 512)
+    assert np.array_equal(st["indices"][0, 0], flat)
+    # block b scores the largest of its 8 token scores
+    bmax = [max(tsc[p] for p in range(8 * b, min(8 * b + 8, HCTX))) for b in range(-(-HCTX // 8))]
+    blocks = _brute_top(np.asarray(bmax), np.arange(len(bmax)), 2048)
+    want_pool = sorted(p for b in blocks for p in range(8 * b, 8 * b + 8) if p < HCTX)
+    pool = np.asarray(st["pool"][0][0])
+    assert np.array_equal(pool[pool >= 0], want_pool) and np.all(pool[len(want_pool):] == -1)
+    assert set(flat) <= set(want_pool)      # the indices' blocks are always kept
+    # a different pool from the block-key reading on the same input
+    _, hpool = oracle.index_hier(iq, None, kv["k8"][0], kv["ks"][0], kv["bk8"][0], kv["bks"][0], HCTX)
+    assert not np.array_equal(hpool, pool)
+    # a pool Reindex with a fresh query ranks that pool
+    re = _hier_layer(oracle.REINDEX, 14, 1)
+    oracle.run_group([re], st, [HCTX - 1], [HCTX], [HCTX - 128], kind="flatpool", reindex_kind="pool")
+    iq2 = re["idx_q"][0, 0]
+    wp = np.asarray(want_pool)
+    assert np.array_equal(st["indices"][0, 0], _brute_top(_brute_scores(iq2, kv["k8"][0][wp], kv["ks"][0][wp]), wp, 512))
+
+
+def test_flat_pool_block_ties_and_partial_blocks():
+    iq = np.full((4, 64), 0x38, np.uint8)            # every code 1.0
+    k8 = np.full((37, 64), 0x38, np.uint8)
+    ks = np.ones(37, np.float32)
+    # equal scores everywhere: the lower blocks win, the partial block 4 keeps
+    # its 5 positions
+    idx, pool = oracle.index_flat_pool(iq, None, k8, ks, 37, k=3, n_blocks=5)
+    assert list(idx) == [0, 1, 2]
+    assert list(pool[:37]) == list(range(37)) and np.all(pool[37:] == -1)
+    idx, pool = oracle.index_flat_pool(iq, None, k8, ks, 37, k=3, n_blocks=2)
+    assert list(pool[:16]) == list(range(16)) and np.all(pool[16:] == -1)
+    # one larger key in the partial block and one in block 1: those two blocks
+    ks2 = ks.copy()
+    ks2[35], ks2[9] = 2.0, 1.5
+    idx, pool = oracle.index_flat_pool(iq, None, k8, ks2, 37, k=2, n_blocks=2)
+    assert list(idx) == [9, 35]
+    assert list(pool[:13]) == list(range(8, 16)) + list(range(32, 37)) and np.all(pool[13:] == -1)
+    # a position past n_visible never counts for its block
+    idx, pool = oracle.index_flat_pool(iq, None, k8, ks2, 34, k=2, n_blocks=1)
+    assert list(pool[:8]) == list(range(8, 16)) and np.all(pool[8:] == -1)
+
+
+def test_flat_full_drops_an_earlier_pool():
+    st = oracle.new_state()
+    kv = _hier_kv(15)
+    _hier_run([_hier_layer(oracle.FULL, 15, 0, kv)], st)
+    assert st["pool"] is not None
+    oracle.run_group([_hier_layer(oracle.FULL, 15, 1, kv)], st, [HCTX - 1], [HCTX], [HCTX - 128], kind="flat")
+    assert st["pool"] is None
+    with pytest.raises(RuntimeError):
+        _hier_run([_hier_layer(oracle.REINDEX, 15, 2)], st, "pool")
