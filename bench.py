@@ -50,37 +50,60 @@ def parse():
                     help="only run a plain device copy of 256 MiB five times (the known-size reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     ap.add_argument("--page-size", type=int, default=256, help="entries per page of --workload paged")
-    ap.add_argument("--workload", choices=["decode", "multi", "prefill", "hier", "paged"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "multi", "prefill", "hier", "paged", "full64k", "tiny4k"],
+                    default="decode",
                     help="decode: the 128K decode group (default, the headline); prefill: a 4,096-token "
                          "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers; hier: the "
                          "hierarchical Full layer at 1M context, batch 4; multi: the decode group with 4 query "
-                         "tokens per sequence (speculative decoding)")
+                         "tokens per sequence (speculative decoding); full64k: one Full layer, batch 8, 65,536 "
+                         "entries with lognormal channel scales; tiny4k: one Full layer, batch 1, 4,096 entries")
     return ap.parse_args()
 
 
-def algorithmic_bytes_per_qtok(ctx, nq=1):
-    """Bytes one query token must move through one 4-layer group: its share
-    of the key scan of the Full/Reindex layer (the nq query tokens of a
-    sequence share one scan), and per layer the 512 gathered entries, the 128
-    window rows, its query and output, the index list."""
-    per_layer = 512 * ENTRY_BYTES + 128 * ROW_BYTES + Q_BYTES + OUT_BYTES + IDX_BYTES
-    return ctx * KEY_BYTES / nq + IDXQ_BYTES + 4 * per_layer
+def algorithmic_bytes_per_qtok(ctx, nq=1, layers=4):
+    """Bytes one query token must move through one group of `layers` layers:
+    its share of the key scan of the Full/Reindex layer (the nq query tokens
+    of a sequence share one scan), and per layer the 512 gathered entries
+    (all of them when fewer are visible), the 128 window rows, its query and
+    output, the index list."""
+    per_layer = min(512, ctx) * ENTRY_BYTES + 128 * ROW_BYTES + Q_BYTES + OUT_BYTES + IDX_BYTES
+    return ctx * KEY_BYTES / nq + IDXQ_BYTES + layers * per_layer
+
+
+def host_cpu():
+    """The host's logical CPUs this process may use, and the CPU model."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return nproc, model
 
 
 def cpu_baseline(x0, k0, layers_host, ctx, seconds):
-    """The oracle, as it stands, on sequence 0 of the first cache copy: both
-    group runs per iteration (2 query-tokens), repeated for ~`seconds`."""
-    import numpy as np
+    """The oracle, as it stands, on sequence 0 of the first cache copy: every
+    group run of a step per iteration (one query-token each), repeated for
+    ~`seconds`.  `cores` is the thread count it runs with: numpy's BLAS pool
+    (the rest of the oracle is single-threaded numpy)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = os.cpu_count()
+    nproc, model = host_cpu()
     nib, sc, k8, ks = oracle.quantize_kv(x0, 1, k0)          # setup, untimed
     kv = dict(nib=[nib], scale=[sc], k8=[k8], ks=[ks])
     runs = []
-    for run in range(2):
+    for run in range(len(layers_host)):
         ls = []
         for j, L in enumerate(layers_host[run]):
             d = dict(mode=L["mode"], q=L["q"][:1], swa=L["swa"][:1])
@@ -99,8 +122,11 @@ def cpu_baseline(x0, k0, layers_host, ctx, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": 2 * iters / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"sequence 0 of the batch, both group runs (F+3U, R+3U) = 2 query-tokens per "
+    plans = ", ".join("+".join("F" if L["mode"] == oracle.FULL else "R" if L["mode"] == oracle.REINDEX else "U"
+                               for L in ls) for ls in runs)
+    return {"value": len(runs) * iters / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "nproc": nproc, "cpu_model": model,
+            "sample": f"sequence 0 of the batch, group runs ({plans}) = {len(runs)} query-token(s) per "
                       f"iteration, {iters} iterations in {el:.1f} s; cache encoding excluded"}
 
 
@@ -346,6 +372,28 @@ def hier(args):
 COPY_BYTES = 256 << 20
 
 
+def stream_copy(reps=20):
+    """The device's streaming rate: a plain copy of 1 GiB (read + write),
+    HIP events around `reps` copies, against the published HBM peak."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    s = a.elapsed_time(b) / 1000.0 / reps
+    gbs = 2 * 4 * n / s / 1e9
+    del src, dst
+    return {"kind": "device copy of 1 GiB (read + write)", "GBs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def calibrate_copy():
     """A plain device-to-device copy of COPY_BYTES, five times: under
     rocprofv3 --pmc FETCH_SIZE (or WRITE_SIZE) each dispatch should read (and
@@ -400,6 +448,11 @@ def main():
 
     dev = "cuda"
     B, ctx, C = args.batch, args.ctx, args.copies
+    lognormal = False
+    if args.workload in ("full64k", "tiny4k"):  # the Full-layer decode configurations
+        c = gen.CONFIGS[1 if args.workload == "full64k" else 0]
+        B, ctx, lognormal = c["batch"], c["ctx"], c["lognormal"]
+    full_only = args.workload in ("full64k", "tiny4k")
     nq = 4 if args.workload == "multi" else 1   # query tokens per sequence per step
     paged, page = args.workload == "paged", args.page_size
     if paged and ctx % page:
@@ -413,7 +466,7 @@ def main():
         k8 = torch.empty((B * ctx, 64), dtype=torch.uint8, device=dev)
         ks = torch.empty((B * ctx,), dtype=torch.float32, device=dev)
         for b in range(B):
-            x = gen.latent(ctx, seed + 100 * c, seq=b, device=dev)
+            x = gen.latent(ctx, seed + 100 * c, seq=b, lognormal=lognormal, device=dev)
             k = gen.index_key(ctx, seed + 100 * c, seq=b, device=dev)
             sl = slice(b * ctx, (b + 1) * ctx)
             csa2.csa2_quantize_kv(x, k_in=k, out=[nib[sl], sc[sl], k8[sl], ks[sl]])
@@ -439,7 +492,7 @@ def main():
     torch.cuda.synchronize()
     # ---- per-layer inputs of the two runs (shared by the copies)
     q_pos0, n_entries, swa_pos0 = [ctx - nq] * B, [ctx] * B, [ctx - nq - 127] * B
-    plans = [["F", "U", "U", "U"], ["R", "U", "U", "U"]]
+    plans = [["F"]] if full_only else [["F", "U", "U", "U"], ["R", "U", "U", "U"]]
     mode_of = {"F": csa2.MODE_FULL, "R": csa2.MODE_REINDEX, "U": csa2.MODE_REUSE}
     layers = []
     for run, plan in enumerate(plans):
@@ -465,6 +518,9 @@ def main():
         csa2.csa2_run_group(ws, states[c], layers[1], q_pos0, n_entries, swa_pos0)
 
     def step(i):
+        if full_only:
+            run_full(i % C)
+            return
         run_full((2 * i) % C)
         run_reindex((2 * i + 1) % C)
 
@@ -499,7 +555,7 @@ def main():
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for g_i in range(C // 2):
+            for g_i in range(C if full_only else C // 2):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=s):
                     step(g_i)
@@ -516,15 +572,18 @@ def main():
 
     best_s = min(eager_s, graph_s) if graph_s is not None else eager_s
     append = append_timing(csa2, gen, B, dev) if nq == 1 and not paged else None
-    qtok_per_step = 2 * B * nq
+    copy = stream_copy()
+    n_runs, n_layers = len(plans), len(plans[0])
+    qtok_per_step = n_runs * B * nq
     value = qtok_per_step * args.steps / best_s
-    step_bytes = int(2 * B * nq * algorithmic_bytes_per_qtok(ctx, nq))
+    step_bytes = int(n_runs * B * nq * algorithmic_bytes_per_qtok(ctx, nq, n_layers))
     scan_bytes = B * ctx * KEY_BYTES                       # one launch scans every sequence once
     scan_avg_s = scan_ms / 1000.0 / scan_n
     achieved = scan_bytes / scan_avg_s / 1e9
     line = {
         "metric": (f"CSA2 multi-token decode query-tokens/s at 128K ctx ({nq} query tokens per sequence)" if nq > 1 else
                    f"CSA2 decode query-tokens/s at 128K ctx, paged KV ({page}-entry pages)" if paged else
+                   f"CSA2 Full-layer decode query-tokens/s, batch {B} at {ctx} ctx" if full_only else
                    "CSA2 decode query-tokens/s at 128K ctx; % of peak HBM GB/s"),
         "value": round(value, 1),
         "unit": "query-tokens/s",
@@ -537,16 +596,23 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"decode group of 4 layers run as Full+3 Reuse then Reindex+3 Reuse, "
-                               f"batch {B}, {ctx} FP4 entries per sequence, top-512 + 128-token window"
-                               + ("" if nq == 1 else f", {nq} query tokens per sequence")
-                               + ("" if not paged else f", caches as a pool of {page}-entry pages in random order"),
-                   "batch": B, "ctx": ctx, "query_tokens_per_sequence": nq, "layers_per_step": 8, "query_tokens_per_step": qtok_per_step,
+        "config": {"workload": (f"one Full layer, batch {B}, {ctx} FP4 entries per sequence"
+                                + (" (N(0,1) latents times lognormal(0, 0.5) channel scales)" if lognormal else "")
+                                + ", top-512 + 128-token window") if full_only else
+                               (f"decode group of 4 layers run as Full+3 Reuse then Reindex+3 Reuse, "
+                                f"batch {B}, {ctx} FP4 entries per sequence, top-512 + 128-token window"
+                                + ("" if nq == 1 else f", {nq} query tokens per sequence")
+                                + ("" if not paged else f", caches as a pool of {page}-entry pages in random order")),
+                   "batch": B, "ctx": ctx, "query_tokens_per_sequence": nq, "layers_per_step": n_runs * n_layers,
+                   "query_tokens_per_step": qtok_per_step,
                    "cache_copies": C, "timing": "graph replay" if best_s == graph_s else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if paged else scan_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": scan_traffic() if args.workload == "decode" else None,
                      "kernel": "k_index_scan", "bytes_per_launch": scan_bytes,
-                     "avg_launch_us": round(scan_avg_s * 1e6, 3)},
+                     "avg_launch_us": round(scan_avg_s * 1e6, 3),
+                     "frac_of_stream_copy": round(achieved / copy["GBs"], 4)},
+        "stream_copy": copy,
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved_GBs": round(step_bytes * args.steps / best_s / 1e9, 1),
                      "frac": round(step_bytes * args.steps / best_s / 1e9 / HBM_PEAK_GBS, 4)},
@@ -556,10 +622,10 @@ def main():
         "append": append,
     }
     if not args.no_cpu_baseline and nq == 1 and not paged:
-        x0 = gen.latent(ctx, seed, seq=0, device=dev).cpu().numpy()
+        x0 = gen.latent(ctx, seed, seq=0, lognormal=lognormal, device=dev).cpu().numpy()
         k0 = gen.index_key(ctx, seed, seq=0, device=dev).cpu().numpy()
         host_layers = []
-        for run in range(2):
+        for run in range(n_runs):
             hl = []
             for L in layers[run]:
                 h = dict(mode=L["mode"], q=gen.bf16_bits(L["q"]), swa=gen.bf16_bits(L["swa"]))

@@ -72,6 +72,7 @@ extern "C" {
 #define CSA2_INDEX_FLAT 0 /* score every visible position                           */
 #define CSA2_INDEX_HIER 1 /* blocks first, then positions inside the kept blocks    */
 #define CSA2_INDEX_POOL 2 /* score only a given candidate pool                      */
+#define CSA2_INDEX_FLAT_POOL 3 /* FLAT, and a pool of the blocks its scores rank highest */
 
 /* Layer modes. */
 #define CSA2_MODE_FULL 0
@@ -202,9 +203,14 @@ typedef struct csa2_pages {
  * keys), keeps the top n_blocks blocks, and scores the visible positions of
  * those blocks; out_pool (optional) receives the kept positions in ascending
  * order, -1 padded.  POOL scores only the positions in cand, which must be
- * ascending with any -1 padding at the end.  With n_q >= 32 (a prefill
- * chunk) FLAT scoring runs on fp8 MFMA; HIER and POOL then return
- * CSA2_ERR_UNSUPPORTED.
+ * ascending with any -1 padding at the end.  FLAT_POOL is FLAT (the same
+ * out_idx) that also keeps a pool, the other reading of the same section:
+ * block b (positions 8b .. 8b+7) scores the largest score among its visible
+ * positions, the top n_blocks blocks are kept (score descending, then lower
+ * block; near-ties settled on exact scores as above), and out_pool
+ * (required) receives their visible positions as for HIER.  With n_q >= 32
+ * (a prefill chunk) FLAT scoring runs on fp8 MFMA; HIER, POOL and FLAT_POOL
+ * then return CSA2_ERR_UNSUPPORTED.
  */
 typedef struct csa2_index_args {
   int32_t kind;              /* CSA2_INDEX_*                                          */
@@ -224,9 +230,9 @@ typedef struct csa2_index_args {
   const int32_t* cand;       /* POOL: device [batch][n_q][n_cand] positions, -1 = none */
   int32_t n_cand;            /* POOL: candidates per query, 1..16384                  */
   int32_t k;                 /* entries kept per query, 1..CSA2_MAX_K (512 normally)  */
-  int32_t n_blocks;          /* HIER: blocks kept, 1..CSA2_MAX_K (2048 normally)      */
+  int32_t n_blocks;          /* HIER, FLAT_POOL: blocks kept, 1..CSA2_MAX_K (2048 normally) */
   int32_t* out_idx;          /* device [batch][n_q][k] (out)                          */
-  int32_t* out_pool;         /* HIER: device [batch][n_q][n_blocks*8] or NULL (out)   */
+  int32_t* out_pool;         /* HIER, FLAT_POOL: device [batch][n_q][n_blocks*8] (out; optional for HIER) */
   csa2_pages pages;          /* paged k8/kscale (FLAT with n_q < 32), or all zero     */
 } csa2_index_args;
 
@@ -291,8 +297,10 @@ int csa2_sparse_swa_attn(const csa2_attn_args* a, void* workspace, size_t ws_byt
  * Every layer then runs csa2_sparse_swa_attn with its own q and window rows.
  * The state persists across calls; Reindex/Reuse with no Full in the state
  * return CSA2_ERR_STATE.  With index_kind HIER the Full layer uses the
- * hierarchical indexer and stores its pool; reindex_kind POOL makes Reindex
- * rank only that pool.
+ * hierarchical indexer and stores its pool; with FLAT_POOL it indexes flat
+ * and stores the pool of the blocks its token scores rank highest (both
+ * need state.pool).  reindex_kind POOL makes Reindex rank only that pool; a
+ * Full layer that stores no pool drops the state's earlier pool.
  */
 typedef struct csa2_kv {
   const uint8_t* nib;      /* device, sequence s at + s*stride*256                    */
@@ -326,7 +334,7 @@ typedef struct csa2_group_state {
 
 typedef struct csa2_group_args {
   int32_t batch, n_q, ratio;
-  int32_t index_kind;      /* CSA2_INDEX_FLAT or CSA2_INDEX_HIER for Full layers      */
+  int32_t index_kind;      /* CSA2_INDEX_FLAT, _HIER or _FLAT_POOL for Full layers    */
   int32_t reindex_kind;    /* CSA2_INDEX_FLAT or CSA2_INDEX_POOL for Reindex layers   */
   const int64_t* q_pos0;   /* host [batch]                                            */
   const int64_t* n_entries;/* host [batch]                                            */

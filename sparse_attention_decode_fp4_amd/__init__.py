@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 D_LATENT, NIB_BYTES, SCALE_BYTES = 512, 256, 32
 D_INDEX, H_INDEX, H_ATTN = 64, 4, 16
 TOP_K, SWA, BLOCK, N_BLOCKS, MAX_K = 512, 128, 8, 2048, 2048
-INDEX_FLAT, INDEX_HIER, INDEX_POOL = 0, 1, 2
+INDEX_FLAT, INDEX_HIER, INDEX_POOL, INDEX_FLAT_POOL = 0, 1, 2, 3
 MODE_FULL, MODE_REINDEX, MODE_REUSE = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_STATE, ERR_WORKSPACE, ERR_HIP = range(6)
 (K_QUANTIZE, K_BLOCK_KEYS, K_INDEX_SCAN, K_INDEX_SAMPLE, K_INDEX_SELECT, K_ATTENTION,
@@ -291,14 +291,15 @@ def csa2_index_topk(ws, idx_q, k8, kscale, n_entries, q_pos0, k_stride, *, kind=
                     k=TOP_K, n_blocks=N_BLOCKS, out_idx=None, out_pool=None, want_pool=False,
                     pages=None, stream=None):
     """Top-k positions per query.  idx_q u8 [batch, n_q, 4, 64]; returns
-    out_idx int32 [batch, n_q, k] (and the pool for HIER when want_pool).
-    With pages (make_pages) k8/kscale are pools and k_stride is not read."""
+    out_idx int32 [batch, n_q, k] (and the pool for HIER or FLAT_POOL when
+    want_pool; FLAT_POOL always makes one).  With pages (make_pages)
+    k8/kscale are pools and k_stride is not read."""
     _need(idx_q, torch.uint8, "idx_q")
     batch, n_q = idx_q.shape[0], idx_q.shape[1]
     dev = idx_q.device
     if out_idx is None:
         out_idx = torch.empty((batch, n_q, k), dtype=torch.int32, device=dev)
-    if kind == INDEX_HIER and want_pool and out_pool is None:
+    if (kind == INDEX_FLAT_POOL or (kind == INDEX_HIER and want_pool)) and out_pool is None:
         out_pool = torch.empty((batch, n_q, n_blocks * BLOCK), dtype=torch.int32, device=dev)
     a = IndexArgs()
     a.kind, a.batch, a.n_q, a.ratio = kind, batch, n_q, ratio

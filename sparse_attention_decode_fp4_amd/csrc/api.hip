@@ -44,9 +44,10 @@ constexpr int64_t kMaxPartialUnits = 2048;  // (layer,row) x split slots of atte
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t stats, chunk_info, seg_list, blocks, nsel, partial;
+  size_t stats, chunk_info, seg_list, blocks, nsel, block_max, row_ksm, partial;
   size_t pf_sample, pf_thresh, pf_count, pf_list, total;
   int32_t max_chunks;     // scan chunks per row covered by the segment buffers
+  int64_t max_blocks;     // blocks of 8 items per row covered by block_max
   int64_t partial_units;  // (layer,row) x split slots the attention partials hold
 };
 
@@ -65,6 +66,9 @@ WsLayout ws_layout(int64_t rows, int64_t max_items, int64_t pf_rows = 0,
   w.seg_list = take((size_t)rows * w.max_chunks * kSeg * 8);
   w.blocks = take((size_t)rows * CSA2_MAX_K * 4);
   w.nsel = take((size_t)rows * 4);
+  w.max_blocks = (std::max<int64_t>(max_items, 1) + 7) / 8;
+  w.block_max = take((size_t)rows * w.max_blocks * 4);
+  w.row_ksm = take((size_t)rows * 4);
   w.partial = take((size_t)partial_units * kPartFloats * 4);
   w.pf_sample = take((size_t)pf_rows * kPfSample * 4);
   w.pf_thresh = take((size_t)pf_rows * 4);
@@ -130,7 +134,7 @@ PageMap page_map(const csa2_pages& pg, int s0) {
 
 int validate_index(const csa2_index_args* a) {
   if (!a) return fail(CSA2_ERR_ARG, "index args are NULL");
-  if (a->kind < CSA2_INDEX_FLAT || a->kind > CSA2_INDEX_POOL) return fail(CSA2_ERR_ARG, "bad index kind %d", a->kind);
+  if (a->kind < CSA2_INDEX_FLAT || a->kind > CSA2_INDEX_FLAT_POOL) return fail(CSA2_ERR_ARG, "bad index kind %d", a->kind);
   if (a->batch < 1 || a->n_q < 1) return fail(CSA2_ERR_ARG, "batch and n_q must be >= 1");
   if (a->ratio != 1 && a->ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
   if (a->k < 1 || a->k > CSA2_MAX_K) return fail(CSA2_ERR_UNSUPPORTED, "k must be in 1..%d", CSA2_MAX_K);
@@ -149,7 +153,7 @@ int validate_index(const csa2_index_args* a) {
   }
   if (max_ne > kMaxEntries) return fail(CSA2_ERR_UNSUPPORTED, "at most %lld entries per sequence", (long long)kMaxEntries);
   if (a->pages.table) {
-    if (a->kind != CSA2_INDEX_FLAT || a->n_q >= kPrefillMinQ)
+    if ((a->kind != CSA2_INDEX_FLAT && a->kind != CSA2_INDEX_FLAT_POOL) || a->n_q >= kPrefillMinQ)
       return fail(CSA2_ERR_UNSUPPORTED, "paged caches take FLAT indexing with fewer than %d queries per sequence", kPrefillMinQ);
     if (int rc = validate_pages(a->pages, max_ne)) return rc;
   } else if (a->batch > 1 && a->k_stride < max_ne) {
@@ -162,8 +166,13 @@ int validate_index(const csa2_index_args* a) {
     if (a->batch > 1 && a->bk_stride < (max_ne + 7) / 8) return fail(CSA2_ERR_ARG, "bk_stride smaller than the block count");
     if (a->out_pool && !aligned(a->out_pool, 4)) return fail(CSA2_ERR_ARG, "out_pool must be 4-byte aligned");
   }
+  if (a->kind == CSA2_INDEX_FLAT_POOL) {
+    if (!a->out_pool || !aligned(a->out_pool, 4)) return fail(CSA2_ERR_ARG, "FLAT_POOL needs a 4-byte aligned out_pool");
+    if (a->n_blocks < 1 || a->n_blocks > CSA2_MAX_K) return fail(CSA2_ERR_UNSUPPORTED, "n_blocks must be in 1..%d", CSA2_MAX_K);
+  }
   if (a->kind != CSA2_INDEX_FLAT && a->n_q >= kPrefillMinQ)
-    return fail(CSA2_ERR_UNSUPPORTED, "HIER and POOL indexing take fewer than %d queries per sequence", kPrefillMinQ);
+    return fail(CSA2_ERR_UNSUPPORTED, "HIER, POOL and FLAT_POOL indexing take fewer than %d queries per sequence",
+                kPrefillMinQ);
   if (a->kind == CSA2_INDEX_POOL) {
     if (!a->cand || !aligned(a->cand, 4)) return fail(CSA2_ERR_ARG, "POOL needs a 4-byte aligned cand");
     if (a->n_cand < 1 || a->n_cand > kMaxPool) return fail(CSA2_ERR_UNSUPPORTED, "n_cand must be in 1..%d", kMaxPool);
@@ -175,7 +184,8 @@ int64_t index_max_items(const csa2_index_args* a) {
   int64_t m = 0;
   for (int s = 0; s < a->batch; ++s) m = std::max(m, a->n_entries[s]);
   if (a->kind == CSA2_INDEX_POOL) m = std::max<int64_t>(m, a->n_cand);
-  if (a->kind == CSA2_INDEX_HIER) m = std::max<int64_t>(m, (int64_t)a->n_blocks * CSA2_BLOCK);
+  if (a->kind == CSA2_INDEX_HIER || a->kind == CSA2_INDEX_FLAT_POOL)
+    m = std::max<int64_t>(m, (int64_t)a->n_blocks * CSA2_BLOCK);
   return m;
 }
 
@@ -198,7 +208,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     if (max_vis == 0) {  // nothing visible in these sequences: every output is -1
       hipError_t f = launch_fill_u32(reinterpret_cast<uint32_t*>(a->out_idx + row0 * a->k),
                                      (size_t)p.rows * a->k, 0xFFFFFFFFu, stream);
-      if (f == hipSuccess && a->kind == CSA2_INDEX_HIER && a->out_pool)
+      if (f == hipSuccess && (a->kind == CSA2_INDEX_HIER || a->kind == CSA2_INDEX_FLAT_POOL) && a->out_pool)
         f = launch_fill_u32(reinterpret_cast<uint32_t*>(a->out_pool + row0 * a->n_blocks * CSA2_BLOCK),
                             (size_t)p.rows * a->n_blocks * CSA2_BLOCK, 0xFFFFFFFFu, stream);
       if (f != hipSuccess) return hip_fail(f, "fill");
@@ -271,7 +281,24 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     p.k_stride = a->k_stride;
     p.out = a->out_idx + row0 * a->k;
     p.out_stride = a->k;
+    if (a->kind == CSA2_INDEX_FLAT_POOL) {  // the flat scan keeps its block maxima
+      p.block_max = at<uint32_t>(ws, w.block_max);
+      p.block_max_stride = w.max_blocks;
+      p.row_ksm = at<uint32_t>(ws, w.row_ksm);
+    }
     if ((e = launch_index_pass(p, stream, window, window_done)) != hipSuccess) return hip_fail(e, "index pass");
+    if (a->kind == CSA2_INDEX_FLAT_POOL) {  // then the blocks by their largest token score
+      IndexPass b = p;
+      b.block_level = 2;
+      b.k = a->n_blocks;
+      b.max_items = (max_vis + 7) / 8;
+      b.out = at<int32_t>(ws, w.blocks);
+      b.out_stride = CSA2_MAX_K;
+      b.out_count = at<int32_t>(ws, w.nsel);
+      b.out_pool = a->out_pool + row0 * a->n_blocks * CSA2_BLOCK;
+      b.pool_stride = a->n_blocks * CSA2_BLOCK;
+      if ((e = launch_index_pass(b, stream)) != hipSuccess) return hip_fail(e, "block-max pass");
+    }
   }
   return CSA2_OK;
 }
@@ -636,8 +663,8 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
   if (!a || !st) return fail(CSA2_ERR_ARG, "group args and state are required");
   if (a->n_layers < 1 || !a->layers) return fail(CSA2_ERR_ARG, "at least one layer is required");
   if (a->ratio != 1 && a->ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
-  if (a->index_kind != CSA2_INDEX_FLAT && a->index_kind != CSA2_INDEX_HIER)
-    return fail(CSA2_ERR_ARG, "index_kind must be FLAT or HIER");
+  if (a->index_kind != CSA2_INDEX_FLAT && a->index_kind != CSA2_INDEX_HIER && a->index_kind != CSA2_INDEX_FLAT_POOL)
+    return fail(CSA2_ERR_ARG, "index_kind must be FLAT, HIER or FLAT_POOL");
   if (a->reindex_kind != CSA2_INDEX_FLAT && a->reindex_kind != CSA2_INDEX_POOL)
     return fail(CSA2_ERR_ARG, "reindex_kind must be FLAT or POOL");
   if ((a->index_kind != CSA2_INDEX_FLAT || a->reindex_kind != CSA2_INDEX_FLAT) && a->n_q >= kPrefillMinQ)
@@ -669,7 +696,7 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       if ((rc = validate_kv_ptrs(L.kv->nib, L.kv->scale))) return rc;
       if (!L.kv->k8 || !L.kv->kscale || !aligned(L.kv->k8, 16)) return fail(CSA2_ERR_ARG, "layer %d: kv.k8/kscale", l);
       if (L.kv->pages.table) {
-        if (a->index_kind != CSA2_INDEX_FLAT || a->n_q >= kPrefillMinQ)
+        if (a->index_kind == CSA2_INDEX_HIER || a->n_q >= kPrefillMinQ)
           return fail(CSA2_ERR_UNSUPPORTED, "layer %d: paged caches take FLAT indexing with fewer than %d queries", l,
                       kPrefillMinQ);
         if ((rc = validate_pages(L.kv->pages, max_ne))) return rc;
@@ -678,17 +705,18 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       }
       if (a->index_kind == CSA2_INDEX_HIER && (!L.kv->bk8 || !L.kv->bkscale))
         return fail(CSA2_ERR_ARG, "layer %d: HIER needs block keys", l);
-      if (a->index_kind == CSA2_INDEX_HIER && !st->pool && a->reindex_kind == CSA2_INDEX_POOL)
+      const bool keeps_pool = a->index_kind == CSA2_INDEX_HIER || a->index_kind == CSA2_INDEX_FLAT_POOL;
+      if (keeps_pool && !st->pool && a->reindex_kind == CSA2_INDEX_POOL)
         return fail(CSA2_ERR_ARG, "POOL reindexing needs state.pool");
       has_full = has_idx = 1;
       paged = L.kv->pages.table != nullptr;
-      // a Full layer replaces the KV: only a hierarchical one leaves a pool
-      // of it (a flat one makes any earlier pool stale)
-      has_pool = (a->index_kind == CSA2_INDEX_HIER && st->pool) ? 1 : 0;
+      // a Full layer replaces the KV: only one that keeps a pool (HIER or
+      // FLAT_POOL) leaves one of it (a flat one makes any earlier pool stale)
+      has_pool = (keeps_pool && st->pool) ? 1 : 0;
     } else if (L.mode == CSA2_MODE_REINDEX) {
       if (!has_full) return fail(CSA2_ERR_STATE, "layer %d: REINDEX before any FULL layer", l);
       if (a->reindex_kind == CSA2_INDEX_POOL && !has_pool)
-        return fail(CSA2_ERR_STATE, "layer %d: POOL REINDEX without a hierarchical pool", l);
+        return fail(CSA2_ERR_STATE, "layer %d: POOL REINDEX without a pool from a HIER or FLAT_POOL Full layer", l);
       if (paged && (a->reindex_kind != CSA2_INDEX_FLAT || a->n_q >= kPrefillMinQ))
         return fail(CSA2_ERR_UNSUPPORTED, "layer %d: paged caches take FLAT indexing with fewer than %d queries", l,
                     kPrefillMinQ);
@@ -737,8 +765,9 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
     if (L.mode != CSA2_MODE_REUSE) {
       csa2_index_args ia{};
       const bool hier = (L.mode == CSA2_MODE_FULL && a->index_kind == CSA2_INDEX_HIER);
+      const bool flat_pool = (L.mode == CSA2_MODE_FULL && a->index_kind == CSA2_INDEX_FLAT_POOL && st->pool);
       const bool pool = (L.mode == CSA2_MODE_REINDEX && a->reindex_kind == CSA2_INDEX_POOL);
-      ia.kind = hier ? CSA2_INDEX_HIER : pool ? CSA2_INDEX_POOL : CSA2_INDEX_FLAT;
+      ia.kind = hier ? CSA2_INDEX_HIER : flat_pool ? CSA2_INDEX_FLAT_POOL : pool ? CSA2_INDEX_POOL : CSA2_INDEX_FLAT;
       ia.batch = a->batch; ia.n_q = a->n_q; ia.ratio = a->ratio;
       ia.q_pos0 = a->q_pos0; ia.n_entries = a->n_entries;
       ia.idx_q = L.idx_q; ia.idx_w = L.idx_w;
@@ -747,14 +776,15 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       ia.cand = st->pool; ia.n_cand = kMaxPool;
       ia.k = CSA2_TOP_K; ia.n_blocks = CSA2_N_BLOCKS;
       ia.out_idx = st->indices;
-      ia.out_pool = hier ? st->pool : nullptr;
+      ia.out_pool = (hier || flat_pool) ? st->pool : nullptr;
       ia.pages = st->kv.pages;
       // a flat decode pass in one launch runs the window tiles of the
       // attention in its select launch (they need nothing the select
       // computes), and the attention launch then takes the entry tiles only
       AttnPass wp;
       const AttnPass* win = nullptr;
-      if (ia.kind == CSA2_INDEX_FLAT && a->batch <= kMaxSeqPerLaunch && a->n_q < kPrefillMinQ) {
+      if ((ia.kind == CSA2_INDEX_FLAT || ia.kind == CSA2_INDEX_FLAT_POOL) && a->batch <= kMaxSeqPerLaunch &&
+          a->n_q < kPrefillMinQ) {
         wp = make_attn_pass(j, 0, a->batch, workspace, w);
         if (tile_form(wp)) win = &wp;
       }
@@ -763,7 +793,7 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       j.window_elsewhere = win_done;
       if (L.mode == CSA2_MODE_FULL) {
         st->has_full = 1;
-        st->has_pool = (hier && st->pool) ? 1 : 0;
+        st->has_pool = (hier || flat_pool) ? 1 : 0;
       }
       st->has_indices = 1;
       st->batch = a->batch; st->n_q = a->n_q;

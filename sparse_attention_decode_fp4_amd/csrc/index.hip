@@ -217,6 +217,24 @@ __device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t
 }
 
 
+// Score of item `pos` (as item_position gives it) in the exact recompute:
+// the quad score of that position, or for a block-max pass the largest
+// score among block `pos`'s visible positions (through the score keys, as
+// the scan took it).
+__device__ __forceinline__ float item_score_at(const IndexPass& p, const half2_t (&q)[kHI][8], float w_mine, int seq,
+                                               int quarter, int64_t pos, bool valid, int64_t vis) {
+  if (p.block_level != 2) return quad_score_at(p, q, w_mine, seq, quarter, pos, valid);
+  uint32_t best = 0u;
+#pragma unroll 1
+  for (int j = 0; j < 8; ++j) {
+    const int64_t tp = 8 * pos + j;
+    const bool v = valid && tp < vis;
+    const float sc = quad_score_at(p, q, w_mine, seq, quarter, v ? tp : 0, v);
+    if (v) best = max(best, score_key(sc));
+  }
+  return key_to_score(best);
+}
+
 // Exact k-th largest of n keys visited by `visit(n, f)` (f(key) per key), by
 // radix steps of 8 bits from bit `top` down.  256 threads; keys are unique
 // or the result is the k-th in the multiset order.
@@ -324,6 +342,12 @@ __device__ __forceinline__ void emit_chunk(const IndexPass& p, int64_t row, int 
     const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) k[j] = 8 * t + j < n_slots ? v[j] : 0u;
+  }
+  if (p.block_max && p.block_level == 0 && 8 * t < n_slots) {
+    // the largest key of block base / 8 + t (its 8 items are k[0 .. 8)),
+    // for a block-max pass after this one
+    const uint32_t bm = max(max(max(k[0], k[1]), max(k[2], k[3])), max(max(k[4], k[5]), max(k[6], k[7])));
+    p.block_max[row * p.block_max_stride + (base >> 3) + t] = bm;
   }
   // bins of the distance below mx; bin 255 takes everything further down
   // (counted by one lane per wave: it can hold most keys)
@@ -520,6 +544,33 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   if (base >= end) return;
   __shared__ ScanLds L;
   scan_chunk<U, kDirect, kPaged>(p, row, chunk, csize, base, end, vis, n_items, L);
+}
+
+// Block-max pass (block_level 2): workgroup (row, chunk of blocks) stages
+// the blocks' keys, written by the flat scan of the same rows, and cuts the
+// bands as the scan does; the key-scale bound is the row's largest.
+__global__ __launch_bounds__(256) void k_index_scan_keys(IndexPass p, int per_row) {
+  int row, chunk;
+  map_row_chunk(p.rows, per_row, row, chunk);
+  if (row >= p.rows) return;
+  const int64_t csize = row_chunk_items_of<true>(p, row);
+  const int64_t base = (int64_t)chunk * csize;
+  const int64_t vis = row_vis_positions(p, row);
+  const int64_t n_items = row_items_of<true>(p, row, vis);
+  const int64_t end = base + csize < n_items ? base + csize : n_items;
+  if (base >= end) return;
+  __shared__ ScanLds L;
+  const uint32_t* src = p.block_max + (int64_t)row * p.block_max_stride;
+  uint32_t mx_lane = 0u;
+  for (int64_t i = base + threadIdx.x; i < end; i += 256) {
+    const uint32_t key = src[i];
+    L.skeys[i - base] = key;
+    mx_lane = max(mx_lane, key);
+  }
+  const uint32_t ks_lane = p.row_ksm[row];
+  const int64_t nch = scan_chunk_count(n_items, csize);
+  emit_chunk(p, row, chunk, L.skeys, (int)(end - base), base, band0_size(n_items, csize, nch, p.k), mx_lane, ks_lane,
+             L.hist, L.sh);
 }
 
 // A pointer every lane holds the same value of, moved to scalar registers.
@@ -775,14 +826,14 @@ __device__ __forceinline__ void load_key_row(const IndexPass& p, int row, int64_
 // lanes of a quad take the four heads (lane quarter h); every lane of the
 // quad returns s.  Lanes with valid == false return 0 and load nothing
 // (whole quads agree on valid).
-__device__ __forceinline__ double exact_score(const IndexPass& p, int row, uint32_t item, bool valid,
-                                              const double (*qd)[4], const float* qw) {
+__device__ __forceinline__ double exact_score_at(const IndexPass& p, int row, int64_t pos, bool valid,
+                                                 const double (*qd)[4], const float* qw) {
 #pragma clang fp contract(off)
   const int h = threadIdx.x & 3;
   double s = 0.0;
   u32x4_t raw[4] = {};
   float ks = 0.0f;
-  if (valid) load_key_row(p, row, item_to_position(p, row, item), raw, ks);
+  if (valid) load_key_row(p, row, pos, raw, ks);
   double d = 0.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -799,6 +850,29 @@ __device__ __forceinline__ double exact_score(const IndexPass& p, int row, uint3
   const double p2 = __shfl(ph, (threadIdx.x & ~3) | 2, 64), p3 = __shfl(ph, (threadIdx.x & ~3) | 3, 64);
   s = (double)ks * (((p0 + p1) + p2) + p3);
   return valid ? s : 0.0;
+}
+
+// Exact score of item `item` of `row` (quad-collective, as exact_score_at).
+// Items of a block-max pass are blocks: the largest exact score among the
+// block's visible positions.
+__device__ __forceinline__ double exact_score(const IndexPass& p, int row, uint32_t item, bool valid,
+                                              const double (*qd)[4], const float* qw) {
+  if (p.block_level != 2) return exact_score_at(p, row, item_to_position(p, row, item), valid, qd, qw);
+  const int64_t vis = row_vis_positions(p, row);
+  double best = 0.0;
+  bool any = false;
+#pragma unroll 1
+  for (int j = 0; j < 8; ++j) {
+    // (the query values are re-read from LDS each time: held across the
+    // loop they would take 128 registers)
+    asm volatile("" ::: "memory");
+    const int64_t pos = 8 * (int64_t)item + j;
+    const bool v = valid && pos < vis;
+    const double e = exact_score_at(p, row, pos, v, qd, qw);
+    if (v && (!any || e > best)) best = e;
+    any |= v;
+  }
+  return best;
 }
 
 // Exact ranking of the near-tie band: items bitem[0 .. nb) (nb <= kBandMax)
@@ -989,6 +1063,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
     if (t == 0) seg_start[nch] = total;
   }
   const float delta = (p.mfma_scores ? kErrMfma : kErrValu) * cq * 448.0f * __uint_as_float(ksm);
+  if (p.row_ksm && p.block_level == 0 && t == 0) p.row_ksm[row] = ksm;
 
   bool fast = total <= (uint32_t)kSelCap;
   uint32_t n_win = 0;
@@ -1328,7 +1403,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
         const uint32_t item = base + (t >> 2);
         bool valid = false;
         const int64_t pos = item < n ? item_position(p, row, item, n, vis, valid) : 0;
-        const float sc = quad_score_at(p, q, w_mine, seq, quarter, pos, valid);
+        const float sc = item_score_at(p, q, w_mine, seq, quarter, pos, valid, vis);
         if (valid && quarter == 0) f(select_key(score_key(sc), item));
       }
     };
@@ -1385,7 +1460,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
       const uint32_t item = base + (t >> 2);
       bool valid = false;
       const int64_t pos = item < ni ? item_position(p, row, item, ni, vis, valid) : 0;
-      const float sc = quad_score_at(p, q, w_mine, seq, quarter, pos, valid);
+      const float sc = item_score_at(p, q, w_mine, seq, quarter, pos, valid, vis);
       const uint64_t kk = select_key(score_key(sc), item);
       bool f = valid && quarter == 0;
       if (f && n_valid > k) {
@@ -1551,7 +1626,10 @@ hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const Attn
   const dim3 sgrid((unsigned)(grid_rows(n_groups) * scan_per_row));
   const bool paged = p.pm.pages != nullptr;  // (direct items only: the host refuses the others)
   int h = prof_begin(CSA2_K_INDEX_SCAN, stream);
-  if (p.source != kItemsDirect)
+  if (p.block_level == 2)
+    hipLaunchKernelGGL(k_index_scan_keys, dim3((unsigned)(grid_rows(p.rows) * scan_per_row)), dim3(256), 0, stream, p,
+                       scan_per_row);
+  else if (p.source != kItemsDirect)
     hipLaunchKernelGGL((k_index_scan<2, false, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 1 && paged)
     hipLaunchKernelGGL((k_index_scan<2, true, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);

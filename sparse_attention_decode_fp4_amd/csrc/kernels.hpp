@@ -85,7 +85,10 @@ enum ItemSource : int32_t {
 struct IndexPass {
   int32_t rows, n_q, ratio, k;
   int32_t source;
-  int32_t block_level;         // 1: scoring block keys (visibility in blocks)
+  // 0: items are positions (or list / block entries); 1: items are blocks
+  // scored by their block keys; 2: items are blocks scored by the largest
+  // score of their visible positions, read from block_max (a block-max pass)
+  int32_t block_level;
   SeqArgs seq;                 // a = q_pos0, b = n_entries (per sequence)
   const uint8_t* idx_q;        // [rows][4][64]
   const float* idx_w;          // [rows][4] or null
@@ -106,6 +109,12 @@ struct IndexPass {
   uint64_t* seg_list;          // [rows][max_chunks][kSeg] (score key << 32 | ~item)
   int32_t max_chunks;
   int32_t mfma_scores;         // scores come from fp8 MFMA (queries sharing a scan)
+  // block_level 0 with block_max set: the scan also writes each block's
+  // largest score key there, and the select the row's largest key scale to
+  // row_ksm; a block-max pass reads both
+  uint32_t* block_max;         // [rows][block_max_stride]
+  int64_t block_max_stride;
+  uint32_t* row_ksm;           // [rows] float bits
   // output: either positions (out, -1 padded to k) or block ids + count
   int32_t* out;                // [rows][out_stride]
   int32_t out_stride;

@@ -85,3 +85,29 @@ def check_hier(gpu_idx, gpu_pool, q, w, k8, ks, bk8, bks, n_vis, k=512, n_blocks
     sc = oracle.scores(q, w, k8[want], ks[want])
     kind_t = check_topk(gpu_idx, ref, dict(zip(want.tolist(), sc.tolist())), k, len(want), f"{what} pool")
     return kind_b, kind_t
+
+
+def check_flat_pool(gpu_idx, gpu_pool, q, w, k8, ks, n_vis, k=512, n_blocks=2048, what=""):
+    """Flat selection that also keeps a pool (FLAT_POOL), with nothing
+    skipped on ties.  The indices: the flat top-k, tie-aware.  The blocks:
+    the GPU's kept blocks (read from its pool) against block scores that are
+    the largest oracle score among each block's visible positions,
+    tie-aware.  The pool must be exactly the visible positions of those
+    blocks, ascending, -1 padded.  Returns (block kind, token kind)."""
+    import oracle
+    sc = oracle.scores(q, w, k8[:n_vis], ks[:n_vis])
+    kind_t = check_topk(gpu_idx, oracle.index_flat(q, w, k8, ks, n_vis, k), sc, k, n_vis, f"{what} indices")
+    nb = -(-n_vis // 8)
+    bscore = np.array([sc[8 * b: min(8 * b + 8, n_vis)].max() for b in range(nb)])
+    gpool = np.asarray(gpu_pool)
+    gblocks = np.unique(gpool[gpool >= 0] // 8)
+    assert len(gblocks) <= n_blocks, f"{what}: more than {n_blocks} blocks in the pool"
+    gb = np.full(n_blocks, -1, dtype=np.int64)
+    gb[: len(gblocks)] = gblocks
+    rb = oracle.top_k(bscore, np.arange(nb), n_blocks)
+    kind_b = check_topk(gb, rb, bscore, n_blocks, nb, f"{what} blocks")
+    want = (gblocks[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    want = want[want < n_vis]
+    assert np.array_equal(gpool[: len(want)], want) and np.all(gpool[len(want):] == -1), \
+        f"{what}: the pool is not the visible positions of its blocks"
+    return kind_b, kind_t

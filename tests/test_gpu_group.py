@@ -6,7 +6,7 @@ import torch
 
 import csa2_inputs as gen
 import oracle
-from parity import check_close, check_hier, check_topk
+from parity import check_close, check_flat_pool, check_hier, check_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,9 @@ def _compare(outs, st, hkv, host_layers, n_entries, q_pos0, swa_pos0, plan, kind
             if kind == "hier" and plan[last] == "F":
                 kinds.append(check_hier(st_idx[b, i], gpool[b, i], iq, None, hkv["k8"][b], hkv["ks"][b],
                                         hkv["bk8"][b], hkv["bks"][b], nv, what=f"seq {b} q {i}"))
+            elif kind == "flatpool" and plan[last] == "F":
+                kinds.append(check_flat_pool(st_idx[b, i], gpool[b, i], iq, None, hkv["k8"][b], hkv["ks"][b], nv,
+                                             what=f"seq {b} q {i}"))
             elif plan[last] == "R" and reindex_kind == "pool":
                 pool = gpool[b, i][gpool[b, i] >= 0]
                 ref = oracle.index_pool(iq, None, hkv["k8"][b], hkv["ks"][b], pool)
@@ -164,6 +167,41 @@ def test_hier_full_then_pool_reindex(csa2):
             for b in range(B):
                 pool = set(st.pool[b, 0].cpu().numpy().tolist()) - {-1}
                 assert set(gi[b, 0].tolist()) <= pool
+    assert ws.fallbacks() == 0
+
+
+def test_flat_pool_full_then_pool_reindex(csa2):
+    """[F(flat pool), U, U, U] then [R(pool), U, U, U]: the Full layer indexes
+    flat and keeps the 2,048 blocks its token scores rank highest; the
+    Reindex layer ranks only that pool (the oracle's plan with kind
+    "flatpool"); 40,000 and 65,536 entries, so the kept blocks are a strict
+    subset."""
+    n_entries = [40000, 65536]
+    stride = 65536
+    B = len(n_entries)
+    dkv, hkv = _kv(csa2, 39, n_entries, stride, False)
+    q_pos0 = [n - 1 for n in n_entries]
+    swa_pos0 = [p - 127 for p in q_pos0]
+    ws = csa2.Workspace(B, 1, stride)
+    st = csa2.State(B, 1, with_pool=True)
+    ref_st = oracle.new_state()
+    for run, plan in enumerate(["FUUU", "RUUU"]):
+        dl, hl = _layers(csa2, 39, plan, B, 128, dkv, hkv, 10 * run)
+        outs = csa2.csa2_run_group(ws, st, dl, q_pos0, n_entries, swa_pos0, index_kind=csa2.INDEX_FLAT_POOL,
+                                   reindex_kind=csa2.INDEX_POOL)
+        torch.cuda.synchronize()
+        kinds = _compare(outs, st, hkv, hl, n_entries, q_pos0, swa_pos0, plan, "flatpool", "pool")
+        print(plan, kinds)
+        ref_outs = oracle.run_group(hl, ref_st, q_pos0, n_entries, swa_pos0, kind="flatpool", reindex_kind="pool")
+        gi = st.indices.cpu().numpy()
+        for b in range(B):
+            if run == 0 and kinds[b][0] == "exact":
+                assert np.array_equal(st.pool[b, 0].cpu().numpy(), ref_st["pool"][b][0])
+            if np.array_equal(gi[b, 0], ref_st["indices"][b, 0]):
+                for j in range(4):
+                    check_close(outs[j][b, 0].cpu().numpy(), ref_outs[j][b, 0], f"plan run {run} layer {j} seq {b}")
+            pool = set(st.pool[b, 0].cpu().numpy().tolist()) - {-1}
+            assert set(gi[b, 0].tolist()) <= pool  # Full's indices and Reindex's both lie in the pool
     assert ws.fallbacks() == 0
 
 

@@ -7,7 +7,7 @@ import torch
 import csa2_inputs as gen
 import oracle
 import oracle_side
-from parity import check_hier, check_topk
+from parity import check_flat_pool, check_hier, check_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +120,39 @@ def test_hierarchical_topk(csa2, n_entries):
         if n <= 16384:
             flat = oracle.index_flat(qh[b, 0], None, kb, sb, n)
             assert np.array_equal(ref_idx, flat)
+    assert ws.fallbacks() == 0
+
+
+@pytest.mark.parametrize("n_entries,n_q", [
+    ([20000, 9000, 16500], 1),   # 2,500 blocks (a strict subset kept), and rows that keep every block
+    ([40000], 2),                # two queries share each scan workgroup (fp8 MFMA scores)
+    ([131072, 70001], 4),        # four queries, 16,384 blocks of 8 at the longest row
+])
+def test_flat_pool_topk(csa2, n_entries, n_q):
+    """FLAT_POOL: the flat indices, and the pool of the blocks whose largest
+    token score ranks highest, against the oracle for every row."""
+    batch = len(n_entries)
+    stride = max(n_entries)
+    k8, ks, k8h, ksh = _keys(csa2, 91, batch, stride)
+    q = gen.index_query((batch, n_q), 17, device="cuda")
+    ws = csa2.Workspace(batch, n_q, stride)
+    q_pos0 = [n - n_q for n in n_entries]
+    out, pool = csa2.csa2_index_topk(ws, q, k8, ks, n_entries, q_pos0, stride, kind=csa2.INDEX_FLAT_POOL,
+                                     want_pool=True)
+    torch.cuda.synchronize()
+    qh = q.cpu().numpy()
+    for b, n in enumerate(n_entries):
+        kb, sb = k8h[b * stride: b * stride + n], ksh[b * stride: b * stride + n]
+        for i in range(n_q):
+            n_vis = min(n, q_pos0[b] + i + 1)
+            gpool = pool[b, i].cpu().numpy()
+            kinds = check_flat_pool(out[b, i].cpu().numpy(), gpool, qh[b, i], None, kb, sb, n_vis,
+                                    what=f"b{b} q{i}")
+            if kinds[0] == "exact":
+                _, ref_pool = oracle.index_flat_pool(qh[b, i], None, kb, sb, n_vis)
+                assert np.array_equal(gpool, ref_pool)
+            if -(-n_vis // 8) <= 2048:  # every block kept: the pool is every visible position
+                assert np.array_equal(gpool[:n_vis], np.arange(n_vis)) and np.all(gpool[n_vis:] == -1)
     assert ws.fallbacks() == 0
 
 
