@@ -25,4 +25,4 @@ from .group import FULL, REINDEX, REUSE, new_state, run_group  # noqa: F401
 from .indexer import (index_flat, index_flat_pool, index_hier, index_pool, scores,  # noqa: F401
                       scores_many, top_k, visible_entries)
 from .kv import (block_keys, compress_pairs, fp4_decode_rows, fp4_encode_rows,  # noqa: F401
-                 index_key_decode, index_key_encode, quantize_kv)
+                 index_key_decode, index_key_encode, index_key_encode_heads, quantize_kv)

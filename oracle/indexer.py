@@ -12,7 +12,9 @@ made of 2,048 blocks of 8.
 Readings (the pages give no formula):
   * score of position p for one query: s_p = ks_p * sum_h w_h * max(0, q_h . k_p)
     over the 4 indexer heads h, with q_h and k_p the E4M3 code values (the
-    indexer key k_p is shared by the heads; w_h defaults to 1).  The inner
+    indexer key k_p is shared by the heads; w_h defaults to 1).  With
+    per-head keys (k8 of shape [n, 4, 64]) head h dots its own key:
+    s_p = ks_p * sum_h w_h * max(0, q_h . k_{p,h}).  The inner
     dot of E4M3 values is exact in float64 (every value is an integer times
     2**-9 below 2**18, so 64 products stay below 2**42 units), the rest is
     float64 arithmetic;
@@ -41,12 +43,15 @@ BLOCK = 8
 def scores(idx_q, idx_w, k8, ks):
     """Scores of one query against keys.
 
-    idx_q u8[4, 64] E4M3 codes; idx_w f32[4] or None; k8 u8[n, 64]; ks f32[n]
-    -> float64[n]."""
+    idx_q u8[4, 64] E4M3 codes; idx_w f32[4] or None; k8 u8[n, 64] (shared
+    key) or u8[n, 4, 64] (per-head keys); ks f32[n] -> float64[n]."""
     q = e4m3_value(np.asarray(idx_q))                          # [4, 64]
     w = np.ones(q.shape[0]) if idx_w is None else np.asarray(idx_w, dtype=np.float64)
-    k = e4m3_value(np.asarray(k8))                             # [n, 64]
-    dots = k @ q.T                                             # [n, 4], exact
+    k = e4m3_value(np.asarray(k8))                             # [n, 64] or [n, 4, 64]
+    if k.ndim == 3:
+        dots = (k * q[None, :, :]).sum(axis=2)                 # [n, 4], exact
+    else:
+        dots = k @ q.T                                         # [n, 4], exact
     per_head = np.maximum(dots, 0.0) * w[None, :]
     return np.asarray(ks, dtype=np.float64) * per_head.sum(axis=1)
 
@@ -56,12 +61,16 @@ def scores_many(idx_q, idx_w, k8, ks):
     scores(idx_q[i], idx_w[i], k8, ks) (idx_w None: all weights 1), with the
     keys decoded once for all queries.
 
-    idx_q u8[n, 4, 64]; idx_w f32[n, 4] or None; k8 u8[m, 64]; ks f32[m]."""
+    idx_q u8[n, 4, 64]; idx_w f32[n, 4] or None; k8 u8[m, 64] or per-head
+    u8[m, 4, 64]; ks f32[m]."""
     q = e4m3_value(np.asarray(idx_q))                          # [n, 4, 64]
     n, h, c = q.shape
     w = np.ones((n, h)) if idx_w is None else np.asarray(idx_w, dtype=np.float64)
-    k = e4m3_value(np.asarray(k8))                             # [m, 64]
-    dots = (k @ q.reshape(n * h, c).T).reshape(-1, n, h)       # [m, n, 4], exact
+    k = e4m3_value(np.asarray(k8))                             # [m, 64] or [m, 4, 64]
+    if k.ndim == 3:
+        dots = np.stack([k[:, j, :] @ q[:, j, :].T for j in range(h)], axis=2)  # [m, n, 4], exact
+    else:
+        dots = (k @ q.reshape(n * h, c).T).reshape(-1, n, h)   # [m, n, 4], exact
     per_head = np.maximum(dots, 0.0) * w[None, :, :]
     return (np.asarray(ks, dtype=np.float64)[:, None] * per_head.sum(axis=2)).T
 

@@ -27,7 +27,11 @@ Readings where the pages are silent:
   * a block key (agentnet.co.il, section "CSA2: compression along the layer
     axis": blocks of 8 positions) is the float32 mean of the dequantised
     keys of the block, summed in position order and divided by the number of
-    keys present, then encoded like any indexer key.
+    keys present, then encoded like any indexer key;
+  * per-head keys (the other layout reading, "4 x 64 fp8 indexer K": each of
+    the 4 indexer heads has its own 64-channel key) are quantised as one
+    256-value vector: one float32 scale ks = fp32(amax / 448) over all four
+    heads, codes as above.
 """
 
 import numpy as np
@@ -88,6 +92,21 @@ def index_key_encode(k):
     k = np.asarray(k, dtype=np.float32)
     if k.shape[1] != D_INDEX:
         raise ValueError("indexer keys have 64 channels")
+    return _key_encode(k)
+
+
+def index_key_encode_heads(k):
+    """Per-head indexer keys float32 [n, 4, 64] -> (codes u8[n, 4, 64],
+    scales f32[n]): one scale per position over its four heads."""
+    k = np.asarray(k, dtype=np.float32)
+    if k.ndim != 3 or k.shape[1:] != (4, D_INDEX):
+        raise ValueError("per-head indexer keys are [n, 4, 64]")
+    codes, ks = _key_encode(k.reshape(k.shape[0], 4 * D_INDEX))
+    return codes.reshape(k.shape), ks
+
+
+def _key_encode(k):
+    """Rows of float32 key values -> (codes, one float32 scale per row)."""
     if not np.all(np.isfinite(k)):
         raise ValueError("non-finite input is outside the contract")
     amax = np.abs(k).max(axis=1)
@@ -130,5 +149,10 @@ def quantize_kv(x, ratio=1, k=None):
     nib, scale = fp4_encode_rows(e)
     if k is None:
         return nib, scale
-    k8, ks = index_key_encode(compress_pairs(k, ratio))
+    k = np.asarray(k, dtype=np.float32)
+    if k.ndim == 3:  # per-head keys [n, 4, 64]
+        e = compress_pairs(k.reshape(k.shape[0], -1), ratio)
+        k8, ks = index_key_encode_heads(e.reshape(e.shape[0], 4, D_INDEX))
+    else:
+        k8, ks = index_key_encode(compress_pairs(k, ratio))
     return nib, scale, k8, ks

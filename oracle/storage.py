@@ -17,7 +17,7 @@ layers store an entry.
 import numpy as np
 
 from .group import FULL, REINDEX, REUSE
-from .kv import fp4_encode_rows, index_key_encode
+from .kv import fp4_encode_rows, index_key_encode, index_key_encode_heads
 
 ENCODER_PLAN = [FULL] + [REUSE] * 5
 ENCODER_GROUPS, ENCODER_RATIO = 3, 2
@@ -34,10 +34,14 @@ def layer_plans():
     return enc + dec
 
 
-def bytes_per_entry():
-    """Bytes one stored entry takes, measured on the encoders' own outputs."""
+def bytes_per_entry(key_heads=1):
+    """Bytes one stored entry takes, measured on the encoders' own outputs
+    (key_heads 4: the per-head indexer-key layout)."""
     nib, scale = fp4_encode_rows(np.zeros((1, 512), dtype=np.float32))
-    k8, ks = index_key_encode(np.zeros((1, 64), dtype=np.float32))
+    if key_heads == 4:
+        k8, ks = index_key_encode_heads(np.zeros((1, 4, 64), dtype=np.float32))
+    else:
+        k8, ks = index_key_encode(np.zeros((1, 64), dtype=np.float32))
     return nib.nbytes + scale.nbytes + k8.nbytes + ks.nbytes
 
 
@@ -46,7 +50,7 @@ def main_kv_bytes_per_entry():
     return nib.nbytes + scale.nbytes
 
 
-def kv_bytes_per_token():
+def kv_bytes_per_token(key_heads=1):
     """Global-KV bytes per context token summed over the Full layers."""
-    per_entry = bytes_per_entry()
+    per_entry = bytes_per_entry(key_heads)
     return sum(per_entry / ratio for mode, ratio in layer_plans() if mode == FULL)

@@ -150,3 +150,34 @@ def test_scores_many_rows_equal_single_query_scores():
     for i in range(5):
         assert np.array_equal(many[i], oracle.scores(q[i], None, k8, ks))
         assert np.array_equal(many_w[i], oracle.scores(q[i], w[i], k8, ks))
+
+
+def test_per_head_keys_dot_each_head_with_its_own_key():
+    import torch
+    rng = np.random.default_rng(9)
+    q = _codes(rng, (4, 64), hi=0x60)
+    k = _codes(rng, (120, 4, 64), hi=0x70)
+    ks = rng.uniform(0.01, 2, 120).astype(np.float32)
+    w = np.array([1.0, 0.5, 2.0, -1.0], np.float32)
+    s = oracle.scores(q, w, k, ks)
+    # brute force with torch's float8 decoder and Python sums
+    qt = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    kt = torch.from_numpy(k).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for p in range(120):
+        tot = 0.0
+        for h in range(4):
+            d = float(sum(float(a) * float(b) for a, b in zip(qt[h], kt[p, h])))
+            tot += float(w[h]) * max(d, 0.0)
+        assert s[p] == float(ks[p]) * tot
+    # four equal heads reduce to the shared-key score
+    k1 = k[:, 0]
+    assert np.array_equal(oracle.scores(q, w, np.repeat(k1[:, None], 4, axis=1), ks), oracle.scores(q, w, k1, ks))
+    # the many-query form agrees row by row
+    qs = np.stack([q, _codes(rng, (4, 64), hi=0x60)])
+    many = oracle.scores_many(qs, None, k, ks)
+    for i in range(2):
+        assert np.array_equal(many[i], oracle.scores(qs[i], None, k, ks))
+    # flat top-k over per-head keys is the top-k of those scores
+    idx = oracle.index_flat(q, w, k, ks, 120, k=10)
+    order = sorted(range(120), key=lambda p: (-s[p], p))[:10]
+    assert list(idx) == sorted(order)

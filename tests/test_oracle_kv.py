@@ -91,3 +91,29 @@ def test_quantize_kv_ratio2_is_pair_mean_then_encode():
     n2, s2 = oracle.fp4_encode_rows(m)
     assert np.array_equal(nib, n2) and np.array_equal(sc, s2)
     assert k8.shape == (3, 64) and ks.shape == (3,)
+
+
+def test_per_head_key_quantiser_and_its_storage():
+    import torch
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((300, 4, 64)).astype(np.float32)
+    k[7] = 0.0
+    k[9, 2] *= 50.0                       # one head dominates the shared scale
+    codes, ks = oracle.index_key_encode_heads(k)
+    assert codes.shape == (300, 4, 64) and ks.dtype == np.float32
+    # one scale over all four heads: fp32(amax / 448)
+    amax = np.abs(k.reshape(300, -1)).max(axis=1)
+    assert np.array_equal(ks, (amax / np.float32(448)).astype(np.float32))
+    assert ks[7] == 0 and not codes[7].any()
+    # codes: E4M3 (torch's round-to-nearest-even float8 cast) of fp32(k / ks)
+    r = (k[ks > 0] / ks[ks > 0][:, None, None]).astype(np.float32)
+    want = torch.from_numpy(np.clip(r, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes[ks > 0], want)
+    # a position whose four heads are equal keeps the shared key's codes
+    same = np.repeat(k[:1, :1], 4, axis=1)
+    c1, s1 = oracle.index_key_encode(k[0, :1])
+    c4, s4 = oracle.index_key_encode_heads(same)
+    assert np.array_equal(s1, s4) and all(np.array_equal(c4[0, h], c1[0]) for h in range(4))
+    # the per-head layout costs 2.5 x (288 + 256 + 4) = 1,370 B/token
+    assert storage.bytes_per_entry(4) == 288 + 256 + 4
+    assert storage.kv_bytes_per_token(4) == 1370
