@@ -50,24 +50,26 @@ def parse():
                     help="only run a plain device copy of 256 MiB five times (the known-size reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     ap.add_argument("--page-size", type=int, default=256, help="entries per page of --workload paged")
-    ap.add_argument("--workload", choices=["decode", "multi", "prefill", "hier", "paged", "full64k", "tiny4k"],
+    ap.add_argument("--workload", choices=["decode", "multi", "prefill", "hier", "paged", "full64k", "tiny4k",
+                                           "heads64k"],
                     default="decode",
                     help="decode: the 128K decode group (default, the headline); prefill: a 4,096-token "
                          "chunk on a 262,144-token prefix at ratio 2, 1 Full + 5 Reuse layers; hier: the "
                          "hierarchical Full layer at 1M context, batch 4; multi: the decode group with 4 query "
                          "tokens per sequence (speculative decoding); full64k: one Full layer, batch 8, 65,536 "
-                         "entries with lognormal channel scales; tiny4k: one Full layer, batch 1, 4,096 entries")
+                         "entries with lognormal channel scales; tiny4k: one Full layer, batch 1, 4,096 entries; "
+                         "heads64k: full64k with per-head 4 x 64 indexer keys")
     return ap.parse_args()
 
 
-def algorithmic_bytes_per_qtok(ctx, nq=1, layers=4):
+def algorithmic_bytes_per_qtok(ctx, nq=1, layers=4, key_bytes=KEY_BYTES):
     """Bytes one query token must move through one group of `layers` layers:
     its share of the key scan of the Full/Reindex layer (the nq query tokens
     of a sequence share one scan), and per layer the 512 gathered entries
     (all of them when fewer are visible), the 128 window rows, its query and
     output, the index list."""
     per_layer = min(512, ctx) * ENTRY_BYTES + 128 * ROW_BYTES + Q_BYTES + OUT_BYTES + IDX_BYTES
-    return ctx * KEY_BYTES / nq + IDXQ_BYTES + layers * per_layer
+    return ctx * key_bytes / nq + IDXQ_BYTES + layers * per_layer
 
 
 def host_cpu():
@@ -449,10 +451,12 @@ def main():
     dev = "cuda"
     B, ctx, C = args.batch, args.ctx, args.copies
     lognormal = False
-    if args.workload in ("full64k", "tiny4k"):  # the Full-layer decode configurations
-        c = gen.CONFIGS[1 if args.workload == "full64k" else 0]
+    if args.workload in ("full64k", "tiny4k", "heads64k"):  # the Full-layer decode configurations
+        c = gen.CONFIGS[0 if args.workload == "tiny4k" else 1]
         B, ctx, lognormal = c["batch"], c["ctx"], c["lognormal"]
-    full_only = args.workload in ("full64k", "tiny4k")
+    full_only = args.workload in ("full64k", "tiny4k", "heads64k")
+    key_heads = 4 if args.workload == "heads64k" else 1
+    key_bytes = 64 * key_heads + 4
     nq = 4 if args.workload == "multi" else 1   # query tokens per sequence per step
     paged, page = args.workload == "paged", args.page_size
     if paged and ctx % page:
@@ -463,13 +467,18 @@ def main():
     for c in range(C):
         nib = torch.empty((B * ctx, 256), dtype=torch.uint8, device=dev)
         sc = torch.empty((B * ctx, 32), dtype=torch.uint8, device=dev)
-        k8 = torch.empty((B * ctx, 64), dtype=torch.uint8, device=dev)
+        k8 = torch.empty((B * ctx, 64 * key_heads), dtype=torch.uint8, device=dev)
         ks = torch.empty((B * ctx,), dtype=torch.float32, device=dev)
         for b in range(B):
             x = gen.latent(ctx, seed + 100 * c, seq=b, lognormal=lognormal, device=dev)
-            k = gen.index_key(ctx, seed + 100 * c, seq=b, device=dev)
             sl = slice(b * ctx, (b + 1) * ctx)
-            csa2.csa2_quantize_kv(x, k_in=k, out=[nib[sl], sc[sl], k8[sl], ks[sl]])
+            if key_heads == 4:
+                k = gen.normal((ctx, 4, 64), seed + 100 * c, "idxk4", seq=b, device=dev)
+                csa2.csa2_quantize_kv(x, out=[nib[sl], sc[sl]])
+                csa2.csa2_quantize_head_keys(k, out=[k8[sl].view(ctx, 4, 64), ks[sl]])
+            else:
+                k = gen.index_key(ctx, seed + 100 * c, seq=b, device=dev)
+                csa2.csa2_quantize_kv(x, k_in=k, out=[nib[sl], sc[sl], k8[sl], ks[sl]])
             del x, k
         if paged:
             # the same cache as a pool of pages in a random order, with its
@@ -487,7 +496,7 @@ def main():
             kvs.append(csa2.make_kv(nib, sc, k8, ks, 0, pages=csa2.make_pages(table, page, n_pages * page)))
             keep.append((nib, sc, k8, ks, table))
         else:
-            kvs.append(csa2.make_kv(nib, sc, k8, ks, ctx))
+            kvs.append(csa2.make_kv(nib, sc, k8, ks, ctx, key_heads=key_heads))
             keep.append((nib, sc, k8, ks))
     torch.cuda.synchronize()
     # ---- per-layer inputs of the two runs (shared by the copies)
@@ -576,14 +585,15 @@ def main():
     n_runs, n_layers = len(plans), len(plans[0])
     qtok_per_step = n_runs * B * nq
     value = qtok_per_step * args.steps / best_s
-    step_bytes = int(n_runs * B * nq * algorithmic_bytes_per_qtok(ctx, nq, n_layers))
-    scan_bytes = B * ctx * KEY_BYTES                       # one launch scans every sequence once
+    step_bytes = int(n_runs * B * nq * algorithmic_bytes_per_qtok(ctx, nq, n_layers, key_bytes))
+    scan_bytes = B * ctx * key_bytes                       # one launch scans every sequence once
     scan_avg_s = scan_ms / 1000.0 / scan_n
     achieved = scan_bytes / scan_avg_s / 1e9
     line = {
         "metric": (f"CSA2 multi-token decode query-tokens/s at 128K ctx ({nq} query tokens per sequence)" if nq > 1 else
                    f"CSA2 decode query-tokens/s at 128K ctx, paged KV ({page}-entry pages)" if paged else
-                   f"CSA2 Full-layer decode query-tokens/s, batch {B} at {ctx} ctx" if full_only else
+                   f"CSA2 Full-layer decode query-tokens/s, batch {B} at {ctx} ctx"
+                   + (", per-head indexer keys" if key_heads == 4 else "") if full_only else
                    "CSA2 decode query-tokens/s at 128K ctx; % of peak HBM GB/s"),
         "value": round(value, 1),
         "unit": "query-tokens/s",
@@ -598,6 +608,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": (f"one Full layer, batch {B}, {ctx} FP4 entries per sequence"
                                 + (" (N(0,1) latents times lognormal(0, 0.5) channel scales)" if lognormal else "")
+                                + (", per-head 4 x 64 fp8 indexer keys (260 B per entry)" if key_heads == 4 else "")
                                 + ", top-512 + 128-token window") if full_only else
                                (f"decode group of 4 layers run as Full+3 Reuse then Reindex+3 Reuse, "
                                 f"batch {B}, {ctx} FP4 entries per sequence, top-512 + 128-token window"
@@ -623,7 +634,8 @@ def main():
     }
     if not args.no_cpu_baseline and nq == 1 and not paged:
         x0 = gen.latent(ctx, seed, seq=0, lognormal=lognormal, device=dev).cpu().numpy()
-        k0 = gen.index_key(ctx, seed, seq=0, device=dev).cpu().numpy()
+        k0 = (gen.normal((ctx, 4, 64), seed, "idxk4", seq=0, device=dev) if key_heads == 4 else
+              gen.index_key(ctx, seed, seq=0, device=dev)).cpu().numpy()
         host_layers = []
         for run in range(n_runs):
             hl = []

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 /* Model constants the kernels are built for. */
 #define CSA2_D_LATENT 512   /* channels of one main-KV latent (key = value)        */
@@ -151,6 +151,23 @@ int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
                           void* stream);
 
 /*
+ * Per-head indexer keys (the other reading of the key layout, "4 x 64 fp8
+ * indexer K": each of the 4 indexer heads has its own 64-channel key).  One
+ * entry's key is quantised as one 256-value vector, with the rule of
+ * csa2_quantize_kv's key: ks = fp32(amax / 448) over all four heads, codes
+ * E4M3(fp32(k / ks)) (round to nearest even, saturating); at ratio 2 the
+ * pair mean is taken first.  Head h of entry e is at k8 + e*256 + h*64.
+ * Scores then dot head h's query with head h's key:
+ *   s = ks * sum_h w_h * max(0, q_h . k_h).
+ *   k_in    device float32 [n_tok][ld_k], ld_k >= 256 (4 heads x 64 channels)
+ *   k8      device [n_tok / ratio][256] (out);  kscale  device float32 [n_tok / ratio] (out)
+ * Errors: CSA2_ERR_ARG for null or misaligned pointers, a bad ratio or
+ * ld_k, or n_tok not a multiple of ratio.
+ */
+int csa2_quantize_head_keys(const float* k_in, int64_t n_tok, int64_t ld_k, int32_t ratio,
+                            uint8_t* k8, float* kscale, void* stream);
+
+/*
  * Paged caches (for serving: a pool of fixed-size pages and a page table per
  * sequence, so sequences grow without a fixed stride).  With table set,
  * position j of sequence s is pool entry
@@ -234,6 +251,10 @@ typedef struct csa2_index_args {
   int32_t* out_idx;          /* device [batch][n_q][k] (out)                          */
   int32_t* out_pool;         /* HIER, FLAT_POOL: device [batch][n_q][n_blocks*8] (out; optional for HIER) */
   csa2_pages pages;          /* paged k8/kscale (FLAT with n_q < 32), or all zero     */
+  int32_t key_heads;         /* indexer-key layout: 0 or 1 shared key (64 B / entry),
+                                4 per-head keys (256 B / entry, see
+                                csa2_quantize_head_keys): FLAT, FLAT_POOL and POOL
+                                with n_q < 32, contiguous caches                      */
 } csa2_index_args;
 
 int csa2_index_topk(const csa2_index_args* a, void* workspace, size_t ws_bytes, void* stream);
@@ -312,6 +333,7 @@ typedef struct csa2_kv {
   const float* bkscale;
   int64_t bk_stride;       /* blocks between sequences                                */
   csa2_pages pages;        /* paged nib/scale/k8/kscale (stride unused), or all zero  */
+  int32_t key_heads;       /* indexer-key layout, as csa2_index_args.key_heads        */
 } csa2_kv;
 
 typedef struct csa2_layer {

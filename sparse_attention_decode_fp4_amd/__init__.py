@@ -28,7 +28,7 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_STATE, ERR_WORKSPACE, ERR_HIP = range(6)
  K_PREFILL_SAMPLE, K_ATTENTION_MERGE, K_PREFILL_FILTER, K_PREFILL_SELECT, K_APPEND) = range(11)
 KERNEL_NAMES = ["quantize", "block_keys", "index_scan", "index_sample", "index_select", "attention",
                 "prefill_sample", "attention_merge", "prefill_filter", "prefill_select", "append"]
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _p = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -45,7 +45,7 @@ class IndexArgs(ctypes.Structure):
                 ("k8", _p), ("kscale", _p), ("k_stride", _i64),
                 ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64),
                 ("cand", _p), ("n_cand", _i32), ("k", _i32), ("n_blocks", _i32),
-                ("out_idx", _p), ("out_pool", _p), ("pages", Pages)]
+                ("out_idx", _p), ("out_pool", _p), ("pages", Pages), ("key_heads", _i32)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -57,7 +57,7 @@ class AttnArgs(ctypes.Structure):
 
 class KV(ctypes.Structure):
     _fields_ = [("nib", _p), ("scale", _p), ("k8", _p), ("kscale", _p), ("stride", _i64),
-                ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64), ("pages", Pages)]
+                ("bk8", _p), ("bkscale", _p), ("bk_stride", _i64), ("pages", Pages), ("key_heads", _i32)]
 
 
 class Layer(ctypes.Structure):
@@ -107,6 +107,7 @@ def _load():
         "csa2_workspace_fallbacks": (_i32, [_p, ctypes.POINTER(ctypes.c_uint32), _p]),
         "csa2_quantize_kv": (_i32, [_p, _i64, _i64, _i32, _p, _p, _p, _i64, _p, _p, _p]),
         "csa2_build_block_keys": (_i32, [_p, _p, _i32, _p, _i64, _p, _p, _i64, _p]),
+        "csa2_quantize_head_keys": (_i32, [_p, _i64, _i64, _i32, _p, _p, _p]),
         "csa2_index_topk": (_i32, [ctypes.POINTER(IndexArgs), _p, ctypes.c_size_t, _p]),
         "csa2_sparse_swa_attn": (_i32, [ctypes.POINTER(AttnArgs), _p, ctypes.c_size_t, _p]),
         "csa2_run_group": (_i32, [ctypes.POINTER(GroupArgs), ctypes.POINTER(GroupState), _p,
@@ -158,6 +159,14 @@ def _need(t, dtype, name, device=True):
         raise ValueError(f"{name} must be contiguous")
     if device and not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _opt(t, dtype, name):
+    """_need for an optional tensor (None passes)."""
+    if t is not None:
+        _need(t, dtype, name)
+    return t
 
 
 def _bits16(t, name):
@@ -212,9 +221,9 @@ def csa2_quantize_kv(x, ratio=1, k_in=None, out=None, stream=None):
         if k_in is not None:
             out += [torch.empty((n, D_INDEX), dtype=torch.uint8, device=dev),
                     torch.empty((n,), dtype=torch.float32, device=dev)]
-    nib, scale = out[0], out[1]
-    k8 = out[2] if k_in is not None else None
-    ks = out[3] if k_in is not None else None
+    nib, scale = _need(out[0], torch.uint8, "nib"), _need(out[1], torch.uint8, "scale")
+    k8 = _need(out[2], torch.uint8, "k8") if k_in is not None else None
+    ks = _need(out[3], torch.float32, "kscale") if k_in is not None else None
     if k_in is not None:
         _need(k_in, torch.float32, "k_in")
         if k_in.shape[0] != n_tok:
@@ -222,6 +231,23 @@ def csa2_quantize_kv(x, ratio=1, k_in=None, out=None, stream=None):
     _check(lib.csa2_quantize_kv(_ptr(x), n_tok, x.shape[1], ratio, _ptr(nib), _ptr(scale),
                                 _ptr(k_in), 0 if k_in is None else k_in.shape[1], _ptr(k8), _ptr(ks),
                                 _stream(stream)))
+    return tuple(out)
+
+
+def csa2_quantize_head_keys(k_in, ratio=1, out=None, stream=None):
+    """Per-head indexer keys: k_in float32 [n_tok, 4, 64] (or [n_tok, >=256])
+    -> (k8 u8[n, 4, 64], kscale f32[n]), one scale per entry over its heads."""
+    _need(k_in, torch.float32, "k_in")
+    k2 = k_in.reshape(k_in.shape[0], -1)
+    n_tok = k2.shape[0]
+    n = n_tok // ratio
+    if out is None:
+        out = [torch.empty((n, H_INDEX, D_INDEX), dtype=torch.uint8, device=k_in.device),
+               torch.empty((n,), dtype=torch.float32, device=k_in.device)]
+    _need(out[0], torch.uint8, "k8")
+    _need(out[1], torch.float32, "kscale")
+    _check(lib.csa2_quantize_head_keys(_ptr(k2), n_tok, k2.shape[1], ratio, _ptr(out[0]), _ptr(out[1]),
+                                       _stream(stream)))
     return tuple(out)
 
 
@@ -235,6 +261,12 @@ def csa2_append(x, k_in, pos, nib, scale, k8, kscale, stride, *, ratio=1, bk8=No
     (make_pages) the cache arrays are pools and stride is not read."""
     _need(x, torch.float32, "x")
     _need(k_in, torch.float32, "k_in")
+    for t, dt, nm in ((nib, torch.uint8, "nib"), (scale, torch.uint8, "scale"), (k8, torch.uint8, "k8"),
+                      (kscale, torch.float32, "kscale")):
+        _need(t, dt, nm)
+    _opt(bk8, torch.uint8, "bk8")
+    _opt(bkscale, torch.float32, "bkscale")
+    _opt(pending, torch.float32, "pending")
     batch = x.shape[0]
     a = AppendArgs()
     a.batch, a.ratio = batch, ratio
@@ -289,12 +321,20 @@ def _set_pages(a, pages):
 def csa2_index_topk(ws, idx_q, k8, kscale, n_entries, q_pos0, k_stride, *, kind=INDEX_FLAT,
                     ratio=1, idx_w=None, bk8=None, bkscale=None, bk_stride=0, cand=None,
                     k=TOP_K, n_blocks=N_BLOCKS, out_idx=None, out_pool=None, want_pool=False,
-                    pages=None, stream=None):
+                    pages=None, key_heads=1, stream=None):
     """Top-k positions per query.  idx_q u8 [batch, n_q, 4, 64]; returns
     out_idx int32 [batch, n_q, k] (and the pool for HIER or FLAT_POOL when
     want_pool; FLAT_POOL always makes one).  With pages (make_pages)
     k8/kscale are pools and k_stride is not read."""
     _need(idx_q, torch.uint8, "idx_q")
+    _need(k8, torch.uint8, "k8")
+    _need(kscale, torch.float32, "kscale")
+    _opt(idx_w, torch.float32, "idx_w")
+    _opt(bk8, torch.uint8, "bk8")
+    _opt(bkscale, torch.float32, "bkscale")
+    _opt(cand, torch.int32, "cand")
+    _opt(out_idx, torch.int32, "out_idx")
+    _opt(out_pool, torch.int32, "out_pool")
     batch, n_q = idx_q.shape[0], idx_q.shape[1]
     dev = idx_q.device
     if out_idx is None:
@@ -312,6 +352,7 @@ def csa2_index_topk(ws, idx_q, k8, kscale, n_entries, q_pos0, k_stride, *, kind=
     a.n_cand = 0 if cand is None else cand.shape[-1]
     a.k, a.n_blocks = k, n_blocks
     a.out_idx, a.out_pool = _ptr(out_idx), _ptr(out_pool)
+    a.key_heads = key_heads
     _set_pages(a, pages)
     _check(lib.csa2_index_topk(ctypes.byref(a), ws.ptr, ws.nbytes, _stream(stream)))
     return (out_idx, out_pool) if want_pool else out_idx
@@ -326,9 +367,12 @@ def csa2_sparse_swa_attn(ws, q, nib, scale, idx, swa, q_pos0, swa_pos0, kv_strid
     qb = _bits16(q, "q")
     sb = _bits16(swa, "swa")
     _need(idx, torch.int32, "idx")
+    _need(nib, torch.uint8, "nib")
+    _need(scale, torch.uint8, "scale")
     batch, n_q = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty((batch, n_q, H_ATTN, D_LATENT), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
     a = AttnArgs()
     a.batch, a.n_q, a.n_idx = batch, n_q, idx.shape[-1]
     qp = _host_i64(q_pos0)
@@ -356,9 +400,15 @@ class State:
         self._keep = []  # tensors the stored KV pointers refer to
 
 
-def make_kv(nib, scale, k8, kscale, stride, bk8=None, bkscale=None, bk_stride=0, pages=None):
+def make_kv(nib, scale, k8, kscale, stride, bk8=None, bkscale=None, bk_stride=0, pages=None, key_heads=1):
+    for t, dt, nm in ((nib, torch.uint8, "nib"), (scale, torch.uint8, "scale"), (k8, torch.uint8, "k8"),
+                      (kscale, torch.float32, "kscale")):
+        _need(t, dt, nm)
+    _opt(bk8, torch.uint8, "bk8")
+    _opt(bkscale, torch.float32, "bkscale")
     kv = KV()
     kv.nib, kv.scale, kv.k8, kv.kscale, kv.stride = _ptr(nib), _ptr(scale), _ptr(k8), _ptr(kscale), stride
+    kv.key_heads = key_heads
     kv.bk8, kv.bkscale, kv.bk_stride = _ptr(bk8), _ptr(bkscale), bk_stride
     _set_pages(kv, pages)
     kv._tensors = (nib, scale, k8, kscale, bk8, bkscale, pages)
@@ -398,11 +448,13 @@ def _group(ws, state, layers, q_pos0, n_entries, swa_pos0, ratio, index_kind, re
         out = L.get("out")
         if out is None:
             out = torch.empty((batch, n_q, H_ATTN, D_LATENT), dtype=torch.float32, device=q.device)
+        _need(out, torch.float32, "out")
         outs.append(out)
         arr[i].mode = L["mode"]
         arr[i].q, arr[i].swa, arr[i].out = _ptr(q), _ptr(swa), _ptr(out)
         if L["mode"] != MODE_REUSE:
             _need(L["idx_q"], torch.uint8, "idx_q")
+            _opt(L.get("idx_w"), torch.float32, "idx_w")
             arr[i].idx_q, arr[i].idx_w = _ptr(L["idx_q"]), _ptr(L.get("idx_w"))
         if L["mode"] == MODE_FULL:
             kv = L["kv"]

@@ -166,6 +166,12 @@ int validate_index(const csa2_index_args* a) {
     if (a->batch > 1 && a->bk_stride < (max_ne + 7) / 8) return fail(CSA2_ERR_ARG, "bk_stride smaller than the block count");
     if (a->out_pool && !aligned(a->out_pool, 4)) return fail(CSA2_ERR_ARG, "out_pool must be 4-byte aligned");
   }
+  if (a->key_heads != 0 && a->key_heads != 1 && a->key_heads != 4)
+    return fail(CSA2_ERR_ARG, "key_heads must be 0, 1 or 4");
+  if (a->key_heads == 4 && (a->kind == CSA2_INDEX_HIER || a->n_q >= kPrefillMinQ || a->pages.table))
+    return fail(CSA2_ERR_UNSUPPORTED,
+                "per-head keys take FLAT, FLAT_POOL or POOL indexing with fewer than %d queries on a contiguous cache",
+                kPrefillMinQ);
   if (a->kind == CSA2_INDEX_FLAT_POOL) {
     if (!a->out_pool || !aligned(a->out_pool, 4)) return fail(CSA2_ERR_ARG, "FLAT_POOL needs a 4-byte aligned out_pool");
     if (a->n_blocks < 1 || a->n_blocks > CSA2_MAX_K) return fail(CSA2_ERR_UNSUPPORTED, "n_blocks must be in 1..%d", CSA2_MAX_K);
@@ -198,6 +204,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     p.rows = nb * a->n_q;
     p.n_q = a->n_q;
     p.ratio = a->ratio;
+    p.key_heads = a->key_heads == 4 ? 4 : 1;
     int64_t max_vis = 0;
     for (int i = 0; i < nb; ++i) {
       p.seq.a[i] = a->q_pos0[s0 + i];
@@ -276,7 +283,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
     p.k = a->k;
     p.pm = page_map(a->pages, s0);
     const int64_t koff = a->pages.table ? 0 : (int64_t)s0 * a->k_stride;  // paged: the pool
-    p.k8 = a->k8 + koff * kDI;
+    p.k8 = a->k8 + koff * kDI * p.key_heads;
     p.kscale = a->kscale + koff;
     p.k_stride = a->k_stride;
     p.out = a->out_idx + row0 * a->k;
@@ -550,6 +557,19 @@ int csa2_quantize_kv(const float* x, int64_t n_tok, int64_t ld_x, int32_t ratio,
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "quantize");
 }
 
+int csa2_quantize_head_keys(const float* k_in, int64_t n_tok, int64_t ld_k, int32_t ratio, uint8_t* k8,
+                            float* kscale, void* stream) {
+  if (ratio != 1 && ratio != 2) return fail(CSA2_ERR_ARG, "ratio must be 1 or 2");
+  if (n_tok < 0 || n_tok % ratio) return fail(CSA2_ERR_ARG, "n_tok must be >= 0 and a multiple of ratio");
+  if (n_tok == 0) return CSA2_OK;
+  if (!k_in || !k8 || !kscale) return fail(CSA2_ERR_ARG, "k_in, k8, kscale are required");
+  if (ld_k < 4 * CSA2_D_INDEX) return fail(CSA2_ERR_ARG, "ld_k must be >= 256");
+  if (!aligned(k_in, 4) || !aligned(k8, 16) || !aligned(kscale, 4))
+    return fail(CSA2_ERR_ARG, "k_in/kscale must be 4-byte and k8 16-byte aligned");
+  hipError_t e = launch_quantize_head_keys(k_in, n_tok / ratio, ld_k, ratio, k8, kscale, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "quantize head keys");
+}
+
 int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
                           const int64_t* n_entries, int64_t k_stride, uint8_t* bk8, float* bkscale,
                           int64_t bk_stride, void* stream) {
@@ -705,6 +725,12 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       }
       if (a->index_kind == CSA2_INDEX_HIER && (!L.kv->bk8 || !L.kv->bkscale))
         return fail(CSA2_ERR_ARG, "layer %d: HIER needs block keys", l);
+      if (L.kv->key_heads != 0 && L.kv->key_heads != 1 && L.kv->key_heads != 4)
+        return fail(CSA2_ERR_ARG, "layer %d: kv.key_heads must be 0, 1 or 4", l);
+      if (L.kv->key_heads == 4 && (a->index_kind == CSA2_INDEX_HIER || a->n_q >= kPrefillMinQ || L.kv->pages.table))
+        return fail(CSA2_ERR_UNSUPPORTED,
+                    "layer %d: per-head keys take FLAT or FLAT_POOL indexing with fewer than %d queries on a "
+                    "contiguous cache", l, kPrefillMinQ);
       const bool keeps_pool = a->index_kind == CSA2_INDEX_HIER || a->index_kind == CSA2_INDEX_FLAT_POOL;
       if (keeps_pool && !st->pool && a->reindex_kind == CSA2_INDEX_POOL)
         return fail(CSA2_ERR_ARG, "POOL reindexing needs state.pool");
@@ -778,6 +804,7 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       ia.out_idx = st->indices;
       ia.out_pool = (hier || flat_pool) ? st->pool : nullptr;
       ia.pages = st->kv.pages;
+      ia.key_heads = st->kv.key_heads;
       // a flat decode pass in one launch runs the window tiles of the
       // attention in its select launch (they need nothing the select
       // computes), and the attention launch then takes the entry tiles only

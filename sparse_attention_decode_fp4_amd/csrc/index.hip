@@ -195,8 +195,39 @@ __device__ __forceinline__ float quad_score(const half2_t (&q)[kHI][8], float w_
   return quad_score_f16(q, w_mine, kh, ks);
 }
 
+// The same with per-head keys: raw[s] holds this lane's 16 channels of the
+// key of head quad_head(s, quarter), the head its query slot s holds.
+__device__ __forceinline__ float quad_score_heads(const half2_t (&q)[kHI][8], float w_mine, const u32x4_t (&raw)[kHI],
+                                                  float ks) {
+  float d[kHI] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kHI; ++s) {
+    half2_t kh[8];
+    key_f16(raw[s], kh);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[s] = __builtin_amdgcn_fdot2(q[s][j], kh[j], d[s], false);
+  }
+  const float e0 = d[0] + quad_xor1(d[2]);
+  const float e1 = d[1] + quad_xor1(d[3]);
+  const float f = e0 + quad_xor2(e1);
+  float v = w_mine * fmaxf(f, 0.0f);
+  v += quad_xor1(v);
+  v += quad_xor2(v);
+  return ks * v;
+}
+
 __device__ __forceinline__ float quad_score_at(const IndexPass& p, const half2_t (&q)[kHI][8], float w_mine,
                                                int seq, int quarter, int64_t pos, bool valid) {
+  if (p.key_heads == 4) {  // per-head keys (contiguous caches only)
+    u32x4_t raw[kHI];
+    float ks = 0.0f;
+    const uint8_t* kp = p.k8 + ((int64_t)seq * p.k_stride + pos) * (4 * kDI) + quarter * 16;
+#pragma unroll
+    for (int s2 = 0; s2 < kHI; ++s2)
+      raw[s2] = valid ? *reinterpret_cast<const u32x4_t*>(kp + quad_head(s2, quarter) * kDI) : u32x4_t{0, 0, 0, 0};
+    if (valid) ks = p.kscale[(int64_t)seq * p.k_stride + pos];
+    return quad_score_heads(q, w_mine, raw, ks);
+  }
   u32x4_t raw = u32x4_t{0, 0, 0, 0};
   float ks = 0.0f;
   if (valid) {
@@ -429,10 +460,15 @@ struct ScanLds {
 
 // Chunk `chunk` of row `row` (base < end): score every item, stage the keys,
 // cut and write the bands.
-template <int U, bool kDirect, bool kPaged>
+template <int U, bool kDirect, bool kPaged, bool kHeads = false>
 __device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chunk, int64_t csize, int64_t base,
                                            int64_t end, int64_t vis, int64_t n_items, ScanLds& L) {
   static_assert(!kPaged || kDirect, "paged caches are read over direct items");
+  static_assert(!kPaged || !kHeads, "per-head keys are read from contiguous caches");
+  // per-head keys: 256 bytes an entry, lane quarter c reads channels
+  // 16c .. 16c+15 of each head's key (the head of each query slot)
+  constexpr int kKB = kHeads ? 4 * kDI : kDI;  // key bytes per entry
+  constexpr int kKH = kHeads ? kHI : 1;        // key loads per item and lane
   const int seq = row / p.n_q;
   uint32_t* skeys = L.skeys;
   uint32_t* hist = L.hist;
@@ -441,7 +477,7 @@ __device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chun
   const int sub = threadIdx.x >> 2;  // item within a 64-item step
   half2_t q[kHI][8];
   float w_mine;  // loaded after the first keys: their loads overlap
-  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
+  const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kKB;
   const float* sb = p.kscale + (int64_t)seq * p.k_stride;
   // (used by the kDirect loads only.)  Paged: descriptors over the pool, and
   // lane j holds the page-table value of the chunk's page j: a batch of
@@ -451,9 +487,12 @@ __device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chun
   constexpr bool paged = kPaged;
   const uint32_t lim = paged ? (uint32_t)p.pm.pool : (uint32_t)end;
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? p.k8 : kb), 0, (int)(lim * kDI), kRawBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? p.k8 : kb), 0, (int)(lim * kKB), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(paged ? p.kscale : sb), 0, (int)(lim * 4), kRawBufferWord3);
+  int head_off[kKH];  // byte offset of the key slice each load takes
+#pragma unroll
+  for (int s2 = 0; s2 < kKH; ++s2) head_off[s2] = (kHeads ? quad_head(s2, quarter) * kDI : 0) + quarter * 16;
   uint32_t page_lane = 0;
   if constexpr (paged) {
     const int64_t pg = (base >> p.pm.lg) + (threadIdx.x & 63);
@@ -462,7 +501,7 @@ __device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chun
 
   // U items per lane quad per batch; two batches in flight (double buffer)
   struct Batch {
-    u32x4_t raw[U];
+    u32x4_t raw[U][kKH];
     float ks[U];
   };
   auto load = [&](Batch& B, int64_t it0) {
@@ -473,18 +512,18 @@ __device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chun
       const int64_t item = it0 + u * 64 + sub;
       if constexpr (kDirect) {
         const uint32_t e = !paged ? (uint32_t)item : item < end ? paged_entry(p.pm, page, item) : lim;
-        B.raw[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kDI) + quarter * 16, 0, kLoadNonTemporal);
+#pragma unroll
+        for (int s2 = 0; s2 < kKH; ++s2)
+          B.raw[u][s2] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(e * kKB) + head_off[s2], 0, kLoadNonTemporal);
         B.ks[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(e * 4), 0, 0));
       } else {
         bool valid;
         const int64_t pos = item_position(p, row, item, end, vis, valid);
-        if (valid) {
-          B.raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + pos * kDI + quarter * 16));
-          B.ks[u] = sb[pos];
-        } else {
-          B.raw[u] = u32x4_t{0, 0, 0, 0};
-          B.ks[u] = 0.0f;
-        }
+#pragma unroll
+        for (int s2 = 0; s2 < kKH; ++s2)
+          B.raw[u][s2] = valid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + pos * kKB + head_off[s2]))
+                               : u32x4_t{0, 0, 0, 0};
+        B.ks[u] = valid ? sb[pos] : 0.0f;
       }
     }
   };
@@ -492,7 +531,9 @@ __device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chun
   auto score = [&](const Batch& B, int64_t it0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float sc = quad_score(q, w_mine, B.raw[u], B.ks[u]);
+      float sc;
+      if constexpr (kHeads) sc = quad_score_heads(q, w_mine, B.raw[u], B.ks[u]);
+      else sc = quad_score(q, w_mine, B.raw[u][0], B.ks[u]);
       const int64_t item = it0 + u * 64 + sub;
       bool valid = item < end;
       if constexpr (!kDirect) {
@@ -531,7 +572,7 @@ __device__ __forceinline__ void scan_chunk(const IndexPass& p, int row, int chun
              hist, sh);
 }
 
-template <int U, bool kDirect, bool kPaged>
+template <int U, bool kDirect, bool kPaged, bool kHeads = false>
 __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, int n_groups) {
   int row, chunk;
   map_row_chunk(n_groups, per_row, row, chunk);
@@ -543,7 +584,7 @@ __global__ __launch_bounds__(256) void k_index_scan(IndexPass p, int per_row, in
   const int64_t end = base + csize < n_items ? base + csize : n_items;
   if (base >= end) return;
   __shared__ ScanLds L;
-  scan_chunk<U, kDirect, kPaged>(p, row, chunk, csize, base, end, vis, n_items, L);
+  scan_chunk<U, kDirect, kPaged, kHeads>(p, row, chunk, csize, base, end, vis, n_items, L);
 }
 
 // Block-max pass (block_level 2): workgroup (row, chunk of blocks) stages
@@ -798,9 +839,18 @@ __device__ __forceinline__ float load_query_codes(const IndexPass& p, int row, f
 }
 
 // Loads of one key's 64 code bytes and scale (position pos of row's
-// sequence) into registers.
-__device__ __forceinline__ void load_key_row(const IndexPass& p, int row, int64_t pos, u32x4_t (&raw)[4], float& ks) {
+// sequence) into registers: the shared key, or head `head`'s key.
+__device__ __forceinline__ void load_key_row(const IndexPass& p, int row, int64_t pos, u32x4_t (&raw)[4], float& ks,
+                                             int head) {
   const int seq = row / p.n_q;
+  if (p.key_heads == 4) {  // head `head`'s 64 bytes of a per-head key (contiguous caches only)
+    const u32x4_t* kp =
+        reinterpret_cast<const u32x4_t*>(p.k8 + ((int64_t)seq * p.k_stride + pos) * (4 * kDI) + head * kDI);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = kp[j];
+    ks = p.kscale[(int64_t)seq * p.k_stride + pos];
+    return;
+  }
   if (p.pm.pages) {
     const uint32_t e = paged_entry_at(p.pm, seq, pos);
     const __amdgpu_buffer_rsrc_t rk =
@@ -822,7 +872,8 @@ __device__ __forceinline__ void load_key_row(const IndexPass& p, int row, int64_
 // operations: d_h = sum_c q_hc k_c exactly (every E4M3 value is n 2^-9 with
 // |n| < 2^18, so each product and every partial sum of 64 is an integer
 // multiple of 2^-18 below 2^42: exact in float64, in any order);
-// p_h = max(0, d_h) * w_h; s = ks * (((p_0 + p_1) + p_2) + p_3).  The four
+// p_h = max(0, d_h) * w_h; s = ks * (((p_0 + p_1) + p_2) + p_3) (with
+// per-head keys d_h dots head h's own key).  The four
 // lanes of a quad take the four heads (lane quarter h); every lane of the
 // quad returns s.  Lanes with valid == false return 0 and load nothing
 // (whole quads agree on valid).
@@ -833,7 +884,7 @@ __device__ __forceinline__ double exact_score_at(const IndexPass& p, int row, in
   double s = 0.0;
   u32x4_t raw[4] = {};
   float ks = 0.0f;
-  if (valid) load_key_row(p, row, pos, raw, ks);
+  if (valid) load_key_row(p, row, pos, raw, ks, h);  // (shared keys: every lane loads the one key)
   double d = 0.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -1620,7 +1671,7 @@ hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const Attn
   if (scan_per_row > p.max_chunks) return hipErrorInvalidValue;
   // the queries of a sequence share the scan of a chunk, up to 4 per
   // workgroup (direct items only), on fp8 MFMA
-  const int nqg = (p.source != kItemsDirect || p.n_q == 1) ? 1 : p.n_q == 2 ? 2 : 4;
+  const int nqg = (p.source != kItemsDirect || p.n_q == 1 || p.key_heads == 4) ? 1 : p.n_q == 2 ? 2 : 4;
   p.mfma_scores = nqg > 1 ? 1 : 0;
   const int n_groups = nqg == 1 ? p.rows : p.rows / p.n_q * ((p.n_q + nqg - 1) / nqg);
   const dim3 sgrid((unsigned)(grid_rows(n_groups) * scan_per_row));
@@ -1629,6 +1680,10 @@ hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const Attn
   if (p.block_level == 2)
     hipLaunchKernelGGL(k_index_scan_keys, dim3((unsigned)(grid_rows(p.rows) * scan_per_row)), dim3(256), 0, stream, p,
                        scan_per_row);
+  else if (p.key_heads == 4 && p.source != kItemsDirect)
+    hipLaunchKernelGGL((k_index_scan<2, false, false, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
+  else if (p.key_heads == 4)
+    hipLaunchKernelGGL((k_index_scan<2, true, false, true>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (p.source != kItemsDirect)
     hipLaunchKernelGGL((k_index_scan<2, false, false>), sgrid, dim3(256), 0, stream, p, scan_per_row, n_groups);
   else if (nqg == 1 && paged)

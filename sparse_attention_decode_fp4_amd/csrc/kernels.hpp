@@ -85,6 +85,7 @@ enum ItemSource : int32_t {
 struct IndexPass {
   int32_t rows, n_q, ratio, k;
   int32_t source;
+  int32_t key_heads;           // 1: one 64-byte key per entry shared by the heads; 4: per-head keys (256 B)
   // 0: items are positions (or list / block entries); 1: items are blocks
   // scored by their block keys; 2: items are blocks scored by the largest
   // score of their visible positions, read from block_max (a block-max pass)
@@ -154,6 +155,8 @@ hipError_t launch_append(const AppendPass& p, int32_t batch, hipStream_t stream)
 hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int32_t ratio,
                            uint8_t* nib, uint8_t* scale, const float* kin, int64_t ld_k,
                            uint8_t* k8, float* kscale, hipStream_t stream);
+hipError_t launch_quantize_head_keys(const float* kin, int64_t n_entries, int64_t ld_k, int32_t ratio, uint8_t* k8,
+                                     float* kscale, hipStream_t stream);
 hipError_t launch_block_keys(const uint8_t* k8, const float* ks, int64_t k_stride,
                              const int64_t* n_entries, int32_t batch, uint8_t* bk8, float* bks,
                              int64_t bk_stride, hipStream_t stream);

@@ -89,6 +89,36 @@ __global__ __launch_bounds__(256) void k_quantize(
   if (blk == 0) kscale[entry] = ks;
 }
 
+// Per-head indexer keys: 16 lanes per entry (256 values, 16 per lane), so
+// a workgroup encodes 16 entries; the scale is the amax over all 16 lanes.
+__global__ __launch_bounds__(256) void k_quantize_head_keys(const float* __restrict__ kin, int64_t ld_k,
+                                                             int32_t ratio, int64_t n_entries,
+                                                             uint8_t* __restrict__ k8,
+                                                             float* __restrict__ kscale) {
+  const int64_t entry = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  if (entry >= n_entries) return;  // whole 16-lane groups leave together
+  float kv[16];
+  float kmax = 0.0f;
+  const float* q0 = kin + entry * ratio * ld_k + part * 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = q0[i];
+    kv[i] = (ratio == 1) ? a : f32_mul(f32_add(a, q0[ld_k + i]), 0.5f);
+    kmax = fmaxf(kmax, __builtin_fabsf(kv[i]));
+  }
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, d, 64));
+  const float ks = f32_div(kmax, 448.0f);
+  uint32_t c[4] = {0, 0, 0, 0};
+  if (ks > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i >> 2] |= e4m3_from_f32(f32_div(kv[i], ks)) << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint4*>(k8 + entry * 4 * CSA2_D_INDEX + part * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+  if (part == 0) kscale[entry] = ks;
+}
+
 // Block keys: one thread per (block, 16-channel quarter); a quad encodes one
 // block.  Block b holds entries 8b .. min(8b+8, n)-1 of its sequence.
 __global__ __launch_bounds__(256) void k_block_keys(
@@ -285,6 +315,16 @@ hipError_t launch_quantize(const float* x, int64_t n_entries, int64_t ld_x, int3
   const int h = prof_begin(CSA2_K_QUANTIZE, stream);
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, stream, x, ld_x, ratio,
                      n_entries, nib, scale, kin, ld_k, k8, kscale);
+  prof_end(h, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_head_keys(const float* kin, int64_t n_entries, int64_t ld_k, int32_t ratio, uint8_t* k8,
+                                     float* kscale, hipStream_t stream) {
+  if (n_entries == 0) return hipSuccess;
+  const int h = prof_begin(CSA2_K_QUANTIZE, stream);
+  hipLaunchKernelGGL(k_quantize_head_keys, dim3((unsigned)((n_entries + 15) / 16)), dim3(256), 0, stream, kin, ld_k,
+                     ratio, n_entries, k8, kscale);
   prof_end(h, stream);
   return hipGetLastError();
 }

@@ -230,6 +230,26 @@ def test_noalloc_validates_like_run_group_and_rejects_calls_past_its_scratch(m):
     assert st.has_full == 0 and st.has_indices == 0  # a refused call leaves the state as it was
 
 
+def test_per_head_key_errors(m):
+    f = m.lib.csa2_quantize_head_keys
+    assert f(None, 8, 256, 1, _p(), _p(0x100), None) == m.ERR_ARG
+    assert f(_p(), 8, 64, 1, _p(), _p(0x100), None) == m.ERR_ARG      # ld_k below 256
+    assert f(_p(), 7, 256, 2, _p(), _p(0x100), None) == m.ERR_ARG     # odd token count at ratio 2
+    assert f(_p(), 0, 256, 1, None, None, None) == m.OK                # nothing to do
+    a = m.IndexArgs()
+    qp, ne = (ctypes.c_int64 * 1)(999), (ctypes.c_int64 * 1)(1000)
+    a.kind, a.batch, a.n_q, a.ratio, a.k, a.n_blocks = m.INDEX_FLAT, 1, 1, 1, 512, 2048
+    a.q_pos0, a.n_entries = ctypes.cast(qp, ctypes.c_void_p), ctypes.cast(ne, ctypes.c_void_p)
+    a.idx_q, a.k8, a.kscale, a.out_idx, a.k_stride = _p(), _p(0x1000), _p(0x2000), _p(0x3000), 1000
+    a.key_heads = 2
+    assert m.lib.csa2_index_topk(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_ARG
+    a.key_heads, a.kind = 4, m.INDEX_HIER
+    a.bk8, a.bkscale = _p(0x4000), _p(0x5000)
+    assert m.lib.csa2_index_topk(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_UNSUPPORTED
+    a.kind, a.n_q = m.INDEX_FLAT, 32                                   # prefill-sized
+    assert m.lib.csa2_index_topk(ctypes.byref(a), _p(), 1 << 30, None) == m.ERR_UNSUPPORTED
+
+
 def _pages(m, table=None, table_stride=1, page_size=128, pool_entries=1024):
     pg = m.Pages()
     pg.table = _p(0x8000) if table is None else table
