@@ -419,23 +419,47 @@ __device__ __forceinline__ void emit_chunk(const IndexPass& p, int64_t row, int 
       sh[9] = complete ? 1u : band_edge(mx, b1);  // band 1: keys >= this (below band 0)
       sh[10] = n0;
       sh[11] = complete ? n_valid : n1;
-      sh[12] = 0u;
-      sh[13] = 0u;
       sh[14] = n0 | ((complete ? n_valid : n1) << 8) | ((uint32_t)(b0 + 1) << 16) | ((uint32_t)(b1 + 1) << 24);
       sh[15] = complete ? 1u : 0u;
     }
   }
   __syncthreads();
   const uint32_t thi = sh[8], tlo = sh[9], n0 = sh[10];
+  // segment slots without LDS atomics: a wave's band-0 (band-1) keys follow
+  // those of the waves before it, in its ballots' lane order
+  uint64_t m0b[8], m1b[8];
+  uint32_t c0 = 0u, c1 = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    m0b[j] = __ballot(k[j] != 0u && k[j] >= thi);
+    m1b[j] = __ballot(k[j] != 0u && k[j] >= tlo && k[j] < thi);
+    c0 += (uint32_t)__popcll(m0b[j]);
+    c1 += (uint32_t)__popcll(m1b[j]);
+  }
+  if (lane == 0) {
+    sh[16 + wave] = c0;
+    sh[20 + wave] = c1;
+  }
+  __syncthreads();
+  uint32_t o0 = 0u, o1 = n0;
+  for (int w = 0; w < wave; ++w) {
+    o0 += sh[16 + w];
+    o1 += sh[20 + w];
+  }
   const __amdgpu_buffer_rsrc_t rseg = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.seg_list + (row * p.max_chunks + chunk) * kSeg), 0, kSeg * 8, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (k[j] != 0u && k[j] >= tlo) {
-      const uint32_t slot = k[j] >= thi ? atomicAdd(&sh[12], 1u) : n0 + atomicAdd(&sh[13], 1u);
+    const bool in0 = (m0b[j] >> lane) & 1ull, in1 = (m1b[j] >> lane) & 1ull;
+    if (in0 || in1) {
+      const uint64_t m = in0 ? m0b[j] : m1b[j];
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t slot = (in0 ? o0 : o1) + below;
       const uint64_t v = select_key(k[j], (uint32_t)(base + 8 * t + j));
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{(uint32_t)v, (uint32_t)(v >> 32)}, rseg, (int)(slot * 8), 0, 0);
     }
+    o0 += (uint32_t)__popcll(m0b[j]);
+    o1 += (uint32_t)__popcll(m1b[j]);
   }
   if (t == 0) {
     const __amdgpu_buffer_rsrc_t rinfo = __builtin_amdgcn_make_buffer_rsrc(
