@@ -193,19 +193,30 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
         // every lane computes its scores before any per-lane branch: the
         // MFMA reads all lanes' operands, so it must not be sunk into one
         asm volatile("" ::"v"(sc[0]), "v"(sc[1]), "v"(sc[2]), "v"(sc[3]));
+        if (kFilter) {
+          // the lane's four pairs against their rows' thresholds, then one
+          // branch for the (rare) appends
+          uint32_t hm = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ql = 64 * wave + 8 * a + 2 * i + half;
-          if (kFilter) {
-            bool hit = slot_ok && sc[i] >= T[a][i];
-            if (hit && !all_visible) hit = slot < vis_row[ql];
-            if (hit) {  // append to this row's segment for this key range
-              const uint32_t at = atomicAdd(&seg_count[ql], 1u);
-              if (at < (uint32_t)kPfSeg)
-                p.list[((row0 + ql) * kPfSplits + split) * kPfSeg + at] = select_key(score_key(sc[i]), (uint32_t)slot);
+          for (int i = 0; i < 4; ++i) hm |= (sc[i] >= T[a][i] ? 1u : 0u) << i;
+          if (!slot_ok) hm = 0u;
+          if (hm) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ql = 64 * wave + 8 * a + 2 * i + half;
+              if (((hm >> i) & 1u) && (all_visible || slot < vis_row[ql])) {
+                // append to this row's segment for this key range
+                const uint32_t at = atomicAdd(&seg_count[ql], 1u);
+                if (at < (uint32_t)kPfSeg)
+                  p.list[((row0 + ql) * kPfSplits + split) * kPfSeg + at] = select_key(score_key(sc[i]), (uint32_t)slot);
+              }
             }
-          } else if (slot_ok && ql < nq_tile) {
-            p.sample[(row0 + ql) * kPfSample + slot] = sc[i];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ql = 64 * wave + 8 * a + 2 * i + half;
+            if (slot_ok && ql < nq_tile) p.sample[(row0 + ql) * kPfSample + slot] = sc[i];
           }
         }
       };
