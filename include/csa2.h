@@ -151,8 +151,8 @@ int csa2_build_block_keys(const uint8_t* k8, const float* kscale, int32_t batch,
                           void* stream);
 
 /*
- * Per-head indexer keys (the other reading of the key layout, "4 x 64 fp8
- * indexer K": each of the 4 indexer heads has its own 64-channel key).  One
+ * Per-head indexer keys (the other reading of the key layout: each of the 4
+ * indexer heads has its own 64-channel key).  One
  * entry's key is quantised as one 256-value vector, with the rule of
  * csa2_quantize_kv's key: ks = fp32(amax / 448) over all four heads, codes
  * E4M3(fp32(k / ks)) (round to nearest even, saturating); at ratio 2 the

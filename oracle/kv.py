@@ -28,8 +28,8 @@ Readings where the pages are silent:
     axis": blocks of 8 positions) is the float32 mean of the dequantised
     keys of the block, summed in position order and divided by the number of
     keys present, then encoded like any indexer key;
-  * per-head keys (the other layout reading, "4 x 64 fp8 indexer K": each of
-    the 4 indexer heads has its own 64-channel key) are quantised as one
+  * per-head keys (the other layout reading: each of the 4 indexer heads
+    has its own 64-channel key) are quantised as one
     256-value vector: one float32 scale ks = fp32(amax / 448) over all four
     heads, codes as above.
 """

@@ -901,14 +901,12 @@ __device__ __forceinline__ void load_key_row(const IndexPass& p, int row, int64_
 // lanes of a quad take the four heads (lane quarter h); every lane of the
 // quad returns s.  Lanes with valid == false return 0 and load nothing
 // (whole quads agree on valid).
-__device__ __forceinline__ double exact_score_at(const IndexPass& p, int row, int64_t pos, bool valid,
+// The arithmetic of exact_score_at on a key already in registers.
+__device__ __forceinline__ double exact_from_raw(const u32x4_t (&raw)[4], float ks, bool valid,
                                                  const double (*qd)[4], const float* qw) {
 #pragma clang fp contract(off)
   const int h = threadIdx.x & 3;
   double s = 0.0;
-  u32x4_t raw[4] = {};
-  float ks = 0.0f;
-  if (valid) load_key_row(p, row, pos, raw, ks, h);  // (shared keys: every lane loads the one key)
   double d = 0.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -925,6 +923,14 @@ __device__ __forceinline__ double exact_score_at(const IndexPass& p, int row, in
   const double p2 = __shfl(ph, (threadIdx.x & ~3) | 2, 64), p3 = __shfl(ph, (threadIdx.x & ~3) | 3, 64);
   s = (double)ks * (((p0 + p1) + p2) + p3);
   return valid ? s : 0.0;
+}
+
+__device__ __forceinline__ double exact_score_at(const IndexPass& p, int row, int64_t pos, bool valid,
+                                                 const double (*qd)[4], const float* qw) {
+  u32x4_t raw[4] = {};
+  float ks = 0.0f;
+  if (valid) load_key_row(p, row, pos, raw, ks, threadIdx.x & 3);  // (shared keys: every lane loads the one key)
+  return exact_from_raw(raw, ks, valid, qd, qw);
 }
 
 // Exact score of item `item` of `row` (quad-collective, as exact_score_at).
@@ -957,24 +963,80 @@ __device__ __forceinline__ double exact_score(const IndexPass& p, int row, uint3
 // position ties are broken by item.
 __device__ __forceinline__ void rank_band(const IndexPass& p, int row, uint32_t nb, uint32_t r, const uint32_t* bitem,
                                           double* bscore, uint32_t* bwin, const double (*qd)[4], const float* qw) {
+#pragma clang fp contract(off)
   const int t = threadIdx.x;
-  for (uint32_t m0 = 0; m0 < nb; m0 += 64) {
-    const uint32_t m = m0 + (t >> 2);
-    const bool valid = m < nb;
-    const double s = exact_score(p, row, valid ? bitem[m] : 0u, valid, qd, qw);
-    if (valid && (t & 3) == 0) bscore[m] = s;
+  if (p.block_level == 2) {  // blocks: each the best of 8 positions (rare, small bands)
+    for (uint32_t m0 = 0; m0 < nb; m0 += 64) {
+      const uint32_t m = m0 + (t >> 2);
+      const bool valid = m < nb;
+      const double s = exact_score(p, row, valid ? bitem[m] : 0u, valid, qd, qw);
+      if (valid && (t & 3) == 0) bscore[m] = s;
+    }
+  } else {
+    // a quad takes keys m, m + 64, m + 128, m + 192 of a pass: their loads
+    // all go out before the arithmetic, so a band of up to 256 keys costs
+    // one round trip
+    constexpr int kPerQuad = 4;
+    for (uint32_t m0 = 0; m0 < nb; m0 += 64 * kPerQuad) {
+      u32x4_t raw[kPerQuad][4];
+      float ks[kPerQuad];
+      // (slot groups past the band are skipped as a whole: the condition is
+      // the same for every thread)
+#pragma unroll
+      for (int i = 0; i < kPerQuad; ++i) {
+        const uint32_t m = m0 + (t >> 2) + 64 * i;
+        raw[i][0] = raw[i][1] = raw[i][2] = raw[i][3] = u32x4_t{0, 0, 0, 0};
+        ks[i] = 0.0f;
+        if (m < nb) load_key_row(p, row, item_to_position(p, row, bitem[m]), raw[i], ks[i], t & 3);
+      }
+      // (the arithmetic key by key: done for the four keys at once the
+      // compiler holds all their converted values and the query's at once)
+#pragma unroll
+      for (int i = 0; i < kPerQuad; ++i) {
+        if (m0 + 64 * i >= nb) break;  // uniform
+        const uint32_t m = m0 + (t >> 2) + 64 * i;
+        const double sc = exact_from_raw(raw[i], ks[i], m < nb, qd, qw);
+        if (m < nb && (t & 3) == 0) bscore[m] = sc;
+      }
+    }
   }
   __syncthreads();
-  for (uint32_t m = t; m < nb; m += 256) {
+  // rank of band key m = keys of the band ahead of it; a small band's
+  // comparisons are split over up to four threads per key (partial ranks
+  // summed in bwin), so every thread of the workgroup takes part
+  const uint32_t parts = nb <= 64 ? 4u : nb <= 128 ? 2u : 1u;
+  for (uint32_t m = t; m < nb; m += 256) bwin[m] = 0u;
+  __syncthreads();
+  for (uint32_t idx = t; idx < nb * parts; idx += 256) {
+    const uint32_t m = idx % nb, part = idx / nb;
+    const uint32_t j0 = part * nb / parts, j1 = (part + 1) * nb / parts;
     const double sm = bscore[m];
     const uint32_t im = bitem[m];
     uint32_t rank = 0;
-    for (uint32_t j = 0; j < nb; ++j) {
-      const double sj = bscore[j];
-      rank += (sj > sm || (sj == sm && bitem[j] < im)) ? 1u : 0u;
+    // eight keys' loads in flight per step: one at a time, the loop is
+    // bound by the LDS latency
+    uint32_t j = j0;
+    for (; j + 8 <= j1; j += 8) {
+      double sj[8];
+      uint32_t ij[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        sj[u] = bscore[j + u];
+        ij[u] = bitem[j + u];
+      }
+      // (bitwise, not short-circuit: no branch per comparison)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        rank += (sj[u] > sm ? 1u : 0u) | ((sj[u] == sm ? 1u : 0u) & (ij[u] < im ? 1u : 0u));
     }
-    bwin[m] = rank < r ? 1u : 0u;
+    for (; j < j1; ++j) {
+      const double sj = bscore[j];
+      rank += (sj > sm ? 1u : 0u) | ((sj == sm ? 1u : 0u) & (bitem[j] < im ? 1u : 0u));
+    }
+    atomicAdd(&bwin[m], rank);
   }
+  __syncthreads();
+  for (uint32_t m = t; m < nb; m += 256) bwin[m] = bwin[m] < r ? 1u : 0u;
   __syncthreads();
 }
 
