@@ -35,8 +35,11 @@ __device__ __forceinline__ uint32_t bf16_round(float x) {  // round to nearest e
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  // exact values only: truncation equals rounding
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  // exact values only (the rounding of the packing convert changes none);
+  // one v_cvt_pk_bf16_f32 instead of a shift and a masked or
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 struct TileLds {
