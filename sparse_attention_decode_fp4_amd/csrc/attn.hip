@@ -365,20 +365,31 @@ __device__ __forceinline__ void stage_q_pair(const AttnPass& p, int l0, int nl, 
   __syncthreads();
 }
 
+// Workgroup (pair of layers, row, split): with one split the whole row and
+// its outputs; with several, tiles tiles_per_split split .. of the row's
+// tile list (selected-entry tiles, then window tiles, each window tile
+// index standing for that window tile of both layers) and a partial
+// softmax per layer for the merge.
 __global__ __launch_bounds__(256, 2) void k_attention_pair(AttnPass p) {
   const int n_pairs = (p.n_layers + 1) / 2;
   const int units = n_pairs * p.rows;
-  int unit;
+  int unit, split;
   {
     const int lin = blockIdx.x;
-    if (units >= kXcds) {
+    if (units >= kXcds && p.max_splits > 1) {  // the splits of a unit share one XCD
+      const int xcd = lin & (kXcds - 1), w = lin >> 3;
+      unit = xcd + kXcds * (w / p.max_splits);
+      split = w % p.max_splits;
+    } else if (units >= kXcds) {
       // each XCD takes a contiguous range of units, so the queries resident
       // on it together are consecutive tokens whose windows overlap in all
       // but one row, and the rows come from its L2
       const int xcd = lin & (kXcds - 1), w = lin >> 3;
       unit = xcd * ((units + kXcds - 1) / kXcds) + w;
+      split = 0;
     } else {
-      unit = lin;
+      unit = lin / p.max_splits;
+      split = lin % p.max_splits;
     }
   }
   if (unit >= units) return;
@@ -389,7 +400,10 @@ __global__ __launch_bounds__(256, 2) void k_attention_pair(AttnPass p) {
   int n_win;
   const int64_t t0 = window_start(p, row, n_win);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
-  const int n_win_tiles = p.n_tiles - n_tile_idx;
+  const int tile_begin = split * p.tiles_per_split;
+  int tile_end = tile_begin + p.tiles_per_split;
+  tile_end = tile_end < p.n_tiles ? tile_end : p.n_tiles;
+  const int sel_end = tile_end < n_tile_idx ? tile_end : n_tile_idx;  // selected-entry tiles here: tile_begin .. sel_end
 
   __shared__ __attribute__((aligned(16))) PairLds s;
   TileLds& st = s.t;  // the tile loads fill its E and row_ok
@@ -407,31 +421,36 @@ __global__ __launch_bounds__(256, 2) void k_attention_pair(AttnPass p) {
 
   EntryFetch f;
   int32_t pos_next = -1;
-  if (n_tile_idx > 0) {
-    fetch_entry(p, seq, tile_position(p, 0, row), f);
-    if (n_tile_idx > 1) pos_next = tile_position(p, 1, row);
+  if (tile_begin < sel_end) {
+    fetch_entry(p, seq, tile_position(p, tile_begin, row), f);
+    if (tile_begin + 1 < sel_end) pos_next = tile_position(p, tile_begin + 1, row);
   }
   stage_q_pair(p, l0, nl, row, s, qb);
-  for (int tile = 0; tile < n_tile_idx; ++tile) {
-    if (tile > 0) __syncthreads();  // the previous tile's readers of E are done
+  for (int tile = tile_begin; tile < sel_end; ++tile) {
+    if (tile > tile_begin) __syncthreads();  // the previous tile's readers of E are done
     store_entry(f, st);
-    if (tile + 1 < n_tile_idx) {
+    if (tile + 1 < sel_end) {
       fetch_entry(p, seq, pos_next, f);
-      if (tile + 2 < n_tile_idx) pos_next = tile_position(p, tile + 2, row);
+      if (tile + 2 < sel_end) pos_next = tile_position(p, tile + 2, row);
     }
     pair_step(s, qb, both, sc2, m_run, l_run, o);
   }
+  const int win_begin = tile_begin > n_tile_idx ? tile_begin : n_tile_idx;
   for (int j = 0; j < nl; ++j) {
-    for (int wt = 0; wt < n_win_tiles; ++wt) {
+    for (int tile = win_begin; tile < tile_end; ++tile) {
       __syncthreads();  // the previous tile's readers of E are done
-      load_window(p, p.layer[l0 + j], wt, seq, t0, n_win, st);
+      load_window(p, p.layer[l0 + j], tile - n_tile_idx, seq, t0, n_win, st);
       pair_step(s, qb, 1 << j, sc2, m_run, l_run, o);
     }
   }
-  // the whole row is here: write the outputs
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j >= nl) break;
+    if (p.max_splits > 1) {  // a partial softmax per layer, merged afterwards
+      write_partial(p, (l0 + j) * p.rows + row, split, m_run[j], l_run[j], o[j]);
+      continue;
+    }
+    // the whole row is here: write the output
     float l_out[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) l_out[r] = __shfl(l_run[j], 4 * g4 + r, 64);
@@ -606,11 +625,11 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
     const int per_row = n_tile_idx * n_groups + (p.window_elsewhere ? 0 : p.n_layers * (p.n_tiles - n_tile_idx));
     const int grows = p.rows >= kXcds ? (p.rows + kXcds - 1) / kXcds * kXcds : p.rows;
     hipLaunchKernelGGL(k_attention_tiles<LG>, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p);
-  } else if (p.max_splits == 1 && p.n_layers >= 2) {
-    // whole rows of two or more layers: the pair form
+  } else if (p.n_layers >= 2) {
+    // two or more layers: the pair form
     const int punits = (p.n_layers + 1) / 2 * p.rows;
     const int pg = punits >= kXcds ? (punits + kXcds - 1) / kXcds * kXcds : punits;
-    hipLaunchKernelGGL(k_attention_pair, dim3((unsigned)pg), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(k_attention_pair, dim3((unsigned)(pg * p.max_splits)), dim3(256), 0, stream, p);
   } else {
     hipLaunchKernelGGL(k_attention<kWalkLG>, dim3((unsigned)(gu * p.max_splits)), dim3(256), 0, stream, p);
   }
