@@ -16,84 +16,20 @@
 // over rows and reads its E operand with the transposing LDS load of gfx950
 // (ds_read_b64_tr_b16), two per MFMA.  E2M1 x E4M3 products are exact in bf16,
 // so only P is rounded: it is split into bf16 hi + lo parts (relative error
-// ~2^-16).  Two forms:
-//   walk   a workgroup walks `tiles_per_split` tiles of one row for a group
-//          of LG layers, one online softmax per layer, a selected-entry tile
-//          dequantised once for the group (many rows: prefill chunks);
-//   tiles  one tile per workgroup (few rows: decode); the tiles of selected
-//          entries are shared by all layers of the launch, since the layers
-//          of a group attend over the same entries, so each is gathered and
-//          dequantised once and then serves every layer.
+// ~2^-16).  The layers of a call attend over the same entries, so a
+// gathered tile serves a pair of layers: waves 0-1 score one, waves 2-3 the
+// other, and every wave updates both layers' O (pair_step).  Three forms:
+//   tiles  one tile per workgroup (few rows: decode);
+//   pair   a workgroup walks `tiles_per_split` tiles of one row for a pair
+//          of layers, one online softmax per layer (many rows: prefill
+//          chunks; or a split of a row: multi-token decode);
+//   walk   the same for a single layer.
 // When a (layer, row) is split over several workgroups, a second kernel
 // merges the partial softmaxes in split order, so results do not depend on
 // scheduling.
 #include "tile.hpp"
 
 namespace csa2 {
-
-// Tile-parallel form (one tile per workgroup, partials merged afterwards):
-// workgroup (row, j).  j < n_tile_idx * n_groups: selected-entry tile
-// j / n_groups for layer group j % n_groups (layers LG g .. LG g + LG - 1):
-// the layers of a group attend over the same entries, so a tile is gathered
-// and dequantised once per layer group and then used by each of its layers
-// in turn (the layer loop is unrolled, so waiting for the next layer's Q
-// does not wait for this layer's partial stores); otherwise a window tile
-// of one layer (none when the select launch ran them: window_elsewhere).
-template <int LG>
-__global__ __launch_bounds__(256) void k_attention_tiles(AttnPass p) {
-  const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
-  const int n_win_tiles = p.n_tiles - n_tile_idx;
-  const int n_groups = (p.n_layers + LG - 1) / LG;
-  const int n_sel = n_tile_idx * n_groups;
-  const int per_row = n_sel + (p.window_elsewhere ? 0 : p.n_layers * n_win_tiles);
-  // workgroup ids are dealt round-robin over the 8 XCDs: with 8 or more rows,
-  // all workgroups of a row run on one XCD, which then reads the row's
-  // queries from memory once
-  int row, j;
-  if (p.rows >= kXcds) {
-    const int xcd = blockIdx.x & (kXcds - 1), w = blockIdx.x >> 3;
-    row = xcd + kXcds * (w / per_row);
-    j = w % per_row;
-  } else {
-    row = blockIdx.x / per_row;
-    j = blockIdx.x - row * per_row;
-  }
-  if (row >= p.rows) return;
-  const int seq = row / p.n_q;
-  __shared__ __attribute__((aligned(16))) TileLds s;
-  const float sc2 = p.softmax_scale * 1.4426950408889634f;  // logits in the log2 domain
-  float m_run, l_run;
-  f32x4_t o[8];
-  auto reset = [&]() {
-    m_run = -INFINITY;
-    l_run = 0.0f;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
-  if (j < n_sel) {
-    const int tile = j / n_groups, l0 = LG * (j % n_groups);
-    const int nl = p.n_layers - l0 < LG ? p.n_layers - l0 : LG;
-    // the positions and the queries go out together; the entries follow as
-    // soon as the positions are in
-    const int32_t pos = tile_position(p, tile, row);
-    uint4 qb[LG][16];
-    EntryFetch f;
-    fetch_entry(p, seq, pos, f);
-    stage_q<LG>(p, l0, nl, row, s, qb);
-    store_entry(f, s);
-#pragma unroll
-    for (int i = 0; i < LG; ++i) {
-      const int l = l0 + i;
-      if (i >= nl) break;  // uniform
-      reset();
-      tile_step(s, qb[i], nullptr, row, sc2, m_run, l_run, o);
-      write_partial(p, l * p.rows + row, tile, m_run, l_run, o);
-    }
-  } else {
-    const int jj = j - n_sel;
-    window_tile(p, row, jj / n_win_tiles, jj % n_win_tiles, s);
-  }
-}
 
 // Walk form: workgroup (group of LG layers, row, split) walks its tiles
 // with one online softmax per layer.  The selected-entry tiles are shared by
@@ -365,6 +301,64 @@ __device__ __forceinline__ void stage_q_pair(const AttnPass& p, int l0, int nl, 
   __syncthreads();
 }
 
+// Tile form (one tile per workgroup, partials merged afterwards): workgroup
+// (row, j).  j < n_tile_idx * n_groups: selected-entry tile j / n_groups for
+// layer pair j % n_groups (layers 2 g, 2 g + 1): the layers of a group
+// attend over the same entries, so a tile is gathered and dequantised once
+// for the pair, whose two layers are scored side by side (pair_step);
+// otherwise a window tile of one layer (none when the select launch ran
+// them: window_elsewhere).
+__global__ __launch_bounds__(256) void k_attention_tiles_pair(AttnPass p) {
+  const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
+  const int n_win_tiles = p.n_tiles - n_tile_idx;
+  const int n_groups = (p.n_layers + 1) / 2;
+  const int n_sel = n_tile_idx * n_groups;
+  const int per_row = n_sel + (p.window_elsewhere ? 0 : p.n_layers * n_win_tiles);
+  // workgroup ids are dealt round-robin over the 8 XCDs: with 8 or more rows,
+  // all workgroups of a row run on one XCD, which then reads the row's
+  // queries from memory once
+  int row, j;
+  if (p.rows >= kXcds) {
+    const int xcd = blockIdx.x & (kXcds - 1), w = blockIdx.x >> 3;
+    row = xcd + kXcds * (w / per_row);
+    j = w % per_row;
+  } else {
+    row = blockIdx.x / per_row;
+    j = blockIdx.x - row * per_row;
+  }
+  if (row >= p.rows) return;
+  const int seq = row / p.n_q;
+  __shared__ __attribute__((aligned(16))) PairLds s;
+  if (j < n_sel) {
+    const int tile = j / n_groups, l0 = 2 * (j % n_groups);
+    const int nl = p.n_layers - l0 < 2 ? p.n_layers - l0 : 2;
+    const float sc2 = p.softmax_scale * 1.4426950408889634f;  // logits in the log2 domain
+    // the positions and the queries go out together; the entries follow as
+    // soon as the positions are in
+    const int32_t pos = tile_position(p, tile, row);
+    uint4 qb[16];
+    EntryFetch f;
+    fetch_entry(p, seq, pos, f);
+    stage_q_pair(p, l0, nl, row, s, qb);
+    store_entry(f, s.t);
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+    f32x4_t o[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) o[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    pair_step(s, qb, nl == 2 ? 3 : 1, sc2, m_run, l_run, o);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i >= nl) break;  // uniform
+      write_partial(p, (l0 + i) * p.rows + row, tile, m_run[i], l_run[i], o[i]);
+    }
+  } else {
+    const int jj = j - n_sel;
+    window_tile(p, row, jj / n_win_tiles, jj % n_win_tiles, s.t);
+  }
+}
+
 // Workgroup (pair of layers, row, split): with one split the whole row and
 // its outputs; with several, tiles tiles_per_split split .. of the row's
 // tile list (selected-entry tiles, then window tiles, each window tile
@@ -617,14 +611,14 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
   int h = prof_begin(CSA2_K_ATTENTION, stream);
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
   if (p.tiles_per_split == 1 && p.max_splits == p.n_tiles) {  // (the tile form)
-    // one tile per workgroup: selected-entry tiles are shared by the layers
-    // layer groups of two: gathering a tile twice is cheap next to running
-    // four layers one after another in one workgroup
+    // one tile per workgroup: a selected-entry tile serves a pair of layers
+    // (gathering a tile twice is cheap next to running four layers in one
+    // workgroup), scored side by side
     constexpr int LG = 2;
     const int n_groups = (p.n_layers + LG - 1) / LG;
     const int per_row = n_tile_idx * n_groups + (p.window_elsewhere ? 0 : p.n_layers * (p.n_tiles - n_tile_idx));
     const int grows = p.rows >= kXcds ? (p.rows + kXcds - 1) / kXcds * kXcds : p.rows;
-    hipLaunchKernelGGL(k_attention_tiles<LG>, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(k_attention_tiles_pair, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p);
   } else if (p.n_layers >= 2) {
     // two or more layers: the pair form
     const int punits = (p.n_layers + 1) / 2 * p.rows;
