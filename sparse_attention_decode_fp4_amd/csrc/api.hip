@@ -226,7 +226,9 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
       f.rows = p.rows; f.n_q = a->n_q; f.ratio = a->ratio; f.k = a->k; f.batch = nb;
       f.tiles_per_seq = (a->n_q + kPfRows - 1) / kPfRows;
       const int tiles = nb * f.tiles_per_seq;
-      f.esplit = std::max(1, std::min(kPfSplits, (1024 + tiles - 1) / tiles));
+      // key ranges per row tile: enough workgroups to fill the device in one round
+      const int slots = prefill_filter_slots(a->idx_w != nullptr);
+      f.esplit = std::max(1, std::min(kPfSplits, (slots + tiles - 1) / tiles));
       f.seq = p.seq;
       f.idx_q = a->idx_q + row0 * kHI * kDI;
       f.idx_w = a->idx_w ? a->idx_w + row0 * kHI : nullptr;

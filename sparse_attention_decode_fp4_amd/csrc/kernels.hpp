@@ -231,10 +231,14 @@ struct PrefillPass {
   float* thresh;                 // [rows]
   uint32_t* fallbacks;           // rows that took the exact recompute (a counter)
   uint32_t* count;               // [rows][kPfSplits] candidates per segment
-  uint64_t* list;                // [rows][kPfSplits][kPfSeg]
+  uint64_t* list;                // [rows][kPfSplits][kPfSeg] (position, score bits) pairs
   int32_t* out;                  // [rows][out_stride]
   int32_t out_stride;
 };
 hipError_t launch_prefill_index(const PrefillPass& p, hipStream_t stream);
+// Filter workgroups resident on the current device at once (CUs x
+// workgroups per CU for the filter variant with or without head weights);
+// the key split of a prefill chunk is sized to fill them in one round.
+int prefill_filter_slots(bool has_w);
 
 }  // namespace csa2

@@ -12,7 +12,9 @@
 //              so that about 2.5 k keys of the full row reach T0;
 //   filter     MFMA scores of every visible (row, key) pair; pairs scoring at
 //              least T0 are appended to the row's candidate list, one segment
-//              per (row, key range) counted in LDS, so no global atomics;
+//              per (row, key range).  A row belongs to one wave, which counts
+//              it in a register lane (no atomics); the grid is sized to fill
+//              the device in one round;
 //   select     if the list holds at least min(k, visible) candidates and did
 //              not overflow, it contains the whole top k.  MFMA scores are
 //              not binary32-exact (measured error up to ~2.5e-5 of the sum
@@ -24,6 +26,8 @@
 //              the sampled threshold) the row is recomputed exactly on its own
 //              (VALU scoring, radix steps over recomputed keys): slow, exact,
 //              and reached only when the sample misleads.
+#include <atomic>
+
 #include "kernels.hpp"
 #include "select.hpp"
 
@@ -51,6 +55,10 @@ __device__ __forceinline__ int64_t pf_visible(const PrefillPass& p, int seq, int
 // visible count of the tile's first query (the smallest of the tile).
 __device__ __forceinline__ int64_t pf_sample_key(int64_t t, int64_t V, int64_t S) {
   return S == V ? t : (t * V) / kPfSample;  // S == kPfSample whenever strided
+}
+
+__device__ __forceinline__ float tv_at(const float4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 __device__ __forceinline__ float key_to_score(uint32_t key) {
@@ -95,12 +103,16 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[2][kPfStage * kDI];
   __shared__ float stage_ks[2][kPfStage];
   __shared__ int64_t vis_row[kPfRows];
-  __shared__ float w_row[kHasW ? kPfRows * kHI : 1];
-  __shared__ uint32_t seg_count[kFilter ? kPfRows : 1];
+  __shared__ __attribute__((aligned(16))) float w_row[kHasW ? kPfRows * kHI : 4];
+  // row thresholds (filter), each group of 8 rows stored as [even rows,
+  // odd rows], so a lane's four rows 8a + 2i + half are one 16-byte read
+  __shared__ __attribute__((aligned(16))) float thr[kFilter ? kPfRows : 4];
 
   for (int i = t; i < kPfRows; i += 256) vis_row[i] = i < nq_tile ? pf_visible(p, seq, q0 + i) : 0;
   if (kFilter)
-    for (int i = t; i < kPfRows; i += 256) seg_count[i] = 0;
+    for (int i = t; i < kPfRows; i += 256) {
+      thr[(i & ~7) + 4 * (i & 1) + ((i & 7) >> 1)] = i < nq_tile ? p.thresh[row0 + i] : INFINITY;
+    }
   if (kHasW)
     for (int i = t; i < kPfRows * kHI; i += 256)
       w_row[i] = (i / kHI) < nq_tile ? p.idx_w[(row0 + i / kHI) * kHI + (i % kHI)] : 0.0f;
@@ -120,18 +132,6 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
     }
     A[a] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
-  // thresholds of the 32 query rows this lane sees (filter only)
-  float T[8][4];
-  if (kFilter) {
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ql = 64 * wave + 8 * a + 2 * i + half;
-        T[a][i] = ql < nq_tile ? p.thresh[row0 + ql] : INFINITY;
-      }
-  }
-
   const int seq_keys = 0;
   (void)seq_keys;
   const uint8_t* kb = p.k8 + (int64_t)seq * p.k_stride * kDI;
@@ -158,6 +158,10 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
     stage_ks[buf][t] = ksv;
   };
 
+  uint32_t cnt = 0u;  // filter: candidates of row 64 wave + lane so far
+  // the lane's segment for the rows 64 wave + 8a + 2i + half of this split
+  uint64_t* const list_lane = p.list + ((row0 + 64 * wave + half) * kPfSplits + split) * kPfSeg;
+  const uint32_t half_mask = half ? 0xFFFFFFFFu : 0u;
   int buf = 0;
   stage_load(0, k_begin);
   for (int64_t base = k_begin; base < k_end; base += kPfStage) {
@@ -172,19 +176,28 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
       const float ksn = stage_ks[buf][bt + l32];
       const int64_t slot = base + bt + l32;
       const bool slot_ok = (bt + l32) < n_here;
+      const uint64_t slot_mask = __builtin_amdgcn_ballot_w64(slot_ok);
       const bool all_visible = kFilter ? (base + bt + 32 <= v_first) : true;
+      // head weights and thresholds of A tile a's rows (LDS), read one tile
+      // ahead of their use
+      auto load_wt = [&](int a, float4 (&wv)[4], float4& tv) {
+        if (kHasW)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            wv[i] = *reinterpret_cast<const float4*>(&w_row[(64 * wave + 8 * a + 2 * i + half) * kHI]);
+        if (kFilter) tv = *reinterpret_cast<const float4*>(&thr[64 * wave + 8 * a + 4 * half]);
+      };
       // epilogue of A tile a: ReLU-sum of the 4 heads, times the key scale;
       // filter: append the pairs at or above the row threshold
-      auto epilogue = [&](const v16f_t& acc, int a) {
+      auto epilogue = [&](const v16f_t& acc, int a, const float4 (&wv)[4], const float4& tv) {
         float sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int ql = 64 * wave + 8 * a + 2 * i + half;
           const float r0 = relu(acc[4 * i]), r1 = relu(acc[4 * i + 1]);
           const float r2 = relu(acc[4 * i + 2]), r3 = relu(acc[4 * i + 3]);
           float sum;
           if (kHasW) {
-            sum = w_row[ql * kHI] * r0 + w_row[ql * kHI + 1] * r1 + w_row[ql * kHI + 2] * r2 + w_row[ql * kHI + 3] * r3;
+            sum = wv[i].x * r0 + wv[i].y * r1 + wv[i].z * r2 + wv[i].w * r3;
           } else {
             sum = (r0 + r1) + (r2 + r3);
           }
@@ -194,24 +207,55 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
         // MFMA reads all lanes' operands, so it must not be sunk into one
         asm volatile("" ::"v"(sc[0]), "v"(sc[1]), "v"(sc[2]), "v"(sc[3]));
         if (kFilter) {
-          // the lane's four pairs against their rows' thresholds, then one
-          // branch for the (rare) appends
-          uint32_t hm = 0u;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) hm |= (sc[i] >= T[a][i] ? 1u : 0u) << i;
-          if (!slot_ok) hm = 0u;
-          if (hm) {
+          // append the pairs at or above their row's threshold.  A row's
+          // pairs all come from this wave (rows 64 wave .. + 63), so its
+          // count lives in lane r of cnt: the 32 lanes of a half share the
+          // row 8a + 2i + half, and each hit takes the slot count + (hits
+          // of its half in lower lanes), with no LDS atomic round trip.
+          // The causal-edge test (check_vis) runs only where the key block
+          // reaches past some row's visible keys: a uniform branch between
+          // two copies, so no per-lane flags are merged across it
+          auto append = [&](bool check_vis) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int ql = 64 * wave + 8 * a + 2 * i + half;
-              if (((hm >> i) & 1u) && (all_visible || slot < vis_row[ql])) {
-                // append to this row's segment for this key range
-                const uint32_t at = atomicAdd(&seg_count[ql], 1u);
-                if (at < (uint32_t)kPfSeg)
-                  p.list[((row0 + ql) * kPfSplits + split) * kPfSeg + at] = select_key(score_key(sc[i]), (uint32_t)slot);
+              // lane masks straight from the compares (slot_ok's mask is
+              // taken once per key block)
+              const bool above = sc[i] >= tv_at(tv, i);
+              const bool vis = !check_vis || slot < vis_row[64 * wave + 8 * a + 2 * i + half];
+              uint64_t m = __builtin_amdgcn_ballot_w64(above) & slot_mask;
+              if (check_vis) m &= __builtin_amdgcn_ballot_w64(vis);
+              const bool h = slot_ok && above && vis;
+              if (m) {
+                const int r0 = 8 * a + 2 * i;  // row of half 0 within the wave
+                const uint32_t b0 = __builtin_amdgcn_readlane(cnt, r0);
+                const uint32_t b1 = __builtin_amdgcn_readlane(cnt, r0 + 1);
+                const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+                const uint32_t n0 = __builtin_popcount(lo), n1 = __builtin_popcount(hi);
+                // entry index in the lane's list: row offset + the row's
+                // count + hits of its half in lower lanes.  mbcnt_lo adds
+                // all of half 0's hits to half 1's lanes, so their base is
+                // b1 - n0; the per-half base is picked with the lane mask
+                const uint32_t rbase = (uint32_t)(r0 * kPfSplits * kPfSeg);
+                const uint32_t x = ((b1 - n0 - b0) & half_mask) + (b0 + rbase);
+                const uint32_t off = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, x));
+                if (h && off < rbase + (uint32_t)kPfSeg) {
+                  // raw (position, score bits); the select makes the key
+                  uint32_t* dst = reinterpret_cast<uint32_t*>(list_lane + off);
+                  dst[0] = (uint32_t)slot;
+                  dst[1] = __float_as_uint(sc[i]);
+                }
+                // lanes r0 and r0 + 1 of cnt take the new counts (lane
+                // writes, no compare against every lane index)
+                asm("v_writelane_b32 %0, %1, %3\n\tv_writelane_b32 %0, %2, %4"
+                    : "+v"(cnt)
+                    : "s"(b0 + n0), "s"(b1 + n1), "i"(r0), "i"(r0 + 1));
               }
             }
-          }
+          };
+          if (all_visible)
+            append(false);
+          else
+            append(true);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -221,26 +265,33 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
         }
       };
       // software pipeline: the MFMA of tile a + 1 is issued before the
-      // epilogue of tile a, so it runs under it
-      v16f_t acc0 = {}, acc1 = {};
-      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[0], B, acc0, 0, 0, 0, kUnitScales, 0, kUnitScales);
-#pragma unroll
-      for (int a = 0; a < 8; a += 2) {
-        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 1], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
+      // epilogue of tile a, so it runs under it.  The empty asm takes the
+      // result as an operand at the issue point, which keeps the compiler
+      // from sinking the MFMA past the epilogue's branch to its own use (the
+      // asm emits nothing, so nothing waits for the result there)
+      v16f_t acc[2];
+      float4 wv[2][4], tv[2];
+      acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[0], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
                                                               kUnitScales);
-        epilogue(acc0, a);
-        if (a + 2 < 8)
-          acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 2], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
-                                                                kUnitScales);
-        epilogue(acc1, a + 1);
+      if (kFilter) asm volatile("" : "+v"(acc[0]));
+      if (kFilter) load_wt(0, wv[0], tv[0]);
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        if (a + 1 < 8) {
+          acc[(a + 1) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a + 1], B, v16f_t{}, 0, 0, 0,
+                                                                            kUnitScales, 0, kUnitScales);
+          if (kFilter) {
+            asm volatile("" : "+v"(acc[(a + 1) & 1]));
+            load_wt(a + 1, wv[(a + 1) & 1], tv[(a + 1) & 1]);
+          }
+        }
+        if (!kFilter) load_wt(a, wv[a & 1], tv[a & 1]);  // the sample pass: no pipeline
+        epilogue(acc[a & 1], a, wv[a & 1], tv[a & 1]);
       }
     }
     buf ^= 1;
   }
-  if (kFilter) {
-    __syncthreads();
-    for (int i = t; i < nq_tile; i += 256) p.count[(row0 + i) * kPfSplits + split] = seg_count[i];
-  }
+  if (kFilter && 64 * wave + lane < nq_tile) p.count[(row0 + 64 * wave + lane) * kPfSplits + split] = cnt;
 }
 
 // ------------------------------------------------------------------ threshold
@@ -437,8 +488,9 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
 #pragma unroll
     for (int i = 0; i < kPfSeg / 4; i += 2) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + i);
-      sv[i] = ((uint64_t)v.y << 32) | v.x;
-      sv[i + 1] = ((uint64_t)v.w << 32) | v.z;
+      // entries are (position, score bits) as the filter wrote them
+      sv[i] = select_key(score_key(__uint_as_float(v.y)), v.x);
+      sv[i + 1] = select_key(score_key(__uint_as_float(v.w)), v.z);
     }
   }
   const bool seg_over = __syncthreads_or((t & 3) == 0 && seg > (uint32_t)kPfSeg);
@@ -627,6 +679,21 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
     }
     for (uint32_t j = written + t; j < k; j += 256) out[j] = -1;
   }
+}
+
+int prefill_filter_slots(bool has_w) {
+  static std::atomic<int> cache[2][64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  int v = cache[has_w][dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, n_cu = 0;
+  const hipError_t e1 = has_w ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_prefill_mfma<true, true>, 256, 0)
+                              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_prefill_mfma<true, false>, 256, 0);
+  const hipError_t e2 = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  v = (e1 == hipSuccess && e2 == hipSuccess && per_cu > 0 && n_cu > 0) ? per_cu * n_cu : 1024;
+  cache[has_w][dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 hipError_t launch_prefill_index(const PrefillPass& p, hipStream_t stream) {
