@@ -159,6 +159,7 @@ struct PairLds {
   uint16_t Phi1[kH * kPStride];    // P of the second layer
   uint16_t Plo1[kH * kPStride];
   float red2[4][kH];               // per scoring wave: exponential sums per head
+  float alpha2[2][kH];             // the step's rescale factor per (layer, head)
 };
 
 // One tile for the layers in `active` (bit j: layer j of the pair): S^T for
@@ -197,8 +198,7 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
       lg[rb][r] = scorer && s.t.row_ok[cr] ? acc[rb][r] * sc2 : -INFINITY;
       mx = fmaxf(mx, lg[rb][r]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = max_xor32(max_xor16(mx));
   if (g4 == 0) s.t.red[wave][l16] = mx;
   __syncthreads();
   float m_new[2], alpha[2];
@@ -207,6 +207,7 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
     const float m_tile = (active >> j) & 1 ? fmaxf(s.t.red[2 * j][l16], s.t.red[2 * j + 1][l16]) : -INFINITY;
     m_new[j] = fmaxf(m_run[j], m_tile);
     alpha[j] = m_run[j] == -INFINITY ? 0.0f : exp2f(m_run[j] - m_new[j]);
+    if (wave == 0 && g4 == 0) s.alpha2[j][l16] = alpha[j];  // read after the barrier below
   }
   if (scorer) {
     const float mn = L == 0 ? m_new[0] : m_new[1];
@@ -222,8 +223,7 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
         (L == 0 ? phi[0] : phi[1])[l16 * kPStride + cr] = (uint16_t)hi;
         (L == 0 ? plo[0] : plo[1])[l16 * kPStride + cr] = (uint16_t)bf16_round(pv - __uint_as_float(hi << 16));
       }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
+    sum = sum_xor32(sum_xor16(sum));
     if (g4 == 0) s.red2[wave][l16] = sum;
   }
   __syncthreads();
@@ -233,13 +233,17 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
     l_run[j] = l_run[j] * alpha[j] + add;
     m_run[j] = m_new[j];
   }
-  // O = alpha O + P . E for each active layer (the rescale factor of row
-  // 4 g4 + r lives in lane 4 g4 + r)
+  // O = alpha O + P . E for each active layer (rows 4 g4 .. +3 of O are
+  // heads 4 g4 .. +3)
   float arow_alpha[2][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) arow_alpha[j][r] = __shfl(alpha[j], 4 * g4 + r, 64);
+  for (int j = 0; j < 2; ++j) {
+    const float4 aa = *reinterpret_cast<const float4*>(&s.alpha2[j][4 * g4]);
+    arow_alpha[j][0] = aa.x;
+    arow_alpha[j][1] = aa.y;
+    arow_alpha[j][2] = aa.z;
+    arow_alpha[j][3] = aa.w;
+  }
   // transposing reads of E: lane (g4, l16) addresses row 8 g4 + l16 / 4 (+4,
   // +32) and 4 channels at 4 (l16 % 4) of each 16-channel block; one layer
   // after the other, so one layer's P operands are live at a time
@@ -549,14 +553,12 @@ __global__ __launch_bounds__(256) void k_attention_merge(AttnPass p, int32_t map
     const int lane = t & 63, wave = t >> 6, s_t = t / kH, h_t = t % kH;
     const bool live = s_t < ns;
     const float m = live ? mv[0] : -INFINITY;
-    float M = fmaxf(m, __shfl_xor(m, 16, 64));
-    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    float M = max_xor32(max_xor16(m));
     if (lane < kH) red_m[wave][lane] = M;
     __syncthreads();
     M = fmaxf(fmaxf(red_m[0][h_t], red_m[1][h_t]), fmaxf(red_m[2][h_t], red_m[3][h_t]));
     const float w = m == -INFINITY ? 0.0f : exp2f(m - M) * lv[0];
-    float L = w + __shfl_xor(w, 16, 64);
-    L += __shfl_xor(L, 32, 64);
+    float L = sum_xor32(sum_xor16(w));
     if (lane < kH) red_l[wave][lane] = L;
     __syncthreads();
     L = (red_l[0][h_t] + red_l[1][h_t]) + (red_l[2][h_t] + red_l[3][h_t]);

@@ -183,6 +183,28 @@ __device__ __forceinline__ uint64_t wave_reduce64(uint64_t x) {
          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
 }
 
+// x[lane] op x[lane ^ 16] and x[lane] op x[lane ^ 32] for a commutative op,
+// through the lane swaps of gfx950 (v_permlane16_swap / v_permlane32_swap:
+// VALU, no LDS round trip).  With both operands the same register, the two
+// results of a swap are x[lane] and x[lane ^ 16] (or ^ 32) in some order.
+// Every lane of the wave must be active.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);

@@ -47,6 +47,7 @@ struct TileLds {
   uint16_t Phi[kH * kPStride];
   uint16_t Plo[kH * kPStride];
   float red[4][kH];
+  float alpha[kH];  // the step's rescale factor per head
   uint8_t row_ok[kAttnSplit];
 };
 
@@ -284,13 +285,13 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
     lg[r] = s.row_ok[16 * wave + 4 * g4 + r] ? acc[r] * sc2 : -INFINITY;
     mx = fmaxf(mx, lg[r]);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = max_xor32(max_xor16(mx));
   if (g4 == 0) s.red[wave][l16] = mx;
   __syncthreads();
   const float m_tile = fmaxf(fmaxf(s.red[0][l16], s.red[1][l16]), fmaxf(s.red[2][l16], s.red[3][l16]));
   const float m_new = fmaxf(m_run, m_tile);
   const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+  if (wave == 0 && g4 == 0) s.alpha[l16] = alpha;  // read after the barriers below
   float sum = 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -301,18 +302,16 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
     s.Phi[l16 * kPStride + cr] = (uint16_t)hi;
     s.Plo[l16 * kPStride + cr] = (uint16_t)bf16_round(pv - __uint_as_float(hi << 16));
   }
-  sum += __shfl_xor(sum, 16, 64);
-  sum += __shfl_xor(sum, 32, 64);
+  sum = sum_xor32(sum_xor16(sum));
   __syncthreads();  // red[] (tile maxima) is read by everyone before reuse
   if (g4 == 0) s.red[wave][l16] = sum;
   __syncthreads();
   l_run = l_run * alpha + (s.red[0][l16] + s.red[1][l16] + s.red[2][l16] + s.red[3][l16]);
   m_run = m_new;
 
-  // O = alpha * O + P . E   (the rescale factor of row 4*g4+r lives in lane 4*g4+r)
-  float arow_alpha[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) arow_alpha[r] = __shfl(alpha, 4 * g4 + r, 64);
+  // O = alpha * O + P . E   (rows 4 g4 .. +3 of O are heads 4 g4 .. +3)
+  const float4 aa = *reinterpret_cast<const float4*>(&s.alpha[4 * g4]);
+  const float arow_alpha[4] = {aa.x, aa.y, aa.z, aa.w};
   const uint4 ahi0 = *reinterpret_cast<const uint4*>(s.Phi + l16 * kPStride + 8 * g4);
   const uint4 ahi1 = *reinterpret_cast<const uint4*>(s.Phi + l16 * kPStride + 32 + 8 * g4);
   const uint4 alo0 = *reinterpret_cast<const uint4*>(s.Plo + l16 * kPStride + 8 * g4);
