@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
   EntryFetch f;
   int32_t pos_next = -1;
   if (tile_begin <= last_sel) {
-    fetch_entry(p, seq, tile_position(p, tile_begin, row), f);
+    fetch_entry<true>(p, seq, tile_position(p, tile_begin, row), f);
     if (tile_begin + 1 <= last_sel) pos_next = tile_position(p, tile_begin + 1, row);
   }
   // the queries, loaded once for the workgroup and staged through E (free
@@ -100,9 +100,9 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     if (tile > tile_begin) __syncthreads();  // the previous tile's readers of E are done
     if (tile <= last_sel) {
-      store_entry(f, s);
+      store_entry<true>(f, s);
       if (tile + 1 <= last_sel) {
-        fetch_entry(p, seq, pos_next, f);
+        fetch_entry<true>(p, seq, pos_next, f);
         if (tile + 2 <= last_sel) pos_next = tile_position(p, tile + 2, row);
       }
 #pragma unroll
@@ -213,16 +213,16 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
     const float mn = L == 0 ? m_new[0] : m_new[1];
     float sum = 0.0f;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+      float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int cr = 32 * hb + 16 * rb + 4 * g4 + r;
-        const float pv = mn == -INFINITY ? 0.0f : exp2f(lg[rb][r] - mn);
-        sum += pv;
-        const uint32_t hi = bf16_round(pv);
-        (L == 0 ? phi[0] : phi[1])[l16 * kPStride + cr] = (uint16_t)hi;
-        (L == 0 ? plo[0] : plo[1])[l16 * kPStride + cr] = (uint16_t)bf16_round(pv - __uint_as_float(hi << 16));
+        pv[r] = mn == -INFINITY ? 0.0f : exp2f(lg[rb][r] - mn);
+        sum += pv[r];
       }
+      const int c0 = l16 * kPStride + 32 * hb + 16 * rb + 4 * g4;
+      store_p4(pv, (L == 0 ? phi[0] : phi[1]) + c0, (L == 0 ? plo[0] : plo[1]) + c0);
+    }
     sum = sum_xor32(sum_xor16(sum));
     if (g4 == 0) s.red2[wave][l16] = sum;
   }
@@ -342,9 +342,9 @@ __global__ __launch_bounds__(256) void k_attention_tiles_pair(AttnPass p) {
     const int32_t pos = tile_position(p, tile, row);
     uint4 qb[16];
     EntryFetch f;
-    fetch_entry(p, seq, pos, f);
+    fetch_entry<false>(p, seq, pos, f);
     stage_q_pair(p, l0, nl, row, s, qb);
-    store_entry(f, s.t);
+    store_entry<false>(f, s.t);
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
     f32x4_t o[2][8];
 #pragma unroll
@@ -420,15 +420,15 @@ __global__ __launch_bounds__(256, 2) void k_attention_pair(AttnPass p) {
   EntryFetch f;
   int32_t pos_next = -1;
   if (tile_begin < sel_end) {
-    fetch_entry(p, seq, tile_position(p, tile_begin, row), f);
+    fetch_entry<true>(p, seq, tile_position(p, tile_begin, row), f);
     if (tile_begin + 1 < sel_end) pos_next = tile_position(p, tile_begin + 1, row);
   }
   stage_q_pair(p, l0, nl, row, s, qb);
   for (int tile = tile_begin; tile < sel_end; ++tile) {
     if (tile > tile_begin) __syncthreads();  // the previous tile's readers of E are done
-    store_entry(f, st);
+    store_entry<true>(f, st);
     if (tile + 1 < sel_end) {
-      fetch_entry(p, seq, pos_next, f);
+      fetch_entry<true>(p, seq, pos_next, f);
       if (tile + 2 < sel_end) pos_next = tile_position(p, tile + 2, row);
     }
     pair_step(s, qb, both, sc2, m_run, l_run, o);

@@ -29,17 +29,25 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-__device__ __forceinline__ uint32_t bf16_round(float x) {  // round to nearest even, bf16 bits
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   // exact values only (the rounding of the packing convert changes none);
   // one v_cvt_pk_bf16_f32 instead of a shift and a masked or
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// P values of 4 consecutive rows of one head as bf16 hi and lo parts, hi
+// the round-to-nearest-even bf16 of p and lo that of p - hi (relative error
+// ~2^-16), one 8-byte LDS store each (16-bit stores of single values
+// conflict in the banks and take four times the instructions)
+__device__ __forceinline__ void store_p4(const float (&pv)[4], uint16_t* hi_dst, uint16_t* lo_dst) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const bf16x4_t h = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+  const bf16x4_t l = {(__bf16)(pv[0] - (float)h[0]), (__bf16)(pv[1] - (float)h[1]), (__bf16)(pv[2] - (float)h[2]),
+                      (__bf16)(pv[3] - (float)h[3])};
+  *reinterpret_cast<uint2*>(hi_dst) = __builtin_bit_cast(uint2, h);
+  *reinterpret_cast<uint2*>(lo_dst) = __builtin_bit_cast(uint2, l);
 }
 
 struct TileLds {
@@ -71,17 +79,26 @@ __device__ __forceinline__ void dequant16(uint2 codes, float s, uint4 (&v)[2]) {
   v[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// A selected-entry tile in flight, read with consecutive lanes on
-// consecutive bytes: in load step i (0..3) wave w takes entries
-// 16 w + 4 i + lane / 16, lane % 16 reading 16 bytes of codes (channels
-// 32 (lane % 16) .. +31, two scale groups) and those groups' two scales.  A
-// wave instruction thus covers four whole entries; a lane per entry, 16
-// bytes each, would touch 64 lines per instruction and take several times
-// as long to load the same tile.
+// A selected-entry tile in flight, in one of two lane layouts (kByRow).
+// Both read 64-byte or longer runs of each entry per wave instruction (a
+// lane per entry, 16 bytes each, would touch 64 lines per instruction and
+// take several times as long).
+//   kByRow = false: in load step i (0..3) wave w takes entries
+//     16 w + 4 i + lane / 16, lane % 16 reading 16 bytes of codes (channels
+//     32 (lane % 16) .. +31, two scale groups) and those groups' two scales:
+//     4 whole entries (8 lines) per instruction, the fewest lines and the
+//     shortest fetch for a tile fetched once (decode).  Its LDS stores put
+//     16 lanes on one row at 64-byte steps, which conflict four ways.
+//   kByRow = true: lane (g = lane / 16, l16) of wave w holds entry
+//     16 w + l16 and in step i reads channels 32 (4 i + g) .. +31: 64 bytes
+//     of each of 16 entries per instruction, and the 16 consecutive lanes
+//     of a store write 16 rows at one column, without bank conflicts (the
+//     stores of a tile take a quarter of the LDS cycles).  For kernels that
+//     stream many tiles through LDS (prefill, multi-token rows).
 struct EntryFetch {
   uint4 raw[4];
   uint32_t sc[4];  // the two E4M3 scales of step i in bits 0..15
-  uint32_t valid;  // bit i: the entry of step i is present
+  uint32_t valid;  // kByRow: the lane's entry is present; else bit i: the entry of step i
 };
 
 __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, int row) {
@@ -95,8 +112,9 @@ __device__ __forceinline__ int32_t tile_position(const AttnPass& p, int tile, in
 // empty slot uses the entry index at the descriptors' limit
 // (CSA2_MAX_ENTRIES, or the pool size), so the hardware returns zeros
 // without touching memory.  No load waits on another.
+template <bool kByRow>
 __device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t pos_lane, EntryFetch& f) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   // paged caches: descriptors over the pool, and each lane first turns its
   // position into a pool entry (one page-table load)
   const bool paged = p.pm.pages != nullptr;
@@ -108,39 +126,57 @@ __device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t 
       (void*)(p.scale + s0 * CSA2_SCALE_BYTES), 0, (int)(lim * CSA2_SCALE_BYTES), kRawBufferWord3);
   uint32_t e_lane = pos_lane >= 0 ? (uint32_t)pos_lane : lim;
   if (paged && pos_lane >= 0) e_lane = paged_entry_at(p.pm, seq, pos_lane);
-  f.valid = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int src = 16 * wave + 4 * i + (lane >> 4);
+  if (kByRow) {
+    const int src = 16 * wave + l16;  // the lane's entry
     const int32_t pos = __shfl(pos_lane, src, 64);
     const uint32_t e = (uint32_t)__shfl((int)e_lane, src, 64);
-    f.valid |= (pos >= 0 ? 1u : 0u) << i;
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(e * CSA2_NIB_BYTES) + 16 * l16, 0, 0);
-    f.raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
-    f.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(e * CSA2_SCALE_BYTES) + 2 * l16, 0, 0);
+    f.valid = pos >= 0 ? 1u : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int piece = 4 * i + g;  // 32 channels: code bytes 16 piece .., scale bytes 2 piece ..
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(e * CSA2_NIB_BYTES) + 16 * piece, 0, 0);
+      f.raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      f.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(e * CSA2_SCALE_BYTES) + 2 * piece, 0, 0);
+    }
+  } else {
+    f.valid = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int src = 16 * wave + 4 * i + g;
+      const int32_t pos = __shfl(pos_lane, src, 64);
+      const uint32_t e = (uint32_t)__shfl((int)e_lane, src, 64);
+      f.valid |= (pos >= 0 ? 1u : 0u) << i;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(e * CSA2_NIB_BYTES) + 16 * l16, 0, 0);
+      f.raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      f.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(e * CSA2_SCALE_BYTES) + 2 * l16, 0, 0);
+    }
   }
 }
 
-// Dequantise a fetched tile into E (zeros for empty slots): each lane
-// writes 64 bytes of one row, the 16 lanes of an entry its whole row.
+// Dequantise a fetched tile into E (zeros for empty slots).  kByRow: in step
+// i each lane writes channels 32 (4 i + g) .. +31 of its own row; else the
+// 16 lanes of an entry write its whole row, 64 bytes each.  Chunk c of row
+// r sits at c ^ (bit 2 of r).
+template <bool kByRow>
 __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int er = 16 * wave + 4 * i + (lane >> 4);
-    const int sw = i & 1;  // bit 2 of er: chunk c of the row sits at c ^ sw
+    const int er = kByRow ? 16 * wave + l16 : 16 * wave + 4 * i + g;
+    const int sw = (er >> 2) & 1;
     uint16_t* dst = s.E + er * kEStride;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint4 v[2];
       dequant16(half ? make_uint2(f.raw[i].z, f.raw[i].w) : make_uint2(f.raw[i].x, f.raw[i].y),
                 e4m3_value((f.sc[i] >> (8 * half)) & 0xFFu), v);
-      const int c = 4 * l16 + 2 * half;
+      const int c = kByRow ? 4 * (4 * i + g) + 2 * half : 4 * l16 + 2 * half;
       *reinterpret_cast<uint4*>(dst + 8 * (c ^ sw)) = v[0];
       *reinterpret_cast<uint4*>(dst + 8 * ((c + 1) ^ sw)) = v[1];
     }
-    if (l16 == 0) s.row_ok[er] = (uint8_t)((f.valid >> i) & 1u);
+    if (!kByRow && l16 == 0) s.row_ok[er] = (uint8_t)((f.valid >> i) & 1u);
   }
+  if (kByRow && g == 0) s.row_ok[16 * wave + l16] = (uint8_t)f.valid;
 }
 
 // A window tile: wave w copies rows 16 w .. +15 of the tile, one row (1 KB,
@@ -207,8 +243,8 @@ __device__ __forceinline__ void load_tile(const AttnPass& p, const AttnLayer& L,
                                           int seq, int64_t t0, int n_win, TileLds& s) {
   if (tile < n_tile_idx) {
     EntryFetch f;
-    fetch_entry(p, seq, tile_position(p, tile, row), f);
-    store_entry(f, s);
+    fetch_entry<false>(p, seq, tile_position(p, tile, row), f);
+    store_entry<false>(f, s);
   } else {
     load_window(p, L, tile - n_tile_idx, seq, t0, n_win, s);
   }
@@ -293,15 +329,13 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
   const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
   if (wave == 0 && g4 == 0) s.alpha[l16] = alpha;  // read after the barriers below
   float sum = 0.0f;
+  float pv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int cr = 16 * wave + 4 * g4 + r;
-    const float pv = (m_new == -INFINITY) ? 0.0f : exp2f(lg[r] - m_new);
-    sum += pv;
-    const uint32_t hi = bf16_round(pv);
-    s.Phi[l16 * kPStride + cr] = (uint16_t)hi;
-    s.Plo[l16 * kPStride + cr] = (uint16_t)bf16_round(pv - __uint_as_float(hi << 16));
+    pv[r] = (m_new == -INFINITY) ? 0.0f : exp2f(lg[r] - m_new);
+    sum += pv[r];
   }
+  store_p4(pv, s.Phi + l16 * kPStride + 16 * wave + 4 * g4, s.Plo + l16 * kPStride + 16 * wave + 4 * g4);
   sum = sum_xor32(sum_xor16(sum));
   __syncthreads();  // red[] (tile maxima) is read by everyone before reuse
   if (g4 == 0) s.red[wave][l16] = sum;
