@@ -179,10 +179,12 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int r = 32 * hb + 16 * rb + l16;
+      // logical chunk 4 ks + g4 of row r at (4 ks + g4) ^ row_swizzle(r)
       const uint16_t* arow = s.t.E + r * kEStride + 8 * (g4 ^ ((r >> 2) & 1));
+      const int d3 = (r & 8) ? 64 : 0;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks);
+        const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks + ((ks & 2) ? -d3 : d3));
         acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[ks]), acc[rb], 0, 0, 0);
       }
     }
@@ -248,6 +250,7 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
   // +32) and 4 channels at 4 (l16 % 4) of each 16-channel block; one layer
   // after the other, so one layer's P operands are live at a time
   const uint16_t* bbase = s.t.E + (8 * g4 + (l16 >> 2)) * kEStride + 128 * wave + 4 * (l16 & 3);
+  const int d8 = (g4 & 1) ? 64 : 0;  // rows with bit 3 set: halves of 256 bytes swapped
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (!((active >> j) & 1)) continue;  // (uniform)
@@ -259,7 +262,7 @@ __device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int
     const uint4 pl1 = *reinterpret_cast<const uint4*>(qj + l16 * kPStride + 32 + 8 * g4);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const uint16_t* bp = bbase + 16 * nt;
+      const uint16_t* bp = bbase + 16 * nt + (nt < 4 ? d8 : -d8);
       const int dsw = (l16 & 2) ? -8 : 8;  // rows +4 and +36 hold their chunks swapped in pairs
       const v4i16_t k0 = lds_read_tr16(bp), k1 = lds_read_tr16(bp + 4 * kEStride + dsw);
       const v4i16_t k2 = lds_read_tr16(bp + 32 * kEStride), k3 = lds_read_tr16(bp + 36 * kEStride + dsw);

@@ -8,12 +8,15 @@
 
 namespace csa2 {
 
-// bf16 per row of E: rows 8 banks apart, so the transposing reads (4 rows x
-// 32 bytes per cycle) do not conflict.  Consecutive lanes write consecutive
-// rows, and in rows whose bit 2 is set the 16-byte chunks are swapped in
-// pairs (chunk c at c ^ 1), so rows r and r + 4 of the 16-byte MFMA operand
-// reads and writes fall in different banks.
+// bf16 per row of E: rows 8 banks apart.  The 16-byte chunk c of row r sits
+// at c ^ row_swizzle(r): chunks swapped in pairs in rows with bit 2 set
+// (rows r and r + 4 of the 16-byte MFMA operand reads fall in different
+// banks) and by halves of 256 bytes in rows with bit 3 set (the transposing
+// reads take rows 8 g4 + 0..3, whose bank offsets repeat every 8 rows).
+// Measured with the SQ bank-conflict counters: every load and store pattern
+// of the attention kernels on this layout runs without conflicts.
 constexpr int kEStride = kD + 16;
+__device__ __forceinline__ int row_swizzle(int r) { return ((r >> 2) & 1) | (((r >> 3) & 1) << 3); }
 constexpr int kPStride = kAttnSplit + 8;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -156,14 +159,14 @@ __device__ __forceinline__ void fetch_entry(const AttnPass& p, int seq, int32_t 
 // Dequantise a fetched tile into E (zeros for empty slots).  kByRow: in step
 // i each lane writes channels 32 (4 i + g) .. +31 of its own row; else the
 // 16 lanes of an entry write its whole row, 64 bytes each.  Chunk c of row
-// r sits at c ^ (bit 2 of r).
+// r sits at c ^ row_swizzle(r).
 template <bool kByRow>
 __device__ __forceinline__ void store_entry(const EntryFetch& f, TileLds& s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int er = kByRow ? 16 * wave + l16 : 16 * wave + 4 * i + g;
-    const int sw = (er >> 2) & 1;
+    const int sw = row_swizzle(er);
     uint16_t* dst = s.E + er * kEStride;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -225,7 +228,7 @@ __device__ __forceinline__ void store_window(const WindowFetch& f, int wtile, in
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int sw = (i >> 2) & 1;  // bit 2 of row 16 wave + i
+    const int sw = row_swizzle(16 * wave + i);
     *reinterpret_cast<uint4*>(s.E + (16 * wave + i) * kEStride + 8 * (lane ^ sw)) = f.v[i];
   }
   if (lane < 16) s.row_ok[16 * wave + lane] = wtile * kAttnSplit + 16 * wave + lane < n_win ? 1 : 0;
@@ -307,10 +310,12 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
   const int l16 = lane & 15, g4 = lane >> 4;
   __syncthreads();  // the tile is in LDS; the previous step's readers of P / red are done
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // row 16 wave + l16: logical chunk 4 ks + g4 at (4 ks + g4) ^ row_swizzle
   const uint16_t* arow = s.E + (16 * wave + l16) * kEStride + 8 * (g4 ^ ((l16 >> 2) & 1));
+  const int d3 = (l16 & 8) ? 64 : 0;  // bit 3 of the row: k blocks swapped in pairs of two
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
-    const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks);
+    const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks + ((ks & 2) ? -d3 : d3));
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[ks]), acc, 0, 0, 0);
   }
   if (q_next) load_q(q_next, row, qb);
@@ -353,9 +358,10 @@ __device__ __forceinline__ void tile_step(TileLds& s, uint4 (&qb)[16], const uin
   // transposing reads of E: lane (g4, l16) addresses row 8 g4 + l16 / 4 (+4,
   // +32) and 4 channels at 4 (l16 % 4) of each 16-channel block
   const uint16_t* bbase = s.E + (8 * g4 + (l16 >> 2)) * kEStride + 128 * wave + 4 * (l16 & 3);
+  const int d8 = (g4 & 1) ? 64 : 0;  // rows with bit 3 set: halves of 256 bytes swapped
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    const uint16_t* bp = bbase + 16 * nt;
+    const uint16_t* bp = bbase + 16 * nt + (nt < 4 ? d8 : -d8);
     const int dsw = (l16 & 2) ? -8 : 8;  // rows +4 and +36 hold their chunks swapped in pairs
     const v4i16_t k0 = lds_read_tr16(bp), k1 = lds_read_tr16(bp + 4 * kEStride + dsw);
     const v4i16_t k2 = lds_read_tr16(bp + 32 * kEStride), k3 = lds_read_tr16(bp + 36 * kEStride + dsw);
