@@ -415,11 +415,17 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
   const uint32_t need_all = vis < (int64_t)k ? (uint32_t)vis : k;
   int32_t* out = p.out + row * p.out_stride;
 
+  // 49 KB in all, so three workgroups share a CU: the k-th key's histogram
+  // and the near-tie band take turns in one array (the histogram is done
+  // with before the band is written, and the band's exact keys move to lc
+  // before the histogram serves the band's own k-th)
+  constexpr uint32_t kPfBand = 2048;  // near-tie band keys, at most (else the exact recompute)
   __shared__ uint64_t lc[kPfCap];  // candidates; after the band is settled, the position bitmap
   __shared__ uint32_t win[CSA2_MAX_K];
-  __shared__ uint32_t bt[kPfCap];
+  __shared__ uint32_t bt_h[kPfBand];
+  uint32_t* const bt = bt_h;
+  uint32_t* const h2048 = bt_h;
   __shared__ uint32_t h256[256];
-  __shared__ uint32_t h2048[2048];
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t sh3[3];
   __shared__ uint64_t sh_kth;
@@ -557,7 +563,7 @@ __global__ __launch_bounds__(256) void k_prefill_select(PrefillPass p) {
         n_win = tot >> 16;
         n_band = tot & 0xFFFFu;
         // every clear winner ranks above the k-th key, so n_win < k <= n_win + n_band
-        if (n_win >= k || n_win + n_band < k) fast = false;
+        if (n_win >= k || n_win + n_band < k || n_band > kPfBand) fast = false;
       }
       if (fast) {
 #pragma unroll
