@@ -295,8 +295,11 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
 }
 
 // ------------------------------------------------------------------ threshold
-// One wave per row: T0 = the k_s-th largest of the row's samples (exact, by
-// 8-bit radix steps over order-preserving keys held in registers).
+// One wave per row: T0 = the lower edge of the 16-bit key bucket that holds
+// the k_s-th largest of the row's samples (two 8-bit radix steps over
+// order-preserving keys held in registers).  Rounding T0 down that way (by
+// at most 2^-7 of its value) only widens the candidate list, and the select
+// checks its near-tie band against the T0 it was filtered with.
 __global__ __launch_bounds__(256) void k_prefill_threshold(PrefillPass p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(256) void k_prefill_threshold(PrefillPass p) {
     keys[j] = s < S ? score_key(p.sample[row * kPfSample + s]) : 0u;
   }
   uint32_t prefix = 0, need = ks;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = 24; shift >= 16; shift -= 8) {
     for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -346,13 +349,8 @@ __global__ __launch_bounds__(256) void k_prefill_threshold(PrefillPass p) {
     const uint32_t c0 = hist[wave][4 * lane], c1 = hist[wave][4 * lane + 1];
     const uint32_t c2 = hist[wave][4 * lane + 2], c3 = hist[wave][4 * lane + 3];
     const uint32_t mine = c0 + c1 + c2 + c3;
-    uint32_t x = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_down(x, d, 64);
-      if (lane + d < 64) x += y;
-    }
-    uint32_t ab = x - mine;
+    const uint32_t incl = wave_incl_add(mine);
+    uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;  // keys in digits above the lane's
     const uint32_t cs[4] = {c0, c1, c2, c3};
     uint32_t found = 0xFFFFFFFFu, nneed = 0;
     for (int j = 3; j >= 0; --j) {
