@@ -196,8 +196,9 @@ int64_t index_max_items(const csa2_index_args* a) {
 }
 
 int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t stream,
-              const AttnPass* window = nullptr, bool* window_done = nullptr) {
+              const AttnPass* window = nullptr, bool* window_done = nullptr, bool* tiles_done = nullptr) {
   if (window_done) *window_done = false;
+  if (tiles_done) *tiles_done = false;
   for (int s0 = 0; s0 < a->batch; s0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, a->batch - s0);
     IndexPass p{};
@@ -295,7 +296,8 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
       p.block_max_stride = w.max_blocks;
       p.row_ksm = at<uint32_t>(ws, w.row_ksm);
     }
-    if ((e = launch_index_pass(p, stream, window, window_done)) != hipSuccess) return hip_fail(e, "index pass");
+    if ((e = launch_index_pass(p, stream, window, window_done, tiles_done)) != hipSuccess)
+      return hip_fail(e, "index pass");
     if (a->kind == CSA2_INDEX_FLAT_POOL) {  // then the blocks by their largest token score
       IndexPass b = p;
       b.block_level = 2;
@@ -358,6 +360,7 @@ struct AttnJob {
   int n_layers;
   AttnLayer layer[kMaxAttnLayers];
   bool window_elsewhere;  // the window tiles ran in the select launch
+  bool tiles_elsewhere;   // so did the selected-entry tiles (only the merge is left)
   csa2_pages pages;       // paged nib / scale, or a zero table
 };
 
@@ -406,6 +409,7 @@ AttnPass make_attn_pass(const AttnJob& j, int s0, int nb, void* ws, const WsLayo
   p.max_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   p.partial = at<float>(ws, w.partial);
   p.window_elsewhere = j.window_elsewhere ? 1 : 0;
+  p.tiles_elsewhere = j.tiles_elsewhere ? 1 : 0;
   return p;
 }
 
@@ -817,9 +821,10 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
         wp = make_attn_pass(j, 0, a->batch, workspace, w);
         if (tile_form(wp)) win = &wp;
       }
-      bool win_done = false;
-      if ((rc = run_index(&ia, workspace, w, s, win, &win_done))) return rc;
+      bool win_done = false, tiles_done = false;
+      if ((rc = run_index(&ia, workspace, w, s, win, &win_done, &tiles_done))) return rc;
       j.window_elsewhere = win_done;
+      j.tiles_elsewhere = tiles_done;
       if (L.mode == CSA2_MODE_FULL) {
         st->has_full = 1;
         st->has_pool = (hier || flat_pool) ? 1 : 0;

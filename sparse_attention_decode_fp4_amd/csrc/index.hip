@@ -425,41 +425,33 @@ __device__ __forceinline__ void emit_chunk(const IndexPass& p, int64_t row, int 
   }
   __syncthreads();
   const uint32_t thi = sh[8], tlo = sh[9], n0 = sh[10];
-  // segment slots without LDS atomics: a wave's band-0 (band-1) keys follow
-  // those of the waves before it, in its ballots' lane order
-  uint64_t m0b[8], m1b[8];
-  uint32_t c0 = 0u, c1 = 0u;
+  // segment slots in item order, without LDS atomics: a lane's band-0
+  // (band-1) keys follow those of the lanes and waves before it (one wave
+  // prefix sum of both counts, packed), so each band lists its items
+  // ascending, which lets the select order its winners by compaction
+  uint32_t f0 = 0u, f1 = 0u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    m0b[j] = __ballot(k[j] != 0u && k[j] >= thi);
-    m1b[j] = __ballot(k[j] != 0u && k[j] >= tlo && k[j] < thi);
-    c0 += (uint32_t)__popcll(m0b[j]);
-    c1 += (uint32_t)__popcll(m1b[j]);
+    f0 |= (k[j] != 0u && k[j] >= thi ? 1u : 0u) << j;
+    f1 |= (k[j] != 0u && k[j] >= tlo && k[j] < thi ? 1u : 0u) << j;
   }
-  if (lane == 0) {
-    sh[16 + wave] = c0;
-    sh[20 + wave] = c1;
-  }
+  const uint32_t cnt = (uint32_t)__builtin_popcount(f0) | ((uint32_t)__builtin_popcount(f1) << 16);
+  const uint32_t incl = wave_incl_add(cnt);
+  if (lane == 63) sh[16 + wave] = incl;
   __syncthreads();
-  uint32_t o0 = 0u, o1 = n0;
-  for (int w = 0; w < wave; ++w) {
-    o0 += sh[16 + w];
-    o1 += sh[20 + w];
-  }
+  uint32_t before = incl - cnt;
+  for (int w = 0; w < wave; ++w) before += sh[16 + w];
+  uint32_t o0 = before & 0xFFFFu, o1 = n0 + (before >> 16);
   const __amdgpu_buffer_rsrc_t rseg = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.seg_list + (row * p.max_chunks + chunk) * kSeg), 0, kSeg * 8, kRawBufferWord3);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const bool in0 = (m0b[j] >> lane) & 1ull, in1 = (m1b[j] >> lane) & 1ull;
+    const bool in0 = (f0 >> j) & 1u, in1 = (f1 >> j) & 1u;
     if (in0 || in1) {
-      const uint64_t m = in0 ? m0b[j] : m1b[j];
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t slot = (in0 ? o0 : o1) + below;
+      const uint32_t slot = in0 ? o0++ : o1++;
       const uint64_t v = select_key(k[j], (uint32_t)(base + 8 * t + j));
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{(uint32_t)v, (uint32_t)(v >> 32)}, rseg, (int)(slot * 8), 0, 0);
     }
-    o0 += (uint32_t)__popcll(m0b[j]);
-    o1 += (uint32_t)__popcll(m1b[j]);
   }
   if (t == 0) {
     const __amdgpu_buffer_rsrc_t rinfo = __builtin_amdgcn_make_buffer_rsrc(
@@ -1080,9 +1072,12 @@ template <int kPer>
 using SelLdsFull = SelLds<kPer, kMaxChunks, CSA2_MAX_K>;
 
 // kPer candidates per thread, 256 kPer in all: 16 for k <= 1,024, 32 for
-// the 2,048-block stage and for rows of more than 128 chunks.
+// the 2,048-block stage and for rows of more than 128 chunks.  Leaves the
+// winners' items in ascending order in S.win (visible to every thread) and
+// returns their number.  Only a `writer` writes the row's outputs and counts
+// an exact recompute (several workgroups may select the same row).
 template <int kPer, class Lds>
-__device__ __forceinline__ void select_row(const IndexPass& p, const int row, Lds& S) {
+__device__ __forceinline__ uint32_t select_row(const IndexPass& p, const int row, Lds& S, const bool writer = true) {
   constexpr int kSelCap = 256 * kPer;
   const int t = threadIdx.x, quarter = t & 3;
   const int wave = t >> 6, lane = t & 63;
@@ -1200,7 +1195,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
     if (t == 0) seg_start[nch] = total;
   }
   const float delta = (p.mfma_scores ? kErrMfma : kErrValu) * cq * 448.0f * __uint_as_float(ksm);
-  if (p.row_ksm && p.block_level == 0 && t == 0) p.row_ksm[row] = ksm;
+  if (writer && p.row_ksm && p.block_level == 0 && t == 0) p.row_ksm[row] = ksm;
 
   bool fast = total <= (uint32_t)kSelCap;
   uint32_t n_win = 0;
@@ -1421,36 +1416,44 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
         fast = __syncthreads_or(dropped ? 1 : 0) == 0;
       }
     }
-    if (fast && use_bitmap) {  // the histogram is done with: clear the bitmap
+    // Without band 1, lc holds band 0 of every chunk in chunk order, and each
+    // segment lists its band in item order: the candidates ascend by item,
+    // and compacting the winners in lc order orders them
+    const bool ordered = !open;
+    if (fast && use_bitmap && !ordered) {  // the histogram is done with: clear the bitmap
       uint4* bm4 = reinterpret_cast<uint4*>(bitmap);
       for (int i = t; i < kBitmapItems / 128; i += 256) bm4[i] = make_uint4(0, 0, 0, 0);
       __syncthreads();
     }
     if (fast) {
       // Winners.  With more than k candidates: keys above hi win for sure
-      // and go to the bitmap at once; keys in [lo, hi] form the near-tie
-      // band, of which the keys at or above the k-th number r = k - (sure
-      // winners): if the band holds just r keys they all win, otherwise the
-      // band is rescored exactly and its r best win.  With at most k
-      // candidates (and no chunk dropping a key) every candidate wins.
+      // (into the bitmap at once, when it orders them); keys in [lo, hi]
+      // form the near-tie band, of which the keys at or above the k-th
+      // number r = k - (sure winners): if the band holds just r keys they
+      // all win, otherwise the band is rescored exactly and its r best win.
+      // With at most k candidates (and no chunk dropping a key) every
+      // candidate wins.
       const bool all = total <= k;
       if (!use_bitmap && t == 0) sh_need = 0;  // (published by the barrier below)
+      uint32_t bslot[kPer];  // 1 + the key's slot in the near-tie band; 0 outside it
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
+        bslot[i] = 0u;
         const uint32_t sk = (uint32_t)(key[i] >> 32);
         if (key[i] == 0ull) continue;
         if (all || sk > hi) {
           const uint32_t it = select_key_pos(key[i]);
-          if (use_bitmap) atomicOr(&bitmap[bitmap_slot(it >> 5)], 1u << (it & 31u));
+          if (use_bitmap && !ordered) atomicOr(&bitmap[bitmap_slot(it >> 5)], 1u << (it & 31u));
         } else if (sk >= lo) {
           const uint32_t at = atomicAdd(&sh_nb, 1u);
           if (at < kBandCap) bitem[at] = select_key_pos(key[i]);
+          bslot[i] = at + 1u;
           if (key[i] >= kth) atomicAdd(&sh_nbge, 1u);
         }
       }
       __syncthreads();
       const uint32_t nb = sh_nb, r = sh_nbge;
-      if (nb > r && nb > kBandCap) {
+      if (nb > kBandCap) {
         fast = false;  // a band this wide: the exact recompute settles the row
       } else if (nb > r) {
         rank_band(p, row, nb, r, bitem, bscore, bwin, qd, qw);
@@ -1458,7 +1461,34 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
         for (uint32_t m = t; m < nb; m += 256) bwin[m] = 1u;
         __syncthreads();
       }
-      if (fast) {
+      if (fast && ordered) {
+        // compaction in lc order (slot t + 256 i): per-wave winner counts of
+        // each i, then every thread adds up the counts ahead of its slots
+        uint32_t* wcnt = bitmap;  // [kPer][4] (the bitmap is unused here)
+        uint64_t bal[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const uint32_t sk = (uint32_t)(key[i] >> 32);
+          const bool f = key[i] != 0ull && (all || sk > hi || (bslot[i] != 0u && bwin[bslot[i] - 1u] != 0u));
+          bal[i] = __ballot(f);
+          if (lane == 0) wcnt[4 * i + wave] = (uint32_t)__popcll(bal[i]);
+        }
+        __syncthreads();
+        uint32_t run = 0u;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const uint4 c4 = reinterpret_cast<const uint4*>(wcnt)[i];
+          const uint32_t ahead = run + (wave > 0 ? c4.x : 0u) + (wave > 1 ? c4.y : 0u) + (wave > 2 ? c4.z : 0u);
+          if ((bal[i] >> lane) & 1ull) {
+            const uint32_t below =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], 0u));
+            win[ahead + below] = select_key_pos(key[i]);
+          }
+          run += (c4.x + c4.y) + (c4.z + c4.w);
+        }
+        n_win = run;
+        __syncthreads();
+      } else if (fast) {
         if (use_bitmap) {
           for (uint32_t m = t; m < nb; m += 256) {
             if (bwin[m]) {
@@ -1529,7 +1559,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
     // over the (score, -item) keys for the k-th, then the near-tie band
     // rescored exactly as above
     if (t == 0) {
-      atomicAdd(p.fallbacks, 1u);
+      if (writer) atomicAdd(p.fallbacks, 1u);
       sh_nb = 0;
     }
     half2_t q[kHI][8];
@@ -1626,6 +1656,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
     __syncthreads();
   }
 
+  if (!writer) return n_win;
   // positions of the winners, in ascending order (then -1 up to k, except
   // for block ids); rows that start on 16 bytes take four per store
   int32_t* orow = p.out + (int64_t)row * p.out_stride;
@@ -1670,6 +1701,7 @@ __device__ __forceinline__ void select_row(const IndexPass& p, const int row, Ld
       for (int32_t j = t; j < n_pool; j += 256) prow[j] = pool_at(j);
     }
   }
+  return n_win;
 }
 
 template <int kPer>
@@ -1712,6 +1744,71 @@ __global__ __launch_bounds__(256) void k_index_select_window(IndexPass p, AttnPa
   window_tile(a, row, jj / n_win_tiles, jj % n_win_tiles, s);
 }
 
+// The select of a decode index pass fused with the group's whole attention
+// launch.  Workgroup (row, j) with j < n_sel: selected-entry tile j / n_groups
+// of layer pair j % n_groups.  It selects the row's winners itself (every
+// such workgroup of a row reaches the same set and order: the select is
+// deterministic), takes winners 64 tile .. +63 from LDS and attends over
+// them as the tile form does (pair_step); workgroup (row, 0) writes the
+// row's indices.  The other workgroups take the window tiles.  Against a
+// select launch followed by a tile launch this drops a kernel boundary and
+// the tiles' round trip for their positions; the repeated selects read the
+// same candidate segments (about 20 KB a row, mostly from L2).  The select
+// and the tile take about 78 KB of LDS each, so two workgroups fit on a CU.
+__global__ __launch_bounds__(256, 2) void k_index_select_attend(IndexPass p, AttnPass a) {
+  __shared__ __attribute__((aligned(16))) union {
+    SelLdsFull<16> sel;
+    PairLds pair;
+  } U;
+  const int n_tile_idx = (a.n_idx + kAttnSplit - 1) / kAttnSplit;
+  const int n_win_tiles = a.n_tiles - n_tile_idx;
+  const int n_groups = (a.n_layers + 1) / 2;
+  const int n_sel = n_tile_idx * n_groups;
+  const int per_row = n_sel + a.n_layers * n_win_tiles;
+  // workgroup ids are dealt round-robin over the 8 XCDs: with a multiple of
+  // 8 rows, every workgroup of row r runs on XCD r mod 8
+  int row, j;
+  if (a.rows >= kXcds && a.rows % kXcds == 0) {
+    const int xcd = blockIdx.x & (kXcds - 1), w = blockIdx.x >> 3;
+    row = xcd + kXcds * (w / per_row);
+    j = w % per_row;
+  } else {
+    row = blockIdx.x / per_row;
+    j = blockIdx.x - row * per_row;
+  }
+  if (row >= a.rows) return;
+  if (j >= n_sel) {
+    const int jj = j - n_sel;
+    window_tile(a, row, jj / n_win_tiles, jj % n_win_tiles, U.pair.t);
+    return;
+  }
+  const int tile = j / n_groups, l0 = 2 * (j % n_groups);
+  const uint32_t n_win = select_row<16>(p, row, U.sel, j == 0);
+  const uint32_t c = (uint32_t)(tile * kAttnSplit + (threadIdx.x & 63));
+  const int32_t pos = c < n_win && (int)c < a.n_idx ? item_to_position(p, row, U.sel.win[c]) : -1;
+  __syncthreads();  // the winners are read: the LDS becomes the tile
+  const int seq = row / a.n_q;
+  const int nl = a.n_layers - l0 < 2 ? a.n_layers - l0 : 2;
+  const float sc2 = a.softmax_scale * 1.4426950408889634f;  // logits in the log2 domain
+  uint4 qb[16];
+  EntryFetch f;
+  fetch_entry<false>(a, seq, pos, f);
+  stage_q_pair(a, l0, nl, row, U.pair, qb);
+  store_entry<false>(f, U.pair.t);
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+  f32x4_t o[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[i][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  pair_step(U.pair, qb, nl == 2 ? 3 : 1, sc2, m_run, l_run, o);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i >= nl) break;  // uniform
+    write_partial(a, (l0 + i) * a.rows + row, tile, m_run[i], l_run[i], o[i]);
+  }
+}
+
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1749,8 +1846,17 @@ static int pass_chunks_per_row(const IndexPass& p) {
   return (int)m;
 }
 
-hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const AttnPass* window, bool* window_done) {
+// The fused select + attention launch takes a token-level pass whose
+// attention is in the tile form over the pass's own rows and k winners.
+static bool attend_fits(const IndexPass& p, const AttnPass& a) {
+  return p.block_level == 0 && a.n_idx == p.k && a.rows == p.rows && a.n_layers >= 1 && a.tiles_per_split == 1 &&
+         a.max_splits == a.n_tiles;
+}
+
+hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const AttnPass* window, bool* window_done,
+                             bool* tiles_done) {
   if (window_done) *window_done = false;
+  if (tiles_done) *tiles_done = false;
   if (p0.rows == 0 || p0.max_items == 0) return hipSuccess;
   IndexPass p = p0;
   const int scan_per_row = pass_chunks_per_row(p);
@@ -1793,6 +1899,13 @@ hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const Attn
   const bool wide = p.k > 1024 || scan_per_row > 128;
   if (wide) {
     hipLaunchKernelGGL(k_index_select<32>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+  } else if (window && tiles_done && attend_fits(p, *window)) {
+    const int n_tile_idx = (window->n_idx + kAttnSplit - 1) / kAttnSplit;
+    const int per_row = n_tile_idx * ((window->n_layers + 1) / 2) + window->n_layers * (window->n_tiles - n_tile_idx);
+    const int grows = window->rows >= kXcds ? (window->rows + kXcds - 1) / kXcds * kXcds : window->rows;
+    hipLaunchKernelGGL(k_index_select_attend, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p, *window);
+    if (window_done) *window_done = true;
+    *tiles_done = true;
   } else if (window) {
     const int n_win_tiles = window->n_tiles - (window->n_idx + kAttnSplit - 1) / kAttnSplit;
     const int n_wg = window->rows * window->n_layers * n_win_tiles;

@@ -451,4 +451,171 @@ __device__ __forceinline__ void window_tile(const AttnPass& p, int row, int laye
   write_partial(p, layer * p.rows + row, n_tile_idx + wtile, m_run, l_run, o);
 }
 
+// The pair step (the pair and tile forms of attn.hip, and the decode select
+// that attends over its own winners in index.hip): a tile serves two layers
+// at once.  Waves 0-1 score
+// the first layer (rows 0-31 and 32-63 of a tile), waves 2-3 the second, so
+// a wave holds only its own layer's Q^T operands; every wave then updates
+// both layers' O for its quarter of the channels.  A selected-entry tile is
+// gathered and dequantised once for the two layers; a window tile belongs to
+// one layer (the other's waves sit out its scoring).  Against the walk form
+// this halves the dequantisation and the tile loads per layer (prefill
+// attention of six layers 2.01 -> 1.59 ms).  The P . E products take one
+// layer after the other, so one layer's P operands are live at a time and
+// the kernel fits 2 waves per SIMD without spills (reading the transposed E
+// operands once for both layers spilled and ran no faster).
+struct PairLds {
+  TileLds t;                       // E, row_ok, P of the first layer, tile maxima per scoring wave
+  uint16_t Phi1[kH * kPStride];    // P of the second layer
+  uint16_t Plo1[kH * kPStride];
+  float red2[4][kH];               // per scoring wave: exponential sums per head
+  float alpha2[2][kH];             // the step's rescale factor per (layer, head)
+};
+
+// One tile for the layers in `active` (bit j: layer j of the pair): S^T for
+// the scoring waves, online-softmax update of both layers' (m, l), and
+// O = alpha O + P . E.  Starts with a workgroup barrier.
+__device__ __forceinline__ void pair_step(PairLds& s, const uint4 (&qb)[16], int active, float sc2, float (&m_run)[2],
+                                          float (&l_run)[2], f32x4_t (&o)[2][8]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int L = wave >> 1, hb = wave & 1;  // this wave scores layer L, rows 32 hb .. +31
+  const bool scorer = (active >> L) & 1;   // (uniform)
+  uint16_t* const phi[2] = {s.t.Phi, s.Phi1};
+  uint16_t* const plo[2] = {s.t.Plo, s.Plo1};
+  __syncthreads();  // the tile is in LDS; the previous step's readers of P / red are done
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  if (scorer) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = 32 * hb + 16 * rb + l16;
+      // logical chunk 4 ks + g4 of row r at (4 ks + g4) ^ row_swizzle(r)
+      const uint16_t* arow = s.t.E + r * kEStride + 8 * (g4 ^ ((r >> 2) & 1));
+      const int d3 = (r & 8) ? 64 : 0;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(arow + 32 * ks + ((ks & 2) ? -d3 : d3));
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[ks]), acc[rb], 0, 0, 0);
+      }
+    }
+  }
+  // lane (l16, g4) holds head l16 of rows 32 hb + 16 rb + 4 g4 + r
+  float lg[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int cr = 32 * hb + 16 * rb + 4 * g4 + r;
+      lg[rb][r] = scorer && s.t.row_ok[cr] ? acc[rb][r] * sc2 : -INFINITY;
+      mx = fmaxf(mx, lg[rb][r]);
+    }
+  mx = max_xor32(max_xor16(mx));
+  if (g4 == 0) s.t.red[wave][l16] = mx;
+  __syncthreads();
+  float m_new[2], alpha[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float m_tile = (active >> j) & 1 ? fmaxf(s.t.red[2 * j][l16], s.t.red[2 * j + 1][l16]) : -INFINITY;
+    m_new[j] = fmaxf(m_run[j], m_tile);
+    alpha[j] = m_run[j] == -INFINITY ? 0.0f : exp2f(m_run[j] - m_new[j]);
+    if (wave == 0 && g4 == 0) s.alpha2[j][l16] = alpha[j];  // read after the barrier below
+  }
+  if (scorer) {
+    const float mn = L == 0 ? m_new[0] : m_new[1];
+    float sum = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = mn == -INFINITY ? 0.0f : exp2f(lg[rb][r] - mn);
+        sum += pv[r];
+      }
+      const int c0 = l16 * kPStride + 32 * hb + 16 * rb + 4 * g4;
+      store_p4(pv, (L == 0 ? phi[0] : phi[1]) + c0, (L == 0 ? plo[0] : plo[1]) + c0);
+    }
+    sum = sum_xor32(sum_xor16(sum));
+    if (g4 == 0) s.red2[wave][l16] = sum;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float add = (active >> j) & 1 ? s.red2[2 * j][l16] + s.red2[2 * j + 1][l16] : 0.0f;
+    l_run[j] = l_run[j] * alpha[j] + add;
+    m_run[j] = m_new[j];
+  }
+  // O = alpha O + P . E for each active layer (rows 4 g4 .. +3 of O are
+  // heads 4 g4 .. +3)
+  float arow_alpha[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float4 aa = *reinterpret_cast<const float4*>(&s.alpha2[j][4 * g4]);
+    arow_alpha[j][0] = aa.x;
+    arow_alpha[j][1] = aa.y;
+    arow_alpha[j][2] = aa.z;
+    arow_alpha[j][3] = aa.w;
+  }
+  // transposing reads of E: lane (g4, l16) addresses row 8 g4 + l16 / 4 (+4,
+  // +32) and 4 channels at 4 (l16 % 4) of each 16-channel block; one layer
+  // after the other, so one layer's P operands are live at a time
+  const uint16_t* bbase = s.t.E + (8 * g4 + (l16 >> 2)) * kEStride + 128 * wave + 4 * (l16 & 3);
+  const int d8 = (g4 & 1) ? 64 : 0;  // rows with bit 3 set: halves of 256 bytes swapped
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!((active >> j) & 1)) continue;  // (uniform)
+    const uint16_t* pj = j == 0 ? s.t.Phi : s.Phi1;
+    const uint16_t* qj = j == 0 ? s.t.Plo : s.Plo1;
+    const uint4 ph0 = *reinterpret_cast<const uint4*>(pj + l16 * kPStride + 8 * g4);
+    const uint4 ph1 = *reinterpret_cast<const uint4*>(pj + l16 * kPStride + 32 + 8 * g4);
+    const uint4 pl0 = *reinterpret_cast<const uint4*>(qj + l16 * kPStride + 8 * g4);
+    const uint4 pl1 = *reinterpret_cast<const uint4*>(qj + l16 * kPStride + 32 + 8 * g4);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const uint16_t* bp = bbase + 16 * nt + (nt < 4 ? d8 : -d8);
+      const int dsw = (l16 & 2) ? -8 : 8;  // rows +4 and +36 hold their chunks swapped in pairs
+      const v4i16_t k0 = lds_read_tr16(bp), k1 = lds_read_tr16(bp + 4 * kEStride + dsw);
+      const v4i16_t k2 = lds_read_tr16(bp + 32 * kEStride), k3 = lds_read_tr16(bp + 36 * kEStride + dsw);
+      const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(k2, k3, 0, 1, 2, 3, 4, 5, 6, 7));
+      f32x4_t acc2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc2[r] = o[j][nt][r] * arow_alpha[j][r];
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ph0), b0, acc2, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl0), b0, acc2, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ph1), b1, acc2, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl1), b1, acc2, 0, 0, 0);
+      o[j][nt] = acc2;
+    }
+  }
+}
+
+// The queries of the pair, staged through E: layer j at rows 16 j .. +15
+// (thread t reads bytes 16 t + 4 KB i of each layer's 16 KB, whole lines per
+// wave instruction); each wave then reads the Q^T operands of the layer it
+// scores.  Ends with E free again.
+__device__ __forceinline__ void stage_q_pair(const AttnPass& p, int l0, int nl, int row, PairLds& s, uint4 (&qb)[16]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l16 = lane & 15, g4 = lane >> 4;
+  uint4 v[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    // a layer past the last loads the first layer's query again, unused
+    const uint4* src = reinterpret_cast<const uint4*>(p.layer[l0 + (j < nl ? j : 0)].q + (int64_t)row * kH * kD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[j][i] = src[t + 256 * i];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = 8 * (t + 256 * i);  // bf16 index within the layer's [16][512]
+      *reinterpret_cast<uint4*>(s.t.E + (16 * j + (o >> 9)) * kEStride + (o & 511)) = v[j][i];
+    }
+  __syncthreads();
+  const uint16_t* qrow = s.t.E + (16 * (wave >> 1) + l16) * kEStride + 8 * g4;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qb[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
+  __syncthreads();
+}
+
 }  // namespace csa2
