@@ -1764,18 +1764,26 @@ __global__ __launch_bounds__(256, 2) void k_index_select_attend(IndexPass p, Att
   const int n_win_tiles = a.n_tiles - n_tile_idx;
   const int n_groups = (a.n_layers + 1) / 2;
   const int n_sel = n_tile_idx * n_groups;
-  const int per_row = n_sel + a.n_layers * n_win_tiles;
-  // workgroup ids are dealt round-robin over the 8 XCDs: with a multiple of
-  // 8 rows, every workgroup of row r runs on XCD r mod 8
+  const int n_wt = a.n_layers * n_win_tiles;
+  // the selected-entry workgroups of every row first, then the window
+  // tiles, so the dispatcher spreads the long-running ones over the CUs
+  // before any CU takes a second workgroup; workgroup ids are dealt
+  // round-robin over the 8 XCDs: with a multiple of 8 rows, every workgroup
+  // of row r runs on XCD r mod 8
+  const int grows = a.rows >= kXcds ? (a.rows + kXcds - 1) / kXcds * kXcds : a.rows;
+  const bool sel_part = (int)blockIdx.x < grows * n_sel;
+  const int b = sel_part ? (int)blockIdx.x : (int)blockIdx.x - grows * n_sel;
+  const int per = sel_part ? n_sel : n_wt;
   int row, j;
   if (a.rows >= kXcds && a.rows % kXcds == 0) {
-    const int xcd = blockIdx.x & (kXcds - 1), w = blockIdx.x >> 3;
-    row = xcd + kXcds * (w / per_row);
-    j = w % per_row;
+    const int xcd = b & (kXcds - 1), w = b >> 3;
+    row = xcd + kXcds * (w / per);
+    j = w % per;
   } else {
-    row = blockIdx.x / per_row;
-    j = blockIdx.x - row * per_row;
+    row = b / per;
+    j = b - row * per;
   }
+  if (!sel_part) j += n_sel;
   if (row >= a.rows) return;
   if (j >= n_sel) {
     const int jj = j - n_sel;
