@@ -1750,7 +1750,8 @@ __global__ __launch_bounds__(256) void k_index_select_window(IndexPass p, AttnPa
 // such workgroup of a row reaches the same set and order: the select is
 // deterministic), takes winners 64 tile .. +63 from LDS and attends over
 // them as the tile form does (pair_step); workgroup (row, 0) writes the
-// row's indices.  The other workgroups take the window tiles.  Against a
+// row's indices.  The other workgroups take the window tiles, one
+// workgroup per (row, layer) walking its tiles.  Against a
 // select launch followed by a tile launch this drops a kernel boundary and
 // the tiles' round trip for their positions; the repeated selects read the
 // same candidate segments (about 20 KB a row, mostly from L2).  The select
@@ -1764,7 +1765,7 @@ __global__ __launch_bounds__(256, 2) void k_index_select_attend(IndexPass p, Att
   const int n_win_tiles = a.n_tiles - n_tile_idx;
   const int n_groups = (a.n_layers + 1) / 2;
   const int n_sel = n_tile_idx * n_groups;
-  const int n_wt = a.n_layers * n_win_tiles;
+  const int n_wt = a.n_layers;  // window workgroups per row: one per layer, walking its window tiles
   // the selected-entry workgroups of every row first, then the window
   // tiles, so the dispatcher spreads the long-running ones over the CUs
   // before any CU takes a second workgroup; workgroup ids are dealt
@@ -1786,8 +1787,10 @@ __global__ __launch_bounds__(256, 2) void k_index_select_attend(IndexPass p, Att
   if (!sel_part) j += n_sel;
   if (row >= a.rows) return;
   if (j >= n_sel) {
-    const int jj = j - n_sel;
-    window_tile(a, row, jj / n_win_tiles, jj % n_win_tiles, U.pair.t);
+    for (int wt = 0; wt < n_win_tiles; ++wt) {
+      if (wt) __syncthreads();  // the previous tile's readers of the LDS are done
+      window_tile(a, row, j - n_sel, wt, U.pair.t);
+    }
     return;
   }
   const int tile = j / n_groups, l0 = 2 * (j % n_groups);
@@ -1909,7 +1912,7 @@ hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const Attn
     hipLaunchKernelGGL(k_index_select<32>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
   } else if (window && tiles_done && attend_fits(p, *window)) {
     const int n_tile_idx = (window->n_idx + kAttnSplit - 1) / kAttnSplit;
-    const int per_row = n_tile_idx * ((window->n_layers + 1) / 2) + window->n_layers * (window->n_tiles - n_tile_idx);
+    const int per_row = n_tile_idx * ((window->n_layers + 1) / 2) + window->n_layers;
     const int grows = window->rows >= kXcds ? (window->rows + kXcds - 1) / kXcds * kXcds : window->rows;
     hipLaunchKernelGGL(k_index_select_attend, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p, *window);
     if (window_done) *window_done = true;
