@@ -811,13 +811,14 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       ia.out_pool = (hier || flat_pool) ? st->pool : nullptr;
       ia.pages = st->kv.pages;
       ia.key_heads = st->kv.key_heads;
-      // a flat decode pass in one launch runs the window tiles of the
-      // attention in its select launch (they need nothing the select
-      // computes), and the attention launch then takes the entry tiles only
+      // a decode index pass in one launch (any kind: the token-level select
+      // of HIER and POOL runs over a position list) runs the tile-form
+      // attention in its select launch (k_index_select_attend), or at least
+      // the window tiles, which need nothing the select computes; the
+      // attention launch then takes what is left
       AttnPass wp;
       const AttnPass* win = nullptr;
-      if ((ia.kind == CSA2_INDEX_FLAT || ia.kind == CSA2_INDEX_FLAT_POOL) && a->batch <= kMaxSeqPerLaunch &&
-          a->n_q < kPrefillMinQ) {
+      if (a->batch <= kMaxSeqPerLaunch && a->n_q < kPrefillMinQ) {
         wp = make_attn_pass(j, 0, a->batch, workspace, w);
         if (tile_form(wp)) win = &wp;
       }
