@@ -196,9 +196,8 @@ int64_t index_max_items(const csa2_index_args* a) {
 }
 
 int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t stream,
-              const AttnPass* window = nullptr, bool* window_done = nullptr, bool* tiles_done = nullptr) {
-  if (window_done) *window_done = false;
-  if (tiles_done) *tiles_done = false;
+              const AttnPass* attn = nullptr, bool* attended = nullptr) {
+  if (attended) *attended = false;
   for (int s0 = 0; s0 < a->batch; s0 += kMaxSeqPerLaunch) {
     const int nb = std::min(kMaxSeqPerLaunch, a->batch - s0);
     IndexPass p{};
@@ -296,7 +295,7 @@ int run_index(const csa2_index_args* a, void* ws, const WsLayout& w, hipStream_t
       p.block_max_stride = w.max_blocks;
       p.row_ksm = at<uint32_t>(ws, w.row_ksm);
     }
-    if ((e = launch_index_pass(p, stream, window, window_done, tiles_done)) != hipSuccess)
+    if ((e = launch_index_pass(p, stream, attn, attended)) != hipSuccess)
       return hip_fail(e, "index pass");
     if (a->kind == CSA2_INDEX_FLAT_POOL) {  // then the blocks by their largest token score
       IndexPass b = p;
@@ -359,8 +358,7 @@ struct AttnJob {
   float softmax_scale;
   int n_layers;
   AttnLayer layer[kMaxAttnLayers];
-  bool window_elsewhere;  // the window tiles ran in the select launch
-  bool tiles_elsewhere;   // so did the selected-entry tiles (only the merge is left)
+  bool tiles_elsewhere;   // the select launch ran every tile (only the merge is left)
   csa2_pages pages;       // paged nib / scale, or a zero table
 };
 
@@ -408,7 +406,6 @@ AttnPass make_attn_pass(const AttnJob& j, int s0, int nb, void* ws, const WsLayo
   p.tiles_per_split = (n_tiles + splits - 1) / splits;
   p.max_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   p.partial = at<float>(ws, w.partial);
-  p.window_elsewhere = j.window_elsewhere ? 1 : 0;
   p.tiles_elsewhere = j.tiles_elsewhere ? 1 : 0;
   return p;
 }
@@ -813,19 +810,17 @@ int run_group(const csa2_group_args* a, csa2_group_state* st, void* workspace, s
       ia.key_heads = st->kv.key_heads;
       // a decode index pass in one launch (any kind: the token-level select
       // of HIER and POOL runs over a position list) runs the tile-form
-      // attention in its select launch (k_index_select_attend), or at least
-      // the window tiles, which need nothing the select computes; the
-      // attention launch then takes what is left
+      // attention in its select launch (k_index_select_attend); the
+      // attention launch then only merges the partials
       AttnPass wp;
-      const AttnPass* win = nullptr;
+      const AttnPass* tiles = nullptr;
       if (a->batch <= kMaxSeqPerLaunch && a->n_q < kPrefillMinQ) {
         wp = make_attn_pass(j, 0, a->batch, workspace, w);
-        if (tile_form(wp)) win = &wp;
+        if (tile_form(wp)) tiles = &wp;
       }
-      bool win_done = false, tiles_done = false;
-      if ((rc = run_index(&ia, workspace, w, s, win, &win_done, &tiles_done))) return rc;
-      j.window_elsewhere = win_done;
-      j.tiles_elsewhere = tiles_done;
+      bool attended = false;
+      if ((rc = run_index(&ia, workspace, w, s, tiles, &attended))) return rc;
+      j.tiles_elsewhere = attended;
       if (L.mode == CSA2_MODE_FULL) {
         st->has_full = 1;
         st->has_pool = (hier || flat_pool) ? 1 : 0;

@@ -147,14 +147,14 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnPass p) {
 // layer pair j % n_groups (layers 2 g, 2 g + 1): the layers of a group
 // attend over the same entries, so a tile is gathered and dequantised once
 // for the pair, whose two layers are scored side by side (pair_step);
-// otherwise a window tile of one layer (none when the select launch ran
-// them: window_elsewhere).
+// otherwise a window tile of one layer.  (A decode group's index pass runs
+// all of these in its select launch instead: k_index_select_attend.)
 __global__ __launch_bounds__(256) void k_attention_tiles_pair(AttnPass p) {
   const int n_tile_idx = (p.n_idx + kAttnSplit - 1) / kAttnSplit;
   const int n_win_tiles = p.n_tiles - n_tile_idx;
   const int n_groups = (p.n_layers + 1) / 2;
   const int n_sel = n_tile_idx * n_groups;
-  const int per_row = n_sel + (p.window_elsewhere ? 0 : p.n_layers * n_win_tiles);
+  const int per_row = n_sel + p.n_layers * n_win_tiles;
   // workgroup ids are dealt round-robin over the 8 XCDs: with 8 or more rows,
   // all workgroups of a row run on one XCD, which then reads the row's
   // queries from memory once
@@ -456,7 +456,7 @@ hipError_t launch_attention(const AttnPass& p, hipStream_t stream) {
     // workgroup), scored side by side
     constexpr int LG = 2;
     const int n_groups = (p.n_layers + LG - 1) / LG;
-    const int per_row = n_tile_idx * n_groups + (p.window_elsewhere ? 0 : p.n_layers * (p.n_tiles - n_tile_idx));
+    const int per_row = n_tile_idx * n_groups + p.n_layers * (p.n_tiles - n_tile_idx);
     const int grows = p.rows >= kXcds ? (p.rows + kXcds - 1) / kXcds * kXcds : p.rows;
     if (tiles_here)
       hipLaunchKernelGGL(k_attention_tiles_pair, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p);

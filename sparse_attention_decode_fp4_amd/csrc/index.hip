@@ -1710,40 +1710,6 @@ __global__ __launch_bounds__(256) void k_index_select(IndexPass p) {
   select_row<kPer>(p, blockIdx.x, S);
 }
 
-// The select of a decode index pass with the window tiles of the group's
-// attention in the same launch: workgroups below p.rows select, each of the
-// others takes one window tile of one (layer, row).  The select occupies a
-// workgroup per row and leaves the rest of the chip idle, and the window
-// tiles need nothing it computes.
-template <int kPer>
-__global__ __launch_bounds__(256) void k_index_select_window(IndexPass p, AttnPass a) {
-  __shared__ union {
-    SelLdsFull<kPer> sel;
-    TileLds tile;
-  } U;
-  if ((int)blockIdx.x < p.rows) {
-    select_row<kPer>(p, blockIdx.x, U.sel);
-    return;
-  }
-  TileLds& s = U.tile;
-  const int n_win_tiles = a.n_tiles - (a.n_idx + kAttnSplit - 1) / kAttnSplit;
-  const int per_row = a.n_layers * n_win_tiles;
-  // with a multiple of 8 rows, the tiles of row r run on XCD r mod 8 (the
-  // XCD of its selected-entry tiles), so the merge finds every partial of
-  // the row in one L2
-  const int w = blockIdx.x - p.rows;
-  int row, jj;
-  if (p.rows >= kXcds && p.rows % kXcds == 0) {
-    const int xcd = w & (kXcds - 1), k = w >> 3;
-    row = xcd + kXcds * (k / per_row);
-    jj = k % per_row;
-  } else {
-    row = w / per_row;
-    jj = w - row * per_row;
-  }
-  window_tile(a, row, jj / n_win_tiles, jj % n_win_tiles, s);
-}
-
 // The select of a decode index pass fused with the group's whole attention
 // launch.  Workgroup (row, j) with j < n_sel: selected-entry tile j / n_groups
 // of layer pair j % n_groups.  It selects the row's winners itself (every
@@ -1864,10 +1830,8 @@ static bool attend_fits(const IndexPass& p, const AttnPass& a) {
          a.max_splits == a.n_tiles;
 }
 
-hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const AttnPass* window, bool* window_done,
-                             bool* tiles_done) {
-  if (window_done) *window_done = false;
-  if (tiles_done) *tiles_done = false;
+hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const AttnPass* attn, bool* attended) {
+  if (attended) *attended = false;
   if (p0.rows == 0 || p0.max_items == 0) return hipSuccess;
   IndexPass p = p0;
   const int scan_per_row = pass_chunks_per_row(p);
@@ -1910,18 +1874,12 @@ hipError_t launch_index_pass(const IndexPass& p0, hipStream_t stream, const Attn
   const bool wide = p.k > 1024 || scan_per_row > 128;
   if (wide) {
     hipLaunchKernelGGL(k_index_select<32>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
-  } else if (window && tiles_done && attend_fits(p, *window)) {
-    const int n_tile_idx = (window->n_idx + kAttnSplit - 1) / kAttnSplit;
-    const int per_row = n_tile_idx * ((window->n_layers + 1) / 2) + window->n_layers;
-    const int grows = window->rows >= kXcds ? (window->rows + kXcds - 1) / kXcds * kXcds : window->rows;
-    hipLaunchKernelGGL(k_index_select_attend, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p, *window);
-    if (window_done) *window_done = true;
-    *tiles_done = true;
-  } else if (window) {
-    const int n_win_tiles = window->n_tiles - (window->n_idx + kAttnSplit - 1) / kAttnSplit;
-    const int n_wg = window->rows * window->n_layers * n_win_tiles;
-    hipLaunchKernelGGL(k_index_select_window<16>, dim3((unsigned)(p.rows + n_wg)), dim3(256), 0, stream, p, *window);
-    if (window_done) *window_done = true;
+  } else if (attn && attend_fits(p, *attn)) {
+    const int n_tile_idx = (attn->n_idx + kAttnSplit - 1) / kAttnSplit;
+    const int per_row = n_tile_idx * ((attn->n_layers + 1) / 2) + attn->n_layers;
+    const int grows = attn->rows >= kXcds ? (attn->rows + kXcds - 1) / kXcds * kXcds : attn->rows;
+    hipLaunchKernelGGL(k_index_select_attend, dim3((unsigned)(grows * per_row)), dim3(256), 0, stream, p, *attn);
+    if (attended) *attended = true;
   } else {
     hipLaunchKernelGGL(k_index_select<16>, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
   }

@@ -161,13 +161,12 @@ hipError_t launch_block_keys(const uint8_t* k8, const float* ks, int64_t k_strid
                              const int64_t* n_entries, int32_t batch, uint8_t* bk8, float* bks,
                              int64_t bk_stride, hipStream_t stream);
 struct AttnPass;
-// `window`, if given, is the attention pass of the group the index pass
-// serves: its window tiles (window_tile) may run in the select launch, and
-// *window_done then says whether they did.  With `tiles_done` as well, the
-// select launch may run the whole tile-form attention (k_index_select_attend),
-// and *tiles_done says whether it did (only the merge is then left).
-hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnPass* window = nullptr,
-                             bool* window_done = nullptr, bool* tiles_done = nullptr);
+// `attn`, if given, is the tile-form attention pass of the group the index
+// pass serves: the select launch may run all of its tiles
+// (k_index_select_attend), and *attended then says whether it did (only the
+// merge is left).
+hipError_t launch_index_pass(const IndexPass& p, hipStream_t stream, const AttnPass* attn = nullptr,
+                             bool* attended = nullptr);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
 
 // Attention over the candidates of each row for one or more layers that
@@ -203,7 +202,6 @@ struct AttnPass {
   int32_t tiles_per_split;      // tiles one workgroup walks (online softmax)
   int32_t max_splits;           // ceil(n_tiles / tiles_per_split)
   int64_t swa_ring;             // 0: linear window rows from seq.b; > 0: token t at row t mod swa_ring
-  int32_t window_elsewhere;     // tile form: the window tiles ran in the select launch (window_tile)
   int32_t tiles_elsewhere;      // tile form: every tile ran in the select launch; only the merge is left
   PageMap pm;                   // paged nib / scale
   // workspace (used when max_splits > 1)
