@@ -12,9 +12,10 @@
 //              so that about 2.5 k keys of the full row reach T0;
 //   filter     MFMA scores of every visible (row, key) pair; pairs scoring at
 //              least T0 are appended to the row's candidate list, one segment
-//              per (row, key range).  A row belongs to one wave, which counts
-//              it in a register lane (no atomics); the grid is sized to fill
-//              the device in one round;
+//              per (row, key range): their scores are staged in LDS and, after
+//              every four A tiles, appended one per lane and round, each slot
+//              from an LDS atomic on its row's count; the grid is sized to
+//              fill the device in one round;
 //   select     if the list holds at least min(k, visible) candidates and did
 //              not overflow, it contains the whole top k.  MFMA scores are
 //              not binary32-exact (measured error up to ~2.5e-5 of the sum
@@ -107,6 +108,11 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
   // row thresholds (filter), each group of 8 rows stored as [even rows,
   // odd rows], so a lane's four rows 8a + 2i + half are one 16-byte read
   __shared__ __attribute__((aligned(16))) float thr[kFilter ? kPfRows : 4];
+  // filter: the scores of a quarter of a key block's pairs (A tiles a0,
+  // a0 + 1) per wave, [wave][4 (a mod 2) + i][lane], and the candidate count
+  // of each row (8 KB + 1 KB: three workgroups still fit on a CU)
+  __shared__ float sst[kFilter ? 4 * 8 * 64 : 4];
+  __shared__ uint32_t lcnt[kFilter ? kPfRows : 4];
 
   for (int i = t; i < kPfRows; i += 256) vis_row[i] = i < nq_tile ? pf_visible(p, seq, q0 + i) : 0;
   if (kFilter)
@@ -158,10 +164,8 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
     stage_ks[buf][t] = ksv;
   };
 
-  uint32_t cnt = 0u;  // filter: candidates of row 64 wave + lane so far
-  // the lane's segment for the rows 64 wave + 8a + 2i + half of this split
-  uint64_t* const list_lane = p.list + ((row0 + 64 * wave + half) * kPfSplits + split) * kPfSeg;
-  const uint32_t half_mask = half ? 0xFFFFFFFFu : 0u;
+  if (kFilter) lcnt[64 * wave + lane] = 0u;  // (a wave counts only its own rows: no barrier)
+  float* const sst_w = sst + (kFilter ? 8 * 64 * wave : 0);
   int buf = 0;
   stage_load(0, k_begin);
   for (int64_t base = k_begin; base < k_end; base += kPfStage) {
@@ -176,8 +180,8 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
       const float ksn = stage_ks[buf][bt + l32];
       const int64_t slot = base + bt + l32;
       const bool slot_ok = (bt + l32) < n_here;
-      const uint64_t slot_mask = __builtin_amdgcn_ballot_w64(slot_ok);
       const bool all_visible = kFilter ? (base + bt + 32 <= v_first) : true;
+      uint32_t hm = 0u;  // filter: bit 4 (a mod 2) + i: the pair of row 8 a + 2 i + half reached its threshold
       // head weights and thresholds of A tile a's rows (LDS), read one tile
       // ahead of their use
       auto load_wt = [&](int a, float4 (&wv)[4], float4& tv) {
@@ -207,55 +211,18 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
         // MFMA reads all lanes' operands, so it must not be sunk into one
         asm volatile("" ::"v"(sc[0]), "v"(sc[1]), "v"(sc[2]), "v"(sc[3]));
         if (kFilter) {
-          // append the pairs at or above their row's threshold.  A row's
-          // pairs all come from this wave (rows 64 wave .. + 63), so its
-          // count lives in lane r of cnt: the 32 lanes of a half share the
-          // row 8a + 2i + half, and each hit takes the slot count + (hits
-          // of its half in lower lanes), with no LDS atomic round trip.
-          // The causal-edge test (check_vis) runs only where the key block
-          // reaches past some row's visible keys: a uniform branch between
-          // two copies, so no per-lane flags are merged across it
-          auto append = [&](bool check_vis) {
+          // pairs at or above their row's threshold: their scores go to the
+          // wave's staging area and their bits to hm, and the appends wait
+          // for the flush after every odd A tile.  The causal-edge test
+          // (check_vis) runs only where the key block reaches past some
+          // row's visible keys (a uniform branch)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // lane masks straight from the compares (slot_ok's mask is
-              // taken once per key block)
-              const bool above = sc[i] >= tv_at(tv, i);
-              const bool vis = !check_vis || slot < vis_row[64 * wave + 8 * a + 2 * i + half];
-              uint64_t m = __builtin_amdgcn_ballot_w64(above) & slot_mask;
-              if (check_vis) m &= __builtin_amdgcn_ballot_w64(vis);
-              const bool h = slot_ok && above && vis;
-              if (m) {
-                const int r0 = 8 * a + 2 * i;  // row of half 0 within the wave
-                const uint32_t b0 = __builtin_amdgcn_readlane(cnt, r0);
-                const uint32_t b1 = __builtin_amdgcn_readlane(cnt, r0 + 1);
-                const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
-                const uint32_t n0 = __builtin_popcount(lo), n1 = __builtin_popcount(hi);
-                // entry index in the lane's list: row offset + the row's
-                // count + hits of its half in lower lanes.  mbcnt_lo adds
-                // all of half 0's hits to half 1's lanes, so their base is
-                // b1 - n0; the per-half base is picked with the lane mask
-                const uint32_t rbase = (uint32_t)(r0 * kPfSplits * kPfSeg);
-                const uint32_t x = ((b1 - n0 - b0) & half_mask) + (b0 + rbase);
-                const uint32_t off = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, x));
-                if (h && off < rbase + (uint32_t)kPfSeg) {
-                  // raw (position, score bits); the select makes the key
-                  uint32_t* dst = reinterpret_cast<uint32_t*>(list_lane + off);
-                  dst[0] = (uint32_t)slot;
-                  dst[1] = __float_as_uint(sc[i]);
-                }
-                // lanes r0 and r0 + 1 of cnt take the new counts (lane
-                // writes, no compare against every lane index)
-                asm("v_writelane_b32 %0, %1, %3\n\tv_writelane_b32 %0, %2, %4"
-                    : "+v"(cnt)
-                    : "s"(b0 + n0), "s"(b1 + n1), "i"(r0), "i"(r0 + 1));
-              }
-            }
-          };
-          if (all_visible)
-            append(false);
-          else
-            append(true);
+          for (int i = 0; i < 4; ++i) {
+            bool h = slot_ok && sc[i] >= tv_at(tv, i);
+            if (!all_visible) h = h && slot < vis_row[64 * wave + 8 * a + 2 * i + half];
+            sst_w[(4 * (a & 1) + i) * 64 + lane] = sc[i];
+            hm |= (h ? 1u : 0u) << (4 * (a & 1) + i);
+          }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -269,6 +236,26 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
       // result as an operand at the issue point, which keeps the compiler
       // from sinking the MFMA past the epilogue's branch to its own use (the
       // asm emits nothing, so nothing waits for the result there)
+      // Appends of the staged pairs of A tiles a0, a0 + 1: one pair per lane
+      // and round, its slot from an LDS atomic on its row's count (a round
+      // per hit of the lane with the most, about 1.25 on average, in place
+      // of a branch per (A tile, row pair) with any hit in the wave)
+      auto flush = [&](int a0) {
+        while (__builtin_amdgcn_ballot_w64(hm != 0u)) {
+          if (hm != 0u) {
+            const int b = __builtin_ctz(hm);
+            hm &= hm - 1u;
+            const float scb = sst_w[b * 64 + lane];
+            const int rl = 64 * wave + 8 * (a0 + (b >> 2)) + 2 * (b & 3) + half;
+            const uint32_t off = atomicAdd(&lcnt[rl], 1u);
+            if (off < (uint32_t)kPfSeg) {
+              // raw (position, score bits); the select makes the key
+              uint32_t* dst = reinterpret_cast<uint32_t*>(p.list + ((row0 + rl) * kPfSplits + split) * kPfSeg + off);
+              *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)slot, __float_as_uint(scb));
+            }
+          }
+        }
+      };
       v16f_t acc[2];
       float4 wv[2][4], tv[2];
       acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[0], B, v16f_t{}, 0, 0, 0, kUnitScales, 0,
@@ -287,11 +274,12 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
         }
         if (!kFilter) load_wt(a, wv[a & 1], tv[a & 1]);  // the sample pass: no pipeline
         epilogue(acc[a & 1], a, wv[a & 1], tv[a & 1]);
+        if (kFilter && (a & 1) == 1) flush(a - 1);
       }
     }
     buf ^= 1;
   }
-  if (kFilter && 64 * wave + lane < nq_tile) p.count[(row0 + 64 * wave + lane) * kPfSplits + split] = cnt;
+  if (kFilter && 64 * wave + lane < nq_tile) p.count[(row0 + 64 * wave + lane) * kPfSplits + split] = lcnt[64 * wave + lane];
 }
 
 // ------------------------------------------------------------------ threshold
