@@ -299,3 +299,30 @@ def test_state_errors(csa2):
     with pytest.raises(csa2.Csa2Error) as e:
         csa2.csa2_run_group(ws, st, [dict(mode=csa2.MODE_REINDEX, q=q, swa=swa, idx_q=iq)], [999], [1000], [872])
     assert e.value.code == csa2.ERR_STATE
+
+
+def test_group_odd_layers_and_rows(csa2):
+    """Plans whose last layer pair holds one layer (F+2U, R+U, F alone) over
+    9 sequences (more than 8 rows, not a multiple of 8), so the decode select
+    that attends over its own winners maps its grid the linear way and runs a
+    pair of one layer; every layer is compared with the oracle, and a Reuse
+    layer with the standalone attention call, bit for bit."""
+    n_entries = [3001 + 997 * b for b in range(9)]
+    stride = max(n_entries) + 15
+    B = len(n_entries)
+    dkv, hkv = _kv(csa2, 43, n_entries, stride, False)
+    rows = 128
+    q_pos0 = [n - 1 for n in n_entries]
+    swa_pos0 = [p - 127 for p in q_pos0]
+    ws = csa2.Workspace(B, 1, stride)
+    st = csa2.State(B, 1)
+    for run, plan in enumerate(["FUU", "RU", "F"]):
+        dl, hl = _layers(csa2, 43, plan, B, rows, dkv, hkv, 10 * run)
+        outs = csa2.csa2_run_group(ws, st, dl, q_pos0, n_entries, swa_pos0)
+        torch.cuda.synchronize()
+        print(plan, _compare(outs, st, hkv, hl, n_entries, q_pos0, swa_pos0, plan, "flat"))
+        if len(plan) > 1:
+            solo = csa2.csa2_sparse_swa_attn(ws, dl[-1]["q"], dkv._tensors[0], dkv._tensors[1], st.indices,
+                                             dl[-1]["swa"], q_pos0, swa_pos0, stride)
+            assert torch.equal(solo, outs[-1])
+    assert ws.fallbacks() == 0
