@@ -245,14 +245,17 @@ __global__ __launch_bounds__(256) void k_prefill_mfma(PrefillPass p) {
           if (hm != 0u) {
             const int b = __builtin_ctz(hm);
             hm &= hm - 1u;
+            // the staged score and the slot come back in one LDS round trip:
+            // the store is unconditional (a slot past the segment goes to
+            // its last entry: the row's count then exceeds the segment, and
+            // the select recomputes such a row without reading its list),
+            // so the score's load is not sunk behind the atomic's return
             const float scb = sst_w[b * 64 + lane];
             const int rl = 64 * wave + 8 * (a0 + (b >> 2)) + 2 * (b & 3) + half;
             const uint32_t off = atomicAdd(&lcnt[rl], 1u);
-            if (off < (uint32_t)kPfSeg) {
-              // raw (position, score bits); the select makes the key
-              uint32_t* dst = reinterpret_cast<uint32_t*>(p.list + ((row0 + rl) * kPfSplits + split) * kPfSeg + off);
-              *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)slot, __float_as_uint(scb));
-            }
+            const uint32_t at = off < (uint32_t)kPfSeg ? off : (uint32_t)kPfSeg - 1u;
+            uint32_t* dst = reinterpret_cast<uint32_t*>(p.list + ((row0 + rl) * kPfSplits + split) * kPfSeg + at);
+            *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)slot, __float_as_uint(scb));  // raw (position, score bits)
           }
         }
       };
