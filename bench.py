@@ -256,35 +256,50 @@ def append_timing(csa2, gen, B, dev, launches=200):
             "bytes_per_launch": B * (512 * 4 + 64 * 4 + 288 + 68 + 68 + (pos % 8) * 68 + 1024)}
 
 
-def graph_replay_seconds(torch, step, n_cycle, steps, warmup):
-    """Time `steps` steps replayed from captured HIP graphs: one graph holds
-    a whole cycle of n_cycle steps (each on its own cache copies), as a
-    serving loop captures the layer groups of a forward pass, so a graph
-    launch (about 8 us here) is paid once per cycle; steps past the last
-    whole cycle replay one-step graphs.  Returns the seconds of the timed
-    replays (exactly `steps` steps)."""
+def graph_replay_seconds(torch, step, n_cycle, steps, warmup, per_graph=4):
+    """Time `steps` steps replayed from captured HIP graphs.  A cycle of
+    n_cycle steps goes through every cache copy once; it is captured as
+    graphs of up to per_graph consecutive steps each (as a serving loop
+    captures the layer groups of a forward pass), so a graph launch (about
+    8 us here) is paid once per graph rather than once per step.  A step
+    that does not start a whole graph in the remaining count replays a
+    one-step graph.  Returns the seconds of the timed replays (exactly
+    `steps` steps)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    singles = []
+    groups, singles = [], []
     with torch.cuda.stream(s):
-        cycle = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(cycle, stream=s):
-            for i in range(n_cycle):
-                step(i)
+        for g0 in range(0, n_cycle, per_graph):
+            n = min(per_graph, n_cycle - g0)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(g0, g0 + n):
+                    step(i)
+            groups.append((g, n))
         for i in range(n_cycle):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
                 step(i)
             singles.append(g)
     torch.cuda.current_stream().wait_stream(s)
+    at = [0]  # the next step's index in the cycle
 
     def run(n):
-        for _ in range(n // n_cycle):
-            cycle.replay()
-        for i in range(n % n_cycle):
-            singles[i].replay()
+        done = 0
+        while done < n:
+            k = at[0]
+            g, cnt = groups[k // per_graph]
+            if k % per_graph == 0 and cnt <= n - done:
+                g.replay()
+            else:
+                cnt = 1
+                singles[k].replay()
+            done += cnt
+            at[0] = (k + cnt) % n_cycle
 
-    run(warmup)
+    # warm up over whole cycles: the timed replays then start a graph, on
+    # copies the last warm-up step did not touch
+    run(-(-warmup // n_cycle) * n_cycle)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(steps)
@@ -364,7 +379,7 @@ def hier(args):
     scan_ms, _ = csa2.csa2_profile_read(csa2.K_INDEX_SCAN)
     graph_s = None
     if not args.no_graph:
-        graph_s = graph_replay_seconds(torch, step, C, args.steps, args.warmup)
+        graph_s = graph_replay_seconds(torch, step, C, args.steps, args.warmup, per_graph=C)
     best_s = min(eager_s, graph_s) if graph_s is not None else eager_s
     # the two scans of a step: every block key once, then the 16,384-position pool
     scan_bytes = B * ((ctx + 7) // 8) * KEY_BYTES + B * 2048 * 8 * KEY_BYTES
@@ -480,6 +495,11 @@ def main():
     paged, page = args.workload == "paged", args.page_size
     if paged and ctx % page:
         raise SystemExit("--ctx must be a multiple of --page-size")
+    if full_only and B * ctx * key_bytes >= (16 << 20):
+        # a copy comes back after the other copies' scans: at least 1 GiB of
+        # them (64K: 32 copies of 35.7 MB), so the 256 MB Infinity Cache does
+        # not serve the scan (the 4K configuration fits it whatever the copies)
+        C = max(C, -(-(1 << 30) // (B * ctx * key_bytes)) + 1)
     seed = 1002
     # ---- caches: C copies, each its own draw
     kvs, keep = [], []
