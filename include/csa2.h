@@ -489,8 +489,10 @@ int csa2_workspace_fallbacks(const void* workspace, uint32_t* count, void* strea
 #define CSA2_K_QUANTIZE 0
 #define CSA2_K_BLOCK_KEYS 1
 #define CSA2_K_INDEX_SCAN 2
-#define CSA2_K_INDEX_SAMPLE 3
-#define CSA2_K_INDEX_SELECT 4
+#define CSA2_K_INDEX_SAMPLE 3     /* kept for numbering: no decode launch records it     */
+#define CSA2_K_INDEX_SELECT 4     /* in csa2_run_group decode calls, the select launch   */
+                                  /* also runs the attention tiles (CSA2_K_ATTENTION then */
+                                  /* records nothing; the merge keeps its own class)     */
 #define CSA2_K_ATTENTION 5
 #define CSA2_K_PREFILL_SAMPLE 6
 #define CSA2_K_ATTENTION_MERGE 7
