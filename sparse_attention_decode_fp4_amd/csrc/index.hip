@@ -25,10 +25,15 @@
 //           than twice the score's error bound above the k-th win, keys
 //           within it are rescored exactly (float64, the products of E4M3
 //           codes summed exactly) and ranked by (score, -position); the
-//           winners are ordered by position and written.  A row whose bands
-//           cannot hold the answer (a chunk holding more than its segment
-//           of the winners, e.g. all scores equal) is recomputed by itself
-//           over every item: slow, exact, rare, and counted.
+//           winners are ordered by position (segments list their bands in
+//           item order, so compacting them in gather order orders them) and
+//           written.  A row whose bands cannot hold the answer (a chunk
+//           holding more than its segment of the winners, e.g. all scores
+//           equal) is recomputed by itself over every item: slow, exact,
+//           rare, and counted.  In a decode group the select runs inside the
+//           group's attention launch (k_index_select_attend): every tile
+//           workgroup selects its row and attends over its share of the
+//           winners.
 // No separate pass picks a threshold for the scan: each chunk cuts its own
 // bands from its own scores, so the scan needs nothing from another kernel.
 #include "kernels.hpp"

@@ -1,7 +1,7 @@
 // Tile pieces of the sparse + SWA attention shared by the attention kernels
-// (attn.hip) and the decode select, whose launch also runs the window tiles
-// of a group (index.hip): the LDS tile, entry and window loads, the staged
-// queries, one online-softmax tile step and the partial write.
+// (attn.hip) and the decode select, whose launch also runs a group's
+// attention tiles (index.hip): the LDS tile, entry and window loads, the
+// staged queries, the online-softmax tile steps and the partial write.
 #pragma once
 
 #include "kernels.hpp"
