@@ -388,10 +388,17 @@ __device__ __forceinline__ void write_partial(const AttnPass& p, int unit, int s
   float* part = p.partial + ((int64_t)unit * p.max_splits + split) * kPartFloats;
   uint16_t* po = reinterpret_cast<uint16_t*>(part);
   float inv[4], down[4], up[4];
+  // a partial of one selected-entry tile holds convex combinations of
+  // dequantised entries, |value| <= 6 * 448 < 2^15: no scaling to search for
+  const bool bounded = p.tiles_per_split == 1 && split < (p.n_idx + kAttnSplit - 1) / kAttnSplit;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float l = __shfl(l_run, 4 * g4 + r, 64);  // l of head 4 g4 + r
     inv[r] = l > 0.0f ? 1.0f / l : 0.0f;
+    if (bounded) {
+      down[r] = up[r] = 1.0f;
+      continue;
+    }
     // the largest |O / l| of head 4 g4 + r over this wave's 128 channels
     // (the 16 lanes of g4, 8 each): its float32 exponent field, since the
     // bit patterns of non-negative floats order as integers
