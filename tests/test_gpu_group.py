@@ -305,9 +305,10 @@ def test_group_odd_layers_and_rows(csa2):
     """Plans whose last layer pair holds one layer (F+2U, R+U, F alone) over
     9 sequences (more than 8 rows, not a multiple of 8), so the decode select
     that attends over its own winners maps its grid the linear way and runs a
-    pair of one layer; every layer is compared with the oracle, and a Reuse
+    pair of one layer; two of the sequences hold fewer entries than k (300)
+    or a single one.  Every layer is compared with the oracle, and a Reuse
     layer with the standalone attention call, bit for bit."""
-    n_entries = [3001 + 997 * b for b in range(9)]
+    n_entries = [3001 + 997 * b for b in range(7)] + [300, 1]
     stride = max(n_entries) + 15
     B = len(n_entries)
     dkv, hkv = _kv(csa2, 43, n_entries, stride, False)
